@@ -1,0 +1,106 @@
+"""Fast LapSum on MI355X: exact-budget differentiable soft top-k.
+
+    p = soft_topk(r, k, t)      # sum(p) == k, p_i = F((r_i - b)/t), F the Laplace CDF
+
+The forward solve and the analytic VJP run in liblapsum.so (hand-written HIP
+for gfx950); this package only marshals torch tensors into the C ABI of
+include/lapsum.h.  It raises if the library is not built -- there is no CPU
+or PyTorch fallback.
+"""
+import ctypes
+
+import torch
+
+from ._binding import (PATH_AUTO, PATH_BRACKET, PATH_FORCE_FALLBACK, PATH_FULL, LapsumError, Options, Stats,
+                       default_options, lib)
+
+__all__ = ["forward", "vjp", "soft_topk", "SoftTopK", "default_options", "Options", "Stats", "LapsumError",
+           "PATH_AUTO", "PATH_FULL", "PATH_BRACKET", "PATH_FORCE_FALLBACK", "release_workspaces"]
+
+
+def _check_scores(x: torch.Tensor, name: str) -> None:
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if x.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device (got {x.device})")
+    if x.dtype != torch.float32:
+        raise ValueError(f"{name} must be float32 (got {x.dtype})")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_ptr(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def forward(r: torch.Tensor, k: float, t: float, *, options: Options = None, stats: bool = False,
+            p_out: torch.Tensor = None, b_out: torch.Tensor = None):
+    """Solve the exact-budget threshold and write p.
+
+    Returns (p, b) -- b is a 1-element float64 tensor on the same device --
+    or (p, b, stats_dict) when stats=True (which waits for the device)."""
+    _check_scores(r, "r")
+    n = r.numel()
+    with torch.cuda.device(r.device):
+        p = p_out if p_out is not None else torch.empty_like(r)
+        b = b_out if b_out is not None else torch.empty(1, dtype=torch.float64, device=r.device)
+        _check_scores(p, "p_out")
+        if b.dtype != torch.float64 or b.device != r.device or b.numel() < 1:
+            raise ValueError("b_out must be a float64 tensor with one element on r's device")
+        st = Stats() if stats else None
+        rc = lib().lapsum_forward_ex(r.data_ptr(), n, float(k), float(t), p.data_ptr(), b.data_ptr(),
+                                     ctypes.byref(options) if options is not None else None,
+                                     ctypes.byref(st) if st is not None else None, _stream_ptr(r.device))
+    if rc != 0:
+        raise LapsumError(rc, "lapsum_forward")
+    if stats:
+        return p, b, st.as_dict()
+    return p, b
+
+
+def vjp(r: torch.Tensor, g: torch.Tensor, t: float, b: torch.Tensor, *, grad_out: torch.Tensor = None):
+    """grad_i = (f_i/t)(g_i - sum g f / sum f), f_i = e^{-|r_i - b|/t}/2."""
+    _check_scores(r, "r")
+    _check_scores(g, "g")
+    if g.numel() != r.numel():
+        raise ValueError("g must have as many elements as r")
+    if b.dtype != torch.float64 or b.device != r.device:
+        raise ValueError("b must be the float64 device tensor returned by forward")
+    with torch.cuda.device(r.device):
+        out = grad_out if grad_out is not None else torch.empty_like(r)
+        _check_scores(out, "grad_out")
+        rc = lib().lapsum_vjp(r.data_ptr(), None, g.data_ptr(), r.numel(), float(t), b.data_ptr(), out.data_ptr(),
+                              _stream_ptr(r.device))
+    if rc != 0:
+        raise LapsumError(rc, "lapsum_vjp")
+    return out
+
+
+class SoftTopK(torch.autograd.Function):
+    """Autograd wrapper: forward solves for b and writes p; backward is the
+    analytic VJP with respect to the scores."""
+
+    @staticmethod
+    def forward(ctx, r, k, t, options=None):
+        rc = r.contiguous()
+        p, b = forward(rc, k, t, options=options)
+        ctx.save_for_backward(rc, b)
+        ctx.t = float(t)
+        return p
+
+    @staticmethod
+    def backward(ctx, g):
+        r, b = ctx.saved_tensors
+        grad = vjp(r, g.contiguous().to(torch.float32), ctx.t, b)
+        return grad, None, None, None
+
+
+def soft_topk(r: torch.Tensor, k: float, t: float, options: Options = None) -> torch.Tensor:
+    """Differentiable exact-budget soft top-k over a flat fp32 tensor."""
+    shape = r.shape
+    p = SoftTopK.apply(r.reshape(-1), k, t, options)
+    return p.reshape(shape)
+
+
+def release_workspaces() -> None:
+    lib().lapsum_release_workspaces()

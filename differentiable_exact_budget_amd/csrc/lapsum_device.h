@@ -1,0 +1,217 @@
+// Device-side definitions shared by the HIP kernels of the Fast LapSum solver
+// (gfx950, wave64).  Host code includes it for the control-block layout only.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lapsum {
+
+// ---------------------------------------------------------------------------
+// sizes
+// ---------------------------------------------------------------------------
+constexpr int kStreamThreads = 256;      // streaming kernels (filter, p, VJP)
+constexpr int kMaxStreamBlocks = 2048;   // 256 CUs x 8 resident blocks
+constexpr int kMaxBuckets = 256;         // band buckets
+constexpr int kBucketCapMax = 16384;     // band scores per bucket (LDS sort capacity)
+constexpr int kSortThreads = 1024;       // single-workgroup LDS sort / solve
+constexpr int kSortItems = 16;           // keys per thread in the LDS sort
+constexpr int kSmallMax = kSortThreads * kSortItems;  // 16384
+constexpr int kRadixThreads = 256;       // multi-workgroup radix pass
+constexpr int kRadixItems = 16;
+constexpr int kRadixTile = kRadixThreads * kRadixItems;  // 4096 keys
+constexpr int kRadixHistBlocks = 512;
+constexpr int kHistStride = 1028;        // 4 x 256 digit counts + a non-finite flag, per workgroup
+constexpr int kCurveThreads = 256;
+constexpr int kCurveTile = kRadixTile;   // sorted keys per curve segment
+constexpr int kSampleMax = 40960;        // sample size cap (select holds it in registers)
+constexpr int kSelectThreads = 1024;
+constexpr int kSelectItems = kSampleMax / kSelectThreads;  // 40
+constexpr int kCandMax = 2048;           // sample values kept for the splitters
+
+// control-block flags
+constexpr int kFlagNonFinite = 1;
+constexpr int kFlagOverflow = 2;
+constexpr int kFlagInternal = 4;
+
+// ---------------------------------------------------------------------------
+// control block: one per workspace, in device memory
+// ---------------------------------------------------------------------------
+struct Ctl {
+    // bracket and bucket layout (written by the select kernel)
+    float aL, aR;
+    int32_t ng;       // gaps between consecutive splitters
+    int32_t J;        // equal-width sub-buckets per finite gap
+    int32_t nb;       // ng * J buckets
+    int32_t flags;    // kFlag*
+    int32_t cap;      // bucket capacity in use
+    int32_t pad0;
+    // streaming filter results (written by the filter's last workgroup)
+    unsigned long long c_L, m, c_R;
+    double S_L, S_R, B_L, B_R;
+    // solve
+    double b;
+    long long jstar;  // 0-based sorted index of the interval's lower end (-1: below the first)
+    // p pass
+    double sum_p;
+    // VJP
+    double sumfg, sumf, c;
+    // last-workgroup tickets (each returns to 0 after use) and tile counters
+    unsigned int done[8];
+    unsigned int tile_ctr[4];
+    unsigned int pad1[4];
+};
+
+// host-pinned summary written by the filter's last workgroup; the host polls seq
+struct HostSummary {
+    unsigned long long c_L, m, c_R;
+    double S_L, S_R, B_L, B_R;
+    float aL, aR;
+    int32_t flags;
+    int32_t nb;
+    unsigned long long max_bucket;
+    volatile unsigned int seq;
+    unsigned int pad;
+};
+
+enum DoneSlot { kDoneFilter = 0, kDoneHist = 1, kDoneCurve = 2, kDoneBucket = 3, kDoneProbs = 4, kDoneVjp = 5 };
+
+#ifdef __HIP_DEVICE_COMPILE__
+#define LS_DEV __device__ __forceinline__
+#else
+#define LS_DEV __device__ __forceinline__
+#endif
+
+// ---------------------------------------------------------------------------
+// order-preserving fp32 <-> u32 keys (-0.0 is read as +0.0)
+// ---------------------------------------------------------------------------
+LS_DEV uint32_t f2key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u << 1) == 0u) u = 0u;
+    return u ^ ((u >> 31) ? 0xFFFFFFFFu : 0x80000000u);
+}
+LS_DEV float key2f(uint32_t k) {
+    uint32_t u = k ^ ((k >> 31) ? 0x80000000u : 0xFFFFFFFFu);
+    return __uint_as_float(u);
+}
+LS_DEV bool finite_f(float v) { return (__float_as_uint(v) & 0x7f800000u) != 0x7f800000u; }
+
+// e^y for y <= 0 with the hardware exp2 (1 ulp); argument pre-scaled by log2(e)
+LS_DEV float exp_neg(float y) { return __builtin_amdgcn_exp2f(y * 1.4426950408889634f); }
+
+// ---------------------------------------------------------------------------
+// wave helpers (wave64)
+// ---------------------------------------------------------------------------
+LS_DEV int lane_id() { return __lane_id(); }
+LS_DEV unsigned long long ballot(bool p) { return __ballot(p); }
+// number of set bits of mask below this lane
+LS_DEV int mbcnt(unsigned long long mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+LS_DEV int popc64(unsigned long long m) { return __popcll(m); }
+
+// lanes of `active` whose 8-bit digit equals this lane's digit
+LS_DEV unsigned long long match_digit8(uint32_t d, unsigned long long active) {
+    unsigned long long m = active;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        const bool bit = (d >> b) & 1u;
+        const unsigned long long bal = ballot(bit);
+        m &= bit ? bal : ~bal;
+    }
+    return m;
+}
+
+// fixed-order butterfly sums over the wave
+LS_DEV double wave_sum(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+LS_DEV unsigned long long wave_sum_u64(unsigned long long v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// inclusive scan of uint32 over the wave (Hillis-Steele with shuffles)
+LS_DEV uint32_t wave_inclusive_scan(uint32_t v) {
+    const int l = lane_id();
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        uint32_t y = __shfl_up(v, o, 64);
+        if (l >= o) v += y;
+    }
+    return v;
+}
+
+// block exclusive scan of uint32 (NT threads); returns the block total in *total
+template <int NT>
+LS_DEV uint32_t block_exclusive_scan(uint32_t v, uint32_t* total, uint32_t* scratch /* >= NT/64 + 1 */) {
+    constexpr int NW = NT / 64;
+    const int tid = threadIdx.x, w = tid >> 6, l = lane_id();
+    uint32_t inc = wave_inclusive_scan(v);
+    if (l == 63) scratch[w] = inc;
+    __syncthreads();
+    if (w == 0) {
+        uint32_t x = (l < NW) ? scratch[l] : 0u;
+        uint32_t xi = wave_inclusive_scan(x);
+        if (l < NW) scratch[l] = xi - x;
+        if (l == NW - 1) scratch[NW] = xi;
+    }
+    __syncthreads();
+    uint32_t res = scratch[w] + inc - v;
+    if (total) *total = scratch[NW];
+    __syncthreads();
+    return res;
+}
+
+// block sum of double in a fixed order (wave butterflies, then wave 0)
+template <int NT>
+LS_DEV double block_sum(double v, double* scratch /* >= NT/64 */) {
+    constexpr int NW = NT / 64;
+    const int w = threadIdx.x >> 6, l = lane_id();
+    v = wave_sum(v);
+    if (l == 0) scratch[w] = v;
+    __syncthreads();
+    double r = 0.0;
+    if (w == 0) {
+        double x = (l < NW) ? scratch[l] : 0.0;
+        r = wave_sum(x);
+    }
+    __syncthreads();
+    return r;  // valid in wave 0
+}
+
+template <int NT>
+LS_DEV unsigned long long block_sum_u64(unsigned long long v, unsigned long long* scratch) {
+    constexpr int NW = NT / 64;
+    const int w = threadIdx.x >> 6, l = lane_id();
+    v = wave_sum_u64(v);
+    if (l == 0) scratch[w] = v;
+    __syncthreads();
+    unsigned long long r = 0;
+    if (w == 0) {
+        unsigned long long x = (l < NW) ? scratch[l] : 0ull;
+        r = wave_sum_u64(x);
+    }
+    __syncthreads();
+    return r;  // valid in wave 0
+}
+
+// device-scope ticket for the last-workgroup pattern: release this
+// workgroup's global writes, take a ticket, and tell every thread whether it
+// is in the last workgroup to finish (which then sees all earlier writes).
+LS_DEV bool last_block_ticket(unsigned int* counter, int* s_flag) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __threadfence();
+        unsigned int prev = atomicAdd(counter, 1u);
+        *s_flag = (prev == gridDim.x - 1) ? 1 : 0;
+    }
+    __syncthreads();
+    bool last = *s_flag != 0;
+    if (last) __threadfence();
+    return last;
+}
+
+}  // namespace lapsum

@@ -1,0 +1,711 @@
+// Host orchestration and C ABI of the Fast LapSum solver (MI355X / gfx950).
+//
+// Paths (Fast LapSum paper, gist.science summary section 2.2):
+//  * full sort: sort, one stable prefix/suffix scan (the threshold curve),
+//    interval search, closed-form root.  One workgroup when n <= 16384,
+//    otherwise an LSD radix sort and per-tile curve aggregates.
+//  * bracketing (n > 10^6 by default): kernel-noised sample, binomial
+//    order statistics a_L = x_(l), a_R = x_(h), one streaming pass that
+//    folds out-of-band scores into fp64 tail sums and buckets the band,
+//    certification, band sort + solve.  The bracket is widened when it
+//    fails ("si no es asi, se amplia iterativamente") and the full sort
+//    covers whatever the bracket cannot (arxivdaily abstract: "a full-sort
+//    fallback that covers the worst-case scenario").
+//
+// Certification.  The streaming pass returns S_L, S_R, the band sums
+// B_L = sum_band e^{(a_L - v)/t}, B_R = sum_band e^{(v - a_R)/t} and the
+// counts.  G at the bracket ends follows exactly from them:
+//   G(a_L) = S_L/2 + m - B_L/2 + c_R - e^{(a_L - a_R)/t} S_R/2
+//   G(a_R) = e^{(a_L - a_R)/t} S_L/2 + B_R/2 + c_R - S_R/2
+// and the bracket holds iff G(a_L) >= k > G(a_R) (G is decreasing).  The
+// host reads these totals once per attempt (a pinned-memory hand-off from
+// the pass's last workgroup), so a failed bracket never costs a band sort.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <chrono>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <limits>
+#include <map>
+#include <mutex>
+#include <tuple>
+#include <vector>
+
+#include "../../include/lapsum.h"
+#include "../../include/lapsum_testing.h"
+#include "lapsum_launch.h"
+
+using namespace lapsum;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+struct Workspace {
+    int device = 0;
+    hipStream_t stream = nullptr;
+    long long n_cap = 0;
+    char* base = nullptr;
+    size_t bytes = 0;
+    Ctl* ctl = nullptr;
+    HostSummary* hs = nullptr;      // pinned host
+    HostSummary* hs_dev = nullptr;  // device view of hs
+    unsigned int seq = 0;
+    double* part = nullptr;
+    float* sample = nullptr;
+    long long* sample_idx = nullptr;
+    float* sp = nullptr;
+    float* iw = nullptr;
+    uint32_t* bucket_cnt = nullptr;
+    uint32_t* bucket_vals = nullptr;
+    SegArrays seg{};
+    SolveScratch sc{};
+    uint32_t* keysA = nullptr;
+    uint32_t* keysB = nullptr;
+    uint32_t* hist_part = nullptr;
+    uint32_t* goff = nullptr;
+    unsigned long long* status = nullptr;
+    size_t status_bytes = 0;
+    uint32_t epoch = 1;
+    std::vector<hipEvent_t> events;
+};
+
+std::mutex g_mu;
+std::map<std::pair<int, hipStream_t>, Workspace*> g_ws;
+
+long long tiles_for(long long n) { return (n + kRadixTile - 1) / kRadixTile; }
+
+// layout of one workspace for forwards up to n_cap scores
+struct Layout {
+    size_t ctl, part, sample, sample_idx, sp, iw, bcnt, bvals, seg_first, seg_last, seg_P, seg_Bx, seg_cnt, seg_off,
+        sc_pk, sc_pv, sc_bk, sc_bv, sc_bfx, sc_rank, sc_eP, sc_eB, keysA, keysB, hist, goff, status, total;
+    size_t status_bytes;
+};
+
+Layout make_layout(long long n_cap) {
+    Layout L{};
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
+    const long long nseg = std::max<long long>(std::max<long long>(kMaxBuckets, tiles_for(n_cap)), 1);
+    const long long elem = std::max<long long>(kBucketCapMax, std::max(kRadixTile, kSmallMax));
+    L.ctl = take(sizeof(Ctl));
+    L.part = take(sizeof(double) * 8 * kMaxStreamBlocks);
+    L.sample = take(sizeof(float) * kSampleMax);
+    L.sample_idx = take(sizeof(long long) * kSampleMax);
+    L.sp = take(sizeof(float) * (kMaxBuckets + 1));
+    L.iw = take(sizeof(float) * kMaxBuckets);
+    L.bcnt = take(sizeof(uint32_t) * kMaxBuckets);
+    L.bvals = take(sizeof(uint32_t) * (size_t)kMaxBuckets * kBucketCapMax);
+    L.seg_first = take(sizeof(float) * nseg);
+    L.seg_last = take(sizeof(float) * nseg);
+    L.seg_P = take(sizeof(double) * nseg);
+    L.seg_Bx = take(sizeof(double) * nseg);
+    L.seg_cnt = take(sizeof(uint32_t) * nseg);
+    L.seg_off = take(sizeof(uint32_t) * nseg);
+    L.sc_pk = take(sizeof(float) * nseg);
+    L.sc_pv = take(sizeof(double) * nseg);
+    L.sc_bk = take(sizeof(float) * nseg);
+    L.sc_bv = take(sizeof(double) * nseg);
+    L.sc_bfx = take(sizeof(double) * nseg);
+    L.sc_rank = take(sizeof(uint32_t) * nseg);
+    L.sc_eP = take(sizeof(double) * elem);
+    L.sc_eB = take(sizeof(double) * elem);
+    const long long nk = std::max<long long>(n_cap, 1);
+    L.keysA = take(sizeof(uint32_t) * nk);
+    L.keysB = take(sizeof(uint32_t) * nk);
+    L.hist = take(sizeof(uint32_t) * kHistStride * kRadixHistBlocks);
+    L.goff = take(sizeof(uint32_t) * 1024);
+    L.status_bytes = sizeof(unsigned long long) * 256 * (size_t)std::max<long long>(tiles_for(n_cap), 1);
+    L.status = take(L.status_bytes);
+    L.total = o;
+    return L;
+}
+
+void free_ws(Workspace* w) {
+    if (!w) return;
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    (void)hipSetDevice(w->device);
+    (void)hipStreamSynchronize(w->stream);
+    for (hipEvent_t e : w->events) (void)hipEventDestroy(e);
+    if (w->base) (void)hipFree(w->base);
+    if (w->hs) (void)hipHostFree(w->hs);
+    (void)hipSetDevice(cur);
+    delete w;
+}
+
+lapsum_status_t alloc_ws(Workspace* w, long long n_cap) {
+    Layout L = make_layout(n_cap);
+    char* base = nullptr;
+    if (hipMalloc(&base, L.total) != hipSuccess) return LAPSUM_ERR_OUT_OF_MEMORY;
+    w->base = base;
+    w->bytes = L.total;
+    w->n_cap = n_cap;
+    w->ctl = reinterpret_cast<Ctl*>(base + L.ctl);
+    w->part = reinterpret_cast<double*>(base + L.part);
+    w->sample = reinterpret_cast<float*>(base + L.sample);
+    w->sample_idx = reinterpret_cast<long long*>(base + L.sample_idx);
+    w->sp = reinterpret_cast<float*>(base + L.sp);
+    w->iw = reinterpret_cast<float*>(base + L.iw);
+    w->bucket_cnt = reinterpret_cast<uint32_t*>(base + L.bcnt);
+    w->bucket_vals = reinterpret_cast<uint32_t*>(base + L.bvals);
+    w->seg = SegArrays{reinterpret_cast<float*>(base + L.seg_first), reinterpret_cast<float*>(base + L.seg_last),
+                       reinterpret_cast<double*>(base + L.seg_P), reinterpret_cast<double*>(base + L.seg_Bx),
+                       reinterpret_cast<uint32_t*>(base + L.seg_cnt), reinterpret_cast<uint32_t*>(base + L.seg_off)};
+    w->sc = SolveScratch{reinterpret_cast<float*>(base + L.sc_pk), reinterpret_cast<double*>(base + L.sc_pv),
+                         reinterpret_cast<float*>(base + L.sc_bk), reinterpret_cast<double*>(base + L.sc_bv),
+                         reinterpret_cast<double*>(base + L.sc_bfx), reinterpret_cast<uint32_t*>(base + L.sc_rank),
+                         reinterpret_cast<double*>(base + L.sc_eP), reinterpret_cast<double*>(base + L.sc_eB)};
+    w->keysA = reinterpret_cast<uint32_t*>(base + L.keysA);
+    w->keysB = reinterpret_cast<uint32_t*>(base + L.keysB);
+    w->hist_part = reinterpret_cast<uint32_t*>(base + L.hist);
+    w->goff = reinterpret_cast<uint32_t*>(base + L.goff);
+    w->status = reinterpret_cast<unsigned long long*>(base + L.status);
+    w->status_bytes = L.status_bytes;
+    w->epoch = 1;
+    // the control block (tickets, counters) and the look-back words start at zero
+    if (hipMemsetAsync(w->ctl, 0, sizeof(Ctl), w->stream) != hipSuccess) return LAPSUM_ERR_HIP;
+    if (hipMemsetAsync(w->status, 0, w->status_bytes, w->stream) != hipSuccess) return LAPSUM_ERR_HIP;
+    return LAPSUM_OK;
+}
+
+lapsum_status_t get_ws(hipStream_t stream, long long n, Workspace** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return LAPSUM_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto key = std::make_pair(dev, stream);
+    auto it = g_ws.find(key);
+    Workspace* w = (it == g_ws.end()) ? nullptr : it->second;
+    if (w && w->n_cap >= n) { *out = w; return LAPSUM_OK; }
+    if (w) {
+        // grow: wait for this stream's work, then replace the device buffer
+        (void)hipStreamSynchronize(stream);
+        (void)hipFree(w->base);
+        w->base = nullptr;
+    } else {
+        w = new Workspace();
+        w->device = dev;
+        w->stream = stream;
+        void* hp = nullptr;
+        if (hipHostMalloc(&hp, sizeof(HostSummary), hipHostMallocCoherent | hipHostMallocMapped) != hipSuccess) {
+            delete w;
+            return LAPSUM_ERR_OUT_OF_MEMORY;
+        }
+        std::memset(hp, 0, sizeof(HostSummary));
+        w->hs = reinterpret_cast<HostSummary*>(hp);
+        void* dp = nullptr;
+        if (hipHostGetDevicePointer(&dp, hp, 0) != hipSuccess) dp = hp;
+        w->hs_dev = reinterpret_cast<HostSummary*>(dp);
+        g_ws[key] = w;
+    }
+    lapsum_status_t st = alloc_ws(w, std::max<long long>(n, 1 << 16));
+    if (st != LAPSUM_OK) {
+        g_ws.erase(key);
+        if (w->hs) (void)hipHostFree(w->hs);
+        if (w->base) (void)hipFree(w->base);
+        delete w;
+        return st;
+    }
+    *out = w;
+    return LAPSUM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// per-launch timing (options.profile)
+// ---------------------------------------------------------------------------
+struct Timer {
+    Workspace* w;
+    hipStream_t st;
+    bool on;
+    int used = 0;
+    std::vector<const char*> names;
+    hipEvent_t ev(int i) {
+        while ((int)w->events.size() <= i) {
+            hipEvent_t e;
+            (void)hipEventCreate(&e);
+            w->events.push_back(e);
+        }
+        return w->events[i];
+    }
+    void begin(const char* name) {
+        if (!on || (int)names.size() >= LAPSUM_MAX_TIMED_KERNELS) return;
+        (void)hipEventRecord(ev(2 * (int)names.size()), st);
+        names.push_back(name);
+    }
+    void end() {
+        if (!on || names.empty() || used >= (int)names.size()) return;
+        (void)hipEventRecord(ev(2 * used + 1), st);
+        ++used;
+    }
+    void collect(lapsum_stats_t* s) {
+        if (!s) return;
+        s->n_timed = 0;
+        if (!on) return;
+        for (int i = 0; i < used; ++i) {
+            float ms = 0.0f;
+            (void)hipEventElapsedTime(&ms, w->events[2 * i], w->events[2 * i + 1]);
+            s->kernel_ms[i] = ms;
+            s->kernel_name[i] = names[i];
+        }
+        s->n_timed = used;
+    }
+};
+
+// ---------------------------------------------------------------------------
+// binomial order-statistic ranks: Y ~ Bin(s, q) scores below b among s samples.
+//   l = largest l with P(Y <= l - 1) <= delta   (0: a_L = -inf)
+//   h = smallest h with P(Y >= h) <= delta      (s + 1: a_R = +inf)
+// The pmf is evaluated from its mode outwards by the ratio recurrence, far
+// enough that the neglected mass is below 1e-300.
+// ---------------------------------------------------------------------------
+void binomial_ranks(long long s, double q, double delta, long long* l_out, long long* h_out) {
+    static std::mutex mu;
+    static std::map<std::tuple<long long, double, double>, std::pair<long long, long long>> cache;
+    {
+        std::lock_guard<std::mutex> lk(mu);
+        auto it = cache.find(std::make_tuple(s, q, delta));
+        if (it != cache.end()) { *l_out = it->second.first; *h_out = it->second.second; return; }
+    }
+    long long mode = (long long)std::floor((double)(s + 1) * q);
+    if (mode > s) mode = s;
+    if (mode < 0) mode = 0;
+    const double lq = std::log(q), l1q = std::log1p(-q);
+    const double lmode = std::lgamma((double)s + 1.0) - std::lgamma((double)mode + 1.0) -
+                         std::lgamma((double)(s - mode) + 1.0) + (double)mode * lq + (double)(s - mode) * l1q;
+    std::vector<double> lp(s + 1, -INFINITY);
+    lp[mode] = lmode;
+    const double odds = lq - l1q;  // ln(q / (1 - q))
+    long long lo = mode, hi = mode;
+    for (long long i = mode; i > 0; --i) {  // pmf(i-1) = pmf(i) * i / (s - i + 1) / odds
+        lp[i - 1] = lp[i] + std::log((double)i) - std::log((double)(s - i + 1)) - odds;
+        lo = i - 1;
+        if (lp[i - 1] < -700.0) break;
+    }
+    for (long long i = mode; i < s; ++i) {  // pmf(i+1) = pmf(i) * (s - i) / (i + 1) * odds
+        lp[i + 1] = lp[i] + std::log((double)(s - i)) - std::log((double)(i + 1)) + odds;
+        hi = i + 1;
+        if (lp[i + 1] < -700.0) break;
+    }
+    long long l = 0;
+    double cdf = 0.0;
+    for (long long y = 0; y <= s; ++y) {
+        if (y >= lo && y <= hi) cdf += std::exp(lp[y]);
+        if (cdf <= delta) l = y + 1; else break;
+        if (y < lo) { y = lo - 1; }  // skip the negligible part in one step
+    }
+    long long h = s + 1;
+    double tail = 0.0;
+    for (long long i = s; i >= 0; --i) {
+        if (i >= lo && i <= hi) tail += std::exp(lp[i]);
+        if (tail <= delta) h = i; else break;
+        if (i > hi) { i = hi + 1; }
+    }
+    *l_out = l;
+    *h_out = h;
+    std::lock_guard<std::mutex> lk(mu);
+    cache[std::make_tuple(s, q, delta)] = std::make_pair(l, h);
+}
+
+lapsum_status_t hip_ok(hipError_t e) { return e == hipSuccess ? LAPSUM_OK : LAPSUM_ERR_HIP; }
+
+lapsum_status_t wait_summary(Workspace* w, hipStream_t st, unsigned int seq) {
+    volatile unsigned int* flag = &w->hs->seq;
+    auto t0 = std::chrono::steady_clock::now();
+    for (unsigned long it = 0;; ++it) {
+        if (*flag == seq) { std::atomic_thread_fence(std::memory_order_acquire); return LAPSUM_OK; }
+        if ((it & 4095u) == 4095u) {
+            hipError_t e = hipStreamQuery(st);
+            if (e == hipSuccess) {
+                if (*flag == seq) { std::atomic_thread_fence(std::memory_order_acquire); return LAPSUM_OK; }
+                return LAPSUM_ERR_INTERNAL;
+            }
+            if (e != hipErrorNotReady) return LAPSUM_ERR_HIP;
+            if (std::chrono::steady_clock::now() - t0 > std::chrono::seconds(120)) return LAPSUM_ERR_INTERNAL;
+        }
+    }
+}
+
+uint32_t next_epoch(Workspace* w, hipStream_t st) {
+    if (w->epoch + 8u >= (1u << 30)) {
+        (void)hipMemsetAsync(w->status, 0, w->status_bytes, st);
+        w->epoch = 1;
+    }
+    uint32_t e = w->epoch;
+    w->epoch += 4;
+    return e;
+}
+
+void run_full(Workspace* w, const float* r, long long n, double k, double t, double* b_out, hipStream_t st, Timer& tm) {
+    if (n <= kSmallMax) {
+        tm.begin("small_solve");
+        launch_small_solve(r, (int)n, k, t, w->ctl, w->sc, b_out, nullptr, st);
+        tm.end();
+        return;
+    }
+    const uint32_t epoch = next_epoch(w, st);
+    tm.begin("radix_sort");
+    launch_radix_sort(r, n, w->keysA, w->keysB, w->hist_part, w->goff, w->status, epoch, w->ctl, st);
+    tm.end();
+    tm.begin("curve_solve");
+    launch_curve_tiles(w->keysB, n, w->ctl, w->seg, w->sc, k, t, b_out, st);
+    tm.end();
+}
+
+struct BracketResult {
+    bool certified = false, overflow = false, nonfinite = false;
+    double gL = 0.0, gR = 0.0;
+    HostSummary h{};
+};
+
+// G(a_L), G(a_R) from the streaming pass's totals
+void certify(const HostSummary& h, double k, double t, BracketResult* res) {
+    const double m = (double)h.m, cR = (double)h.c_R;
+    const bool finL = std::isfinite(h.aL), finR = std::isfinite(h.aR);
+    const double cross = (finL && finR) ? std::exp(((double)h.aL - (double)h.aR) / t) : 0.0;
+    res->gL = finL ? 0.5 * h.S_L + m - 0.5 * h.B_L + cR - 0.5 * cross * h.S_R : (double)(h.c_L + h.m + h.c_R);
+    res->gR = finR ? 0.5 * cross * h.S_L + 0.5 * h.B_R + cR - 0.5 * h.S_R : 0.0;
+    res->certified = (res->gL >= k) && (res->gR < k);
+}
+
+lapsum_status_t check_args(const float* r, int64_t n, double k, float t, const void* p, const void* b) {
+    if (!r || !p || !b) return LAPSUM_ERR_INVALID_ARGUMENT;
+    if (n < 1 || n > 0xFFFFFFFFll) return LAPSUM_ERR_INVALID_ARGUMENT;
+    if (!(k > 0.0) || !(k < (double)n) || !std::isfinite(k)) return LAPSUM_ERR_INVALID_ARGUMENT;
+    if (!(t > 0.0f) || !std::isfinite(t)) return LAPSUM_ERR_INVALID_ARGUMENT;
+    return LAPSUM_OK;
+}
+
+lapsum_status_t fill_stats(Workspace* w, hipStream_t st, lapsum_stats_t* stats) {
+    if (!stats) return LAPSUM_OK;
+    if (hipStreamSynchronize(st) != hipSuccess) return LAPSUM_ERR_HIP;
+    Ctl c;
+    if (hipMemcpy(&c, w->ctl, sizeof(Ctl), hipMemcpyDeviceToHost) != hipSuccess) return LAPSUM_ERR_HIP;
+    stats->b = c.b;
+    stats->sum_p = c.sum_p;
+    if (c.flags & kFlagNonFinite) stats->status = LAPSUM_ERR_NONFINITE_INPUT;
+    else if (c.flags & kFlagInternal) stats->status = LAPSUM_ERR_INTERNAL;
+    else stats->status = LAPSUM_OK;
+    return LAPSUM_OK;
+}
+
+lapsum_status_t forward_impl(const float* r, int64_t n, double k, float t_f, float* p, double* b_out,
+                             const lapsum_options_t& opt, lapsum_stats_t* stats, hipStream_t st) {
+    lapsum_status_t a = check_args(r, n, k, t_f, p, b_out);
+    if (a != LAPSUM_OK) return a;
+    if (opt.bucket_capacity < 1 || opt.bucket_capacity > kBucketCapMax || !(opt.sample_factor > 0.0) ||
+        !(opt.delta > 0.0 && opt.delta < 0.5) || !(opt.margin_scale >= 0.0) || opt.max_widen < 0)
+        return LAPSUM_ERR_INVALID_ARGUMENT;
+    Workspace* w = nullptr;
+    lapsum_status_t gs = get_ws(st, n, &w);
+    if (gs != LAPSUM_OK) return gs;
+    const double t = (double)t_f;
+    Timer tm{w, st, opt.profile != 0};
+    if (stats) {
+        std::memset(stats, 0, sizeof(*stats));
+        stats->a_L = -INFINITY; stats->a_R = INFINITY;
+    }
+    int path = opt.path;
+    if (path == LAPSUM_PATH_AUTO) path = (n > opt.auto_threshold) ? LAPSUM_PATH_BRACKET : LAPSUM_PATH_FULL;
+
+    if (path == LAPSUM_PATH_FULL) {
+        run_full(w, r, n, k, t, b_out, st, tm);
+        tm.begin("probs");
+        launch_probs(r, n, t, p, w->ctl, w->part, st);
+        tm.end();
+        if (hipGetLastError() != hipSuccess) return LAPSUM_ERR_HIP;
+        if (stats) {
+            stats->path_taken = 1;
+            stats->band_size = n;
+            lapsum_status_t fs = fill_stats(w, st, stats);
+            tm.collect(stats);
+            return fs;
+        }
+        return LAPSUM_OK;
+    }
+
+    // ---- bracketing ----
+    long long s = (long long)std::ceil(opt.sample_factor * std::sqrt((double)n));
+    if (s < 1) s = 1;
+    if (s > kSampleMax) s = kSampleMax;
+    const double q = 1.0 - k / (double)n;
+    long long l0, h0;
+    binomial_ranks(s, q, opt.delta, &l0, &h0);
+    const double c0 = (double)s * q;
+    long long l = (long long)std::llround(c0 - opt.margin_scale * (c0 - (double)l0));
+    long long h = (long long)std::llround(c0 + opt.margin_scale * ((double)h0 - c0));
+    if (l < 0) l = 0;
+    if (h > s + 1) h = s + 1;
+    if (l > s) l = s;
+    if (h < 1) h = 1;
+    if (opt.margin_scale == 1.0) { l = l0; h = h0; }
+    const int cap = opt.bucket_capacity;
+
+    tm.begin("sample");
+    launch_sample(r, n, t, opt.seed, (int)s, w->sample, nullptr, st);
+    tm.end();
+    BracketResult br;
+    int widen = 0;
+    for (;;) {
+        tm.begin("select");
+        launch_select(w->sample, (int)s, l, h, cap, w->ctl, w->sp, w->iw, w->bucket_cnt, st);
+        tm.end();
+        const unsigned int seq = ++w->seq;
+        tm.begin("filter");
+        launch_filter(r, n, t, w->ctl, w->sp, w->iw, w->bucket_cnt, w->bucket_vals, cap, w->part, nullptr,
+                      w->hs_dev, seq, st);
+        tm.end();
+        if (hipGetLastError() != hipSuccess) return LAPSUM_ERR_HIP;
+        lapsum_status_t ws = wait_summary(w, st, seq);
+        if (ws != LAPSUM_OK) return ws;
+        br.h = *const_cast<HostSummary*>(w->hs);
+        br.nonfinite = (br.h.flags & kFlagNonFinite) != 0;
+        br.overflow = (br.h.flags & kFlagOverflow) != 0;
+        if (br.nonfinite) break;
+        certify(br.h, k, t, &br);
+        if (br.overflow || br.certified || path == LAPSUM_PATH_FORCE_FALLBACK) break;
+        if (widen >= opt.max_widen) break;
+        // widen the failing side: double its distance from s q
+        if (br.gL < k) {
+            const double d = std::max(1.0, 2.0 * (c0 - (double)l));
+            l = (long long)std::floor(c0 - d);
+            if (l < 0) l = 0;
+        } else {
+            const double d = std::max(1.0, 2.0 * ((double)h - c0));
+            h = (long long)std::ceil(c0 + d);
+            if (h > s + 1) h = s + 1;
+        }
+        ++widen;
+    }
+    if (stats) {
+        stats->widenings = widen;
+        stats->certified = br.certified ? 1 : 0;
+        stats->count_below = (int64_t)br.h.c_L;
+        stats->band_size = (int64_t)br.h.m;
+        stats->count_above = (int64_t)br.h.c_R;
+        stats->sample_size = s;
+        stats->rank_lo = l;
+        stats->rank_hi = h;
+        stats->buckets = br.h.nb;
+        stats->a_L = br.h.aL;
+        stats->a_R = br.h.aR;
+        stats->g_aL = br.gL;
+        stats->g_aR = br.gR;
+        stats->tail_S_L = br.h.S_L; stats->tail_S_R = br.h.S_R;
+        stats->band_B_L = br.h.B_L; stats->band_B_R = br.h.B_R;
+    }
+    if (br.nonfinite) {
+        launch_set_nan_b(w->ctl, b_out, st);
+        launch_fill(p, n, std::numeric_limits<float>::quiet_NaN(), st);
+        if (stats) { fill_stats(w, st, stats); stats->status = LAPSUM_ERR_NONFINITE_INPUT; tm.collect(stats); }
+        return LAPSUM_ERR_NONFINITE_INPUT;
+    }
+    const bool fallback = !br.certified || br.overflow || path == LAPSUM_PATH_FORCE_FALLBACK;
+    if (fallback) {
+        run_full(w, r, n, k, t, b_out, st, tm);
+    } else {
+        tm.begin("bucket_solve");
+        launch_bucket_solve(w->bucket_vals, w->bucket_cnt, cap, br.h.nb, w->ctl, w->seg, w->sc, k, t, b_out, st);
+        tm.end();
+    }
+    tm.begin("probs");
+    launch_probs(r, n, t, p, w->ctl, w->part, st);
+    tm.end();
+    if (hipGetLastError() != hipSuccess) return LAPSUM_ERR_HIP;
+    if (stats) {
+        stats->path_taken = fallback ? 3 : 2;
+        lapsum_status_t fs = fill_stats(w, st, stats);
+        tm.collect(stats);
+        return fs;
+    }
+    return LAPSUM_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+extern "C" {
+
+void lapsum_default_options(lapsum_options_t* opt) {
+    if (!opt) return;
+    std::memset(opt, 0, sizeof(*opt));
+    opt->path = LAPSUM_PATH_AUTO;
+    opt->max_widen = 2;
+    opt->seed = 0x5EEDull;
+    opt->sample_factor = 4.0;
+    opt->delta = 1e-5;
+    opt->margin_scale = 1.0;
+    opt->auto_threshold = 1000000;
+    opt->bucket_capacity = kBucketCapMax;
+    opt->profile = 0;
+}
+
+const char* lapsum_status_string(lapsum_status_t s) {
+    switch (s) {
+        case LAPSUM_OK: return "ok";
+        case LAPSUM_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case LAPSUM_ERR_NONFINITE_INPUT: return "non-finite score";
+        case LAPSUM_ERR_OUT_OF_MEMORY: return "out of device memory";
+        case LAPSUM_ERR_HIP: return "HIP runtime error";
+        case LAPSUM_ERR_INTERNAL: return "internal consistency check failed";
+    }
+    return "unknown status";
+}
+
+lapsum_status_t lapsum_forward_ex(const float* scores, int64_t n, double k, float t, float* p_out, double* b_out,
+                                  const lapsum_options_t* opt, lapsum_stats_t* stats, lapsum_stream_t stream) {
+    lapsum_options_t o;
+    if (opt) o = *opt; else lapsum_default_options(&o);
+    try {
+        return forward_impl(scores, n, k, t, p_out, b_out, o, stats, reinterpret_cast<hipStream_t>(stream));
+    } catch (...) {
+        return LAPSUM_ERR_INTERNAL;
+    }
+}
+
+lapsum_status_t lapsum_forward(const float* scores, int64_t n, double k, float t, float* p_out, double* b_out,
+                               lapsum_stream_t stream) {
+    return lapsum_forward_ex(scores, n, k, t, p_out, b_out, nullptr, nullptr, stream);
+}
+
+lapsum_status_t lapsum_vjp(const float* scores, const float* /*p*/, const float* g, int64_t n, float t,
+                           const double* b, float* grad_out, lapsum_stream_t stream) {
+    if (!scores || !g || !b || !grad_out) return LAPSUM_ERR_INVALID_ARGUMENT;
+    if (n < 1 || n > 0xFFFFFFFFll) return LAPSUM_ERR_INVALID_ARGUMENT;
+    if (!(t > 0.0f) || !std::isfinite(t)) return LAPSUM_ERR_INVALID_ARGUMENT;
+    try {
+        hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+        Workspace* w = nullptr;
+        lapsum_status_t gs = get_ws(st, 0, &w);
+        if (gs != LAPSUM_OK) return gs;
+        launch_vjp(scores, g, n, (double)t, b, grad_out, w->ctl, w->part, st, nullptr);
+        return hip_ok(hipGetLastError());
+    } catch (...) {
+        return LAPSUM_ERR_INTERNAL;
+    }
+}
+
+void lapsum_release_workspaces(void) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    for (auto& kv : g_ws) free_ws(kv.second);
+    g_ws.clear();
+}
+
+size_t lapsum_workspace_bytes(int64_t n) { return make_layout(std::max<long long>(n, 1 << 16)).total; }
+
+// ---------------------------------------------------------------------------
+// stage entry points for parity tests
+// ---------------------------------------------------------------------------
+lapsum_status_t lapsum_test_sort(const float* scores, int64_t n, float* out, lapsum_stream_t stream) {
+    if (!scores || !out || n < 1 || n > 0xFFFFFFFFll) return LAPSUM_ERR_INVALID_ARGUMENT;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    Workspace* w = nullptr;
+    lapsum_status_t gs = get_ws(st, n, &w);
+    if (gs != LAPSUM_OK) return gs;
+    const double k = n > 1 ? 0.5 * (double)n : 0.5;
+    if (n <= kSmallMax) {
+        launch_small_solve(scores, (int)n, k, 1.0, w->ctl, w->sc, nullptr, w->keysB, st);
+    } else {
+        const uint32_t epoch = next_epoch(w, st);
+        launch_radix_sort(scores, n, w->keysA, w->keysB, w->hist_part, w->goff, w->status, epoch, w->ctl, st);
+    }
+    if (hipStreamSynchronize(st) != hipSuccess) return LAPSUM_ERR_HIP;
+    std::vector<uint32_t> keys((size_t)n);
+    if (hipMemcpy(keys.data(), w->keysB, sizeof(uint32_t) * (size_t)n, hipMemcpyDeviceToHost) != hipSuccess)
+        return LAPSUM_ERR_HIP;
+    std::vector<float> vals((size_t)n);
+    for (size_t i = 0; i < (size_t)n; ++i) {
+        const uint32_t kk = keys[i];
+        const uint32_t u = kk ^ ((kk >> 31) ? 0x80000000u : 0xFFFFFFFFu);
+        std::memcpy(&vals[i], &u, 4);
+    }
+    return hip_ok(hipMemcpy(out, vals.data(), sizeof(float) * (size_t)n, hipMemcpyHostToDevice));
+}
+
+lapsum_status_t lapsum_test_sample(const float* scores, int64_t n, float t, uint64_t seed, int64_t s, float* x_out,
+                                   int64_t* idx_out, lapsum_stream_t stream) {
+    if (!scores || !x_out || n < 1 || s < 1 || s > kSampleMax || !(t > 0.0f)) return LAPSUM_ERR_INVALID_ARGUMENT;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    launch_sample(scores, n, (double)t, seed, (int)s, x_out, reinterpret_cast<long long*>(idx_out), st);
+    return hip_ok(hipStreamSynchronize(st));
+}
+
+lapsum_status_t lapsum_test_select(const float* x, int64_t s, int64_t l, int64_t h, float* aL_host, float* aR_host,
+                                   int32_t* nbuckets_host, lapsum_stream_t stream) {
+    if (!x || s < 1 || s > kSampleMax || l < 0 || h > s + 1 || l > s || h < 1) return LAPSUM_ERR_INVALID_ARGUMENT;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    Workspace* w = nullptr;
+    lapsum_status_t gs = get_ws(st, 0, &w);
+    if (gs != LAPSUM_OK) return gs;
+    launch_select(x, (int)s, l, h, kBucketCapMax, w->ctl, w->sp, w->iw, w->bucket_cnt, st);
+    if (hipStreamSynchronize(st) != hipSuccess) return LAPSUM_ERR_HIP;
+    Ctl c;
+    if (hipMemcpy(&c, w->ctl, sizeof(Ctl), hipMemcpyDeviceToHost) != hipSuccess) return LAPSUM_ERR_HIP;
+    if (aL_host) *aL_host = c.aL;
+    if (aR_host) *aR_host = c.aR;
+    if (nbuckets_host) *nbuckets_host = c.nb;
+    return LAPSUM_OK;
+}
+
+lapsum_status_t lapsum_test_filter(const float* scores, int64_t n, float t, float a_L, float a_R, int64_t* counts_host,
+                                   double* sums_host, float* band_out, int64_t band_cap, int64_t* band_size_host,
+                                   lapsum_stream_t stream) {
+    if (!scores || n < 1 || n > 0xFFFFFFFFll || !(t > 0.0f) || !(a_L <= a_R)) return LAPSUM_ERR_INVALID_ARGUMENT;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    Workspace* w = nullptr;
+    lapsum_status_t gs = get_ws(st, n, &w);
+    if (gs != LAPSUM_OK) return gs;
+    // a two-point "sample" whose order statistics are exactly a_L and a_R
+    float two[2] = {a_L, a_R};
+    if (hipMemcpy(w->sample, two, sizeof(two), hipMemcpyHostToDevice) != hipSuccess) return LAPSUM_ERR_HIP;
+    const long long l = std::isinf(a_L) ? 0 : 1;
+    const long long h = std::isinf(a_R) ? 3 : 2;
+    launch_select(w->sample, 2, l, h, kBucketCapMax, w->ctl, w->sp, w->iw, w->bucket_cnt, st);
+    const unsigned int seq = ++w->seq;
+    launch_filter(scores, n, (double)t, w->ctl, w->sp, w->iw, w->bucket_cnt, w->bucket_vals, kBucketCapMax, w->part,
+                  nullptr, w->hs_dev, seq, st);
+    lapsum_status_t ws = wait_summary(w, st, seq);
+    if (ws != LAPSUM_OK) return ws;
+    HostSummary hsum = *const_cast<HostSummary*>(w->hs);
+    if (counts_host) { counts_host[0] = (int64_t)hsum.c_L; counts_host[1] = (int64_t)hsum.m; counts_host[2] = (int64_t)hsum.c_R; }
+    if (sums_host) { sums_host[0] = hsum.S_L; sums_host[1] = hsum.S_R; sums_host[2] = hsum.B_L; sums_host[3] = hsum.B_R; }
+    if (hsum.flags & kFlagOverflow || (int64_t)hsum.m > band_cap) {
+        if (band_size_host) *band_size_host = -1;
+        return LAPSUM_OK;
+    }
+    // sort every bucket on the device (the band solve's first stage), then gather in bucket order
+    const double kk = (double)hsum.c_R + 0.5 * (double)hsum.m + 0.25;
+    launch_bucket_solve(w->bucket_vals, w->bucket_cnt, kBucketCapMax, hsum.nb, w->ctl, w->seg, w->sc,
+                        kk > 0 ? kk : 0.5, (double)t, nullptr, st);
+    if (hipStreamSynchronize(st) != hipSuccess) return LAPSUM_ERR_HIP;
+    std::vector<uint32_t> cnt(kMaxBuckets);
+    if (hipMemcpy(cnt.data(), w->bucket_cnt, sizeof(uint32_t) * kMaxBuckets, hipMemcpyDeviceToHost) != hipSuccess)
+        return LAPSUM_ERR_HIP;
+    std::vector<float> band;
+    band.reserve((size_t)hsum.m);
+    std::vector<uint32_t> buf;
+    for (int b = 0; b < hsum.nb; ++b) {
+        if (!cnt[b]) continue;
+        buf.resize(cnt[b]);
+        if (hipMemcpy(buf.data(), w->bucket_vals + (size_t)b * kBucketCapMax, sizeof(uint32_t) * cnt[b],
+                      hipMemcpyDeviceToHost) != hipSuccess)
+            return LAPSUM_ERR_HIP;
+        for (uint32_t kkey : buf) {
+            const uint32_t u = kkey ^ ((kkey >> 31) ? 0x80000000u : 0xFFFFFFFFu);
+            float f;
+            std::memcpy(&f, &u, 4);
+            band.push_back(f);
+        }
+    }
+    if (band_size_host) *band_size_host = (int64_t)band.size();
+    if (band_out && !band.empty())
+        if (hipMemcpy(band_out, band.data(), sizeof(float) * band.size(), hipMemcpyHostToDevice) != hipSuccess)
+            return LAPSUM_ERR_HIP;
+    return LAPSUM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,45 @@
+// Host-side launchers of the Fast LapSum kernels (each defined next to its kernels).
+#pragma once
+#include "lapsum_blocksolve.h"
+#include "lapsum_device.h"
+
+namespace lapsum {
+
+struct SegArrays {
+    float* first;
+    float* last;
+    double* P;
+    double* Bx;
+    uint32_t* cnt;
+    uint32_t* off;
+};
+
+// lapsum_sample.hip
+void launch_sample(const float* r, long long n, double t, unsigned long long seed, int s, float* x, long long* idx_out,
+                   hipStream_t st);
+void launch_select(const float* x, int s, long long l, long long h, int cap, Ctl* ctl, float* sp, float* iw,
+                   uint32_t* bucket_cnt, hipStream_t st);
+
+// lapsum_stream.hip
+int stream_blocks(long long n);
+void launch_filter(const float* r, long long n, double t, Ctl* ctl, const float* sp, const float* iw,
+                   uint32_t* bucket_cnt, uint32_t* bucket_vals, int cap, double* part, unsigned long long* partc,
+                   HostSummary* hs_dev, unsigned int seq, hipStream_t st);
+void launch_probs(const float* r, long long n, double t, float* p, Ctl* ctl, double* part, hipStream_t st);
+void launch_vjp(const float* r, const float* g, long long n, double t, const double* b, float* grad, Ctl* ctl,
+                double* part, hipStream_t st, hipEvent_t* ev_mid);
+void launch_fill(float* p, long long n, float v, hipStream_t st);
+void launch_set_nan_b(Ctl* ctl, double* b_out, hipStream_t st);
+
+// lapsum_sort.hip
+void launch_small_solve(const float* r, int n, double k, double t, Ctl* ctl, SolveScratch sc, double* b_out,
+                        uint32_t* keys_out, hipStream_t s);
+void launch_bucket_solve(uint32_t* bucket_vals, const uint32_t* bucket_cnt, int cap, int nb, Ctl* ctl, SegArrays seg,
+                         SolveScratch sc, double k, double t, double* b_out, hipStream_t s);
+int radix_hist_blocks(long long n);
+void launch_radix_sort(const float* r, long long n, uint32_t* keysA, uint32_t* keysB, uint32_t* hist_part,
+                       uint32_t* goff, unsigned long long* status, uint32_t epoch_base, Ctl* ctl, hipStream_t s);
+void launch_curve_tiles(const uint32_t* keys, long long n, Ctl* ctl, SegArrays seg, SolveScratch sc, double k, double t,
+                        double* b_out, hipStream_t s);
+
+}  // namespace lapsum

@@ -1,0 +1,374 @@
+// Sorting and threshold-solve kernels of the Fast LapSum solver (gfx950).
+//
+// Full-sort solver (Fast LapSum paper, gist.science section 2.2): sort all
+// scores, build the threshold curve with one stable prefix/suffix scan,
+// search the interval where the budget balances and take the closed-form
+// root there.  Band solve (same section, "Solucion Exacta"): the same on the
+// middle band only, with the out-of-band scores entering as tail sums.
+//
+// Kernels
+//   k_small_solve   n <= 16384: one workgroup sorts in LDS and solves.
+//   k_bucket_solve  one workgroup per band bucket sorts it in LDS and
+//                   publishes segment aggregates; the last one solves.
+//   k_radix_hist    all four 8-bit digit histograms in one read; the last
+//                   workgroup turns them into global digit offsets.
+//   k_radix_pass    one LSD digit pass (decoupled look-back across tiles).
+//   k_curve_tiles   per-tile curve aggregates of the sorted scores; the last
+//                   workgroup solves.
+#include "lapsum_blocksolve.h"
+#include "lapsum_launch.h"
+
+namespace lapsum {
+
+// segment aggregates of sorted scores v_0..v_{c-1} held as keys in `keys`
+// (LDS or global): P = sum e^{(v_i - v_last)/t}, Bx = sum_{i>0} e^{(v_0 - v_i)/t}.
+// Argument in fp64 (exact difference), exponential in fp32, sums in fp64.
+template <int NT>
+__device__ void segment_aggregates(const uint32_t* keys, int c, double inv_t, float* first, float* last,
+                                   double* P, double* Bx, double* scratch) {
+    const float f = key2f(keys[0]);
+    const float l = key2f(keys[c - 1]);
+    double p = 0.0, bx = 0.0;
+    for (int i = threadIdx.x; i < c; i += NT) {
+        const double v = (double)key2f(keys[i]);
+        p += (double)exp_neg((float)((v - (double)l) * inv_t));
+        if (i > 0) bx += (double)exp_neg((float)(((double)f - v) * inv_t));
+    }
+    const double ps = block_sum<NT>(p, scratch);
+    const double bs = block_sum<NT>(bx, scratch);
+    if (threadIdx.x == 0) { *first = f; *last = l; *P = ps; *Bx = bs; }
+}
+
+// ---------------------------------------------------------------------------
+// n <= 16384: everything in one workgroup
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kSortThreads) void k_small_solve(const float* __restrict__ r, int n, double k,
+                                                               double t, double inv_t, Ctl* ctl, SolveScratch sc,
+                                                               double* b_out, uint32_t* keys_out) {
+    __shared__ uint32_t keys[kSmallMax];
+    __shared__ uint32_t cnt[256 * (kSortThreads / 64)];
+    __shared__ uint32_t scr[32];
+    __shared__ float s_k[kSortThreads];
+    __shared__ double s_v[kSortThreads];
+    __shared__ int s_int[32];
+    __shared__ double s_red[kSortThreads / 64];
+    __shared__ float sg_first, sg_last;
+    __shared__ double sg_P, sg_Bx;
+    __shared__ uint32_t sg_cnt, sg_off;
+    __shared__ int s_bad;
+
+    const int tid = threadIdx.x;
+    if (tid == 0) s_bad = 0;
+    __syncthreads();
+    int bad = 0;
+    for (int i = tid; i < n; i += kSortThreads) {
+        const float v = r[i];
+        bad |= !finite_f(v);
+        keys[i] = f2key(v);
+    }
+    if (bad) atomicOr(&s_bad, 1);
+    __syncthreads();
+    block_sort_lds<kSortThreads, kSortItems>(keys, n, cnt, scr);
+    if (keys_out)
+        for (int i = tid; i < n; i += kSortThreads) keys_out[i] = keys[i];
+    segment_aggregates<kSortThreads>(keys, n, inv_t, &sg_first, &sg_last, &sg_P, &sg_Bx, s_red);
+    if (tid == 0) { sg_cnt = (uint32_t)n; sg_off = 0u; }
+    __syncthreads();
+    SegView sv{1, &sg_first, &sg_last, &sg_P, &sg_Bx, &sg_cnt, &sg_off, keys};
+    Tails tl{-INFINITY, INFINITY, 0.0, 0.0, (double)n, 0.0, k, t, inv_t};
+    SolveOut o = segment_solve<kSortThreads, kSortItems>(sv, tl, sc, s_k, s_v, s_int);
+    if (tid == 0) {
+        double b = o.b;
+        int flags = 0;
+        if (s_bad) { b = __longlong_as_double(0x7ff8000000000000ll); flags = kFlagNonFinite; }
+        else if (!o.ok) flags = kFlagInternal;
+        ctl->flags = flags;
+        ctl->b = b;
+        ctl->jstar = o.jstar;
+        if (b_out) *b_out = b;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// band buckets: sort each in LDS, publish aggregates, last workgroup solves
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kSortThreads) void k_bucket_solve(uint32_t* __restrict__ bucket_vals, const uint32_t* bucket_cnt,
+                                                                int cap, Ctl* ctl, SegArrays seg, SolveScratch sc,
+                                                                double k, double t, double inv_t, double* b_out) {
+    __shared__ uint32_t keys[kBucketCapMax];
+    __shared__ uint32_t cnt[256 * (kSortThreads / 64)];
+    __shared__ uint32_t scr[32];
+    __shared__ float s_k[kSortThreads];
+    __shared__ double s_v[kSortThreads];
+    __shared__ int s_int[32];
+    __shared__ double s_red[kSortThreads / 64];
+    __shared__ int s_last;
+
+    const int tid = threadIdx.x;
+    const int bkt = blockIdx.x;
+    const uint32_t c0 = bucket_cnt[bkt];
+    const int c = (int)min(c0, (uint32_t)cap);
+    uint32_t* vals = bucket_vals + (size_t)bkt * (size_t)cap;
+    if (c > 0) {
+        for (int i = tid; i < c; i += kSortThreads) keys[i] = f2key(__uint_as_float(vals[i]));
+        __syncthreads();
+        block_sort_lds<kSortThreads, kSortItems>(keys, c, cnt, scr);
+        for (int i = tid; i < c; i += kSortThreads) vals[i] = keys[i];
+        segment_aggregates<kSortThreads>(keys, c, inv_t, &seg.first[bkt], &seg.last[bkt], &seg.P[bkt],
+                                         &seg.Bx[bkt], s_red);
+    }
+    if (tid == 0) { seg.cnt[bkt] = (uint32_t)c; seg.off[bkt] = (uint32_t)((size_t)bkt * (size_t)cap); }
+    if (!last_block_ticket(&ctl->done[kDoneBucket], &s_last)) return;
+
+    // last workgroup: solve over all buckets
+    SegView sv{(int)gridDim.x, seg.first, seg.last, seg.P, seg.Bx, seg.cnt, seg.off, bucket_vals};
+    Tails tl{ctl->aL, ctl->aR, ctl->S_L, ctl->S_R, (double)ctl->m, (double)ctl->c_R, k, t, inv_t};
+    SolveOut o = segment_solve<kSortThreads, kSortItems>(sv, tl, sc, s_k, s_v, s_int);
+    if (tid == 0) {
+        if (!o.ok) atomicOr(&ctl->flags, kFlagInternal);
+        ctl->b = o.b;
+        ctl->jstar = o.jstar;
+        if (b_out) *b_out = o.b;
+        ctl->done[kDoneBucket] = 0u;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// multi-workgroup LSD radix sort (Onesweep-style: one histogram pass, then
+// one pass per 8-bit digit with decoupled look-back; Merrill & Garland,
+// "Single-pass parallel prefix scan with decoupled look-back", and Adinets
+// & Merrill, "Onesweep", 2022)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kRadixThreads) void k_radix_hist(const float* __restrict__ r, long long n,
+                                                               uint32_t* __restrict__ hist_part, uint32_t* goff,
+                                                               Ctl* ctl) {
+    __shared__ uint32_t h[4 * 256];
+    __shared__ int s_last;
+    __shared__ int s_bad;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < 1024; i += kRadixThreads) h[i] = 0u;
+    if (tid == 0) s_bad = 0;
+    __syncthreads();
+    int bad = 0;
+    const long long stride = (long long)gridDim.x * kRadixThreads;
+    for (long long i = (long long)blockIdx.x * kRadixThreads + tid; i < n; i += stride) {
+        const float v = r[i];
+        bad |= !finite_f(v);
+        const uint32_t key = f2key(v);
+        atomicAdd(&h[key & 0xFFu], 1u);
+        atomicAdd(&h[256 + ((key >> 8) & 0xFFu)], 1u);
+        atomicAdd(&h[512 + ((key >> 16) & 0xFFu)], 1u);
+        atomicAdd(&h[768 + (key >> 24)], 1u);
+    }
+    if (bad) atomicOr(&s_bad, 1);
+    __syncthreads();
+    for (int i = tid; i < 1024; i += kRadixThreads) hist_part[(size_t)blockIdx.x * kHistStride + i] = h[i];
+    if (tid == 0) hist_part[(size_t)blockIdx.x * kHistStride + 1024] = (uint32_t)s_bad;
+    if (!last_block_ticket(&ctl->done[kDoneHist], &s_last)) return;
+    // last workgroup: totals (fixed order) and exclusive digit offsets
+    for (int i = tid; i < 1024; i += kRadixThreads) {
+        uint32_t s = 0u;
+        for (unsigned b = 0; b < gridDim.x; ++b) s += hist_part[(size_t)b * kHistStride + i];
+        h[i] = s;
+    }
+    if (tid == 0) {
+        uint32_t anybad = 0u;
+        for (unsigned b = 0; b < gridDim.x; ++b) anybad |= hist_part[(size_t)b * kHistStride + 1024];
+        ctl->flags = anybad ? kFlagNonFinite : 0;
+    }
+    __syncthreads();
+    if (tid < 4) {
+        uint32_t acc = 0u;
+        for (int d = 0; d < 256; ++d) { const uint32_t x = h[tid * 256 + d]; goff[tid * 256 + d] = acc; acc += x; }
+    }
+    if (tid == 0) {
+        for (int p = 0; p < 4; ++p) ctl->tile_ctr[p] = 0u;
+        ctl->done[kDoneHist] = 0u;
+    }
+}
+
+constexpr unsigned long long kStAgg = 1ull, kStInc = 2ull;
+
+LS_DEV unsigned long long st_pack(uint32_t epoch, unsigned long long flag, uint32_t v) {
+    return ((unsigned long long)epoch << 34) | (flag << 32) | (unsigned long long)v;
+}
+
+__global__ __launch_bounds__(kRadixThreads) void k_radix_pass(const uint32_t* __restrict__ in, int in_is_float,
+                                                               uint32_t* __restrict__ out, long long n, int pass,
+                                                               unsigned long long* status, uint32_t epoch,
+                                                               const uint32_t* goff, Ctl* ctl) {
+    constexpr int NW = kRadixThreads / 64;
+    __shared__ uint32_t cnt[256 * NW];
+    __shared__ uint32_t stage[kRadixTile];
+    __shared__ uint32_t loc[256];
+    __shared__ uint32_t gbase[256];
+    __shared__ uint32_t scr[NW + 2];
+    __shared__ uint32_t s_tile;
+    const int tid = threadIdx.x, w = tid >> 6, lane = lane_id();
+    const int shift = 8 * pass;
+    if (tid == 0) s_tile = atomicAdd(&ctl->tile_ctr[pass], 1u);
+    for (int e = tid; e < 256 * NW; e += kRadixThreads) cnt[e] = 0u;
+    __syncthreads();
+    const uint32_t tile = s_tile;
+    const long long base = (long long)tile * kRadixTile;
+    uint32_t kr[kRadixItems];
+    uint32_t rk[kRadixItems];
+#pragma unroll
+    for (int i = 0; i < kRadixItems; ++i) {
+        const long long idx = base + (long long)((w * kRadixItems + i) * 64 + lane);
+        uint32_t key = 0u;
+        if (idx < n) key = in_is_float ? f2key(__uint_as_float(in[idx])) : in[idx];
+        kr[i] = key;
+    }
+    volatile uint32_t* vc = cnt;
+#pragma unroll
+    for (int i = 0; i < kRadixItems; ++i) {
+        const long long idx = base + (long long)((w * kRadixItems + i) * 64 + lane);
+        const bool valid = idx < n;
+        const unsigned long long act = ballot(valid);
+        rk[i] = 0u;
+        if (act != 0ull) {
+            const uint32_t d = (kr[i] >> shift) & 0xFFu;
+            const unsigned long long peers = match_digit8(d, act);
+            const uint32_t b0 = vc[d * NW + w];
+            rk[i] = b0 + (uint32_t)mbcnt(peers);
+            if (valid && lane == 63 - __clzll(peers)) vc[d * NW + w] = b0 + (uint32_t)popc64(peers);
+        }
+    }
+    __syncthreads();
+    // thread d: per-wave exclusive offsets and the tile total of digit d
+    const int d = tid;  // kRadixThreads == 256
+    uint32_t tot = 0u;
+#pragma unroll
+    for (int q = 0; q < NW; ++q) { const uint32_t x = cnt[d * NW + q]; cnt[d * NW + q] = tot; tot += x; }
+    uint32_t dex = block_exclusive_scan<kRadixThreads>(tot, nullptr, scr);
+    loc[d] = dex;
+    // decoupled look-back on digit d
+    unsigned long long* st = status + (size_t)tile * 256 + d;
+    if (tile == 0) {
+        __hip_atomic_store(st, st_pack(epoch, kStInc, tot), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        gbase[d] = goff[pass * 256 + d];
+    } else {
+        __hip_atomic_store(st, st_pack(epoch, kStAgg, tot), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t excl = 0u;
+        long long j = (long long)tile - 1;
+        unsigned int spins = 0u;
+        while (j >= 0) {
+            const unsigned long long s = __hip_atomic_load(status + (size_t)j * 256 + d, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t ep = (uint32_t)(s >> 34);
+            const unsigned long long fl = (s >> 32) & 3ull;
+            if (ep != epoch || fl == 0ull) {
+                // tiles are handed out in order, so the predecessor is resident and
+                // publishes within microseconds; a bounded wait turns a broken
+                // invariant into a reported error instead of a hang
+                if (++spins > (1u << 24)) { atomicOr(&ctl->flags, kFlagInternal); break; }
+                __builtin_amdgcn_s_sleep(1);
+                continue;
+            }
+            excl += (uint32_t)s;
+            if (fl == kStInc) break;
+            --j;
+        }
+        __hip_atomic_store(st, st_pack(epoch, kStInc, excl + tot), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        gbase[d] = goff[pass * 256 + d] + excl;
+    }
+    __syncthreads();
+    // local scatter into LDS in digit order, then coalesced runs to global
+#pragma unroll
+    for (int i = 0; i < kRadixItems; ++i) {
+        const long long idx = base + (long long)((w * kRadixItems + i) * 64 + lane);
+        if (idx < n) {
+            const uint32_t dd = (kr[i] >> shift) & 0xFFu;
+            stage[loc[dd] + cnt[dd * NW + w] + rk[i]] = kr[i];
+        }
+    }
+    __syncthreads();
+    const long long rem = n - base;
+    const int tcount = rem < kRadixTile ? (int)rem : kRadixTile;
+    for (int j = tid; j < tcount; j += kRadixThreads) {
+        const uint32_t key = stage[j];
+        const uint32_t dd = (key >> shift) & 0xFFu;
+        out[(size_t)gbase[dd] + (size_t)(j - (int)loc[dd])] = key;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// curve aggregates of the fully sorted scores, then the solve
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kCurveThreads) void k_curve_tiles(const uint32_t* __restrict__ keys, long long n,
+                                                                Ctl* ctl, SegArrays seg, SolveScratch sc, double k,
+                                                                double t, double inv_t, double* b_out) {
+    __shared__ float s_k[kCurveThreads];
+    __shared__ double s_v[kCurveThreads];
+    __shared__ int s_int[32];
+    __shared__ double s_red[kCurveThreads / 64];
+    __shared__ int s_last;
+    const int tile = blockIdx.x;
+    const long long base = (long long)tile * kCurveTile;
+    const long long rem = n - base;
+    const int c = rem < kCurveTile ? (int)rem : kCurveTile;
+    segment_aggregates<kCurveThreads>(keys + base, c, inv_t, &seg.first[tile], &seg.last[tile], &seg.P[tile],
+                                      &seg.Bx[tile], s_red);
+    if (threadIdx.x == 0) { seg.cnt[tile] = (uint32_t)c; seg.off[tile] = (uint32_t)base; }
+    if (!last_block_ticket(&ctl->done[kDoneCurve], &s_last)) return;
+    SegView sv{(int)gridDim.x, seg.first, seg.last, seg.P, seg.Bx, seg.cnt, seg.off, keys};
+    Tails tl{-INFINITY, INFINITY, 0.0, 0.0, (double)n, 0.0, k, t, inv_t};
+    SolveOut o = segment_solve<kCurveThreads, kRadixItems>(sv, tl, sc, s_k, s_v, s_int);
+    if (threadIdx.x == 0) {
+        double b = o.b;
+        if (ctl->flags & kFlagNonFinite) b = __longlong_as_double(0x7ff8000000000000ll);
+        else if (!o.ok) atomicOr(&ctl->flags, kFlagInternal);
+        ctl->b = b;
+        ctl->jstar = o.jstar;
+        if (b_out) *b_out = b;
+        ctl->done[kDoneCurve] = 0u;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+void launch_small_solve(const float* r, int n, double k, double t, Ctl* ctl, SolveScratch sc, double* b_out,
+                        uint32_t* keys_out, hipStream_t s) {
+    hipLaunchKernelGGL(k_small_solve, dim3(1), dim3(kSortThreads), 0, s, r, n, k, t, 1.0 / t, ctl, sc, b_out,
+                       keys_out);
+}
+
+void launch_bucket_solve(uint32_t* bucket_vals, const uint32_t* bucket_cnt, int cap, int nb, Ctl* ctl,
+                         SegArrays seg, SolveScratch sc, double k, double t, double* b_out, hipStream_t s) {
+    hipLaunchKernelGGL(k_bucket_solve, dim3(nb), dim3(kSortThreads), 0, s, bucket_vals, bucket_cnt, cap, ctl, seg,
+                       sc, k, t, 1.0 / t, b_out);
+}
+
+int radix_hist_blocks(long long n) {
+    long long b = (n + 16LL * kRadixThreads - 1) / (16LL * kRadixThreads);
+    if (b < 1) b = 1;
+    if (b > kRadixHistBlocks) b = kRadixHistBlocks;
+    return (int)b;
+}
+
+void launch_radix_sort(const float* r, long long n, uint32_t* keysA, uint32_t* keysB, uint32_t* hist_part,
+                       uint32_t* goff, unsigned long long* status, uint32_t epoch_base, Ctl* ctl, hipStream_t s) {
+    const int hb = radix_hist_blocks(n);
+    hipLaunchKernelGGL(k_radix_hist, dim3(hb), dim3(kRadixThreads), 0, s, r, n, hist_part, goff, ctl);
+    const unsigned tiles = (unsigned)((n + kRadixTile - 1) / kRadixTile);
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(r);
+    uint32_t* dst = keysA;
+    for (int p = 0; p < 4; ++p) {
+        hipLaunchKernelGGL(k_radix_pass, dim3(tiles), dim3(kRadixThreads), 0, s, src, p == 0 ? 1 : 0, dst, n, p,
+                           status, epoch_base + (uint32_t)p, goff, ctl);
+        src = dst;
+        dst = (dst == keysA) ? keysB : keysA;
+    }
+    // four passes: r -> A -> B -> A -> B; the sorted keys end in keysB
+}
+
+void launch_curve_tiles(const uint32_t* keys, long long n, Ctl* ctl, SegArrays seg, SolveScratch sc, double k,
+                        double t, double* b_out, hipStream_t s) {
+    const unsigned tiles = (unsigned)((n + kCurveTile - 1) / kCurveTile);
+    hipLaunchKernelGGL(k_curve_tiles, dim3(tiles), dim3(kCurveThreads), 0, s, keys, n, ctl, seg, sc, k, t, 1.0 / t,
+                       b_out);
+}
+
+}  // namespace lapsum

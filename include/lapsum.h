@@ -1,0 +1,162 @@
+/*
+ * lapsum.h -- C ABI of the MI355X (gfx950) Fast LapSum solver.
+ *
+ * The operator (Fast LapSum paper, gist.science summary section 2.1 "El
+ * Operador LapSum"): given scores r[n], a temperature t > 0 and a budget
+ * 0 < k < n, the threshold b is the unique root of
+ *
+ *     G(b) = sum_i F((r_i - b) / t) = k,
+ *
+ * F the Laplace CDF with scale 1 (F(x) = e^x/2 for x < 0, 1 - e^-x/2 for
+ * x >= 0).  The selection probabilities are p_i = F((r_i - b)/t), and they
+ * sum to exactly k.  The backward pass is the analytic vector-Jacobian
+ * product (same section):
+ *
+ *     grad_i = (f_i / t) (g_i - sum_j g_j f_j / sum_j f_j),
+ *     f_i = e^{-|r_i - b| / t} / 2  (the Laplace density).
+ *
+ * Two forward paths (section 2.2 "Fast LapSum: El Solucionador de GPU"):
+ * a full sort followed by one stable prefix/suffix scan, an interval search
+ * and a closed-form root; and, for large n, probabilistic bracketing (a
+ * kernel-noised sample and a binomial order statistic give a band
+ * [a_L, a_R); one streaming pass folds the scores outside it into tail sums;
+ * only the band is sorted and solved; the bracket is certified and widened
+ * when it fails, with the full sort as the fallback -- the arxivdaily
+ * abstract's "certification pass" and "full-sort fallback").
+ *
+ * Conventions for every entry point:
+ *  - Pointers to scores, p, g, grad and b are DEVICE pointers (gfx950), owned
+ *    by the caller.  The library never frees caller memory.
+ *  - All work is ordered on `stream` (a hipStream_t; NULL is the default
+ *    stream).  Scratch memory is a per-(device, stream) workspace that the
+ *    library allocates on first use and keeps until lapsum_release_workspaces.
+ *  - Argument errors are returned before anything is launched and nothing is
+ *    written.  Errors found on the device (non-finite scores) are returned
+ *    by the bracketing path, which waits for its certification verdict; the
+ *    full-sort path never blocks the host and reports them through
+ *    lapsum_stats_t (b and p are then NaN).
+ *  - n is limited to [1, 2^32 - 1].
+ *  - No exception crosses this ABI; every call is thread-safe.
+ */
+#ifndef LAPSUM_H_
+#define LAPSUM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* hipStream_t is `struct ihipStream_t*`; declared here so C callers need no HIP header. */
+typedef struct ihipStream_t* lapsum_stream_t;
+
+typedef enum {
+    LAPSUM_OK = 0,
+    LAPSUM_ERR_INVALID_ARGUMENT = 1, /* n, k, t or a pointer out of range; nothing written */
+    LAPSUM_ERR_NONFINITE_INPUT = 2,  /* a score is NaN or +-inf; b and p set to NaN */
+    LAPSUM_ERR_OUT_OF_MEMORY = 3,    /* workspace allocation failed */
+    LAPSUM_ERR_HIP = 4,              /* a HIP runtime call failed */
+    LAPSUM_ERR_INTERNAL = 5          /* a consistency check failed (reported, never silent) */
+} lapsum_status_t;
+
+typedef enum {
+    LAPSUM_PATH_AUTO = 0,           /* bracketing iff n > auto_threshold (default 10^6) */
+    LAPSUM_PATH_FULL = 1,           /* full sort */
+    LAPSUM_PATH_BRACKET = 2,        /* bracketing (with widening and full-sort fallback) */
+    LAPSUM_PATH_FORCE_FALLBACK = 3  /* bracketing pass, then the full-sort fallback regardless */
+} lapsum_path_t;
+
+/* Options of lapsum_forward_ex.  Obtain defaults from lapsum_default_options. */
+typedef struct {
+    int32_t path;           /* lapsum_path_t */
+    int32_t max_widen;      /* bracket widenings before the full-sort fallback (default 2) */
+    uint64_t seed;          /* Philox4x32-10 key of the sampler (default 0x5EED) */
+    double sample_factor;   /* sample size s = ceil(sample_factor * sqrt(n)), capped at 40960 (default 4) */
+    double delta;           /* per-side probability that the bracket misses b (default 1e-5) */
+    double margin_scale;    /* multiplies both order-statistic margins; 1 = exact binomial ranks,
+                               0 = a zero-width bracket (forces widening; for tests) */
+    int64_t auto_threshold; /* LAPSUM_PATH_AUTO uses bracketing iff n > auto_threshold (default 10^6) */
+    int32_t bucket_capacity;/* band scores per bucket, <= 16384 (default 16384; small values force
+                               the overflow fallback in tests) */
+    int32_t profile;        /* 1: time every kernel with HIP events (reported in stats) */
+} lapsum_options_t;
+
+#define LAPSUM_MAX_TIMED_KERNELS 24
+
+/* Filled by lapsum_forward_ex when stats is not NULL (the call then waits
+ * for the device before returning). */
+typedef struct {
+    int32_t status;          /* lapsum_status_t of the device-side checks */
+    int32_t path_taken;      /* 1 full sort, 2 bracketing certified, 3 bracketing -> full-sort fallback */
+    int32_t widenings;       /* bracket widenings performed */
+    int32_t certified;       /* 1 if the final bracket held (G(a_L) >= k > G(a_R)) */
+    int64_t count_below;     /* scores < a_L */
+    int64_t band_size;       /* scores in [a_L, a_R) */
+    int64_t count_above;     /* scores >= a_R */
+    int64_t sample_size;     /* s */
+    int64_t rank_lo, rank_hi;/* order-statistic ranks l, h (1-based; 0 = -inf, s+1 = +inf) */
+    int32_t buckets;         /* band buckets used */
+    int32_t n_timed;         /* entries in kernel_ms / kernel_name */
+    float a_L, a_R;          /* final bracket */
+    double g_aL, g_aR;       /* G at the bracket ends, rebuilt from the streaming pass's tail sums */
+    double sum_p;            /* sum of the written p, accumulated in fp64 on the device */
+    double b;                /* threshold */
+    double tail_S_L, tail_S_R, band_B_L, band_B_R; /* the streaming pass's fp64 sums */
+    float kernel_ms[LAPSUM_MAX_TIMED_KERNELS];     /* with options.profile: per-launch times */
+    const char* kernel_name[LAPSUM_MAX_TIMED_KERNELS];
+} lapsum_stats_t;
+
+/* Default options (see the field comments). */
+void lapsum_default_options(lapsum_options_t* opt);
+
+/* Human-readable name of a status code (static storage). */
+const char* lapsum_status_string(lapsum_status_t status);
+
+/*
+ * Forward solve (gist.science section 2.1 and 2.2).
+ *   scores : device fp32[n], read only.
+ *   n      : number of scores, 1 <= n < 2^32.
+ *   k      : budget, 0 < k < n (real valued).
+ *   t      : temperature, finite and > 0.
+ *   p_out  : device fp32[n], receives p_i = F((r_i - b)/t) (may alias nothing else).
+ *   b_out  : device fp64[1], receives b.
+ * Path: full sort for n <= 10^6, bracketing above.  Returns LAPSUM_OK,
+ * LAPSUM_ERR_INVALID_ARGUMENT, LAPSUM_ERR_NONFINITE_INPUT (bracketing path),
+ * LAPSUM_ERR_OUT_OF_MEMORY or LAPSUM_ERR_HIP.
+ */
+lapsum_status_t lapsum_forward(const float* scores, int64_t n, double k, float t,
+                               float* p_out, double* b_out, lapsum_stream_t stream);
+
+/* lapsum_forward with explicit options (NULL = defaults) and optional host
+ * stats (NULL = none; non-NULL makes the call wait for the device). */
+lapsum_status_t lapsum_forward_ex(const float* scores, int64_t n, double k, float t,
+                                  float* p_out, double* b_out, const lapsum_options_t* opt,
+                                  lapsum_stats_t* stats, lapsum_stream_t stream);
+
+/*
+ * Analytic VJP (gist.science section 2.1): grad_i = (f_i/t)(g_i - c),
+ * c = sum g f / sum f, f_i = e^{-|r_i - b|/t}/2, recomputed from (scores, b).
+ *   scores  : device fp32[n], the forward's scores.
+ *   p       : device fp32[n] or NULL; accepted for symmetry and not read
+ *             (f from an fp32 p near 1 would lose the accuracy f needs).
+ *   g       : device fp32[n], upstream gradient dL/dp.
+ *   t       : the forward's temperature.
+ *   b       : device fp64[1], the forward's threshold.
+ *   grad_out: device fp32[n], receives dL/dr.
+ * Never blocks the host.
+ */
+lapsum_status_t lapsum_vjp(const float* scores, const float* p, const float* g, int64_t n, float t,
+                           const double* b, float* grad_out, lapsum_stream_t stream);
+
+/* Free every cached workspace (waits for their streams). */
+void lapsum_release_workspaces(void);
+
+/* Bytes of workspace a forward of size n needs (informational). */
+size_t lapsum_workspace_bytes(int64_t n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LAPSUM_H_ */

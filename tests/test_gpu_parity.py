@@ -1,0 +1,226 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU fp64 oracle
+on the same seeded inputs.  Sizes here let the oracle finish in seconds while
+spanning several tiles, buckets and a ragged tail; the full-size workloads are
+in test_gpu_fullsize.py."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_helpers import check_forward, check_vjp, t32, to_dev
+
+pytestmark = pytest.mark.gpu
+
+L = pytest.importorskip("differentiable_exact_budget_amd")
+
+
+def run(r, k, t, g=None, **opts):
+    rd = to_dev(r)
+    o = L.default_options(**opts) if opts else None
+    p, b, st = L.forward(rd, k, t, options=o, stats=True)
+    grad = None
+    if g is not None:
+        grad = L.vjp(rd, to_dev(g), t, b).cpu().numpy()
+    torch.cuda.synchronize()
+    return p.cpu().numpy(), float(b.cpu().item()), st, grad
+
+
+# ---------------------------------------------------------------------------
+# full-sort path
+# ---------------------------------------------------------------------------
+def test_c1_small_solve(oracle_mod):
+    r, g, cfg = workloads.config_inputs("C1")
+    p, b, st, grad = run(r, cfg.k, cfg.t, g)
+    assert st["path_taken"] == 1 and st["status"] == 0
+    b_ref = check_forward(oracle_mod, r, cfg.k, cfg.t, p, b, label="C1")
+    check_vjp(oracle_mod, r, g, cfg.t, b_ref, grad, label="C1")
+
+
+@pytest.mark.parametrize("n,k,t", [(1, 0.3, 0.5), (2, 1.0, 0.1), (3, 2.5, 1.0), (17, 4.0, 0.05),
+                                   (1000, 999.5, 0.01), (16384, 100.0, 0.01), (5, 0.001, 0.2)])
+def test_small_solve_edges(oracle_mod, n, k, t):
+    rng = np.random.default_rng(n)
+    r = rng.standard_normal(n).astype(np.float32)
+    g = rng.standard_normal(n).astype(np.float32)
+    p, b, st, grad = run(r, k, t, g)
+    b_ref = check_forward(oracle_mod, r, k, t, p, b, label=f"n={n}")
+    check_vjp(oracle_mod, r, g, t, b_ref, grad, label=f"n={n}")
+
+
+def test_small_solve_ties_and_zero_temperature(oracle_mod):
+    r = np.array([0.5, 0.5, 0.5, -1.0, 2.0, 2.0, 0.0, -0.0], dtype=np.float32)
+    for k in (0.5, 1.0, 2.0, 3.0, 4.5, 7.9):
+        for t in (0.01, 0.3, 3.0):
+            p, b, st, _ = run(r, k, t)
+            check_forward(oracle_mod, r, k, t, p, b, label=f"ties k={k} t={t}")
+    r = np.random.default_rng(3).permutation(np.arange(20, dtype=np.float32))
+    p, b, st, _ = run(r, 5.0, 0.01)
+    assert abs(b - 14.5) <= 1e-6
+    assert np.max(np.abs(p - (r >= 15))) <= 1e-6
+
+
+@pytest.mark.parametrize("n", [1, 2, 17, 4096, 16384, 16385, 65537, 300_001])
+def test_sort_bit_exact(oracle_mod, n):
+    rng = np.random.default_rng(100 + n)
+    r = rng.standard_normal(n).astype(np.float32)
+    if n > 8:
+        r[::7] = r[1]            # ties
+        r[3] = -0.0
+        r[5] = 0.0
+        r[6] = np.float32(-1e-40)  # subnormal
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    rc = L.lib().lapsum_test_sort(to_dev(r).data_ptr(), n, out.data_ptr(), None)
+    assert rc == 0
+    got = out.cpu().numpy()
+    ref = oracle_mod.sort_keys(r)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("n,dist", [(16385, "normal"), (200_000, "student_t3"), (1_000_000, "normal")])
+def test_full_sort_path(oracle_mod, n, dist):
+    r = workloads.scores(dist, n, 7 + n)
+    g = workloads.upstream(n, 8 + n)
+    k, t = 200.0, 0.05
+    p, b, st, grad = run(r, k, t, g, path=L.PATH_FULL)
+    assert st["path_taken"] == 1 and st["status"] == 0
+    b_ref = check_forward(oracle_mod, r, k, t, p, b, label=f"full n={n}")
+    check_vjp(oracle_mod, r, g, t, b_ref, grad, label=f"full n={n}")
+
+
+def test_c2_full_path(oracle_mod):
+    r, g, cfg = workloads.config_inputs("C2")
+    p, b, st, grad = run(r, cfg.k, cfg.t, g)
+    assert st["path_taken"] == 1
+    b_ref = check_forward(oracle_mod, r, cfg.k, cfg.t, p, b, label="C2")
+    check_vjp(oracle_mod, r, g, cfg.t, b_ref, grad, label="C2")
+
+
+# ---------------------------------------------------------------------------
+# bracketing stages
+# ---------------------------------------------------------------------------
+def test_sample_matches_oracle(oracle_mod):
+    r, _, _ = workloads.config_inputs("C3", 100_000)
+    s, t, seed = 12650, 0.01, 0x5EED
+    x = torch.empty(s, dtype=torch.float32, device="cuda")
+    idx = torch.empty(s, dtype=torch.int64, device="cuda")
+    rc = L.lib().lapsum_test_sample(to_dev(r).data_ptr(), r.size, t, seed, s, x.data_ptr(), idx.data_ptr(), None)
+    assert rc == 0
+    oi, ox = oracle_mod.sample(r, t32(t), seed, s)
+    assert np.array_equal(idx.cpu().numpy(), oi), "Philox index stream must be bit-exact"
+    gx = x.cpu().numpy()
+    ulps = np.abs(gx.view(np.int32).astype(np.int64) - ox.view(np.int32).astype(np.int64))
+    assert ulps.max() <= 1, f"noised sample differs by {ulps.max()} ulp"
+
+
+def test_select_order_statistics():
+    rng = np.random.default_rng(5)
+    for s in (1, 2, 100, 12650, 40000):
+        x = rng.standard_normal(s).astype(np.float32)
+        xs = np.sort(x)
+        for l, h in ((1, s), (0, s + 1), (max(1, s // 3), max(1, (2 * s) // 3)), (s, s)):
+            aL = L._binding.ctypes.c_float()
+            aR = L._binding.ctypes.c_float()
+            nb = L._binding.ctypes.c_int32()
+            rc = L.lib().lapsum_test_select(to_dev(x).data_ptr(), s, l, h, L._binding.ctypes.byref(aL),
+                                            L._binding.ctypes.byref(aR), L._binding.ctypes.byref(nb), None)
+            assert rc == 0
+            eL = -np.inf if l < 1 else xs[l - 1]
+            eR = np.inf if h > s else xs[h - 1]
+            assert aL.value == eL and aR.value == eR, (s, l, h, aL.value, eL, aR.value, eR)
+            assert 1 <= nb.value <= 256
+
+
+@pytest.mark.parametrize("aL,aR", [(1.0, 2.5), (-np.inf, -1.0), (2.0, np.inf), (0.3, 0.3001), (0.5, 0.5)])
+def test_filter_band_bit_exact(oracle_mod, aL, aR):
+    r, _, _ = workloads.config_inputs("C3", 400_003)
+    t = 0.01
+    ctypes = L._binding.ctypes
+    counts = (ctypes.c_int64 * 3)()
+    sums = (ctypes.c_double * 4)()
+    msize = ctypes.c_int64()
+    cap = 400_003
+    band = torch.empty(cap, dtype=torch.float32, device="cuda")
+    rc = L.lib().lapsum_test_filter(to_dev(r).data_ptr(), r.size, t, float(np.float32(aL)), float(np.float32(aR)),
+                                    counts, sums, band.data_ptr(), cap, ctypes.byref(msize), None)
+    assert rc == 0
+    ref = oracle_mod.bracket(r, t32(t), float(np.float32(aL)), float(np.float32(aR)))
+    assert (counts[0], counts[1], counts[2]) == (ref["below"], ref["band"], ref["above"])
+    if msize.value >= 0:
+        got = band[: msize.value].cpu().numpy()
+        assert np.array_equal(got.astype(np.float64), ref["band_values"]), "sorted band must be bit-exact"
+    for i, key in enumerate(("S_L", "S_R", "B_L", "B_R")):
+        assert abs(sums[i] - ref[key]) <= 1e-6 * max(ref[key], 1e-300) + 1e-300, (key, sums[i], ref[key])
+
+
+# ---------------------------------------------------------------------------
+# bracketing end to end (scaled-down configurations)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name,n", [("C3", 2_000_000), ("C4", 3_000_000), ("C5", 2_000_000)])
+def test_bracket_path(oracle_mod, name, n):
+    cfg = workloads.CONFIGS[name]
+    r = workloads.scores(cfg.dist, n, 1000 + cfg.number, k=cfg.k * n / cfg.n)
+    g = workloads.upstream(n, 2000 + cfg.number)
+    k = cfg.k * n / cfg.n
+    p, b, st, grad = run(r, k, cfg.t, g)
+    assert st["status"] == 0
+    assert st["path_taken"] in (2, 3)
+    b_ref = check_forward(oracle_mod, r, k, cfg.t, p, b, label=name)
+    check_vjp(oracle_mod, r, g, cfg.t, b_ref, grad, label=name)
+    if st["path_taken"] == 2:
+        # certification quantities agree with the oracle's direct sums
+        ref = oracle_mod.bracket(r, t32(cfg.t), st["a_L"], st["a_R"], want_band=False)
+        assert (st["count_below"], st["band_size"], st["count_above"]) == (ref["below"], ref["band"], ref["above"])
+        if np.isfinite(st["a_L"]):
+            assert abs(st["g_aL"] - ref["G_aL"]) <= 1e-6 * ref["G_aL"]
+        if np.isfinite(st["a_R"]):
+            assert abs(st["g_aR"] - ref["G_aR"]) <= 1e-6 * max(ref["G_aR"], 1.0)
+        assert st["g_aL"] >= k > st["g_aR"]
+
+
+def test_forced_fallback_and_widening(oracle_mod):
+    r, g, cfg = workloads.config_inputs("C5", 1_500_000)
+    k = 15000.0
+    p, b, st, grad = run(r, k, cfg.t, g, path=L.PATH_FORCE_FALLBACK)
+    assert st["path_taken"] == 3
+    b_ref = check_forward(oracle_mod, r, k, cfg.t, p, b, label="forced fallback")
+    check_vjp(oracle_mod, r, g, cfg.t, b_ref, grad, label="forced fallback")
+    # zero margins: the first bracket has zero width and must be widened
+    p, b, st, _ = run(r, k, cfg.t, path=L.PATH_BRACKET, margin_scale=0.0)
+    assert st["widenings"] >= 1
+    check_forward(oracle_mod, r, k, cfg.t, p, b, b_ref=b_ref, label="widened")
+    # tiny buckets: overflow goes to the full sort
+    p, b, st, _ = run(r, k, cfg.t, path=L.PATH_BRACKET, bucket_capacity=4)
+    assert st["path_taken"] == 3
+    check_forward(oracle_mod, r, k, cfg.t, p, b, b_ref=b_ref, label="overflow")
+
+
+def test_deterministic(oracle_mod):
+    r, _, cfg = workloads.config_inputs("C3", 2_000_000)
+    p1, b1, _, _ = run(r, 2000.0, cfg.t)
+    p2, b2, _, _ = run(r, 2000.0, cfg.t)
+    assert b1 == b2 and np.array_equal(p1.view(np.uint32), p2.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# errors
+# ---------------------------------------------------------------------------
+def test_invalid_arguments():
+    r = torch.zeros(8, device="cuda")
+    for k, t in ((0.0, 1.0), (8.0, 1.0), (1.0, 0.0), (1.0, float("nan")), (float("inf"), 1.0)):
+        with pytest.raises(L.LapsumError) as e:
+            L.forward(r, k, t)
+        assert e.value.code == 1
+
+
+@pytest.mark.parametrize("n,bad", [(1000, np.nan), (2_000_000, np.nan), (2_000_000, np.inf), (50_000, -np.inf)])
+def test_nonfinite_scores(n, bad):
+    r = workloads.scores("normal", n, 3)
+    r[n // 2] = bad
+    rd = to_dev(r)
+    if n > 1_000_000:
+        with pytest.raises(L.LapsumError) as e:
+            L.forward(rd, 10.0, 0.1)
+        assert e.value.code == 2
+    else:
+        p, b, st = L.forward(rd, 10.0, 0.1, stats=True)
+        assert st["status"] == 2 and np.isnan(b.item())
