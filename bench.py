@@ -1,0 +1,210 @@
+"""Benchmark of the Fast LapSum solver on one MI355X.
+
+A step is one forward solve (threshold b and p) plus one VJP over one batch
+of resident synthetic scores.  Default workload: n = 10^8 fp32 scores drawn
+per element from U(0,1) w.p. 0.9 else N(2, sd 0.5), k = 10^5, t = 0.01, on
+the bracketing path with certification (the largest configuration, 400 MB).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C4]
+
+Prints ONE JSON line.  Per-kernel durations come from HIP events recorded on
+the library's stream in a second timed loop (options.profile); the roofline
+entry uses the dominant kernel's algorithmic bytes per launch.  The CPU
+baseline times the fp64 oracle on a bounded prefix of the same workload.
+"""
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "median ms and scores/s per forward+VJP solve at n=1e6/1e7/1e8; % peak HBM GB/s"
+PEAK_HBM_GBPS = 8000.0
+
+# algorithmic bytes per score moved by each kernel (reads + writes of n-sized arrays)
+ALG_BYTES = {
+    "filter": 4,        # read r
+    "probs": 8,         # read r, write p
+    "vjp_reduce": 8,    # read r, g
+    "vjp_apply": 12,    # read r, g, write grad
+    "radix_sort": 36,   # histogram read 4 + four digit passes (read 4 + write 4)
+    "curve_solve": 4,   # read the sorted keys
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="C4")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=10_000_000, help="oracle prefix size for the CPU baseline")
+    return ap.parse_args()
+
+
+def describe(cfg):
+    dist = {"normal": "N(0,1)", "student_t3": "Student-t(3)",
+            "mixture": "0.9*U(0,1)+0.1*N(2,0.5)", "adversarial": "N(0,1) + 1% tied at the (1-k/n) quantile"}[cfg.dist]
+    path = {"full": "full sort", "bracket": "bracketing+certification", "fallback": "forced full-sort fallback"}
+    return f"{cfg.name}: n={cfg.n} fp32 {dist}, k={cfg.k:g}, t={cfg.t:g}, {path[cfg.path]}, forward+VJP"
+
+
+def time_steps(L, torch, rd, gd, k, t, steps, warmup, options=None):
+    """Time `steps` forward+VJP steps; returns (total_s, per-step ms list)."""
+    p = torch.empty_like(rd)
+    b = torch.empty(1, dtype=torch.float64, device=rd.device)
+    grad = torch.empty_like(rd)
+    for _ in range(warmup):
+        L.forward(rd, k, t, options=options, p_out=p, b_out=b)
+        L.vjp(rd, gd, t, b, grad_out=grad)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        L.forward(rd, k, t, options=options, p_out=p, b_out=b)
+        L.vjp(rd, gd, t, b, grad_out=grad)
+        ends[i].record()
+    torch.cuda.synchronize()
+    total = time.perf_counter() - t0
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return total, per
+
+
+def kernel_profile(L, torch, rd, gd, k, t, steps):
+    """Per-kernel durations (ms) from HIP events recorded by the library."""
+    opt = L.default_options(profile=1)
+    acc = {}
+    info = None
+    p = torch.empty_like(rd)
+    b = torch.empty(1, dtype=torch.float64, device=rd.device)
+    grad = torch.empty_like(rd)
+    for _ in range(steps):
+        _, _, st = L.forward(rd, k, t, options=opt, stats=True, p_out=p, b_out=b)
+        _, sv = L.vjp(rd, gd, t, b, grad_out=grad, options=opt, stats=True)
+        info = st
+        for name, ms in st["kernels"] + sv["kernels"]:
+            acc.setdefault(name, []).append(ms)
+    return {n: statistics.mean(v) for n, v in acc.items()}, info
+
+
+def cpu_baseline(cfg, r, g, n_sample):
+    import numpy as np
+    import oracle
+    ns = min(n_sample, r.size)
+    rs = np.ascontiguousarray(r[:ns]).astype(np.float64)
+    gs = np.ascontiguousarray(g[:ns]).astype(np.float64)
+    ks = max(cfg.k * ns / r.size, 1.0)
+    t = float(np.float32(cfg.t))
+    oracle._load()
+    t0 = time.perf_counter()
+    b, _ = oracle.solve(rs, ks, t)
+    oracle.probs(rs, t, b)
+    oracle.vjp(rs, gs, t, b)
+    dt = time.perf_counter() - t0
+    return {"value": ns / dt, "unit": "scores/s", "cores": oracle.get_threads(), "kind": "oracle",
+            "sample": f"first {ns} scores of the {cfg.name} input (k scaled to {ks:g}), fp64 bisection solve + p + "
+                      f"VJP, {dt:.2f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 (no multi-GPU path)"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import differentiable_exact_budget_amd as L
+    import workloads
+
+    cfg = workloads.CONFIGS[args.config]
+    r, g, _ = workloads.config_inputs(cfg.name)
+    dev = torch.device("cuda:0")
+    rd = torch.from_numpy(r).to(dev)
+    gd = torch.from_numpy(g).to(dev)
+    opts = L.default_options(path=L.PATH_FORCE_FALLBACK) if cfg.path == "fallback" else None
+
+    total, per = time_steps(L, torch, rd, gd, cfg.k, cfg.t, args.steps, args.warmup, opts)
+    ms_per_step = total * 1000.0 / args.steps
+    med = statistics.median(per)
+    kern, info = kernel_profile(L, torch, rd, gd, cfg.k, cfg.t, max(5, min(args.steps, 20)))
+
+    # roofline of the dominant kernel (largest average duration)
+    dom = max(kern, key=kern.get)
+    alg = ALG_BYTES.get(dom, 0) * cfg.n
+    achieved = alg / (kern[dom] * 1e-3) / 1e9 if kern[dom] > 0 else 0.0
+    roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+            "alg_bytes_per_launch": alg, "avg_ms": round(kern[dom], 5)}
+    kernels = {}
+    for name, ms in sorted(kern.items(), key=lambda kv: -kv[1]):
+        e = {"avg_ms": round(ms, 5)}
+        if name in ALG_BYTES and ms > 0:
+            gbps = ALG_BYTES[name] * cfg.n / (ms * 1e-3) / 1e9
+            e["alg_GBps"] = round(gbps, 1)
+            e["frac_peak"] = round(gbps / PEAK_HBM_GBPS, 4)
+        kernels[name] = e
+    # whole-step byte roofline (bracketing path: 32 B per score)
+    step_bytes = 32 * cfg.n if cfg.path == "bracket" else None
+
+    out = {
+        "metric": METRIC,
+        "value": cfg.n * args.steps / total,
+        "unit": "scores/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "median_ms": med,
+        "p10_ms": float(np.percentile(per, 10)),
+        "p90_ms": float(np.percentile(per, 90)),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic (seeded numpy PCG64)",
+        "config": {"workload": describe(cfg), "n": cfg.n, "k": cfg.k, "t": cfg.t, "parallelism": "single GPU"},
+        "roofline": roof,
+        "kernels": kernels,
+        "path": {"path_taken": info["path_taken"], "certified": info["certified"], "widenings": info["widenings"],
+                 "band_size": info["band_size"], "buckets": info["buckets"], "sample_size": info["sample_size"]},
+    }
+    if step_bytes:
+        out["step_roofline"] = {"alg_bytes": step_bytes, "ideal_ms_at_peak": step_bytes / PEAK_HBM_GBPS / 1e6,
+                                "frac_of_median": round(step_bytes / PEAK_HBM_GBPS / 1e6 / med, 4)}
+
+    if not args.no_other_configs:
+        others = {}
+        for name in ("C1", "C2", "C3", "C5"):
+            c2 = workloads.CONFIGS[name]
+            r2, g2, _ = workloads.config_inputs(name)
+            a = torch.from_numpy(r2).to(dev)
+            b2 = torch.from_numpy(g2).to(dev)
+            tot2, per2 = time_steps(L, torch, a, b2, c2.k, c2.t, 20, 3)
+            others[name] = {"median_ms": round(statistics.median(per2), 5),
+                            "scores_per_s": c2.n / (statistics.median(per2) * 1e-3)}
+            if name == "C5":
+                o5 = L.default_options(path=L.PATH_FORCE_FALLBACK)
+                tot3, per3 = time_steps(L, torch, a, b2, c2.k, c2.t, 10, 2, o5)
+                others["C5_forced_fallback"] = {"median_ms": round(statistics.median(per3), 5),
+                                                "scores_per_s": c2.n / (statistics.median(per3) * 1e-3)}
+            del a, b2
+        out["other_configs"] = others
+
+    out["pages_context_ms"] = {"forward_only_1e8": 5.23, "certified_median_1e8": 7.24,
+                               "note": "the pages' forward solve times on unnamed hardware; not this metric"}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, r, g, args.cpu_sample)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

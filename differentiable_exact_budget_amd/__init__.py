@@ -58,8 +58,10 @@ def forward(r: torch.Tensor, k: float, t: float, *, options: Options = None, sta
     return p, b
 
 
-def vjp(r: torch.Tensor, g: torch.Tensor, t: float, b: torch.Tensor, *, grad_out: torch.Tensor = None):
-    """grad_i = (f_i/t)(g_i - sum g f / sum f), f_i = e^{-|r_i - b|/t}/2."""
+def vjp(r: torch.Tensor, g: torch.Tensor, t: float, b: torch.Tensor, *, grad_out: torch.Tensor = None,
+        options: Options = None, stats: bool = False):
+    """grad_i = (f_i/t)(g_i - sum g f / sum f), f_i = e^{-|r_i - b|/t}/2.
+    Returns grad, or (grad, stats_dict) when stats=True (which waits)."""
     _check_scores(r, "r")
     _check_scores(g, "g")
     if g.numel() != r.numel():
@@ -69,10 +71,14 @@ def vjp(r: torch.Tensor, g: torch.Tensor, t: float, b: torch.Tensor, *, grad_out
     with torch.cuda.device(r.device):
         out = grad_out if grad_out is not None else torch.empty_like(r)
         _check_scores(out, "grad_out")
-        rc = lib().lapsum_vjp(r.data_ptr(), None, g.data_ptr(), r.numel(), float(t), b.data_ptr(), out.data_ptr(),
-                              _stream_ptr(r.device))
+        st = Stats() if stats else None
+        rc = lib().lapsum_vjp_ex(r.data_ptr(), None, g.data_ptr(), r.numel(), float(t), b.data_ptr(), out.data_ptr(),
+                                 ctypes.byref(options) if options is not None else None,
+                                 ctypes.byref(st) if st is not None else None, _stream_ptr(r.device))
     if rc != 0:
         raise LapsumError(rc, "lapsum_vjp")
+    if stats:
+        return out, st.as_dict()
     return out
 
 

@@ -70,6 +70,8 @@ class Stats(ctypes.Structure):
         ("tail_S_R", ctypes.c_double),
         ("band_B_L", ctypes.c_double),
         ("band_B_R", ctypes.c_double),
+        ("vjp_c", ctypes.c_double),
+        ("vjp_sum_f", ctypes.c_double),
         ("kernel_ms", ctypes.c_float * MAX_TIMED),
         ("kernel_name", ctypes.c_char_p * MAX_TIMED),
     ]
@@ -84,6 +86,7 @@ _lib = None
 
 EXPORTED = [
     "lapsum_default_options", "lapsum_status_string", "lapsum_forward", "lapsum_forward_ex", "lapsum_vjp",
+    "lapsum_vjp_ex",
     "lapsum_release_workspaces", "lapsum_workspace_bytes",
     "lapsum_test_sort", "lapsum_test_sample", "lapsum_test_select", "lapsum_test_filter",
 ]
@@ -109,6 +112,8 @@ def lib():
     L.lapsum_forward_ex.restype = ctypes.c_int
     L.lapsum_vjp.argtypes = [vp, vp, vp, i64, f32, vp, vp, vp]
     L.lapsum_vjp.restype = ctypes.c_int
+    L.lapsum_vjp_ex.argtypes = [vp, vp, vp, i64, f32, vp, vp, ctypes.POINTER(Options), ctypes.POINTER(Stats), vp]
+    L.lapsum_vjp_ex.restype = ctypes.c_int
     L.lapsum_release_workspaces.argtypes = []
     L.lapsum_release_workspaces.restype = None
     L.lapsum_workspace_bytes.argtypes = [i64]

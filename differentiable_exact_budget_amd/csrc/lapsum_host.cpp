@@ -572,8 +572,9 @@ lapsum_status_t lapsum_forward(const float* scores, int64_t n, double k, float t
     return lapsum_forward_ex(scores, n, k, t, p_out, b_out, nullptr, nullptr, stream);
 }
 
-lapsum_status_t lapsum_vjp(const float* scores, const float* /*p*/, const float* g, int64_t n, float t,
-                           const double* b, float* grad_out, lapsum_stream_t stream) {
+lapsum_status_t lapsum_vjp_ex(const float* scores, const float* /*p*/, const float* g, int64_t n, float t,
+                              const double* b, float* grad_out, const lapsum_options_t* opt,
+                              lapsum_stats_t* stats, lapsum_stream_t stream) {
     if (!scores || !g || !b || !grad_out) return LAPSUM_ERR_INVALID_ARGUMENT;
     if (n < 1 || n > 0xFFFFFFFFll) return LAPSUM_ERR_INVALID_ARGUMENT;
     if (!(t > 0.0f) || !std::isfinite(t)) return LAPSUM_ERR_INVALID_ARGUMENT;
@@ -582,11 +583,39 @@ lapsum_status_t lapsum_vjp(const float* scores, const float* /*p*/, const float*
         Workspace* w = nullptr;
         lapsum_status_t gs = get_ws(st, 0, &w);
         if (gs != LAPSUM_OK) return gs;
-        launch_vjp(scores, g, n, (double)t, b, grad_out, w->ctl, w->part, st, nullptr);
-        return hip_ok(hipGetLastError());
+        const bool prof = opt && opt->profile;
+        if (stats) std::memset(stats, 0, sizeof(*stats));
+        if (prof) {
+            while (w->events.size() < 3) { hipEvent_t e; (void)hipEventCreate(&e); w->events.push_back(e); }
+            (void)hipEventRecord(w->events[0], st);
+        }
+        launch_vjp(scores, g, n, (double)t, b, grad_out, w->ctl, w->part, st, prof ? &w->events[1] : nullptr);
+        if (prof) (void)hipEventRecord(w->events[2], st);
+        if (hipGetLastError() != hipSuccess) return LAPSUM_ERR_HIP;
+        if (stats) {
+            if (hipStreamSynchronize(st) != hipSuccess) return LAPSUM_ERR_HIP;
+            Ctl c;
+            if (hipMemcpy(&c, w->ctl, sizeof(Ctl), hipMemcpyDeviceToHost) != hipSuccess) return LAPSUM_ERR_HIP;
+            stats->vjp_c = c.c;
+            stats->vjp_sum_f = c.sumf;
+            if (prof) {
+                float a = 0.0f, bms = 0.0f;
+                (void)hipEventElapsedTime(&a, w->events[0], w->events[1]);
+                (void)hipEventElapsedTime(&bms, w->events[1], w->events[2]);
+                stats->kernel_ms[0] = a; stats->kernel_name[0] = "vjp_reduce";
+                stats->kernel_ms[1] = bms; stats->kernel_name[1] = "vjp_apply";
+                stats->n_timed = 2;
+            }
+        }
+        return LAPSUM_OK;
     } catch (...) {
         return LAPSUM_ERR_INTERNAL;
     }
+}
+
+lapsum_status_t lapsum_vjp(const float* scores, const float* p, const float* g, int64_t n, float t, const double* b,
+                           float* grad_out, lapsum_stream_t stream) {
+    return lapsum_vjp_ex(scores, p, g, n, t, b, grad_out, nullptr, nullptr, stream);
 }
 
 void lapsum_release_workspaces(void) {

@@ -103,6 +103,7 @@ typedef struct {
     double sum_p;            /* sum of the written p, accumulated in fp64 on the device */
     double b;                /* threshold */
     double tail_S_L, tail_S_R, band_B_L, band_B_R; /* the streaming pass's fp64 sums */
+    double vjp_c, vjp_sum_f;  /* lapsum_vjp_ex: c = sum g f / sum f and sum f */
     float kernel_ms[LAPSUM_MAX_TIMED_KERNELS];     /* with options.profile: per-launch times */
     const char* kernel_name[LAPSUM_MAX_TIMED_KERNELS];
 } lapsum_stats_t;
@@ -148,6 +149,12 @@ lapsum_status_t lapsum_forward_ex(const float* scores, int64_t n, double k, floa
  */
 lapsum_status_t lapsum_vjp(const float* scores, const float* p, const float* g, int64_t n, float t,
                            const double* b, float* grad_out, lapsum_stream_t stream);
+
+/* lapsum_vjp with options (only `profile` is read) and optional host stats
+ * (kernel times, vjp_c, vjp_sum_f; non-NULL makes the call wait). */
+lapsum_status_t lapsum_vjp_ex(const float* scores, const float* p, const float* g, int64_t n, float t,
+                              const double* b, float* grad_out, const lapsum_options_t* opt,
+                              lapsum_stats_t* stats, lapsum_stream_t stream);
 
 /* Free every cached workspace (waits for their streams). */
 void lapsum_release_workspaces(void);
