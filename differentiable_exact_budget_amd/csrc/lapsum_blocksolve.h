@@ -180,6 +180,13 @@ struct SegView {
     const uint32_t* cnt;   // scores in the segment (0 = empty)
     const uint32_t* off;   // offset of the segment's keys in `keys`
     const uint32_t* keys;  // sorted order-preserving keys (global or LDS)
+    // optional local curves (indexed like keys): with ref = the segment's
+    // first score and u_j = e^{(v_j - ref)/t}, eU_j = sum_{i<=j} u_i and
+    // eW_j = sum_{i>j} 1/u_i inside the segment; `wide` marks segments whose
+    // span exceeds 600 t (no local curve: computed in the solve instead)
+    const double* eU;
+    const double* eW;
+    const uint8_t* wide;
 };
 
 struct Tails {
@@ -209,190 +216,291 @@ LS_DEV double log_root(double lnA, double lnB, double D) {
     return 0.5 * (lnA - lnB);
 }
 
+// wave-level exclusive scans of curve carries (wave 0 of the workgroup)
+LS_DEV void wave_scan_fwd_excl(float& k, double& v, double inv_t) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const float lk = __shfl_up(k, o, 64);
+        const double lv = __shfl_up(v, o, 64);
+        if (lane >= o) fwd_combine(lk, lv, k, v, inv_t);
+    }
+    float ek = __shfl_up(k, 1, 64);
+    double ev = __shfl_up(v, 1, 64);
+    if (lane == 0) { ek = -INFINITY; ev = 0.0; }
+    k = ek; v = ev;
+}
+LS_DEV void wave_scan_bwd_excl(float& k, double& v, double inv_t) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const float rk = __shfl_down(k, o, 64);
+        const double rv = __shfl_down(v, o, 64);
+        if (lane + o < 64) bwd_combine(k, v, rk, rv, inv_t);
+    }
+    float ek = __shfl_down(k, 1, 64);
+    double ev = __shfl_down(v, 1, 64);
+    if (lane == 63) { ek = INFINITY; ev = 0.0; }
+    k = ek; v = ev;
+}
+
 // Runs on all NT threads of one workgroup; result valid in thread 0.
+// Memory round trips are kept to a handful: each lane of wave 0 fetches its
+// segments' aggregates in one batch, the root segment's scores are read
+// once, and the root is taken by the thread that owns j* with its
+// neighbour's values exchanged through LDS.
 template <int NT, int EMAX>
 __device__ SolveOut segment_solve(const SegView sv, const Tails tl, const SolveScratch sc,
                                   float* s_k, double* s_v, int* s_int) {
+    constexpr int SEGB = 8;  // segments fetched per batch by each lane of wave 0
     const int tid = threadIdx.x;
     const double inv_t = tl.inv_t;
     const int nseg = sv.nseg;
-    const int per = (nseg + NT - 1) / NT;
-    const int s0 = min(nseg, tid * per), s1 = min(nseg, s0 + per);
+    __shared__ double s_root[4];
+    __shared__ int s_owner;
 
-    // ---- phase 1: forward carries across segments, and segment ranks ----
-    float ak = -INFINITY; double av = 0.0; uint32_t rc = 0u;
-    for (int s = s0; s < s1; ++s) {
-        const uint32_t c = sv.cnt[s];
-        if (c) { float lk = ak; double lv = av; ak = sv.last[s]; av = sv.P[s]; fwd_combine(lk, lv, ak, av, inv_t); }
-        rc += c;
-    }
-    uint32_t rbase = block_exclusive_scan<NT>(rc, nullptr, (uint32_t*)s_int);
-    block_scan_fwd_excl<NT>(ak, av, s_k, s_v, inv_t);
-    {   // the lower tail precedes everything
-        float ck = ak; double cv = av;
-        float tk = -INFINITY; double tv = 0.0;
-        if (tl.S_L > 0.0 && tl.aL > -INFINITY) { tk = tl.aL; tv = tl.S_L; }
-        ak = tk; av = tv;
-        fwd_combine(ak, av, ck, cv, inv_t);  // (tail) then (threads before)
-        ak = ck; av = cv;
-    }
-    for (int s = s0; s < s1; ++s) {
-        const uint32_t c = sv.cnt[s];
-        sc.pk[s] = ak; sc.pv[s] = av; sc.rank[s] = rbase;
-        rbase += c;
-        if (c) { float lk = ak; double lv = av; ak = sv.last[s]; av = sv.P[s]; fwd_combine(lk, lv, ak, av, inv_t); }
-    }
-    // ---- phase 2: backward carries across segments ----
-    float bk = INFINITY; double bvv = 0.0;
-    for (int s = s1 - 1; s >= s0; --s) {
-        if (sv.cnt[s]) { float k2 = sv.first[s]; double v2 = 1.0 + sv.Bx[s]; bwd_combine(k2, v2, bk, bvv, inv_t); bk = k2; bvv = v2; }
-    }
-    block_scan_bwd_excl<NT>(bk, bvv, s_k, s_v, inv_t);
-    {   // the upper tail follows everything
+    // ---- phases 1-2 (wave 0): carries before/after every segment, segment ranks ----
+    if (tid < 64) {
+        const int lane = tid;
+        const int per = (nseg + 63) / 64;
+        const int s0 = min(nseg, lane * per), s1 = min(nseg, s0 + per);
+        float ak = -INFINITY; double av = 0.0; uint32_t rc = 0u;
+        for (int sb = s0; sb < s1; sb += SEGB) {
+            uint32_t c[SEGB]; float lst[SEGB]; double pp[SEGB];
+#pragma unroll
+            for (int q = 0; q < SEGB; ++q) {
+                const int s = sb + q;
+                c[q] = s < s1 ? sv.cnt[s] : 0u;
+                lst[q] = s < s1 ? sv.last[s] : 0.0f;
+                pp[q] = s < s1 ? sv.P[s] : 0.0;
+            }
+#pragma unroll
+            for (int q = 0; q < SEGB; ++q) {
+                if (c[q]) { float lk = ak; double lv = av; ak = lst[q]; av = pp[q]; fwd_combine(lk, lv, ak, av, inv_t); }
+                rc += c[q];
+            }
+        }
+        uint32_t rbase = wave_inclusive_scan(rc) - rc;
+        wave_scan_fwd_excl(ak, av, inv_t);
+        {   // the lower tail precedes everything
+            float ck = ak; double cv = av;
+            float tk = -INFINITY; double tv = 0.0;
+            if (tl.S_L > 0.0 && tl.aL > -INFINITY) { tk = tl.aL; tv = tl.S_L; }
+            fwd_combine(tk, tv, ck, cv, inv_t);
+            ak = ck; av = cv;
+        }
+        for (int s = s0; s < s1; ++s) {  // values are cached from the pass above
+            const uint32_t c = sv.cnt[s];
+            sc.pk[s] = ak; sc.pv[s] = av; sc.rank[s] = rbase;
+            rbase += c;
+            if (c) { float lk = ak; double lv = av; ak = sv.last[s]; av = sv.P[s]; fwd_combine(lk, lv, ak, av, inv_t); }
+        }
+        float bk = INFINITY; double bvv = 0.0;
+        for (int s = s1 - 1; s >= s0; --s) {
+            if (sv.cnt[s]) { float k2 = sv.first[s]; double v2 = 1.0 + sv.Bx[s]; bwd_combine(k2, v2, bk, bvv, inv_t); bk = k2; bvv = v2; }
+        }
+        wave_scan_bwd_excl(bk, bvv, inv_t);
         if (tl.S_R > 0.0 && tl.aR < INFINITY) bwd_combine(bk, bvv, tl.aR, tl.S_R, inv_t);
+        for (int s = s1 - 1; s >= s0; --s) {
+            sc.bk[s] = bk; sc.bv[s] = bvv;
+            if (sv.cnt[s]) { float k2 = sv.first[s]; double v2 = 1.0 + sv.Bx[s]; bwd_combine(k2, v2, bk, bvv, inv_t); bk = k2; bvv = v2; }
+        }
     }
-    for (int s = s1 - 1; s >= s0; --s) {
-        sc.bk[s] = bk; sc.bv[s] = bvv;
-        if (sv.cnt[s]) { float k2 = sv.first[s]; double v2 = 1.0 + sv.Bx[s]; bwd_combine(k2, v2, bk, bvv, inv_t); bk = k2; bvv = v2; }
-    }
+    __threadfence_block();
     __syncthreads();
     // ---- phase 3: G at every segment's first score; last segment with G >= k ----
     int cand = -1;
-    for (int s = s0; s < s1; ++s) {
+    for (int s = tid; s < nseg; s += NT) {
         if (!sv.cnt[s]) continue;
         const float f = sv.first[s];
         const double Pf = 1.0 + (sc.pv[s] != 0.0 ? ecoef(((double)sc.pk[s] - (double)f) * inv_t) * sc.pv[s] : 0.0);
         const double Bf = sv.Bx[s] + (sc.bv[s] != 0.0 ? ecoef(((double)f - (double)sc.bk[s]) * inv_t) * sc.bv[s] : 0.0);
         sc.bfx[s] = Bf;
         const double G = 0.5 * Pf + (tl.m - 1.0 - (double)sc.rank[s]) + tl.c_R - 0.5 * Bf;
-        if (G >= tl.k) cand = s;
+        if (G >= tl.k) cand = max(cand, s);
     }
     const int sstar = block_max_int<NT>(cand, s_int);
     __threadfence_block();
     __syncthreads();
 
     SolveOut out; out.b = 0.0; out.jstar = -1; out.ok = 1;
-    int jl = -1;
-    uint32_t cS = 0u, offS = 0u, rankS = 0u;
+    if (tid == 0) s_owner = -1;
     if (sstar >= 0) {
         // ---- phase 4: per-score curve inside the root segment ----
-        cS = sv.cnt[sstar]; offS = sv.off[sstar]; rankS = sc.rank[sstar];
+        const uint32_t cS = sv.cnt[sstar], offS = sv.off[sstar], rankS = sc.rank[sstar];
         const int E = ((int)cS + NT - 1) / NT;
         const int e0 = min((int)cS, tid * E), e1 = min((int)cS, e0 + E);
         float vv[EMAX];
-        double al[EMAX];   // al[q] = e^{(v_{j-1} - v_j)/t} for j = e0 + q (q > 0)
 #pragma unroll
         for (int q = 0; q < EMAX; ++q) {
             const int j = e0 + q;
             vv[q] = (j < e1) ? key2f(sv.keys[offS + j]) : 0.0f;
         }
+        const float vfirst = key2f(sv.keys[offS]);
+        const float vlast = key2f(sv.keys[offS + cS - 1]);
+        const float pk0 = sc.pk[sstar]; const double pv0 = sc.pv[sstar];
+        const float bk0 = sc.bk[sstar]; const double bv0 = sc.bv[sstar];
+        double Pj[EMAX], Bj[EMAX];
+        const bool have_local = sv.eU != nullptr && !sv.wide[sstar];
+        if (have_local || ((double)vlast - (double)vfirst) * inv_t <= 600.0) {
+            // additive form relative to ref = v_first: u_j = e^{(v_j - ref)/t} in [1, e^600]
+            //   P_j = (carry_P + sum_{i<=j} u_i) / u_j,  B_j = u_j (carry_B + sum_{i>j} 1/u_i)
+            const double ref = (double)vfirst;
+            double u[EMAX], Ul[EMAX], Wl[EMAX];
 #pragma unroll
-        for (int q = 1; q < EMAX; ++q) {
-            al[q] = (e0 + q < e1) ? ecoef(((double)vv[q - 1] - (double)vv[q]) * inv_t) : 0.0;
-        }
-        al[0] = 0.0;
-        // forward: local prefix then workgroup carry
-        float fk = -INFINITY; double fv = 0.0;
+            for (int q = 0; q < EMAX; ++q) u[q] = (e0 + q < e1) ? ecoef(((double)vv[q] - ref) * inv_t) : 1.0;
+            if (have_local) {
 #pragma unroll
-        for (int q = 0; q < EMAX; ++q) {
-            if (e0 + q < e1) { fv = 1.0 + (q > 0 ? al[q] * fv : 0.0); fk = vv[q]; }
-        }
-        block_scan_fwd_excl<NT>(fk, fv, s_k, s_v, inv_t);
-        {   // carry from everything before the segment
-            float pk0 = sc.pk[sstar]; double pv0 = sc.pv[sstar];
-            float ck = fk; double cv = fv;
-            fwd_combine(pk0, pv0, ck, cv, inv_t);
-            fk = ck; fv = cv;
-        }
-        double Pj[EMAX];
+                for (int q = 0; q < EMAX; ++q) {
+                    const int j = e0 + q;
+                    Ul[q] = j < e1 ? sv.eU[offS + j] : 0.0;
+                    Wl[q] = j < e1 ? sv.eW[offS + j] : 0.0;
+                }
+            } else {
+                double ut = 0.0, wt = 0.0;
 #pragma unroll
-        for (int q = 0; q < EMAX; ++q) {
-            if (e0 + q < e1) {
-                double carry = (q == 0) ? (fv != 0.0 ? ecoef(((double)fk - (double)vv[0]) * inv_t) * fv : 0.0)
-                                        : al[q] * Pj[q - 1];
-                Pj[q] = 1.0 + carry;
+                for (int q = 0; q < EMAX; ++q)
+                    if (e0 + q < e1) { ut += u[q]; wt += 1.0 / u[q]; }
+                double U = block_scan_add_excl<NT>(ut, s_v, false);
+                double W = block_scan_add_excl<NT>(wt, s_v, true);
+#pragma unroll
+                for (int q = 0; q < EMAX; ++q)
+                    if (e0 + q < e1) { U += u[q]; Ul[q] = U; }
+#pragma unroll
+                for (int q = EMAX - 1; q >= 0; --q)
+                    if (e0 + q < e1) { Wl[q] = W; W += 1.0 / u[q]; }
+            }
+            const double pc = (pv0 != 0.0) ? pv0 * ecoef(((double)pk0 - ref) * inv_t) : 0.0;
+            const double bc = (bv0 != 0.0) ? bv0 * ecoef((ref - (double)bk0) * inv_t) : 0.0;
+#pragma unroll
+            for (int q = 0; q < EMAX; ++q) {
+                Pj[q] = (pc + Ul[q]) / u[q];
+                Bj[q] = u[q] * (bc + Wl[q]);
+            }
+        } else {
+            // wide segment: affine carries with every exponent <= 0
+            double al[EMAX];
+#pragma unroll
+            for (int q = 1; q < EMAX; ++q)
+                al[q] = (e0 + q < e1) ? ecoef(((double)vv[q - 1] - (double)vv[q]) * inv_t) : 0.0;
+            al[0] = 0.0;
+            float fk = -INFINITY; double fv = 0.0;
+#pragma unroll
+            for (int q = 0; q < EMAX; ++q)
+                if (e0 + q < e1) { fv = 1.0 + (q > 0 ? al[q] * fv : 0.0); fk = vv[q]; }
+            block_scan_fwd_excl<NT>(fk, fv, s_k, s_v, inv_t);
+            {
+                float pk = pk0; double pv = pv0;
+                float ck = fk; double cv = fv;
+                fwd_combine(pk, pv, ck, cv, inv_t);
+                fk = ck; fv = cv;
+            }
+#pragma unroll
+            for (int q = 0; q < EMAX; ++q) {
+                if (e0 + q < e1) {
+                    const double carry = (q == 0) ? (fv != 0.0 ? ecoef(((double)fk - (double)vv[0]) * inv_t) * fv : 0.0)
+                                                  : al[q] * Pj[q - 1];
+                    Pj[q] = 1.0 + carry;
+                }
+            }
+            float rk2 = INFINITY; double rv2 = 0.0;
+#pragma unroll
+            for (int q = EMAX - 1; q >= 0; --q) {
+                if (e0 + q < e1) {
+                    rv2 = 1.0 + (rv2 != 0.0 ? ecoef(((double)vv[q] - (double)rk2) * inv_t) * rv2 : 0.0);
+                    rk2 = vv[q];
+                }
+            }
+            block_scan_bwd_excl<NT>(rk2, rv2, s_k, s_v, inv_t);
+            {
+                float bk = bk0; double bvv = bv0;
+                bwd_combine(rk2, rv2, bk, bvv, inv_t);
+            }
+#pragma unroll
+            for (int q = EMAX - 1; q >= 0; --q) {
+                const int j = e0 + q;
+                if (j < e1) {
+                    if (q + 1 < EMAX && j + 1 < e1) Bj[q] = al[q + 1] * (1.0 + Bj[q + 1]);
+                    else Bj[q] = (rv2 != 0.0) ? ecoef(((double)vv[q] - (double)rk2) * inv_t) * rv2 : 0.0;
+                }
             }
         }
-        // backward: local inclusive suffix then workgroup carry
-        float rk2 = INFINITY; double rv2 = 0.0;
-#pragma unroll
-        for (int q = EMAX - 1; q >= 0; --q) {
-            if (e0 + q < e1) {
-                rv2 = 1.0 + (rv2 != 0.0 ? ecoef(((double)vv[q] - (double)rk2) * inv_t) * rv2 : 0.0);
-                rk2 = vv[q];
-            }
-        }
-        block_scan_bwd_excl<NT>(rk2, rv2, s_k, s_v, inv_t);
-        {
-            float bk0 = sc.bk[sstar]; double bv0 = sc.bv[sstar];
-            bwd_combine(rk2, rv2, bk0, bv0, inv_t);
-        }
-        double Bj[EMAX];
         int myj = -1;
-#pragma unroll
-        for (int q = EMAX - 1; q >= 0; --q) {
-            if (e0 + q < e1) {
-                double bx;
-                if (q + 1 < EMAX && e0 + q + 1 < e1) bx = al[q + 1] * (1.0 + Bj[q + 1]);
-                else bx = (rv2 != 0.0) ? ecoef(((double)vv[q] - (double)rk2) * inv_t) * rv2 : 0.0;
-                Bj[q] = bx;
-            }
-        }
 #pragma unroll
         for (int q = 0; q < EMAX; ++q) {
             const int j = e0 + q;
             if (j < e1) {
-                sc.eP[j] = Pj[q];
-                sc.eB[j] = Bj[q];
                 const double G = 0.5 * Pj[q] + (tl.m - 1.0 - (double)(rankS + (uint32_t)j)) + tl.c_R - 0.5 * Bj[q];
                 if (G >= tl.k) myj = j;
             }
         }
-        jl = block_max_int<NT>(myj, s_int);
-        if (jl < 0) jl = 0;  // the segment's first score passed in phase 3
-        __threadfence_block();
-        __syncthreads();
-    }
-
-    if (tid == 0) {
-        double ref, lnA, lnB, D, clo, chi;
-        if (sstar >= 0) {
-            const float lo = key2f(sv.keys[offS + jl]);
-            ref = lo; clo = lo;
-            lnA = log(sc.eP[jl]);
-            const double J = (double)(rankS + (uint32_t)jl);
-            D = (tl.m - 1.0 - J) + tl.c_R - tl.k;
-            out.jstar = (long long)(rankS + (uint32_t)jl);
-            float vnext = 0.0f; double Bnext = 0.0; bool has_next = false;
-            if ((uint32_t)jl + 1u < cS) { vnext = key2f(sv.keys[offS + jl + 1]); Bnext = sc.eB[jl + 1]; has_next = true; }
-            else {
-                for (int s = sstar + 1; s < nseg; ++s)
-                    if (sv.cnt[s]) { vnext = sv.first[s]; Bnext = sc.bfx[s]; has_next = true; break; }
+        // neighbour exchange: every thread publishes its first score and its B there
+        s_k[tid] = vv[0];
+        s_v[tid] = e0 < e1 ? Bj[0] : 0.0;
+        int jl = block_max_int<NT>(myj, s_int);  // (has barriers; also orders the LDS writes above)
+        if (jl < 0) jl = 0;                       // the segment's first score passed in phase 3
+        if (jl >= e0 && jl < e1) {
+            // this thread owns j*: lower end, P there, and the next score with its B
+            const int q = jl - e0;
+            double Pjs = 0.0, vlo = 0.0, vnx = 0.0, Bnx = 0.0;
+            int has_next = 0;
+#pragma unroll
+            for (int qq = 0; qq < EMAX; ++qq) if (qq == q) { Pjs = Pj[qq]; vlo = (double)vv[qq]; }
+            if (jl + 1 < e1) {
+#pragma unroll
+                for (int qq = 0; qq < EMAX - 1; ++qq) if (qq == q) { vnx = (double)vv[qq + 1]; Bnx = Bj[qq + 1]; }
+                has_next = 1;
+            } else if ((uint32_t)jl + 1u < cS) {
+                vnx = (double)s_k[tid + 1]; Bnx = s_v[tid + 1]; has_next = 1;
             }
-            if (has_next) { chi = vnext; lnB = ((double)lo - (double)vnext) * inv_t + log1p(Bnext); }
+            s_root[0] = Pjs; s_root[1] = vlo; s_root[2] = vnx; s_root[3] = Bnx;
+            s_owner = has_next;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            const double lo = s_root[1];
+            double lnA = log(s_root[0]), lnB, chi;
+            const double J = (double)(rankS + (uint32_t)jl);
+            const double D = (tl.m - 1.0 - J) + tl.c_R - tl.k;
+            out.jstar = (long long)(rankS + (uint32_t)jl);
+            int has_next = s_owner;
+            double vnext = s_root[2], Bnext = s_root[3];
+            if (!has_next) {
+                for (int s = sstar + 1; s < nseg; ++s)
+                    if (sv.cnt[s]) { vnext = sv.first[s]; Bnext = sc.bfx[s]; has_next = 1; break; }
+            }
+            if (has_next) { chi = vnext; lnB = (lo - vnext) * inv_t + log1p(Bnext); }
             else {
                 chi = tl.aR;
-                lnB = (tl.S_R > 0.0 && tl.aR < INFINITY) ? log(tl.S_R) + ((double)lo - (double)tl.aR) * inv_t : -INFINITY;
+                lnB = (tl.S_R > 0.0 && tl.aR < INFINITY) ? log(tl.S_R) + (lo - (double)tl.aR) * inv_t : -INFINITY;
+            }
+            const double lnw = log_root(lnA, lnB, D);
+            double b = lo + tl.t * lnw;
+            if (b < lo) b = lo;
+            if (b > chi) b = chi;
+            out.b = b;
+            out.ok = (b == b) && (b > -INFINITY) && (b < INFINITY);
+        }
+    } else if (tid == 0) {
+        // the root lies below the first score of the segments
+        double ref, lnA, lnB, clo, chi;
+        int s0n = -1;
+        for (int s = 0; s < nseg; ++s) if (sv.cnt[s]) { s0n = s; break; }
+        const double D = tl.m + tl.c_R - tl.k;
+        if (tl.aL > -INFINITY) {
+            ref = tl.aL; clo = tl.aL;
+            lnA = tl.S_L > 0.0 ? log(tl.S_L) : -INFINITY;
+            if (s0n >= 0) { chi = sv.first[s0n]; lnB = ((double)tl.aL - chi) * inv_t + log1p(sc.bfx[s0n]); }
+            else {
+                chi = tl.aR;
+                lnB = (tl.S_R > 0.0 && tl.aR < INFINITY) ? log(tl.S_R) + ((double)tl.aL - (double)tl.aR) * inv_t : -INFINITY;
             }
         } else {
-            int s0n = -1;
-            for (int s = 0; s < nseg; ++s) if (sv.cnt[s]) { s0n = s; break; }
-            D = tl.m + tl.c_R - tl.k;
-            if (tl.aL > -INFINITY) {
-                ref = tl.aL; clo = tl.aL;
-                lnA = tl.S_L > 0.0 ? log(tl.S_L) : -INFINITY;
-                if (s0n >= 0) { chi = sv.first[s0n]; lnB = ((double)tl.aL - chi) * inv_t + log1p(sc.bfx[s0n]); }
-                else {
-                    chi = tl.aR;
-                    lnB = (tl.S_R > 0.0 && tl.aR < INFINITY) ? log(tl.S_R) + ((double)tl.aL - (double)tl.aR) * inv_t : -INFINITY;
-                }
-            } else {
-                clo = -INFINITY; lnA = -INFINITY;
-                if (s0n >= 0) { ref = sv.first[s0n]; chi = ref; lnB = log1p(sc.bfx[s0n]); }
-                else { ref = tl.aR; chi = tl.aR; lnB = tl.S_R > 0.0 ? log(tl.S_R) : -INFINITY; }
-            }
-            out.jstar = -1;
+            clo = -INFINITY; lnA = -INFINITY;
+            if (s0n >= 0) { ref = sv.first[s0n]; chi = ref; lnB = log1p(sc.bfx[s0n]); }
+            else { ref = tl.aR; chi = tl.aR; lnB = tl.S_R > 0.0 ? log(tl.S_R) : -INFINITY; }
         }
+        out.jstar = -1;
         const double lnw = log_root(lnA, lnB, D);
         double b = ref + tl.t * lnw;
         if (b < clo) b = clo;

@@ -198,6 +198,146 @@ LS_DEV unsigned long long block_sum_u64(unsigned long long v, unsigned long long
     return r;  // valid in wave 0
 }
 
+// ---------------------------------------------------------------------------
+// Grid-stride streaming over float4 elements [0, n4) with U loads in flight
+// per thread: the next U loads are issued before the current U are consumed
+// (software pipelining -- a single load in flight per wave leaves HBM idle
+// while the wave computes).  The main loop's trip test uses the wave's last
+// lane, so all 64 lanes iterate together (wave-wide ballots are safe inside
+// main); leftover elements go to tail, one per lane.  reverse = true walks
+// the array from its end, so a pass can start on the part of an array the
+// previous pass read last (still in the memory-side cache).
+// main(v, idx) / tail(v, idx): v = element idx.
+// ---------------------------------------------------------------------------
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+// 16-byte load, optionally non-temporal (streamed past the caches)
+template <bool NT>
+LS_DEV float4 ld4(const float4* p) {
+    if (NT) {
+        const f4v v = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(p));
+        return make_float4(v.x, v.y, v.z, v.w);
+    }
+    return *p;
+}
+
+template <int U, bool NT = false, class Main, class Tail>
+LS_DEV void stream_f4(const float4* __restrict__ a, long long n4, bool reverse, Main&& main, Tail&& tail) {
+    const long long stride = (long long)gridDim.x * blockDim.x;
+    long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;  // logical position
+    const long long last = 63 - (long long)lane_id();
+    const long long step = reverse ? -stride : stride;                // physical step (wave-uniform)
+    long long idx = reverse ? n4 - 1 - i : i;                         // physical index of i
+    // the trip test is made explicitly wave-uniform; the prefetch offset is a
+    // wave-uniform scalar (when there is no next batch the prefetch re-reads
+    // the current one), so every load address is base + scalar and the
+    // compiler keeps the prefetches in flight while the current batch is used
+    auto uniform = [](bool c) { return __builtin_amdgcn_readfirstlane((int)c) != 0; };
+    if (uniform(i + last + (long long)(U - 1) * stride < n4)) {
+        float4 cur[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) cur[u] = ld4<NT>(a + idx + u * step);
+        while (true) {
+            const bool hn = uniform(i + (long long)U * stride + last + (long long)(U - 1) * stride < n4);
+            const long long poff = hn ? (long long)U * step : 0;
+            float4 nx[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) nx[u] = ld4<NT>(a + idx + poff + u * step);
+#pragma unroll
+            for (int u = 0; u < U; ++u) main(cur[u], idx + u * step);
+            i += (long long)U * stride;
+            idx += (long long)U * step;
+            if (!hn) break;
+#pragma unroll
+            for (int u = 0; u < U; ++u) cur[u] = nx[u];
+        }
+    }
+    for (; i < n4; i += stride, idx += step) tail(a[idx], idx);
+}
+
+// the same over two arrays read in lockstep
+template <int U, bool NT = false, class Main, class Tail>
+LS_DEV void stream_f4x2(const float4* __restrict__ a, const float4* __restrict__ b, long long n4, bool reverse,
+                        Main&& main, Tail&& tail) {
+    const long long stride = (long long)gridDim.x * blockDim.x;
+    long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long long last = 63 - (long long)lane_id();
+    const long long step = reverse ? -stride : stride;
+    long long idx = reverse ? n4 - 1 - i : i;
+    auto uniform = [](bool c) { return __builtin_amdgcn_readfirstlane((int)c) != 0; };
+    if (uniform(i + last + (long long)(U - 1) * stride < n4)) {
+        float4 ca[U], cb[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) { ca[u] = ld4<NT>(a + idx + u * step); cb[u] = ld4<NT>(b + idx + u * step); }
+        while (true) {
+            const bool hn = uniform(i + (long long)U * stride + last + (long long)(U - 1) * stride < n4);
+            const long long poff = hn ? (long long)U * step : 0;
+            float4 na[U], nb[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                na[u] = ld4<NT>(a + idx + poff + u * step);
+                nb[u] = ld4<NT>(b + idx + poff + u * step);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) main(ca[u], cb[u], idx + u * step);
+            i += (long long)U * stride;
+            idx += (long long)U * step;
+            if (!hn) break;
+#pragma unroll
+            for (int u = 0; u < U; ++u) { ca[u] = na[u]; cb[u] = nb[u]; }
+        }
+    }
+    for (; i < n4; i += stride, idx += step) tail(a[idx], b[idx], idx);
+}
+
+// ascending bitonic sort of N (a power of two) keys in LDS by NT threads
+template <int NT>
+LS_DEV void bitonic_sort_lds(uint32_t* a, int N) {
+    for (int size = 2; size <= N; size <<= 1) {
+        for (int half = size >> 1; half > 0; half >>= 1) {
+            for (int t = threadIdx.x; t < (N >> 1); t += NT) {
+                const int i = ((t & ~(half - 1)) << 1) | (t & (half - 1));  // half is a power of two
+                const int j = i + half;
+                const bool up = (i & size) == 0;
+                const uint32_t x = a[i], y = a[j];
+                if ((x > y) == up) { a[i] = y; a[j] = x; }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+LS_DEV int next_pow2(int x) {
+    int p = 1;
+    while (p < x) p <<= 1;
+    return p;
+}
+
+// additive exclusive scan of double over the workgroup (Hillis-Steele in
+// LDS).  reverse = false: sum over lower thread indices; true: over higher
+// ones.  The exclusive value is read from the neighbour's inclusive sum, never
+// formed as (inclusive - own).
+template <int NT>
+LS_DEV double block_scan_add_excl(double v, double* s, bool reverse) {
+    const int tid = threadIdx.x;
+    s[tid] = v;
+    __syncthreads();
+    double acc = v;
+    for (int o = 1; o < NT; o <<= 1) {
+        const int src = reverse ? tid + o : tid - o;
+        const bool has = reverse ? (src < NT) : (src >= 0);
+        const double y = has ? s[src] : 0.0;
+        __syncthreads();
+        acc += y;
+        s[tid] = acc;
+        __syncthreads();
+    }
+    const int nb = reverse ? tid + 1 : tid - 1;
+    const double ex = (reverse ? (nb < NT) : (nb >= 0)) ? s[nb] : 0.0;
+    __syncthreads();
+    return ex;
+}
+
 // device-scope ticket for the last-workgroup pattern: release this
 // workgroup's global writes, take a ticket, and tell every thread whether it
 // is in the last workgroup to finish (which then sees all earlier writes).

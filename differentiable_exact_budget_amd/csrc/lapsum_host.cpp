@@ -33,8 +33,8 @@
 #include <tuple>
 #include <vector>
 
-#include "../../include/lapsum.h"
-#include "../../include/lapsum_testing.h"
+#include "lapsum.h"
+#include "lapsum_testing.h"
 #include "lapsum_launch.h"
 
 using namespace lapsum;
@@ -61,6 +61,9 @@ struct Workspace {
     float* iw = nullptr;
     uint32_t* bucket_cnt = nullptr;
     uint32_t* bucket_vals = nullptr;
+    double* eU = nullptr;
+    double* eW = nullptr;
+    uint8_t* wide = nullptr;
     SegArrays seg{};
     SolveScratch sc{};
     uint32_t* keysA = nullptr;
@@ -80,7 +83,7 @@ long long tiles_for(long long n) { return (n + kRadixTile - 1) / kRadixTile; }
 
 // layout of one workspace for forwards up to n_cap scores
 struct Layout {
-    size_t ctl, part, sample, sample_idx, sp, iw, bcnt, bvals, seg_first, seg_last, seg_P, seg_Bx, seg_cnt, seg_off,
+    size_t ctl, part, sample, sample_idx, sp, iw, bcnt, bvals, eU, eW, wide, seg_first, seg_last, seg_P, seg_Bx, seg_cnt, seg_off,
         sc_pk, sc_pv, sc_bk, sc_bv, sc_bfx, sc_rank, sc_eP, sc_eB, keysA, keysB, hist, goff, status, total;
     size_t status_bytes;
 };
@@ -99,6 +102,9 @@ Layout make_layout(long long n_cap) {
     L.iw = take(sizeof(float) * kMaxBuckets);
     L.bcnt = take(sizeof(uint32_t) * kMaxBuckets);
     L.bvals = take(sizeof(uint32_t) * (size_t)kMaxBuckets * kBucketCapMax);
+    L.eU = take(sizeof(double) * (size_t)kMaxBuckets * kBucketCapMax);
+    L.eW = take(sizeof(double) * (size_t)kMaxBuckets * kBucketCapMax);
+    L.wide = take(kMaxBuckets);
     L.seg_first = take(sizeof(float) * nseg);
     L.seg_last = take(sizeof(float) * nseg);
     L.seg_P = take(sizeof(double) * nseg);
@@ -152,6 +158,9 @@ lapsum_status_t alloc_ws(Workspace* w, long long n_cap) {
     w->iw = reinterpret_cast<float*>(base + L.iw);
     w->bucket_cnt = reinterpret_cast<uint32_t*>(base + L.bcnt);
     w->bucket_vals = reinterpret_cast<uint32_t*>(base + L.bvals);
+    w->eU = reinterpret_cast<double*>(base + L.eU);
+    w->eW = reinterpret_cast<double*>(base + L.eW);
+    w->wide = reinterpret_cast<uint8_t*>(base + L.wide);
     w->seg = SegArrays{reinterpret_cast<float*>(base + L.seg_first), reinterpret_cast<float*>(base + L.seg_last),
                        reinterpret_cast<double*>(base + L.seg_P), reinterpret_cast<double*>(base + L.seg_Bx),
                        reinterpret_cast<uint32_t*>(base + L.seg_cnt), reinterpret_cast<uint32_t*>(base + L.seg_off)};
@@ -378,8 +387,9 @@ lapsum_status_t check_args(const float* r, int64_t n, double k, float t, const v
     return LAPSUM_OK;
 }
 
-lapsum_status_t fill_stats(Workspace* w, hipStream_t st, lapsum_stats_t* stats) {
+lapsum_status_t fill_stats(Workspace* w, hipStream_t st, long long n, lapsum_stats_t* stats) {
     if (!stats) return LAPSUM_OK;
+    launch_sum_p(w->ctl, w->part, n, st);
     if (hipStreamSynchronize(st) != hipSuccess) return LAPSUM_ERR_HIP;
     Ctl c;
     if (hipMemcpy(&c, w->ctl, sizeof(Ctl), hipMemcpyDeviceToHost) != hipSuccess) return LAPSUM_ERR_HIP;
@@ -419,7 +429,7 @@ lapsum_status_t forward_impl(const float* r, int64_t n, double k, float t_f, flo
         if (stats) {
             stats->path_taken = 1;
             stats->band_size = n;
-            lapsum_status_t fs = fill_stats(w, st, stats);
+            lapsum_status_t fs = fill_stats(w, st, n, stats);
             tm.collect(stats);
             return fs;
         }
@@ -499,7 +509,7 @@ lapsum_status_t forward_impl(const float* r, int64_t n, double k, float t_f, flo
     if (br.nonfinite) {
         launch_set_nan_b(w->ctl, b_out, st);
         launch_fill(p, n, std::numeric_limits<float>::quiet_NaN(), st);
-        if (stats) { fill_stats(w, st, stats); stats->status = LAPSUM_ERR_NONFINITE_INPUT; tm.collect(stats); }
+        if (stats) { fill_stats(w, st, n, stats); stats->status = LAPSUM_ERR_NONFINITE_INPUT; tm.collect(stats); }
         return LAPSUM_ERR_NONFINITE_INPUT;
     }
     const bool fallback = !br.certified || br.overflow || path == LAPSUM_PATH_FORCE_FALLBACK;
@@ -507,7 +517,8 @@ lapsum_status_t forward_impl(const float* r, int64_t n, double k, float t_f, flo
         run_full(w, r, n, k, t, b_out, st, tm);
     } else {
         tm.begin("bucket_solve");
-        launch_bucket_solve(w->bucket_vals, w->bucket_cnt, cap, br.h.nb, w->ctl, w->seg, w->sc, k, t, b_out, st);
+        launch_bucket_solve(w->bucket_vals, w->bucket_cnt, cap, br.h.nb, w->ctl, w->seg, w->eU, w->eW, w->wide, w->sc, k,
+                            t, b_out, st);
         tm.end();
     }
     tm.begin("probs");
@@ -516,7 +527,7 @@ lapsum_status_t forward_impl(const float* r, int64_t n, double k, float t_f, flo
     if (hipGetLastError() != hipSuccess) return LAPSUM_ERR_HIP;
     if (stats) {
         stats->path_taken = fallback ? 3 : 2;
-        lapsum_status_t fs = fill_stats(w, st, stats);
+        lapsum_status_t fs = fill_stats(w, st, n, stats);
         tm.collect(stats);
         return fs;
     }
@@ -708,8 +719,8 @@ lapsum_status_t lapsum_test_filter(const float* scores, int64_t n, float t, floa
     }
     // sort every bucket on the device (the band solve's first stage), then gather in bucket order
     const double kk = (double)hsum.c_R + 0.5 * (double)hsum.m + 0.25;
-    launch_bucket_solve(w->bucket_vals, w->bucket_cnt, kBucketCapMax, hsum.nb, w->ctl, w->seg, w->sc,
-                        kk > 0 ? kk : 0.5, (double)t, nullptr, st);
+    launch_bucket_solve(w->bucket_vals, w->bucket_cnt, kBucketCapMax, hsum.nb, w->ctl, w->seg, w->eU, w->eW, w->wide,
+                        w->sc, kk > 0 ? kk : 0.5, (double)t, nullptr, st);
     if (hipStreamSynchronize(st) != hipSuccess) return LAPSUM_ERR_HIP;
     std::vector<uint32_t> cnt(kMaxBuckets);
     if (hipMemcpy(cnt.data(), w->bucket_cnt, sizeof(uint32_t) * kMaxBuckets, hipMemcpyDeviceToHost) != hipSuccess)

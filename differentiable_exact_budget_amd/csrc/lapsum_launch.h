@@ -26,6 +26,7 @@ void launch_filter(const float* r, long long n, double t, Ctl* ctl, const float*
                    uint32_t* bucket_cnt, uint32_t* bucket_vals, int cap, double* part, unsigned long long* partc,
                    HostSummary* hs_dev, unsigned int seq, hipStream_t st);
 void launch_probs(const float* r, long long n, double t, float* p, Ctl* ctl, double* part, hipStream_t st);
+void launch_sum_p(Ctl* ctl, const double* part, long long n, hipStream_t st);
 void launch_vjp(const float* r, const float* g, long long n, double t, const double* b, float* grad, Ctl* ctl,
                 double* part, hipStream_t st, hipEvent_t* ev_mid);
 void launch_fill(float* p, long long n, float v, hipStream_t st);
@@ -35,7 +36,8 @@ void launch_set_nan_b(Ctl* ctl, double* b_out, hipStream_t st);
 void launch_small_solve(const float* r, int n, double k, double t, Ctl* ctl, SolveScratch sc, double* b_out,
                         uint32_t* keys_out, hipStream_t s);
 void launch_bucket_solve(uint32_t* bucket_vals, const uint32_t* bucket_cnt, int cap, int nb, Ctl* ctl, SegArrays seg,
-                         SolveScratch sc, double k, double t, double* b_out, hipStream_t s);
+                         double* eU, double* eW, uint8_t* wide, SolveScratch sc, double k, double t, double* b_out,
+                         hipStream_t s);
 int radix_hist_blocks(long long n);
 void launch_radix_sort(const float* r, long long n, uint32_t* keysA, uint32_t* keysB, uint32_t* hist_part,
                        uint32_t* goff, unsigned long long* status, uint32_t epoch_base, Ctl* ctl, hipStream_t s);

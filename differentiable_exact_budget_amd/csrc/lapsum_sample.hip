@@ -51,14 +51,28 @@ void launch_sample(const float* r, long long n, double t, unsigned long long see
 
 // ---------------------------------------------------------------------------
 // select
+// Fast path: sort a subsample of 2048 sample keys, read off a rank window
+// that contains ranks l..h with a wide safety margin, count the sample keys
+// below the window and collect the ones inside it, and sort only those
+// (<= 4096).  The exact order statistics x_(l) .. x_(h) are then read from
+// the sorted window.  If the window check fails (or the window is too wide)
+// an 8-bit MSD radix select finds x_(l) and x_(h) instead.
 // ---------------------------------------------------------------------------
+constexpr int kWinMax = 4096;
+constexpr int kSubMax = 2048;
+
 __global__ __launch_bounds__(kSelectThreads) void k_select(const float* __restrict__ x, int s, long long l, long long h,
                                                             int cap, Ctl* ctl, float* sp, float* iw,
                                                             uint32_t* bucket_cnt) {
     __shared__ uint32_t hist[2][256];
-    __shared__ uint32_t cand[kCandMax];
+    __shared__ uint32_t sub[kSubMax];
+    __shared__ uint32_t win[kWinMax];
     __shared__ uint32_t scr[kSelectThreads / 64 + 2];
+    __shared__ unsigned long long s_redu[kSelectThreads / 64];
     __shared__ uint32_t s_pre[2], s_rem[2];
+    __shared__ uint32_t s_lo, s_hi;
+    __shared__ int s_fast;
+    __shared__ long long s_nlo;
     const int tid = threadIdx.x;
     uint32_t kr[kSelectItems];
 #pragma unroll
@@ -68,83 +82,137 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(const float* __restri
     }
     const bool want_l = l >= 1 && l <= s;
     const bool want_h = h >= 1 && h <= s;
+
+    // ---- subsample and window ----
+    const int msub = s < kSubMax ? s : kSubMax;
+    for (int i = tid; i < kSubMax; i += kSelectThreads)
+        sub[i] = i < msub ? f2key(x[(int)((float)i * ((float)s / (float)msub))]) : 0xFFFFFFFFu;
+    __syncthreads();
+    bitonic_sort_lds<kSelectThreads>(sub, kSubMax);
     if (tid == 0) {
-        s_pre[0] = 0u; s_pre[1] = 0u;
-        s_rem[0] = want_l ? (uint32_t)l : 1u;
-        s_rem[1] = want_h ? (uint32_t)h : 1u;
+        uint32_t lo = 0u, hi = 0xFFFFFFFFu;
+        if (want_l) {
+            const double pl = (double)l / (double)s;
+            const long long r0 = (long long)floor((double)msub * pl - 5.0 * sqrt((double)msub * pl * (1.0 - pl)) - 3.0);
+            lo = r0 < 0 ? 0u : sub[r0];
+        }
+        if (want_h) {
+            const double ph = (double)h / (double)s;
+            const long long r1 = (long long)ceil((double)msub * ph + 5.0 * sqrt((double)msub * ph * (1.0 - ph)) + 3.0);
+            hi = r1 >= msub ? 0xFFFFFFFFu : sub[r1];
+        }
+        s_lo = lo; s_hi = hi;
     }
-    // MSD radix select of ranks l and h (1-based), 8 bits at a time
-    for (int pass = 3; pass >= 0; --pass) {
-        const int shift = 8 * pass;
-        const uint32_t hmask = pass == 3 ? 0u : (0xFFFFFFFFu << (shift + 8));
-        for (int e = tid; e < 512; e += kSelectThreads) (&hist[0][0])[e] = 0u;
-        __syncthreads();
-        const uint32_t p0 = s_pre[0], p1 = s_pre[1];
+    __syncthreads();
+    const uint32_t wlo = s_lo, whi = s_hi;
+    uint32_t nbelow = 0u, nin = 0u;
+#pragma unroll
+    for (int i = 0; i < kSelectItems; ++i) {
+        const int j = i * kSelectThreads + tid;
+        if (j < s) { nbelow += kr[i] < wlo; nin += (kr[i] >= wlo && kr[i] <= whi); }
+    }
+    const unsigned long long NLO = block_sum_u64<kSelectThreads>((unsigned long long)nbelow, s_redu);
+    uint32_t W = 0u;
+    uint32_t pos = block_exclusive_scan<kSelectThreads>(nin, &W, scr);
+    if (tid == 0) {
+        const long long nlo = (long long)NLO;
+        const bool okl = !want_l || nlo <= l - 1;
+        const bool okh = !want_h || nlo + (long long)W >= h;
+        s_fast = (okl && okh && W >= 1 && W <= (uint32_t)kWinMax) ? 1 : 0;
+        s_nlo = nlo;
+    }
+    __syncthreads();
+    const bool fast = s_fast != 0;
+
+    uint32_t key_l = 0u, key_h = 0xFFFFFFFFu;
+    const uint32_t* csorted;  // sorted sample keys from x_(l) (or the minimum) to x_(h) (or the maximum)
+    int cc;
+    if (fast) {
 #pragma unroll
         for (int i = 0; i < kSelectItems; ++i) {
             const int j = i * kSelectThreads + tid;
-            if (j < s) {
-                const uint32_t kk = kr[i];
-                const uint32_t d = (kk >> shift) & 0xFFu;
-                if ((kk & hmask) == (p0 & hmask)) atomicAdd(&hist[0][d], 1u);
-                if ((kk & hmask) == (p1 & hmask)) atomicAdd(&hist[1][d], 1u);
-            }
+            if (j < s && kr[i] >= wlo && kr[i] <= whi) win[pos++] = kr[i];
         }
+        const int wp = next_pow2((int)W);
+        for (int e = (int)W + tid; e < wp; e += kSelectThreads) win[e] = 0xFFFFFFFFu;
         __syncthreads();
-        if (tid == 0 || tid == 64) {
-            const int q = tid == 0 ? 0 : 1;
-            uint32_t rem = s_rem[q], cum = 0u;
-            int d = 0;
-            for (; d < 255; ++d) {
-                const uint32_t c = hist[q][d];
-                if (cum + c >= rem) break;
-                cum += c;
+        bitonic_sort_lds<kSelectThreads>(win, wp);
+        const long long nlo = s_nlo;
+        const int i0 = want_l ? (int)(l - 1 - nlo) : 0;
+        const int i1 = want_h ? (int)(h - 1 - nlo) : (int)W - 1;
+        key_l = win[i0];
+        key_h = win[i1];
+        csorted = win + i0;
+        cc = i1 - i0 + 1;
+    } else {
+        // ---- fallback: MSD radix select of ranks l and h ----
+        if (tid == 0) {
+            s_pre[0] = 0u; s_pre[1] = 0u;
+            s_rem[0] = want_l ? (uint32_t)l : 1u;
+            s_rem[1] = want_h ? (uint32_t)h : 1u;
+        }
+        for (int pass = 3; pass >= 0; --pass) {
+            const int shift = 8 * pass;
+            const uint32_t hmask = pass == 3 ? 0u : (0xFFFFFFFFu << (shift + 8));
+            for (int e = tid; e < 512; e += kSelectThreads) (&hist[0][0])[e] = 0u;
+            __syncthreads();
+            const uint32_t p0 = s_pre[0], p1 = s_pre[1];
+#pragma unroll
+            for (int i = 0; i < kSelectItems; ++i) {
+                const int j = i * kSelectThreads + tid;
+                if (j < s) {
+                    const uint32_t kk = kr[i];
+                    const uint32_t d = (kk >> shift) & 0xFFu;
+                    if ((kk & hmask) == (p0 & hmask)) atomicAdd(&hist[0][d], 1u);
+                    if ((kk & hmask) == (p1 & hmask)) atomicAdd(&hist[1][d], 1u);
+                }
             }
-            s_pre[q] |= (uint32_t)d << shift;
-            s_rem[q] = rem - cum;
-        }
-        __syncthreads();
-    }
-    const uint32_t key_l = s_pre[0], key_h = s_pre[1];
-    const float aL = want_l ? key2f(key_l) : -INFINITY;
-    const float aR = want_h ? key2f(key_h) : INFINITY;
-    const uint32_t klo = want_l ? key_l : 0u;
-    const uint32_t khi = want_h ? key_h : 0xFFFFFFFFu;
-
-    // candidates for splitters: sample keys in [klo, khi], in sample order
-    uint32_t mine = 0u;
-#pragma unroll
-    for (int i = 0; i < kSelectItems; ++i) {
-        const int j = i * kSelectThreads + tid;
-        if (j < s && kr[i] >= klo && kr[i] <= khi) ++mine;
-    }
-    // order candidates by (thread, item): deterministic
-    uint32_t total = 0u;
-    uint32_t pos = block_exclusive_scan<kSelectThreads>(mine, &total, scr);
-    const uint32_t stride = (total + kCandMax - 1) / kCandMax > 0 ? (total + kCandMax - 1) / kCandMax : 1u;
-#pragma unroll
-    for (int i = 0; i < kSelectItems; ++i) {
-        const int j = i * kSelectThreads + tid;
-        if (j < s && kr[i] >= klo && kr[i] <= khi) {
-            if (pos % stride == 0u) cand[pos / stride] = kr[i];
-            ++pos;
-        }
-    }
-    const int cc = (int)((total + stride - 1) / stride);
-    __syncthreads();
-    for (int e = cc + tid; e < kCandMax; e += kSelectThreads) cand[e] = 0xFFFFFFFFu;
-    __syncthreads();
-    // bitonic sort of kCandMax keys (one pair per thread per step)
-    for (int size = 2; size <= kCandMax; size <<= 1) {
-        for (int half = size >> 1; half > 0; half >>= 1) {
-            const int a = 2 * half * (tid / half) + (tid % half);
-            const int b = a + half;
-            const bool up = (a & size) == 0;
-            const uint32_t va = cand[a], vb = cand[b];
-            if ((va > vb) == up) { cand[a] = vb; cand[b] = va; }
+            __syncthreads();
+            if (tid == 0 || tid == 64) {
+                const int qq = tid == 0 ? 0 : 1;
+                uint32_t rem = s_rem[qq], cum = 0u;
+                int d = 0;
+                for (; d < 255; ++d) {
+                    const uint32_t c = hist[qq][d];
+                    if (cum + c >= rem) break;
+                    cum += c;
+                }
+                s_pre[qq] |= (uint32_t)d << shift;
+                s_rem[qq] = rem - cum;
+            }
             __syncthreads();
         }
+        key_l = want_l ? s_pre[0] : 0u;
+        key_h = want_h ? s_pre[1] : 0xFFFFFFFFu;
+        // candidates for splitters: sample keys in [key_l, key_h], thinned in sample order
+        uint32_t mine = 0u;
+#pragma unroll
+        for (int i = 0; i < kSelectItems; ++i) {
+            const int j = i * kSelectThreads + tid;
+            if (j < s && kr[i] >= key_l && kr[i] <= key_h) ++mine;
+        }
+        uint32_t total = 0u;
+        uint32_t cpos = block_exclusive_scan<kSelectThreads>(mine, &total, scr);
+        const uint32_t stride = (total + kCandMax - 1) / kCandMax > 0 ? (total + kCandMax - 1) / kCandMax : 1u;
+#pragma unroll
+        for (int i = 0; i < kSelectItems; ++i) {
+            const int j = i * kSelectThreads + tid;
+            if (j < s && kr[i] >= key_l && kr[i] <= key_h) {
+                if (cpos % stride == 0u) sub[cpos / stride] = kr[i];
+                ++cpos;
+            }
+        }
+        cc = (int)((total + stride - 1) / stride);
+        __syncthreads();
+        for (int e = cc + tid; e < kCandMax; e += kSelectThreads) sub[e] = 0xFFFFFFFFu;
+        __syncthreads();
+        bitonic_sort_lds<kSelectThreads>(sub, kCandMax);
+        csorted = sub;
+        if (cc < 1) cc = 1;
     }
+    const float aL = want_l ? key2f(key_l) : -INFINITY;
+    const float aR = want_h ? key2f(key_h) : INFINITY;
+
     // gaps: ng <= 256, interior splitters evenly spaced over the sorted candidates
     const int ng = cc >= 2 ? (cc - 1 < kMaxBuckets ? cc - 1 : kMaxBuckets) : 1;
     const int J = kMaxBuckets / ng > 0 ? kMaxBuckets / ng : 1;
@@ -152,7 +220,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(const float* __restri
         float v;
         if (g == 0) v = aL;
         else if (g == ng) v = aR;
-        else v = key2f(cand[(int)(((long long)g * (cc - 1)) / ng)]);
+        else v = key2f(csorted[(int)(((long long)g * (cc - 1)) / ng)]);
         sp[g] = v;
     }
     __syncthreads();
@@ -173,6 +241,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(const float* __restri
         ctl->ng = ng; ctl->J = J; ctl->nb = ng * J;
         ctl->cap = cap;
         ctl->flags = 0;
+        ctl->pad0 = fast ? 1 : 0;
     }
 }
 

@@ -39,11 +39,22 @@ struct FilterPart {
     int pad;
 };
 
+constexpr int kQueueCap = 2048;  // band scores a workgroup holds in LDS before spilling
+
+// Traversal order of the second pass over an array: walking it backwards
+// starts on the part the previous pass read last, which the 256 MB
+// memory-side cache may still hold.
+constexpr int kProbsReverse = 1;
+constexpr int kApplyReverse = 1;
+// non-temporal loads for the read-only passes
+constexpr bool kFilterNT = true;
+constexpr bool kReduceNT = true;
+
 // ---------------------------------------------------------------------------
 // streaming filter
 // ---------------------------------------------------------------------------
 struct FilterState {
-    float aL, aR, ls, ng_f;
+    float aL, aR, ls;
     int ng, J, cap;
     const float* sp;
     const float* iw;
@@ -51,9 +62,9 @@ struct FilterState {
     uint32_t* bucket_vals;
 };
 
-// band score: bucket by splitter gap, then equal-width sub-bucket (monotone in v)
-LS_DEV void filter_band(const FilterState& fs, float v, double& BL, int& nan, int& ovf) {
-    if (v != v) { nan = 1; return; }
+// bucket of a band score: splitter gap by binary search, then equal-width
+// sub-bucket inside a finite gap (monotone in v)
+LS_DEV int band_bucket(const FilterState& fs, float v) {
     int g = 0;
     for (int step = 128; step > 0; step >>= 1)
         if (g + step < fs.ng && fs.sp[g + step] <= v) g += step;
@@ -63,176 +74,243 @@ LS_DEV void filter_band(const FilterState& fs, float v, double& BL, int& nan, in
         const float f = (v - fs.sp[g]) * iwg;
         sub = f < (float)(fs.J - 1) ? (int)f : fs.J - 1;
     }
-    const int bkt = g * fs.J + sub;
+    return g * fs.J + sub;
+}
+
+// e^{(a_L - v)/t} and e^{(v - a_R)/t} of a band score (0 for an open end)
+LS_DEV void band_sums(const FilterState& fs, float v, double& BL, double& BR) {
     if (fs.aL > -INFINITY) BL += (double)__builtin_amdgcn_exp2f(-(v - fs.aL) * fs.ls);
+    if (fs.aR < INFINITY) BR += (double)__builtin_amdgcn_exp2f(-(fs.aR - v) * fs.ls);
+}
+
+// spill path for a band score when the workgroup's LDS queue is full
+LS_DEV void band_direct(const FilterState& fs, float v, double& BL, double& BR, int& nan, uint32_t& nnan) {
+    if (v != v) { nan = 1; ++nnan; return; }
+    band_sums(fs, v, BL, BR);
+    const int bkt = band_bucket(fs, v);
     const uint32_t pos = atomicAdd(&fs.bucket_cnt[bkt], 1u);
     if (pos < (uint32_t)fs.cap) fs.bucket_vals[(size_t)bkt * (size_t)fs.cap + pos] = __float_as_uint(v);
-    else ovf = 1;
 }
 
 template <bool VEC>
 __global__ __launch_bounds__(kStreamThreads) void k_filter(const float* __restrict__ r, long long n, float ls,
-                                                            Ctl* ctl, const float* __restrict__ sp_g,
+                                                            const Ctl* ctl, const float* __restrict__ sp_g,
                                                             const float* __restrict__ iw_g, uint32_t* bucket_cnt,
-                                                            uint32_t* bucket_vals, int cap, FilterPart* part,
-                                                            HostSummary* hs, unsigned int seq) {
+                                                            uint32_t* bucket_vals, int cap, FilterPart* part) {
     __shared__ float sp[kMaxBuckets + 1];
     __shared__ float iw[kMaxBuckets];
+    __shared__ float q[kQueueCap];
+    __shared__ uint32_t lcnt[kMaxBuckets];
+    __shared__ uint32_t gbase[kMaxBuckets];
+    __shared__ uint32_t s_qn;
     __shared__ double s_red[kStreamThreads / 64];
     __shared__ unsigned long long s_redu[kStreamThreads / 64];
-    __shared__ uint32_t s_mn, s_mx;
     __shared__ int s_nan;
-    __shared__ unsigned long long s_mxb;
-    __shared__ int s_last;
     const int tid = threadIdx.x;
+    const int lane = lane_id();
     FilterState fs;
     fs.aL = ctl->aL; fs.aR = ctl->aR; fs.ls = ls;
     fs.ng = ctl->ng; fs.J = ctl->J; fs.cap = cap;
+    const int nb = ctl->nb;
     for (int i = tid; i <= fs.ng; i += kStreamThreads) sp[i] = sp_g[i];
     for (int i = tid; i < fs.ng; i += kStreamThreads) iw[i] = iw_g[i];
-    if (tid == 0) { s_mn = 0xFFFFFFFFu; s_mx = 0u; s_nan = 0; s_mxb = 0ull; }
+    for (int i = tid; i < nb; i += kStreamThreads) lcnt[i] = 0u;
+    if (tid == 0) { s_qn = 0u; s_nan = 0; }
     fs.sp = sp; fs.iw = iw; fs.bucket_cnt = bucket_cnt; fs.bucket_vals = bucket_vals;
     __syncthreads();
 
+    // Per score: one exponential, e = e^{-|r - edge|/t} with edge a_L below the
+    // band and a_R otherwise; it feeds S_L (below) or S_R (at/above a_R).
+    // Only the count at/above a_R is kept: the count below follows from
+    // n - band - above - NaNs.  Band scores (rare) go to an LDS queue with one
+    // LDS atomic per wave; NaNs land there too and are sorted out at the
+    // flush; +-inf shows up in max |r|.
     double SL = 0.0, SR = 0.0, BL = 0.0, BR = 0.0;
-    unsigned long long cLw = 0ull, cRw = 0ull;  // wave totals from ballots (same in every lane)
-    unsigned long long cLl = 0ull, cRl = 0ull;  // this lane's own counts (tail and scalar path)
-    float mn = INFINITY, mx = -INFINITY;
-    int nan = 0, ovf = 0;
+    uint32_t cR = 0u;
+    uint32_t nnan = 0u;
+    float amax = 0.0f;
+    int nan = 0;
     const float aL = fs.aL, aR = fs.aR;
 
-    // one score, every lane of the wave active (ballots are wave-wide)
-    auto elem = [&](float v, float& eL, float& eR) {
+    auto one = [&](float v, float& eL, float& eR, bool& band) {
         const bool below = v < aL;
         const bool above = v >= aR;
         const float e = __builtin_amdgcn_exp2f(-fabsf(v - (below ? aL : aR)) * ls);
         eL += below ? e : 0.0f;
         eR += above ? e : 0.0f;
-        mn = fminf(mn, v);
-        mx = fmaxf(mx, v);
-        cLw += (unsigned long long)popc64(ballot(below));
-        cRw += (unsigned long long)popc64(ballot(above));
-        const bool band = !(below || above);
-        if (ballot(band)) {
-            if (band) {
-                BR += (double)e;
-                filter_band(fs, v, BL, nan, ovf);
-            }
-        }
+        cR += above ? 1u : 0u;
+        amax = fmaxf(amax, fabsf(v));
+        band = !(below || above);
     };
-    // one score, per-lane bookkeeping (no ballots)
-    auto elem_lane = [&](float v) {
-        const bool below = v < aL;
-        const bool above = v >= aR;
-        const float e = __builtin_amdgcn_exp2f(-fabsf(v - (below ? aL : aR)) * ls);
-        if (below) SL += (double)e;
-        if (above) SR += (double)e;
-        mn = fminf(mn, v);
-        mx = fmaxf(mx, v);
-        cLl += below;
-        cRl += above;
-        if (!(below || above)) { BR += (double)e; filter_band(fs, v, BL, nan, ovf); }
+    auto put = [&](float v, uint32_t pos) {
+        if (pos < (uint32_t)kQueueCap) q[pos] = v;
+        else band_direct(fs, v, BL, BR, nan, nnan);
     };
-    auto quad = [&](float4 q) {
+    // four scores, all lanes of the wave active; the band scores among them
+    // (rare) take one LDS atomic for the whole wave
+    auto quad = [&](float4 qv) {
         float eL = 0.0f, eR = 0.0f;
-        elem(q.x, eL, eR);
-        elem(q.y, eL, eR);
-        elem(q.z, eL, eR);
-        elem(q.w, eL, eR);
+        bool b0, b1, b2, b3;
+        one(qv.x, eL, eR, b0);
+        one(qv.y, eL, eR, b1);
+        one(qv.z, eL, eR, b2);
+        one(qv.w, eL, eR, b3);
         SL += (double)eL;
         SR += (double)eR;
+        const unsigned long long m0 = ballot(b0), m1 = ballot(b1), m2 = ballot(b2), m3 = ballot(b3);
+        if (m0 | m1 | m2 | m3) {
+            const uint32_t c0 = (uint32_t)popc64(m0), c1 = (uint32_t)popc64(m1), c2 = (uint32_t)popc64(m2);
+            const uint32_t tot = c0 + c1 + c2 + (uint32_t)popc64(m3);
+            uint32_t base = 0u;
+            if (lane == 0) base = atomicAdd(&s_qn, tot);
+            base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+            if (b0) put(qv.x, base + (uint32_t)mbcnt(m0));
+            if (b1) put(qv.y, base + c0 + (uint32_t)mbcnt(m1));
+            if (b2) put(qv.z, base + c0 + c1 + (uint32_t)mbcnt(m2));
+            if (b3) put(qv.w, base + c0 + c1 + c2 + (uint32_t)mbcnt(m3));
+        }
+    };
+    // one score, no wave-wide operations
+    auto one_lane = [&](float v) {
+        float eL = 0.0f, eR = 0.0f;
+        bool band;
+        one(v, eL, eR, band);
+        SL += (double)eL;
+        SR += (double)eR;
+        if (band) band_direct(fs, v, BL, BR, nan, nnan);
     };
 
-    const long long stride = (long long)gridDim.x * kStreamThreads;
-    const long long gt = (long long)blockIdx.x * kStreamThreads + tid;
     if (VEC) {
         const long long n4 = n >> 2;
-        const float4* r4 = reinterpret_cast<const float4*>(r);
-        long long i = gt;
-        // main loop: the trip test uses the wave's last lane, so the whole wave
-        // iterates together and the ballot counts see every lane
-        const long long to_last_lane = 63 - lane_id();
-        for (; i + to_last_lane + 3 * stride < n4; i += 4 * stride) {
-            const float4 q0 = r4[i], q1 = r4[i + stride], q2 = r4[i + 2 * stride], q3 = r4[i + 3 * stride];
-            quad(q0); quad(q1); quad(q2); quad(q3);
-        }
-        for (; i < n4; i += stride) {
-            const float4 q = r4[i];
-            elem_lane(q.x); elem_lane(q.y); elem_lane(q.z); elem_lane(q.w);
-        }
+        stream_f4<4, kFilterNT>(reinterpret_cast<const float4*>(r), n4, false,
+                     [&](float4 qv, long long) { quad(qv); },
+                     [&](float4 qv, long long) { one_lane(qv.x); one_lane(qv.y); one_lane(qv.z); one_lane(qv.w); });
         if (blockIdx.x == 0 && tid < 4) {
             const long long j = (n4 << 2) + tid;
-            if (j < n) elem_lane(r[j]);
+            if (j < n) one_lane(r[j]);
         }
     } else {
-        for (long long i = gt; i < n; i += stride) elem_lane(r[i]);
+        const long long stride = (long long)gridDim.x * kStreamThreads;
+        for (long long i = (long long)blockIdx.x * kStreamThreads + tid; i < n; i += stride) one_lane(r[i]);
     }
-    (void)ovf;  // per-bucket overflow is decided from the bucket counts below
 
-    // ---- workgroup reduction (fixed order) ----
-    const unsigned long long myL = cLl + (lane_id() == 0 ? cLw : 0ull);
-    const unsigned long long myR = cRl + (lane_id() == 0 ? cRw : 0ull);
+    // ---- flush the LDS queue: bucket by value, one global atomic per bucket ----
+    __syncthreads();
+    const uint32_t nq = min(s_qn, (uint32_t)kQueueCap);
+    constexpr int QPT = kQueueCap / kStreamThreads;
+    int bk[QPT];
+    uint32_t rk[QPT];
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) {
+        const uint32_t i = (uint32_t)tid + (uint32_t)k * kStreamThreads;
+        bk[k] = -1;
+        if (i < nq) {
+            const float v = q[i];
+            if (v != v) { nan = 1; ++nnan; continue; }
+            band_sums(fs, v, BL, BR);
+            bk[k] = band_bucket(fs, v);
+            rk[k] = atomicAdd(&lcnt[bk[k]], 1u);
+        }
+    }
+    __syncthreads();
+    for (int j = tid; j < nb; j += kStreamThreads) {
+        const uint32_t c = lcnt[j];
+        gbase[j] = c ? atomicAdd(&bucket_cnt[j], c) : 0u;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) {
+        if (bk[k] >= 0) {
+            const uint32_t i = (uint32_t)tid + (uint32_t)k * kStreamThreads;
+            const uint32_t pos = gbase[bk[k]] + rk[k];
+            if (pos < (uint32_t)cap) bucket_vals[(size_t)bk[k] * (size_t)cap + pos] = __float_as_uint(q[i]);
+        }
+    }
+
+    // ---- workgroup partials (fixed-order reduction; reduced by k_filter_finalize) ----
     const double tS0 = block_sum<kStreamThreads>(SL, s_red);
     const double tS1 = block_sum<kStreamThreads>(SR, s_red);
     const double tS2 = block_sum<kStreamThreads>(BL, s_red);
     const double tS3 = block_sum<kStreamThreads>(BR, s_red);
-    const unsigned long long tcL = block_sum_u64<kStreamThreads>(myL, s_redu);
-    const unsigned long long tcR = block_sum_u64<kStreamThreads>(myR, s_redu);
-    if (mn <= mx) { atomicMin(&s_mn, f2key(mn)); atomicMax(&s_mx, f2key(mx)); }
+    const unsigned long long tcR = block_sum_u64<kStreamThreads>((unsigned long long)cR, s_redu);
+    const unsigned long long tnan = block_sum_u64<kStreamThreads>((unsigned long long)nnan, s_redu);
     if (nan) atomicOr(&s_nan, 1);
+    __shared__ float s_amax;
+    if (tid == 0) s_amax = 0.0f;
+    __syncthreads();
+    atomicMax(reinterpret_cast<unsigned int*>(&s_amax), __float_as_uint(amax));  // |v| >= 0: uint order = float order
     __syncthreads();
     if (tid == 0) {
         FilterPart& fp = part[blockIdx.x];
         fp.S[0] = tS0; fp.S[1] = tS1; fp.S[2] = tS2; fp.S[3] = tS3;
-        fp.c[0] = tcL; fp.c[1] = tcR;
-        fp.mn = (s_mn == 0xFFFFFFFFu) ? INFINITY : key2f(s_mn);
-        fp.mx = (s_mx == 0u) ? -INFINITY : key2f(s_mx);
+        fp.c[0] = tnan; fp.c[1] = tcR;
+        fp.mn = 0.0f;
+        fp.mx = s_amax;
         fp.nan = s_nan;
     }
-    if (!last_block_ticket(&ctl->done[kDoneFilter], &s_last)) return;
+}
 
-    // ---- last workgroup: totals in a fixed order, bucket statistics, hand-off ----
-    if (tid == 0) { s_mn = 0xFFFFFFFFu; s_mx = 0u; s_nan = 0; }
+// one workgroup: totals of the filter's partials in a fixed order, band
+// statistics from the bucket counters, hand-off to the host
+__global__ __launch_bounds__(kStreamThreads) void k_filter_finalize(const FilterPart* part, int nparts, long long n,
+                                                                     Ctl* ctl, const uint32_t* bucket_cnt, int cap,
+                                                                     HostSummary* hs, unsigned int seq) {
+    __shared__ double s_red[kStreamThreads / 64];
+    __shared__ unsigned long long s_redu[kStreamThreads / 64];
+    __shared__ unsigned int s_amax;
+    __shared__ int s_nan;
+    __shared__ unsigned long long s_mxb;
+    const int tid = threadIdx.x;
+    if (tid == 0) { s_amax = 0u; s_nan = 0; s_mxb = 0ull; }
     __syncthreads();
+    // every load first (one memory round trip), then combine in a fixed order
+    constexpr int PP = kMaxStreamBlocks / kStreamThreads;
+    FilterPart fp[PP];
+#pragma unroll
+    for (int q = 0; q < PP; ++q) {
+        const int b = tid + q * kStreamThreads;
+        if (b < nparts) fp[q] = part[b];
+    }
+    uint32_t bc = 0u;
+    if (tid < ctl->nb) bc = bucket_cnt[tid];
     double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
     unsigned long long u0 = 0ull, u1 = 0ull;
-    for (unsigned b = tid; b < gridDim.x; b += kStreamThreads) {
-        const FilterPart& fp = part[b];
-        a0 += fp.S[0]; a1 += fp.S[1]; a2 += fp.S[2]; a3 += fp.S[3];
-        u0 += fp.c[0]; u1 += fp.c[1];
-        if (fp.nan) atomicOr(&s_nan, 1);
-        if (fp.mn <= fp.mx) { atomicMin(&s_mn, f2key(fp.mn)); atomicMax(&s_mx, f2key(fp.mx)); }
+    int anynan = 0;
+    float amx = 0.0f;
+#pragma unroll
+    for (int q = 0; q < PP; ++q) {
+        const int b = tid + q * kStreamThreads;
+        if (b < nparts) {
+            a0 += fp[q].S[0]; a1 += fp[q].S[1]; a2 += fp[q].S[2]; a3 += fp[q].S[3];
+            u0 += fp[q].c[0]; u1 += fp[q].c[1];
+            anynan |= fp[q].nan;
+            amx = fmaxf(amx, fp[q].mx);
+        }
     }
+    if (anynan) atomicOr(&s_nan, 1);
+    atomicMax(&s_amax, __float_as_uint(amx));
     const double T0 = block_sum<kStreamThreads>(a0, s_red);
     const double T1 = block_sum<kStreamThreads>(a1, s_red);
     const double T2 = block_sum<kStreamThreads>(a2, s_red);
     const double T3 = block_sum<kStreamThreads>(a3, s_red);
-    const unsigned long long U0 = block_sum_u64<kStreamThreads>(u0, s_redu);
-    const unsigned long long U1 = block_sum_u64<kStreamThreads>(u1, s_redu);
-    unsigned long long mloc = 0ull, mxb = 0ull;
+    const unsigned long long NAN_ = block_sum_u64<kStreamThreads>(u0, s_redu);
+    const unsigned long long CR = block_sum_u64<kStreamThreads>(u1, s_redu);
     const int nb = ctl->nb;
-    for (int b = tid; b < nb; b += kStreamThreads) {
-        const unsigned long long c = bucket_cnt[b];
-        mloc += c;
-        mxb = c > mxb ? c : mxb;
-    }
-    const unsigned long long M = block_sum_u64<kStreamThreads>(mloc, s_redu);
-    atomicMax(&s_mxb, mxb);
+    const unsigned long long M = block_sum_u64<kStreamThreads>((unsigned long long)bc, s_redu);
+    atomicMax(&s_mxb, (unsigned long long)bc);
     __syncthreads();
     if (tid == 0) {
         int flags = 0;
-        const float gmn = (s_mn == 0xFFFFFFFFu) ? INFINITY : key2f(s_mn);
-        const float gmx = (s_mx == 0u) ? -INFINITY : key2f(s_mx);
-        if (s_nan || !finite_f(gmn) || !finite_f(gmx)) flags |= kFlagNonFinite;
+        if (s_nan || !finite_f(__uint_as_float(s_amax))) flags |= kFlagNonFinite;
         if (s_mxb > (unsigned long long)cap) flags |= kFlagOverflow;
+        const unsigned long long CL = (unsigned long long)n - M - CR - NAN_;
         ctl->S_L = T0; ctl->S_R = T1; ctl->B_L = T2; ctl->B_R = T3;
-        ctl->c_L = U0; ctl->c_R = U1; ctl->m = M;
+        ctl->c_L = CL; ctl->c_R = CR; ctl->m = M;
         ctl->flags = flags;
-        ctl->done[kDoneFilter] = 0u;
         if (hs) {
-            hs->c_L = U0; hs->m = M; hs->c_R = U1;
+            hs->c_L = CL; hs->m = M; hs->c_R = CR;
             hs->S_L = T0; hs->S_R = T1; hs->B_L = T2; hs->B_R = T3;
-            hs->aL = fs.aL; hs->aR = fs.aR;
+            hs->aL = ctl->aL; hs->aR = ctl->aR;
             hs->flags = flags; hs->nb = nb; hs->max_bucket = s_mxb;
             __threadfence_system();
             hs->seq = seq;
@@ -249,10 +327,12 @@ void launch_filter(const float* r, long long n, double t, Ctl* ctl, const float*
     FilterPart* fp = reinterpret_cast<FilterPart*>(part);
     if ((reinterpret_cast<uintptr_t>(r) & 15u) == 0u)
         hipLaunchKernelGGL(k_filter<true>, dim3(blocks), dim3(kStreamThreads), 0, st, r, n, ls, ctl, sp, iw,
-                           bucket_cnt, bucket_vals, cap, fp, hs_dev, seq);
+                           bucket_cnt, bucket_vals, cap, fp);
     else
         hipLaunchKernelGGL(k_filter<false>, dim3(blocks), dim3(kStreamThreads), 0, st, r, n, ls, ctl, sp, iw,
-                           bucket_cnt, bucket_vals, cap, fp, hs_dev, seq);
+                           bucket_cnt, bucket_vals, cap, fp);
+    hipLaunchKernelGGL(k_filter_finalize, dim3(1), dim3(kStreamThreads), 0, st, fp, blocks, n, ctl, bucket_cnt, cap,
+                       hs_dev, seq);
 }
 
 // ---------------------------------------------------------------------------
@@ -265,9 +345,8 @@ LS_DEV float lap_cdf_f(float x) {
 
 template <bool VEC>
 __global__ __launch_bounds__(kStreamThreads) void k_probs(const float* __restrict__ r, long long n, double inv_t,
-                                                           float* __restrict__ p, Ctl* ctl, double* part) {
+                                                           float* __restrict__ p, const Ctl* ctl, double* part, int rev) {
     __shared__ double s_red[kStreamThreads / 64];
-    __shared__ int s_last;
     const double b = ctl->b;
     const int tid = threadIdx.x;
     double sum = 0.0;
@@ -281,20 +360,9 @@ __global__ __launch_bounds__(kStreamThreads) void k_probs(const float* __restric
     };
     if (VEC) {
         const long long n4 = n >> 2;
-        const float4* r4 = reinterpret_cast<const float4*>(r);
         float4* p4 = reinterpret_cast<float4*>(p);
-        long long i = gt;
-        for (; i + 3 * stride < n4; i += 4 * stride) {
-            const float4 q0 = r4[i], q1 = r4[i + stride], q2 = r4[i + 2 * stride], q3 = r4[i + 3 * stride];
-            p4[i] = make_float4(one(q0.x), one(q0.y), one(q0.z), one(q0.w));
-            p4[i + stride] = make_float4(one(q1.x), one(q1.y), one(q1.z), one(q1.w));
-            p4[i + 2 * stride] = make_float4(one(q2.x), one(q2.y), one(q2.z), one(q2.w));
-            p4[i + 3 * stride] = make_float4(one(q3.x), one(q3.y), one(q3.z), one(q3.w));
-        }
-        for (; i < n4; i += stride) {
-            const float4 q = r4[i];
-            p4[i] = make_float4(one(q.x), one(q.y), one(q.z), one(q.w));
-        }
+        auto body = [&](float4 q, long long idx) { p4[idx] = make_float4(one(q.x), one(q.y), one(q.z), one(q.w)); };
+        stream_f4<4>(reinterpret_cast<const float4*>(r), n4, rev != 0, body, body);
         if (blockIdx.x == 0) {
             const long long j = (n4 << 2) + tid;
             if (tid < 4 && j < n) p[j] = one(r[j]);
@@ -304,20 +372,29 @@ __global__ __launch_bounds__(kStreamThreads) void k_probs(const float* __restric
     }
     const double tot = block_sum<kStreamThreads>(sum, s_red);
     if (tid == 0) part[blockIdx.x] = tot;
-    if (!last_block_ticket(&ctl->done[kDoneProbs], &s_last)) return;
+}
+
+// sum of the p pass's partials (for statistics only)
+__global__ __launch_bounds__(kStreamThreads) void k_sum_partials(const double* part, int nparts, double* out) {
+    __shared__ double s_red[kStreamThreads / 64];
     double a = 0.0;
-    for (unsigned bb = tid; bb < gridDim.x; bb += kStreamThreads) a += part[bb];
+    for (int b = threadIdx.x; b < nparts; b += kStreamThreads) a += part[b];
     const double T = block_sum<kStreamThreads>(a, s_red);
-    if (tid == 0) { ctl->sum_p = T; ctl->done[kDoneProbs] = 0u; }
+    if (threadIdx.x == 0) *out = T;
+}
+
+void launch_sum_p(Ctl* ctl, const double* part, long long n, hipStream_t st) {
+    hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(kStreamThreads), 0, st, part, stream_blocks(n), &ctl->sum_p);
 }
 
 void launch_probs(const float* r, long long n, double t, float* p, Ctl* ctl, double* part, hipStream_t st) {
     const int blocks = stream_blocks(n);
     const bool vec = ((reinterpret_cast<uintptr_t>(r) | reinterpret_cast<uintptr_t>(p)) & 15u) == 0u;
     if (vec)
-        hipLaunchKernelGGL(k_probs<true>, dim3(blocks), dim3(kStreamThreads), 0, st, r, n, 1.0 / t, p, ctl, part);
+        hipLaunchKernelGGL(k_probs<true>, dim3(blocks), dim3(kStreamThreads), 0, st, r, n, 1.0 / t, p, ctl, part,
+                           kProbsReverse);
     else
-        hipLaunchKernelGGL(k_probs<false>, dim3(blocks), dim3(kStreamThreads), 0, st, r, n, 1.0 / t, p, ctl, part);
+        hipLaunchKernelGGL(k_probs<false>, dim3(blocks), dim3(kStreamThreads), 0, st, r, n, 1.0 / t, p, ctl, part, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -328,9 +405,8 @@ LS_DEV float lap_pdf_f(float x) { return 0.5f * __builtin_amdgcn_exp2f(-fabsf(x)
 template <bool VEC>
 __global__ __launch_bounds__(kStreamThreads) void k_vjp_reduce(const float* __restrict__ r, const float* __restrict__ g,
                                                                 long long n, const double* bptr, double inv_t,
-                                                                Ctl* ctl, double* part) {
+                                                                double* part) {
     __shared__ double s_red[kStreamThreads / 64];
-    __shared__ int s_last;
     const double b = *bptr;
     const int tid = threadIdx.x;
     double sfg = 0.0, sf = 0.0;
@@ -346,15 +422,9 @@ __global__ __launch_bounds__(kStreamThreads) void k_vjp_reduce(const float* __re
     };
     if (VEC) {
         const long long n4 = n >> 2;
-        const float4* r4 = reinterpret_cast<const float4*>(r);
-        const float4* g4 = reinterpret_cast<const float4*>(g);
-        long long i = gt;
-        for (; i + 1 * stride < n4; i += 2 * stride) {
-            const float4 q0 = r4[i], q1 = r4[i + stride];
-            const float4 h0 = g4[i], h1 = g4[i + stride];
-            quad(q0, h0); quad(q1, h1);
-        }
-        for (; i < n4; i += stride) quad(r4[i], g4[i]);
+        auto body = [&](float4 q, float4 gg, long long) { quad(q, gg); };
+        stream_f4x2<4, kReduceNT>(reinterpret_cast<const float4*>(r), reinterpret_cast<const float4*>(g), n4, false, body,
+                                  body);
         if (blockIdx.x == 0) {
             const long long j = (n4 << 2) + tid;
             if (tid < 4 && j < n) {
@@ -371,15 +441,6 @@ __global__ __launch_bounds__(kStreamThreads) void k_vjp_reduce(const float* __re
     const double t0 = block_sum<kStreamThreads>(sfg, s_red);
     const double t1 = block_sum<kStreamThreads>(sf, s_red);
     if (tid == 0) { part[2 * blockIdx.x] = t0; part[2 * blockIdx.x + 1] = t1; }
-    if (!last_block_ticket(&ctl->done[kDoneVjp], &s_last)) return;
-    double a0 = 0.0, a1 = 0.0;
-    for (unsigned bb = tid; bb < gridDim.x; bb += kStreamThreads) { a0 += part[2 * bb]; a1 += part[2 * bb + 1]; }
-    const double T0 = block_sum<kStreamThreads>(a0, s_red);
-    const double T1 = block_sum<kStreamThreads>(a1, s_red);
-    if (tid == 0) {
-        ctl->sumfg = T0; ctl->sumf = T1; ctl->c = T0 / T1;
-        ctl->done[kDoneVjp] = 0u;
-    }
 }
 
 // f/t = e^{-|x|}/(2t) evaluated as one exp2 with log2(1/(2t)) folded into the
@@ -390,10 +451,33 @@ __global__ __launch_bounds__(kStreamThreads) void k_vjp_reduce(const float* __re
 template <bool VEC>
 __global__ __launch_bounds__(kStreamThreads) void k_vjp_apply(const float* __restrict__ r, const float* __restrict__ g,
                                                                long long n, const double* bptr, double inv_t,
-                                                               float log2_inv_2t, const Ctl* ctl,
-                                                               float* __restrict__ grad) {
+                                                               float log2_inv_2t, const double* part, int nparts,
+                                                               Ctl* ctl, float* __restrict__ grad, int rev) {
+    __shared__ double s_red[kStreamThreads / 64];
+    __shared__ double s_c;
+    // every workgroup forms c = sum f g / sum f from the reduce pass's partials
+    // in the same fixed order, so all of them use the identical c
+    {
+        constexpr int PP = kMaxStreamBlocks / kStreamThreads;
+        double2 pv[PP];
+#pragma unroll
+        for (int q = 0; q < PP; ++q) {
+            const int bb = threadIdx.x + q * kStreamThreads;
+            pv[q] = bb < nparts ? reinterpret_cast<const double2*>(part)[bb] : make_double2(0.0, 0.0);
+        }
+        double a0 = 0.0, a1 = 0.0;
+#pragma unroll
+        for (int q = 0; q < PP; ++q) { a0 += pv[q].x; a1 += pv[q].y; }
+        const double T0 = block_sum<kStreamThreads>(a0, s_red);
+        const double T1 = block_sum<kStreamThreads>(a1, s_red);
+        if (threadIdx.x == 0) {
+            s_c = T0 / T1;
+            if (blockIdx.x == 0) { ctl->sumfg = T0; ctl->sumf = T1; ctl->c = T0 / T1; }
+        }
+        __syncthreads();
+    }
     const double b = *bptr;
-    const float c = (float)ctl->c;
+    const float c = (float)s_c;
     const long long stride = (long long)gridDim.x * kStreamThreads;
     const long long gt = (long long)blockIdx.x * kStreamThreads + threadIdx.x;
     auto one = [&](float v, float gv) -> float {
@@ -403,20 +487,11 @@ __global__ __launch_bounds__(kStreamThreads) void k_vjp_apply(const float* __res
     };
     if (VEC) {
         const long long n4 = n >> 2;
-        const float4* r4 = reinterpret_cast<const float4*>(r);
-        const float4* g4 = reinterpret_cast<const float4*>(g);
         float4* o4 = reinterpret_cast<float4*>(grad);
-        long long i = gt;
-        for (; i + 1 * stride < n4; i += 2 * stride) {
-            const float4 q0 = r4[i], q1 = r4[i + stride];
-            const float4 h0 = g4[i], h1 = g4[i + stride];
-            o4[i] = make_float4(one(q0.x, h0.x), one(q0.y, h0.y), one(q0.z, h0.z), one(q0.w, h0.w));
-            o4[i + stride] = make_float4(one(q1.x, h1.x), one(q1.y, h1.y), one(q1.z, h1.z), one(q1.w, h1.w));
-        }
-        for (; i < n4; i += stride) {
-            const float4 q = r4[i], h = g4[i];
-            o4[i] = make_float4(one(q.x, h.x), one(q.y, h.y), one(q.z, h.z), one(q.w, h.w));
-        }
+        auto body = [&](float4 q, float4 h, long long idx) {
+            o4[idx] = make_float4(one(q.x, h.x), one(q.y, h.y), one(q.z, h.z), one(q.w, h.w));
+        };
+        stream_f4x2<2>(reinterpret_cast<const float4*>(r), reinterpret_cast<const float4*>(g), n4, rev != 0, body, body);
         if (blockIdx.x == 0) {
             const long long j = (n4 << 2) + threadIdx.x;
             if (threadIdx.x < 4 && j < n) grad[j] = one(r[j], g[j]);
@@ -432,14 +507,14 @@ void launch_vjp(const float* r, const float* g, long long n, double t, const dou
     const bool vec = ((reinterpret_cast<uintptr_t>(r) | reinterpret_cast<uintptr_t>(g) |
                        reinterpret_cast<uintptr_t>(grad)) & 15u) == 0u;
     const double inv_t = 1.0 / t;
-    if (vec) hipLaunchKernelGGL(k_vjp_reduce<true>, dim3(blocks), dim3(kStreamThreads), 0, st, r, g, n, b, inv_t, ctl, part);
-    else hipLaunchKernelGGL(k_vjp_reduce<false>, dim3(blocks), dim3(kStreamThreads), 0, st, r, g, n, b, inv_t, ctl, part);
+    if (vec) hipLaunchKernelGGL(k_vjp_reduce<true>, dim3(blocks), dim3(kStreamThreads), 0, st, r, g, n, b, inv_t, part);
+    else hipLaunchKernelGGL(k_vjp_reduce<false>, dim3(blocks), dim3(kStreamThreads), 0, st, r, g, n, b, inv_t, part);
     if (ev_mid) (void)hipEventRecord(*ev_mid, st);
     const float l2 = (float)(std::log2(0.5 * inv_t) + 32.0);
     if (vec) hipLaunchKernelGGL(k_vjp_apply<true>, dim3(blocks), dim3(kStreamThreads), 0, st, r, g, n, b, inv_t, l2,
-                                ctl, grad);
+                                part, blocks, ctl, grad, kApplyReverse);
     else hipLaunchKernelGGL(k_vjp_apply<false>, dim3(blocks), dim3(kStreamThreads), 0, st, r, g, n, b, inv_t, l2,
-                            ctl, grad);
+                            part, blocks, ctl, grad, 0);
 }
 
 // ---------------------------------------------------------------------------
