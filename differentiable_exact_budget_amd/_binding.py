@@ -126,7 +126,7 @@ def lib():
                                      ctypes.POINTER(ctypes.c_int32), vp]
     L.lapsum_test_select.restype = ctypes.c_int
     L.lapsum_test_filter.argtypes = [vp, i64, f32, f32, f32, ctypes.POINTER(i64), ctypes.POINTER(f64), vp, i64,
-                                     ctypes.POINTER(i64), vp]
+                                     ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(i64), vp]
     L.lapsum_test_filter.restype = ctypes.c_int
     _lib = L
     return L

@@ -116,44 +116,84 @@ LS_DEV void bwd_combine(float& k, double& v, float rk, double rv, double inv_t) 
     if (rv != 0.0) v += ecoef(((double)k - (double)rk) * inv_t) * rv;
 }
 
-// exclusive scans over the NT threads of the workgroup (Hillis-Steele in LDS)
+// exclusive scans of carries over the NT threads of the workgroup: shuffles
+// inside each wave, then the wave totals scanned by wave 0 through LDS
+// (sk, sv: >= NT/64 entries)
 template <int NT>
 LS_DEV void block_scan_fwd_excl(float& k, double& v, float* sk, double* sv, double inv_t) {
-    const int tid = threadIdx.x;
-    sk[tid] = k; sv[tid] = v;
-    __syncthreads();
-    for (int o = 1; o < NT; o <<= 1) {
-        float lk = -INFINITY; double lv = 0.0;
-        const bool has = tid >= o;
-        if (has) { lk = sk[tid - o]; lv = sv[tid - o]; }
+    constexpr int NW = NT / 64;
+    const int lane = lane_id(), w = threadIdx.x >> 6;
+    float ik = k; double iv = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const float lk = __shfl_up(ik, o, 64);
+        const double lv = __shfl_up(iv, o, 64);
+        if (lane >= o) fwd_combine(lk, lv, ik, iv, inv_t);
+    }
+    float ek = __shfl_up(ik, 1, 64);
+    double ev = __shfl_up(iv, 1, 64);
+    if (lane == 0) { ek = -INFINITY; ev = 0.0; }
+    if (NW > 1) {
+        if (lane == 63) { sk[w] = ik; sv[w] = iv; }
         __syncthreads();
-        if (has) fwd_combine(lk, lv, k, v, inv_t);
-        sk[tid] = k; sv[tid] = v;
+        if (w == 0) {
+            float tk = lane < NW ? sk[lane] : -INFINITY;
+            double tv = lane < NW ? sv[lane] : 0.0;
+#pragma unroll
+            for (int o = 1; o < NW; o <<= 1) {
+                const float lk = __shfl_up(tk, o, 64);
+                const double lv = __shfl_up(tv, o, 64);
+                if (lane >= o) fwd_combine(lk, lv, tk, tv, inv_t);
+            }
+            float xk = __shfl_up(tk, 1, 64);
+            double xv = __shfl_up(tv, 1, 64);
+            if (lane == 0) { xk = -INFINITY; xv = 0.0; }
+            if (lane < NW) { sk[lane] = xk; sv[lane] = xv; }
+        }
+        __syncthreads();
+        const float pk = sk[w];
+        const double pv = sv[w];
+        fwd_combine(pk, pv, ek, ev, inv_t);
         __syncthreads();
     }
-    float ek = -INFINITY; double ev = 0.0;
-    if (tid > 0) { ek = sk[tid - 1]; ev = sv[tid - 1]; }
-    __syncthreads();
     k = ek; v = ev;
 }
 
 template <int NT>
 LS_DEV void block_scan_bwd_excl(float& k, double& v, float* sk, double* sv, double inv_t) {
-    const int tid = threadIdx.x;
-    sk[tid] = k; sv[tid] = v;
-    __syncthreads();
-    for (int o = 1; o < NT; o <<= 1) {
-        float rk = INFINITY; double rv = 0.0;
-        const bool has = tid + o < NT;
-        if (has) { rk = sk[tid + o]; rv = sv[tid + o]; }
+    constexpr int NW = NT / 64;
+    const int lane = lane_id(), w = threadIdx.x >> 6;
+    float ik = k; double iv = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const float rk = __shfl_down(ik, o, 64);
+        const double rv = __shfl_down(iv, o, 64);
+        if (lane + o < 64) bwd_combine(ik, iv, rk, rv, inv_t);
+    }
+    float ek = __shfl_down(ik, 1, 64);
+    double ev = __shfl_down(iv, 1, 64);
+    if (lane == 63) { ek = INFINITY; ev = 0.0; }
+    if (NW > 1) {
+        if (lane == 0) { sk[w] = ik; sv[w] = iv; }
         __syncthreads();
-        if (has) bwd_combine(k, v, rk, rv, inv_t);
-        sk[tid] = k; sv[tid] = v;
+        if (w == 0) {
+            float tk = lane < NW ? sk[lane] : INFINITY;
+            double tv = lane < NW ? sv[lane] : 0.0;
+#pragma unroll
+            for (int o = 1; o < NW; o <<= 1) {
+                const float rk = __shfl_down(tk, o, 64);
+                const double rv = __shfl_down(tv, o, 64);
+                if (lane + o < NW) bwd_combine(tk, tv, rk, rv, inv_t);
+            }
+            float xk = __shfl_down(tk, 1, 64);
+            double xv = __shfl_down(tv, 1, 64);
+            if (lane + 1 >= NW) { xk = INFINITY; xv = 0.0; }
+            if (lane < NW) { sk[lane] = xk; sv[lane] = xv; }
+        }
+        __syncthreads();
+        bwd_combine(ek, ev, sk[w], sv[w], inv_t);
         __syncthreads();
     }
-    float ek = INFINITY; double ev = 0.0;
-    if (tid + 1 < NT) { ek = sk[tid + 1]; ev = sv[tid + 1]; }
-    __syncthreads();
     k = ek; v = ev;
 }
 
@@ -187,6 +227,9 @@ struct SegView {
     const double* eU;
     const double* eW;
     const uint8_t* wide;
+    // when set, segments hold raw (unsorted) fp32 bit patterns and the root
+    // segment is sorted into this LDS buffer (capacity kBucketCapMax)
+    uint32_t* sortbuf;
 };
 
 struct Tails {
@@ -259,66 +302,74 @@ __device__ SolveOut segment_solve(const SegView sv, const Tails tl, const SolveS
     __shared__ double s_root[4];
     __shared__ int s_owner;
 
-    // ---- phases 1-2 (wave 0): carries before/after every segment, segment ranks ----
-    if (tid < 64) {
-        const int lane = tid;
-        const int per = (nseg + 63) / 64;
-        const int s0 = min(nseg, lane * per), s1 = min(nseg, s0 + per);
-        float ak = -INFINITY; double av = 0.0; uint32_t rc = 0u;
-        for (int sb = s0; sb < s1; sb += SEGB) {
-            uint32_t c[SEGB]; float lst[SEGB]; double pp[SEGB];
-#pragma unroll
-            for (int q = 0; q < SEGB; ++q) {
-                const int s = sb + q;
-                c[q] = s < s1 ? sv.cnt[s] : 0u;
-                lst[q] = s < s1 ? sv.last[s] : 0.0f;
-                pp[q] = s < s1 ? sv.P[s] : 0.0;
+    // ---- phases 1-3: carries before/after every segment, segment ranks, and
+    // G at every segment's first score; each thread owns a contiguous run of
+    // segments (one segment when nseg <= NT, kept in registers) ----
+    const int per = (nseg + NT - 1) / NT;
+    const int s0 = min(nseg, tid * per), s1 = min(nseg, s0 + per);
+    float ak = -INFINITY, bk = INFINITY;
+    double av = 0.0, bvv = 0.0;
+    uint32_t rc = 0u;
+    uint32_t c1 = 0u; float f1 = 0.0f; double Bx1 = 0.0;  // the one segment (per == 1)
+    if (per == 1) {
+        if (s0 < s1) {
+            c1 = sv.cnt[s0];
+            if (c1) {
+                f1 = sv.first[s0]; Bx1 = sv.Bx[s0];
+                ak = sv.last[s0]; av = sv.P[s0];
+                bk = f1; bvv = 1.0 + Bx1;
             }
-#pragma unroll
-            for (int q = 0; q < SEGB; ++q) {
-                if (c[q]) { float lk = ak; double lv = av; ak = lst[q]; av = pp[q]; fwd_combine(lk, lv, ak, av, inv_t); }
-                rc += c[q];
-            }
+            rc = c1;
         }
-        uint32_t rbase = wave_inclusive_scan(rc) - rc;
-        wave_scan_fwd_excl(ak, av, inv_t);
-        {   // the lower tail precedes everything
-            float ck = ak; double cv = av;
-            float tk = -INFINITY; double tv = 0.0;
-            if (tl.S_L > 0.0 && tl.aL > -INFINITY) { tk = tl.aL; tv = tl.S_L; }
-            fwd_combine(tk, tv, ck, cv, inv_t);
-            ak = ck; av = cv;
+    } else {
+        for (int s = s0; s < s1; ++s) {
+            const uint32_t c = sv.cnt[s];
+            if (c) { float lk = ak; double lv = av; ak = sv.last[s]; av = sv.P[s]; fwd_combine(lk, lv, ak, av, inv_t); }
+            rc += c;
         }
-        for (int s = s0; s < s1; ++s) {  // values are cached from the pass above
+        for (int s = s1 - 1; s >= s0; --s) {
+            if (sv.cnt[s]) { float k2 = sv.first[s]; double v2 = 1.0 + sv.Bx[s]; bwd_combine(k2, v2, bk, bvv, inv_t); bk = k2; bvv = v2; }
+        }
+    }
+    uint32_t rbase = block_exclusive_scan<NT>(rc, nullptr, reinterpret_cast<uint32_t*>(s_int));
+    block_scan_fwd_excl<NT>(ak, av, s_k, s_v, inv_t);
+    {   // the lower tail precedes everything
+        float tk = -INFINITY; double tv = 0.0;
+        if (tl.S_L > 0.0 && tl.aL > -INFINITY) { tk = tl.aL; tv = tl.S_L; }
+        fwd_combine(tk, tv, ak, av, inv_t);
+    }
+    block_scan_bwd_excl<NT>(bk, bvv, s_k, s_v, inv_t);
+    if (tl.S_R > 0.0 && tl.aR < INFINITY) bwd_combine(bk, bvv, tl.aR, tl.S_R, inv_t);
+    int cand = -1;
+    auto g_at_first = [&](int s, float f, double Bx, float pk, double pv, float nk, double nv, uint32_t rank) {
+        const double Pf = 1.0 + (pv != 0.0 ? ecoef(((double)pk - (double)f) * inv_t) * pv : 0.0);
+        const double Bf = Bx + (nv != 0.0 ? ecoef(((double)f - (double)nk) * inv_t) * nv : 0.0);
+        sc.bfx[s] = Bf;
+        const double G = 0.5 * Pf + (tl.m - 1.0 - (double)rank) + tl.c_R - 0.5 * Bf;
+        if (G >= tl.k) cand = max(cand, s);
+    };
+    if (per == 1) {
+        if (s0 < s1) {
+            sc.pk[s0] = ak; sc.pv[s0] = av; sc.bk[s0] = bk; sc.bv[s0] = bvv; sc.rank[s0] = rbase;
+            if (c1) g_at_first(s0, f1, Bx1, ak, av, bk, bvv, rbase);
+        }
+    } else {
+        for (int s = s0; s < s1; ++s) {
             const uint32_t c = sv.cnt[s];
             sc.pk[s] = ak; sc.pv[s] = av; sc.rank[s] = rbase;
             rbase += c;
             if (c) { float lk = ak; double lv = av; ak = sv.last[s]; av = sv.P[s]; fwd_combine(lk, lv, ak, av, inv_t); }
         }
-        float bk = INFINITY; double bvv = 0.0;
-        for (int s = s1 - 1; s >= s0; --s) {
-            if (sv.cnt[s]) { float k2 = sv.first[s]; double v2 = 1.0 + sv.Bx[s]; bwd_combine(k2, v2, bk, bvv, inv_t); bk = k2; bvv = v2; }
-        }
-        wave_scan_bwd_excl(bk, bvv, inv_t);
-        if (tl.S_R > 0.0 && tl.aR < INFINITY) bwd_combine(bk, bvv, tl.aR, tl.S_R, inv_t);
         for (int s = s1 - 1; s >= s0; --s) {
             sc.bk[s] = bk; sc.bv[s] = bvv;
-            if (sv.cnt[s]) { float k2 = sv.first[s]; double v2 = 1.0 + sv.Bx[s]; bwd_combine(k2, v2, bk, bvv, inv_t); bk = k2; bvv = v2; }
+            if (sv.cnt[s]) {
+                const float f = sv.first[s]; const double Bx = sv.Bx[s];
+                g_at_first(s, f, Bx, sc.pk[s], sc.pv[s], bk, bvv, sc.rank[s]);
+                float k2 = f; double v2 = 1.0 + Bx; bwd_combine(k2, v2, bk, bvv, inv_t); bk = k2; bvv = v2;
+            }
         }
     }
     __threadfence_block();
-    __syncthreads();
-    // ---- phase 3: G at every segment's first score; last segment with G >= k ----
-    int cand = -1;
-    for (int s = tid; s < nseg; s += NT) {
-        if (!sv.cnt[s]) continue;
-        const float f = sv.first[s];
-        const double Pf = 1.0 + (sc.pv[s] != 0.0 ? ecoef(((double)sc.pk[s] - (double)f) * inv_t) * sc.pv[s] : 0.0);
-        const double Bf = sv.Bx[s] + (sc.bv[s] != 0.0 ? ecoef(((double)f - (double)sc.bk[s]) * inv_t) * sc.bv[s] : 0.0);
-        sc.bfx[s] = Bf;
-        const double G = 0.5 * Pf + (tl.m - 1.0 - (double)sc.rank[s]) + tl.c_R - 0.5 * Bf;
-        if (G >= tl.k) cand = max(cand, s);
-    }
     const int sstar = block_max_int<NT>(cand, s_int);
     __threadfence_block();
     __syncthreads();
@@ -328,16 +379,26 @@ __device__ SolveOut segment_solve(const SegView sv, const Tails tl, const SolveS
     if (sstar >= 0) {
         // ---- phase 4: per-score curve inside the root segment ----
         const uint32_t cS = sv.cnt[sstar], offS = sv.off[sstar], rankS = sc.rank[sstar];
+        const uint32_t* rk = sv.keys + offS;
+        if (sv.sortbuf) {
+            // unsorted segment: sort it in LDS first
+            const int cp = max(next_pow2((int)cS), 64);
+            for (int i = tid; i < cp; i += NT)
+                sv.sortbuf[i] = i < (int)cS ? f2key(__uint_as_float(sv.keys[offS + i])) : 0xFFFFFFFFu;
+            __syncthreads();
+            sort_pow2_lds<NT>(sv.sortbuf, cp);
+            rk = sv.sortbuf;
+        }
         const int E = ((int)cS + NT - 1) / NT;
         const int e0 = min((int)cS, tid * E), e1 = min((int)cS, e0 + E);
         float vv[EMAX];
 #pragma unroll
         for (int q = 0; q < EMAX; ++q) {
             const int j = e0 + q;
-            vv[q] = (j < e1) ? key2f(sv.keys[offS + j]) : 0.0f;
+            vv[q] = (j < e1) ? key2f(rk[j]) : 0.0f;
         }
-        const float vfirst = key2f(sv.keys[offS]);
-        const float vlast = key2f(sv.keys[offS + cS - 1]);
+        const float vfirst = key2f(rk[0]);
+        const float vlast = key2f(rk[cS - 1]);
         const float pk0 = sc.pk[sstar]; const double pv0 = sc.pv[sstar];
         const float bk0 = sc.bk[sstar]; const double bv0 = sc.bv[sstar];
         double Pj[EMAX], Bj[EMAX];
@@ -463,16 +524,17 @@ __device__ SolveOut segment_solve(const SegView sv, const Tails tl, const SolveS
             const double J = (double)(rankS + (uint32_t)jl);
             const double D = (tl.m - 1.0 - J) + tl.c_R - tl.k;
             out.jstar = (long long)(rankS + (uint32_t)jl);
-            int has_next = s_owner;
-            double vnext = s_root[2], Bnext = s_root[3];
-            if (!has_next) {
-                for (int s = sstar + 1; s < nseg; ++s)
-                    if (sv.cnt[s]) { vnext = sv.first[s]; Bnext = sc.bfx[s]; has_next = 1; break; }
-            }
-            if (has_next) { chi = vnext; lnB = (lo - vnext) * inv_t + log1p(Bnext); }
-            else {
-                chi = tl.aR;
-                lnB = (tl.S_R > 0.0 && tl.aR < INFINITY) ? log(tl.S_R) + (lo - (double)tl.aR) * inv_t : -INFINITY;
+            const int has_next = s_owner;
+            if (has_next) {
+                const double vnext = s_root[2], Bnext = s_root[3];
+                chi = vnext; lnB = (lo - vnext) * inv_t + log1p(Bnext);
+            } else if (bv0 != 0.0) {
+                // the backward carry after the root segment: its position is the
+                // next score (first of a later segment, or a_R) and its value the
+                // sum of e^{(position - v)/t} over every score from there up
+                chi = (double)bk0; lnB = (lo - (double)bk0) * inv_t + log(bv0);
+            } else {
+                chi = tl.aR; lnB = -INFINITY;
             }
             const double lnw = log_root(lnA, lnB, D);
             double b = lo + tl.t * lnw;

@@ -11,7 +11,7 @@ namespace lapsum {
 // ---------------------------------------------------------------------------
 constexpr int kStreamThreads = 256;      // streaming kernels (filter, p, VJP)
 constexpr int kMaxStreamBlocks = 2048;   // 256 CUs x 8 resident blocks
-constexpr int kMaxBuckets = 256;         // band buckets
+constexpr int kMaxBuckets = 1024;        // band buckets
 constexpr int kBucketCapMax = 16384;     // band scores per bucket (LDS sort capacity)
 constexpr int kSortThreads = 1024;       // single-workgroup LDS sort / solve
 constexpr int kSortItems = 16;           // keys per thread in the LDS sort
@@ -307,35 +307,182 @@ LS_DEV void bitonic_sort_lds(uint32_t* a, int N) {
     }
 }
 
+// Ascending bitonic sort of N = NT * IPT keys (a power of two) held in LDS.
+// Thread t keeps keys t*IPT .. t*IPT + IPT - 1 in registers: compare-exchanges
+// at strides < IPT stay in registers, strides < 64 * IPT go through wave
+// shuffles, and only wider strides go through LDS (consecutive LDS stages
+// are done between one store and one reload).  With NT = 64 one wave sorts
+// alone (no barrier).  The caller synchronises before reading the result.
+template <int NT, int IPT>
+LS_DEV void bitonic_sort_hybrid(uint32_t* lds) {
+    constexpr int N = NT * IPT;
+    const int tid = threadIdx.x;
+    uint32_t x[IPT];
+#pragma unroll
+    for (int q = 0; q < IPT; ++q) x[q] = lds[tid * IPT + q];
+    for (int size = 2; size <= N; size <<= 1) {
+        int half = size >> 1;
+        if (half >= 64 * IPT) {
+#pragma unroll
+            for (int q = 0; q < IPT; ++q) lds[tid * IPT + q] = x[q];
+            __syncthreads();
+            for (; half >= 64 * IPT; half >>= 1) {
+                for (int t = tid; t < (N >> 1); t += NT) {
+                    const int i = ((t & ~(half - 1)) << 1) | (t & (half - 1));
+                    const int j = i + half;
+                    const bool up = (i & size) == 0;
+                    const uint32_t a = lds[i], b = lds[j];
+                    if ((a > b) == up) { lds[i] = b; lds[j] = a; }
+                }
+                __syncthreads();
+            }
+#pragma unroll
+            for (int q = 0; q < IPT; ++q) x[q] = lds[tid * IPT + q];
+            __syncthreads();
+        }
+        for (; half >= IPT; half >>= 1) {
+            const int lx = half / IPT;  // partner lane distance
+#pragma unroll
+            for (int q = 0; q < IPT; ++q) {
+                const int i = tid * IPT + q;
+                const uint32_t y = (uint32_t)__shfl_xor((int)x[q], lx, 64);
+                const bool up = (i & size) == 0;
+                const bool lower = (i & half) == 0;
+                const uint32_t mn = x[q] < y ? x[q] : y, mx = x[q] < y ? y : x[q];
+                x[q] = (lower == up) ? mn : mx;
+            }
+        }
+        for (; half >= 1; half >>= 1) {
+#pragma unroll
+            for (int q = 0; q < IPT; ++q) {
+                if ((q & half) == 0 && (q | half) < IPT) {
+                    const int i = tid * IPT + q;
+                    const bool up = (i & size) == 0;
+                    const uint32_t a = x[q], b = x[q | half];
+                    if ((a > b) == up) { x[q] = b; x[q | half] = a; }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < IPT; ++q) lds[tid * IPT + q] = x[q];
+}
+
+// Ascending sort of the first N keys of lds (N a power of two, N >= 64) by
+// all NT threads: N <= 512 by wave 0 alone, NT <= N <= 16 NT with the
+// hybrid bitonic sort over the workgroup, anything else with the plain LDS
+// bitonic sort.  Ends with a barrier.
+template <int NT>
+LS_DEV void sort_pow2_lds(uint32_t* lds, int N) {
+    if (N <= 512) {
+        if (threadIdx.x < 64) {
+            if (N == 64) bitonic_sort_hybrid<64, 1>(lds);
+            else if (N == 128) bitonic_sort_hybrid<64, 2>(lds);
+            else if (N == 256) bitonic_sort_hybrid<64, 4>(lds);
+            else bitonic_sort_hybrid<64, 8>(lds);
+        }
+        __syncthreads();
+    } else if (N == NT) { bitonic_sort_hybrid<NT, 1>(lds); __syncthreads(); }
+    else if (N == 2 * NT) { bitonic_sort_hybrid<NT, 2>(lds); __syncthreads(); }
+    else if (N == 4 * NT) { bitonic_sort_hybrid<NT, 4>(lds); __syncthreads(); }
+    else if (N == 8 * NT) { bitonic_sort_hybrid<NT, 8>(lds); __syncthreads(); }
+    else if (N == 16 * NT) { bitonic_sort_hybrid<NT, 16>(lds); __syncthreads(); }
+    else bitonic_sort_lds<NT>(lds, N);
+}
+
 LS_DEV int next_pow2(int x) {
     int p = 1;
     while (p < x) p <<= 1;
     return p;
 }
 
-// additive exclusive scan of double over the workgroup (Hillis-Steele in
-// LDS).  reverse = false: sum over lower thread indices; true: over higher
-// ones.  The exclusive value is read from the neighbour's inclusive sum, never
+// additive exclusive scan of double over the workgroup.  reverse = false:
+// sum over lower thread indices; true: over higher ones.  Shuffles inside
+// each wave, then the wave totals scanned by wave 0 (s: >= NT/64 entries).
+// The exclusive value is read from the neighbour's inclusive sum, never
 // formed as (inclusive - own).
+LS_DEV double wave_scan_add_incl(double v, bool reverse) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const double y = reverse ? __shfl_down(v, o, 64) : __shfl_up(v, o, 64);
+        if (reverse ? (lane + o < 64) : (lane >= o)) v += y;
+    }
+    return v;
+}
+LS_DEV double wave_excl_from_incl(double inc, bool reverse) {
+    const int lane = lane_id();
+    const double e = reverse ? __shfl_down(inc, 1, 64) : __shfl_up(inc, 1, 64);
+    return (reverse ? lane == 63 : lane == 0) ? 0.0 : e;
+}
 template <int NT>
 LS_DEV double block_scan_add_excl(double v, double* s, bool reverse) {
-    const int tid = threadIdx.x;
-    s[tid] = v;
-    __syncthreads();
-    double acc = v;
-    for (int o = 1; o < NT; o <<= 1) {
-        const int src = reverse ? tid + o : tid - o;
-        const bool has = reverse ? (src < NT) : (src >= 0);
-        const double y = has ? s[src] : 0.0;
+    constexpr int NW = NT / 64;
+    const int lane = lane_id(), w = threadIdx.x >> 6;
+    const double inc = wave_scan_add_incl(v, reverse);
+    double ex = wave_excl_from_incl(inc, reverse);
+    if (NW > 1) {
+        if (lane == (reverse ? 0 : 63)) s[w] = inc;
         __syncthreads();
-        acc += y;
-        s[tid] = acc;
+        if (w == 0) {
+            const double x = lane < NW ? s[lane] : 0.0;
+            const double xe = wave_excl_from_incl(wave_scan_add_incl(x, reverse), reverse);
+            if (lane < NW) s[lane] = xe;
+        }
+        __syncthreads();
+        ex = s[w] + ex;
         __syncthreads();
     }
-    const int nb = reverse ? tid + 1 : tid - 1;
-    const double ex = (reverse ? (nb < NT) : (nb >= 0)) ? s[nb] : 0.0;
-    __syncthreads();
     return ex;
+}
+
+// ---------------------------------------------------------------------------
+// 128-bit fixed-point sums of terms in [0, 1] (62 fractional bits): integer
+// addition is associative, so a sum over scores in any order (e.g. the order
+// atomics appended them) is bit-reproducible.  Each term is truncated to
+// 2^-62 (below fp64 summation error).
+// ---------------------------------------------------------------------------
+struct Fx128 { unsigned long long lo, hi; };
+LS_DEV Fx128 fx_zero() { Fx128 r; r.lo = 0ull; r.hi = 0ull; return r; }
+LS_DEV void fx_add_term(Fx128& a, double e) {
+    const unsigned long long x = (unsigned long long)(e * 0x1p62);
+    const unsigned long long lo = a.lo + x;
+    a.hi += (lo < a.lo) ? 1ull : 0ull;
+    a.lo = lo;
+}
+LS_DEV Fx128 fx_add(Fx128 a, Fx128 b) {
+    Fx128 r;
+    r.lo = a.lo + b.lo;
+    r.hi = a.hi + b.hi + ((r.lo < a.lo) ? 1ull : 0ull);
+    return r;
+}
+LS_DEV double fx_to_double(Fx128 a) { return (double)a.hi * 0x1p2 + (double)a.lo * 0x1p-62; }
+// a - 1 (the own term of one score), exact
+LS_DEV Fx128 fx_minus_one(Fx128 a) {
+    Fx128 r;
+    r.lo = a.lo - (1ull << 62);
+    r.hi = a.hi - ((a.lo < (1ull << 62)) ? 1ull : 0ull);
+    return r;
+}
+template <int NT>
+LS_DEV Fx128 block_sum_fx(Fx128 v, unsigned long long* s /* >= 2 * NT/64 */) {
+    constexpr int NW = NT / 64;
+    const int w = threadIdx.x >> 6, l = lane_id();
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        Fx128 y;
+        y.lo = __shfl_xor(v.lo, o, 64);
+        y.hi = __shfl_xor(v.hi, o, 64);
+        v = fx_add(v, y);
+    }
+    if (l == 0) { s[2 * w] = v.lo; s[2 * w + 1] = v.hi; }
+    __syncthreads();
+    Fx128 r = fx_zero();
+    if (w == 0) {
+        for (int q = 0; q < NW; ++q) { Fx128 y; y.lo = s[2 * q]; y.hi = s[2 * q + 1]; r = fx_add(r, y); }
+    }
+    __syncthreads();
+    return r;  // valid in wave 0
 }
 
 // device-scope ticket for the last-workgroup pattern: release this

@@ -61,9 +61,6 @@ struct Workspace {
     float* iw = nullptr;
     uint32_t* bucket_cnt = nullptr;
     uint32_t* bucket_vals = nullptr;
-    double* eU = nullptr;
-    double* eW = nullptr;
-    uint8_t* wide = nullptr;
     SegArrays seg{};
     SolveScratch sc{};
     uint32_t* keysA = nullptr;
@@ -102,9 +99,7 @@ Layout make_layout(long long n_cap) {
     L.iw = take(sizeof(float) * kMaxBuckets);
     L.bcnt = take(sizeof(uint32_t) * kMaxBuckets);
     L.bvals = take(sizeof(uint32_t) * (size_t)kMaxBuckets * kBucketCapMax);
-    L.eU = take(sizeof(double) * (size_t)kMaxBuckets * kBucketCapMax);
-    L.eW = take(sizeof(double) * (size_t)kMaxBuckets * kBucketCapMax);
-    L.wide = take(kMaxBuckets);
+    L.eU = 0; L.eW = 0; L.wide = 0;
     L.seg_first = take(sizeof(float) * nseg);
     L.seg_last = take(sizeof(float) * nseg);
     L.seg_P = take(sizeof(double) * nseg);
@@ -158,9 +153,7 @@ lapsum_status_t alloc_ws(Workspace* w, long long n_cap) {
     w->iw = reinterpret_cast<float*>(base + L.iw);
     w->bucket_cnt = reinterpret_cast<uint32_t*>(base + L.bcnt);
     w->bucket_vals = reinterpret_cast<uint32_t*>(base + L.bvals);
-    w->eU = reinterpret_cast<double*>(base + L.eU);
-    w->eW = reinterpret_cast<double*>(base + L.eW);
-    w->wide = reinterpret_cast<uint8_t*>(base + L.wide);
+
     w->seg = SegArrays{reinterpret_cast<float*>(base + L.seg_first), reinterpret_cast<float*>(base + L.seg_last),
                        reinterpret_cast<double*>(base + L.seg_P), reinterpret_cast<double*>(base + L.seg_Bx),
                        reinterpret_cast<uint32_t*>(base + L.seg_cnt), reinterpret_cast<uint32_t*>(base + L.seg_off)};
@@ -517,8 +510,7 @@ lapsum_status_t forward_impl(const float* r, int64_t n, double k, float t_f, flo
         run_full(w, r, n, k, t, b_out, st, tm);
     } else {
         tm.begin("bucket_solve");
-        launch_bucket_solve(w->bucket_vals, w->bucket_cnt, cap, br.h.nb, w->ctl, w->seg, w->eU, w->eW, w->wide, w->sc, k,
-                            t, b_out, st);
+        launch_bucket_solve(w->bucket_vals, w->bucket_cnt, cap, br.h.nb, w->ctl, w->seg, w->sc, k, t, b_out, st);
         tm.end();
     }
     tm.begin("probs");
@@ -693,7 +685,7 @@ lapsum_status_t lapsum_test_select(const float* x, int64_t s, int64_t l, int64_t
 
 lapsum_status_t lapsum_test_filter(const float* scores, int64_t n, float t, float a_L, float a_R, int64_t* counts_host,
                                    double* sums_host, float* band_out, int64_t band_cap, int64_t* band_size_host,
-                                   lapsum_stream_t stream) {
+                                   int32_t* nbuckets_host, int64_t* bucket_sizes_host, lapsum_stream_t stream) {
     if (!scores || n < 1 || n > 0xFFFFFFFFll || !(t > 0.0f) || !(a_L <= a_R)) return LAPSUM_ERR_INVALID_ARGUMENT;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     Workspace* w = nullptr;
@@ -717,10 +709,7 @@ lapsum_status_t lapsum_test_filter(const float* scores, int64_t n, float t, floa
         if (band_size_host) *band_size_host = -1;
         return LAPSUM_OK;
     }
-    // sort every bucket on the device (the band solve's first stage), then gather in bucket order
-    const double kk = (double)hsum.c_R + 0.5 * (double)hsum.m + 0.25;
-    launch_bucket_solve(w->bucket_vals, w->bucket_cnt, kBucketCapMax, hsum.nb, w->ctl, w->seg, w->eU, w->eW, w->wide,
-                        w->sc, kk > 0 ? kk : 0.5, (double)t, nullptr, st);
+    // gather the band in bucket order (scores inside a bucket are unordered)
     if (hipStreamSynchronize(st) != hipSuccess) return LAPSUM_ERR_HIP;
     std::vector<uint32_t> cnt(kMaxBuckets);
     if (hipMemcpy(cnt.data(), w->bucket_cnt, sizeof(uint32_t) * kMaxBuckets, hipMemcpyDeviceToHost) != hipSuccess)
@@ -728,16 +717,17 @@ lapsum_status_t lapsum_test_filter(const float* scores, int64_t n, float t, floa
     std::vector<float> band;
     band.reserve((size_t)hsum.m);
     std::vector<uint32_t> buf;
+    if (nbuckets_host) *nbuckets_host = hsum.nb;
     for (int b = 0; b < hsum.nb; ++b) {
+        if (bucket_sizes_host) bucket_sizes_host[b] = cnt[b];
         if (!cnt[b]) continue;
         buf.resize(cnt[b]);
         if (hipMemcpy(buf.data(), w->bucket_vals + (size_t)b * kBucketCapMax, sizeof(uint32_t) * cnt[b],
                       hipMemcpyDeviceToHost) != hipSuccess)
             return LAPSUM_ERR_HIP;
-        for (uint32_t kkey : buf) {
-            const uint32_t u = kkey ^ ((kkey >> 31) ? 0x80000000u : 0xFFFFFFFFu);
+        for (uint32_t bits : buf) {
             float f;
-            std::memcpy(&f, &u, 4);
+            std::memcpy(&f, &bits, 4);
             band.push_back(f);
         }
     }

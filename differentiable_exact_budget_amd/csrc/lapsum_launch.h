@@ -36,8 +36,7 @@ void launch_set_nan_b(Ctl* ctl, double* b_out, hipStream_t st);
 void launch_small_solve(const float* r, int n, double k, double t, Ctl* ctl, SolveScratch sc, double* b_out,
                         uint32_t* keys_out, hipStream_t s);
 void launch_bucket_solve(uint32_t* bucket_vals, const uint32_t* bucket_cnt, int cap, int nb, Ctl* ctl, SegArrays seg,
-                         double* eU, double* eW, uint8_t* wide, SolveScratch sc, double k, double t, double* b_out,
-                         hipStream_t s);
+                         SolveScratch sc, double k, double t, double* b_out, hipStream_t s);
 int radix_hist_blocks(long long n);
 void launch_radix_sort(const float* r, long long n, uint32_t* keysA, uint32_t* keysB, uint32_t* hist_part,
                        uint32_t* goff, unsigned long long* status, uint32_t epoch_base, Ctl* ctl, hipStream_t s);

@@ -9,7 +9,7 @@
 //            Random numbers: Philox4x32-10 (Salmon et al., SC'11), counter
 //            (j_lo, j_hi, 0, 0), key (seed_lo, seed_hi).
 //  k_select  one workgroup: a_L = x_(l), a_R = x_(h) by 8-bit MSD radix
-//            select, then up to 256 value-ordered buckets for the band:
+//            select, then up to 1024 value-ordered buckets for the band:
 //            sample values between a_L and a_R as gap splitters, each finite
 //            gap cut into J equal-width sub-buckets.
 #include "lapsum_launch.h"
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(const float* __restri
     const float aL = want_l ? key2f(key_l) : -INFINITY;
     const float aR = want_h ? key2f(key_h) : INFINITY;
 
-    // gaps: ng <= 256, interior splitters evenly spaced over the sorted candidates
+    // gaps: ng <= kMaxBuckets, interior splitters evenly spaced over the sorted candidates
     const int ng = cc >= 2 ? (cc - 1 < kMaxBuckets ? cc - 1 : kMaxBuckets) : 1;
     const int J = kMaxBuckets / ng > 0 ? kMaxBuckets / ng : 1;
     for (int g = tid; g <= ng; g += kSelectThreads) {

@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kSortThreads) void k_small_solve(const float* __res
     segment_aggregates<kSortThreads>(keys, n, inv_t, &sg_first, &sg_last, &sg_P, &sg_Bx, s_red);
     if (tid == 0) { sg_cnt = (uint32_t)n; sg_off = 0u; }
     __syncthreads();
-    SegView sv{1, &sg_first, &sg_last, &sg_P, &sg_Bx, &sg_cnt, &sg_off, keys, nullptr, nullptr, nullptr};
+    SegView sv{1, &sg_first, &sg_last, &sg_P, &sg_Bx, &sg_cnt, &sg_off, keys, nullptr, nullptr, nullptr, nullptr};
     Tails tl{-INFINITY, INFINITY, 0.0, 0.0, (double)n, 0.0, k, t, inv_t};
     SolveOut o = segment_solve<kSortThreads, kSortItems>(sv, tl, sc, s_k, s_v, s_int);
     if (tid == 0) {
@@ -90,100 +90,64 @@ __global__ __launch_bounds__(kSortThreads) void k_small_solve(const float* __res
 }
 
 // ---------------------------------------------------------------------------
-// band buckets: one workgroup per bucket sorts it in LDS and publishes its
-// aggregates and local curve; k_band_root then solves
+// band buckets: the buckets are value-ordered (every score of bucket i is <=
+// every score of bucket i+1), so the curve across buckets only needs, per
+// bucket, its count, minimum, maximum and the two sums
+//   P = sum e^{(v - max)/t},  Bx = sum e^{(min - v)/t} - 1,
+// which do not depend on the order of the scores inside it.  k_bucket_agg
+// forms them (fixed-point sums: bit-reproducible whatever order the filter
+// appended the scores in); k_band_root finds the bucket holding the root,
+// sorts only that one and solves.
 // ---------------------------------------------------------------------------
-// local curve of one sorted segment held in LDS: with ref = v_0 and
-// u_j = e^{(v_j - ref)/t}, eU_j = sum_{i<=j} u_i and eW_j = sum_{i>j} 1/u_i.
-// Only when the segment spans <= 600 t (u <= e^600); otherwise `wide` is set
-// and the aggregates are plain sums.
-template <int NT, int EMAX>
-__device__ void segment_local_curve(const uint32_t* keys, int c, double inv_t, double* eU, double* eW, float* first,
-                                    float* last, double* P, double* Bx, uint8_t* wide, double* s_scan, double* s_red) {
-    const int tid = threadIdx.x;
-    const float f = key2f(keys[0]);
-    const float l = key2f(keys[c - 1]);
-    const bool additive = ((double)l - (double)f) * inv_t <= 600.0;
-    if (additive) {
-        const int E = (c + NT - 1) / NT;
-        const int e0 = min(c, tid * E), e1 = min(c, e0 + E);
-        double u[EMAX];
-        double ut = 0.0, wt = 0.0;
-#pragma unroll
-        for (int q = 0; q < EMAX; ++q) {
-            u[q] = 1.0;
-            if (e0 + q < e1) {
-                u[q] = exp(((double)key2f(keys[e0 + q]) - (double)f) * inv_t);
-                ut += u[q];
-                wt += 1.0 / u[q];
-            }
-        }
-        double U = block_scan_add_excl<NT>(ut, s_scan, false);
-        double W = block_scan_add_excl<NT>(wt, s_scan, true);
-#pragma unroll
-        for (int q = 0; q < EMAX; ++q) {
-            if (e0 + q < e1) {
-                U += u[q];
-                eU[e0 + q] = U;
-                if (e0 + q == c - 1) { *P = U / u[q]; *last = l; }
-            }
-        }
-#pragma unroll
-        for (int q = EMAX - 1; q >= 0; --q) {
-            if (e0 + q < e1) {
-                eW[e0 + q] = W;
-                if (e0 + q == 0) { *Bx = W; *first = f; *wide = 0; }
-                W += 1.0 / u[q];
-            }
-        }
-    } else {
-        double p = 0.0, bx = 0.0;
-        for (int i = tid; i < c; i += NT) {
-            const double v = (double)key2f(keys[i]);
-            p += (double)exp_neg((float)((v - (double)l) * inv_t));
-            if (i > 0) bx += (double)exp_neg((float)(((double)f - v) * inv_t));
-        }
-        const double ps = block_sum<NT>(p, s_red);
-        const double bs = block_sum<NT>(bx, s_red);
-        if (tid == 0) { *first = f; *last = l; *P = ps; *Bx = bs; *wide = 1; }
-    }
-}
+constexpr int kAggThreads = 256;
 
-__global__ __launch_bounds__(kSortThreads) void k_bucket_sort(uint32_t* __restrict__ bucket_vals,
-                                                               const uint32_t* bucket_cnt, int cap, SegArrays seg,
-                                                               double* eU, double* eW, uint8_t* wide, double inv_t) {
-    __shared__ uint32_t keys[kBucketCapMax];
-    __shared__ uint32_t cnt[256 * (kSortThreads / 64)];
-    __shared__ uint32_t scr[32];
-    __shared__ double s_scan[kSortThreads];
-    __shared__ double s_red[kSortThreads / 64];
+__global__ __launch_bounds__(kAggThreads) void k_bucket_agg(const uint32_t* __restrict__ bucket_vals,
+                                                             const uint32_t* bucket_cnt, int cap, SegArrays seg,
+                                                             double inv_t) {
+    __shared__ uint32_t s_kmin, s_kmax;
+    __shared__ unsigned long long s_fx[2 * kAggThreads / 64];
     const int tid = threadIdx.x;
     const int bkt = blockIdx.x;
     const int c = (int)min(bucket_cnt[bkt], (uint32_t)cap);
     const size_t off = (size_t)bkt * (size_t)cap;
-    if (tid == 0) { seg.cnt[bkt] = (uint32_t)c; seg.off[bkt] = (uint32_t)off; }
+    if (tid == 0) { seg.cnt[bkt] = (uint32_t)c; seg.off[bkt] = (uint32_t)off; s_kmin = 0xFFFFFFFFu; s_kmax = 0u; }
     if (c == 0) return;
-    uint32_t* vals = bucket_vals + off;
-    const int cp = next_pow2(c);
-    const bool small = cp <= 4096;
-    for (int i = tid; i < (small ? cp : c); i += kSortThreads)
-        keys[i] = i < c ? f2key(__uint_as_float(vals[i])) : 0xFFFFFFFFu;
+    const uint32_t* vals = bucket_vals + off;
     __syncthreads();
-    if (small) bitonic_sort_lds<kSortThreads>(keys, cp);
-    else block_sort_lds<kSortThreads, kSortItems>(keys, c, cnt, scr);
-    for (int i = tid; i < c; i += kSortThreads) vals[i] = keys[i];
-    segment_local_curve<kSortThreads, kSortItems>(keys, c, inv_t, eU + off, eW + off, &seg.first[bkt], &seg.last[bkt],
-                                                   &seg.P[bkt], &seg.Bx[bkt], &wide[bkt], s_scan, s_red);
+    uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+    for (int i = tid; i < c; i += kAggThreads) {
+        const uint32_t k = f2key(__uint_as_float(vals[i]));
+        kmn = min(kmn, k);
+        kmx = max(kmx, k);
+    }
+    atomicMin(&s_kmin, kmn);
+    atomicMax(&s_kmax, kmx);
+    __syncthreads();
+    const double vmin = (double)key2f(s_kmin), vmax = (double)key2f(s_kmax);
+    Fx128 P = fx_zero(), Q = fx_zero();
+    for (int i = tid; i < c; i += kAggThreads) {
+        const double v = (double)key2f(f2key(__uint_as_float(vals[i])));
+        fx_add_term(P, exp((v - vmax) * inv_t));
+        fx_add_term(Q, exp((vmin - v) * inv_t));
+    }
+    const Fx128 Ps = block_sum_fx<kAggThreads>(P, s_fx);
+    const Fx128 Qs = block_sum_fx<kAggThreads>(Q, s_fx);
+    if (tid == 0) {
+        seg.first[bkt] = (float)vmin;
+        seg.last[bkt] = (float)vmax;
+        seg.P[bkt] = fx_to_double(Ps);
+        seg.Bx[bkt] = fx_to_double(fx_minus_one(Qs));
+    }
 }
 
-__global__ __launch_bounds__(kSortThreads) void k_band_root(const uint32_t* bucket_keys, int nb, Ctl* ctl,
-                                                             SegArrays seg, const double* eU, const double* eW,
-                                                             const uint8_t* wide, SolveScratch sc, double k, double t,
+__global__ __launch_bounds__(kSortThreads) void k_band_root(const uint32_t* bucket_vals, int nb, Ctl* ctl,
+                                                             SegArrays seg, SolveScratch sc, double k, double t,
                                                              double inv_t, double* b_out) {
+    __shared__ uint32_t sortbuf[kBucketCapMax];
     __shared__ float s_k[kSortThreads];
     __shared__ double s_v[kSortThreads];
     __shared__ int s_int[32];
-    SegView sv{nb, seg.first, seg.last, seg.P, seg.Bx, seg.cnt, seg.off, bucket_keys, eU, eW, wide};
+    SegView sv{nb, seg.first, seg.last, seg.P, seg.Bx, seg.cnt, seg.off, bucket_vals, nullptr, nullptr, nullptr, sortbuf};
     Tails tl{ctl->aL, ctl->aR, ctl->S_L, ctl->S_R, (double)ctl->m, (double)ctl->c_R, k, t, inv_t};
     SolveOut o = segment_solve<kSortThreads, kSortItems>(sv, tl, sc, s_k, s_v, s_int);
     if (threadIdx.x == 0) {
@@ -375,7 +339,7 @@ __global__ __launch_bounds__(kCurveThreads) void k_curve_root(const uint32_t* __
     __shared__ float s_k[kCurveThreads];
     __shared__ double s_v[kCurveThreads];
     __shared__ int s_int[32];
-    SegView sv{ntiles, seg.first, seg.last, seg.P, seg.Bx, seg.cnt, seg.off, keys, nullptr, nullptr, nullptr};
+    SegView sv{ntiles, seg.first, seg.last, seg.P, seg.Bx, seg.cnt, seg.off, keys, nullptr, nullptr, nullptr, nullptr};
     Tails tl{-INFINITY, INFINITY, 0.0, 0.0, (double)n, 0.0, k, t, inv_t};
     SolveOut o = segment_solve<kCurveThreads, kRadixItems>(sv, tl, sc, s_k, s_v, s_int);
     if (threadIdx.x == 0) {
@@ -398,12 +362,10 @@ void launch_small_solve(const float* r, int n, double k, double t, Ctl* ctl, Sol
 }
 
 void launch_bucket_solve(uint32_t* bucket_vals, const uint32_t* bucket_cnt, int cap, int nb, Ctl* ctl, SegArrays seg,
-                         double* eU, double* eW, uint8_t* wide, SolveScratch sc, double k, double t, double* b_out,
-                         hipStream_t s) {
-    hipLaunchKernelGGL(k_bucket_sort, dim3(nb), dim3(kSortThreads), 0, s, bucket_vals, bucket_cnt, cap, seg, eU, eW,
-                       wide, 1.0 / t);
-    hipLaunchKernelGGL(k_band_root, dim3(1), dim3(kSortThreads), 0, s, bucket_vals, nb, ctl, seg, eU, eW, wide, sc, k, t,
-                       1.0 / t, b_out);
+                         SolveScratch sc, double k, double t, double* b_out, hipStream_t s) {
+    hipLaunchKernelGGL(k_bucket_agg, dim3(nb), dim3(kAggThreads), 0, s, bucket_vals, bucket_cnt, cap, seg, 1.0 / t);
+    hipLaunchKernelGGL(k_band_root, dim3(1), dim3(kSortThreads), 0, s, bucket_vals, nb, ctl, seg, sc, k, t, 1.0 / t,
+                       b_out);
 }
 
 int radix_hist_blocks(long long n) {

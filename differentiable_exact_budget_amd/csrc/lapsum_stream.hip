@@ -271,8 +271,19 @@ __global__ __launch_bounds__(kStreamThreads) void k_filter_finalize(const Filter
         const int b = tid + q * kStreamThreads;
         if (b < nparts) fp[q] = part[b];
     }
-    uint32_t bc = 0u;
-    if (tid < ctl->nb) bc = bucket_cnt[tid];
+    // bucket counts: a thread sums its buckets, the maximum goes to s_mxb
+    const int nbk = ctl->nb;
+    constexpr int BQ = kMaxBuckets / kStreamThreads;
+    uint32_t bcv[BQ];
+#pragma unroll
+    for (int q = 0; q < BQ; ++q) {
+        const int b = tid + q * kStreamThreads;
+        bcv[q] = b < nbk ? bucket_cnt[b] : 0u;
+    }
+    unsigned long long bc = 0ull;
+    uint32_t bmx = 0u;
+#pragma unroll
+    for (int q = 0; q < BQ; ++q) { bc += bcv[q]; bmx = max(bmx, bcv[q]); }
     double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
     unsigned long long u0 = 0ull, u1 = 0ull;
     int anynan = 0;
@@ -296,8 +307,8 @@ __global__ __launch_bounds__(kStreamThreads) void k_filter_finalize(const Filter
     const unsigned long long NAN_ = block_sum_u64<kStreamThreads>(u0, s_redu);
     const unsigned long long CR = block_sum_u64<kStreamThreads>(u1, s_redu);
     const int nb = ctl->nb;
-    const unsigned long long M = block_sum_u64<kStreamThreads>((unsigned long long)bc, s_redu);
-    atomicMax(&s_mxb, (unsigned long long)bc);
+    const unsigned long long M = block_sum_u64<kStreamThreads>(bc, s_redu);
+    atomicMax(&s_mxb, (unsigned long long)bmx);
     __syncthreads();
     if (tid == 0) {
         int flags = 0;

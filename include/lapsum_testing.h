@@ -41,13 +41,17 @@ lapsum_status_t lapsum_test_select(const float* x, int64_t s, int64_t l, int64_t
 /*
  * The streaming filter for a given bracket [a_L, a_R) (section 2.2,
  * streaming and filtering), with no interior splitters: counts_host gets
- * {below, band, above}, sums_host {S_L, S_R, B_L, B_R}; the band values,
- * ascending, go to band_out (device fp32, capacity band_cap); *band_size_host
- * gets the band size (or -1 if it exceeded band_cap or a bucket's capacity).
+ * {below, band, above}, sums_host {S_L, S_R, B_L, B_R}; the band values go
+ * to band_out (device fp32, capacity band_cap) bucket by bucket in bucket
+ * order (unordered inside a bucket; buckets are value-ordered);
+ * *band_size_host gets the band size (or -1 if it exceeded band_cap or a
+ * bucket's capacity), *nbuckets_host the bucket count and
+ * bucket_sizes_host[0..nbuckets) (host, capacity 1024) their sizes.
  */
 lapsum_status_t lapsum_test_filter(const float* scores, int64_t n, float t, float a_L, float a_R,
                                    int64_t* counts_host, double* sums_host, float* band_out,
-                                   int64_t band_cap, int64_t* band_size_host, lapsum_stream_t stream);
+                                   int64_t band_cap, int64_t* band_size_host, int32_t* nbuckets_host,
+                                   int64_t* bucket_sizes_host, lapsum_stream_t stream);
 
 #ifdef __cplusplus
 }
