@@ -7,9 +7,9 @@
  * with the HIP library; the two meet only through seeded inputs.
  *
  * What it computes, and where the definition comes from (the pages are the
- * Fast LapSum paper "Fast LapSum: Exact Differentiable Top-k at Million
- * Scale" as summarised on gist.science, section 2.1 "El Operador LapSum",
- * and the arxivdaily abstract of the same paper):
+ * paper Fast LapSum: Exact Differentiable Top-k at Million Scale as
+ * summarised on gist.science, section 2.1 on the LapSum operator, and the
+ * arxivdaily abstract of the same paper):
  *
  *   F(x) = Laplace CDF with scale 1:  F(x) = e^x / 2 for x < 0,
  *                                      F(x) = 1 - e^-x / 2 for x >= 0.
@@ -325,8 +325,8 @@ void oracle_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], ui
 }
 
 /*
- * The kernel-noised sample (gist.science 2.2, "Localizacion"; the arxivdaily
- * abstract calls it a binomial order statistic from kernel-noised samples):
+ * The kernel-noised sample (gist.science summary 2.2, bracketing step 1;
+ * the arxivdaily abstract names the same step):
  * draw j = 0..s-1: Philox4x32-10 with counter (j_lo, j_hi, 0, 0) and key
  * (seed_lo, seed_hi) gives words w0..w3;
  *   index I_j = floor(((w1 << 32) | w0) * n / 2^64)       (uniform, with replacement)
@@ -353,7 +353,7 @@ void oracle_sample(const double* r, int64_t n, double t, uint64_t seed, int64_t 
 }
 
 /* ------------------------------------------------------------------ */
-/* Binomial order-statistic bounds (gist.science 2.2, "Localizacion").  */
+/* Binomial order-statistic bounds (gist.science summary 2.2, bracketing step 1). */
 /* Y = #{samples below b} ~ Bin(s, q), q = 1 - k/n.                     */
 /*   a_L = x_(l) <= b  <=>  Y >= l ;  l = largest l with P(Y <= l-1) <= delta */
 /*   a_R = x_(h) >  b  <=>  Y <= h-1; h = smallest h with P(Y >= h) <= delta  */
