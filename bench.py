@@ -11,9 +11,17 @@ Prints ONE JSON line.  Per-kernel durations come from HIP events recorded on
 the library's stream in a second timed loop (options.profile); the roofline
 entry uses the dominant kernel's algorithmic bytes per launch.  The CPU
 baseline times the fp64 oracle on a bounded prefix of the same workload.
+
+The roofline's `traffic` is the dominant kernel's HBM bytes per launch from
+hardware counters (FETCH_SIZE and WRITE_SIZE, calibrated against a plain
+copy of known size), read from the summary committed under profiles/; it is
+reported only while the sources it was measured on are unchanged (their
+SHA-256 is recorded next to the figure), else null.
 """
 import argparse
+import hashlib
 import json
+import re
 import os
 import statistics
 import sys
@@ -36,6 +44,67 @@ ALG_BYTES = {
 }
 
 
+# sources whose kernels the counter-based traffic figure was taken on
+TRAFFIC_SOURCES = ("differentiable_exact_budget_amd/csrc/lapsum_stream.hip",
+                   "differentiable_exact_budget_amd/csrc/lapsum_streamio.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_C4.md")
+
+
+def sources_sha256():
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def counter_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m = re.search(r"sources_sha256:\s*([0-9a-f]{64})", text)
+    if not m or m.group(1) != sources_sha256():
+        return None
+    for line in text.splitlines():
+        q = re.match(r"\|\s*" + re.escape(kernel) + r"\s*\|(.*)\|\s*$", line)
+        if q:
+            cells = [c.strip() for c in q.group(1).split("|")]
+            try:
+                return float(cells[-1])
+            except ValueError:
+                return None
+    return None
+
+
+def measure_ceilings(torch, L, dev, n=100_000_000, reps=10):
+    """Achievable HBM rates of the library's plain streaming kernels on the
+    same device: a copy (read + write n fp32) and a read of n fp32, launched
+    like the solver's streaming passes."""
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    sink = torch.zeros(256, dtype=torch.float32, device=dev)
+    lib = L.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {}
+    for name, fn, nbytes in (("copy", lambda: lib.lapsum_test_copy(a.data_ptr(), b.data_ptr(), n, stream), 8 * n),
+                             ("read", lambda: lib.lapsum_test_read(a.data_ptr(), n, sink.data_ptr(), stream), 4 * n)):
+        assert fn() == 0
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for s0, s1 in ev:
+            s0.record()
+            fn()
+            s1.record()
+        torch.cuda.synchronize()
+        ms = statistics.median(s0.elapsed_time(s1) for s0, s1 in ev)
+        res[name + "_GBps"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    del a, b, sink
+    res["note"] = "k_copy and k_read over 10^8 fp32 (400 MB), median of 10"
+    return res
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -44,7 +113,8 @@ def parse():
     ap.add_argument("--config", default="C4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=10_000_000, help="oracle prefix size for the CPU baseline")
+    ap.add_argument("--cpu-sample", type=int, default=0,
+                    help="oracle prefix size for the CPU baseline (0: the whole workload)")
     return ap.parse_args()
 
 
@@ -98,7 +168,7 @@ def kernel_profile(L, torch, rd, gd, k, t, steps):
 def cpu_baseline(cfg, r, g, n_sample):
     import numpy as np
     import oracle
-    ns = min(n_sample, r.size)
+    ns = min(n_sample, r.size) if n_sample > 0 else r.size
     rs = np.ascontiguousarray(r[:ns]).astype(np.float64)
     gs = np.ascontiguousarray(g[:ns]).astype(np.float64)
     ks = max(cfg.k * ns / r.size, 1.0)
@@ -110,8 +180,9 @@ def cpu_baseline(cfg, r, g, n_sample):
     oracle.vjp(rs, gs, t, b)
     dt = time.perf_counter() - t0
     return {"value": ns / dt, "unit": "scores/s", "cores": oracle.get_threads(), "kind": "oracle",
-            "sample": f"first {ns} scores of the {cfg.name} input (k scaled to {ks:g}), fp64 bisection solve + p + "
-                      f"VJP, {dt:.2f} s wall"}
+            "sample": (f"first {ns} scores of the {cfg.name} input (k scaled to {ks:g})" if ns < r.size else
+                       f"the whole {cfg.name} input ({ns} scores, k={ks:g})") +
+                      f": fp64 bisection solve + p + VJP, {dt:.2f} s wall"}
 
 
 def main():
@@ -142,8 +213,10 @@ def main():
     alg = ALG_BYTES.get(dom, 0) * cfg.n
     achieved = alg / (kern[dom] * 1e-3) / 1e9 if kern[dom] > 0 else 0.0
     roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+            "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": counter_traffic(dom) if cfg.name == "C4" else None,
             "alg_bytes_per_launch": alg, "avg_ms": round(kern[dom], 5)}
+    ceil = measure_ceilings(torch, L, dev)
+    roof["frac_of_copy_ceiling"] = round(achieved / ceil["copy_GBps"], 4)
     kernels = {}
     for name, ms in sorted(kern.items(), key=lambda kv: -kv[1]):
         e = {"avg_ms": round(ms, 5)}
@@ -173,6 +246,7 @@ def main():
         "data": "synthetic (seeded numpy PCG64)",
         "config": {"workload": describe(cfg), "n": cfg.n, "k": cfg.k, "t": cfg.t, "parallelism": "single GPU"},
         "roofline": roof,
+        "ceilings": ceil,
         "kernels": kernels,
         "path": {"path_taken": info["path_taken"], "certified": info["certified"], "widenings": info["widenings"],
                  "band_size": info["band_size"], "buckets": info["buckets"], "sample_size": info["sample_size"]},

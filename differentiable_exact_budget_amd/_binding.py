@@ -89,6 +89,7 @@ EXPORTED = [
     "lapsum_vjp_ex",
     "lapsum_release_workspaces", "lapsum_workspace_bytes",
     "lapsum_test_sort", "lapsum_test_sample", "lapsum_test_select", "lapsum_test_filter",
+    "lapsum_test_copy", "lapsum_test_read", "lapsum_test_binomial_ranks",
 ]
 
 
@@ -128,6 +129,12 @@ def lib():
     L.lapsum_test_filter.argtypes = [vp, i64, f32, f32, f32, ctypes.POINTER(i64), ctypes.POINTER(f64), vp, i64,
                                      ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(i64), vp]
     L.lapsum_test_filter.restype = ctypes.c_int
+    L.lapsum_test_copy.argtypes = [vp, vp, i64, vp]
+    L.lapsum_test_copy.restype = ctypes.c_int
+    L.lapsum_test_read.argtypes = [vp, i64, vp, vp]
+    L.lapsum_test_read.restype = ctypes.c_int
+    L.lapsum_test_binomial_ranks.argtypes = [i64, f64, f64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    L.lapsum_test_binomial_ranks.restype = ctypes.c_int
     _lib = L
     return L
 

@@ -19,6 +19,7 @@
 // The suffix is always carried as e^{-gap/t} (1 + B_{j+1}), never as a
 // difference of inclusive sums.
 #pragma once
+#include <type_traits>
 #include "lapsum_device.h"
 
 namespace lapsum {
@@ -293,7 +294,7 @@ LS_DEV void wave_scan_bwd_excl(float& k, double& v, double inv_t) {
 // once, and the root is taken by the thread that owns j* with its
 // neighbour's values exchanged through LDS.
 template <int NT, int EMAX>
-__device__ SolveOut segment_solve(const SegView sv, const Tails tl, const SolveScratch sc,
+__device__ __attribute__((always_inline)) SolveOut segment_solve(const SegView sv, const Tails tl, const SolveScratch sc,
                                   float* s_k, double* s_v, int* s_int) {
     constexpr int SEGB = 8;  // segments fetched per batch by each lane of wave 0
     const int tid = threadIdx.x;
@@ -389,160 +390,171 @@ __device__ SolveOut segment_solve(const SegView sv, const Tails tl, const SolveS
             sort_pow2_lds<NT>(sv.sortbuf, cp);
             rk = sv.sortbuf;
         }
-        const int E = ((int)cS + NT - 1) / NT;
-        const int e0 = min((int)cS, tid * E), e1 = min((int)cS, e0 + E);
-        float vv[EMAX];
-#pragma unroll
-        for (int q = 0; q < EMAX; ++q) {
-            const int j = e0 + q;
-            vv[q] = (j < e1) ? key2f(rk[j]) : 0.0f;
-        }
-        const float vfirst = key2f(rk[0]);
-        const float vlast = key2f(rk[cS - 1]);
-        const float pk0 = sc.pk[sstar]; const double pv0 = sc.pv[sstar];
-        const float bk0 = sc.bk[sstar]; const double bv0 = sc.bv[sstar];
-        double Pj[EMAX], Bj[EMAX];
-        const bool have_local = sv.eU != nullptr && !sv.wide[sstar];
-        if (have_local || ((double)vlast - (double)vfirst) * inv_t <= 600.0) {
-            // additive form relative to ref = v_first: u_j = e^{(v_j - ref)/t} in [1, e^600]
-            //   P_j = (carry_P + sum_{i<=j} u_i) / u_j,  B_j = u_j (carry_B + sum_{i>j} 1/u_i)
-            const double ref = (double)vfirst;
-            double u[EMAX], Ul[EMAX], Wl[EMAX];
-#pragma unroll
-            for (int q = 0; q < EMAX; ++q) u[q] = (e0 + q < e1) ? ecoef(((double)vv[q] - ref) * inv_t) : 1.0;
-            if (have_local) {
-#pragma unroll
-                for (int q = 0; q < EMAX; ++q) {
-                    const int j = e0 + q;
-                    Ul[q] = j < e1 ? sv.eU[offS + j] : 0.0;
-                    Wl[q] = j < e1 ? sv.eW[offS + j] : 0.0;
+        // the per-score arrays are sized by the thread's share of the segment,
+        // instantiated for a few shares so a small segment costs one element
+        // per thread
+        auto phase4 = [&](auto em_tag) {
+            constexpr int EMX = decltype(em_tag)::value;
+            const int E = ((int)cS + NT - 1) / NT;
+            const int e0 = min((int)cS, tid * E), e1 = min((int)cS, e0 + E);
+            float vv[EMX];
+    #pragma unroll
+            for (int q = 0; q < EMX; ++q) {
+                const int j = e0 + q;
+                vv[q] = (j < e1) ? key2f(rk[j]) : 0.0f;
+            }
+            const float vfirst = key2f(rk[0]);
+            const float vlast = key2f(rk[cS - 1]);
+            const float pk0 = sc.pk[sstar]; const double pv0 = sc.pv[sstar];
+            const float bk0 = sc.bk[sstar]; const double bv0 = sc.bv[sstar];
+            double Pj[EMX], Bj[EMX];
+            const bool have_local = sv.eU != nullptr && !sv.wide[sstar];
+            if (have_local || ((double)vlast - (double)vfirst) * inv_t <= 600.0) {
+                // additive form relative to ref = v_first: u_j = e^{(v_j - ref)/t} in [1, e^600]
+                //   P_j = (carry_P + sum_{i<=j} u_i) / u_j,  B_j = u_j (carry_B + sum_{i>j} 1/u_i)
+                const double ref = (double)vfirst;
+                double u[EMX], Ul[EMX], Wl[EMX];
+    #pragma unroll
+                for (int q = 0; q < EMX; ++q) u[q] = (e0 + q < e1) ? ecoef(((double)vv[q] - ref) * inv_t) : 1.0;
+                if (have_local) {
+    #pragma unroll
+                    for (int q = 0; q < EMX; ++q) {
+                        const int j = e0 + q;
+                        Ul[q] = j < e1 ? sv.eU[offS + j] : 0.0;
+                        Wl[q] = j < e1 ? sv.eW[offS + j] : 0.0;
+                    }
+                } else {
+                    double ut = 0.0, wt = 0.0;
+    #pragma unroll
+                    for (int q = 0; q < EMX; ++q)
+                        if (e0 + q < e1) { ut += u[q]; wt += 1.0 / u[q]; }
+                    double U = block_scan_add_excl<NT>(ut, s_v, false);
+                    double W = block_scan_add_excl<NT>(wt, s_v, true);
+    #pragma unroll
+                    for (int q = 0; q < EMX; ++q)
+                        if (e0 + q < e1) { U += u[q]; Ul[q] = U; }
+    #pragma unroll
+                    for (int q = EMX - 1; q >= 0; --q)
+                        if (e0 + q < e1) { Wl[q] = W; W += 1.0 / u[q]; }
+                }
+                const double pc = (pv0 != 0.0) ? pv0 * ecoef(((double)pk0 - ref) * inv_t) : 0.0;
+                const double bc = (bv0 != 0.0) ? bv0 * ecoef((ref - (double)bk0) * inv_t) : 0.0;
+    #pragma unroll
+                for (int q = 0; q < EMX; ++q) {
+                    Pj[q] = (pc + Ul[q]) / u[q];
+                    Bj[q] = u[q] * (bc + Wl[q]);
                 }
             } else {
-                double ut = 0.0, wt = 0.0;
-#pragma unroll
-                for (int q = 0; q < EMAX; ++q)
-                    if (e0 + q < e1) { ut += u[q]; wt += 1.0 / u[q]; }
-                double U = block_scan_add_excl<NT>(ut, s_v, false);
-                double W = block_scan_add_excl<NT>(wt, s_v, true);
-#pragma unroll
-                for (int q = 0; q < EMAX; ++q)
-                    if (e0 + q < e1) { U += u[q]; Ul[q] = U; }
-#pragma unroll
-                for (int q = EMAX - 1; q >= 0; --q)
-                    if (e0 + q < e1) { Wl[q] = W; W += 1.0 / u[q]; }
-            }
-            const double pc = (pv0 != 0.0) ? pv0 * ecoef(((double)pk0 - ref) * inv_t) : 0.0;
-            const double bc = (bv0 != 0.0) ? bv0 * ecoef((ref - (double)bk0) * inv_t) : 0.0;
-#pragma unroll
-            for (int q = 0; q < EMAX; ++q) {
-                Pj[q] = (pc + Ul[q]) / u[q];
-                Bj[q] = u[q] * (bc + Wl[q]);
-            }
-        } else {
-            // wide segment: affine carries with every exponent <= 0
-            double al[EMAX];
-#pragma unroll
-            for (int q = 1; q < EMAX; ++q)
-                al[q] = (e0 + q < e1) ? ecoef(((double)vv[q - 1] - (double)vv[q]) * inv_t) : 0.0;
-            al[0] = 0.0;
-            float fk = -INFINITY; double fv = 0.0;
-#pragma unroll
-            for (int q = 0; q < EMAX; ++q)
-                if (e0 + q < e1) { fv = 1.0 + (q > 0 ? al[q] * fv : 0.0); fk = vv[q]; }
-            block_scan_fwd_excl<NT>(fk, fv, s_k, s_v, inv_t);
-            {
-                float pk = pk0; double pv = pv0;
-                float ck = fk; double cv = fv;
-                fwd_combine(pk, pv, ck, cv, inv_t);
-                fk = ck; fv = cv;
-            }
-#pragma unroll
-            for (int q = 0; q < EMAX; ++q) {
-                if (e0 + q < e1) {
-                    const double carry = (q == 0) ? (fv != 0.0 ? ecoef(((double)fk - (double)vv[0]) * inv_t) * fv : 0.0)
-                                                  : al[q] * Pj[q - 1];
-                    Pj[q] = 1.0 + carry;
+                // wide segment: affine carries with every exponent <= 0
+                double al[EMX];
+    #pragma unroll
+                for (int q = 1; q < EMX; ++q)
+                    al[q] = (e0 + q < e1) ? ecoef(((double)vv[q - 1] - (double)vv[q]) * inv_t) : 0.0;
+                al[0] = 0.0;
+                float fk = -INFINITY; double fv = 0.0;
+    #pragma unroll
+                for (int q = 0; q < EMX; ++q)
+                    if (e0 + q < e1) { fv = 1.0 + (q > 0 ? al[q] * fv : 0.0); fk = vv[q]; }
+                block_scan_fwd_excl<NT>(fk, fv, s_k, s_v, inv_t);
+                {
+                    float pk = pk0; double pv = pv0;
+                    float ck = fk; double cv = fv;
+                    fwd_combine(pk, pv, ck, cv, inv_t);
+                    fk = ck; fv = cv;
+                }
+    #pragma unroll
+                for (int q = 0; q < EMX; ++q) {
+                    if (e0 + q < e1) {
+                        const double carry = (q == 0) ? (fv != 0.0 ? ecoef(((double)fk - (double)vv[0]) * inv_t) * fv : 0.0)
+                                                      : al[q] * Pj[q - 1];
+                        Pj[q] = 1.0 + carry;
+                    }
+                }
+                float rk2 = INFINITY; double rv2 = 0.0;
+    #pragma unroll
+                for (int q = EMX - 1; q >= 0; --q) {
+                    if (e0 + q < e1) {
+                        rv2 = 1.0 + (rv2 != 0.0 ? ecoef(((double)vv[q] - (double)rk2) * inv_t) * rv2 : 0.0);
+                        rk2 = vv[q];
+                    }
+                }
+                block_scan_bwd_excl<NT>(rk2, rv2, s_k, s_v, inv_t);
+                {
+                    float bk = bk0; double bvv = bv0;
+                    bwd_combine(rk2, rv2, bk, bvv, inv_t);
+                }
+    #pragma unroll
+                for (int q = EMX - 1; q >= 0; --q) {
+                    const int j = e0 + q;
+                    if (j < e1) {
+                        if (q + 1 < EMX && j + 1 < e1) Bj[q] = al[q + 1] * (1.0 + Bj[q + 1]);
+                        else Bj[q] = (rv2 != 0.0) ? ecoef(((double)vv[q] - (double)rk2) * inv_t) * rv2 : 0.0;
+                    }
                 }
             }
-            float rk2 = INFINITY; double rv2 = 0.0;
-#pragma unroll
-            for (int q = EMAX - 1; q >= 0; --q) {
-                if (e0 + q < e1) {
-                    rv2 = 1.0 + (rv2 != 0.0 ? ecoef(((double)vv[q] - (double)rk2) * inv_t) * rv2 : 0.0);
-                    rk2 = vv[q];
-                }
-            }
-            block_scan_bwd_excl<NT>(rk2, rv2, s_k, s_v, inv_t);
-            {
-                float bk = bk0; double bvv = bv0;
-                bwd_combine(rk2, rv2, bk, bvv, inv_t);
-            }
-#pragma unroll
-            for (int q = EMAX - 1; q >= 0; --q) {
+            int myj = -1;
+    #pragma unroll
+            for (int q = 0; q < EMX; ++q) {
                 const int j = e0 + q;
                 if (j < e1) {
-                    if (q + 1 < EMAX && j + 1 < e1) Bj[q] = al[q + 1] * (1.0 + Bj[q + 1]);
-                    else Bj[q] = (rv2 != 0.0) ? ecoef(((double)vv[q] - (double)rk2) * inv_t) * rv2 : 0.0;
+                    const double G = 0.5 * Pj[q] + (tl.m - 1.0 - (double)(rankS + (uint32_t)j)) + tl.c_R - 0.5 * Bj[q];
+                    if (G >= tl.k) myj = j;
                 }
             }
-        }
-        int myj = -1;
-#pragma unroll
-        for (int q = 0; q < EMAX; ++q) {
-            const int j = e0 + q;
-            if (j < e1) {
-                const double G = 0.5 * Pj[q] + (tl.m - 1.0 - (double)(rankS + (uint32_t)j)) + tl.c_R - 0.5 * Bj[q];
-                if (G >= tl.k) myj = j;
+            // neighbour exchange: every thread publishes its first score and its B there
+            s_k[tid] = vv[0];
+            s_v[tid] = e0 < e1 ? Bj[0] : 0.0;
+            int jl = block_max_int<NT>(myj, s_int);  // (has barriers; also orders the LDS writes above)
+            if (jl < 0) jl = 0;                       // the segment's first score passed in phase 3
+            if (jl >= e0 && jl < e1) {
+                // this thread owns j*: lower end, P there, and the next score with its B
+                const int q = jl - e0;
+                double Pjs = 0.0, vlo = 0.0, vnx = 0.0, Bnx = 0.0;
+                int has_next = 0;
+    #pragma unroll
+                for (int qq = 0; qq < EMX; ++qq) if (qq == q) { Pjs = Pj[qq]; vlo = (double)vv[qq]; }
+                if (jl + 1 < e1) {
+    #pragma unroll
+                    for (int qq = 0; qq < EMX - 1; ++qq) if (qq == q) { vnx = (double)vv[qq + 1]; Bnx = Bj[qq + 1]; }
+                    has_next = 1;
+                } else if ((uint32_t)jl + 1u < cS) {
+                    vnx = (double)s_k[tid + 1]; Bnx = s_v[tid + 1]; has_next = 1;
+                }
+                s_root[0] = Pjs; s_root[1] = vlo; s_root[2] = vnx; s_root[3] = Bnx;
+                s_owner = has_next;
             }
-        }
-        // neighbour exchange: every thread publishes its first score and its B there
-        s_k[tid] = vv[0];
-        s_v[tid] = e0 < e1 ? Bj[0] : 0.0;
-        int jl = block_max_int<NT>(myj, s_int);  // (has barriers; also orders the LDS writes above)
-        if (jl < 0) jl = 0;                       // the segment's first score passed in phase 3
-        if (jl >= e0 && jl < e1) {
-            // this thread owns j*: lower end, P there, and the next score with its B
-            const int q = jl - e0;
-            double Pjs = 0.0, vlo = 0.0, vnx = 0.0, Bnx = 0.0;
-            int has_next = 0;
-#pragma unroll
-            for (int qq = 0; qq < EMAX; ++qq) if (qq == q) { Pjs = Pj[qq]; vlo = (double)vv[qq]; }
-            if (jl + 1 < e1) {
-#pragma unroll
-                for (int qq = 0; qq < EMAX - 1; ++qq) if (qq == q) { vnx = (double)vv[qq + 1]; Bnx = Bj[qq + 1]; }
-                has_next = 1;
-            } else if ((uint32_t)jl + 1u < cS) {
-                vnx = (double)s_k[tid + 1]; Bnx = s_v[tid + 1]; has_next = 1;
+            __syncthreads();
+            if (tid == 0) {
+                const double lo = s_root[1];
+                double lnA = log(s_root[0]), lnB, chi;
+                const double J = (double)(rankS + (uint32_t)jl);
+                const double D = (tl.m - 1.0 - J) + tl.c_R - tl.k;
+                out.jstar = (long long)(rankS + (uint32_t)jl);
+                const int has_next = s_owner;
+                if (has_next) {
+                    const double vnext = s_root[2], Bnext = s_root[3];
+                    chi = vnext; lnB = (lo - vnext) * inv_t + log1p(Bnext);
+                } else if (bv0 != 0.0) {
+                    // the backward carry after the root segment: its position is the
+                    // next score (first of a later segment, or a_R) and its value the
+                    // sum of e^{(position - v)/t} over every score from there up
+                    chi = (double)bk0; lnB = (lo - (double)bk0) * inv_t + log(bv0);
+                } else {
+                    chi = tl.aR; lnB = -INFINITY;
+                }
+                const double lnw = log_root(lnA, lnB, D);
+                double b = lo + tl.t * lnw;
+                if (b < lo) b = lo;
+                if (b > chi) b = chi;
+                out.b = b;
+                out.ok = (b == b) && (b > -INFINITY) && (b < INFINITY);
             }
-            s_root[0] = Pjs; s_root[1] = vlo; s_root[2] = vnx; s_root[3] = Bnx;
-            s_owner = has_next;
-        }
-        __syncthreads();
-        if (tid == 0) {
-            const double lo = s_root[1];
-            double lnA = log(s_root[0]), lnB, chi;
-            const double J = (double)(rankS + (uint32_t)jl);
-            const double D = (tl.m - 1.0 - J) + tl.c_R - tl.k;
-            out.jstar = (long long)(rankS + (uint32_t)jl);
-            const int has_next = s_owner;
-            if (has_next) {
-                const double vnext = s_root[2], Bnext = s_root[3];
-                chi = vnext; lnB = (lo - vnext) * inv_t + log1p(Bnext);
-            } else if (bv0 != 0.0) {
-                // the backward carry after the root segment: its position is the
-                // next score (first of a later segment, or a_R) and its value the
-                // sum of e^{(position - v)/t} over every score from there up
-                chi = (double)bk0; lnB = (lo - (double)bk0) * inv_t + log(bv0);
-            } else {
-                chi = tl.aR; lnB = -INFINITY;
-            }
-            const double lnw = log_root(lnA, lnB, D);
-            double b = lo + tl.t * lnw;
-            if (b < lo) b = lo;
-            if (b > chi) b = chi;
-            out.b = b;
-            out.ok = (b == b) && (b > -INFINITY) && (b < INFINITY);
-        }
+        };
+        if ((int)cS <= NT) phase4(std::integral_constant<int, 1>{});
+        else if constexpr (EMAX > 4) {
+            if ((int)cS <= 4 * NT) phase4(std::integral_constant<int, 4>{});
+            else phase4(std::integral_constant<int, EMAX>{});
+        } else phase4(std::integral_constant<int, EMAX>{});
     } else if (tid == 0) {
         // the root lies below the first score of the segments
         double ref, lnA, lnB, clo, chi;

@@ -11,6 +11,7 @@ namespace lapsum {
 // ---------------------------------------------------------------------------
 constexpr int kStreamThreads = 256;      // streaming kernels (filter, p, VJP)
 constexpr int kMaxStreamBlocks = 2048;   // 256 CUs x 8 resident blocks
+constexpr int kMaxStreamParts = 131072;  // workgroups of a tiled streaming pass that leave partials
 constexpr int kMaxBuckets = 1024;        // band buckets
 constexpr int kBucketCapMax = 16384;     // band scores per bucket (LDS sort capacity)
 constexpr int kSortThreads = 1024;       // single-workgroup LDS sort / solve
@@ -198,98 +199,6 @@ LS_DEV unsigned long long block_sum_u64(unsigned long long v, unsigned long long
     return r;  // valid in wave 0
 }
 
-// ---------------------------------------------------------------------------
-// Grid-stride streaming over float4 elements [0, n4) with U loads in flight
-// per thread: the next U loads are issued before the current U are consumed
-// (software pipelining -- a single load in flight per wave leaves HBM idle
-// while the wave computes).  The main loop's trip test uses the wave's last
-// lane, so all 64 lanes iterate together (wave-wide ballots are safe inside
-// main); leftover elements go to tail, one per lane.  reverse = true walks
-// the array from its end, so a pass can start on the part of an array the
-// previous pass read last (still in the memory-side cache).
-// main(v, idx) / tail(v, idx): v = element idx.
-// ---------------------------------------------------------------------------
-typedef float f4v __attribute__((ext_vector_type(4)));
-
-// 16-byte load, optionally non-temporal (streamed past the caches)
-template <bool NT>
-LS_DEV float4 ld4(const float4* p) {
-    if (NT) {
-        const f4v v = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(p));
-        return make_float4(v.x, v.y, v.z, v.w);
-    }
-    return *p;
-}
-
-template <int U, bool NT = false, class Main, class Tail>
-LS_DEV void stream_f4(const float4* __restrict__ a, long long n4, bool reverse, Main&& main, Tail&& tail) {
-    const long long stride = (long long)gridDim.x * blockDim.x;
-    long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;  // logical position
-    const long long last = 63 - (long long)lane_id();
-    const long long step = reverse ? -stride : stride;                // physical step (wave-uniform)
-    long long idx = reverse ? n4 - 1 - i : i;                         // physical index of i
-    // the trip test is made explicitly wave-uniform; the prefetch offset is a
-    // wave-uniform scalar (when there is no next batch the prefetch re-reads
-    // the current one), so every load address is base + scalar and the
-    // compiler keeps the prefetches in flight while the current batch is used
-    auto uniform = [](bool c) { return __builtin_amdgcn_readfirstlane((int)c) != 0; };
-    if (uniform(i + last + (long long)(U - 1) * stride < n4)) {
-        float4 cur[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) cur[u] = ld4<NT>(a + idx + u * step);
-        while (true) {
-            const bool hn = uniform(i + (long long)U * stride + last + (long long)(U - 1) * stride < n4);
-            const long long poff = hn ? (long long)U * step : 0;
-            float4 nx[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) nx[u] = ld4<NT>(a + idx + poff + u * step);
-#pragma unroll
-            for (int u = 0; u < U; ++u) main(cur[u], idx + u * step);
-            i += (long long)U * stride;
-            idx += (long long)U * step;
-            if (!hn) break;
-#pragma unroll
-            for (int u = 0; u < U; ++u) cur[u] = nx[u];
-        }
-    }
-    for (; i < n4; i += stride, idx += step) tail(a[idx], idx);
-}
-
-// the same over two arrays read in lockstep
-template <int U, bool NT = false, class Main, class Tail>
-LS_DEV void stream_f4x2(const float4* __restrict__ a, const float4* __restrict__ b, long long n4, bool reverse,
-                        Main&& main, Tail&& tail) {
-    const long long stride = (long long)gridDim.x * blockDim.x;
-    long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    const long long last = 63 - (long long)lane_id();
-    const long long step = reverse ? -stride : stride;
-    long long idx = reverse ? n4 - 1 - i : i;
-    auto uniform = [](bool c) { return __builtin_amdgcn_readfirstlane((int)c) != 0; };
-    if (uniform(i + last + (long long)(U - 1) * stride < n4)) {
-        float4 ca[U], cb[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) { ca[u] = ld4<NT>(a + idx + u * step); cb[u] = ld4<NT>(b + idx + u * step); }
-        while (true) {
-            const bool hn = uniform(i + (long long)U * stride + last + (long long)(U - 1) * stride < n4);
-            const long long poff = hn ? (long long)U * step : 0;
-            float4 na[U], nb[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                na[u] = ld4<NT>(a + idx + poff + u * step);
-                nb[u] = ld4<NT>(b + idx + poff + u * step);
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) main(ca[u], cb[u], idx + u * step);
-            i += (long long)U * stride;
-            idx += (long long)U * step;
-            if (!hn) break;
-#pragma unroll
-            for (int u = 0; u < U; ++u) { ca[u] = na[u]; cb[u] = nb[u]; }
-        }
-    }
-    for (; i < n4; i += stride, idx += step) tail(a[idx], b[idx], idx);
-}
-
 // ascending bitonic sort of N (a power of two) keys in LDS by NT threads
 template <int NT>
 LS_DEV void bitonic_sort_lds(uint32_t* a, int N) {
@@ -369,24 +278,16 @@ LS_DEV void bitonic_sort_hybrid(uint32_t* lds) {
 }
 
 // Ascending sort of the first N keys of lds (N a power of two, N >= 64) by
-// all NT threads: N <= 512 by wave 0 alone, NT <= N <= 16 NT with the
-// hybrid bitonic sort over the workgroup, anything else with the plain LDS
-// bitonic sort.  Ends with a barrier.
+// all NT threads; ends with a barrier.  The choice follows measurements on
+// gfx950 with NT = 1024: the hybrid sort wins for NT <= N <= 4 NT, the plain
+// LDS bitonic sort below that (one wave alone is slower: its shuffle stages
+// run back to back) and above it (the hybrid's register blocks then
+// conflict in LDS).
 template <int NT>
 LS_DEV void sort_pow2_lds(uint32_t* lds, int N) {
-    if (N <= 512) {
-        if (threadIdx.x < 64) {
-            if (N == 64) bitonic_sort_hybrid<64, 1>(lds);
-            else if (N == 128) bitonic_sort_hybrid<64, 2>(lds);
-            else if (N == 256) bitonic_sort_hybrid<64, 4>(lds);
-            else bitonic_sort_hybrid<64, 8>(lds);
-        }
-        __syncthreads();
-    } else if (N == NT) { bitonic_sort_hybrid<NT, 1>(lds); __syncthreads(); }
+    if (N == NT) { bitonic_sort_hybrid<NT, 1>(lds); __syncthreads(); }
     else if (N == 2 * NT) { bitonic_sort_hybrid<NT, 2>(lds); __syncthreads(); }
     else if (N == 4 * NT) { bitonic_sort_hybrid<NT, 4>(lds); __syncthreads(); }
-    else if (N == 8 * NT) { bitonic_sort_hybrid<NT, 8>(lds); __syncthreads(); }
-    else if (N == 16 * NT) { bitonic_sort_hybrid<NT, 16>(lds); __syncthreads(); }
     else bitonic_sort_lds<NT>(lds, N);
 }
 

@@ -7,10 +7,10 @@
 //  * bracketing (n > 10^6 by default): kernel-noised sample, binomial
 //    order statistics a_L = x_(l), a_R = x_(h), one streaming pass that
 //    folds out-of-band scores into fp64 tail sums and buckets the band,
-//    certification, band sort + solve.  The bracket is widened when it
-//    fails ("si no es asi, se amplia iterativamente") and the full sort
-//    covers whatever the bracket cannot (arxivdaily abstract: "a full-sort
-//    fallback that covers the worst-case scenario").
+//    certification, band sort + solve.  A bracket that fails is widened
+//    and tried again (section 2.2, step 4), and the full sort covers the
+//    worst case the bracket cannot (the arxivdaily abstract names this
+//    fallback).
 //
 // Certification.  The streaming pass returns S_L, S_R, the band sums
 // B_L = sum_band e^{(a_L - v)/t}, B_R = sum_band e^{(v - a_R)/t} and the
@@ -55,6 +55,7 @@ struct Workspace {
     HostSummary* hs_dev = nullptr;  // device view of hs
     unsigned int seq = 0;
     double* part = nullptr;
+    int probs_parts = 1;  // partials the last p pass left
     float* sample = nullptr;
     long long* sample_idx = nullptr;
     float* sp = nullptr;
@@ -92,7 +93,7 @@ Layout make_layout(long long n_cap) {
     const long long nseg = std::max<long long>(std::max<long long>(kMaxBuckets, tiles_for(n_cap)), 1);
     const long long elem = std::max<long long>(kBucketCapMax, std::max(kRadixTile, kSmallMax));
     L.ctl = take(sizeof(Ctl));
-    L.part = take(sizeof(double) * 8 * kMaxStreamBlocks);
+    L.part = take(sizeof(double) * 2 * (size_t)kMaxStreamParts);
     L.sample = take(sizeof(float) * kSampleMax);
     L.sample_idx = take(sizeof(long long) * kSampleMax);
     L.sp = take(sizeof(float) * (kMaxBuckets + 1));
@@ -382,7 +383,7 @@ lapsum_status_t check_args(const float* r, int64_t n, double k, float t, const v
 
 lapsum_status_t fill_stats(Workspace* w, hipStream_t st, long long n, lapsum_stats_t* stats) {
     if (!stats) return LAPSUM_OK;
-    launch_sum_p(w->ctl, w->part, n, st);
+    launch_sum_p(w->ctl, w->part, w->probs_parts, st);
     if (hipStreamSynchronize(st) != hipSuccess) return LAPSUM_ERR_HIP;
     Ctl c;
     if (hipMemcpy(&c, w->ctl, sizeof(Ctl), hipMemcpyDeviceToHost) != hipSuccess) return LAPSUM_ERR_HIP;
@@ -398,6 +399,7 @@ lapsum_status_t forward_impl(const float* r, int64_t n, double k, float t_f, flo
                              const lapsum_options_t& opt, lapsum_stats_t* stats, hipStream_t st) {
     lapsum_status_t a = check_args(r, n, k, t_f, p, b_out);
     if (a != LAPSUM_OK) return a;
+    if (opt.path < LAPSUM_PATH_AUTO || opt.path > LAPSUM_PATH_FORCE_FALLBACK) return LAPSUM_ERR_INVALID_ARGUMENT;
     if (opt.bucket_capacity < 1 || opt.bucket_capacity > kBucketCapMax || !(opt.sample_factor > 0.0) ||
         !(opt.delta > 0.0 && opt.delta < 0.5) || !(opt.margin_scale >= 0.0) || opt.max_widen < 0)
         return LAPSUM_ERR_INVALID_ARGUMENT;
@@ -416,7 +418,7 @@ lapsum_status_t forward_impl(const float* r, int64_t n, double k, float t_f, flo
     if (path == LAPSUM_PATH_FULL) {
         run_full(w, r, n, k, t, b_out, st, tm);
         tm.begin("probs");
-        launch_probs(r, n, t, p, w->ctl, w->part, st);
+        w->probs_parts = launch_probs(r, n, t, p, w->ctl, w->part, st);
         tm.end();
         if (hipGetLastError() != hipSuccess) return LAPSUM_ERR_HIP;
         if (stats) {
@@ -514,7 +516,7 @@ lapsum_status_t forward_impl(const float* r, int64_t n, double k, float t_f, flo
         tm.end();
     }
     tm.begin("probs");
-    launch_probs(r, n, t, p, w->ctl, w->part, st);
+    w->probs_parts = launch_probs(r, n, t, p, w->ctl, w->part, st);
     tm.end();
     if (hipGetLastError() != hipSuccess) return LAPSUM_ERR_HIP;
     if (stats) {
@@ -632,6 +634,35 @@ size_t lapsum_workspace_bytes(int64_t n) { return make_layout(std::max<long long
 // ---------------------------------------------------------------------------
 // stage entry points for parity tests
 // ---------------------------------------------------------------------------
+lapsum_status_t lapsum_test_binomial_ranks(int64_t s, double q, double delta, int64_t* l, int64_t* h) {
+    if (!l || !h || s < 1 || !(q > 0.0 && q < 1.0) || !(delta > 0.0 && delta < 0.5)) return LAPSUM_ERR_INVALID_ARGUMENT;
+    long long lo = 0, hi = 0;
+    try {
+        binomial_ranks(s, q, delta, &lo, &hi);
+    } catch (...) {
+        return LAPSUM_ERR_INTERNAL;
+    }
+    *l = lo;
+    *h = hi;
+    return LAPSUM_OK;
+}
+
+lapsum_status_t lapsum_test_copy(const float* src, float* dst, int64_t n, lapsum_stream_t stream) {
+    if (!src || !dst || n < 1) return LAPSUM_ERR_INVALID_ARGUMENT;
+    if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u) return LAPSUM_ERR_INVALID_ARGUMENT;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    launch_copy(src, dst, n, st);
+    return hip_ok(hipGetLastError());
+}
+
+lapsum_status_t lapsum_test_read(const float* src, int64_t n, float* sink, lapsum_stream_t stream) {
+    if (!src || !sink || n < 1) return LAPSUM_ERR_INVALID_ARGUMENT;
+    if (reinterpret_cast<uintptr_t>(src) & 15u) return LAPSUM_ERR_INVALID_ARGUMENT;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    launch_read(src, n, sink, st);
+    return hip_ok(hipGetLastError());
+}
+
 lapsum_status_t lapsum_test_sort(const float* scores, int64_t n, float* out, lapsum_stream_t stream) {
     if (!scores || !out || n < 1 || n > 0xFFFFFFFFll) return LAPSUM_ERR_INVALID_ARGUMENT;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);

@@ -25,12 +25,17 @@ int stream_blocks(long long n);
 void launch_filter(const float* r, long long n, double t, Ctl* ctl, const float* sp, const float* iw,
                    uint32_t* bucket_cnt, uint32_t* bucket_vals, int cap, double* part, unsigned long long* partc,
                    HostSummary* hs_dev, unsigned int seq, hipStream_t st);
-void launch_probs(const float* r, long long n, double t, float* p, Ctl* ctl, double* part, hipStream_t st);
-void launch_sum_p(Ctl* ctl, const double* part, long long n, hipStream_t st);
+// returns the number of partials it left (for launch_sum_p)
+int launch_probs(const float* r, long long n, double t, float* p, Ctl* ctl, double* part, hipStream_t st);
+void launch_sum_p(Ctl* ctl, const double* part, int nparts, hipStream_t st);
 void launch_vjp(const float* r, const float* g, long long n, double t, const double* b, float* grad, Ctl* ctl,
                 double* part, hipStream_t st, hipEvent_t* ev_mid);
 void launch_fill(float* p, long long n, float v, hipStream_t st);
 void launch_set_nan_b(Ctl* ctl, double* b_out, hipStream_t st);
+
+// lapsum_ceiling.hip
+void launch_copy(const float* a, float* b, long long n, hipStream_t st);
+void launch_read(const float* a, long long n, float* sink, hipStream_t st);
 
 // lapsum_sort.hip
 void launch_small_solve(const float* r, int n, double k, double t, Ctl* ctl, SolveScratch sc, double* b_out,

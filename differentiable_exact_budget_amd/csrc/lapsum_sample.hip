@@ -1,6 +1,6 @@
 // Localisation step of the bracketing path (Fast LapSum paper, gist.science
-// section 2.2, "Localizacion"; the arxivdaily abstract: "a binomial
-// order-statistic from kernel-noised samples").
+// summary section 2.2, bracketing step 1; the arxivdaily abstract names the
+// same step: order statistics of a sample noised with the operator's kernel).
 //
 //  k_sample  x_j = r_{I_j} + eps_j, j < s: I_j uniform in [0, n) with
 //            replacement, eps_j ~ Laplace(0, t) by inverse CDF.  Because the
@@ -74,11 +74,41 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(const float* __restri
     __shared__ int s_fast;
     __shared__ long long s_nlo;
     const int tid = threadIdx.x;
+    // the sample, 16 bytes per load where it can (thread tid holds elements
+    // i * kSelectThreads + tid)
     uint32_t kr[kSelectItems];
+    unsigned long long vmask = 0ull;
+    static_assert(kSelectItems % 4 == 0 && kSelectItems <= 64, "");
+    if ((reinterpret_cast<uintptr_t>(x) & 15u) == 0u) {
+        const float4* x4 = reinterpret_cast<const float4*>(x);
 #pragma unroll
-    for (int i = 0; i < kSelectItems; ++i) {
-        const int j = i * kSelectThreads + tid;
-        kr[i] = j < s ? f2key(x[j]) : 0u;
+        for (int i = 0; i < kSelectItems; i += 4) {
+            // float4 number (i/4)*kSelectThreads + tid: elements 4*that .. +3
+            // (every use of kr treats it as an unordered set of the sample's
+            // keys; vmask marks the slots that hold one)
+            const int j4 = (i / 4) * kSelectThreads + tid;
+            float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (4 * j4 + 3 < s) v = x4[j4];
+            else {
+                if (4 * j4 + 0 < s) v.x = x[4 * j4 + 0];
+                if (4 * j4 + 1 < s) v.y = x[4 * j4 + 1];
+                if (4 * j4 + 2 < s) v.z = x[4 * j4 + 2];
+            }
+            kr[i + 0] = f2key(v.x);
+            kr[i + 1] = f2key(v.y);
+            kr[i + 2] = f2key(v.z);
+            kr[i + 3] = f2key(v.w);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (4 * j4 + c < s) vmask |= 1ull << (i + c);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kSelectItems; ++i) {
+            const int j = i * kSelectThreads + tid;
+            kr[i] = j < s ? f2key(x[j]) : 0u;
+            if (j < s) vmask |= 1ull << i;
+        }
     }
     const bool want_l = l >= 1 && l <= s;
     const bool want_h = h >= 1 && h <= s;
@@ -88,7 +118,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(const float* __restri
     for (int i = tid; i < kSubMax; i += kSelectThreads)
         sub[i] = i < msub ? f2key(x[(int)((float)i * ((float)s / (float)msub))]) : 0xFFFFFFFFu;
     __syncthreads();
-    bitonic_sort_lds<kSelectThreads>(sub, kSubMax);
+    sort_pow2_lds<kSelectThreads>(sub, kSubMax);
     if (tid == 0) {
         uint32_t lo = 0u, hi = 0xFFFFFFFFu;
         if (want_l) {
@@ -108,8 +138,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(const float* __restri
     uint32_t nbelow = 0u, nin = 0u;
 #pragma unroll
     for (int i = 0; i < kSelectItems; ++i) {
-        const int j = i * kSelectThreads + tid;
-        if (j < s) { nbelow += kr[i] < wlo; nin += (kr[i] >= wlo && kr[i] <= whi); }
+        if ((vmask >> i) & 1ull) { nbelow += kr[i] < wlo; nin += (kr[i] >= wlo && kr[i] <= whi); }
     }
     const unsigned long long NLO = block_sum_u64<kSelectThreads>((unsigned long long)nbelow, s_redu);
     uint32_t W = 0u;
@@ -130,13 +159,12 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(const float* __restri
     if (fast) {
 #pragma unroll
         for (int i = 0; i < kSelectItems; ++i) {
-            const int j = i * kSelectThreads + tid;
-            if (j < s && kr[i] >= wlo && kr[i] <= whi) win[pos++] = kr[i];
+            if (((vmask >> i) & 1ull) && kr[i] >= wlo && kr[i] <= whi) win[pos++] = kr[i];
         }
-        const int wp = next_pow2((int)W);
+        const int wp = max(next_pow2((int)W), 64);
         for (int e = (int)W + tid; e < wp; e += kSelectThreads) win[e] = 0xFFFFFFFFu;
         __syncthreads();
-        bitonic_sort_lds<kSelectThreads>(win, wp);
+        sort_pow2_lds<kSelectThreads>(win, wp);
         const long long nlo = s_nlo;
         const int i0 = want_l ? (int)(l - 1 - nlo) : 0;
         const int i1 = want_h ? (int)(h - 1 - nlo) : (int)W - 1;
@@ -159,8 +187,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(const float* __restri
             const uint32_t p0 = s_pre[0], p1 = s_pre[1];
 #pragma unroll
             for (int i = 0; i < kSelectItems; ++i) {
-                const int j = i * kSelectThreads + tid;
-                if (j < s) {
+                if ((vmask >> i) & 1ull) {
                     const uint32_t kk = kr[i];
                     const uint32_t d = (kk >> shift) & 0xFFu;
                     if ((kk & hmask) == (p0 & hmask)) atomicAdd(&hist[0][d], 1u);
@@ -188,16 +215,14 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(const float* __restri
         uint32_t mine = 0u;
 #pragma unroll
         for (int i = 0; i < kSelectItems; ++i) {
-            const int j = i * kSelectThreads + tid;
-            if (j < s && kr[i] >= key_l && kr[i] <= key_h) ++mine;
+            if (((vmask >> i) & 1ull) && kr[i] >= key_l && kr[i] <= key_h) ++mine;
         }
         uint32_t total = 0u;
         uint32_t cpos = block_exclusive_scan<kSelectThreads>(mine, &total, scr);
         const uint32_t stride = (total + kCandMax - 1) / kCandMax > 0 ? (total + kCandMax - 1) / kCandMax : 1u;
 #pragma unroll
         for (int i = 0; i < kSelectItems; ++i) {
-            const int j = i * kSelectThreads + tid;
-            if (j < s && kr[i] >= key_l && kr[i] <= key_h) {
+            if (((vmask >> i) & 1ull) && kr[i] >= key_l && kr[i] <= key_h) {
                 if (cpos % stride == 0u) sub[cpos / stride] = kr[i];
                 ++cpos;
             }
@@ -206,7 +231,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(const float* __restri
         __syncthreads();
         for (int e = cc + tid; e < kCandMax; e += kSelectThreads) sub[e] = 0xFFFFFFFFu;
         __syncthreads();
-        bitonic_sort_lds<kSelectThreads>(sub, kCandMax);
+        sort_pow2_lds<kSelectThreads>(sub, kCandMax);
         csorted = sub;
         if (cc < 1) cc = 1;
     }

@@ -1,8 +1,8 @@
 // Streaming (HBM-bound) kernels of the Fast LapSum solver (gfx950).
 //
 //  k_filter      the single streaming pass of the bracketing path (Fast
-//                LapSum paper, gist.science section 2.2, "Streaming y
-//                Filtrado"): scores below a_L are folded into
+//                LapSum paper, gist.science summary section 2.2, bracketing
+//                step 2): scores below a_L are folded into
 //                S_L = sum e^{(r - a_L)/t}, scores at or above a_R into
 //                S_R = sum e^{(a_R - r)/t}, and the middle band is kept,
 //                already split into value-ordered buckets.  Its last
@@ -17,9 +17,11 @@
 // in flight per thread (the host picks the scalar variant for misaligned
 // pointers).  Reductions: fp32 within one float4, fp64 across float4s and
 // workgroups, combined in a fixed order (bitwise reproducible).
+#include <algorithm>
 #include <cmath>
 
 #include "lapsum_launch.h"
+#include "lapsum_streamio.h"
 
 namespace lapsum {
 
@@ -40,15 +42,51 @@ struct FilterPart {
 };
 
 constexpr int kQueueCap = 2048;  // band scores a workgroup holds in LDS before spilling
+constexpr int kQueuePerWave = kQueueCap / (kStreamThreads / 64);  // each wave appends to its own slice
 
+// Launch shapes of the tiled passes (tile = kStreamThreads * V float4).  The
+// filter ends every workgroup with an LDS queue flush and six reductions, so
+// a bounded number of workgroups walk the tiles; the light passes run one
+// tile per workgroup up to the partials' capacity.
+constexpr int kFilterV = 4, kFilterGrid = 1536;
+constexpr int kProbsV = 2, kProbsGrid = kMaxStreamParts;
+constexpr int kReduceV = 4, kReduceGrid = 8192;
+constexpr int kApplyV = 1, kApplyGrid = 1 << 24;
 // Traversal order of the second pass over an array: walking it backwards
 // starts on the part the previous pass read last, which the 256 MB
 // memory-side cache may still hold.
 constexpr int kProbsReverse = 1;
 constexpr int kApplyReverse = 1;
-// non-temporal loads for the read-only passes
+// non-temporal loads for the read-only inputs
 constexpr bool kFilterNT = true;
+constexpr bool kProbsNT = true;
 constexpr bool kReduceNT = true;
+constexpr bool kApplyNT = true;
+
+template <int V>
+int tiled_grid(long long n4, int cap) {
+    const long long t = stream_tiles<V>(n4);
+    return (int)std::max<long long>(1, std::min<long long>(t, cap));
+}
+
+// sum over a workgroup of NT threads of part[i * stride + off], i < nparts, in a
+// fixed order (each thread a strided subset in batches of 8 loads, then the
+// block reduction)
+template <int NT>
+LS_DEV double sum_parts(const double* part, int stride, int off, int nparts, double* s_red) {
+    double a = 0.0;
+    for (int i0 = threadIdx.x; i0 < nparts; i0 += 8 * NT) {
+        double v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int i = i0 + q * NT;
+            v[q] = i < nparts ? part[(size_t)i * stride + off] : 0.0;
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) a += v[q];
+    }
+    return block_sum<NT>(a, s_red);
+}
 
 // ---------------------------------------------------------------------------
 // streaming filter
@@ -102,7 +140,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_filter(const float* __restri
     __shared__ float q[kQueueCap];
     __shared__ uint32_t lcnt[kMaxBuckets];
     __shared__ uint32_t gbase[kMaxBuckets];
-    __shared__ uint32_t s_qn;
+    __shared__ uint32_t s_wq[kStreamThreads / 64];
     __shared__ double s_red[kStreamThreads / 64];
     __shared__ unsigned long long s_redu[kStreamThreads / 64];
     __shared__ int s_nan;
@@ -115,16 +153,17 @@ __global__ __launch_bounds__(kStreamThreads) void k_filter(const float* __restri
     for (int i = tid; i <= fs.ng; i += kStreamThreads) sp[i] = sp_g[i];
     for (int i = tid; i < fs.ng; i += kStreamThreads) iw[i] = iw_g[i];
     for (int i = tid; i < nb; i += kStreamThreads) lcnt[i] = 0u;
-    if (tid == 0) { s_qn = 0u; s_nan = 0; }
+    if (tid == 0) s_nan = 0;
     fs.sp = sp; fs.iw = iw; fs.bucket_cnt = bucket_cnt; fs.bucket_vals = bucket_vals;
     __syncthreads();
 
     // Per score: one exponential, e = e^{-|r - edge|/t} with edge a_L below the
     // band and a_R otherwise; it feeds S_L (below) or S_R (at/above a_R).
     // Only the count at/above a_R is kept: the count below follows from
-    // n - band - above - NaNs.  Band scores (rare) go to an LDS queue with one
-    // LDS atomic per wave; NaNs land there too and are sorted out at the
-    // flush; +-inf shows up in max |r|.
+    // n - band - above - NaNs.  Band scores (rare) go to the wave's own slice
+    // of an LDS queue, its fill count kept in a wave-uniform register (no
+    // atomic, no wait); NaNs land there too and are sorted out at the flush;
+    // +-inf shows up in max |r|.
     double SL = 0.0, SR = 0.0, BL = 0.0, BR = 0.0;
     uint32_t cR = 0u;
     uint32_t nnan = 0u;
@@ -142,12 +181,14 @@ __global__ __launch_bounds__(kStreamThreads) void k_filter(const float* __restri
         amax = fmaxf(amax, fabsf(v));
         band = !(below || above);
     };
+    float* const wq = q + (tid >> 6) * kQueuePerWave;
+    uint32_t wfill = 0u;  // wave-uniform
     auto put = [&](float v, uint32_t pos) {
-        if (pos < (uint32_t)kQueueCap) q[pos] = v;
+        if (pos < (uint32_t)kQueuePerWave) wq[pos] = v;
         else band_direct(fs, v, BL, BR, nan, nnan);
     };
     // four scores, all lanes of the wave active; the band scores among them
-    // (rare) take one LDS atomic for the whole wave
+    // (rare) are appended to the wave's queue slice
     auto quad = [&](float4 qv) {
         float eL = 0.0f, eR = 0.0f;
         bool b0, b1, b2, b3;
@@ -161,9 +202,8 @@ __global__ __launch_bounds__(kStreamThreads) void k_filter(const float* __restri
         if (m0 | m1 | m2 | m3) {
             const uint32_t c0 = (uint32_t)popc64(m0), c1 = (uint32_t)popc64(m1), c2 = (uint32_t)popc64(m2);
             const uint32_t tot = c0 + c1 + c2 + (uint32_t)popc64(m3);
-            uint32_t base = 0u;
-            if (lane == 0) base = atomicAdd(&s_qn, tot);
-            base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+            const uint32_t base = wfill;
+            wfill += tot;
             if (b0) put(qv.x, base + (uint32_t)mbcnt(m0));
             if (b1) put(qv.y, base + c0 + (uint32_t)mbcnt(m1));
             if (b2) put(qv.z, base + c0 + c1 + (uint32_t)mbcnt(m2));
@@ -182,7 +222,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_filter(const float* __restri
 
     if (VEC) {
         const long long n4 = n >> 2;
-        stream_f4<4, kFilterNT>(reinterpret_cast<const float4*>(r), n4, false,
+        tile_f4_pipelined<kFilterV, kFilterNT>(reinterpret_cast<const float4*>(r), n4,
                      [&](float4 qv, long long) { quad(qv); },
                      [&](float4 qv, long long) { one_lane(qv.x); one_lane(qv.y); one_lane(qv.z); one_lane(qv.w); });
         if (blockIdx.x == 0 && tid < 4) {
@@ -195,8 +235,8 @@ __global__ __launch_bounds__(kStreamThreads) void k_filter(const float* __restri
     }
 
     // ---- flush the LDS queue: bucket by value, one global atomic per bucket ----
+    if (lane == 0) s_wq[tid >> 6] = min(wfill, (uint32_t)kQueuePerWave);
     __syncthreads();
-    const uint32_t nq = min(s_qn, (uint32_t)kQueueCap);
     constexpr int QPT = kQueueCap / kStreamThreads;
     int bk[QPT];
     uint32_t rk[QPT];
@@ -204,7 +244,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_filter(const float* __restri
     for (int k = 0; k < QPT; ++k) {
         const uint32_t i = (uint32_t)tid + (uint32_t)k * kStreamThreads;
         bk[k] = -1;
-        if (i < nq) {
+        if (i % (uint32_t)kQueuePerWave < s_wq[i / (uint32_t)kQueuePerWave]) {
             const float v = q[i];
             if (v != v) { nan = 1; ++nnan; continue; }
             band_sums(fs, v, BL, BR);
@@ -333,10 +373,11 @@ __global__ __launch_bounds__(kStreamThreads) void k_filter_finalize(const Filter
 void launch_filter(const float* r, long long n, double t, Ctl* ctl, const float* sp, const float* iw,
                    uint32_t* bucket_cnt, uint32_t* bucket_vals, int cap, double* part, unsigned long long* /*partc*/,
                    HostSummary* hs_dev, unsigned int seq, hipStream_t st) {
-    const int blocks = stream_blocks(n);
     const float ls = (float)(1.4426950408889634 / t);
     FilterPart* fp = reinterpret_cast<FilterPart*>(part);
-    if ((reinterpret_cast<uintptr_t>(r) & 15u) == 0u)
+    const bool vec = (reinterpret_cast<uintptr_t>(r) & 15u) == 0u;
+    const int blocks = vec ? tiled_grid<kFilterV>(n >> 2, kFilterGrid) : stream_blocks(n);
+    if (vec)
         hipLaunchKernelGGL(k_filter<true>, dim3(blocks), dim3(kStreamThreads), 0, st, r, n, ls, ctl, sp, iw,
                            bucket_cnt, bucket_vals, cap, fp);
     else
@@ -361,8 +402,6 @@ __global__ __launch_bounds__(kStreamThreads) void k_probs(const float* __restric
     const double b = ctl->b;
     const int tid = threadIdx.x;
     double sum = 0.0;
-    const long long stride = (long long)gridDim.x * kStreamThreads;
-    const long long gt = (long long)blockIdx.x * kStreamThreads + tid;
     auto one = [&](float v) -> float {
         const float x = (float)(((double)v - b) * inv_t);
         const float q = lap_cdf_f(x);
@@ -373,39 +412,39 @@ __global__ __launch_bounds__(kStreamThreads) void k_probs(const float* __restric
         const long long n4 = n >> 2;
         float4* p4 = reinterpret_cast<float4*>(p);
         auto body = [&](float4 q, long long idx) { p4[idx] = make_float4(one(q.x), one(q.y), one(q.z), one(q.w)); };
-        stream_f4<4>(reinterpret_cast<const float4*>(r), n4, rev != 0, body, body);
+        tile_f4<kProbsV, kProbsNT>(reinterpret_cast<const float4*>(r), n4, rev != 0, body, body);
         if (blockIdx.x == 0) {
             const long long j = (n4 << 2) + tid;
             if (tid < 4 && j < n) p[j] = one(r[j]);
         }
     } else {
-        for (long long i = gt; i < n; i += stride) p[i] = one(r[i]);
+        const long long stride = (long long)gridDim.x * kStreamThreads;
+        for (long long i = (long long)blockIdx.x * kStreamThreads + tid; i < n; i += stride) p[i] = one(r[i]);
     }
     const double tot = block_sum<kStreamThreads>(sum, s_red);
     if (tid == 0) part[blockIdx.x] = tot;
 }
 
 // sum of the p pass's partials (for statistics only)
-__global__ __launch_bounds__(kStreamThreads) void k_sum_partials(const double* part, int nparts, double* out) {
-    __shared__ double s_red[kStreamThreads / 64];
-    double a = 0.0;
-    for (int b = threadIdx.x; b < nparts; b += kStreamThreads) a += part[b];
-    const double T = block_sum<kStreamThreads>(a, s_red);
+__global__ __launch_bounds__(1024) void k_sum_partials(const double* part, int nparts, double* out) {
+    __shared__ double s_red[1024 / 64];
+    const double T = sum_parts<1024>(part, 1, 0, nparts, s_red);
     if (threadIdx.x == 0) *out = T;
 }
 
-void launch_sum_p(Ctl* ctl, const double* part, long long n, hipStream_t st) {
-    hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(kStreamThreads), 0, st, part, stream_blocks(n), &ctl->sum_p);
+void launch_sum_p(Ctl* ctl, const double* part, int nparts, hipStream_t st) {
+    hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(1024), 0, st, part, nparts, &ctl->sum_p);
 }
 
-void launch_probs(const float* r, long long n, double t, float* p, Ctl* ctl, double* part, hipStream_t st) {
-    const int blocks = stream_blocks(n);
+int launch_probs(const float* r, long long n, double t, float* p, Ctl* ctl, double* part, hipStream_t st) {
     const bool vec = ((reinterpret_cast<uintptr_t>(r) | reinterpret_cast<uintptr_t>(p)) & 15u) == 0u;
+    const int blocks = vec ? tiled_grid<kProbsV>(n >> 2, kProbsGrid) : stream_blocks(n);
     if (vec)
         hipLaunchKernelGGL(k_probs<true>, dim3(blocks), dim3(kStreamThreads), 0, st, r, n, 1.0 / t, p, ctl, part,
                            kProbsReverse);
     else
         hipLaunchKernelGGL(k_probs<false>, dim3(blocks), dim3(kStreamThreads), 0, st, r, n, 1.0 / t, p, ctl, part, 0);
+    return blocks;
 }
 
 // ---------------------------------------------------------------------------
@@ -421,8 +460,6 @@ __global__ __launch_bounds__(kStreamThreads) void k_vjp_reduce(const float* __re
     const double b = *bptr;
     const int tid = threadIdx.x;
     double sfg = 0.0, sf = 0.0;
-    const long long stride = (long long)gridDim.x * kStreamThreads;
-    const long long gt = (long long)blockIdx.x * kStreamThreads + tid;
     auto quad = [&](float4 q, float4 gg) {
         const float f0 = lap_pdf_f((float)(((double)q.x - b) * inv_t));
         const float f1 = lap_pdf_f((float)(((double)q.y - b) * inv_t));
@@ -434,8 +471,8 @@ __global__ __launch_bounds__(kStreamThreads) void k_vjp_reduce(const float* __re
     if (VEC) {
         const long long n4 = n >> 2;
         auto body = [&](float4 q, float4 gg, long long) { quad(q, gg); };
-        stream_f4x2<4, kReduceNT>(reinterpret_cast<const float4*>(r), reinterpret_cast<const float4*>(g), n4, false, body,
-                                  body);
+        tile_f4x2<kReduceV, kReduceNT>(reinterpret_cast<const float4*>(r), reinterpret_cast<const float4*>(g), n4,
+                                       false, body, body);
         if (blockIdx.x == 0) {
             const long long j = (n4 << 2) + tid;
             if (tid < 4 && j < n) {
@@ -444,7 +481,8 @@ __global__ __launch_bounds__(kStreamThreads) void k_vjp_reduce(const float* __re
             }
         }
     } else {
-        for (long long i = gt; i < n; i += stride) {
+        const long long stride = (long long)gridDim.x * kStreamThreads;
+        for (long long i = (long long)blockIdx.x * kStreamThreads + tid; i < n; i += stride) {
             const float f = lap_pdf_f((float)(((double)r[i] - b) * inv_t));
             sfg += (double)(f * g[i]); sf += (double)f;
         }
@@ -452,6 +490,14 @@ __global__ __launch_bounds__(kStreamThreads) void k_vjp_reduce(const float* __re
     const double t0 = block_sum<kStreamThreads>(sfg, s_red);
     const double t1 = block_sum<kStreamThreads>(sf, s_red);
     if (tid == 0) { part[2 * blockIdx.x] = t0; part[2 * blockIdx.x + 1] = t1; }
+}
+
+// c = sum f g / sum f from the reduce pass's partials, in a fixed order
+__global__ __launch_bounds__(1024) void k_vjp_c(const double* part, int nparts, Ctl* ctl) {
+    __shared__ double s_red[1024 / 64];
+    const double T0 = sum_parts<1024>(part, 2, 0, nparts, s_red);
+    const double T1 = sum_parts<1024>(part, 2, 1, nparts, s_red);
+    if (threadIdx.x == 0) { ctl->sumfg = T0; ctl->sumf = T1; ctl->c = T0 / T1; }
 }
 
 // f/t = e^{-|x|}/(2t) evaluated as one exp2 with log2(1/(2t)) folded into the
@@ -462,35 +508,10 @@ __global__ __launch_bounds__(kStreamThreads) void k_vjp_reduce(const float* __re
 template <bool VEC>
 __global__ __launch_bounds__(kStreamThreads) void k_vjp_apply(const float* __restrict__ r, const float* __restrict__ g,
                                                                long long n, const double* bptr, double inv_t,
-                                                               float log2_inv_2t, const double* part, int nparts,
-                                                               Ctl* ctl, float* __restrict__ grad, int rev) {
-    __shared__ double s_red[kStreamThreads / 64];
-    __shared__ double s_c;
-    // every workgroup forms c = sum f g / sum f from the reduce pass's partials
-    // in the same fixed order, so all of them use the identical c
-    {
-        constexpr int PP = kMaxStreamBlocks / kStreamThreads;
-        double2 pv[PP];
-#pragma unroll
-        for (int q = 0; q < PP; ++q) {
-            const int bb = threadIdx.x + q * kStreamThreads;
-            pv[q] = bb < nparts ? reinterpret_cast<const double2*>(part)[bb] : make_double2(0.0, 0.0);
-        }
-        double a0 = 0.0, a1 = 0.0;
-#pragma unroll
-        for (int q = 0; q < PP; ++q) { a0 += pv[q].x; a1 += pv[q].y; }
-        const double T0 = block_sum<kStreamThreads>(a0, s_red);
-        const double T1 = block_sum<kStreamThreads>(a1, s_red);
-        if (threadIdx.x == 0) {
-            s_c = T0 / T1;
-            if (blockIdx.x == 0) { ctl->sumfg = T0; ctl->sumf = T1; ctl->c = T0 / T1; }
-        }
-        __syncthreads();
-    }
+                                                               float log2_inv_2t, const Ctl* ctl,
+                                                               float* __restrict__ grad, int rev) {
     const double b = *bptr;
-    const float c = (float)s_c;
-    const long long stride = (long long)gridDim.x * kStreamThreads;
-    const long long gt = (long long)blockIdx.x * kStreamThreads + threadIdx.x;
+    const float c = (float)ctl->c;
     auto one = [&](float v, float gv) -> float {
         const float x = (float)(((double)v - b) * inv_t);
         const float f_over_t_2p32 = __builtin_amdgcn_exp2f(fmaf(-fabsf(x), 1.4426950408889634f, log2_inv_2t));
@@ -502,30 +523,35 @@ __global__ __launch_bounds__(kStreamThreads) void k_vjp_apply(const float* __res
         auto body = [&](float4 q, float4 h, long long idx) {
             o4[idx] = make_float4(one(q.x, h.x), one(q.y, h.y), one(q.z, h.z), one(q.w, h.w));
         };
-        stream_f4x2<2>(reinterpret_cast<const float4*>(r), reinterpret_cast<const float4*>(g), n4, rev != 0, body, body);
+        tile_f4x2<kApplyV, kApplyNT>(reinterpret_cast<const float4*>(r), reinterpret_cast<const float4*>(g), n4,
+                                     rev != 0, body, body);
         if (blockIdx.x == 0) {
             const long long j = (n4 << 2) + threadIdx.x;
             if (threadIdx.x < 4 && j < n) grad[j] = one(r[j], g[j]);
         }
     } else {
-        for (long long i = gt; i < n; i += stride) grad[i] = one(r[i], g[i]);
+        const long long stride = (long long)gridDim.x * kStreamThreads;
+        for (long long i = (long long)blockIdx.x * kStreamThreads + threadIdx.x; i < n; i += stride)
+            grad[i] = one(r[i], g[i]);
     }
 }
 
 void launch_vjp(const float* r, const float* g, long long n, double t, const double* b, float* grad, Ctl* ctl,
                 double* part, hipStream_t st, hipEvent_t* ev_mid) {
-    const int blocks = stream_blocks(n);
     const bool vec = ((reinterpret_cast<uintptr_t>(r) | reinterpret_cast<uintptr_t>(g) |
                        reinterpret_cast<uintptr_t>(grad)) & 15u) == 0u;
     const double inv_t = 1.0 / t;
-    if (vec) hipLaunchKernelGGL(k_vjp_reduce<true>, dim3(blocks), dim3(kStreamThreads), 0, st, r, g, n, b, inv_t, part);
-    else hipLaunchKernelGGL(k_vjp_reduce<false>, dim3(blocks), dim3(kStreamThreads), 0, st, r, g, n, b, inv_t, part);
+    const int rblocks = vec ? tiled_grid<kReduceV>(n >> 2, kReduceGrid) : stream_blocks(n);
+    if (vec) hipLaunchKernelGGL(k_vjp_reduce<true>, dim3(rblocks), dim3(kStreamThreads), 0, st, r, g, n, b, inv_t, part);
+    else hipLaunchKernelGGL(k_vjp_reduce<false>, dim3(rblocks), dim3(kStreamThreads), 0, st, r, g, n, b, inv_t, part);
+    hipLaunchKernelGGL(k_vjp_c, dim3(1), dim3(1024), 0, st, part, rblocks, ctl);
     if (ev_mid) (void)hipEventRecord(*ev_mid, st);
     const float l2 = (float)(std::log2(0.5 * inv_t) + 32.0);
-    if (vec) hipLaunchKernelGGL(k_vjp_apply<true>, dim3(blocks), dim3(kStreamThreads), 0, st, r, g, n, b, inv_t, l2,
-                                part, blocks, ctl, grad, kApplyReverse);
-    else hipLaunchKernelGGL(k_vjp_apply<false>, dim3(blocks), dim3(kStreamThreads), 0, st, r, g, n, b, inv_t, l2,
-                            part, blocks, ctl, grad, 0);
+    const int ablocks = vec ? tiled_grid<kApplyV>(n >> 2, kApplyGrid) : stream_blocks(n);
+    if (vec) hipLaunchKernelGGL(k_vjp_apply<true>, dim3(ablocks), dim3(kStreamThreads), 0, st, r, g, n, b, inv_t, l2,
+                                ctl, grad, kApplyReverse);
+    else hipLaunchKernelGGL(k_vjp_apply<false>, dim3(ablocks), dim3(kStreamThreads), 0, st, r, g, n, b, inv_t, l2,
+                            ctl, grad, 0);
 }
 
 // ---------------------------------------------------------------------------

@@ -22,7 +22,7 @@
  * [a_L, a_R); one streaming pass folds the scores outside it into tail sums;
  * only the band is sorted and solved; the bracket is certified and widened
  * when it fails, with the full sort as the fallback -- the arxivdaily
- * abstract's "certification pass" and "full-sort fallback").
+ * abstract names both the certification pass and the full-sort fallback).
  *
  * Conventions for every entry point:
  *  - Pointers to scores, p, g, grad and b are DEVICE pointers (gfx950), owned

@@ -1,7 +1,8 @@
 /*
  * lapsum_testing.h -- entry points that expose single stages of the Fast
  * LapSum solver for parity tests.  They run the same kernels as
- * lapsum_forward_ex; each waits for the device before returning.
+ * lapsum_forward_ex; each waits for the device before returning, except the
+ * two bandwidth-ceiling kernels at the end.
  * All pointers are device pointers unless named *_host.
  */
 #ifndef LAPSUM_TESTING_H_
@@ -52,6 +53,28 @@ lapsum_status_t lapsum_test_filter(const float* scores, int64_t n, float t, floa
                                    int64_t* counts_host, double* sums_host, float* band_out,
                                    int64_t band_cap, int64_t* band_size_host, int32_t* nbuckets_host,
                                    int64_t* bucket_sizes_host, lapsum_stream_t stream);
+
+/*
+ * The bracket's sample ranks (section 2.2, bracketing step 1), host only:
+ * for a sample of s noised scores each above b with probability 1 - q,
+ * l = the largest rank with P(Bin(s, q) < l) <= delta and h = the smallest
+ * with P(Bin(s, q) >= h) <= delta, so a_L = x_(l) and a_R = x_(h) (1-based;
+ * l = 0 and h = s + 1 mean an open end).  Needs no device.
+ */
+lapsum_status_t lapsum_test_binomial_ranks(int64_t s, double q, double delta, int64_t* l, int64_t* h);
+
+/*
+ * Plain streaming kernels: the achievable HBM ceilings the solver's
+ * streaming passes are compared with, and a transfer of known size for
+ * calibrating hardware traffic counters.  lapsum_test_copy copies n fp32
+ * from src to dst (device, 16-byte aligned, not overlapping);
+ * lapsum_test_read reads n fp32 from src (16-byte aligned) and may write
+ * to sink (device fp32[256]).  Both are asynchronous on `stream` (they do
+ * not wait for the device); misaligned or NULL pointers and n < 1 give
+ * LAPSUM_ERR_INVALID_ARGUMENT before any launch.
+ */
+lapsum_status_t lapsum_test_copy(const float* src, float* dst, int64_t n, lapsum_stream_t stream);
+lapsum_status_t lapsum_test_read(const float* src, int64_t n, float* sink, lapsum_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -1,0 +1,145 @@
+"""The C ABI on the host, no device needed.
+
+liblapsum.so loads, exports every function the public headers declare, its
+structs have the layout a C compiler gives the headers, argument errors come
+back before anything touches the device, and the host-side order-statistic
+ranks of the bracket agree exactly with the oracle's.
+"""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+import differentiable_exact_budget_amd as L
+from differentiable_exact_budget_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INCLUDE = os.path.join(ROOT, "include")
+HEADERS = ("lapsum.h", "lapsum_testing.h")
+
+INVALID = 1  # LAPSUM_ERR_INVALID_ARGUMENT
+FAKE = 4096  # a non-NULL, 16-byte aligned address that is never dereferenced
+
+
+def declared_functions():
+    names = []
+    for h in HEADERS:
+        text = open(os.path.join(INCLUDE, h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:lapsum_status_t|const char\s*\*|void|size_t)\s+(lapsum_\w+)\s*\(", text, re.M)
+    return names
+
+
+def test_library_exports_every_declared_function():
+    lib = L.lib()
+    names = declared_functions()
+    assert len(names) >= 14
+    for name in names:
+        assert hasattr(lib, name), f"{name} is declared but not exported"
+    assert sorted(names) == sorted(_binding.EXPORTED), "binding list out of step with the headers"
+
+
+def c_layout():
+    """sizeof / offsetof of the ABI structs as gcc sees the public header."""
+    fields_o = [f for f, _ in _binding.Options._fields_]
+    fields_s = [f for f, _ in _binding.Stats._fields_]
+    src = ['#include <stddef.h>', '#include <stdio.h>', '#include "lapsum.h"', "int main(void) {",
+           'printf("Options %zu\\n", sizeof(lapsum_options_t));',
+           'printf("Stats %zu\\n", sizeof(lapsum_stats_t));']
+    for f in fields_o:
+        src.append(f'printf("Options.{f} %zu\\n", offsetof(lapsum_options_t, {f}));')
+    for f in fields_s:
+        src.append(f'printf("Stats.{f} %zu\\n", offsetof(lapsum_stats_t, {f}));')
+    src.append("return 0; }")
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "layout.c")
+        exe = os.path.join(d, "layout")
+        open(c, "w").write("\n".join(src))
+        subprocess.run(["gcc", "-std=c11", "-I", INCLUDE, c, "-o", exe], check=True)
+        out = subprocess.run([exe], check=True, capture_output=True, text=True).stdout
+    return dict(line.rsplit(" ", 1) for line in out.strip().splitlines())
+
+
+def test_struct_layout_matches_header():
+    lay = c_layout()
+    assert int(lay["Options"]) == ctypes.sizeof(_binding.Options)
+    assert int(lay["Stats"]) == ctypes.sizeof(_binding.Stats)
+    for f, _ in _binding.Options._fields_:
+        assert int(lay[f"Options.{f}"]) == getattr(_binding.Options, f).offset, f
+    for f, _ in _binding.Stats._fields_:
+        assert int(lay[f"Stats.{f}"]) == getattr(_binding.Stats, f).offset, f
+
+
+def test_default_options_and_status_strings():
+    o = L.default_options()
+    assert o.path == 0 and o.max_widen == 2
+    assert o.sample_factor == 4.0 and o.delta == 1e-5
+    assert o.margin_scale == 1.0 and o.auto_threshold == 1_000_000
+    assert 1 <= o.bucket_capacity <= 16384
+    lib = L.lib()
+    seen = set()
+    for code in range(6):
+        s = lib.lapsum_status_string(code).decode()
+        assert s and s not in seen
+        seen.add(s)
+    assert lib.lapsum_status_string(99).decode() == "unknown status"
+
+
+def test_workspace_bytes_grows_with_n():
+    lib = L.lib()
+    a, b, c = (lib.lapsum_workspace_bytes(n) for n in (1, 10**6, 10**8))
+    assert 0 < a <= b < c
+    assert c >= 4 * 10**8  # at least one fp32 array of n for the full-sort fallback
+
+
+@pytest.mark.parametrize("n,k,t", [
+    (0, 1.0, 0.1), (-5, 1.0, 0.1), (2**32, 1.0, 0.1),           # n out of range
+    (100, 0.0, 0.1), (100, 100.0, 0.1), (100, -1.0, 0.1),       # k not in (0, n)
+    (100, float("nan"), 0.1), (100, float("inf"), 0.1),
+    (100, 5.0, 0.0), (100, 5.0, -1.0), (100, 5.0, float("nan")), (100, 5.0, float("inf")),  # t
+])
+def test_forward_rejects_bad_arguments_before_any_launch(n, k, t):
+    lib = L.lib()
+    assert lib.lapsum_forward(FAKE, n, k, t, FAKE, FAKE, None) == INVALID
+    assert lib.lapsum_forward_ex(FAKE, n, k, t, FAKE, FAKE, None, None, None) == INVALID
+
+
+def test_forward_rejects_null_pointers_and_bad_options():
+    lib = L.lib()
+    assert lib.lapsum_forward(None, 100, 5.0, 0.1, FAKE, FAKE, None) == INVALID
+    assert lib.lapsum_forward(FAKE, 100, 5.0, 0.1, None, FAKE, None) == INVALID
+    assert lib.lapsum_forward(FAKE, 100, 5.0, 0.1, FAKE, None, None) == INVALID
+    for field, value in (("path", 4), ("path", -1), ("bucket_capacity", 0), ("bucket_capacity", 1 << 20),
+                         ("sample_factor", 0.0), ("delta", 0.0), ("delta", 0.5), ("margin_scale", -1.0),
+                         ("max_widen", -1)):
+        o = L.default_options(**{field: value})
+        rc = lib.lapsum_forward_ex(FAKE, 100, 5.0, 0.1, FAKE, FAKE, ctypes.byref(o), None, None)
+        assert rc == INVALID, (field, value)
+
+
+def test_vjp_and_stage_entry_points_reject_bad_arguments():
+    lib = L.lib()
+    assert lib.lapsum_vjp(None, None, FAKE, 100, 0.1, FAKE, FAKE, None) == INVALID
+    assert lib.lapsum_vjp(FAKE, None, None, 100, 0.1, FAKE, FAKE, None) == INVALID
+    assert lib.lapsum_vjp(FAKE, None, FAKE, 100, 0.1, None, FAKE, None) == INVALID
+    assert lib.lapsum_vjp(FAKE, None, FAKE, 100, 0.1, FAKE, None, None) == INVALID
+    assert lib.lapsum_vjp(FAKE, None, FAKE, 0, 0.1, FAKE, FAKE, None) == INVALID
+    assert lib.lapsum_vjp(FAKE, None, FAKE, 100, 0.0, FAKE, FAKE, None) == INVALID
+    assert lib.lapsum_test_sort(None, 10, FAKE, None) == INVALID
+    assert lib.lapsum_test_copy(FAKE + 4, FAKE, 10, None) == INVALID  # misaligned
+    assert lib.lapsum_test_read(FAKE, 0, FAKE, None) == INVALID
+    lo, hi = ctypes.c_int64(), ctypes.c_int64()
+    assert lib.lapsum_test_binomial_ranks(10, 1.0, 1e-5, ctypes.byref(lo), ctypes.byref(hi)) == INVALID
+    assert lib.lapsum_test_binomial_ranks(0, 0.5, 1e-5, ctypes.byref(lo), ctypes.byref(hi)) == INVALID
+
+
+@pytest.mark.parametrize("s", [1, 7, 100, 1000, 12650, 40000])
+@pytest.mark.parametrize("q", [1e-3, 0.02, 0.5, 0.98, 0.999, 0.9999])
+@pytest.mark.parametrize("delta", [1e-5, 1e-3, 0.1])
+def test_bracket_ranks_match_oracle(oracle_mod, s, q, delta):
+    lo, hi = ctypes.c_int64(), ctypes.c_int64()
+    assert L.lib().lapsum_test_binomial_ranks(s, q, delta, ctypes.byref(lo), ctypes.byref(hi)) == 0
+    assert (lo.value, hi.value) == oracle_mod.binomial_bounds(s, q, delta)

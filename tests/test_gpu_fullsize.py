@@ -1,0 +1,59 @@
+"""GPU parity at the full sizes of the bracketing workloads.
+
+Workloads: C3 (10^7 Student-t), C4 (10^8 mixture), and C5 (10^7 with a
+cluster of 10^5 tied scores at the quantile), C5 also forced onto the
+full-sort fallback.  Each runs in the launch configuration bench.py times:
+default options, inputs resident on the device, one stream.
+
+The oracle solves each whole input in fp64 in a few seconds on the host's
+cores, so every output element is compared, not a sample.  Where the bracket
+was certified, its bookkeeping (counts, and G at both ends) is compared with
+the oracle's direct sums over all n.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_helpers import check_forward, check_vjp, t32, to_dev
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+L = pytest.importorskip("differentiable_exact_budget_amd")
+
+CASES = [("C3", None), ("C4", None), ("C5", None), ("C5", "fallback")]
+
+
+@pytest.mark.parametrize("name,mode", CASES, ids=["C3", "C4", "C5", "C5-forced-fallback"])
+def test_full_size(oracle_mod, name, mode):
+    print(f"\nfull-size {name} {mode or 'auto'}", flush=True)
+    r, g, cfg = workloads.config_inputs(name)
+    rd, gd = to_dev(r), to_dev(g)
+    opts = L.default_options(path=L.PATH_FORCE_FALLBACK) if mode == "fallback" else None
+    p, b, st = L.forward(rd, cfg.k, cfg.t, options=opts, stats=True)
+    grad = L.vjp(rd, gd, cfg.t, b)
+    torch.cuda.synchronize()
+    p_h, b_h, grad_h = p.cpu().numpy(), float(b.cpu().item()), grad.cpu().numpy()
+    del rd, gd, p, grad
+    torch.cuda.empty_cache()
+
+    assert st["status"] == 0
+    if mode == "fallback":
+        assert st["path_taken"] == 3
+    else:
+        assert st["path_taken"] in (2, 3)
+    if name == "C4":
+        assert st["path_taken"] == 2 and st["certified"] == 1 and st["band_size"] > 0
+
+    b_ref = check_forward(oracle_mod, r, cfg.k, cfg.t, p_h, b_h, label=name)
+    check_vjp(oracle_mod, r, g, cfg.t, b_ref, grad_h, label=name)
+
+    if st["path_taken"] == 2:
+        ref = oracle_mod.bracket(r, t32(cfg.t), st["a_L"], st["a_R"], want_band=False)
+        assert (st["count_below"], st["band_size"], st["count_above"]) == (ref["below"], ref["band"], ref["above"])
+        if np.isfinite(st["a_L"]):
+            assert abs(st["g_aL"] - ref["G_aL"]) <= 1e-6 * ref["G_aL"]
+            assert ref["G_aL"] >= cfg.k
+        if np.isfinite(st["a_R"]):
+            assert abs(st["g_aR"] - ref["G_aR"]) <= 1e-6 * max(ref["G_aR"], 1.0)
+            assert ref["G_aR"] < cfg.k
