@@ -45,6 +45,8 @@ def _load():
     lib.oracle_probs.restype = ctypes.c_double
     lib.oracle_vjp.argtypes = [_dp, _dp, ctypes.c_int64, ctypes.c_double, ctypes.c_double, _dp, _dp, _dp]
     lib.oracle_vjp.restype = None
+    lib.oracle_vjp_kt.argtypes = [_dp, _dp, ctypes.c_int64, ctypes.c_double, ctypes.c_double, _dp, _dp]
+    lib.oracle_vjp_kt.restype = None
     lib.oracle_bracket.argtypes = [_dp, ctypes.c_int64, ctypes.c_double, ctypes.c_double, ctypes.c_double,
                                    _i64p, _dp, _dp, ctypes.c_int64]
     lib.oracle_bracket.restype = ctypes.c_int64
@@ -131,6 +133,16 @@ def forward(r, k: float, t: float):
     b, _ = solve(r, k, t)
     p, s = probs(r, t, b)
     return b, p, s
+
+
+def vjp_kt(r, g, t: float, b: float):
+    """(dL/dk, dL/dt) for L = sum g_i p_i through the threshold b(k, t)."""
+    r = _f64(r)
+    g = _f64(g)
+    dk = ctypes.c_double(0.0)
+    dt = ctypes.c_double(0.0)
+    _load().oracle_vjp_kt(_ptr(r, _dp), _ptr(g, _dp), r.size, float(t), float(b), ctypes.byref(dk), ctypes.byref(dt))
+    return dk.value, dt.value
 
 
 def bracket(r, t: float, a_L: float, a_R: float, want_band: bool = True):

@@ -98,7 +98,7 @@ static int64_t chunk_lo(int64_t n, int64_t nc, int64_t c) { return (n / nc) * c 
  * Generic chunked reduction of up to 4 per-element terms.
  * kind selects the terms (see the switch in term_eval).
  */
-enum { T_G = 0, T_PROBS = 1, T_VJP = 2, T_BRACKET = 3 };
+enum { T_G = 0, T_PROBS = 1, T_VJP = 2, T_BRACKET = 3, T_VJP_KT = 4 };
 
 typedef struct {
     const double* r; const double* g; double* out; double t, b, aL, aR;
@@ -123,6 +123,10 @@ static void term_eval(int kind, const red_args_t* a, int64_t i, double v[4], int
     case T_VJP: {
         double f = lap_pdf((ri - a->b) / a->t);
         v[0] = f * a->g[i]; v[1] = f; break; }
+    case T_VJP_KT: {
+        double d = ri - a->b;
+        double f = lap_pdf(d / a->t);
+        v[0] = f * a->g[i]; v[1] = f; v[2] = f * a->g[i] * d; v[3] = f * d; break; }
     case T_BRACKET: {
         /* band is a_L <= r < a_R; below r < a_L; above r >= a_R (gist.science 2.2 step 2) */
         if (ri < a->aL) { cnt[0]++; v[0] = exp((ri - a->aL) / a->t); }
@@ -251,6 +255,26 @@ void oracle_vjp(const double* r, const double* g, int64_t n, double t, double b,
     }
     if (c_out) *c_out = c;
     if (sumf_out) *sumf_out = res[1];
+}
+
+/*
+ * Gradients of L = sum_i g_i p_i with respect to the budget k and the
+ * temperature t, through the threshold b(k, t) that G(b) = k fixes
+ * (gist.science 2.1; implicit differentiation of the budget equation).
+ * With d_i = r_i - b and f_i = 0.5 e^{-|d_i|/t}, dp_i/dx_i = f_i for
+ * x_i = d_i / t, and differentiating sum_i F(d_i / t) = k gives
+ *   db/dk = -t / sum f,        so dL/dk = sum g f / sum f;
+ *   db/dt = -mu,  mu = sum f d / sum f,
+ *                              so dL/dt = -(sum g f d - mu sum g f) / t^2.
+ */
+void oracle_vjp_kt(const double* r, const double* g, int64_t n, double t, double b,
+                   double* dk_out, double* dt_out) {
+    red_args_t a = {r, g, NULL, t, b, 0, 0};
+    double res[4];
+    reduce(T_VJP_KT, &a, n, res, NULL);
+    const double mu = res[3] / res[1];
+    if (dk_out) *dk_out = res[0] / res[1];
+    if (dt_out) *dt_out = -(res[2] - mu * res[0]) / (t * t);
 }
 
 /*

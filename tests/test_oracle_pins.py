@@ -246,6 +246,59 @@ def test_vjp_identities(oracle_mod):
 
 
 # ---------------------------------------------------------------------------
+# gradients with respect to the budget and the temperature
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("seed,n,k,t", [(11, 50, 7.3, 0.3), (12, 200, 0.7, 0.05), (13, 40, 33.0, 2.0)])
+def test_vjp_kt_central_differences(oracle_mod, seed, n, k, t):
+    """dL/dk and dL/dt against central differences of L = sum g p through
+    the oracle's own solve."""
+    rng = np.random.default_rng(seed)
+    r = rng.standard_normal(n)
+    g = rng.standard_normal(n)
+    b, _ = oracle_mod.solve(r, k, t)
+    dk, dt = oracle_mod.vjp_kt(r, g, t, b)
+    hk = 1e-6 * k
+    fdk = (_loss(oracle_mod, r, g, k + hk, t) - _loss(oracle_mod, r, g, k - hk, t)) / (2 * hk)
+    ht = 1e-6 * t
+    fdt = (_loss(oracle_mod, r, g, k, t + ht) - _loss(oracle_mod, r, g, k, t - ht)) / (2 * ht)
+    scale_k = np.abs(g).max()
+    scale_t = np.abs(g).sum() * (np.abs(r).max() + abs(b)) / t ** 2
+    assert abs(fdk - dk) <= 1e-7 * abs(dk) + 1e-10 * scale_k, (fdk, dk)
+    assert abs(fdt - dt) <= 1e-6 * abs(dt) + 1e-12 * scale_t, (fdt, dt)
+
+
+def test_vjp_kt_closed_forms(oracle_mod):
+    rng = np.random.default_rng(14)
+    g = rng.standard_normal(64)
+    # equal scores: p_i = k/n whatever t, so dL/dk = mean(g) and dL/dt = 0
+    r = np.full(64, 0.75)
+    b, _ = oracle_mod.solve(r, 10.0, 0.2)
+    dk, dt = oracle_mod.vjp_kt(r, g, 0.2, b)
+    assert abs(dk - g.mean()) <= 1e-14 * np.abs(g).sum()
+    assert abs(dt) <= 1e-12 * np.abs(g).sum()
+    # g = 1: L = sum p = k, so dL/dk = 1 and dL/dt = 0
+    r = rng.standard_normal(300)
+    b, _ = oracle_mod.solve(r, 12.5, 0.1)
+    dk, dt = oracle_mod.vjp_kt(r, np.ones(300), 0.1, b)
+    assert abs(dk - 1.0) <= 1e-14
+    assert abs(dt) <= 1e-10
+
+
+def test_vjp_kt_scale_identity(oracle_mod):
+    """p is unchanged by (r, t) -> (a r, a t), so d/da L(a r, a t) = 0 at a = 1:
+    t dL/dt = -sum_i r_i dL/dr_i, tying the temperature gradient to the
+    score gradient."""
+    rng = np.random.default_rng(15)
+    r = rng.standard_normal(400) * 3.0 + 1.0
+    g = rng.standard_normal(400)
+    k, t = 31.0, 0.4
+    b, _ = oracle_mod.solve(r, k, t)
+    grad, _, _ = oracle_mod.vjp(r, g, t, b)
+    _, dt = oracle_mod.vjp_kt(r, g, t, b)
+    assert abs(t * dt + np.dot(r, grad)) <= 1e-12 * np.abs(r * grad).sum()
+
+
+# ---------------------------------------------------------------------------
 # bracket bookkeeping (gist.science 2.2, streaming and filtering)
 # ---------------------------------------------------------------------------
 def test_bracket_counts_band_and_tail_identity(oracle_mod):
