@@ -14,7 +14,7 @@ import torch
 from ._binding import (PATH_AUTO, PATH_BRACKET, PATH_FORCE_FALLBACK, PATH_FULL, LapsumError, Options, Stats,
                        default_options, lib)
 
-__all__ = ["forward", "vjp", "soft_topk", "SoftTopK", "default_options", "Options", "Stats", "LapsumError",
+__all__ = ["forward", "vjp", "vjp_kt", "soft_topk", "SoftTopK", "default_options", "Options", "Stats", "LapsumError",
            "PATH_AUTO", "PATH_FULL", "PATH_BRACKET", "PATH_FORCE_FALLBACK", "release_workspaces"]
 
 
@@ -82,27 +82,72 @@ def vjp(r: torch.Tensor, g: torch.Tensor, t: float, b: torch.Tensor, *, grad_out
     return out
 
 
+def vjp_kt(r: torch.Tensor, g: torch.Tensor, t: float, b: torch.Tensor, *, want_grad: bool = True,
+           grad_out: torch.Tensor = None, options: Options = None, stats: bool = False):
+    """The VJP together with dL/dk and dL/dt (L = sum g p).
+
+    Returns (grad, dk, dt): grad as in vjp (None when want_grad is False:
+    then a single pass over r and g forms the scalars), dk and dt 1-element
+    float64 device tensors; plus a stats dict when stats=True (which waits)."""
+    _check_scores(r, "r")
+    _check_scores(g, "g")
+    if g.numel() != r.numel():
+        raise ValueError("g must have as many elements as r")
+    if b.dtype != torch.float64 or b.device != r.device:
+        raise ValueError("b must be the float64 device tensor returned by forward")
+    with torch.cuda.device(r.device):
+        out = None
+        if want_grad:
+            out = grad_out if grad_out is not None else torch.empty_like(r)
+            _check_scores(out, "grad_out")
+        dk = torch.empty(1, dtype=torch.float64, device=r.device)
+        dt = torch.empty(1, dtype=torch.float64, device=r.device)
+        st = Stats() if stats else None
+        rc = lib().lapsum_vjp_kt(r.data_ptr(), g.data_ptr(), r.numel(), float(t), b.data_ptr(),
+                                 out.data_ptr() if out is not None else None, dk.data_ptr(), dt.data_ptr(),
+                                 ctypes.byref(options) if options is not None else None,
+                                 ctypes.byref(st) if st is not None else None, _stream_ptr(r.device))
+    if rc != 0:
+        raise LapsumError(rc, "lapsum_vjp_kt")
+    if stats:
+        return out, dk, dt, st.as_dict()
+    return out, dk, dt
+
+
 class SoftTopK(torch.autograd.Function):
     """Autograd wrapper: forward solves for b and writes p; backward is the
-    analytic VJP with respect to the scores."""
+    analytic VJP with respect to the scores, and with respect to k and t
+    when those are tensors that require a gradient."""
 
     @staticmethod
     def forward(ctx, r, k, t, options=None):
         rc = r.contiguous()
-        p, b = forward(rc, k, t, options=options)
+        p, b = forward(rc, float(k), float(t), options=options)
         ctx.save_for_backward(rc, b)
         ctx.t = float(t)
+        ctx.k_meta = (k.shape, k.dtype, k.device) if isinstance(k, torch.Tensor) else None
+        ctx.t_meta = (t.shape, t.dtype, t.device) if isinstance(t, torch.Tensor) else None
         return p
 
     @staticmethod
     def backward(ctx, g):
         r, b = ctx.saved_tensors
-        grad = vjp(r, g.contiguous().to(torch.float32), ctx.t, b)
-        return grad, None, None, None
+        g32 = g.contiguous().to(torch.float32)
+        need_r, need_k, need_t = ctx.needs_input_grad[0], ctx.needs_input_grad[1], ctx.needs_input_grad[2]
+        if not (need_k or need_t):
+            return vjp(r, g32, ctx.t, b), None, None, None
+        grad, dk, dt = vjp_kt(r, g32, ctx.t, b, want_grad=need_r)
+
+        def like(x, meta):
+            shape, dtype, device = meta
+            return x.to(device=device, dtype=dtype).reshape(shape)
+
+        return (grad, like(dk, ctx.k_meta) if need_k else None, like(dt, ctx.t_meta) if need_t else None, None)
 
 
-def soft_topk(r: torch.Tensor, k: float, t: float, options: Options = None) -> torch.Tensor:
-    """Differentiable exact-budget soft top-k over a flat fp32 tensor."""
+def soft_topk(r: torch.Tensor, k, t, options: Options = None) -> torch.Tensor:
+    """Differentiable exact-budget soft top-k over a flat fp32 tensor.  k and t
+    are numbers, or one-element tensors when their gradients are wanted."""
     shape = r.shape
     p = SoftTopK.apply(r.reshape(-1), k, t, options)
     return p.reshape(shape)

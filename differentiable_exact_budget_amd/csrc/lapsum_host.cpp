@@ -577,10 +577,13 @@ lapsum_status_t lapsum_forward(const float* scores, int64_t n, double k, float t
     return lapsum_forward_ex(scores, n, k, t, p_out, b_out, nullptr, nullptr, stream);
 }
 
-lapsum_status_t lapsum_vjp_ex(const float* scores, const float* /*p*/, const float* g, int64_t n, float t,
-                              const double* b, float* grad_out, const lapsum_options_t* opt,
-                              lapsum_stats_t* stats, lapsum_stream_t stream) {
-    if (!scores || !g || !b || !grad_out) return LAPSUM_ERR_INVALID_ARGUMENT;
+}  // extern "C"
+
+namespace {
+lapsum_status_t vjp_impl(const float* scores, const float* g, int64_t n, float t, const double* b, float* grad_out,
+                         bool kt, double* dk_out, double* dt_out, const lapsum_options_t* opt,
+                         lapsum_stats_t* stats, lapsum_stream_t stream) {
+    if (!scores || !g || !b) return LAPSUM_ERR_INVALID_ARGUMENT;
     if (n < 1 || n > 0xFFFFFFFFll) return LAPSUM_ERR_INVALID_ARGUMENT;
     if (!(t > 0.0f) || !std::isfinite(t)) return LAPSUM_ERR_INVALID_ARGUMENT;
     try {
@@ -594,7 +597,8 @@ lapsum_status_t lapsum_vjp_ex(const float* scores, const float* /*p*/, const flo
             while (w->events.size() < 3) { hipEvent_t e; (void)hipEventCreate(&e); w->events.push_back(e); }
             (void)hipEventRecord(w->events[0], st);
         }
-        launch_vjp(scores, g, n, (double)t, b, grad_out, w->ctl, w->part, st, prof ? &w->events[1] : nullptr);
+        launch_vjp(scores, g, n, (double)t, b, grad_out, w->ctl, w->part, st, prof ? &w->events[1] : nullptr, kt,
+                   dk_out, dt_out);
         if (prof) (void)hipEventRecord(w->events[2], st);
         if (hipGetLastError() != hipSuccess) return LAPSUM_ERR_HIP;
         if (stats) {
@@ -608,14 +612,31 @@ lapsum_status_t lapsum_vjp_ex(const float* scores, const float* /*p*/, const flo
                 (void)hipEventElapsedTime(&a, w->events[0], w->events[1]);
                 (void)hipEventElapsedTime(&bms, w->events[1], w->events[2]);
                 stats->kernel_ms[0] = a; stats->kernel_name[0] = "vjp_reduce";
-                stats->kernel_ms[1] = bms; stats->kernel_name[1] = "vjp_apply";
-                stats->n_timed = 2;
+                stats->n_timed = 1;
+                if (grad_out) { stats->kernel_ms[1] = bms; stats->kernel_name[1] = "vjp_apply"; stats->n_timed = 2; }
             }
         }
         return LAPSUM_OK;
     } catch (...) {
         return LAPSUM_ERR_INTERNAL;
     }
+}
+}  // namespace
+
+extern "C" {
+
+lapsum_status_t lapsum_vjp_ex(const float* scores, const float* /*p*/, const float* g, int64_t n, float t,
+                              const double* b, float* grad_out, const lapsum_options_t* opt,
+                              lapsum_stats_t* stats, lapsum_stream_t stream) {
+    if (!grad_out) return LAPSUM_ERR_INVALID_ARGUMENT;
+    return vjp_impl(scores, g, n, t, b, grad_out, false, nullptr, nullptr, opt, stats, stream);
+}
+
+lapsum_status_t lapsum_vjp_kt(const float* scores, const float* g, int64_t n, float t, const double* b,
+                              float* grad_out, double* dk_out, double* dt_out, const lapsum_options_t* opt,
+                              lapsum_stats_t* stats, lapsum_stream_t stream) {
+    if (!grad_out && !dk_out && !dt_out) return LAPSUM_ERR_INVALID_ARGUMENT;
+    return vjp_impl(scores, g, n, t, b, grad_out, true, dk_out, dt_out, opt, stats, stream);
 }
 
 lapsum_status_t lapsum_vjp(const float* scores, const float* p, const float* g, int64_t n, float t, const double* b,

@@ -28,8 +28,9 @@ void launch_filter(const float* r, long long n, double t, Ctl* ctl, const float*
 // returns the number of partials it left (for launch_sum_p)
 int launch_probs(const float* r, long long n, double t, float* p, Ctl* ctl, double* part, hipStream_t st);
 void launch_sum_p(Ctl* ctl, const double* part, int nparts, hipStream_t st);
+// grad may be null (only the reduction and c); kt adds dL/dk, dL/dt (each output may be null)
 void launch_vjp(const float* r, const float* g, long long n, double t, const double* b, float* grad, Ctl* ctl,
-                double* part, hipStream_t st, hipEvent_t* ev_mid);
+                double* part, hipStream_t st, hipEvent_t* ev_mid, bool kt, double* dk_out, double* dt_out);
 void launch_fill(float* p, long long n, float v, hipStream_t st);
 void launch_set_nan_b(Ctl* ctl, double* b_out, hipStream_t st);
 

@@ -452,21 +452,35 @@ int launch_probs(const float* r, long long n, double t, float* p, Ctl* ctl, doub
 // ---------------------------------------------------------------------------
 LS_DEV float lap_pdf_f(float x) { return 0.5f * __builtin_amdgcn_exp2f(-fabsf(x) * 1.4426950408889634f); }
 
-template <bool VEC>
+// Per workgroup: sum f g and sum f; with KT also sum f g d and sum f d
+// (d = r - b), which the budget and temperature gradients need.
+template <bool VEC, bool KT>
 __global__ __launch_bounds__(kStreamThreads) void k_vjp_reduce(const float* __restrict__ r, const float* __restrict__ g,
                                                                 long long n, const double* bptr, double inv_t,
                                                                 double* part) {
     __shared__ double s_red[kStreamThreads / 64];
     const double b = *bptr;
     const int tid = threadIdx.x;
-    double sfg = 0.0, sf = 0.0;
+    double sfg = 0.0, sf = 0.0, sfgd = 0.0, sfd = 0.0;
+    auto one = [&](float v, float gv) {
+        const double d = (double)v - b;
+        const float f = lap_pdf_f((float)(d * inv_t));
+        const float fg = f * gv;
+        sfg += (double)fg;
+        sf += (double)f;
+        if (KT) { sfgd += (double)fg * d; sfd += (double)f * d; }
+    };
     auto quad = [&](float4 q, float4 gg) {
-        const float f0 = lap_pdf_f((float)(((double)q.x - b) * inv_t));
-        const float f1 = lap_pdf_f((float)(((double)q.y - b) * inv_t));
-        const float f2 = lap_pdf_f((float)(((double)q.z - b) * inv_t));
-        const float f3 = lap_pdf_f((float)(((double)q.w - b) * inv_t));
-        sfg += (double)(f0 * gg.x + f1 * gg.y) + (double)(f2 * gg.z + f3 * gg.w);
-        sf += (double)((f0 + f1) + (f2 + f3));
+        if (KT) {
+            one(q.x, gg.x); one(q.y, gg.y); one(q.z, gg.z); one(q.w, gg.w);
+        } else {
+            const float f0 = lap_pdf_f((float)(((double)q.x - b) * inv_t));
+            const float f1 = lap_pdf_f((float)(((double)q.y - b) * inv_t));
+            const float f2 = lap_pdf_f((float)(((double)q.z - b) * inv_t));
+            const float f3 = lap_pdf_f((float)(((double)q.w - b) * inv_t));
+            sfg += (double)(f0 * gg.x + f1 * gg.y) + (double)(f2 * gg.z + f3 * gg.w);
+            sf += (double)((f0 + f1) + (f2 + f3));
+        }
     };
     if (VEC) {
         const long long n4 = n >> 2;
@@ -475,29 +489,50 @@ __global__ __launch_bounds__(kStreamThreads) void k_vjp_reduce(const float* __re
                                        false, body, body);
         if (blockIdx.x == 0) {
             const long long j = (n4 << 2) + tid;
-            if (tid < 4 && j < n) {
-                const float f = lap_pdf_f((float)(((double)r[j] - b) * inv_t));
-                sfg += (double)(f * g[j]); sf += (double)f;
-            }
+            if (tid < 4 && j < n) one(r[j], g[j]);
         }
     } else {
         const long long stride = (long long)gridDim.x * kStreamThreads;
-        for (long long i = (long long)blockIdx.x * kStreamThreads + tid; i < n; i += stride) {
-            const float f = lap_pdf_f((float)(((double)r[i] - b) * inv_t));
-            sfg += (double)(f * g[i]); sf += (double)f;
-        }
+        for (long long i = (long long)blockIdx.x * kStreamThreads + tid; i < n; i += stride) one(r[i], g[i]);
     }
+    constexpr int NP = KT ? 4 : 2;
     const double t0 = block_sum<kStreamThreads>(sfg, s_red);
     const double t1 = block_sum<kStreamThreads>(sf, s_red);
-    if (tid == 0) { part[2 * blockIdx.x] = t0; part[2 * blockIdx.x + 1] = t1; }
+    double t2 = 0.0, t3 = 0.0;
+    if (KT) {
+        t2 = block_sum<kStreamThreads>(sfgd, s_red);
+        t3 = block_sum<kStreamThreads>(sfd, s_red);
+    }
+    if (tid == 0) {
+        part[NP * blockIdx.x] = t0;
+        part[NP * blockIdx.x + 1] = t1;
+        if (KT) { part[NP * blockIdx.x + 2] = t2; part[NP * blockIdx.x + 3] = t3; }
+    }
 }
 
-// c = sum f g / sum f from the reduce pass's partials, in a fixed order
-__global__ __launch_bounds__(1024) void k_vjp_c(const double* part, int nparts, Ctl* ctl) {
+// c = sum f g / sum f from the reduce pass's partials, in a fixed order; with
+// KT also dL/dk = c and dL/dt = -(sum f g d - mu sum f g)/t^2,
+// mu = sum f d / sum f, written to dk_out / dt_out when they are not null
+template <bool KT>
+__global__ __launch_bounds__(1024) void k_vjp_c(const double* part, int nparts, Ctl* ctl, double t, double* dk_out,
+                                                double* dt_out) {
     __shared__ double s_red[1024 / 64];
-    const double T0 = sum_parts<1024>(part, 2, 0, nparts, s_red);
-    const double T1 = sum_parts<1024>(part, 2, 1, nparts, s_red);
-    if (threadIdx.x == 0) { ctl->sumfg = T0; ctl->sumf = T1; ctl->c = T0 / T1; }
+    constexpr int NP = KT ? 4 : 2;
+    const double T0 = sum_parts<1024>(part, NP, 0, nparts, s_red);
+    const double T1 = sum_parts<1024>(part, NP, 1, nparts, s_red);
+    double T2 = 0.0, T3 = 0.0;
+    if (KT) {
+        T2 = sum_parts<1024>(part, NP, 2, nparts, s_red);
+        T3 = sum_parts<1024>(part, NP, 3, nparts, s_red);
+    }
+    if (threadIdx.x == 0) {
+        ctl->sumfg = T0; ctl->sumf = T1; ctl->c = T0 / T1;
+        if (KT) {
+            const double mu = T3 / T1;
+            if (dk_out) *dk_out = T0 / T1;
+            if (dt_out) *dt_out = -(T2 - mu * T0) / (t * t);
+        }
+    }
 }
 
 // f/t = e^{-|x|}/(2t) evaluated as one exp2 with log2(1/(2t)) folded into the
@@ -537,15 +572,26 @@ __global__ __launch_bounds__(kStreamThreads) void k_vjp_apply(const float* __res
 }
 
 void launch_vjp(const float* r, const float* g, long long n, double t, const double* b, float* grad, Ctl* ctl,
-                double* part, hipStream_t st, hipEvent_t* ev_mid) {
+                double* part, hipStream_t st, hipEvent_t* ev_mid, bool kt, double* dk_out, double* dt_out) {
     const bool vec = ((reinterpret_cast<uintptr_t>(r) | reinterpret_cast<uintptr_t>(g) |
                        reinterpret_cast<uintptr_t>(grad)) & 15u) == 0u;
     const double inv_t = 1.0 / t;
     const int rblocks = vec ? tiled_grid<kReduceV>(n >> 2, kReduceGrid) : stream_blocks(n);
-    if (vec) hipLaunchKernelGGL(k_vjp_reduce<true>, dim3(rblocks), dim3(kStreamThreads), 0, st, r, g, n, b, inv_t, part);
-    else hipLaunchKernelGGL(k_vjp_reduce<false>, dim3(rblocks), dim3(kStreamThreads), 0, st, r, g, n, b, inv_t, part);
-    hipLaunchKernelGGL(k_vjp_c, dim3(1), dim3(1024), 0, st, part, rblocks, ctl);
+    if (kt) {
+        if (vec) hipLaunchKernelGGL((k_vjp_reduce<true, true>), dim3(rblocks), dim3(kStreamThreads), 0, st, r, g, n, b,
+                                    inv_t, part);
+        else hipLaunchKernelGGL((k_vjp_reduce<false, true>), dim3(rblocks), dim3(kStreamThreads), 0, st, r, g, n, b,
+                                inv_t, part);
+        hipLaunchKernelGGL(k_vjp_c<true>, dim3(1), dim3(1024), 0, st, part, rblocks, ctl, t, dk_out, dt_out);
+    } else {
+        if (vec) hipLaunchKernelGGL((k_vjp_reduce<true, false>), dim3(rblocks), dim3(kStreamThreads), 0, st, r, g, n, b,
+                                    inv_t, part);
+        else hipLaunchKernelGGL((k_vjp_reduce<false, false>), dim3(rblocks), dim3(kStreamThreads), 0, st, r, g, n, b,
+                                inv_t, part);
+        hipLaunchKernelGGL(k_vjp_c<false>, dim3(1), dim3(1024), 0, st, part, rblocks, ctl, t, nullptr, nullptr);
+    }
     if (ev_mid) (void)hipEventRecord(*ev_mid, st);
+    if (!grad) return;
     const float l2 = (float)(std::log2(0.5 * inv_t) + 32.0);
     const int ablocks = vec ? tiled_grid<kApplyV>(n >> 2, kApplyGrid) : stream_blocks(n);
     if (vec) hipLaunchKernelGGL(k_vjp_apply<true>, dim3(ablocks), dim3(kStreamThreads), 0, st, r, g, n, b, inv_t, l2,

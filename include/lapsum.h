@@ -156,6 +156,24 @@ lapsum_status_t lapsum_vjp_ex(const float* scores, const float* p, const float* 
                               const double* b, float* grad_out, const lapsum_options_t* opt,
                               lapsum_stats_t* stats, lapsum_stream_t stream);
 
+/*
+ * Analytic VJP together with the gradients with respect to the budget and the
+ * temperature (gist.science summary section 2.1; implicit differentiation of
+ * the budget equation G(b) = k).  With d_i = r_i - b and
+ * f_i = e^{-|d_i|/t}/2, for L = sum_i g_i p_i:
+ *
+ *     dL/dk = sum g f / sum f,
+ *     dL/dt = -(sum g f d - mu sum g f) / t^2,   mu = sum f d / sum f.
+ *
+ * grad_out: device fp32[n], the score gradient as in lapsum_vjp (NULL: only
+ * the two scalars are formed, one pass over scores and g).  dk_out, dt_out:
+ * device fp64[1] each, or NULL.  At least one of the three outputs must be
+ * given.  Argument rules, errors and stream semantics as lapsum_vjp_ex.
+ */
+lapsum_status_t lapsum_vjp_kt(const float* scores, const float* g, int64_t n, float t, const double* b,
+                              float* grad_out, double* dk_out, double* dt_out,
+                              const lapsum_options_t* opt, lapsum_stats_t* stats, lapsum_stream_t stream);
+
 /* Free every cached workspace (waits for their streams). */
 void lapsum_release_workspaces(void);
 
