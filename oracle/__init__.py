@@ -47,6 +47,12 @@ def _load():
     lib.oracle_vjp.restype = None
     lib.oracle_vjp_kt.argtypes = [_dp, _dp, ctypes.c_int64, ctypes.c_double, ctypes.c_double, _dp, _dp]
     lib.oracle_vjp_kt.restype = None
+    lib.oracle_order_stats.argtypes = [_dp, ctypes.c_int64, ctypes.c_int64, _dp, _dp]
+    lib.oracle_order_stats.restype = ctypes.c_int
+    lib.oracle_hard_topk.argtypes = [_dp, ctypes.c_int64, ctypes.c_int64, _dp, _dp]
+    lib.oracle_hard_topk.restype = ctypes.c_int64
+    lib.oracle_dftopk.argtypes = [_dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_double, _dp, _dp]
+    lib.oracle_dftopk.restype = ctypes.c_double
     lib.oracle_bracket.argtypes = [_dp, ctypes.c_int64, ctypes.c_double, ctypes.c_double, ctypes.c_double,
                                    _i64p, _dp, _dp, ctypes.c_int64]
     lib.oracle_bracket.restype = ctypes.c_int64
@@ -143,6 +149,39 @@ def vjp_kt(r, g, t: float, b: float):
     dt = ctypes.c_double(0.0)
     _load().oracle_vjp_kt(_ptr(r, _dp), _ptr(g, _dp), r.size, float(t), float(b), ctypes.byref(dk), ctypes.byref(dt))
     return dk.value, dt.value
+
+
+def order_stats(r, k: int):
+    """(k-th largest, (k+1)-th largest) of r; the second is -inf when k = n."""
+    r = _f64(r)
+    a = ctypes.c_double(0.0)
+    b = ctypes.c_double(0.0)
+    if _load().oracle_order_stats(_ptr(r, _dp), r.size, int(k), ctypes.byref(a), ctypes.byref(b)) != 0:
+        raise ValueError("k must be in [1, n]")
+    return a.value, b.value
+
+
+def hard_topk(r, k: int):
+    """(mask, threshold, ones): mask_i = 1 where r_i >= the k-th largest."""
+    r = _f64(r)
+    m = np.empty(r.size)
+    tau = ctypes.c_double(0.0)
+    ones = _load().oracle_hard_topk(_ptr(r, _dp), r.size, int(k), _ptr(m, _dp), ctypes.byref(tau))
+    if ones < 0:
+        raise ValueError("k must be in [1, n]")
+    return m, tau.value, int(ones)
+
+
+def dftopk(r, k: int, t: float):
+    """(p, b, sum p) of the DFTopK operator: b = midpoint of the k-th and
+    (k+1)-th largest, p_i = F((r_i - b)/t)."""
+    r = _f64(r)
+    p = np.empty(r.size)
+    b = ctypes.c_double(0.0)
+    s = _load().oracle_dftopk(_ptr(r, _dp), r.size, int(k), float(t), _ptr(p, _dp), ctypes.byref(b))
+    if s != s:
+        raise ValueError("k must be in [1, n - 1]")
+    return p, b.value, float(s)
 
 
 def bracket(r, t: float, a_L: float, a_R: float, want_band: bool = True):

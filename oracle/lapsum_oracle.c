@@ -327,6 +327,54 @@ void oracle_sort_keys(const float* r, int64_t n, float* out) {
 }
 
 /* ------------------------------------------------------------------ */
+/* Order statistics from the top, the hard top-k threshold and the      */
+/* DFTopK operator (gist.science summary 2.3: DFTopK puts the threshold */
+/* at the midpoint of the k-th and (k+1)-th order statistics, which is */
+/* the zero-temperature limit of LapSum; at finite t its mass sum p     */
+/* drifts from k).                                                      */
+/* ------------------------------------------------------------------ */
+
+/* k-th and (k+1)-th largest of r (1 <= k <= n; the (k+1)-th is -inf when
+ * k = n), from a sorted copy.  Returns 0, or -1 on a bad k or allocation. */
+int oracle_order_stats(const double* r, int64_t n, int64_t k, double* tk_out, double* tk1_out) {
+    if (n < 1 || k < 1 || k > n) return -1;
+    double* v = (double*)malloc(sizeof(double) * (size_t)n);
+    if (!v) return -1;
+    for (int64_t i = 0; i < n; ++i) v[i] = r[i];
+    qsort(v, (size_t)n, sizeof(double), cmp_double);
+    *tk_out = v[n - k];
+    *tk1_out = k < n ? v[n - k - 1] : -INFINITY;
+    free(v);
+    return 0;
+}
+
+/* hard top-k: mask_i = 1 when r_i >= the k-th largest score, else 0.  With
+ * ties at the threshold more than k scores qualify.  Returns the number of
+ * ones (-1 on a bad k); *tau_out gets the threshold. */
+int64_t oracle_hard_topk(const double* r, int64_t n, int64_t k, double* mask_out, double* tau_out) {
+    double tk, tk1;
+    if (oracle_order_stats(r, n, k, &tk, &tk1) != 0) return -1;
+    int64_t ones = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        mask_out[i] = r[i] >= tk ? 1.0 : 0.0;
+        ones += r[i] >= tk;
+    }
+    *tau_out = tk;
+    return ones;
+}
+
+/* DFTopK: b = (k-th largest + (k+1)-th largest) / 2 (1 <= k < n) and
+ * p_i = F((r_i - b)/t) with the same Laplace CDF as LapSum.  Returns sum p
+ * (NaN on a bad k); *b_out gets b. */
+double oracle_dftopk(const double* r, int64_t n, int64_t k, double t, double* p_out, double* b_out) {
+    double tk, tk1;
+    if (k >= n || oracle_order_stats(r, n, k, &tk, &tk1) != 0) return NAN;
+    const double b = 0.5 * (tk + tk1);
+    *b_out = b;
+    return oracle_probs(r, n, t, b, p_out);
+}
+
+/* ------------------------------------------------------------------ */
 /* Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: */
 /* as easy as 1, 2, 3", SC'11): 10 rounds of the Philox S-box          */
 /* (two 32x32->64 multiplies by 0xD2511F53 and 0xCD9E8D57) with a Weyl */

@@ -299,6 +299,75 @@ def test_vjp_kt_scale_identity(oracle_mod):
 
 
 # ---------------------------------------------------------------------------
+# order statistics, hard top-k and DFTopK (gist.science 2.3)
+# ---------------------------------------------------------------------------
+def _kth_largest_by_counts(r, k):
+    """The k-th largest written as a count condition, no sorting: the score v
+    with #(r > v) < k <= #(r >= v)."""
+    cands = [v for v in set(r.tolist()) if np.sum(r > v) < k <= np.sum(r >= v)]
+    assert len(cands) == 1
+    return cands[0]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_order_stats_count_definition(oracle_mod, seed):
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(1, 40))
+    r = rng.integers(-3, 4, size=n).astype(np.float64)  # many ties
+    for k in range(1, n + 1):
+        tk, tk1 = oracle_mod.order_stats(r, k)
+        assert tk == _kth_largest_by_counts(r, k)
+        assert tk1 == (_kth_largest_by_counts(r, k + 1) if k < n else -np.inf)
+        mask, tau, ones = oracle_mod.hard_topk(r, k)
+        assert tau == tk and ones == int(np.sum(r >= tk)) and ones >= k
+        assert np.array_equal(mask, (r >= tk).astype(np.float64))
+    with pytest.raises(ValueError):
+        oracle_mod.order_stats(r, 0)
+    with pytest.raises(ValueError):
+        oracle_mod.order_stats(r, n + 1)
+
+
+def test_hard_topk_tie_free_selects_exactly_k(oracle_mod):
+    rng = np.random.default_rng(7)
+    r = rng.permutation(5000).astype(np.float64) * 0.37 - 100.0
+    for k in (1, 2, 17, 2500, 4999, 5000):
+        mask, tau, ones = oracle_mod.hard_topk(r, k)
+        assert ones == k
+        top = np.argpartition(-r, k - 1)[:k]
+        expect = np.zeros(r.size)
+        expect[top] = 1.0
+        assert np.array_equal(mask, expect)
+
+
+def test_dftopk_is_the_zero_temperature_limit(oracle_mod):
+    """The DFTopK threshold is the value LapSum's b tends to as t -> 0 (the
+    golden row: scores 0..19, k = 5, b -> 14.5)."""
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "zero_temperature_topk.txt")
+    row = [ln.split() for ln in open(path) if ln.strip() and not ln.startswith("#")][0]
+    n, k, t, b_limit = int(row[0]), int(row[1]), float(row[2]), float(row[3])
+    r = np.random.default_rng(3).permutation(np.arange(n, dtype=np.float64))
+    p, b, s = oracle_mod.dftopk(r, k, t)
+    assert b == b_limit
+    b_lapsum, _ = oracle_mod.solve(r, k, t)
+    assert abs(b - b_lapsum) <= 1e-9
+
+
+def test_dftopk_mass_closed_forms(oracle_mod):
+    """DFTopK keeps the midpoint whatever t, so its mass drifts from k.
+    Scores {0, 1, 2}, k = 1: b = 1.5 and sum p = 1 + e^{-1.5/t}/2 exactly.
+    Scores {0, 1}, k = 1: b = 0.5 and sum p = 1 by symmetry."""
+    for t in (0.05, 0.5, 2.0):
+        _, b, s = oracle_mod.dftopk(np.array([2.0, 0.0, 1.0]), 1, t)
+        assert b == 1.5
+        assert abs(s - (1.0 + 0.5 * math.exp(-1.5 / t))) <= 1e-15
+        _, b, s = oracle_mod.dftopk(np.array([1.0, 0.0]), 1, t)
+        assert b == 0.5 and abs(s - 1.0) <= 1e-15
+    with pytest.raises(ValueError):
+        oracle_mod.dftopk(np.array([1.0, 0.0]), 2, 0.1)
+
+
+# ---------------------------------------------------------------------------
 # bracket bookkeeping (gist.science 2.2, streaming and filtering)
 # ---------------------------------------------------------------------------
 def test_bracket_counts_band_and_tail_identity(oracle_mod):
