@@ -165,6 +165,40 @@ def kernel_profile(L, torch, rd, gd, k, t, steps):
     return {n: statistics.mean(v) for n, v in acc.items()}, info
 
 
+def timed(torch, fn, reps=10, warm=2):
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for s0, s1 in ev:
+        s0.record()
+        fn()
+        s1.record()
+    torch.cuda.synchronize()
+    return statistics.median(s0.elapsed_time(s1) for s0, s1 in ev)
+
+
+def extras(L, torch, rd, gd, cfg):
+    """The operator's other entry points on the same resident input:
+    the VJP with budget and temperature gradients, hard top-k (threshold and
+    mask) and DFTopK (threshold and p).  Median ms over 10 calls; bytes are
+    the n-sized arrays each call must move."""
+    n, k, t = cfg.n, int(cfg.k), cfg.t
+    _, b = L.forward(rd, cfg.k, t)
+    grad = torch.empty_like(rd)
+    res = {}
+    for name, fn, bpe in (
+            ("vjp", lambda: L.vjp(rd, gd, t, b, grad_out=grad), 20),
+            ("vjp_kt", lambda: L.vjp_kt(rd, gd, t, b, grad_out=grad), 20),
+            ("vjp_kt_scalars_only", lambda: L.vjp_kt(rd, gd, t, b, want_grad=False), 8),
+            ("hard_topk", lambda: L.hard_topk(rd, k), 12),
+            ("dftopk", lambda: L.dftopk(rd, k, t), 12)):
+        ms = timed(torch, fn)
+        res[name] = {"median_ms": round(ms, 5), "scores_per_s": n / (ms * 1e-3),
+                     "alg_GBps": round(bpe * n / (ms * 1e-3) / 1e9, 1)}
+    return res
+
+
 def cpu_baseline(cfg, r, g, n_sample):
     import numpy as np
     import oracle
@@ -272,6 +306,9 @@ def main():
                                                 "scores_per_s": c2.n / (statistics.median(per3) * 1e-3)}
             del a, b2
         out["other_configs"] = others
+
+    if not args.no_other_configs and cfg.name == "C4":
+        out["extras"] = extras(L, torch, rd, gd, cfg)
 
     out["pages_context_ms"] = {"forward_only_1e8": 5.23, "certified_median_1e8": 7.24,
                                "note": "the pages' forward solve times on unnamed hardware; not this metric"}

@@ -14,7 +14,7 @@ import torch
 from ._binding import (PATH_AUTO, PATH_BRACKET, PATH_FORCE_FALLBACK, PATH_FULL, LapsumError, Options, Stats,
                        default_options, lib)
 
-__all__ = ["forward", "vjp", "vjp_kt", "soft_topk", "SoftTopK", "default_options", "Options", "Stats", "LapsumError",
+__all__ = ["forward", "vjp", "vjp_kt", "soft_topk", "topk_threshold", "hard_topk", "dftopk", "SoftTopK", "default_options", "Options", "Stats", "LapsumError",
            "PATH_AUTO", "PATH_FULL", "PATH_BRACKET", "PATH_FORCE_FALLBACK", "release_workspaces"]
 
 
@@ -151,6 +151,53 @@ def soft_topk(r: torch.Tensor, k, t, options: Options = None) -> torch.Tensor:
     shape = r.shape
     p = SoftTopK.apply(r.reshape(-1), k, t, options)
     return p.reshape(shape)
+
+
+def _opts(options):
+    return ctypes.byref(options) if options is not None else None
+
+
+def topk_threshold(r: torch.Tensor, k: int, *, options: Options = None, stats: bool = False):
+    """(k-th largest, (k+1)-th largest) of r as a 2-element float64 device
+    tensor (the second is -inf when k = n)."""
+    _check_scores(r, "r")
+    with torch.cuda.device(r.device):
+        tau = torch.empty(2, dtype=torch.float64, device=r.device)
+        st = Stats() if stats else None
+        rc = lib().lapsum_topk_threshold(r.data_ptr(), r.numel(), int(k), tau.data_ptr(), _opts(options),
+                                         ctypes.byref(st) if st is not None else None, _stream_ptr(r.device))
+    if rc != 0:
+        raise LapsumError(rc, "lapsum_topk_threshold")
+    return (tau, st.as_dict()) if stats else tau
+
+
+def hard_topk(r: torch.Tensor, k: int, *, options: Options = None, stats: bool = False):
+    """mask (fp32, 1 where r >= the k-th largest) and the two order statistics."""
+    _check_scores(r, "r")
+    with torch.cuda.device(r.device):
+        mask = torch.empty_like(r)
+        tau = torch.empty(2, dtype=torch.float64, device=r.device)
+        st = Stats() if stats else None
+        rc = lib().lapsum_hard_topk(r.data_ptr(), r.numel(), int(k), mask.data_ptr(), tau.data_ptr(), _opts(options),
+                                    ctypes.byref(st) if st is not None else None, _stream_ptr(r.device))
+    if rc != 0:
+        raise LapsumError(rc, "lapsum_hard_topk")
+    return (mask, tau, st.as_dict()) if stats else (mask, tau)
+
+
+def dftopk(r: torch.Tensor, k: int, t: float, *, options: Options = None, stats: bool = False):
+    """DFTopK: b = midpoint of the k-th and (k+1)-th largest, p = F((r - b)/t).
+    Returns (p, b) with b a 1-element float64 device tensor."""
+    _check_scores(r, "r")
+    with torch.cuda.device(r.device):
+        p = torch.empty_like(r)
+        b = torch.empty(1, dtype=torch.float64, device=r.device)
+        st = Stats() if stats else None
+        rc = lib().lapsum_dftopk(r.data_ptr(), r.numel(), int(k), float(t), p.data_ptr(), b.data_ptr(),
+                                 _opts(options), ctypes.byref(st) if st is not None else None, _stream_ptr(r.device))
+    if rc != 0:
+        raise LapsumError(rc, "lapsum_dftopk")
+    return (p, b, st.as_dict()) if stats else (p, b)
 
 
 def release_workspaces() -> None:

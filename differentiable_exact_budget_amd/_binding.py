@@ -86,7 +86,7 @@ _lib = None
 
 EXPORTED = [
     "lapsum_default_options", "lapsum_status_string", "lapsum_forward", "lapsum_forward_ex", "lapsum_vjp",
-    "lapsum_vjp_ex", "lapsum_vjp_kt",
+    "lapsum_vjp_ex", "lapsum_vjp_kt", "lapsum_topk_threshold", "lapsum_hard_topk", "lapsum_dftopk",
     "lapsum_release_workspaces", "lapsum_workspace_bytes",
     "lapsum_test_sort", "lapsum_test_sample", "lapsum_test_select", "lapsum_test_filter",
     "lapsum_test_copy", "lapsum_test_read", "lapsum_test_binomial_ranks",
@@ -117,6 +117,12 @@ def lib():
     L.lapsum_vjp_ex.restype = ctypes.c_int
     L.lapsum_vjp_kt.argtypes = [vp, vp, i64, f32, vp, vp, vp, vp, ctypes.POINTER(Options), ctypes.POINTER(Stats), vp]
     L.lapsum_vjp_kt.restype = ctypes.c_int
+    L.lapsum_topk_threshold.argtypes = [vp, i64, i64, vp, ctypes.POINTER(Options), ctypes.POINTER(Stats), vp]
+    L.lapsum_topk_threshold.restype = ctypes.c_int
+    L.lapsum_hard_topk.argtypes = [vp, i64, i64, vp, vp, ctypes.POINTER(Options), ctypes.POINTER(Stats), vp]
+    L.lapsum_hard_topk.restype = ctypes.c_int
+    L.lapsum_dftopk.argtypes = [vp, i64, i64, f32, vp, vp, ctypes.POINTER(Options), ctypes.POINTER(Stats), vp]
+    L.lapsum_dftopk.restype = ctypes.c_int
     L.lapsum_release_workspaces.argtypes = []
     L.lapsum_release_workspaces.restype = None
     L.lapsum_workspace_bytes.argtypes = [i64]

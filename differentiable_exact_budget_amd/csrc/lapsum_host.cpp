@@ -528,6 +528,135 @@ lapsum_status_t forward_impl(const float* r, int64_t n, double k, float t_f, flo
     return LAPSUM_OK;
 }
 
+// ---------------------------------------------------------------------------
+// k-th and (k+1)-th largest scores (hard top-k threshold, DFTopK midpoint):
+// the full sort up to the bracketing threshold, else a noiseless sample, the
+// streaming filter and a count-based certification -- both order statistics
+// are in the band iff c_R <= k - 1 and c_R + m >= k + 1 (>= n when k = n).
+// Leaves the k-th largest in ctl->aR, the (k+1)-th in ctl->aL and their
+// midpoint in ctl->b; tau_out (device fp64[2]) may be null.
+// ---------------------------------------------------------------------------
+lapsum_status_t order_stats_impl(Workspace* w, const float* r, long long n, long long k,
+                                 const lapsum_options_t& opt, lapsum_stats_t* stats, hipStream_t st,
+                                 double* tau_out) {
+    Timer tm{w, st, opt.profile != 0};
+    if (stats) {
+        std::memset(stats, 0, sizeof(*stats));
+        stats->a_L = -INFINITY; stats->a_R = INFINITY;
+    }
+    int path = opt.path;
+    if (path == LAPSUM_PATH_AUTO) path = (n > opt.auto_threshold) ? LAPSUM_PATH_BRACKET : LAPSUM_PATH_FULL;
+    auto full_sort = [&]() {
+        if (n <= kSmallMax) {
+            tm.begin("small_sort");
+            launch_small_sort(r, (int)n, w->ctl, w->keysB, st);
+            tm.end();
+        } else {
+            tm.begin("radix_sort");
+            const uint32_t epoch = next_epoch(w, st);
+            launch_radix_sort(r, n, w->keysA, w->keysB, w->hist_part, w->goff, w->status, epoch, w->ctl, st);
+            tm.end();
+        }
+        tm.begin("pick");
+        launch_pick_sorted(w->keysB, n, k, w->ctl, tau_out, st);
+        tm.end();
+    };
+    bool fallback = false, certified = false;
+    int widen = 0;
+    HostSummary h{};
+    if (path == LAPSUM_PATH_FULL) {
+        full_sort();
+        if (stats) stats->path_taken = 1;
+    } else {
+        long long s = (long long)std::ceil(opt.sample_factor * std::sqrt((double)n));
+        s = std::max<long long>(1, std::min<long long>(s, kSampleMax));
+        const double q = 1.0 - (double)k / (double)n;
+        long long l, hh;
+        binomial_ranks(s, q, opt.delta, &l, &hh);
+        const double c0 = (double)s * q;
+        const int cap = opt.bucket_capacity;
+        tm.begin("sample");
+        launch_sample(r, n, 0.0, opt.seed, (int)s, w->sample, nullptr, st);  // no noise: the scores themselves
+        tm.end();
+        for (;;) {
+            tm.begin("select");
+            launch_select(w->sample, (int)s, l, hh, cap, w->ctl, w->sp, w->iw, w->bucket_cnt, st);
+            tm.end();
+            const unsigned int seq = ++w->seq;
+            tm.begin("filter");
+            launch_filter(r, n, 1.0, w->ctl, w->sp, w->iw, w->bucket_cnt, w->bucket_vals, cap, w->part, nullptr,
+                          w->hs_dev, seq, st);
+            tm.end();
+            if (hipGetLastError() != hipSuccess) return LAPSUM_ERR_HIP;
+            lapsum_status_t ws = wait_summary(w, st, seq);
+            if (ws != LAPSUM_OK) return ws;
+            h = *const_cast<HostSummary*>(w->hs);
+            if (h.flags & kFlagNonFinite) {
+                if (stats) { stats->status = LAPSUM_ERR_NONFINITE_INPUT; tm.collect(stats); }
+                return LAPSUM_ERR_NONFINITE_INPUT;
+            }
+            const long long cR = (long long)h.c_R, m = (long long)h.m;
+            const bool okR = cR <= k - 1;
+            const bool okL = cR + m >= std::min<long long>(k + 1, n);
+            if (h.flags & kFlagOverflow) { fallback = true; break; }
+            if (okR && okL) { certified = true; break; }
+            if (path == LAPSUM_PATH_FORCE_FALLBACK || widen >= opt.max_widen) { fallback = true; break; }
+            if (!okR) {
+                const double d = std::max(1.0, 2.0 * ((double)hh - c0));
+                hh = std::min<long long>((long long)std::ceil(c0 + d), s + 1);
+            }
+            if (!okL) {
+                const double d = std::max(1.0, 2.0 * (c0 - (double)l));
+                l = std::max<long long>((long long)std::floor(c0 - d), 0);
+            }
+            ++widen;
+        }
+        if (path == LAPSUM_PATH_FORCE_FALLBACK) fallback = true;
+        if (fallback) {
+            full_sort();
+        } else {
+            tm.begin("bucket_pick");
+            launch_bucket_pick(w->bucket_vals, w->bucket_cnt, cap, k, w->ctl, tau_out, st);
+            tm.end();
+        }
+        if (stats) {
+            stats->path_taken = fallback ? 3 : 2;
+            stats->widenings = widen;
+            stats->certified = certified ? 1 : 0;
+            stats->count_below = (int64_t)h.c_L;
+            stats->band_size = (int64_t)h.m;
+            stats->count_above = (int64_t)h.c_R;
+            stats->sample_size = s;
+            stats->rank_lo = l;
+            stats->rank_hi = hh;
+            stats->buckets = h.nb;
+            stats->a_L = h.aL;
+            stats->a_R = h.aR;
+        }
+    }
+    if (hipGetLastError() != hipSuccess) return LAPSUM_ERR_HIP;
+    if (stats) {
+        if (hipStreamSynchronize(st) != hipSuccess) return LAPSUM_ERR_HIP;
+        Ctl c;
+        if (hipMemcpy(&c, w->ctl, sizeof(Ctl), hipMemcpyDeviceToHost) != hipSuccess) return LAPSUM_ERR_HIP;
+        stats->b = c.b;
+        stats->status = (c.flags & kFlagNonFinite) ? LAPSUM_ERR_NONFINITE_INPUT
+                        : (c.flags & kFlagInternal) ? LAPSUM_ERR_INTERNAL : LAPSUM_OK;
+        tm.collect(stats);
+    }
+    return LAPSUM_OK;
+}
+
+lapsum_status_t check_topk_args(const float* r, int64_t n, int64_t k, long long kmax, const lapsum_options_t& o) {
+    if (!r || n < 1 || n > 0xFFFFFFFFll) return LAPSUM_ERR_INVALID_ARGUMENT;
+    if (k < 1 || k > kmax) return LAPSUM_ERR_INVALID_ARGUMENT;
+    if (o.path < LAPSUM_PATH_AUTO || o.path > LAPSUM_PATH_FORCE_FALLBACK) return LAPSUM_ERR_INVALID_ARGUMENT;
+    if (o.bucket_capacity < 1 || o.bucket_capacity > kBucketCapMax || !(o.sample_factor > 0.0) ||
+        !(o.delta > 0.0 && o.delta < 0.5) || o.max_widen < 0)
+        return LAPSUM_ERR_INVALID_ARGUMENT;
+    return LAPSUM_OK;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -788,6 +917,89 @@ lapsum_status_t lapsum_test_filter(const float* scores, int64_t n, float t, floa
         if (hipMemcpy(band_out, band.data(), sizeof(float) * band.size(), hipMemcpyHostToDevice) != hipSuccess)
             return LAPSUM_ERR_HIP;
     return LAPSUM_OK;
+}
+
+
+// ---------------------------------------------------------------------------
+// order statistics, hard top-k, DFTopK
+// ---------------------------------------------------------------------------
+lapsum_status_t lapsum_topk_threshold(const float* scores, int64_t n, int64_t k, double* tau_out,
+                                      const lapsum_options_t* opt, lapsum_stats_t* stats, lapsum_stream_t stream) {
+    lapsum_options_t o;
+    if (opt) o = *opt; else lapsum_default_options(&o);
+    lapsum_status_t a = check_topk_args(scores, n, k, n, o);
+    if (a != LAPSUM_OK || !tau_out) return LAPSUM_ERR_INVALID_ARGUMENT;
+    try {
+        hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+        Workspace* w = nullptr;
+        lapsum_status_t gs = get_ws(st, n, &w);
+        if (gs != LAPSUM_OK) return gs;
+        return order_stats_impl(w, scores, n, k, o, stats, st, tau_out);
+    } catch (...) {
+        return LAPSUM_ERR_INTERNAL;
+    }
+}
+
+lapsum_status_t lapsum_hard_topk(const float* scores, int64_t n, int64_t k, float* mask_out, double* tau_out,
+                                 const lapsum_options_t* opt, lapsum_stats_t* stats, lapsum_stream_t stream) {
+    lapsum_options_t o;
+    if (opt) o = *opt; else lapsum_default_options(&o);
+    lapsum_status_t a = check_topk_args(scores, n, k, n, o);
+    if (a != LAPSUM_OK || !mask_out) return LAPSUM_ERR_INVALID_ARGUMENT;
+    try {
+        hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+        Workspace* w = nullptr;
+        lapsum_status_t gs = get_ws(st, n, &w);
+        if (gs != LAPSUM_OK) return gs;
+        lapsum_status_t rs = order_stats_impl(w, scores, n, k, o, stats, st, tau_out);
+        if (rs == LAPSUM_ERR_NONFINITE_INPUT) {
+            launch_fill(mask_out, n, std::numeric_limits<float>::quiet_NaN(), st);
+            return rs;
+        }
+        if (rs != LAPSUM_OK) return rs;
+        launch_mask(scores, n, w->ctl, mask_out, st);
+        return hip_ok(hipGetLastError());
+    } catch (...) {
+        return LAPSUM_ERR_INTERNAL;
+    }
+}
+
+lapsum_status_t lapsum_dftopk(const float* scores, int64_t n, int64_t k, float t, float* p_out, double* b_out,
+                              const lapsum_options_t* opt, lapsum_stats_t* stats, lapsum_stream_t stream) {
+    lapsum_options_t o;
+    if (opt) o = *opt; else lapsum_default_options(&o);
+    lapsum_status_t a = check_topk_args(scores, n, k, n - 1, o);
+    if (a != LAPSUM_OK || !p_out || !(t > 0.0f) || !std::isfinite(t)) return LAPSUM_ERR_INVALID_ARGUMENT;
+    try {
+        hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+        Workspace* w = nullptr;
+        lapsum_status_t gs = get_ws(st, n, &w);
+        if (gs != LAPSUM_OK) return gs;
+        lapsum_status_t rs = order_stats_impl(w, scores, n, k, o, nullptr, st, nullptr);
+        if (rs == LAPSUM_ERR_NONFINITE_INPUT) {
+            launch_set_nan_b(w->ctl, b_out, st);
+            launch_fill(p_out, n, std::numeric_limits<float>::quiet_NaN(), st);
+            return rs;
+        }
+        if (rs != LAPSUM_OK) return rs;
+        launch_copy_b(w->ctl, b_out, st);
+        w->probs_parts = launch_probs(scores, n, (double)t, p_out, w->ctl, w->part, st);
+        if (hipGetLastError() != hipSuccess) return LAPSUM_ERR_HIP;
+        if (stats) {
+            std::memset(stats, 0, sizeof(*stats));
+            launch_sum_p(w->ctl, w->part, w->probs_parts, st);
+            if (hipStreamSynchronize(st) != hipSuccess) return LAPSUM_ERR_HIP;
+            Ctl c;
+            if (hipMemcpy(&c, w->ctl, sizeof(Ctl), hipMemcpyDeviceToHost) != hipSuccess) return LAPSUM_ERR_HIP;
+            stats->b = c.b;
+            stats->sum_p = c.sum_p;
+            stats->status = (c.flags & kFlagNonFinite) ? LAPSUM_ERR_NONFINITE_INPUT
+                            : (c.flags & kFlagInternal) ? LAPSUM_ERR_INTERNAL : LAPSUM_OK;
+        }
+        return LAPSUM_OK;
+    } catch (...) {
+        return LAPSUM_ERR_INTERNAL;
+    }
 }
 
 }  // extern "C"

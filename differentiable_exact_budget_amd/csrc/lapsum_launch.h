@@ -33,10 +33,18 @@ void launch_vjp(const float* r, const float* g, long long n, double t, const dou
                 double* part, hipStream_t st, hipEvent_t* ev_mid, bool kt, double* dk_out, double* dt_out);
 void launch_fill(float* p, long long n, float v, hipStream_t st);
 void launch_set_nan_b(Ctl* ctl, double* b_out, hipStream_t st);
+void launch_copy_b(const Ctl* ctl, double* b_out, hipStream_t st);  // b_out may be null
 
 // lapsum_ceiling.hip
 void launch_copy(const float* a, float* b, long long n, hipStream_t st);
 void launch_read(const float* a, long long n, float* sink, hipStream_t st);
+
+// lapsum_topk.hip
+void launch_small_sort(const float* r, int n, Ctl* ctl, uint32_t* keys_out, hipStream_t st);
+void launch_pick_sorted(const uint32_t* keys, long long n, long long k, Ctl* ctl, double* tau_out, hipStream_t st);
+void launch_bucket_pick(const uint32_t* bucket_vals, const uint32_t* bucket_cnt, int cap, long long k, Ctl* ctl,
+                        double* tau_out, hipStream_t st);
+void launch_mask(const float* r, long long n, const Ctl* ctl, float* mask, hipStream_t st);
 
 // lapsum_sort.hip
 void launch_small_solve(const float* r, int n, double k, double t, Ctl* ctl, SolveScratch sc, double* b_out,

@@ -174,6 +174,38 @@ lapsum_status_t lapsum_vjp_kt(const float* scores, const float* g, int64_t n, fl
                               float* grad_out, double* dk_out, double* dt_out,
                               const lapsum_options_t* opt, lapsum_stats_t* stats, lapsum_stream_t stream);
 
+/*
+ * Order statistics from the top (hard top-k and DFTopK; gist.science summary
+ * section 2.3: DFTopK puts the threshold at the midpoint of the k-th and
+ * (k+1)-th order statistics and is LapSum's zero-temperature limit).  They
+ * run through the same machinery as lapsum_forward_ex: the full sort for
+ * n <= opt->auto_threshold, else a noiseless sample, the streaming filter and
+ * a count-based certification (both order statistics inside the band), with
+ * widening and the full-sort fallback.  opt and stats as in
+ * lapsum_forward_ex (the LapSum-only stats fields stay zero).
+ *
+ * lapsum_topk_threshold: tau_out (device fp64[2]) gets the k-th largest score
+ *   and the (k+1)-th largest (-inf when k = n).  1 <= k <= n.
+ * lapsum_hard_topk: mask_out (device fp32[n]) gets 1 where
+ *   scores[i] >= the k-th largest, else 0 (with ties at the threshold more
+ *   than k entries are 1); tau_out as above, or NULL.  1 <= k <= n.
+ * lapsum_dftopk: b_out (device fp64[1], or NULL) gets
+ *   b = (k-th largest + (k+1)-th largest) / 2, p_out (device fp32[n]) gets
+ *   p_i = F((scores[i] - b)/t) with LapSum's Laplace CDF; its mass generally
+ *   differs from k.  1 <= k <= n - 1, t > 0.
+ * Errors: LAPSUM_ERR_INVALID_ARGUMENT (checked before any launch) for NULL
+ * required pointers, n outside [1, 2^32), k outside its range, a bad t or
+ * bad options; LAPSUM_ERR_NONFINITE_INPUT when the bracketing path meets a
+ * NaN or infinity (outputs become NaN; the full-sort path reports it in
+ * stats->status).
+ */
+lapsum_status_t lapsum_topk_threshold(const float* scores, int64_t n, int64_t k, double* tau_out,
+                                      const lapsum_options_t* opt, lapsum_stats_t* stats, lapsum_stream_t stream);
+lapsum_status_t lapsum_hard_topk(const float* scores, int64_t n, int64_t k, float* mask_out, double* tau_out,
+                                 const lapsum_options_t* opt, lapsum_stats_t* stats, lapsum_stream_t stream);
+lapsum_status_t lapsum_dftopk(const float* scores, int64_t n, int64_t k, float t, float* p_out, double* b_out,
+                              const lapsum_options_t* opt, lapsum_stats_t* stats, lapsum_stream_t stream);
+
 /* Free every cached workspace (waits for their streams). */
 void lapsum_release_workspaces(void);
 

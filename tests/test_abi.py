@@ -143,3 +143,22 @@ def test_bracket_ranks_match_oracle(oracle_mod, s, q, delta):
     lo, hi = ctypes.c_int64(), ctypes.c_int64()
     assert L.lib().lapsum_test_binomial_ranks(s, q, delta, ctypes.byref(lo), ctypes.byref(hi)) == 0
     assert (lo.value, hi.value) == oracle_mod.binomial_bounds(s, q, delta)
+
+
+def test_order_statistic_entry_points_reject_bad_arguments():
+    lib = L.lib()
+    for n, k in ((100, 0), (100, 101), (0, 1), (2**32, 1)):
+        assert lib.lapsum_topk_threshold(FAKE, n, k, FAKE, None, None, None) == INVALID
+        assert lib.lapsum_hard_topk(FAKE, n, k, FAKE, None, None, None, None) == INVALID
+    assert lib.lapsum_topk_threshold(FAKE, 100, 5, None, None, None, None) == INVALID
+    assert lib.lapsum_hard_topk(FAKE, 100, 5, None, FAKE, None, None, None) == INVALID
+    assert lib.lapsum_hard_topk(None, 100, 5, FAKE, FAKE, None, None, None) == INVALID
+    # DFTopK needs the (k+1)-th largest: k <= n - 1, and t > 0
+    assert lib.lapsum_dftopk(FAKE, 100, 100, 0.1, FAKE, FAKE, None, None, None) == INVALID
+    assert lib.lapsum_dftopk(FAKE, 100, 5, 0.0, FAKE, FAKE, None, None, None) == INVALID
+    assert lib.lapsum_dftopk(FAKE, 100, 5, float("nan"), FAKE, FAKE, None, None, None) == INVALID
+    assert lib.lapsum_dftopk(FAKE, 100, 5, 0.1, None, FAKE, None, None, None) == INVALID
+    o = L.default_options(path=7)
+    assert lib.lapsum_topk_threshold(FAKE, 100, 5, FAKE, ctypes.byref(o), None, None) == INVALID
+    # the budget/temperature VJP needs at least one output
+    assert lib.lapsum_vjp_kt(FAKE, FAKE, 100, 0.1, FAKE, None, None, None, None, None, None) == INVALID

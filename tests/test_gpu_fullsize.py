@@ -57,3 +57,30 @@ def test_full_size(oracle_mod, name, mode):
         if np.isfinite(st["a_R"]):
             assert abs(st["g_aR"] - ref["G_aR"]) <= 1e-6 * max(ref["G_aR"], 1.0)
             assert ref["G_aR"] < cfg.k
+
+
+def test_full_size_order_statistics(oracle_mod):
+    """Hard top-k and DFTopK on the 10^8-score mixture, k = 10^5, in the launch
+    configuration bench.py times."""
+    print("\nfull-size C4 order statistics", flush=True)
+    r, _, cfg = workloads.config_inputs("C4")
+    rd = to_dev(r)
+    k = int(cfg.k)
+    mask, tau, st = L.hard_topk(rd, k, stats=True)
+    p, b = L.dftopk(rd, k, cfg.t)
+    torch.cuda.synchronize()
+    assert st["status"] == 0 and st["path_taken"] == 2
+    got = tau.cpu().numpy()
+    m = mask.cpu().numpy()
+    ph = p.cpu().numpy()
+    bg = float(b.item())
+    del rd, mask, p
+    torch.cuda.empty_cache()
+    r64 = r.astype(np.float64)
+    mask_ref, tau_ref, _ = oracle_mod.hard_topk(r64, k)
+    assert got[0] == tau_ref
+    assert np.array_equal(m.astype(np.float64), mask_ref)
+    p_ref, b_ref, s_ref = oracle_mod.dftopk(r64, k, t32(cfg.t))
+    assert bg == b_ref and got[1] == 2.0 * b_ref - got[0]
+    assert np.max(np.abs(ph.astype(np.float64) - p_ref)) <= 2e-6
+    assert abs(float(ph.astype(np.float64).sum()) - s_ref) <= 1e-5 * k
