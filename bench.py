@@ -196,6 +196,19 @@ def extras(L, torch, rd, gd, cfg):
         ms = timed(torch, fn)
         res[name] = {"median_ms": round(ms, 5), "scores_per_s": n / (ms * 1e-3),
                      "alg_GBps": round(bpe * n / (ms * 1e-3) / 1e9, 1)}
+    # many independent rows (seeded N(0,1) rows, k = n/32 per row, t = 0.05)
+    import numpy as np
+    for rows, m in ((4096, 4096), (65536, 256)):
+        rng = np.random.default_rng(rows + m)
+        rr = torch.from_numpy(rng.standard_normal((rows, m)).astype(np.float32)).to(rd.device)
+        gg = torch.from_numpy(rng.standard_normal((rows, m)).astype(np.float32)).to(rd.device)
+        kk = m / 32.0
+        _, bb = L.forward_rows(rr, kk, 0.05)
+        fwd = timed(torch, lambda: L.forward_rows(rr, kk, 0.05))
+        bwd = timed(torch, lambda: L.vjp_rows(rr, gg, 0.05, bb))
+        res[f"rows_{rows}x{m}"] = {"forward_ms": round(fwd, 5), "vjp_ms": round(bwd, 5),
+                                   "scores_per_s": rows * m / ((fwd + bwd) * 1e-3)}
+        del rr, gg
     return res
 
 

@@ -14,7 +14,8 @@ import torch
 from ._binding import (PATH_AUTO, PATH_BRACKET, PATH_FORCE_FALLBACK, PATH_FULL, LapsumError, Options, Stats,
                        default_options, lib)
 
-__all__ = ["forward", "vjp", "vjp_kt", "soft_topk", "topk_threshold", "hard_topk", "dftopk", "SoftTopK", "default_options", "Options", "Stats", "LapsumError",
+__all__ = ["forward", "vjp", "vjp_kt", "soft_topk", "topk_threshold", "hard_topk", "dftopk",
+           "forward_rows", "vjp_rows", "soft_topk_rows", "SoftTopK", "default_options", "Options", "Stats", "LapsumError",
            "PATH_AUTO", "PATH_FULL", "PATH_BRACKET", "PATH_FORCE_FALLBACK", "release_workspaces"]
 
 
@@ -198,6 +199,71 @@ def dftopk(r: torch.Tensor, k: int, t: float, *, options: Options = None, stats:
     if rc != 0:
         raise LapsumError(rc, "lapsum_dftopk")
     return (p, b, st.as_dict()) if stats else (p, b)
+
+
+def forward_rows(r: torch.Tensor, k, t: float):
+    """Row-wise solve of a 2-D fp32 tensor [rows, n]: k is a number or a
+    float64 tensor of rows budgets on r's device.  Returns (p, b), b float64[rows]."""
+    _check_scores(r, "r")
+    if r.dim() != 2:
+        raise ValueError("r must be 2-D [rows, n]")
+    rows, n = r.shape
+    with torch.cuda.device(r.device):
+        p = torch.empty_like(r)
+        b = torch.empty(rows, dtype=torch.float64, device=r.device)
+        if isinstance(k, torch.Tensor):
+            kr = k.to(device=r.device, dtype=torch.float64).contiguous()
+            if kr.numel() != rows:
+                raise ValueError("k must have one budget per row")
+            rc = lib().lapsum_forward_batched(r.data_ptr(), rows, n, 0.0, kr.data_ptr(), float(t), p.data_ptr(),
+                                              b.data_ptr(), _stream_ptr(r.device))
+        else:
+            rc = lib().lapsum_forward_batched(r.data_ptr(), rows, n, float(k), None, float(t), p.data_ptr(),
+                                              b.data_ptr(), _stream_ptr(r.device))
+    if rc != 0:
+        raise LapsumError(rc, "lapsum_forward_batched")
+    return p, b
+
+
+def vjp_rows(r: torch.Tensor, g: torch.Tensor, t: float, b: torch.Tensor):
+    """Row-wise VJP: grad[i] = (f/t)(g[i] - sum g f / sum f) within row i."""
+    _check_scores(r, "r")
+    _check_scores(g, "g")
+    if r.dim() != 2 or g.shape != r.shape:
+        raise ValueError("r and g must be 2-D tensors of one shape")
+    if b.dtype != torch.float64 or b.numel() != r.shape[0]:
+        raise ValueError("b must be the float64[rows] tensor returned by forward_rows")
+    with torch.cuda.device(r.device):
+        out = torch.empty_like(r)
+        rc = lib().lapsum_vjp_batched(r.data_ptr(), g.data_ptr(), r.shape[0], r.shape[1], float(t), b.data_ptr(),
+                                      out.data_ptr(), _stream_ptr(r.device))
+    if rc != 0:
+        raise LapsumError(rc, "lapsum_vjp_batched")
+    return out
+
+
+class SoftTopKRows(torch.autograd.Function):
+    """Row-wise exact-budget soft top-k with the analytic VJP per row."""
+
+    @staticmethod
+    def forward(ctx, r, k, t):
+        rc = r.contiguous()
+        p, b = forward_rows(rc, k, t)
+        ctx.save_for_backward(rc, b)
+        ctx.t = float(t)
+        return p
+
+    @staticmethod
+    def backward(ctx, g):
+        r, b = ctx.saved_tensors
+        return vjp_rows(r, g.contiguous().to(torch.float32), ctx.t, b), None, None
+
+
+def soft_topk_rows(r: torch.Tensor, k, t: float) -> torch.Tensor:
+    """Differentiable exact-budget soft top-k along the last dimension."""
+    shape = r.shape
+    p = SoftTopKRows.apply(r.reshape(-1, shape[-1]), k, t)
+    return p.reshape(shape)
 
 
 def release_workspaces() -> None:

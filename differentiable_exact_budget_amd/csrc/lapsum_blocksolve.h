@@ -209,6 +209,25 @@ LS_DEV int block_max_int(int x, int* s) {
     return r;
 }
 
+// segment aggregates of sorted scores v_0..v_{c-1} held as keys in `keys`
+// (LDS or global): P = sum e^{(v_i - v_last)/t}, Bx = sum_{i>0} e^{(v_0 - v_i)/t}.
+// Argument in fp64 (exact difference), exponential in fp32, sums in fp64.
+template <int NT>
+__device__ void segment_aggregates(const uint32_t* keys, int c, double inv_t, float* first, float* last,
+                                   double* P, double* Bx, double* scratch) {
+    const float f = key2f(keys[0]);
+    const float l = key2f(keys[c - 1]);
+    double p = 0.0, bx = 0.0;
+    for (int i = threadIdx.x; i < c; i += NT) {
+        const double v = (double)key2f(keys[i]);
+        p += (double)exp_neg((float)((v - (double)l) * inv_t));
+        if (i > 0) bx += (double)exp_neg((float)(((double)f - v) * inv_t));
+    }
+    const double ps = block_sum<NT>(p, scratch);
+    const double bs = block_sum<NT>(bx, scratch);
+    if (threadIdx.x == 0) { *first = f; *last = l; *P = ps; *Bx = bs; }
+}
+
 // ---------------------------------------------------------------------------
 // Threshold solve over sorted segments.
 // ---------------------------------------------------------------------------

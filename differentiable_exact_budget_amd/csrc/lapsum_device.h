@@ -166,7 +166,8 @@ LS_DEV uint32_t block_exclusive_scan(uint32_t v, uint32_t* total, uint32_t* scra
     return res;
 }
 
-// block sum of double in a fixed order (wave butterflies, then wave 0)
+// block sum of double in a fixed order (wave butterflies, then wave 0); the
+// result is valid in wave 0 only (broadcast it through LDS where others need it)
 template <int NT>
 LS_DEV double block_sum(double v, double* scratch /* >= NT/64 */) {
     constexpr int NW = NT / 64;

@@ -1002,4 +1002,74 @@ lapsum_status_t lapsum_dftopk(const float* scores, int64_t n, int64_t k, float t
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// many independent rows
+// ---------------------------------------------------------------------------
+lapsum_status_t lapsum_forward_batched(const float* scores, int64_t rows, int64_t n, double k, const double* k_rows,
+                                       float t, float* p_out, double* b_out, lapsum_stream_t stream) {
+    if (!scores || !p_out || !b_out || rows < 1 || rows > 0x7FFFFFFFll || n < 1 || n > 0xFFFFFFFFll)
+        return LAPSUM_ERR_INVALID_ARGUMENT;
+    if (!k_rows && !(k > 0.0 && k < (double)n && std::isfinite(k))) return LAPSUM_ERR_INVALID_ARGUMENT;
+    if (!(t > 0.0f) || !std::isfinite(t)) return LAPSUM_ERR_INVALID_ARGUMENT;
+    try {
+        hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+        if (n <= rows_supported_max()) {
+            launch_rows_forward(scores, rows, (int)n, k_rows, k, (double)t, p_out, b_out, st);
+            return hip_ok(hipGetLastError());
+        }
+        // long rows: the single-vector solver, row by row
+        std::vector<double> kh;
+        if (k_rows) {
+            kh.resize((size_t)rows);
+            if (hipMemcpyAsync(kh.data(), k_rows, sizeof(double) * (size_t)rows, hipMemcpyDeviceToHost, st) !=
+                    hipSuccess ||
+                hipStreamSynchronize(st) != hipSuccess)
+                return LAPSUM_ERR_HIP;
+        }
+        lapsum_options_t o;
+        lapsum_default_options(&o);
+        Workspace* w = nullptr;
+        lapsum_status_t gs = get_ws(st, n, &w);
+        if (gs != LAPSUM_OK) return gs;
+        for (int64_t i = 0; i < rows; ++i) {
+            const double ki = k_rows ? kh[(size_t)i] : k;
+            const float* ri = scores + i * n;
+            if (!(ki > 0.0 && ki < (double)n)) {
+                launch_set_nan_b(w->ctl, b_out + i, st);
+                launch_fill(p_out + i * n, n, std::numeric_limits<float>::quiet_NaN(), st);
+                continue;
+            }
+            lapsum_status_t rs = forward_impl(ri, n, ki, t, p_out + i * n, b_out + i, o, nullptr, st);
+            if (rs != LAPSUM_OK && rs != LAPSUM_ERR_NONFINITE_INPUT) return rs;
+        }
+        return hip_ok(hipGetLastError());
+    } catch (...) {
+        return LAPSUM_ERR_INTERNAL;
+    }
+}
+
+lapsum_status_t lapsum_vjp_batched(const float* scores, const float* g, int64_t rows, int64_t n, float t,
+                                   const double* b, float* grad_out, lapsum_stream_t stream) {
+    if (!scores || !g || !b || !grad_out || rows < 1 || rows > 0x7FFFFFFFll || n < 1 || n > 0xFFFFFFFFll)
+        return LAPSUM_ERR_INVALID_ARGUMENT;
+    if (!(t > 0.0f) || !std::isfinite(t)) return LAPSUM_ERR_INVALID_ARGUMENT;
+    try {
+        hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+        if (n <= rows_supported_max()) {
+            launch_rows_vjp(scores, g, rows, (int)n, (double)t, b, grad_out, st);
+            return hip_ok(hipGetLastError());
+        }
+        Workspace* w = nullptr;
+        lapsum_status_t gs = get_ws(st, 0, &w);
+        if (gs != LAPSUM_OK) return gs;
+        for (int64_t i = 0; i < rows; ++i)
+            launch_vjp(scores + i * n, g + i * n, n, (double)t, b + i, grad_out + i * n, w->ctl, w->part, st, nullptr,
+                       false, nullptr, nullptr);
+        return hip_ok(hipGetLastError());
+    } catch (...) {
+        return LAPSUM_ERR_INTERNAL;
+    }
+}
+
 }  // extern "C"

@@ -46,6 +46,13 @@ void launch_bucket_pick(const uint32_t* bucket_vals, const uint32_t* bucket_cnt,
                         double* tau_out, hipStream_t st);
 void launch_mask(const float* r, long long n, const Ctl* ctl, float* mask, hipStream_t st);
 
+// lapsum_batched.hip
+int rows_supported_max();
+void launch_rows_forward(const float* r, long long rows, int n, const double* k_rows, double k_all, double t, float* p,
+                         double* b_out, hipStream_t st);
+void launch_rows_vjp(const float* r, const float* g, long long rows, int n, double t, const double* b, float* grad,
+                     hipStream_t st);
+
 // lapsum_sort.hip
 void launch_small_solve(const float* r, int n, double k, double t, Ctl* ctl, SolveScratch sc, double* b_out,
                         uint32_t* keys_out, hipStream_t s);

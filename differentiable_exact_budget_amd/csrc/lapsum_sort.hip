@@ -3,13 +3,15 @@
 // Full-sort solver (Fast LapSum paper, gist.science section 2.2): sort all
 // scores, build the threshold curve with one stable prefix/suffix scan,
 // search the interval where the budget balances and take the closed-form
-// root there.  Band solve (same section, "Solucion Exacta"): the same on the
+// root there.  Band solve (same section, bracketing step 3): the same on the
 // middle band only, with the out-of-band scores entering as tail sums.
 //
 // Kernels
 //   k_small_solve   n <= 16384: one workgroup sorts in LDS and solves.
-//   k_bucket_solve  one workgroup per band bucket sorts it in LDS and
-//                   publishes segment aggregates; the last one solves.
+//   k_bucket_agg    one workgroup per band bucket: count, min, max and the
+//                   two order-free exp-sums of its (unsorted) scores.
+//   k_band_root     one workgroup: the curve across buckets, the root bucket
+//                   sorted in LDS, the root.
 //   k_radix_hist    all four 8-bit digit histograms in one read; the last
 //                   workgroup turns them into global digit offsets.
 //   k_radix_pass    one LSD digit pass (decoupled look-back across tiles).
@@ -19,25 +21,6 @@
 #include "lapsum_launch.h"
 
 namespace lapsum {
-
-// segment aggregates of sorted scores v_0..v_{c-1} held as keys in `keys`
-// (LDS or global): P = sum e^{(v_i - v_last)/t}, Bx = sum_{i>0} e^{(v_0 - v_i)/t}.
-// Argument in fp64 (exact difference), exponential in fp32, sums in fp64.
-template <int NT>
-__device__ void segment_aggregates(const uint32_t* keys, int c, double inv_t, float* first, float* last,
-                                   double* P, double* Bx, double* scratch) {
-    const float f = key2f(keys[0]);
-    const float l = key2f(keys[c - 1]);
-    double p = 0.0, bx = 0.0;
-    for (int i = threadIdx.x; i < c; i += NT) {
-        const double v = (double)key2f(keys[i]);
-        p += (double)exp_neg((float)((v - (double)l) * inv_t));
-        if (i > 0) bx += (double)exp_neg((float)(((double)f - v) * inv_t));
-    }
-    const double ps = block_sum<NT>(p, scratch);
-    const double bs = block_sum<NT>(bx, scratch);
-    if (threadIdx.x == 0) { *first = f; *last = l; *P = ps; *Bx = bs; }
-}
 
 // ---------------------------------------------------------------------------
 // n <= 16384: everything in one workgroup

@@ -206,6 +206,26 @@ lapsum_status_t lapsum_hard_topk(const float* scores, int64_t n, int64_t k, floa
 lapsum_status_t lapsum_dftopk(const float* scores, int64_t n, int64_t k, float t, float* p_out, double* b_out,
                               const lapsum_options_t* opt, lapsum_stats_t* stats, lapsum_stream_t stream);
 
+/*
+ * Many independent rows (the operator applied per row, as in routing and
+ * pruning; gist.science summary sections 1 and 5).  scores, p_out, g,
+ * grad_out: device fp32[rows * n], row i at offset i * n.  b_out / b: device
+ * fp64[rows].  Budget: k_rows (device fp64[rows], each in (0, n)) when not
+ * NULL, else the scalar k for every row.  Rows with n <= 16384 are solved one
+ * workgroup per row in LDS (sort, curve scan, closed-form root, p); longer
+ * rows run through lapsum_forward_ex's solver one after another.  A row with
+ * a non-finite score or a budget outside (0, n) gets b = NaN and p = NaN;
+ * the call still returns LAPSUM_OK.  Argument errors (NULL pointers,
+ * rows < 1, n outside [1, 2^32), a bad scalar k when k_rows is NULL, a bad t)
+ * return LAPSUM_ERR_INVALID_ARGUMENT before any launch.  Asynchronous on
+ * `stream` (except for long rows with k_rows, whose budgets are read first).
+ */
+lapsum_status_t lapsum_forward_batched(const float* scores, int64_t rows, int64_t n, double k,
+                                       const double* k_rows, float t, float* p_out, double* b_out,
+                                       lapsum_stream_t stream);
+lapsum_status_t lapsum_vjp_batched(const float* scores, const float* g, int64_t rows, int64_t n, float t,
+                                   const double* b, float* grad_out, lapsum_stream_t stream);
+
 /* Free every cached workspace (waits for their streams). */
 void lapsum_release_workspaces(void);
 

@@ -162,3 +162,15 @@ def test_order_statistic_entry_points_reject_bad_arguments():
     assert lib.lapsum_topk_threshold(FAKE, 100, 5, FAKE, ctypes.byref(o), None, None) == INVALID
     # the budget/temperature VJP needs at least one output
     assert lib.lapsum_vjp_kt(FAKE, FAKE, 100, 0.1, FAKE, None, None, None, None, None, None) == INVALID
+
+
+def test_batched_entry_points_reject_bad_arguments():
+    lib = L.lib()
+    assert lib.lapsum_forward_batched(None, 4, 10, 2.0, None, 0.1, FAKE, FAKE, None) == INVALID
+    assert lib.lapsum_forward_batched(FAKE, 0, 10, 2.0, None, 0.1, FAKE, FAKE, None) == INVALID
+    assert lib.lapsum_forward_batched(FAKE, 4, 0, 2.0, None, 0.1, FAKE, FAKE, None) == INVALID
+    assert lib.lapsum_forward_batched(FAKE, 4, 10, 10.0, None, 0.1, FAKE, FAKE, None) == INVALID  # k = n
+    assert lib.lapsum_forward_batched(FAKE, 4, 10, 2.0, None, 0.0, FAKE, FAKE, None) == INVALID
+    assert lib.lapsum_forward_batched(FAKE, 4, 10, 2.0, None, 0.1, None, FAKE, None) == INVALID
+    assert lib.lapsum_vjp_batched(FAKE, FAKE, 4, 10, 0.1, None, FAKE, None) == INVALID
+    assert lib.lapsum_vjp_batched(FAKE, FAKE, 2**31, 10, 0.1, FAKE, FAKE, None) == INVALID
