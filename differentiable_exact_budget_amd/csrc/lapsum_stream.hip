@@ -22,6 +22,7 @@
 
 #include "lapsum_launch.h"
 #include "lapsum_streamio.h"
+#include "lapsum_band.h"
 
 namespace lapsum {
 
@@ -91,30 +92,6 @@ LS_DEV double sum_parts(const double* part, int stride, int off, int nparts, dou
 // ---------------------------------------------------------------------------
 // streaming filter
 // ---------------------------------------------------------------------------
-struct FilterState {
-    float aL, aR, ls;
-    int ng, J, cap;
-    const float* sp;
-    const float* iw;
-    uint32_t* bucket_cnt;
-    uint32_t* bucket_vals;
-};
-
-// bucket of a band score: splitter gap by binary search, then equal-width
-// sub-bucket inside a finite gap (monotone in v)
-LS_DEV int band_bucket(const FilterState& fs, float v) {
-    int g = 0;
-    for (int step = 128; step > 0; step >>= 1)
-        if (g + step < fs.ng && fs.sp[g + step] <= v) g += step;
-    int sub = 0;
-    const float iwg = fs.iw[g];
-    if (fs.J > 1 && iwg > 0.0f) {
-        const float f = (v - fs.sp[g]) * iwg;
-        sub = f < (float)(fs.J - 1) ? (int)f : fs.J - 1;
-    }
-    return g * fs.J + sub;
-}
-
 // e^{(a_L - v)/t} and e^{(v - a_R)/t} of a band score (0 for an open end)
 LS_DEV void band_sums(const FilterState& fs, float v, double& BL, double& BR) {
     if (fs.aL > -INFINITY) BL += (double)__builtin_amdgcn_exp2f(-(v - fs.aL) * fs.ls);

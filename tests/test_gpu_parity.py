@@ -239,3 +239,20 @@ def test_nonfinite_scores(n, bad):
     else:
         p, b, st = L.forward(rd, 10.0, 0.1, stats=True)
         assert st["status"] == 2 and np.isnan(b.item())
+
+
+@pytest.mark.parametrize("frac", [0.25, 0.5])
+def test_bracket_many_splitter_gaps(oracle_mod, frac):
+    """Large budgets put hundreds of sample points inside the bracket, hence
+    hundreds of splitter gaps: every gap must get its own buckets (no pile-up
+    in one bucket, no overflow fallback)."""
+    n = 2_000_000
+    r = workloads.scores("normal", n, 77)
+    g = workloads.upstream(n, 78)
+    k = frac * n
+    p, b, st, grad = run(r, k, 0.05, g)
+    # before every gap had its own buckets, the scores above gap 255 piled
+    # into one bucket, overflowed it and forced the full-sort fallback
+    assert st["status"] == 0 and st["path_taken"] == 2, st["path_taken"]
+    b_ref = check_forward(oracle_mod, r, k, 0.05, p, b, label=f"k={k}")
+    check_vjp(oracle_mod, r, g, 0.05, b_ref, grad, label=f"k={k}")
