@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 OUT = os.path.join(HERE, "liblapsum.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["lapsum_sample.hip", "lapsum_stream.hip", "lapsum_sort.hip", "lapsum_ceiling.hip", "lapsum_topk.hip", "lapsum_batched.hip", "lapsum_host.cpp"]
+SOURCES = ["lapsum_sample.hip", "lapsum_stream.hip", "lapsum_sort.hip", "lapsum_ceiling.hip", "lapsum_topk.hip", "lapsum_batched.hip", "lapsum_heavy.hip", "lapsum_host.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang",

@@ -268,7 +268,9 @@ struct SolveScratch {      // global scratch
     double* eP; double* eB;    // per score of the root segment: P_j, B_j
 };
 
-struct SolveOut { double b; long long jstar; int ok; };
+// big: the root segment holds more scores than the LDS sort buffer; jstar is
+// then the segment's index and b is not formed
+struct SolveOut { double b; long long jstar; int ok; int big; };
 
 // log-space closed-form root of  A/(2w) + D - B w/2 = 0  (w > 0)
 LS_DEV double log_root(double lnA, double lnB, double D) {
@@ -394,11 +396,15 @@ __device__ __attribute__((always_inline)) SolveOut segment_solve(const SegView s
     __threadfence_block();
     __syncthreads();
 
-    SolveOut out; out.b = 0.0; out.jstar = -1; out.ok = 1;
+    SolveOut out; out.b = 0.0; out.jstar = -1; out.ok = 1; out.big = 0;
     if (tid == 0) s_owner = -1;
     if (sstar >= 0) {
         // ---- phase 4: per-score curve inside the root segment ----
         const uint32_t cS = sv.cnt[sstar], offS = sv.off[sstar], rankS = sc.rank[sstar];
+        if (sv.sortbuf && cS > (uint32_t)kBucketCapMax) {
+            out.big = 1;
+            out.jstar = sstar;
+        } else {
         const uint32_t* rk = sv.keys + offS;
         if (sv.sortbuf) {
             // unsorted segment: sort it in LDS first
@@ -574,6 +580,7 @@ __device__ __attribute__((always_inline)) SolveOut segment_solve(const SegView s
             if ((int)cS <= 4 * NT) phase4(std::integral_constant<int, 4>{});
             else phase4(std::integral_constant<int, EMAX>{});
         } else phase4(std::integral_constant<int, EMAX>{});
+        }  // not a big root segment
     } else if (tid == 0) {
         // the root lies below the first score of the segments
         double ref, lnA, lnB, clo, chi;

@@ -33,6 +33,8 @@ constexpr int kCandMax = 2048;           // sample values kept for the splitters
 constexpr int kFlagNonFinite = 1;
 constexpr int kFlagOverflow = 2;
 constexpr int kFlagInternal = 4;
+constexpr int kFlagBigRoot = 8;   // the root lies in a bucket too large for LDS (host sorts it)
+constexpr uint32_t kNotHeavy = 0xFFFFFFFFu;  // bucket slot offset marker: not an overflowed bucket
 
 // ---------------------------------------------------------------------------
 // control block: one per workspace, in device memory

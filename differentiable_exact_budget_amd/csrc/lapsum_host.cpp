@@ -62,6 +62,9 @@ struct Workspace {
     float* iw = nullptr;
     uint32_t* bucket_cnt = nullptr;
     uint32_t* bucket_vals = nullptr;
+    uint32_t* hoff = nullptr;   // per bucket: slot offset of an overflowed bucket's scores, or kNotHeavy
+    uint32_t* hfill = nullptr;  // per bucket: scores placed in that slot
+    std::vector<uint32_t> cnt_h, hoff_h;  // host copies (kept alive across async copies)
     SegArrays seg{};
     SolveScratch sc{};
     uint32_t* keysA = nullptr;
@@ -81,7 +84,7 @@ long long tiles_for(long long n) { return (n + kRadixTile - 1) / kRadixTile; }
 
 // layout of one workspace for forwards up to n_cap scores
 struct Layout {
-    size_t ctl, part, sample, sample_idx, sp, iw, bcnt, bvals, eU, eW, wide, seg_first, seg_last, seg_P, seg_Bx, seg_cnt, seg_off,
+    size_t ctl, part, sample, sample_idx, sp, iw, bcnt, bvals, hoff, hfill, eU, eW, wide, seg_first, seg_last, seg_P, seg_Bx, seg_cnt, seg_off,
         sc_pk, sc_pv, sc_bk, sc_bv, sc_bfx, sc_rank, sc_eP, sc_eB, keysA, keysB, hist, goff, status, total;
     size_t status_bytes;
 };
@@ -100,6 +103,8 @@ Layout make_layout(long long n_cap) {
     L.iw = take(sizeof(float) * kMaxBuckets);
     L.bcnt = take(sizeof(uint32_t) * kMaxBuckets);
     L.bvals = take(sizeof(uint32_t) * (size_t)kMaxBuckets * kBucketCapMax);
+    L.hoff = take(sizeof(uint32_t) * kMaxBuckets);
+    L.hfill = take(sizeof(uint32_t) * kMaxBuckets);
     L.eU = 0; L.eW = 0; L.wide = 0;
     L.seg_first = take(sizeof(float) * nseg);
     L.seg_last = take(sizeof(float) * nseg);
@@ -154,6 +159,8 @@ lapsum_status_t alloc_ws(Workspace* w, long long n_cap) {
     w->iw = reinterpret_cast<float*>(base + L.iw);
     w->bucket_cnt = reinterpret_cast<uint32_t*>(base + L.bcnt);
     w->bucket_vals = reinterpret_cast<uint32_t*>(base + L.bvals);
+    w->hoff = reinterpret_cast<uint32_t*>(base + L.hoff);
+    w->hfill = reinterpret_cast<uint32_t*>(base + L.hfill);
 
     w->seg = SegArrays{reinterpret_cast<float*>(base + L.seg_first), reinterpret_cast<float*>(base + L.seg_last),
                        reinterpret_cast<double*>(base + L.seg_P), reinterpret_cast<double*>(base + L.seg_Bx),
@@ -395,6 +402,36 @@ lapsum_status_t fill_stats(Workspace* w, hipStream_t st, long long n, lapsum_sta
     return LAPSUM_OK;
 }
 
+// Buckets that overflowed (more band scores than their capacity; the counts
+// and sums stay exact): give each one a slot in keysB sized by its exact
+// count and collect its scores with one more pass over r.  Returns false when
+// the slots would not fit (the caller then takes the full-sort fallback).
+bool heavy_buckets(Workspace* w, const float* r, long long n, int nb, int cap, hipStream_t st,
+                   long long* max_heavy) {
+    w->cnt_h.assign((size_t)nb, 0u);
+    if (hipMemcpyAsync(w->cnt_h.data(), w->bucket_cnt, sizeof(uint32_t) * (size_t)nb, hipMemcpyDeviceToHost, st) !=
+            hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+        return false;
+    const unsigned long long base_off = (unsigned long long)(w->keysB - w->bucket_vals);
+    w->hoff_h.assign((size_t)kMaxBuckets, kNotHeavy);
+    unsigned long long tot = 0;
+    *max_heavy = 0;
+    for (int b = 0; b < nb; ++b) {
+        if (w->cnt_h[(size_t)b] > (uint32_t)cap) {
+            w->hoff_h[(size_t)b] = (uint32_t)(base_off + tot);
+            tot += w->cnt_h[(size_t)b];
+            *max_heavy = std::max<long long>(*max_heavy, w->cnt_h[(size_t)b]);
+            if (base_off + tot >= 0xFFFFFFFFull || tot > (unsigned long long)w->n_cap) return false;
+        }
+    }
+    if (hipMemcpyAsync(w->hoff, w->hoff_h.data(), sizeof(uint32_t) * kMaxBuckets, hipMemcpyHostToDevice, st) !=
+        hipSuccess)
+        return false;
+    launch_heavy_collect(r, n, w->ctl, w->sp, w->iw, w->hoff, w->hfill, w->bucket_vals, st);
+    return hipGetLastError() == hipSuccess;
+}
+
 lapsum_status_t forward_impl(const float* r, int64_t n, double k, float t_f, float* p, double* b_out,
                              const lapsum_options_t& opt, lapsum_stats_t* stats, hipStream_t st) {
     lapsum_status_t a = check_args(r, n, k, t_f, p, b_out);
@@ -469,8 +506,8 @@ lapsum_status_t forward_impl(const float* r, int64_t n, double k, float t_f, flo
         br.nonfinite = (br.h.flags & kFlagNonFinite) != 0;
         br.overflow = (br.h.flags & kFlagOverflow) != 0;
         if (br.nonfinite) break;
-        certify(br.h, k, t, &br);
-        if (br.overflow || br.certified || path == LAPSUM_PATH_FORCE_FALLBACK) break;
+        certify(br.h, k, t, &br);  // overflow leaves the counts and sums exact
+        if (br.certified || path == LAPSUM_PATH_FORCE_FALLBACK) break;
         if (widen >= opt.max_widen) break;
         // widen the failing side: double its distance from s q
         if (br.gL < k) {
@@ -507,13 +544,43 @@ lapsum_status_t forward_impl(const float* r, int64_t n, double k, float t_f, flo
         if (stats) { fill_stats(w, st, n, stats); stats->status = LAPSUM_ERR_NONFINITE_INPUT; tm.collect(stats); }
         return LAPSUM_ERR_NONFINITE_INPUT;
     }
-    const bool fallback = !br.certified || br.overflow || path == LAPSUM_PATH_FORCE_FALLBACK;
+    bool fallback = !br.certified || path == LAPSUM_PATH_FORCE_FALLBACK;
+    long long max_heavy = 0;
+    bool heavy = false;
+    if (!fallback && br.overflow) {
+        tm.begin("heavy_collect");
+        heavy = heavy_buckets(w, r, n, br.h.nb, cap, st, &max_heavy);
+        tm.end();
+        if (!heavy) fallback = true;
+    }
     if (fallback) {
         run_full(w, r, n, k, t, b_out, st, tm);
     } else {
         tm.begin("bucket_solve");
-        launch_bucket_solve(w->bucket_vals, w->bucket_cnt, cap, br.h.nb, w->ctl, w->seg, w->sc, k, t, b_out, st);
+        launch_bucket_solve(w->bucket_vals, w->bucket_cnt, cap, br.h.nb, w->ctl, w->seg, w->sc, k, t, b_out, st,
+                            heavy ? w->hoff : nullptr);
         tm.end();
+        if (heavy && max_heavy > kBucketCapMax) {
+            // the root may lie in a bucket too large for the LDS sort: then the
+            // band root handed it over (flag, carries as tails); sort it and solve
+            Ctl c;
+            if (hipMemcpyAsync(&c, w->ctl, sizeof(Ctl), hipMemcpyDeviceToHost, st) != hipSuccess ||
+                hipStreamSynchronize(st) != hipSuccess)
+                return LAPSUM_ERR_HIP;
+            if (c.flags & kFlagBigRoot) {
+                const size_t bkt = (size_t)c.jstar;
+                const unsigned long long cnt = c.m;
+                const float* src = reinterpret_cast<const float*>(w->bucket_vals + w->hoff_h[bkt]);
+                tm.begin("root_bucket_sort");
+                const uint32_t epoch = next_epoch(w, st);
+                launch_radix_sort(src, (long long)cnt, w->keysA, w->keysB, w->hist_part, w->goff, w->status, epoch,
+                                  w->ctl, st);
+                tm.end();
+                tm.begin("root_bucket_solve");
+                launch_curve_tiles(w->keysB, (long long)cnt, w->ctl, w->seg, w->sc, k, t, b_out, st, true);
+                tm.end();
+            }
+        }
     }
     tm.begin("probs");
     w->probs_parts = launch_probs(r, n, t, p, w->ctl, w->part, st);

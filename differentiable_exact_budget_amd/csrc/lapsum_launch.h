@@ -46,6 +46,10 @@ void launch_bucket_pick(const uint32_t* bucket_vals, const uint32_t* bucket_cnt,
                         double* tau_out, hipStream_t st);
 void launch_mask(const float* r, long long n, const Ctl* ctl, float* mask, hipStream_t st);
 
+// lapsum_heavy.hip
+void launch_heavy_collect(const float* r, long long n, const Ctl* ctl, const float* sp, const float* iw,
+                          const uint32_t* hoff, uint32_t* hfill, uint32_t* base, hipStream_t st);
+
 // lapsum_batched.hip
 int rows_supported_max();
 void launch_rows_forward(const float* r, long long rows, int n, const double* k_rows, double k_all, double t, float* p,
@@ -56,12 +60,14 @@ void launch_rows_vjp(const float* r, const float* g, long long rows, int n, doub
 // lapsum_sort.hip
 void launch_small_solve(const float* r, int n, double k, double t, Ctl* ctl, SolveScratch sc, double* b_out,
                         uint32_t* keys_out, hipStream_t s);
+// hoff: null, or per bucket the slot offset of an overflowed bucket's scores (kNotHeavy otherwise)
 void launch_bucket_solve(uint32_t* bucket_vals, const uint32_t* bucket_cnt, int cap, int nb, Ctl* ctl, SegArrays seg,
-                         SolveScratch sc, double k, double t, double* b_out, hipStream_t s);
+                         SolveScratch sc, double k, double t, double* b_out, hipStream_t s,
+                         const uint32_t* hoff = nullptr);
 int radix_hist_blocks(long long n);
 void launch_radix_sort(const float* r, long long n, uint32_t* keysA, uint32_t* keysB, uint32_t* hist_part,
                        uint32_t* goff, unsigned long long* status, uint32_t epoch_base, Ctl* ctl, hipStream_t s);
 void launch_curve_tiles(const uint32_t* keys, long long n, Ctl* ctl, SegArrays seg, SolveScratch sc, double k, double t,
-                        double* b_out, hipStream_t s);
+                        double* b_out, hipStream_t s, bool ctl_tails = false);
 
 }  // namespace lapsum

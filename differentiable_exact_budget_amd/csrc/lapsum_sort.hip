@@ -84,15 +84,18 @@ __global__ __launch_bounds__(kSortThreads) void k_small_solve(const float* __res
 // ---------------------------------------------------------------------------
 constexpr int kAggThreads = 256;
 
+// hoff (may be null): per bucket, kNotHeavy, or the element offset from
+// bucket_vals of the slot holding all of an overflowed bucket's scores
 __global__ __launch_bounds__(kAggThreads) void k_bucket_agg(const uint32_t* __restrict__ bucket_vals,
                                                              const uint32_t* bucket_cnt, int cap, SegArrays seg,
-                                                             double inv_t) {
+                                                             double inv_t, const uint32_t* hoff) {
     __shared__ uint32_t s_kmin, s_kmax;
     __shared__ unsigned long long s_fx[2 * kAggThreads / 64];
     const int tid = threadIdx.x;
     const int bkt = blockIdx.x;
-    const int c = (int)min(bucket_cnt[bkt], (uint32_t)cap);
-    const size_t off = (size_t)bkt * (size_t)cap;
+    const uint32_t ho = hoff ? hoff[bkt] : kNotHeavy;
+    const int c = ho != kNotHeavy ? (int)bucket_cnt[bkt] : (int)min(bucket_cnt[bkt], (uint32_t)cap);
+    const size_t off = ho != kNotHeavy ? (size_t)ho : (size_t)bkt * (size_t)cap;
     if (tid == 0) { seg.cnt[bkt] = (uint32_t)c; seg.off[bkt] = (uint32_t)off; s_kmin = 0xFFFFFFFFu; s_kmax = 0u; }
     if (c == 0) return;
     const uint32_t* vals = bucket_vals + off;
@@ -134,10 +137,24 @@ __global__ __launch_bounds__(kSortThreads) void k_band_root(const uint32_t* buck
     Tails tl{ctl->aL, ctl->aR, ctl->S_L, ctl->S_R, (double)ctl->m, (double)ctl->c_R, k, t, inv_t};
     SolveOut o = segment_solve<kSortThreads, kSortItems>(sv, tl, sc, s_k, s_v, s_int);
     if (threadIdx.x == 0) {
-        if (!o.ok) atomicOr(&ctl->flags, kFlagInternal);
-        ctl->b = o.b;
-        ctl->jstar = o.jstar;
-        if (b_out) *b_out = o.b;
+        if (o.big) {
+            // hand the root bucket over to a multi-workgroup sort: everything
+            // below it becomes the lower tail (its carry), everything above it
+            // the upper tail, and the bucket itself the scores to solve over
+            const int s = (int)o.jstar;
+            const unsigned long long cnt = seg.cnt[s], rank = sc.rank[s];
+            ctl->c_R = ctl->c_R + (ctl->m - rank - cnt);
+            ctl->m = cnt;
+            ctl->aL = sc.pk[s]; ctl->S_L = sc.pv[s];
+            ctl->aR = sc.bk[s]; ctl->S_R = sc.bv[s];
+            ctl->jstar = s;
+            atomicOr(&ctl->flags, kFlagBigRoot);
+        } else {
+            if (!o.ok) atomicOr(&ctl->flags, kFlagInternal);
+            ctl->b = o.b;
+            ctl->jstar = o.jstar;
+            if (b_out) *b_out = o.b;
+        }
     }
 }
 
@@ -316,14 +333,21 @@ __global__ __launch_bounds__(kCurveThreads) void k_curve_tiles(const uint32_t* _
     if (threadIdx.x == 0) { seg.cnt[tile] = (uint32_t)c; seg.off[tile] = (uint32_t)base; }
 }
 
+// ctl_tails: the scores are a part of a larger set whose rest is summarised
+// in ctl as tails (aL, S_L below; aR, S_R and the count c_R above)
 __global__ __launch_bounds__(kCurveThreads) void k_curve_root(const uint32_t* __restrict__ keys, long long n, int ntiles,
                                                                Ctl* ctl, SegArrays seg, SolveScratch sc, double k,
-                                                               double t, double inv_t, double* b_out) {
+                                                               double t, double inv_t, double* b_out, int ctl_tails) {
     __shared__ float s_k[kCurveThreads];
     __shared__ double s_v[kCurveThreads];
     __shared__ int s_int[32];
     SegView sv{ntiles, seg.first, seg.last, seg.P, seg.Bx, seg.cnt, seg.off, keys, nullptr, nullptr, nullptr, nullptr};
     Tails tl{-INFINITY, INFINITY, 0.0, 0.0, (double)n, 0.0, k, t, inv_t};
+    if (ctl_tails) {
+        tl.aL = ctl->aL; tl.S_L = ctl->S_L;
+        tl.aR = ctl->aR; tl.S_R = ctl->S_R;
+        tl.c_R = (double)ctl->c_R;
+    }
     SolveOut o = segment_solve<kCurveThreads, kRadixItems>(sv, tl, sc, s_k, s_v, s_int);
     if (threadIdx.x == 0) {
         double b = o.b;
@@ -345,8 +369,9 @@ void launch_small_solve(const float* r, int n, double k, double t, Ctl* ctl, Sol
 }
 
 void launch_bucket_solve(uint32_t* bucket_vals, const uint32_t* bucket_cnt, int cap, int nb, Ctl* ctl, SegArrays seg,
-                         SolveScratch sc, double k, double t, double* b_out, hipStream_t s) {
-    hipLaunchKernelGGL(k_bucket_agg, dim3(nb), dim3(kAggThreads), 0, s, bucket_vals, bucket_cnt, cap, seg, 1.0 / t);
+                         SolveScratch sc, double k, double t, double* b_out, hipStream_t s, const uint32_t* hoff) {
+    hipLaunchKernelGGL(k_bucket_agg, dim3(nb), dim3(kAggThreads), 0, s, bucket_vals, bucket_cnt, cap, seg, 1.0 / t,
+                       hoff);
     hipLaunchKernelGGL(k_band_root, dim3(1), dim3(kSortThreads), 0, s, bucket_vals, nb, ctl, seg, sc, k, t, 1.0 / t,
                        b_out);
 }
@@ -375,11 +400,11 @@ void launch_radix_sort(const float* r, long long n, uint32_t* keysA, uint32_t* k
 }
 
 void launch_curve_tiles(const uint32_t* keys, long long n, Ctl* ctl, SegArrays seg, SolveScratch sc, double k,
-                        double t, double* b_out, hipStream_t s) {
+                        double t, double* b_out, hipStream_t s, bool ctl_tails) {
     const unsigned tiles = (unsigned)((n + kCurveTile - 1) / kCurveTile);
     hipLaunchKernelGGL(k_curve_tiles, dim3(tiles), dim3(kCurveThreads), 0, s, keys, n, seg, 1.0 / t);
     hipLaunchKernelGGL(k_curve_root, dim3(1), dim3(kCurveThreads), 0, s, keys, n, (int)tiles, ctl, seg, sc, k, t,
-                       1.0 / t, b_out);
+                       1.0 / t, b_out, ctl_tails ? 1 : 0);
 }
 
 }  // namespace lapsum

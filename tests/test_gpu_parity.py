@@ -203,9 +203,10 @@ def test_forced_fallback_and_widening(oracle_mod):
     p, b, st, _ = run(r, k, cfg.t, path=L.PATH_BRACKET, margin_scale=0.0)
     assert st["widenings"] >= 1
     check_forward(oracle_mod, r, k, cfg.t, p, b, b_ref=b_ref, label="widened")
-    # tiny buckets: overflow goes to the full sort
+    # tiny buckets: nearly every bucket overflows; their scores are collected
+    # by a second pass and the bracket is still solved (no full sort)
     p, b, st, _ = run(r, k, cfg.t, path=L.PATH_BRACKET, bucket_capacity=4)
-    assert st["path_taken"] == 3
+    assert st["path_taken"] == 2
     check_forward(oracle_mod, r, k, cfg.t, p, b, b_ref=b_ref, label="overflow")
 
 
@@ -256,3 +257,37 @@ def test_bracket_many_splitter_gaps(oracle_mod, frac):
     assert st["status"] == 0 and st["path_taken"] == 2, st["path_taken"]
     b_ref = check_forward(oracle_mod, r, k, 0.05, p, b, label=f"k={k}")
     check_vjp(oracle_mod, r, g, 0.05, b_ref, grad, label=f"k={k}")
+
+
+@pytest.mark.parametrize("copies,k", [(20_000, 20_000.0), (60_000, 10_000.0), (60_000, 90_000.0), (3_000, 5_000.0),
+                                      (60_000, None), (20_000, None)])
+def test_bracket_tie_cluster(oracle_mod, copies, k):
+    """A cluster of equal scores near the budget's quantile.  When the bracket
+    takes it in, it overflows its bucket; the bracket stays certified (the
+    filter's counts and sums are exact), the overflowed bucket's scores are
+    collected by a second pass, and when the root lies in a bucket too large
+    for LDS that bucket alone is sorted with the multi-workgroup sort.  k=None
+    puts the root inside the cluster (k = #above + copies/2), which forces
+    both.  Never a full-sort fallback."""
+    n = 2_000_000
+    rng = np.random.default_rng(copies + int(k or 1))
+    r = rng.standard_normal(n).astype(np.float32)
+    q = np.sort(r)[n - int(k or 50_000)]
+    idx = rng.choice(n, copies, replace=False)
+    r[idx] = q
+    inside = k is None
+    if inside:
+        # just under G(q): b lies above q by less than q's fp32 spacing, so the
+        # root interval starts at the cluster's last copy
+        k = oracle_mod.budget_G(r, t32(0.01), float(q)) - 1e-3
+    g = workloads.upstream(n, 79)
+    p, b, st, grad = run(r, k, 0.01, g, profile=1)
+    assert st["status"] == 0 and st["path_taken"] == 2, st
+    names = [nm for nm, _ in st["kernels"]]
+    if inside:
+        assert "heavy_collect" in names, names
+        if copies > 16384:
+            info = {key: st[key] for key in ("a_L", "a_R", "band_size", "count_above", "buckets", "b")}
+            assert "root_bucket_sort" in names, (names, info, float(q), k)
+    b_ref = check_forward(oracle_mod, r, k, 0.01, p, b, label=f"cluster {copies}")
+    check_vjp(oracle_mod, r, g, 0.01, b_ref, grad, label=f"cluster {copies}")
