@@ -34,6 +34,7 @@ constexpr int kFlagNonFinite = 1;
 constexpr int kFlagOverflow = 2;
 constexpr int kFlagInternal = 4;
 constexpr int kFlagBigRoot = 8;   // the root lies in a bucket too large for LDS (host sorts it)
+constexpr int kFlagCertified = 16;  // G(a_L) >= k > G(a_R) from the filter's sums
 constexpr uint32_t kNotHeavy = 0xFFFFFFFFu;  // bucket slot offset marker: not an overflowed bucket
 
 // ---------------------------------------------------------------------------
@@ -62,12 +63,17 @@ struct Ctl {
     unsigned int done[8];
     unsigned int tile_ctr[4];
     unsigned int pad1[4];
+    // 1 when the filter certified the bracket with every band score stored:
+    // the band solve and p pass launched right behind it then do their work
+    int32_t gate;
+    int32_t pad2;
 };
 
 // host-pinned summary written by the filter's last workgroup; the host polls seq
 struct HostSummary {
     unsigned long long c_L, m, c_R;
     double S_L, S_R, B_L, B_R;
+    double g_aL, g_aR;  // G at the bracket ends (the certification quantities)
     float aL, aR;
     int32_t flags;
     int32_t nb;

@@ -371,13 +371,13 @@ struct BracketResult {
 };
 
 // G(a_L), G(a_R) from the streaming pass's totals
-void certify(const HostSummary& h, double k, double t, BracketResult* res) {
-    const double m = (double)h.m, cR = (double)h.c_R;
-    const bool finL = std::isfinite(h.aL), finR = std::isfinite(h.aR);
-    const double cross = (finL && finR) ? std::exp(((double)h.aL - (double)h.aR) / t) : 0.0;
-    res->gL = finL ? 0.5 * h.S_L + m - 0.5 * h.B_L + cR - 0.5 * cross * h.S_R : (double)(h.c_L + h.m + h.c_R);
-    res->gR = finR ? 0.5 * cross * h.S_L + 0.5 * h.B_R + cR - 0.5 * h.S_R : 0.0;
-    res->certified = (res->gL >= k) && (res->gR < k);
+// The filter's finalize kernel forms G(a_L), G(a_R) from its sums and the
+// verdict; the host takes the device's verdict as it is, so that the kernels
+// launched behind the filter (which test the same verdict) and the host agree.
+void certify(const HostSummary& h, BracketResult* res) {
+    res->gL = h.g_aL;
+    res->gR = h.g_aR;
+    res->certified = (h.flags & kFlagCertified) != 0;
 }
 
 lapsum_status_t check_args(const float* r, int64_t n, double k, float t, const void* p, const void* b) {
@@ -497,8 +497,20 @@ lapsum_status_t forward_impl(const float* r, int64_t n, double k, float t_f, flo
         const unsigned int seq = ++w->seq;
         tm.begin("filter");
         launch_filter(r, n, t, w->ctl, w->sp, w->iw, w->bucket_cnt, w->bucket_vals, cap, w->part, nullptr,
-                      w->hs_dev, seq, st);
+                      w->hs_dev, seq, st, k);
         tm.end();
+        if (path != LAPSUM_PATH_FORCE_FALLBACK) {
+            // launched before the host has the verdict: they run only when the
+            // finalize kernel opened the gate (certified, every band score
+            // stored), so the device never waits for the host on this path
+            tm.begin("bucket_solve");
+            launch_bucket_solve(w->bucket_vals, w->bucket_cnt, cap, kMaxBuckets, w->ctl, w->seg, w->sc, k, t, b_out,
+                                st, nullptr, &w->ctl->gate);
+            tm.end();
+            tm.begin("probs");
+            w->probs_parts = launch_probs(r, n, t, p, w->ctl, w->part, st, &w->ctl->gate);
+            tm.end();
+        }
         if (hipGetLastError() != hipSuccess) return LAPSUM_ERR_HIP;
         lapsum_status_t ws = wait_summary(w, st, seq);
         if (ws != LAPSUM_OK) return ws;
@@ -506,7 +518,7 @@ lapsum_status_t forward_impl(const float* r, int64_t n, double k, float t_f, flo
         br.nonfinite = (br.h.flags & kFlagNonFinite) != 0;
         br.overflow = (br.h.flags & kFlagOverflow) != 0;
         if (br.nonfinite) break;
-        certify(br.h, k, t, &br);  // overflow leaves the counts and sums exact
+        certify(br.h, &br);  // overflow leaves the counts and sums exact
         if (br.certified || path == LAPSUM_PATH_FORCE_FALLBACK) break;
         if (widen >= opt.max_widen) break;
         // widen the failing side: double its distance from s q
@@ -545,6 +557,16 @@ lapsum_status_t forward_impl(const float* r, int64_t n, double k, float t_f, flo
         return LAPSUM_ERR_NONFINITE_INPUT;
     }
     bool fallback = !br.certified || path == LAPSUM_PATH_FORCE_FALLBACK;
+    if (!fallback && !br.overflow) {
+        // the gate was open: the band solve and p pass launched behind the filter did the work
+        if (stats) {
+            stats->path_taken = 2;
+            lapsum_status_t fs = fill_stats(w, st, n, stats);
+            tm.collect(stats);
+            return fs;
+        }
+        return LAPSUM_OK;
+    }
     long long max_heavy = 0;
     bool heavy = false;
     if (!fallback && br.overflow) {
@@ -652,7 +674,7 @@ lapsum_status_t order_stats_impl(Workspace* w, const float* r, long long n, long
             const unsigned int seq = ++w->seq;
             tm.begin("filter");
             launch_filter(r, n, 1.0, w->ctl, w->sp, w->iw, w->bucket_cnt, w->bucket_vals, cap, w->part, nullptr,
-                          w->hs_dev, seq, st);
+                          w->hs_dev, seq, st, (double)k);
             tm.end();
             if (hipGetLastError() != hipSuccess) return LAPSUM_ERR_HIP;
             lapsum_status_t ws = wait_summary(w, st, seq);
@@ -947,7 +969,7 @@ lapsum_status_t lapsum_test_filter(const float* scores, int64_t n, float t, floa
     launch_select(w->sample, 2, l, h, kBucketCapMax, w->ctl, w->sp, w->iw, w->bucket_cnt, st);
     const unsigned int seq = ++w->seq;
     launch_filter(scores, n, (double)t, w->ctl, w->sp, w->iw, w->bucket_cnt, w->bucket_vals, kBucketCapMax, w->part,
-                  nullptr, w->hs_dev, seq, st);
+                  nullptr, w->hs_dev, seq, st, 0.5 * (double)n);
     lapsum_status_t ws = wait_summary(w, st, seq);
     if (ws != LAPSUM_OK) return ws;
     HostSummary hsum = *const_cast<HostSummary*>(w->hs);

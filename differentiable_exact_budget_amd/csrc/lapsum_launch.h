@@ -22,11 +22,14 @@ void launch_select(const float* x, int s, long long l, long long h, int cap, Ctl
 
 // lapsum_stream.hip
 int stream_blocks(long long n);
+// k: the budget the finalize kernel certifies the bracket against
 void launch_filter(const float* r, long long n, double t, Ctl* ctl, const float* sp, const float* iw,
                    uint32_t* bucket_cnt, uint32_t* bucket_vals, int cap, double* part, unsigned long long* partc,
-                   HostSummary* hs_dev, unsigned int seq, hipStream_t st);
+                   HostSummary* hs_dev, unsigned int seq, hipStream_t st, double k);
 // returns the number of partials it left (for launch_sum_p)
-int launch_probs(const float* r, long long n, double t, float* p, Ctl* ctl, double* part, hipStream_t st);
+// gate (device, may be null): when it holds 0 the kernels return at once
+int launch_probs(const float* r, long long n, double t, float* p, Ctl* ctl, double* part, hipStream_t st,
+                 const int* gate = nullptr);
 void launch_sum_p(Ctl* ctl, const double* part, int nparts, hipStream_t st);
 // grad may be null (only the reduction and c); kt adds dL/dk, dL/dt (each output may be null)
 void launch_vjp(const float* r, const float* g, long long n, double t, const double* b, float* grad, Ctl* ctl,
@@ -63,7 +66,7 @@ void launch_small_solve(const float* r, int n, double k, double t, Ctl* ctl, Sol
 // hoff: null, or per bucket the slot offset of an overflowed bucket's scores (kNotHeavy otherwise)
 void launch_bucket_solve(uint32_t* bucket_vals, const uint32_t* bucket_cnt, int cap, int nb, Ctl* ctl, SegArrays seg,
                          SolveScratch sc, double k, double t, double* b_out, hipStream_t s,
-                         const uint32_t* hoff = nullptr);
+                         const uint32_t* hoff = nullptr, const int* gate = nullptr);
 int radix_hist_blocks(long long n);
 void launch_radix_sort(const float* r, long long n, uint32_t* keysA, uint32_t* keysB, uint32_t* hist_part,
                        uint32_t* goff, unsigned long long* status, uint32_t epoch_base, Ctl* ctl, hipStream_t s);

@@ -88,9 +88,10 @@ constexpr int kAggThreads = 256;
 // bucket_vals of the slot holding all of an overflowed bucket's scores
 __global__ __launch_bounds__(kAggThreads) void k_bucket_agg(const uint32_t* __restrict__ bucket_vals,
                                                              const uint32_t* bucket_cnt, int cap, SegArrays seg,
-                                                             double inv_t, const uint32_t* hoff) {
+                                                             double inv_t, const uint32_t* hoff, const int* gate) {
     __shared__ uint32_t s_kmin, s_kmax;
     __shared__ unsigned long long s_fx[2 * kAggThreads / 64];
+    if (gate && *gate == 0) return;  // launched ahead of a certification that failed
     const int tid = threadIdx.x;
     const int bkt = blockIdx.x;
     const uint32_t ho = hoff ? hoff[bkt] : kNotHeavy;
@@ -128,7 +129,8 @@ __global__ __launch_bounds__(kAggThreads) void k_bucket_agg(const uint32_t* __re
 
 __global__ __launch_bounds__(kSortThreads) void k_band_root(const uint32_t* bucket_vals, int nb, Ctl* ctl,
                                                              SegArrays seg, SolveScratch sc, double k, double t,
-                                                             double inv_t, double* b_out) {
+                                                             double inv_t, double* b_out, const int* gate) {
+    if (gate && *gate == 0) return;  // launched ahead of a certification that failed
     __shared__ uint32_t sortbuf[kBucketCapMax];
     __shared__ float s_k[kSortThreads];
     __shared__ double s_v[kSortThreads];
@@ -369,11 +371,12 @@ void launch_small_solve(const float* r, int n, double k, double t, Ctl* ctl, Sol
 }
 
 void launch_bucket_solve(uint32_t* bucket_vals, const uint32_t* bucket_cnt, int cap, int nb, Ctl* ctl, SegArrays seg,
-                         SolveScratch sc, double k, double t, double* b_out, hipStream_t s, const uint32_t* hoff) {
+                         SolveScratch sc, double k, double t, double* b_out, hipStream_t s, const uint32_t* hoff,
+                         const int* gate) {
     hipLaunchKernelGGL(k_bucket_agg, dim3(nb), dim3(kAggThreads), 0, s, bucket_vals, bucket_cnt, cap, seg, 1.0 / t,
-                       hoff);
+                       hoff, gate);
     hipLaunchKernelGGL(k_band_root, dim3(1), dim3(kSortThreads), 0, s, bucket_vals, nb, ctl, seg, sc, k, t, 1.0 / t,
-                       b_out);
+                       b_out, gate);
 }
 
 int radix_hist_blocks(long long n) {

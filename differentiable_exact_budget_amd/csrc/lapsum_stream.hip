@@ -269,9 +269,15 @@ __global__ __launch_bounds__(kStreamThreads) void k_filter(const float* __restri
 
 // one workgroup: totals of the filter's partials in a fixed order, band
 // statistics from the bucket counters, hand-off to the host
+// Also the certification: G at both bracket ends follows from the sums,
+//   G(a_L) = S_L/2 + m - B_L/2 + c_R - e^{(a_L - a_R)/t} S_R/2,
+//   G(a_R) = e^{(a_L - a_R)/t} S_L/2 + B_R/2 + c_R - S_R/2,
+// and the bracket holds iff G(a_L) >= k > G(a_R) (an open end holds); the
+// gate opens when it holds and every band score was stored.
 __global__ __launch_bounds__(kStreamThreads) void k_filter_finalize(const FilterPart* part, int nparts, long long n,
                                                                      Ctl* ctl, const uint32_t* bucket_cnt, int cap,
-                                                                     HostSummary* hs, unsigned int seq) {
+                                                                     HostSummary* hs, unsigned int seq, double k,
+                                                                     double t) {
     __shared__ double s_red[kStreamThreads / 64];
     __shared__ unsigned long long s_redu[kStreamThreads / 64];
     __shared__ unsigned int s_amax;
@@ -334,10 +340,18 @@ __global__ __launch_bounds__(kStreamThreads) void k_filter_finalize(const Filter
         const unsigned long long CL = (unsigned long long)n - M - CR - NAN_;
         ctl->S_L = T0; ctl->S_R = T1; ctl->B_L = T2; ctl->B_R = T3;
         ctl->c_L = CL; ctl->c_R = CR; ctl->m = M;
+        const float aLf = ctl->aL, aRf = ctl->aR;
+        const bool finL = finite_f(aLf), finR = finite_f(aRf);
+        const double cross = (finL && finR) ? exp(((double)aLf - (double)aRf) / t) : 0.0;
+        const double gL = finL ? 0.5 * T0 + (double)M - 0.5 * T2 + (double)CR - 0.5 * cross * T1 : (double)(CL + M + CR);
+        const double gR = finR ? 0.5 * cross * T0 + 0.5 * T3 + (double)CR - 0.5 * T1 : 0.0;
+        if (gL >= k && gR < k) flags |= kFlagCertified;
+        ctl->gate = (flags == kFlagCertified) ? 1 : 0;
         ctl->flags = flags;
         if (hs) {
             hs->c_L = CL; hs->m = M; hs->c_R = CR;
             hs->S_L = T0; hs->S_R = T1; hs->B_L = T2; hs->B_R = T3;
+            hs->g_aL = gL; hs->g_aR = gR;
             hs->aL = ctl->aL; hs->aR = ctl->aR;
             hs->flags = flags; hs->nb = nb; hs->max_bucket = s_mxb;
             __threadfence_system();
@@ -349,7 +363,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_filter_finalize(const Filter
 
 void launch_filter(const float* r, long long n, double t, Ctl* ctl, const float* sp, const float* iw,
                    uint32_t* bucket_cnt, uint32_t* bucket_vals, int cap, double* part, unsigned long long* /*partc*/,
-                   HostSummary* hs_dev, unsigned int seq, hipStream_t st) {
+                   HostSummary* hs_dev, unsigned int seq, hipStream_t st, double k) {
     const float ls = (float)(1.4426950408889634 / t);
     FilterPart* fp = reinterpret_cast<FilterPart*>(part);
     const bool vec = (reinterpret_cast<uintptr_t>(r) & 15u) == 0u;
@@ -361,7 +375,7 @@ void launch_filter(const float* r, long long n, double t, Ctl* ctl, const float*
         hipLaunchKernelGGL(k_filter<false>, dim3(blocks), dim3(kStreamThreads), 0, st, r, n, ls, ctl, sp, iw,
                            bucket_cnt, bucket_vals, cap, fp);
     hipLaunchKernelGGL(k_filter_finalize, dim3(1), dim3(kStreamThreads), 0, st, fp, blocks, n, ctl, bucket_cnt, cap,
-                       hs_dev, seq);
+                       hs_dev, seq, k, t);
 }
 
 // ---------------------------------------------------------------------------
@@ -374,8 +388,10 @@ LS_DEV float lap_cdf_f(float x) {
 
 template <bool VEC>
 __global__ __launch_bounds__(kStreamThreads) void k_probs(const float* __restrict__ r, long long n, double inv_t,
-                                                           float* __restrict__ p, const Ctl* ctl, double* part, int rev) {
+                                                           float* __restrict__ p, const Ctl* ctl, double* part, int rev,
+                                                           const int* gate) {
     __shared__ double s_red[kStreamThreads / 64];
+    if (gate && *gate == 0) return;  // launched ahead of a certification that failed
     const double b = ctl->b;
     const int tid = threadIdx.x;
     double sum = 0.0;
@@ -413,14 +429,16 @@ void launch_sum_p(Ctl* ctl, const double* part, int nparts, hipStream_t st) {
     hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(1024), 0, st, part, nparts, &ctl->sum_p);
 }
 
-int launch_probs(const float* r, long long n, double t, float* p, Ctl* ctl, double* part, hipStream_t st) {
+int launch_probs(const float* r, long long n, double t, float* p, Ctl* ctl, double* part, hipStream_t st,
+                 const int* gate) {
     const bool vec = ((reinterpret_cast<uintptr_t>(r) | reinterpret_cast<uintptr_t>(p)) & 15u) == 0u;
     const int blocks = vec ? tiled_grid<kProbsV>(n >> 2, kProbsGrid) : stream_blocks(n);
     if (vec)
         hipLaunchKernelGGL(k_probs<true>, dim3(blocks), dim3(kStreamThreads), 0, st, r, n, 1.0 / t, p, ctl, part,
-                           kProbsReverse);
+                           kProbsReverse, gate);
     else
-        hipLaunchKernelGGL(k_probs<false>, dim3(blocks), dim3(kStreamThreads), 0, st, r, n, 1.0 / t, p, ctl, part, 0);
+        hipLaunchKernelGGL(k_probs<false>, dim3(blocks), dim3(kStreamThreads), 0, st, r, n, 1.0 / t, p, ctl, part, 0,
+                           gate);
     return blocks;
 }
 
