@@ -179,6 +179,8 @@ lapsum_status_t alloc_ws(Workspace* w, long long n_cap) {
     // the control block (tickets, counters) and the look-back words start at zero
     if (hipMemsetAsync(w->ctl, 0, sizeof(Ctl), w->stream) != hipSuccess) return LAPSUM_ERR_HIP;
     if (hipMemsetAsync(w->status, 0, w->status_bytes, w->stream) != hipSuccess) return LAPSUM_ERR_HIP;
+    // the radix sort's global digit totals start (and are left) at zero
+    if (hipMemsetAsync(w->hist_part, 0, sizeof(uint32_t) * 1025, w->stream) != hipSuccess) return LAPSUM_ERR_HIP;
     return LAPSUM_OK;
 }
 

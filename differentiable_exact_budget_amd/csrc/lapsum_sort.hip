@@ -166,51 +166,82 @@ __global__ __launch_bounds__(kSortThreads) void k_band_root(const uint32_t* buck
 // "Single-pass parallel prefix scan with decoupled look-back", and Adinets
 // & Merrill, "Onesweep", 2022)
 // ---------------------------------------------------------------------------
+// Digit histograms of all four LSD passes in one read.  Per workgroup in LDS:
+// the lanes of a wave that share a digit are found with ballots and one of
+// them adds their count (many keys share the high digits; plain per-lane
+// atomics on one LDS word would serialise).  The workgroup totals then go
+// into the global totals with integer atomics (order-free: deterministic).
+// hist: global uint32[1025] (four 256-bin histograms, then a non-finite
+// flag), all zero on entry; k_radix_offsets reads and re-zeroes it.
 __global__ __launch_bounds__(kRadixThreads) void k_radix_hist(const float* __restrict__ r, long long n,
-                                                               uint32_t* __restrict__ hist_part, uint32_t* goff,
-                                                               Ctl* ctl) {
+                                                               uint32_t* __restrict__ hist) {
     __shared__ uint32_t h[4 * 256];
-    __shared__ int s_last;
     __shared__ int s_bad;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = lane_id();
     for (int i = tid; i < 1024; i += kRadixThreads) h[i] = 0u;
     if (tid == 0) s_bad = 0;
     __syncthreads();
     int bad = 0;
-    const long long stride = (long long)gridDim.x * kRadixThreads;
-    for (long long i = (long long)blockIdx.x * kRadixThreads + tid; i < n; i += stride) {
-        const float v = r[i];
-        bad |= !finite_f(v);
+    // whole-wave call: valid marks the lanes that hold a key
+    auto add = [&](float v, bool valid) {
+        bad |= valid && !finite_f(v);
         const uint32_t key = f2key(v);
-        atomicAdd(&h[key & 0xFFu], 1u);
-        atomicAdd(&h[256 + ((key >> 8) & 0xFFu)], 1u);
-        atomicAdd(&h[512 + ((key >> 16) & 0xFFu)], 1u);
-        atomicAdd(&h[768 + (key >> 24)], 1u);
+        const unsigned long long act = ballot(valid);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t d = (key >> (8 * p)) & 0xFFu;
+            const unsigned long long peers = match_digit8(d, act);
+            if (valid && lane == __ffsll((long long)peers) - 1) atomicAdd(&h[p * 256 + d], (uint32_t)popc64(peers));
+        }
+    };
+    const long long stride = (long long)gridDim.x * kRadixThreads;
+    if ((reinterpret_cast<uintptr_t>(r) & 15u) == 0u) {
+        const long long n4 = n >> 2;
+        const float4* r4 = reinterpret_cast<const float4*>(r);
+        for (long long base = (long long)blockIdx.x * kRadixThreads; base < n4; base += stride) {
+            const long long i = base + tid;
+            const bool valid = i < n4;
+            const float4 v = valid ? r4[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            add(v.x, valid); add(v.y, valid); add(v.z, valid); add(v.w, valid);
+        }
+        if (blockIdx.x == 0 && tid < 64) {  // the last n % 4 keys, one wave
+            const long long j = (n4 << 2) + tid;
+            const bool valid = tid < 4 && j < n;
+            add(valid ? r[j] : 0.0f, valid);
+        }
+    } else {
+        for (long long base = (long long)blockIdx.x * kRadixThreads; base < n; base += stride) {
+            const long long i = base + tid;
+            const bool valid = i < n;
+            add(valid ? r[i] : 0.0f, valid);
+        }
     }
     if (bad) atomicOr(&s_bad, 1);
     __syncthreads();
-    for (int i = tid; i < 1024; i += kRadixThreads) hist_part[(size_t)blockIdx.x * kHistStride + i] = h[i];
-    if (tid == 0) hist_part[(size_t)blockIdx.x * kHistStride + 1024] = (uint32_t)s_bad;
-    if (!last_block_ticket(&ctl->done[kDoneHist], &s_last)) return;
-    // last workgroup: totals (fixed order) and exclusive digit offsets
-    for (int i = tid; i < 1024; i += kRadixThreads) {
-        uint32_t s = 0u;
-        for (unsigned b = 0; b < gridDim.x; ++b) s += hist_part[(size_t)b * kHistStride + i];
-        h[i] = s;
-    }
-    if (tid == 0) {
-        uint32_t anybad = 0u;
-        for (unsigned b = 0; b < gridDim.x; ++b) anybad |= hist_part[(size_t)b * kHistStride + 1024];
-        ctl->flags = anybad ? kFlagNonFinite : 0;
-    }
+    for (int i = tid; i < 1024; i += kRadixThreads)
+        if (h[i]) atomicAdd(&hist[i], h[i]);
+    if (tid == 0 && s_bad) atomicOr(&hist[1024], 1u);
+}
+
+// exclusive digit offsets of the four passes from the global totals; the
+// totals are re-zeroed for the next sort
+__global__ __launch_bounds__(256) void k_radix_offsets(uint32_t* hist, uint32_t* goff, Ctl* ctl) {
+    __shared__ uint32_t scr[256 / 64 + 2];
+    const int tid = threadIdx.x;
+    uint32_t x[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) x[p] = hist[p * 256 + tid];
+    const uint32_t bad = hist[1024];
     __syncthreads();
-    if (tid < 4) {
-        uint32_t acc = 0u;
-        for (int d = 0; d < 256; ++d) { const uint32_t x = h[tid * 256 + d]; goff[tid * 256 + d] = acc; acc += x; }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        goff[p * 256 + tid] = block_exclusive_scan<256>(x[p], nullptr, scr);
+        hist[p * 256 + tid] = 0u;
     }
     if (tid == 0) {
+        hist[1024] = 0u;
+        ctl->flags = bad ? kFlagNonFinite : 0;
         for (int p = 0; p < 4; ++p) ctl->tile_ctr[p] = 0u;
-        ctl->done[kDoneHist] = 0u;
     }
 }
 
@@ -380,7 +411,7 @@ void launch_bucket_solve(uint32_t* bucket_vals, const uint32_t* bucket_cnt, int 
 }
 
 int radix_hist_blocks(long long n) {
-    long long b = (n + 16LL * kRadixThreads - 1) / (16LL * kRadixThreads);
+    long long b = (n + 16LL * kRadixThreads - 1) / (16LL * kRadixThreads);  // >= 16 keys per thread
     if (b < 1) b = 1;
     if (b > kRadixHistBlocks) b = kRadixHistBlocks;
     return (int)b;
@@ -389,7 +420,8 @@ int radix_hist_blocks(long long n) {
 void launch_radix_sort(const float* r, long long n, uint32_t* keysA, uint32_t* keysB, uint32_t* hist_part,
                        uint32_t* goff, unsigned long long* status, uint32_t epoch_base, Ctl* ctl, hipStream_t s) {
     const int hb = radix_hist_blocks(n);
-    hipLaunchKernelGGL(k_radix_hist, dim3(hb), dim3(kRadixThreads), 0, s, r, n, hist_part, goff, ctl);
+    hipLaunchKernelGGL(k_radix_hist, dim3(hb), dim3(kRadixThreads), 0, s, r, n, hist_part);
+    hipLaunchKernelGGL(k_radix_offsets, dim3(1), dim3(256), 0, s, hist_part, goff, ctl);
     const unsigned tiles = (unsigned)((n + kRadixTile - 1) / kRadixTile);
     const uint32_t* src = reinterpret_cast<const uint32_t*>(r);
     uint32_t* dst = keysA;
