@@ -74,6 +74,7 @@ struct Workspace {
     unsigned long long* status = nullptr;
     size_t status_bytes = 0;
     uint32_t epoch = 1;
+    bool status_dirty = false;  // the status region holds split-pass data
     std::vector<hipEvent_t> events;
 };
 
@@ -341,13 +342,24 @@ lapsum_status_t wait_summary(Workspace* w, hipStream_t st, unsigned int seq) {
 }
 
 uint32_t next_epoch(Workspace* w, hipStream_t st) {
-    if (w->epoch + 8u >= (1u << 30)) {
+    if (w->epoch + 8u >= (1u << 30) || w->status_dirty) {
         (void)hipMemsetAsync(w->status, 0, w->status_bytes, st);
         w->epoch = 1;
+        w->status_dirty = false;
     }
     uint32_t e = w->epoch;
     w->epoch += 4;
     return e;
+}
+
+// Radix sort of n fp32 scores (keys end in keysB).  The one-kernel passes
+// read epoch-tagged status words; the split passes leave counts and offsets
+// in the same region, which must not pass for status words: the region is
+// cleared before the next sort that reads it.
+void sort_keys(Workspace* w, const float* r, long long n, hipStream_t st) {
+    const uint32_t epoch = next_epoch(w, st);
+    launch_radix_sort(r, n, w->keysA, w->keysB, w->hist_part, w->goff, w->status, epoch, w->ctl, st);
+    if (!radix_uses_onesweep(n)) w->status_dirty = true;
 }
 
 void run_full(Workspace* w, const float* r, long long n, double k, double t, double* b_out, hipStream_t st, Timer& tm) {
@@ -357,9 +369,8 @@ void run_full(Workspace* w, const float* r, long long n, double k, double t, dou
         tm.end();
         return;
     }
-    const uint32_t epoch = next_epoch(w, st);
     tm.begin("radix_sort");
-    launch_radix_sort(r, n, w->keysA, w->keysB, w->hist_part, w->goff, w->status, epoch, w->ctl, st);
+    sort_keys(w, r, n, st);
     tm.end();
     tm.begin("curve_solve");
     launch_curve_tiles(w->keysB, n, w->ctl, w->seg, w->sc, k, t, b_out, st);
@@ -596,9 +607,7 @@ lapsum_status_t forward_impl(const float* r, int64_t n, double k, float t_f, flo
                 const unsigned long long cnt = c.m;
                 const float* src = reinterpret_cast<const float*>(w->bucket_vals + w->hoff_h[bkt]);
                 tm.begin("root_bucket_sort");
-                const uint32_t epoch = next_epoch(w, st);
-                launch_radix_sort(src, (long long)cnt, w->keysA, w->keysB, w->hist_part, w->goff, w->status, epoch,
-                                  w->ctl, st);
+                sort_keys(w, src, (long long)cnt, st);
                 tm.end();
                 tm.begin("root_bucket_solve");
                 launch_curve_tiles(w->keysB, (long long)cnt, w->ctl, w->seg, w->sc, k, t, b_out, st, true);
@@ -644,8 +653,7 @@ lapsum_status_t order_stats_impl(Workspace* w, const float* r, long long n, long
             tm.end();
         } else {
             tm.begin("radix_sort");
-            const uint32_t epoch = next_epoch(w, st);
-            launch_radix_sort(r, n, w->keysA, w->keysB, w->hist_part, w->goff, w->status, epoch, w->ctl, st);
+            sort_keys(w, r, n, st);
             tm.end();
         }
         tm.begin("pick");
@@ -914,8 +922,7 @@ lapsum_status_t lapsum_test_sort(const float* scores, int64_t n, float* out, lap
     if (n <= kSmallMax) {
         launch_small_solve(scores, (int)n, k, 1.0, w->ctl, w->sc, nullptr, w->keysB, st);
     } else {
-        const uint32_t epoch = next_epoch(w, st);
-        launch_radix_sort(scores, n, w->keysA, w->keysB, w->hist_part, w->goff, w->status, epoch, w->ctl, st);
+        sort_keys(w, scores, n, st);
     }
     if (hipStreamSynchronize(st) != hipSuccess) return LAPSUM_ERR_HIP;
     std::vector<uint32_t> keys((size_t)n);

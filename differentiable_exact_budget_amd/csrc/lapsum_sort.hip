@@ -245,6 +245,11 @@ __global__ __launch_bounds__(256) void k_radix_offsets(uint32_t* hist, uint32_t*
     }
 }
 
+// One LSD pass in one kernel (onesweep): each tile takes its digit offsets
+// from its predecessors' published counts (decoupled look-back).  Fastest
+// when the tiles are few; the look-back chain runs through status words that
+// cross the XCDs' separate L2 caches, so for many tiles the split form below
+// wins.
 constexpr unsigned long long kStAgg = 1ull, kStInc = 2ull;
 
 LS_DEV unsigned long long st_pack(uint32_t epoch, unsigned long long flag, uint32_t v) {
@@ -351,6 +356,149 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_pass(const uint32_t* __
     }
 }
 
+// One LSD pass as count, scan, scatter (no tile waits on another; for many
+// tiles a second read of the tile costs less than the look-back chain).
+//   k_radix_count    per tile (4096 keys): its 256 digit counts, written
+//                    digit-major: counts[d * T + tile]
+//   k_radix_scan     per digit, over the tiles: tile_base[d * T + tile] =
+//                    the digit's global offset + the counts of earlier tiles
+//   k_radix_scatter  per tile: stable ranks (wave-level multisplit), a local
+//                    scatter into LDS in digit order, coalesced runs to global
+LS_DEV uint32_t radix_key(const uint32_t* in, int in_is_float, long long idx) {
+    return in_is_float ? f2key(__uint_as_float(in[idx])) : in[idx];
+}
+
+__global__ __launch_bounds__(kRadixThreads) void k_radix_count(const uint32_t* __restrict__ in, int in_is_float,
+                                                                long long n, int pass, uint32_t* __restrict__ counts,
+                                                                long long T) {
+    constexpr int NW = kRadixThreads / 64;
+    __shared__ uint32_t cnt[256 * NW];
+    const int tid = threadIdx.x, w = tid >> 6, lane = lane_id();
+    const int shift = 8 * pass;
+    const long long tile = blockIdx.x;
+    const long long base = tile * kRadixTile;
+    for (int e = tid; e < 256 * NW; e += kRadixThreads) cnt[e] = 0u;
+    __syncthreads();
+    uint32_t kr[kRadixItems];
+#pragma unroll
+    for (int i = 0; i < kRadixItems; ++i) {
+        const long long idx = base + (long long)((w * kRadixItems + i) * 64 + lane);
+        kr[i] = idx < n ? radix_key(in, in_is_float, idx) : 0u;
+    }
+    volatile uint32_t* vc = cnt;  // successive leader lanes update one word: keep the wave's order
+#pragma unroll
+    for (int i = 0; i < kRadixItems; ++i) {
+        const long long idx = base + (long long)((w * kRadixItems + i) * 64 + lane);
+        const bool valid = idx < n;
+        const unsigned long long act = ballot(valid);
+        if (act != 0ull) {
+            const uint32_t d = (kr[i] >> shift) & 0xFFu;
+            const unsigned long long peers = match_digit8(d, act);
+            if (valid && lane == 63 - __clzll(peers)) vc[d * NW + w] = vc[d * NW + w] + (uint32_t)popc64(peers);
+        }
+    }
+    __syncthreads();
+    uint32_t tot = 0u;
+#pragma unroll
+    for (int q = 0; q < NW; ++q) tot += cnt[tid * NW + q];
+    counts[(size_t)tid * (size_t)T + (size_t)tile] = tot;  // kRadixThreads == 256: thread = digit
+}
+
+// one workgroup per digit: exclusive scan of its counts over the tiles
+__global__ __launch_bounds__(1024) void k_radix_scan(const uint32_t* __restrict__ counts, long long T, int pass,
+                                                      const uint32_t* __restrict__ goff,
+                                                      uint32_t* __restrict__ tile_base) {
+    constexpr int IT = 8;
+    __shared__ uint32_t scr[1024 / 64 + 2];
+    const int d = blockIdx.x, tid = threadIdx.x;
+    const uint32_t* col = counts + (size_t)d * (size_t)T;
+    uint32_t* out = tile_base + (size_t)d * (size_t)T;
+    uint32_t carry = goff[pass * 256 + d];
+    for (long long c0 = 0; c0 < T; c0 += 1024LL * IT) {
+        uint32_t v[IT];
+        uint32_t sum = 0u;
+#pragma unroll
+        for (int q = 0; q < IT; ++q) {
+            const long long t = c0 + (long long)tid * IT + q;
+            v[q] = t < T ? col[t] : 0u;
+            sum += v[q];
+        }
+        uint32_t total = 0u;
+        uint32_t ex = block_exclusive_scan<1024>(sum, &total, scr) + carry;
+#pragma unroll
+        for (int q = 0; q < IT; ++q) {
+            const long long t = c0 + (long long)tid * IT + q;
+            if (t < T) out[t] = ex;
+            ex += v[q];
+        }
+        carry += total;
+    }
+}
+
+__global__ __launch_bounds__(kRadixThreads) void k_radix_scatter(const uint32_t* __restrict__ in, int in_is_float,
+                                                                  uint32_t* __restrict__ out, long long n, int pass,
+                                                                  const uint32_t* __restrict__ tile_base, long long T) {
+    constexpr int NW = kRadixThreads / 64;
+    __shared__ uint32_t cnt[256 * NW];
+    __shared__ uint32_t stage[kRadixTile];
+    __shared__ uint32_t loc[256];
+    __shared__ uint32_t gbase[256];
+    __shared__ uint32_t scr[NW + 2];
+    const int tid = threadIdx.x, w = tid >> 6, lane = lane_id();
+    const int shift = 8 * pass;
+    const long long tile = blockIdx.x;
+    const long long base = tile * kRadixTile;
+    for (int e = tid; e < 256 * NW; e += kRadixThreads) cnt[e] = 0u;
+    gbase[tid] = tile_base[(size_t)tid * (size_t)T + (size_t)tile];
+    __syncthreads();
+    uint32_t kr[kRadixItems];
+    uint32_t rk[kRadixItems];
+#pragma unroll
+    for (int i = 0; i < kRadixItems; ++i) {
+        const long long idx = base + (long long)((w * kRadixItems + i) * 64 + lane);
+        kr[i] = idx < n ? radix_key(in, in_is_float, idx) : 0u;
+    }
+    volatile uint32_t* vc = cnt;
+#pragma unroll
+    for (int i = 0; i < kRadixItems; ++i) {
+        const long long idx = base + (long long)((w * kRadixItems + i) * 64 + lane);
+        const bool valid = idx < n;
+        const unsigned long long act = ballot(valid);
+        rk[i] = 0u;
+        if (act != 0ull) {
+            const uint32_t d = (kr[i] >> shift) & 0xFFu;
+            const unsigned long long peers = match_digit8(d, act);
+            const uint32_t b0 = vc[d * NW + w];
+            rk[i] = b0 + (uint32_t)mbcnt(peers);
+            if (valid && lane == 63 - __clzll(peers)) vc[d * NW + w] = b0 + (uint32_t)popc64(peers);
+        }
+    }
+    __syncthreads();
+    // thread d: per-wave exclusive offsets and the tile's exclusive digit offsets
+    const int d = tid;  // kRadixThreads == 256
+    uint32_t tot = 0u;
+#pragma unroll
+    for (int q = 0; q < NW; ++q) { const uint32_t x = cnt[d * NW + q]; cnt[d * NW + q] = tot; tot += x; }
+    loc[d] = block_exclusive_scan<kRadixThreads>(tot, nullptr, scr);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kRadixItems; ++i) {
+        const long long idx = base + (long long)((w * kRadixItems + i) * 64 + lane);
+        if (idx < n) {
+            const uint32_t dd = (kr[i] >> shift) & 0xFFu;
+            stage[loc[dd] + cnt[dd * NW + w] + rk[i]] = kr[i];
+        }
+    }
+    __syncthreads();
+    const long long rem = n - base;
+    const int tcount = rem < kRadixTile ? (int)rem : kRadixTile;
+    for (int j = tid; j < tcount; j += kRadixThreads) {
+        const uint32_t key = stage[j];
+        const uint32_t dd = (key >> shift) & 0xFFu;
+        out[(size_t)gbase[dd] + (size_t)(j - (int)loc[dd])] = key;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // curve aggregates of the fully sorted scores, then the solve
 // ---------------------------------------------------------------------------
@@ -417,17 +565,34 @@ int radix_hist_blocks(long long n) {
     return (int)b;
 }
 
+constexpr long long kOnesweepMaxTiles = 512;  // up to ~2M keys: one kernel per pass
+
+bool radix_uses_onesweep(long long n) { return (n + kRadixTile - 1) / kRadixTile <= kOnesweepMaxTiles; }
+
 void launch_radix_sort(const float* r, long long n, uint32_t* keysA, uint32_t* keysB, uint32_t* hist_part,
                        uint32_t* goff, unsigned long long* status, uint32_t epoch_base, Ctl* ctl, hipStream_t s) {
     const int hb = radix_hist_blocks(n);
     hipLaunchKernelGGL(k_radix_hist, dim3(hb), dim3(kRadixThreads), 0, s, r, n, hist_part);
     hipLaunchKernelGGL(k_radix_offsets, dim3(1), dim3(256), 0, s, hist_part, goff, ctl);
-    const unsigned tiles = (unsigned)((n + kRadixTile - 1) / kRadixTile);
+    const long long T = (n + kRadixTile - 1) / kRadixTile;
+    // the status region holds 256 * T words of 8 bytes: look-back status words,
+    // or (split form) the tile counts followed by the tile bases
+    uint32_t* counts = reinterpret_cast<uint32_t*>(status);
+    uint32_t* tile_base = counts + (size_t)256 * (size_t)T;
     const uint32_t* src = reinterpret_cast<const uint32_t*>(r);
     uint32_t* dst = keysA;
     for (int p = 0; p < 4; ++p) {
-        hipLaunchKernelGGL(k_radix_pass, dim3(tiles), dim3(kRadixThreads), 0, s, src, p == 0 ? 1 : 0, dst, n, p,
-                           status, epoch_base + (uint32_t)p, goff, ctl);
+        const int is_float = p == 0 ? 1 : 0;
+        if (T <= kOnesweepMaxTiles) {
+            hipLaunchKernelGGL(k_radix_pass, dim3((unsigned)T), dim3(kRadixThreads), 0, s, src, is_float, dst, n, p,
+                               status, epoch_base + (uint32_t)p, goff, ctl);
+        } else {
+            hipLaunchKernelGGL(k_radix_count, dim3((unsigned)T), dim3(kRadixThreads), 0, s, src, is_float, n, p,
+                               counts, T);
+            hipLaunchKernelGGL(k_radix_scan, dim3(256), dim3(1024), 0, s, counts, T, p, goff, tile_base);
+            hipLaunchKernelGGL(k_radix_scatter, dim3((unsigned)T), dim3(kRadixThreads), 0, s, src, is_float, dst, n,
+                               p, tile_base, T);
+        }
         src = dst;
         dst = (dst == keysA) ? keysB : keysA;
     }

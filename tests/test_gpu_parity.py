@@ -76,6 +76,20 @@ def test_sort_bit_exact(oracle_mod, n):
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
 
 
+def test_sort_forms_alternate(oracle_mod):
+    """Large inputs take the split radix passes (counts, scan, scatter), small
+    ones the one-kernel passes with look-back; the split passes leave data in
+    the region the look-back reads, which must be cleared in between.  Sorts of
+    both kinds, alternating on one workspace, all bit-exact."""
+    for n in (2_500_001, 300_001, 4_000_000, 65_537):
+        r = np.random.default_rng(n).standard_normal(n).astype(np.float32)
+        r[::5] = r[2]
+        out = torch.empty(n, dtype=torch.float32, device="cuda")
+        assert L.lib().lapsum_test_sort(to_dev(r).data_ptr(), n, out.data_ptr(), None) == 0
+        got = out.cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), oracle_mod.sort_keys(r).view(np.uint32)), n
+
+
 @pytest.mark.parametrize("n,dist", [(16385, "normal"), (200_000, "student_t3"), (1_000_000, "normal")])
 def test_full_sort_path(oracle_mod, n, dist):
     r = workloads.scores(dist, n, 7 + n)
