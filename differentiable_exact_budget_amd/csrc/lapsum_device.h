@@ -174,6 +174,57 @@ LS_DEV uint32_t block_exclusive_scan(uint32_t v, uint32_t* total, uint32_t* scra
     return res;
 }
 
+// Several workgroup reductions behind one barrier: ND double sums, NU uint64
+// sums and NM uint32 maxima.  Wave butterflies first, then every thread adds
+// the waves' results in wave order, so all threads get the same totals in a
+// fixed order.  Scratch: sd >= ND*NT/64, su >= NU*NT/64, sm >= NM*NT/64; it
+// must not be written again before another barrier.
+template <int NT, int ND, int NU, int NM>
+LS_DEV void block_reduce_multi(double (&d)[ND], unsigned long long (&u)[NU], uint32_t (&m)[NM], double* sd,
+                               unsigned long long* su, uint32_t* sm) {
+    constexpr int NW = NT / 64;
+    const int w = threadIdx.x >> 6, l = lane_id();
+#pragma unroll
+    for (int i = 0; i < ND; ++i) d[i] = wave_sum(d[i]);
+#pragma unroll
+    for (int i = 0; i < NU; ++i) u[i] = wave_sum_u64(u[i]);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) m[i] = max(m[i], (uint32_t)__shfl_xor((int)m[i], o, 64));
+    }
+    if (l == 0) {
+#pragma unroll
+        for (int i = 0; i < ND; ++i) sd[i * NW + w] = d[i];
+#pragma unroll
+        for (int i = 0; i < NU; ++i) su[i * NW + w] = u[i];
+#pragma unroll
+        for (int i = 0; i < NM; ++i) sm[i * NW + w] = m[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < ND; ++i) {
+        double a = sd[i * NW];
+#pragma unroll
+        for (int x = 1; x < NW; ++x) a += sd[i * NW + x];
+        d[i] = a;
+    }
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+        unsigned long long a = su[i * NW];
+#pragma unroll
+        for (int x = 1; x < NW; ++x) a += su[i * NW + x];
+        u[i] = a;
+    }
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+        uint32_t a = sm[i * NW];
+#pragma unroll
+        for (int x = 1; x < NW; ++x) a = max(a, sm[i * NW + x]);
+        m[i] = a;
+    }
+}
+
 // block sum of double in a fixed order (wave butterflies, then wave 0); the
 // result is valid in wave 0 only (broadcast it through LDS where others need it)
 template <int NT>

@@ -36,7 +36,7 @@ int stream_blocks(long long n) {
 
 struct FilterPart {
     double S[4];               // S_L, S_R, B_L, B_R
-    unsigned long long c[2];   // below, above
+    unsigned long long c[2];   // NaNs, count at/above a_R
     float mn, mx;              // smallest and largest score seen
     int nan;                   // a NaN was seen
     int pad;
@@ -46,9 +46,9 @@ constexpr int kQueueCap = 2048;  // band scores a workgroup holds in LDS before 
 constexpr int kQueuePerWave = kQueueCap / (kStreamThreads / 64);  // each wave appends to its own slice
 
 // Launch shapes of the tiled passes (tile = kStreamThreads * V float4).  The
-// filter ends every workgroup with an LDS queue flush and six reductions, so
-// a bounded number of workgroups walk the tiles; the light passes run one
-// tile per workgroup up to the partials' capacity.
+// filter ends every workgroup with an LDS queue flush and a reduction, so a
+// bounded number of workgroups walk the tiles; the light passes run one tile
+// per workgroup up to the partials' capacity.
 constexpr int kFilterV = 4, kFilterGrid = 1536;
 constexpr int kProbsV = 2, kProbsGrid = kMaxStreamParts;
 constexpr int kReduceV = 4, kReduceGrid = 8192;
@@ -118,9 +118,9 @@ __global__ __launch_bounds__(kStreamThreads) void k_filter(const float* __restri
     __shared__ uint32_t lcnt[kMaxBuckets];
     __shared__ uint32_t gbase[kMaxBuckets];
     __shared__ uint32_t s_wq[kStreamThreads / 64];
-    __shared__ double s_red[kStreamThreads / 64];
-    __shared__ unsigned long long s_redu[kStreamThreads / 64];
-    __shared__ int s_nan;
+    __shared__ double s_rd[4 * (kStreamThreads / 64)];
+    __shared__ unsigned long long s_ru[2 * (kStreamThreads / 64)];
+    __shared__ uint32_t s_rm[2 * (kStreamThreads / 64)];
     const int tid = threadIdx.x;
     const int lane = lane_id();
     FilterState fs;
@@ -130,7 +130,6 @@ __global__ __launch_bounds__(kStreamThreads) void k_filter(const float* __restri
     for (int i = tid; i <= fs.ng; i += kStreamThreads) sp[i] = sp_g[i];
     for (int i = tid; i < fs.ng; i += kStreamThreads) iw[i] = iw_g[i];
     for (int i = tid; i < nb; i += kStreamThreads) lcnt[i] = 0u;
-    if (tid == 0) s_nan = 0;
     fs.sp = sp; fs.iw = iw; fs.bucket_cnt = bucket_cnt; fs.bucket_vals = bucket_vals;
     __syncthreads();
 
@@ -212,58 +211,78 @@ __global__ __launch_bounds__(kStreamThreads) void k_filter(const float* __restri
     }
 
     // ---- flush the LDS queue: bucket by value, one global atomic per bucket ----
+    // The wave slices, concatenated, are the workgroup's queue; its item i
+    // goes to thread i mod NT, so the usual handful of band scores takes a
+    // single pass (one bucket search) instead of one per slice position.
+    constexpr int NWV = kStreamThreads / 64;
     if (lane == 0) s_wq[tid >> 6] = min(wfill, (uint32_t)kQueuePerWave);
     __syncthreads();
+    uint32_t qoff[NWV + 1];
+    qoff[0] = 0u;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) qoff[w + 1] = qoff[w] + s_wq[w];
+    const uint32_t qn = qoff[NWV];
     constexpr int QPT = kQueueCap / kStreamThreads;
     int bk[QPT];
     uint32_t rk[QPT];
+    float qv[QPT];
 #pragma unroll
     for (int k = 0; k < QPT; ++k) {
-        const uint32_t i = (uint32_t)tid + (uint32_t)k * kStreamThreads;
         bk[k] = -1;
-        if (i % (uint32_t)kQueuePerWave < s_wq[i / (uint32_t)kQueuePerWave]) {
-            const float v = q[i];
-            if (v != v) { nan = 1; ++nnan; continue; }
-            band_sums(fs, v, BL, BR);
-            bk[k] = band_bucket(fs, v);
-            rk[k] = atomicAdd(&lcnt[bk[k]], 1u);
+        const uint32_t i = (uint32_t)tid + (uint32_t)k * kStreamThreads;
+        if (i < qn) {
+            int w = 0;
+#pragma unroll
+            for (int x = 1; x < NWV; ++x) w += i >= qoff[x] ? 1 : 0;
+            const float v = q[w * kQueuePerWave + (i - qoff[w])];
+            qv[k] = v;
+            if (v != v) {
+                nan = 1;
+                ++nnan;
+            } else {
+                band_sums(fs, v, BL, BR);
+                bk[k] = band_bucket(fs, v);
+                rk[k] = atomicAdd(&lcnt[bk[k]], 1u);
+            }
         }
     }
     __syncthreads();
-    for (int j = tid; j < nb; j += kStreamThreads) {
-        const uint32_t c = lcnt[j];
-        gbase[j] = c ? atomicAdd(&bucket_cnt[j], c) : 0u;
+    // a thread's (up to kMaxBuckets / NT) returning atomics are all in flight
+    // before any result is used: one round trip, not one per bucket
+    constexpr int BPT = kMaxBuckets / kStreamThreads;
+    uint32_t got[BPT];
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+        const int j = tid + u * kStreamThreads;
+        const uint32_t c = j < nb ? lcnt[j] : 0u;
+        got[u] = c ? atomicAdd(&bucket_cnt[j], c) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+        const int j = tid + u * kStreamThreads;
+        if (j < nb) gbase[j] = got[u];
     }
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < QPT; ++k) {
         if (bk[k] >= 0) {
-            const uint32_t i = (uint32_t)tid + (uint32_t)k * kStreamThreads;
             const uint32_t pos = gbase[bk[k]] + rk[k];
-            if (pos < (uint32_t)cap) bucket_vals[(size_t)bk[k] * (size_t)cap + pos] = __float_as_uint(q[i]);
+            if (pos < (uint32_t)cap) bucket_vals[(size_t)bk[k] * (size_t)cap + pos] = __float_as_uint(qv[k]);
         }
     }
 
     // ---- workgroup partials (fixed-order reduction; reduced by k_filter_finalize) ----
-    const double tS0 = block_sum<kStreamThreads>(SL, s_red);
-    const double tS1 = block_sum<kStreamThreads>(SR, s_red);
-    const double tS2 = block_sum<kStreamThreads>(BL, s_red);
-    const double tS3 = block_sum<kStreamThreads>(BR, s_red);
-    const unsigned long long tcR = block_sum_u64<kStreamThreads>((unsigned long long)cR, s_redu);
-    const unsigned long long tnan = block_sum_u64<kStreamThreads>((unsigned long long)nnan, s_redu);
-    if (nan) atomicOr(&s_nan, 1);
-    __shared__ float s_amax;
-    if (tid == 0) s_amax = 0.0f;
-    __syncthreads();
-    atomicMax(reinterpret_cast<unsigned int*>(&s_amax), __float_as_uint(amax));  // |v| >= 0: uint order = float order
-    __syncthreads();
+    double d[4] = {SL, SR, BL, BR};
+    unsigned long long u[2] = {(unsigned long long)nnan, (unsigned long long)cR};
+    uint32_t m[2] = {__float_as_uint(amax), (uint32_t)nan};  // |v| >= 0: uint order = float order
+    block_reduce_multi<kStreamThreads>(d, u, m, s_rd, s_ru, s_rm);
     if (tid == 0) {
         FilterPart& fp = part[blockIdx.x];
-        fp.S[0] = tS0; fp.S[1] = tS1; fp.S[2] = tS2; fp.S[3] = tS3;
-        fp.c[0] = tnan; fp.c[1] = tcR;
+        fp.S[0] = d[0]; fp.S[1] = d[1]; fp.S[2] = d[2]; fp.S[3] = d[3];
+        fp.c[0] = u[0]; fp.c[1] = u[1];
         fp.mn = 0.0f;
-        fp.mx = s_amax;
-        fp.nan = s_nan;
+        fp.mx = __uint_as_float(m[0]);
+        fp.nan = (int)m[1];
     }
 }
 
@@ -278,14 +297,10 @@ __global__ __launch_bounds__(kStreamThreads) void k_filter_finalize(const Filter
                                                                      Ctl* ctl, const uint32_t* bucket_cnt, int cap,
                                                                      HostSummary* hs, unsigned int seq, double k,
                                                                      double t) {
-    __shared__ double s_red[kStreamThreads / 64];
-    __shared__ unsigned long long s_redu[kStreamThreads / 64];
-    __shared__ unsigned int s_amax;
-    __shared__ int s_nan;
-    __shared__ unsigned long long s_mxb;
+    __shared__ double s_rd[4 * (kStreamThreads / 64)];
+    __shared__ unsigned long long s_ru[3 * (kStreamThreads / 64)];
+    __shared__ uint32_t s_rm[3 * (kStreamThreads / 64)];
     const int tid = threadIdx.x;
-    if (tid == 0) { s_amax = 0u; s_nan = 0; s_mxb = 0ull; }
-    __syncthreads();
     // every load first (one memory round trip), then combine in a fixed order
     constexpr int PP = kMaxStreamBlocks / kStreamThreads;
     FilterPart fp[PP];
@@ -294,7 +309,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_filter_finalize(const Filter
         const int b = tid + q * kStreamThreads;
         if (b < nparts) fp[q] = part[b];
     }
-    // bucket counts: a thread sums its buckets, the maximum goes to s_mxb
+    // bucket counts: a thread sums its buckets and keeps their maximum
     const int nbk = ctl->nb;
     constexpr int BQ = kMaxBuckets / kStreamThreads;
     uint32_t bcv[BQ];
@@ -321,22 +336,17 @@ __global__ __launch_bounds__(kStreamThreads) void k_filter_finalize(const Filter
             amx = fmaxf(amx, fp[q].mx);
         }
     }
-    if (anynan) atomicOr(&s_nan, 1);
-    atomicMax(&s_amax, __float_as_uint(amx));
-    const double T0 = block_sum<kStreamThreads>(a0, s_red);
-    const double T1 = block_sum<kStreamThreads>(a1, s_red);
-    const double T2 = block_sum<kStreamThreads>(a2, s_red);
-    const double T3 = block_sum<kStreamThreads>(a3, s_red);
-    const unsigned long long NAN_ = block_sum_u64<kStreamThreads>(u0, s_redu);
-    const unsigned long long CR = block_sum_u64<kStreamThreads>(u1, s_redu);
+    double d[4] = {a0, a1, a2, a3};
+    unsigned long long u[3] = {u0, u1, bc};
+    uint32_t mx[3] = {__float_as_uint(amx), (uint32_t)anynan, bmx};  // |v| >= 0: uint order = float order
+    block_reduce_multi<kStreamThreads>(d, u, mx, s_rd, s_ru, s_rm);
+    const double T0 = d[0], T1 = d[1], T2 = d[2], T3 = d[3];
+    const unsigned long long NAN_ = u[0], CR = u[1], M = u[2];
     const int nb = ctl->nb;
-    const unsigned long long M = block_sum_u64<kStreamThreads>(bc, s_redu);
-    atomicMax(&s_mxb, (unsigned long long)bmx);
-    __syncthreads();
     if (tid == 0) {
         int flags = 0;
-        if (s_nan || !finite_f(__uint_as_float(s_amax))) flags |= kFlagNonFinite;
-        if (s_mxb > (unsigned long long)cap) flags |= kFlagOverflow;
+        if (mx[1] || !finite_f(__uint_as_float(mx[0]))) flags |= kFlagNonFinite;
+        if (mx[2] > (uint32_t)cap) flags |= kFlagOverflow;
         const unsigned long long CL = (unsigned long long)n - M - CR - NAN_;
         ctl->S_L = T0; ctl->S_R = T1; ctl->B_L = T2; ctl->B_R = T3;
         ctl->c_L = CL; ctl->c_R = CR; ctl->m = M;
@@ -353,7 +363,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_filter_finalize(const Filter
             hs->S_L = T0; hs->S_R = T1; hs->B_L = T2; hs->B_R = T3;
             hs->g_aL = gL; hs->g_aR = gR;
             hs->aL = ctl->aL; hs->aR = ctl->aR;
-            hs->flags = flags; hs->nb = nb; hs->max_bucket = s_mxb;
+            hs->flags = flags; hs->nb = nb; hs->max_bucket = mx[2];
             __threadfence_system();
             hs->seq = seq;
             __threadfence_system();
