@@ -309,6 +309,58 @@ LS_DEV void wave_scan_bwd_excl(float& k, double& v, double inv_t) {
     k = ek; v = ev;
 }
 
+// Exclusive scans of one segment per thread in the additive frame, all
+// behind one barrier: forward sums of the score counts and of U, the
+// running maximum of the segments' last scores, and backward sums of W with
+// the running minimum of their first scores.  Wave scans first, then each
+// thread adds the totals of the waves before (after) its own, in wave order.
+// Scratch: sr, sU, sW, sl, sf >= NT/64 entries each.  Ends with a barrier.
+struct BandScan {
+    uint32_t rank;
+    double U, W;
+    float last, first;
+};
+template <int NT>
+LS_DEV BandScan block_scan_band(uint32_t rc, double U, float lastk, double W, float firstk, uint32_t* sr, double* sU,
+                                double* sW, float* sl, float* sf) {
+    constexpr int NW = NT / 64;
+    const int lane = lane_id(), w = threadIdx.x >> 6;
+    uint32_t ir = rc;
+    double iU = U, iW = W;
+    float il = lastk, iF = firstk;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t a = __shfl_up(ir, o, 64);
+        const double b = __shfl_up(iU, o, 64);
+        const float c = __shfl_up(il, o, 64);
+        const double d = __shfl_down(iW, o, 64);
+        const float e = __shfl_down(iF, o, 64);
+        if (lane >= o) { ir += a; iU += b; il = fmaxf(il, c); }
+        if (lane + o < 64) { iW += d; iF = fminf(iF, e); }
+    }
+    if (lane == 63) { sr[w] = ir; sU[w] = iU; sl[w] = il; }
+    if (lane == 0) { sW[w] = iW; sf[w] = iF; }
+    uint32_t er = __shfl_up(ir, 1, 64);
+    double eU = __shfl_up(iU, 1, 64), eW = __shfl_down(iW, 1, 64);
+    float el = __shfl_up(il, 1, 64), eF = __shfl_down(iF, 1, 64);
+    if (lane == 0) { er = 0u; eU = 0.0; el = -INFINITY; }
+    if (lane == 63) { eW = 0.0; eF = INFINITY; }
+    __syncthreads();
+    uint32_t pr = 0u;
+    double pU = 0.0, pW = 0.0;
+    float pl = -INFINITY, pF = INFINITY;
+    for (int x = 0; x < w; ++x) { pr += sr[x]; pU += sU[x]; pl = fmaxf(pl, sl[x]); }
+    for (int x = NW - 1; x > w; --x) { pW += sW[x]; pF = fminf(pF, sf[x]); }
+    __syncthreads();
+    BandScan r;
+    r.rank = pr + er;
+    r.U = pU + eU;
+    r.W = pW + eW;
+    r.last = fmaxf(pl, el);
+    r.first = fminf(pF, eF);
+    return r;
+}
+
 // Runs on all NT threads of one workgroup; result valid in thread 0.
 // Memory round trips are kept to a handful: each lane of wave 0 fetches its
 // segments' aggregates in one batch, the root segment's scores are read
@@ -353,15 +405,48 @@ __device__ __attribute__((always_inline)) SolveOut segment_solve(const SegView s
             if (sv.cnt[s]) { float k2 = sv.first[s]; double v2 = 1.0 + sv.Bx[s]; bwd_combine(k2, v2, bk, bvv, inv_t); bk = k2; bvv = v2; }
         }
     }
-    uint32_t rbase = block_exclusive_scan<NT>(rc, nullptr, reinterpret_cast<uint32_t*>(s_int));
-    block_scan_fwd_excl<NT>(ak, av, s_k, s_v, inv_t);
-    {   // the lower tail precedes everything
-        float tk = -INFINITY; double tv = 0.0;
-        if (tl.S_L > 0.0 && tl.aL > -INFINITY) { tk = tl.aL; tv = tl.S_L; }
-        fwd_combine(tk, tv, ak, av, inv_t);
+    // Additive frame: with both bracket ends finite and at most 600 t apart,
+    // every band score v has u = e^{(v - a_L)/t} in [1, e^600], so the
+    // carries are plain prefix sums of U = sum u and W = sum 1/u per segment
+    // (no exponential on the scan chain); a carry is then put back in the
+    // (nearest score, sum) form with one exponential.
+    const bool additive = per == 1 && tl.aL > -INFINITY && tl.aR < INFINITY &&
+                          ((double)tl.aR - (double)tl.aL) * inv_t <= 600.0;
+    uint32_t rbase;
+    if (additive) {
+        const double ref = (double)tl.aL;
+        double U = 0.0, W = 0.0;
+        float lastk = -INFINITY, firstk = INFINITY;
+        if (c1) {
+            U = av * exp(((double)ak - ref) * inv_t);
+            W = (1.0 + Bx1) * exp((ref - (double)f1) * inv_t);
+            lastk = ak;
+            firstk = f1;
+        }
+        const BandScan bs = block_scan_band<NT>(rc, U, lastk, W, firstk, reinterpret_cast<uint32_t*>(s_int), s_v,
+                                                s_v + NT / 64, s_k, s_k + NT / 64);
+        rbase = bs.rank;
+        // the lower tail: sum over v < a_L of e^{(v - a_L)/t} = S_L; the upper
+        // tail: sum over v >= a_R of e^{(a_L - v)/t} = e^{(a_L - a_R)/t} S_R
+        const double Ub = tl.S_L + bs.U;
+        const double Wa = (tl.S_R > 0.0 ? tl.S_R * exp((ref - (double)tl.aR) * inv_t) : 0.0) + bs.W;
+        if (bs.last > -INFINITY) { ak = bs.last; av = Ub * exp((ref - (double)ak) * inv_t); }
+        else if (tl.S_L > 0.0) { ak = tl.aL; av = tl.S_L; }
+        else { ak = -INFINITY; av = 0.0; }
+        if (bs.first < INFINITY) { bk = bs.first; bvv = Wa * exp(((double)bk - ref) * inv_t); }
+        else if (tl.S_R > 0.0) { bk = tl.aR; bvv = tl.S_R; }
+        else { bk = INFINITY; bvv = 0.0; }
+    } else {
+        rbase = block_exclusive_scan<NT>(rc, nullptr, reinterpret_cast<uint32_t*>(s_int));
+        block_scan_fwd_excl<NT>(ak, av, s_k, s_v, inv_t);
+        {   // the lower tail precedes everything
+            float tk = -INFINITY; double tv = 0.0;
+            if (tl.S_L > 0.0 && tl.aL > -INFINITY) { tk = tl.aL; tv = tl.S_L; }
+            fwd_combine(tk, tv, ak, av, inv_t);
+        }
+        block_scan_bwd_excl<NT>(bk, bvv, s_k, s_v, inv_t);
+        if (tl.S_R > 0.0 && tl.aR < INFINITY) bwd_combine(bk, bvv, tl.aR, tl.S_R, inv_t);
     }
-    block_scan_bwd_excl<NT>(bk, bvv, s_k, s_v, inv_t);
-    if (tl.S_R > 0.0 && tl.aR < INFINITY) bwd_combine(bk, bvv, tl.aR, tl.S_R, inv_t);
     int cand = -1;
     auto g_at_first = [&](int s, float f, double Bx, float pk, double pv, float nk, double nv, uint32_t rank) {
         const double Pf = 1.0 + (pv != 0.0 ? ecoef(((double)pk - (double)f) * inv_t) * pv : 0.0);

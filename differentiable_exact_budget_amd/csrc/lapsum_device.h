@@ -3,6 +3,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 
 namespace lapsum {
 
@@ -130,15 +131,77 @@ LS_DEV unsigned long long match_digit8(uint32_t d, unsigned long long active) {
     return m;
 }
 
+// The value of lane (lane XOR D) for D = 1 .. 32 with data-parallel
+// primitives instead of an LDS permute: DPP quad permutations (D = 1, 2),
+// row shifts into alternate 4-lane banks (D = 4), a row rotation (D = 8),
+// and the gfx950 row-pair / half-wave swaps (D = 16, 32).  All 64 lanes must
+// be active.
+template <int D>
+LS_DEV uint32_t xor_lane(uint32_t x) {
+    static_assert(D == 1 || D == 2 || D == 4 || D == 8 || D == 16 || D == 32, "lane distance");
+    if constexpr (D == 1) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+    } else if constexpr (D == 2) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+    } else if constexpr (D == 4) {
+        const int y = __builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xA, false);  // row_shr:4 -> banks 1, 3
+        return (uint32_t)__builtin_amdgcn_update_dpp(y, (int)x, 0x104, 0xF, 0x5, false);  // row_shl:4 -> banks 0, 2
+    } else if constexpr (D == 8) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, false);  // row_ror:8
+    } else if constexpr (D == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        return ((__lane_id() >> 4) & 1) ? r[0] : r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return ((__lane_id() >> 5) & 1) ? r[0] : r[1];
+    }
+}
+template <int D>
+LS_DEV unsigned long long xor_lane64(unsigned long long x) {
+    return ((unsigned long long)xor_lane<D>((uint32_t)(x >> 32)) << 32) | xor_lane<D>((uint32_t)x);
+}
+template <int D>
+LS_DEV double xor_lane_f64(double x) {
+    return __longlong_as_double((long long)xor_lane64<D>((unsigned long long)__double_as_longlong(x)));
+}
+// run-time lane distance (a power of two, 1 .. 32, wave-uniform)
+LS_DEV uint32_t xor_lane_rt(uint32_t x, int d) {
+    switch (d) {
+        case 1: return xor_lane<1>(x);
+        case 2: return xor_lane<2>(x);
+        case 4: return xor_lane<4>(x);
+        case 8: return xor_lane<8>(x);
+        case 16: return xor_lane<16>(x);
+        default: return xor_lane<32>(x);
+    }
+}
+
 // fixed-order butterfly sums over the wave
 LS_DEV double wave_sum(double v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    v += xor_lane_f64<32>(v);
+    v += xor_lane_f64<16>(v);
+    v += xor_lane_f64<8>(v);
+    v += xor_lane_f64<4>(v);
+    v += xor_lane_f64<2>(v);
+    v += xor_lane_f64<1>(v);
     return v;
 }
 LS_DEV unsigned long long wave_sum_u64(unsigned long long v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    v += xor_lane64<32>(v);
+    v += xor_lane64<16>(v);
+    v += xor_lane64<8>(v);
+    v += xor_lane64<4>(v);
+    v += xor_lane64<2>(v);
+    v += xor_lane64<1>(v);
+    return v;
+}
+LS_DEV uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, xor_lane<32>(v));
+    v = max(v, xor_lane<16>(v));
+    v = max(v, xor_lane<8>(v));
+    v = max(v, xor_lane<4>(v));
+    v = max(v, xor_lane<2>(v));
+    v = max(v, xor_lane<1>(v));
     return v;
 }
 
@@ -189,10 +252,7 @@ LS_DEV void block_reduce_multi(double (&d)[ND], unsigned long long (&u)[NU], uin
 #pragma unroll
     for (int i = 0; i < NU; ++i) u[i] = wave_sum_u64(u[i]);
 #pragma unroll
-    for (int i = 0; i < NM; ++i) {
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) m[i] = max(m[i], (uint32_t)__shfl_xor((int)m[i], o, 64));
-    }
+    for (int i = 0; i < NM; ++i) m[i] = wave_max_u32(m[i]);
     if (l == 0) {
 #pragma unroll
         for (int i = 0; i < ND; ++i) sd[i * NW + w] = d[i];
@@ -276,26 +336,42 @@ LS_DEV void bitonic_sort_lds(uint32_t* a, int N) {
     }
 }
 
-// Ascending bitonic sort of N = NT * IPT keys (a power of two) held in LDS.
+constexpr int ilog2_c(int v) { return v <= 1 ? 0 : 1 + ilog2_c(v >> 1); }
+
+// Ascending bitonic sort of N = NA * IPT keys (a power of two) held in LDS,
+// called by all NT threads of the workgroup; the first NA (whole waves) sort.
 // Thread t keeps keys t*IPT .. t*IPT + IPT - 1 in registers: compare-exchanges
-// at strides < IPT stay in registers, strides < 64 * IPT go through wave
-// shuffles, and only wider strides go through LDS (consecutive LDS stages
-// are done between one store and one reload).  With NT = 64 one wave sorts
-// alone (no barrier).  The caller synchronises before reading the result.
-template <int NT, int IPT>
+// at strides < IPT stay in registers, strides < 64 * IPT go through lane
+// exchanges inside the wave (DPP and lane swaps), and only wider strides go
+// through LDS (consecutive LDS stages are done between one store and one
+// reload).  With NT = 64 one wave sorts alone (no barrier).  The caller
+// synchronises before reading the result.
+template <int NT, int NA, int IPT>
 LS_DEV void bitonic_sort_hybrid(uint32_t* lds) {
-    constexpr int N = NT * IPT;
+    constexpr int N = NA * IPT;
+    constexpr int LOGN = ilog2_c(N), LOGI = ilog2_c(IPT), LOGW = ilog2_c(64 * IPT);
+    static_assert((1 << LOGN) == N && (1 << LOGI) == IPT, "powers of two");
+    static_assert(NA % 64 == 0 && NA <= NT, "whole waves");
     const int tid = threadIdx.x;
+    const bool act = tid < NA;  // wave-uniform
     uint32_t x[IPT];
 #pragma unroll
-    for (int q = 0; q < IPT; ++q) x[q] = lds[tid * IPT + q];
-    for (int size = 2; size <= N; size <<= 1) {
-        int half = size >> 1;
-        if (half >= 64 * IPT) {
+    for (int q = 0; q < IPT; ++q) x[q] = act ? lds[tid * IPT + q] : 0u;
+    // every loop below has a compile-time trip count and is unrolled, so each
+    // stage's lane distance is a constant and picks its exchange statically
 #pragma unroll
-            for (int q = 0; q < IPT; ++q) lds[tid * IPT + q] = x[q];
+    for (int ls = 1; ls <= LOGN; ++ls) {
+        const int size = 1 << ls;
+        int lh = ls - 1;
+        if (lh >= LOGW) {
+            if (act) {
+#pragma unroll
+                for (int q = 0; q < IPT; ++q) lds[tid * IPT + q] = x[q];
+            }
             __syncthreads();
-            for (; half >= 64 * IPT; half >>= 1) {
+#pragma unroll
+            for (; lh >= LOGW; --lh) {
+                const int half = 1 << lh;
                 for (int t = tid; t < (N >> 1); t += NT) {
                     const int i = ((t & ~(half - 1)) << 1) | (t & (half - 1));
                     const int j = i + half;
@@ -305,23 +381,30 @@ LS_DEV void bitonic_sort_hybrid(uint32_t* lds) {
                 }
                 __syncthreads();
             }
+            if (act) {
 #pragma unroll
-            for (int q = 0; q < IPT; ++q) x[q] = lds[tid * IPT + q];
+                for (int q = 0; q < IPT; ++q) x[q] = lds[tid * IPT + q];
+            }
             __syncthreads();
         }
-        for (; half >= IPT; half >>= 1) {
-            const int lx = half / IPT;  // partner lane distance
+        if (!act) continue;  // idle waves only take part in the barriers
+#pragma unroll
+        for (; lh >= LOGI; --lh) {
+            const int half = 1 << lh;
+            const int lx = 1 << (lh - LOGI);  // partner lane distance
 #pragma unroll
             for (int q = 0; q < IPT; ++q) {
                 const int i = tid * IPT + q;
-                const uint32_t y = (uint32_t)__shfl_xor((int)x[q], lx, 64);
+                const uint32_t y = xor_lane_rt(x[q], lx);
                 const bool up = (i & size) == 0;
                 const bool lower = (i & half) == 0;
                 const uint32_t mn = x[q] < y ? x[q] : y, mx = x[q] < y ? y : x[q];
                 x[q] = (lower == up) ? mn : mx;
             }
         }
-        for (; half >= 1; half >>= 1) {
+#pragma unroll
+        for (; lh >= 0; --lh) {
+            const int half = 1 << lh;
 #pragma unroll
             for (int q = 0; q < IPT; ++q) {
                 if ((q & half) == 0 && (q | half) < IPT) {
@@ -333,22 +416,35 @@ LS_DEV void bitonic_sort_hybrid(uint32_t* lds) {
             }
         }
     }
+    if (act) {
 #pragma unroll
-    for (int q = 0; q < IPT; ++q) lds[tid * IPT + q] = x[q];
+        for (int q = 0; q < IPT; ++q) lds[tid * IPT + q] = x[q];
+    }
 }
 
 // Ascending sort of the first N keys of lds (N a power of two, N >= 64) by
-// all NT threads; ends with a barrier.  The choice follows measurements on
-// gfx950 with NT = 1024: the hybrid sort wins for NT <= N <= 4 NT, the plain
-// LDS bitonic sort below that (one wave alone is slower: its shuffle stages
-// run back to back) and above it (the hybrid's register blocks then
-// conflict in LDS).
+// all NT threads; ends with a barrier.  Up to 4 NT keys: the hybrid sort on
+// min(N, NT) threads (measured on gfx950 with NT = 1024: more threads beat
+// more keys per thread, and the hybrid beats the plain LDS sort at every
+// size); larger N: the plain LDS bitonic sort.
+template <int NT, int NA>
+LS_DEV bool sort_pow2_hybrid(uint32_t* lds, int N) {
+    if (N == NA) {
+        bitonic_sort_hybrid<NT, NA, 1>(lds);
+        return true;
+    }
+    if constexpr (NA < NT) return sort_pow2_hybrid<NT, 2 * NA>(lds, N);
+    return false;
+}
 template <int NT>
 LS_DEV void sort_pow2_lds(uint32_t* lds, int N) {
-    if (N == NT) { bitonic_sort_hybrid<NT, 1>(lds); __syncthreads(); }
-    else if (N == 2 * NT) { bitonic_sort_hybrid<NT, 2>(lds); __syncthreads(); }
-    else if (N == 4 * NT) { bitonic_sort_hybrid<NT, 4>(lds); __syncthreads(); }
-    else bitonic_sort_lds<NT>(lds, N);
+    if (N == 2 * NT) bitonic_sort_hybrid<NT, NT, 2>(lds);
+    else if (N == 4 * NT) bitonic_sort_hybrid<NT, NT, 4>(lds);
+    else if (!sort_pow2_hybrid<NT, 64>(lds, N)) {
+        bitonic_sort_lds<NT>(lds, N);
+        return;
+    }
+    __syncthreads();
 }
 
 LS_DEV int next_pow2(int x) {
@@ -429,13 +525,19 @@ template <int NT>
 LS_DEV Fx128 block_sum_fx(Fx128 v, unsigned long long* s /* >= 2 * NT/64 */) {
     constexpr int NW = NT / 64;
     const int w = threadIdx.x >> 6, l = lane_id();
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
+    auto step = [&](auto d_tag) {
+        constexpr int D = decltype(d_tag)::value;
         Fx128 y;
-        y.lo = __shfl_xor(v.lo, o, 64);
-        y.hi = __shfl_xor(v.hi, o, 64);
+        y.lo = xor_lane64<D>(v.lo);
+        y.hi = xor_lane64<D>(v.hi);
         v = fx_add(v, y);
-    }
+    };
+    step(std::integral_constant<int, 32>());
+    step(std::integral_constant<int, 16>());
+    step(std::integral_constant<int, 8>());
+    step(std::integral_constant<int, 4>());
+    step(std::integral_constant<int, 2>());
+    step(std::integral_constant<int, 1>());
     if (l == 0) { s[2 * w] = v.lo; s[2 * w + 1] = v.hi; }
     __syncthreads();
     Fx128 r = fx_zero();
