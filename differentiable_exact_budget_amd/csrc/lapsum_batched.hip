@@ -36,14 +36,22 @@ __global__ __launch_bounds__(NT) void k_rows_forward(const float* __restrict__ r
     if (tid == 0) s_bad = !(k > 0.0 && k < (double)n);
     __syncthreads();
     int bad = 0;
-    for (int i = tid; i < n; i += NT) {
-        const float v = rr[i];
-        bad |= !finite_f(v);
-        keys[i] = f2key(v);
+    // up to 4 keys per thread the bitonic sort (padded with the largest key)
+    // beats the radix sort
+    const int np = n <= 4 * NT ? max(next_pow2(n), 64) : n;
+    for (int i = tid; i < np; i += NT) {
+        if (i < n) {
+            const float v = rr[i];
+            bad |= !finite_f(v);
+            keys[i] = f2key(v);
+        } else {
+            keys[i] = 0xFFFFFFFFu;
+        }
     }
     if (bad) atomicOr(&s_bad, 1);
     __syncthreads();
-    block_sort_lds<NT, ITEMS>(keys, n, cnt, scr);
+    if (n <= 4 * NT) sort_pow2_lds<NT>(keys, np);
+    else block_sort_lds<NT, ITEMS>(keys, n, cnt, scr);
     segment_aggregates<NT>(keys, n, inv_t, &sg_first, &sg_last, &sg_P, &sg_Bx, s_red);
     if (tid == 0) { sg_cnt = (uint32_t)n; sg_off = 0u; }
     __syncthreads();

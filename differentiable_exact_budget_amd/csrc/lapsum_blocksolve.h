@@ -48,20 +48,25 @@ __device__ void block_sort_lds(uint32_t* keys, int m, uint32_t* cnt, uint32_t* s
     uint32_t kr[ITEMS];
     uint32_t rk[ITEMS];
     volatile uint32_t* vc = cnt;
+    // each wave ranks a contiguous run of rpw rows of 64 keys: spreading the
+    // rows over all waves keeps each wave's serial chain of counter updates
+    // short when m is small
+    const int rows = (m + 63) >> 6;
+    const int rpw = (rows + NW - 1) / NW;  // <= ITEMS
     for (int pass = 0; pass < 4; ++pass) {
         const int shift = 8 * pass;
         if (((diff >> shift) & 0xFFu) == 0u) continue;
 #pragma unroll
         for (int i = 0; i < ITEMS; ++i) {
-            const int idx = (w * ITEMS + i) * 64 + lane;
-            kr[i] = idx < m ? keys[idx] : 0u;
+            const int idx = (w * rpw + i) * 64 + lane;
+            kr[i] = (i < rpw && idx < m) ? keys[idx] : 0u;
         }
         for (int e = tid; e < 256 * NW; e += NT) cnt[e] = 0u;
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < ITEMS; ++i) {
-            const int idx = (w * ITEMS + i) * 64 + lane;
-            const bool valid = idx < m;
+            const int idx = (w * rpw + i) * 64 + lane;
+            const bool valid = i < rpw && idx < m;
             const unsigned long long act = ballot(valid);
             rk[i] = 0u;
             if (act != 0ull) {  // wave-uniform
@@ -87,8 +92,8 @@ __device__ void block_sort_lds(uint32_t* keys, int m, uint32_t* cnt, uint32_t* s
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < ITEMS; ++i) {
-            const int idx = (w * ITEMS + i) * 64 + lane;
-            if (idx < m) {
+            const int idx = (w * rpw + i) * 64 + lane;
+            if (i < rpw && idx < m) {
                 const uint32_t d = (kr[i] >> shift) & 0xFFu;
                 keys[cnt[d * NW + w] + rk[i]] = kr[i];
             }

@@ -44,14 +44,22 @@ __global__ __launch_bounds__(kSortThreads) void k_small_solve(const float* __res
     if (tid == 0) s_bad = 0;
     __syncthreads();
     int bad = 0;
-    for (int i = tid; i < n; i += kSortThreads) {
-        const float v = r[i];
-        bad |= !finite_f(v);
-        keys[i] = f2key(v);
+    // up to 4 keys per thread the bitonic sort (padded with the largest key,
+    // which sorts to the end) is the faster of the two LDS sorts
+    const int np = n <= 4 * kSortThreads ? max(next_pow2(n), 64) : n;
+    for (int i = tid; i < np; i += kSortThreads) {
+        if (i < n) {
+            const float v = r[i];
+            bad |= !finite_f(v);
+            keys[i] = f2key(v);
+        } else {
+            keys[i] = 0xFFFFFFFFu;
+        }
     }
     if (bad) atomicOr(&s_bad, 1);
     __syncthreads();
-    block_sort_lds<kSortThreads, kSortItems>(keys, n, cnt, scr);
+    if (n <= 4 * kSortThreads) sort_pow2_lds<kSortThreads>(keys, np);
+    else block_sort_lds<kSortThreads, kSortItems>(keys, n, cnt, scr);
     if (keys_out)
         for (int i = tid; i < n; i += kSortThreads) keys_out[i] = keys[i];
     segment_aggregates<kSortThreads>(keys, n, inv_t, &sg_first, &sg_last, &sg_P, &sg_Bx, s_red);
