@@ -314,55 +314,209 @@ LS_DEV void wave_scan_bwd_excl(float& k, double& v, double inv_t) {
     k = ek; v = ev;
 }
 
-// Exclusive scans of one segment per thread in the additive frame, all
-// behind one barrier: forward sums of the score counts and of U, the
-// running maximum of the segments' last scores, and backward sums of W with
-// the running minimum of their first scores.  Wave scans first, then each
-// thread adds the totals of the waves before (after) its own, in wave order.
-// Scratch: sr, sU, sW, sl, sf >= NT/64 entries each.  Ends with a barrier.
-struct BandScan {
-    uint32_t rank;
-    double U, W;
-    float last, first;
+// Carries of one segment per thread.  A carry (K, V) stands for a sum over
+// a set of scores v: forward, V = sum e^{(v - K)/t}; backward,
+// V = sum e^{(K - v)/t}.  A wave works in an additive frame when its
+// segments span at most 600 t: with ref its smallest score, every
+// u = e^{(v - ref)/t} lies in [1, e^600], so its carries are plain prefix
+// and suffix sums of U = sum u and W = sum 1/u (key ref, no exponential on
+// the scan chain), and the carries from the other waves and the tails are
+// put in the same frame.  When the whole band [a_L, a_R) spans at most
+// 600 t (global frame), every wave uses ref = a_L and the waves' totals add
+// up without exponentials too.  A wider wave scans (K, V) pairs with the
+// exponential combine.  Keys rise with the segment index, so every combine
+// and every later evaluation at a score of the segment has an exponent
+// <= 0; the one exception, a backward carry in an additive frame, has a
+// factor e^{(x - ref)/t} <= e^600 on a sum of terms e^{(ref - v)/t} with
+// v >= x, so the product stays below the count: no overflow.
+struct SegCarries {
+    uint32_t rank;               // scores in earlier segments
+    int frame;                   // 1: all four carries below have key ref
+    double E;                    // frame: e^{(first - ref)/t} of this segment
+    float kf_in, kb_in;          // earlier / later segments of this wave
+    double vf_in, vb_in;
+    float kf_w, kb_w;            // lower tail and earlier waves / upper tail and later waves
+    double vf_w, vb_w;
+    float kf_o, kb_o;            // the same before the move into the frame (keys: nearest scores)
+    double vf_o, vb_o;
+    float last_before, first_after;  // nearest segment scores outside the segment (+-inf: none)
 };
+// scratch: sk >= 8 NT/64 floats, sv >= 6 NT/64 doubles, su >= 3 NT/64 words;
+// not written again before the caller's next barrier
 template <int NT>
-LS_DEV BandScan block_scan_band(uint32_t rc, double U, float lastk, double W, float firstk, uint32_t* sr, double* sU,
-                                double* sW, float* sl, float* sf) {
+LS_DEV SegCarries block_seg_carries(uint32_t c, float f, float l, double P, double Bx, const Tails& tl, bool global,
+                                    float* sk, double* sv, uint32_t* su) {
     constexpr int NW = NT / 64;
     const int lane = lane_id(), w = threadIdx.x >> 6;
-    uint32_t ir = rc;
-    double iU = U, iW = W;
-    float il = lastk, iF = firstk;
+    const double inv_t = tl.inv_t;
+    const float fk = c ? f : INFINITY;
+    const float lk = c ? l : -INFINITY;
+    // the wave's score range decides its frame (wave-uniform)
+    const float wmin = __uint_as_float(wave_min_f32_bits(fk)), wmax = __uint_as_float(wave_max_f32_bits(lk));
+    const bool empty = !(wmax > -INFINITY);
+    const bool wadd = global || empty || ((double)wmax - (double)wmin) * inv_t <= 600.0;
+    const float ref = global ? tl.aL : (empty ? -INFINITY : wmin);
+    SegCarries r;
+    r.frame = wadd ? 1 : 0;
+    r.E = 1.0;
+    // in-wave scans: counts, largest last score before, smallest first score
+    // after, and the carries (plain sums in a frame, (K, V) pairs otherwise)
+    uint32_t ir = c;
+    float il = lk, iF = fk;
+    float ak = lk, bk = fk;
+    double av = 0.0, bv = 0.0;
+    if (wadd) {
+        if (c) {
+            const double rd = (double)ref;
+            r.E = exp(((double)f - rd) * inv_t);
+            av = P * exp(((double)l - rd) * inv_t);
+            bv = (1.0 + Bx) / r.E;
+        }
+    } else if (c) {
+        av = P;
+        bv = 1.0 + Bx;
+    }
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t a = __shfl_up(ir, o, 64);
-        const double b = __shfl_up(iU, o, 64);
-        const float c = __shfl_up(il, o, 64);
-        const double d = __shfl_down(iW, o, 64);
-        const float e = __shfl_down(iF, o, 64);
-        if (lane >= o) { ir += a; iU += b; il = fmaxf(il, c); }
-        if (lane + o < 64) { iW += d; iF = fminf(iF, e); }
+        const uint32_t a2 = __shfl_up(ir, o, 64);
+        const float il2 = __shfl_up(il, o, 64);
+        const float iF2 = __shfl_down(iF, o, 64);
+        const double lv2 = __shfl_up(av, o, 64);
+        const double rv2 = __shfl_down(bv, o, 64);
+        float lk2 = 0.0f, rk2 = 0.0f;
+        if (!wadd) {
+            lk2 = __shfl_up(ak, o, 64);
+            rk2 = __shfl_down(bk, o, 64);
+        }
+        if (lane >= o) {
+            ir += a2;
+            il = fmaxf(il, il2);
+            if (wadd) av += lv2;
+            else fwd_combine(lk2, lv2, ak, av, inv_t);
+        }
+        if (lane + o < 64) {
+            iF = fminf(iF, iF2);
+            if (wadd) bv += rv2;
+            else bwd_combine(bk, bv, rk2, rv2, inv_t);
+        }
     }
-    if (lane == 63) { sr[w] = ir; sU[w] = iU; sl[w] = il; }
-    if (lane == 0) { sW[w] = iW; sf[w] = iF; }
-    uint32_t er = __shfl_up(ir, 1, 64);
-    double eU = __shfl_up(iU, 1, 64), eW = __shfl_down(iW, 1, 64);
-    float el = __shfl_up(il, 1, 64), eF = __shfl_down(iF, 1, 64);
-    if (lane == 0) { er = 0u; eU = 0.0; el = -INFINITY; }
-    if (lane == 63) { eW = 0.0; eF = INFINITY; }
+    r.rank = __shfl_up(ir, 1, 64);
+    if (lane == 0) r.rank = 0u;
+    float el = __shfl_up(il, 1, 64);
+    if (lane == 0) el = -INFINITY;
+    float eF = __shfl_down(iF, 1, 64);
+    if (lane == 63) eF = INFINITY;
+    r.vf_in = __shfl_up(av, 1, 64);
+    if (lane == 0) r.vf_in = 0.0;
+    r.vb_in = __shfl_down(bv, 1, 64);
+    if (lane == 63) r.vb_in = 0.0;
+    float tfk, tbk;
+    if (wadd) {
+        r.kf_in = ref;
+        r.kb_in = ref;
+        tfk = ref;
+        tbk = empty && !global ? INFINITY : ref;
+    } else {
+        r.kf_in = __shfl_up(ak, 1, 64);
+        if (lane == 0) r.kf_in = -INFINITY;
+        r.kb_in = __shfl_down(bk, 1, 64);
+        if (lane == 63) r.kb_in = INFINITY;
+        tfk = __shfl(ak, 63, 64);
+        tbk = __shfl(bk, 0, 64);
+    }
+    const double tfv = __shfl(av, 63, 64), tbv = __shfl(bv, 0, 64);
+    if (lane == 0) {
+        sk[w] = tfk; sv[w] = tfv;
+        sk[NW + w] = tbk; sv[NW + w] = tbv;
+        sk[2 * NW + w] = wmax; sk[3 * NW + w] = wmin;
+        sk[4 * NW + w] = ref;
+        su[2 * NW + w] = (wadd && !empty) ? 1u : 0u;  // the wave's carries go in its frame
+    }
+    if (lane == 63) su[w] = ir;
     __syncthreads();
-    uint32_t pr = 0u;
-    double pU = 0.0, pW = 0.0;
-    float pl = -INFINITY, pF = INFINITY;
-    for (int x = 0; x < w; ++x) { pr += sr[x]; pU += sU[x]; pl = fmaxf(pl, sl[x]); }
-    for (int x = NW - 1; x > w; --x) { pW += sW[x]; pF = fminf(pF, sf[x]); }
+    if (global) {
+        // one frame for the whole band: each thread adds the other waves'
+        // totals itself, in wave order (no exponential, no second stage)
+        uint32_t pcn = 0u;
+        double pv = tl.S_L > 0.0 ? tl.S_L : 0.0, qv = 0.0;
+        float pmx = -INFINITY, qmn = INFINITY;
+        for (int x = 0; x < w; ++x) { pcn += su[x]; pv += sv[x]; pmx = fmaxf(pmx, sk[2 * NW + x]); }
+        for (int x = NW - 1; x > w; --x) { qv += sv[NW + x]; qmn = fminf(qmn, sk[3 * NW + x]); }
+        if (tl.S_R > 0.0) qv += tl.S_R * exp(((double)tl.aL - (double)tl.aR) * inv_t);
+        r.rank += pcn;
+        r.kf_w = r.kb_w = r.kf_o = r.kb_o = tl.aL;
+        r.vf_w = r.vf_o = pv;
+        r.vb_w = r.vb_o = qv;
+        r.last_before = fmaxf(el, pmx);
+        r.first_after = fminf(eF, qmn);
+        __syncthreads();
+        return r;
+    }
+    if (w == 0) {
+        // lane x < NW: the carries of the waves before / after wave x, tails included
+        const bool in = lane < NW;
+        float ak = in ? sk[lane] : -INFINITY, bk = in ? sk[NW + lane] : INFINITY;
+        double av = in ? sv[lane] : 0.0, bv = in ? sv[NW + lane] : 0.0;
+        float mx = in ? sk[2 * NW + lane] : -INFINITY, mn = in ? sk[3 * NW + lane] : INFINITY;
+        const float rx = in ? sk[4 * NW + lane] : 0.0f;
+        const bool fx = in && su[2 * NW + lane] != 0u;
+        uint32_t cn = in ? su[lane] : 0u;
+#pragma unroll
+        for (int o = 1; o < NW; o <<= 1) {
+            const float lk2 = __shfl_up(ak, o, 64);
+            const double lv2 = __shfl_up(av, o, 64);
+            const float rk2 = __shfl_down(bk, o, 64);
+            const double rv2 = __shfl_down(bv, o, 64);
+            const float mx2 = __shfl_up(mx, o, 64), mn2 = __shfl_down(mn, o, 64);
+            const uint32_t cn2 = __shfl_up(cn, o, 64);
+            if (lane >= o) { fwd_combine(lk2, lv2, ak, av, inv_t); mx = fmaxf(mx, mx2); cn += cn2; }
+            if (lane + o < NW) { bwd_combine(bk, bv, rk2, rv2, inv_t); mn = fminf(mn, mn2); }
+        }
+        float pk = __shfl_up(ak, 1, 64);
+        if (lane == 0) pk = -INFINITY;
+        double pv = __shfl_up(av, 1, 64);
+        if (lane == 0) pv = 0.0;
+        float qk = __shfl_down(bk, 1, 64);
+        if (lane + 1 >= NW) qk = INFINITY;
+        double qv = __shfl_down(bv, 1, 64);
+        if (lane + 1 >= NW) qv = 0.0;
+        float pmx = __shfl_up(mx, 1, 64);
+        if (lane == 0) pmx = -INFINITY;
+        float qmn = __shfl_down(mn, 1, 64);
+        if (lane + 1 >= NW) qmn = INFINITY;
+        uint32_t pcn = __shfl_up(cn, 1, 64);
+        if (lane == 0) pcn = 0u;
+        {   // the lower tail precedes everything, the upper tail follows everything
+            float tk = -INFINITY; double tv = 0.0;
+            if (tl.S_L > 0.0 && tl.aL > -INFINITY) { tk = tl.aL; tv = tl.S_L; }
+            fwd_combine(tk, tv, pk, pv, inv_t);
+            if (tl.S_R > 0.0 && tl.aR < INFINITY) bwd_combine(qk, qv, tl.aR, tl.S_R, inv_t);
+        }
+        if (in) {
+            sk[6 * NW + lane] = pk; sv[4 * NW + lane] = pv;
+            sk[7 * NW + lane] = qk; sv[5 * NW + lane] = qv;
+        }
+        if (fx) {  // into the wave's own frame (key ref: every exponent <= 0)
+            pv = pv != 0.0 ? pv * exp(((double)pk - (double)rx) * inv_t) : 0.0;
+            qv = qv != 0.0 ? qv * exp(((double)rx - (double)qk) * inv_t) : 0.0;
+            pk = rx;
+            qk = rx;
+        }
+        if (in) {
+            sk[5 * NW + lane] = pk; sv[2 * NW + lane] = pv;
+            sk[NW + lane] = qk; sv[3 * NW + lane] = qv;
+            sk[2 * NW + lane] = pmx; sk[3 * NW + lane] = qmn;
+            su[NW + lane] = pcn;
+        }
+    }
     __syncthreads();
-    BandScan r;
-    r.rank = pr + er;
-    r.U = pU + eU;
-    r.W = pW + eW;
-    r.last = fmaxf(pl, el);
-    r.first = fminf(pF, eF);
+    r.kf_w = sk[5 * NW + w]; r.vf_w = sv[2 * NW + w];
+    r.kb_w = sk[NW + w]; r.vb_w = sv[3 * NW + w];
+    r.kf_o = sk[6 * NW + w]; r.vf_o = sv[4 * NW + w];
+    r.kb_o = sk[7 * NW + w]; r.vb_o = sv[5 * NW + w];
+    r.rank += su[NW + w];
+    r.last_before = fmaxf(el, sk[2 * NW + w]);
+    r.first_after = fminf(eF, sk[3 * NW + w]);
     return r;
 }
 
@@ -389,10 +543,11 @@ __device__ __attribute__((always_inline)) SolveOut segment_solve(const SegView s
     float ak = -INFINITY, bk = INFINITY;
     double av = 0.0, bvv = 0.0;
     uint32_t rc = 0u;
-    uint32_t c1 = 0u; float f1 = 0.0f; double Bx1 = 0.0;  // the one segment (per == 1)
+    uint32_t c1 = 0u, o1 = 0u; float f1 = 0.0f; double Bx1 = 0.0;  // the one segment (per == 1)
     if (per == 1) {
         if (s0 < s1) {
             c1 = sv.cnt[s0];
+            o1 = sv.off[s0];
             if (c1) {
                 f1 = sv.first[s0]; Bx1 = sv.Bx[s0];
                 ak = sv.last[s0]; av = sv.P[s0];
@@ -410,37 +565,12 @@ __device__ __attribute__((always_inline)) SolveOut segment_solve(const SegView s
             if (sv.cnt[s]) { float k2 = sv.first[s]; double v2 = 1.0 + sv.Bx[s]; bwd_combine(k2, v2, bk, bvv, inv_t); bk = k2; bvv = v2; }
         }
     }
-    // Additive frame: with both bracket ends finite and at most 600 t apart,
-    // every band score v has u = e^{(v - a_L)/t} in [1, e^600], so the
-    // carries are plain prefix sums of U = sum u and W = sum 1/u per segment
-    // (no exponential on the scan chain); a carry is then put back in the
-    // (nearest score, sum) form with one exponential.
-    const bool additive = per == 1 && tl.aL > -INFINITY && tl.aR < INFINITY &&
-                          ((double)tl.aR - (double)tl.aL) * inv_t <= 600.0;
     uint32_t rbase;
-    if (additive) {
-        const double ref = (double)tl.aL;
-        double U = 0.0, W = 0.0;
-        float lastk = -INFINITY, firstk = INFINITY;
-        if (c1) {
-            U = av * exp(((double)ak - ref) * inv_t);
-            W = (1.0 + Bx1) * exp((ref - (double)f1) * inv_t);
-            lastk = ak;
-            firstk = f1;
-        }
-        const BandScan bs = block_scan_band<NT>(rc, U, lastk, W, firstk, reinterpret_cast<uint32_t*>(s_int), s_v,
-                                                s_v + NT / 64, s_k, s_k + NT / 64);
-        rbase = bs.rank;
-        // the lower tail: sum over v < a_L of e^{(v - a_L)/t} = S_L; the upper
-        // tail: sum over v >= a_R of e^{(a_L - v)/t} = e^{(a_L - a_R)/t} S_R
-        const double Ub = tl.S_L + bs.U;
-        const double Wa = (tl.S_R > 0.0 ? tl.S_R * exp((ref - (double)tl.aR) * inv_t) : 0.0) + bs.W;
-        if (bs.last > -INFINITY) { ak = bs.last; av = Ub * exp((ref - (double)ak) * inv_t); }
-        else if (tl.S_L > 0.0) { ak = tl.aL; av = tl.S_L; }
-        else { ak = -INFINITY; av = 0.0; }
-        if (bs.first < INFINITY) { bk = bs.first; bvv = Wa * exp(((double)bk - ref) * inv_t); }
-        else if (tl.S_R > 0.0) { bk = tl.aR; bvv = tl.S_R; }
-        else { bk = INFINITY; bvv = 0.0; }
+    SegCarries cr{};  // per == 1
+    if (per == 1) {
+        const bool global = tl.aL > -INFINITY && tl.aR < INFINITY && ((double)tl.aR - (double)tl.aL) * inv_t <= 600.0;
+        cr = block_seg_carries<NT>(c1, f1, ak, av, Bx1, tl, global, s_k, s_v, reinterpret_cast<uint32_t*>(s_int));
+        rbase = cr.rank;
     } else {
         rbase = block_exclusive_scan<NT>(rc, nullptr, reinterpret_cast<uint32_t*>(s_int));
         block_scan_fwd_excl<NT>(ak, av, s_k, s_v, inv_t);
@@ -453,17 +583,31 @@ __device__ __attribute__((always_inline)) SolveOut segment_solve(const SegView s
         if (tl.S_R > 0.0 && tl.aR < INFINITY) bwd_combine(bk, bvv, tl.aR, tl.S_R, inv_t);
     }
     int cand = -1;
-    auto g_at_first = [&](int s, float f, double Bx, float pk, double pv, float nk, double nv, uint32_t rank) {
-        const double Pf = 1.0 + (pv != 0.0 ? ecoef(((double)pk - (double)f) * inv_t) * pv : 0.0);
-        const double Bf = Bx + (nv != 0.0 ? ecoef(((double)f - (double)nk) * inv_t) * nv : 0.0);
+    auto g_test = [&](int s, double Pf, double Bf, uint32_t rank) {
         sc.bfx[s] = Bf;
         const double G = 0.5 * Pf + (tl.m - 1.0 - (double)rank) + tl.c_R - 0.5 * Bf;
         if (G >= tl.k) cand = max(cand, s);
     };
+    auto g_at_first = [&](int s, float f, double Bx, float pk, double pv, float nk, double nv, uint32_t rank) {
+        const double Pf = 1.0 + (pv != 0.0 ? ecoef(((double)pk - (double)f) * inv_t) * pv : 0.0);
+        const double Bf = Bx + (nv != 0.0 ? ecoef(((double)f - (double)nk) * inv_t) * nv : 0.0);
+        g_test(s, Pf, Bf, rank);
+    };
     if (per == 1) {
-        if (s0 < s1) {
-            sc.pk[s0] = ak; sc.pv[s0] = av; sc.bk[s0] = bk; sc.bv[s0] = bvv; sc.rank[s0] = rbase;
-            if (c1) g_at_first(s0, f1, Bx1, ak, av, bk, bvv, rbase);
+        if (s0 < s1 && c1) {
+            // the curve at the segment's first score from the four carries
+            const double x = (double)f1;
+            double Pf = 1.0, Bf = Bx1;
+            if (cr.frame) {  // all four carries have key ref; E = e^{(x - ref)/t}
+                Pf += (cr.vf_in + cr.vf_w) / cr.E;
+                Bf += (cr.vb_in + cr.vb_w) * cr.E;
+            } else {
+                if (cr.vf_in != 0.0) Pf += cr.vf_in * exp(((double)cr.kf_in - x) * inv_t);
+                if (cr.vf_w != 0.0) Pf += cr.vf_w * exp(((double)cr.kf_w - x) * inv_t);
+                if (cr.vb_in != 0.0) Bf += cr.vb_in * exp((x - (double)cr.kb_in) * inv_t);
+                if (cr.vb_w != 0.0) Bf += cr.vb_w * exp((x - (double)cr.kb_w) * inv_t);
+            }
+            g_test(s0, Pf, Bf, rbase);
         }
     } else {
         for (int s = s0; s < s1; ++s) {
@@ -483,6 +627,43 @@ __device__ __attribute__((always_inline)) SolveOut segment_solve(const SegView s
     }
     __threadfence_block();
     const int sstar = block_max_int<NT>(cand, s_int);
+    // the root segment's count, offset, rank and carries, published through
+    // LDS by the thread that holds them (per == 1) or read back by thread 0
+    __shared__ uint32_t s_seg[3];
+    __shared__ float s_ck[2];
+    __shared__ double s_cv[2];
+    if (sstar >= 0) {
+        if (per == 1) {
+            if (tid == sstar) {
+                // the carries in (nearest score, sum) form: key = the nearest
+                // score of another segment (else the tail's end), every
+                // exponent <= 0 (the in-wave backward carry of an additive
+                // wave: at most 600 t)
+                // (the carries from other waves in their form before the move
+                // into this wave's frame: their keys are scores of those waves)
+                if (cr.last_before > -INFINITY) {
+                    ak = cr.last_before;
+                    av = 0.0;
+                    if (cr.vf_in != 0.0) av += cr.vf_in * exp(((double)cr.kf_in - (double)ak) * inv_t);
+                    if (cr.vf_o != 0.0) av += cr.vf_o * exp(((double)cr.kf_o - (double)ak) * inv_t);
+                } else if (tl.S_L > 0.0 && tl.aL > -INFINITY) { ak = tl.aL; av = tl.S_L; }
+                else { ak = -INFINITY; av = 0.0; }
+                if (cr.first_after < INFINITY) {
+                    bk = cr.first_after;
+                    bvv = 0.0;
+                    if (cr.vb_in != 0.0) bvv += cr.vb_in * exp(((double)bk - (double)cr.kb_in) * inv_t);
+                    if (cr.vb_o != 0.0) bvv += cr.vb_o * exp(((double)bk - (double)cr.kb_o) * inv_t);
+                } else if (tl.S_R > 0.0 && tl.aR < INFINITY) { bk = tl.aR; bvv = tl.S_R; }
+                else { bk = INFINITY; bvv = 0.0; }
+                sc.pk[s0] = ak; sc.pv[s0] = av; sc.bk[s0] = bk; sc.bv[s0] = bvv; sc.rank[s0] = rbase;
+                s_seg[0] = c1; s_seg[1] = o1; s_seg[2] = rbase;
+                s_ck[0] = ak; s_cv[0] = av; s_ck[1] = bk; s_cv[1] = bvv;
+            }
+        } else if (tid == 0) {
+            s_seg[0] = sv.cnt[sstar]; s_seg[1] = sv.off[sstar]; s_seg[2] = sc.rank[sstar];
+            s_ck[0] = sc.pk[sstar]; s_cv[0] = sc.pv[sstar]; s_ck[1] = sc.bk[sstar]; s_cv[1] = sc.bv[sstar];
+        }
+    }
     __threadfence_block();
     __syncthreads();
 
@@ -490,7 +671,7 @@ __device__ __attribute__((always_inline)) SolveOut segment_solve(const SegView s
     if (tid == 0) s_owner = -1;
     if (sstar >= 0) {
         // ---- phase 4: per-score curve inside the root segment ----
-        const uint32_t cS = sv.cnt[sstar], offS = sv.off[sstar], rankS = sc.rank[sstar];
+        const uint32_t cS = s_seg[0], offS = s_seg[1], rankS = s_seg[2];
         if (sv.sortbuf && cS > (uint32_t)kBucketCapMax) {
             out.big = 1;
             out.jstar = sstar;
@@ -520,8 +701,8 @@ __device__ __attribute__((always_inline)) SolveOut segment_solve(const SegView s
             }
             const float vfirst = key2f(rk[0]);
             const float vlast = key2f(rk[cS - 1]);
-            const float pk0 = sc.pk[sstar]; const double pv0 = sc.pv[sstar];
-            const float bk0 = sc.bk[sstar]; const double bv0 = sc.bv[sstar];
+            const float pk0 = s_ck[0]; const double pv0 = s_cv[0];
+            const float bk0 = s_ck[1]; const double bv0 = s_cv[1];
             double Pj[EMX], Bj[EMX];
             const bool have_local = sv.eU != nullptr && !sv.wide[sstar];
             if (have_local || ((double)vlast - (double)vfirst) * inv_t <= 600.0) {
@@ -543,8 +724,8 @@ __device__ __attribute__((always_inline)) SolveOut segment_solve(const SegView s
     #pragma unroll
                     for (int q = 0; q < EMX; ++q)
                         if (e0 + q < e1) { ut += u[q]; wt += 1.0 / u[q]; }
-                    double U = block_scan_add_excl<NT>(ut, s_v, false);
-                    double W = block_scan_add_excl<NT>(wt, s_v, true);
+                    double U, W;
+                    block_scan_add_excl2<NT>(ut, wt, U, W, s_v);
     #pragma unroll
                     for (int q = 0; q < EMX; ++q)
                         if (e0 + q < e1) { U += u[q]; Ul[q] = U; }

@@ -493,6 +493,34 @@ LS_DEV double block_scan_add_excl(double v, double* s, bool reverse) {
     return ex;
 }
 
+// a forward exclusive scan of a and a backward one of b behind the barriers
+// of one (the same arithmetic as two block_scan_add_excl calls); s: >= 2 NT/64
+template <int NT>
+LS_DEV void block_scan_add_excl2(double a, double b, double& ea, double& eb, double* s) {
+    constexpr int NW = NT / 64;
+    const int lane = lane_id(), w = threadIdx.x >> 6;
+    const double ia = wave_scan_add_incl(a, false);
+    const double ib = wave_scan_add_incl(b, true);
+    ea = wave_excl_from_incl(ia, false);
+    eb = wave_excl_from_incl(ib, true);
+    if (NW > 1) {
+        if (lane == 63) s[w] = ia;
+        if (lane == 0) s[NW + w] = ib;
+        __syncthreads();
+        if (w == 0) {
+            const double x = lane < NW ? s[lane] : 0.0;
+            const double y = lane < NW ? s[NW + lane] : 0.0;
+            const double xe = wave_excl_from_incl(wave_scan_add_incl(x, false), false);
+            const double ye = wave_excl_from_incl(wave_scan_add_incl(y, true), true);
+            if (lane < NW) { s[lane] = xe; s[NW + lane] = ye; }
+        }
+        __syncthreads();
+        ea = s[w] + ea;
+        eb = s[NW + w] + eb;
+        __syncthreads();
+    }
+}
+
 // ---------------------------------------------------------------------------
 // 128-bit fixed-point sums of terms in [0, 1] (62 fractional bits): integer
 // addition is associative, so a sum over scores in any order (e.g. the order
@@ -546,6 +574,76 @@ LS_DEV Fx128 block_sum_fx(Fx128 v, unsigned long long* s /* >= 2 * NT/64 */) {
     }
     __syncthreads();
     return r;  // valid in wave 0
+}
+
+// two fixed-point block sums behind one barrier pair (results valid in wave 0)
+template <int NT>
+LS_DEV void block_sum_fx2(Fx128& a, Fx128& b, unsigned long long* s /* >= 4 * NT/64 */) {
+    constexpr int NW = NT / 64;
+    const int w = threadIdx.x >> 6, l = lane_id();
+    auto step = [&](auto d_tag) {
+        constexpr int D = decltype(d_tag)::value;
+        Fx128 y, z;
+        y.lo = xor_lane64<D>(a.lo);
+        y.hi = xor_lane64<D>(a.hi);
+        z.lo = xor_lane64<D>(b.lo);
+        z.hi = xor_lane64<D>(b.hi);
+        a = fx_add(a, y);
+        b = fx_add(b, z);
+    };
+    step(std::integral_constant<int, 32>());
+    step(std::integral_constant<int, 16>());
+    step(std::integral_constant<int, 8>());
+    step(std::integral_constant<int, 4>());
+    step(std::integral_constant<int, 2>());
+    step(std::integral_constant<int, 1>());
+    if (l == 0) { s[4 * w] = a.lo; s[4 * w + 1] = a.hi; s[4 * w + 2] = b.lo; s[4 * w + 3] = b.hi; }
+    __syncthreads();
+    Fx128 ra = fx_zero(), rb = fx_zero();
+    if (w == 0) {
+        for (int q = 0; q < NW; ++q) {
+            Fx128 y, z;
+            y.lo = s[4 * q]; y.hi = s[4 * q + 1];
+            z.lo = s[4 * q + 2]; z.hi = s[4 * q + 3];
+            ra = fx_add(ra, y);
+            rb = fx_add(rb, z);
+        }
+    }
+    __syncthreads();
+    a = ra;
+    b = rb;
+}
+
+// wave minimum / maximum of a float, returned as its bits (NaN-free inputs)
+LS_DEV uint32_t wave_min_f32_bits(float x) {
+    uint32_t v = __float_as_uint(x);
+    v = __float_as_uint(fminf(__uint_as_float(v), __uint_as_float(xor_lane<32>(v))));
+    v = __float_as_uint(fminf(__uint_as_float(v), __uint_as_float(xor_lane<16>(v))));
+    v = __float_as_uint(fminf(__uint_as_float(v), __uint_as_float(xor_lane<8>(v))));
+    v = __float_as_uint(fminf(__uint_as_float(v), __uint_as_float(xor_lane<4>(v))));
+    v = __float_as_uint(fminf(__uint_as_float(v), __uint_as_float(xor_lane<2>(v))));
+    v = __float_as_uint(fminf(__uint_as_float(v), __uint_as_float(xor_lane<1>(v))));
+    return v;
+}
+LS_DEV uint32_t wave_max_f32_bits(float x) {
+    uint32_t v = __float_as_uint(x);
+    v = __float_as_uint(fmaxf(__uint_as_float(v), __uint_as_float(xor_lane<32>(v))));
+    v = __float_as_uint(fmaxf(__uint_as_float(v), __uint_as_float(xor_lane<16>(v))));
+    v = __float_as_uint(fmaxf(__uint_as_float(v), __uint_as_float(xor_lane<8>(v))));
+    v = __float_as_uint(fmaxf(__uint_as_float(v), __uint_as_float(xor_lane<4>(v))));
+    v = __float_as_uint(fmaxf(__uint_as_float(v), __uint_as_float(xor_lane<2>(v))));
+    v = __float_as_uint(fmaxf(__uint_as_float(v), __uint_as_float(xor_lane<1>(v))));
+    return v;
+}
+
+LS_DEV uint32_t wave_min_u32(uint32_t v) {
+    v = min(v, xor_lane<32>(v));
+    v = min(v, xor_lane<16>(v));
+    v = min(v, xor_lane<8>(v));
+    v = min(v, xor_lane<4>(v));
+    v = min(v, xor_lane<2>(v));
+    v = min(v, xor_lane<1>(v));
+    return v;
 }
 
 // device-scope ticket for the last-workgroup pattern: release this

@@ -97,41 +97,55 @@ constexpr int kAggThreads = 256;
 __global__ __launch_bounds__(kAggThreads) void k_bucket_agg(const uint32_t* __restrict__ bucket_vals,
                                                              const uint32_t* bucket_cnt, int cap, SegArrays seg,
                                                              double inv_t, const uint32_t* hoff, const int* gate) {
-    __shared__ uint32_t s_kmin, s_kmax;
-    __shared__ unsigned long long s_fx[2 * kAggThreads / 64];
+    constexpr int NW = kAggThreads / 64;
+    constexpr int R = 4;  // scores a thread keeps in registers; a larger bucket is read twice
+    __shared__ uint32_t s_mm[2 * NW];
+    __shared__ unsigned long long s_fx[4 * NW];
     if (gate && *gate == 0) return;  // launched ahead of a certification that failed
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, w = tid >> 6;
     const int bkt = blockIdx.x;
     const uint32_t ho = hoff ? hoff[bkt] : kNotHeavy;
     const int c = ho != kNotHeavy ? (int)bucket_cnt[bkt] : (int)min(bucket_cnt[bkt], (uint32_t)cap);
     const size_t off = ho != kNotHeavy ? (size_t)ho : (size_t)bkt * (size_t)cap;
-    if (tid == 0) { seg.cnt[bkt] = (uint32_t)c; seg.off[bkt] = (uint32_t)off; s_kmin = 0xFFFFFFFFu; s_kmax = 0u; }
+    if (tid == 0) { seg.cnt[bkt] = (uint32_t)c; seg.off[bkt] = (uint32_t)off; }
     if (c == 0) return;
     const uint32_t* vals = bucket_vals + off;
-    __syncthreads();
+    uint32_t kk[R];
     uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
-    for (int i = tid; i < c; i += kAggThreads) {
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+        const int i = tid + q * kAggThreads;
+        kk[q] = i < c ? f2key(__uint_as_float(vals[i])) : 0u;
+        if (i < c) { kmn = min(kmn, kk[q]); kmx = max(kmx, kk[q]); }
+    }
+    for (int i = tid + R * kAggThreads; i < c; i += kAggThreads) {
         const uint32_t k = f2key(__uint_as_float(vals[i]));
         kmn = min(kmn, k);
         kmx = max(kmx, k);
     }
-    atomicMin(&s_kmin, kmn);
-    atomicMax(&s_kmax, kmx);
+    kmn = wave_min_u32(kmn);
+    kmx = wave_max_u32(kmx);
+    if (lane_id() == 0) { s_mm[w] = kmn; s_mm[NW + w] = kmx; }
     __syncthreads();
-    const double vmin = (double)key2f(s_kmin), vmax = (double)key2f(s_kmax);
+#pragma unroll
+    for (int x = 0; x < NW; ++x) { kmn = min(kmn, s_mm[x]); kmx = max(kmx, s_mm[NW + x]); }
+    const double vmin = (double)key2f(kmn), vmax = (double)key2f(kmx);
     Fx128 P = fx_zero(), Q = fx_zero();
-    for (int i = tid; i < c; i += kAggThreads) {
-        const double v = (double)key2f(f2key(__uint_as_float(vals[i])));
+    auto add = [&](uint32_t k) {
+        const double v = (double)key2f(k);
         fx_add_term(P, exp((v - vmax) * inv_t));
         fx_add_term(Q, exp((vmin - v) * inv_t));
-    }
-    const Fx128 Ps = block_sum_fx<kAggThreads>(P, s_fx);
-    const Fx128 Qs = block_sum_fx<kAggThreads>(Q, s_fx);
+    };
+#pragma unroll
+    for (int q = 0; q < R; ++q)
+        if (tid + q * kAggThreads < c) add(kk[q]);
+    for (int i = tid + R * kAggThreads; i < c; i += kAggThreads) add(f2key(__uint_as_float(vals[i])));
+    block_sum_fx2<kAggThreads>(P, Q, s_fx);
     if (tid == 0) {
         seg.first[bkt] = (float)vmin;
         seg.last[bkt] = (float)vmax;
-        seg.P[bkt] = fx_to_double(Ps);
-        seg.Bx[bkt] = fx_to_double(fx_minus_one(Qs));
+        seg.P[bkt] = fx_to_double(P);
+        seg.Bx[bkt] = fx_to_double(fx_minus_one(Q));
     }
 }
 
