@@ -1,22 +1,24 @@
 // Streaming (HBM-bound) kernels of the Fast LapSum solver (gfx950).
 //
-//  k_filter      the single streaming pass of the bracketing path (Fast
-//                LapSum paper, gist.science summary section 2.2, bracketing
-//                step 2): scores below a_L are folded into
-//                S_L = sum e^{(r - a_L)/t}, scores at or above a_R into
-//                S_R = sum e^{(a_R - r)/t}, and the middle band is kept,
-//                already split into value-ordered buckets.  Its last
-//                workgroup reduces the per-workgroup partials in a fixed
-//                order and hands the totals to the host (certification).
-//  k_probs       p_i = F((r_i - b)/t) and sum p (section 2.1).
-//  k_vjp_reduce  sum f g and sum f, f_i = e^{-|r_i - b|/t}/2 (section 2.1, VJP);
-//                the last workgroup forms c = sum f g / sum f.
-//  k_vjp_apply   grad_i = (f_i / t)(g_i - c).
+//  k_filter           the single streaming pass of the bracketing path (Fast
+//                     LapSum paper, gist.science summary section 2.2,
+//                     bracketing step 2): scores below a_L are folded into
+//                     S_L = sum e^{(r - a_L)/t}, scores at or above a_R into
+//                     S_R = sum e^{(a_R - r)/t}, and the middle band is kept,
+//                     already split into value-ordered buckets.
+//  k_filter_finalize  one workgroup: the per-workgroup partials reduced in a
+//                     fixed order, the certification quantities, the gate for
+//                     the kernels launched behind it, and the host summary.
+//  k_probs            p_i = F((r_i - b)/t) and sum p (section 2.1).
+//  k_vjp_reduce       per workgroup sum f g and sum f, f_i = e^{-|r_i - b|/t}/2
+//                     (section 2.1, VJP); k_vjp_c forms c = sum f g / sum f.
+//  k_vjp_apply        grad_i = (f_i / t)(g_i - c).
 //
-// Memory access: 16-byte loads/stores in a grid-stride loop with four loads
-// in flight per thread (the host picks the scalar variant for misaligned
-// pointers).  Reductions: fp32 within one float4, fp64 across float4s and
-// workgroups, combined in a fixed order (bitwise reproducible).
+// Memory access: 16-byte loads/stores over tiles of kStreamThreads * V
+// float4s with all V loads of a thread in flight (the host picks the scalar
+// variant for misaligned pointers).  Reductions: fp32 within one float4, fp64
+// across float4s and workgroups, combined in a fixed order (bitwise
+// reproducible).
 #include <algorithm>
 #include <cmath>
 
@@ -50,6 +52,7 @@ constexpr int kQueuePerWave = kQueueCap / (kStreamThreads / 64);  // each wave a
 // bounded number of workgroups walk the tiles; the light passes run one tile
 // per workgroup up to the partials' capacity.
 constexpr int kFilterV = 4, kFilterGrid = 1536;
+constexpr int kFinalizeThreads = 1024;  // one workgroup: two filter partials per thread
 constexpr int kProbsV = 2, kProbsGrid = kMaxStreamParts;
 constexpr int kReduceV = 4, kReduceGrid = 8192;
 constexpr int kApplyV = 1, kApplyGrid = 1 << 24;
@@ -293,29 +296,29 @@ __global__ __launch_bounds__(kStreamThreads) void k_filter(const float* __restri
 //   G(a_R) = e^{(a_L - a_R)/t} S_L/2 + B_R/2 + c_R - S_R/2,
 // and the bracket holds iff G(a_L) >= k > G(a_R) (an open end holds); the
 // gate opens when it holds and every band score was stored.
-__global__ __launch_bounds__(kStreamThreads) void k_filter_finalize(const FilterPart* part, int nparts, long long n,
+__global__ __launch_bounds__(kFinalizeThreads) void k_filter_finalize(const FilterPart* part, int nparts, long long n,
                                                                      Ctl* ctl, const uint32_t* bucket_cnt, int cap,
                                                                      HostSummary* hs, unsigned int seq, double k,
                                                                      double t) {
-    __shared__ double s_rd[4 * (kStreamThreads / 64)];
-    __shared__ unsigned long long s_ru[3 * (kStreamThreads / 64)];
-    __shared__ uint32_t s_rm[3 * (kStreamThreads / 64)];
+    __shared__ double s_rd[4 * (kFinalizeThreads / 64)];
+    __shared__ unsigned long long s_ru[3 * (kFinalizeThreads / 64)];
+    __shared__ uint32_t s_rm[3 * (kFinalizeThreads / 64)];
     const int tid = threadIdx.x;
     // every load first (one memory round trip), then combine in a fixed order
-    constexpr int PP = kMaxStreamBlocks / kStreamThreads;
+    constexpr int PP = kMaxStreamBlocks / kFinalizeThreads;
     FilterPart fp[PP];
 #pragma unroll
     for (int q = 0; q < PP; ++q) {
-        const int b = tid + q * kStreamThreads;
+        const int b = tid + q * kFinalizeThreads;
         if (b < nparts) fp[q] = part[b];
     }
     // bucket counts: a thread sums its buckets and keeps their maximum
     const int nbk = ctl->nb;
-    constexpr int BQ = kMaxBuckets / kStreamThreads;
+    constexpr int BQ = kMaxBuckets / kFinalizeThreads;
     uint32_t bcv[BQ];
 #pragma unroll
     for (int q = 0; q < BQ; ++q) {
-        const int b = tid + q * kStreamThreads;
+        const int b = tid + q * kFinalizeThreads;
         bcv[q] = b < nbk ? bucket_cnt[b] : 0u;
     }
     unsigned long long bc = 0ull;
@@ -328,7 +331,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_filter_finalize(const Filter
     float amx = 0.0f;
 #pragma unroll
     for (int q = 0; q < PP; ++q) {
-        const int b = tid + q * kStreamThreads;
+        const int b = tid + q * kFinalizeThreads;
         if (b < nparts) {
             a0 += fp[q].S[0]; a1 += fp[q].S[1]; a2 += fp[q].S[2]; a3 += fp[q].S[3];
             u0 += fp[q].c[0]; u1 += fp[q].c[1];
@@ -339,7 +342,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_filter_finalize(const Filter
     double d[4] = {a0, a1, a2, a3};
     unsigned long long u[3] = {u0, u1, bc};
     uint32_t mx[3] = {__float_as_uint(amx), (uint32_t)anynan, bmx};  // |v| >= 0: uint order = float order
-    block_reduce_multi<kStreamThreads>(d, u, mx, s_rd, s_ru, s_rm);
+    block_reduce_multi<kFinalizeThreads>(d, u, mx, s_rd, s_ru, s_rm);
     const double T0 = d[0], T1 = d[1], T2 = d[2], T3 = d[3];
     const unsigned long long NAN_ = u[0], CR = u[1], M = u[2];
     const int nb = ctl->nb;
@@ -384,7 +387,7 @@ void launch_filter(const float* r, long long n, double t, Ctl* ctl, const float*
     else
         hipLaunchKernelGGL(k_filter<false>, dim3(blocks), dim3(kStreamThreads), 0, st, r, n, ls, ctl, sp, iw,
                            bucket_cnt, bucket_vals, cap, fp);
-    hipLaunchKernelGGL(k_filter_finalize, dim3(1), dim3(kStreamThreads), 0, st, fp, blocks, n, ctl, bucket_cnt, cap,
+    hipLaunchKernelGGL(k_filter_finalize, dim3(1), dim3(kFinalizeThreads), 0, st, fp, blocks, n, ctl, bucket_cnt, cap,
                        hs_dev, seq, k, t);
 }
 
@@ -463,7 +466,9 @@ template <bool VEC, bool KT>
 __global__ __launch_bounds__(kStreamThreads) void k_vjp_reduce(const float* __restrict__ r, const float* __restrict__ g,
                                                                 long long n, const double* bptr, double inv_t,
                                                                 double* part) {
-    __shared__ double s_red[kStreamThreads / 64];
+    __shared__ double s_rd[4 * (kStreamThreads / 64)];
+    __shared__ unsigned long long s_ru[kStreamThreads / 64];
+    __shared__ uint32_t s_rm[kStreamThreads / 64];
     const double b = *bptr;
     const int tid = threadIdx.x;
     double sfg = 0.0, sf = 0.0, sfgd = 0.0, sfd = 0.0;
@@ -501,17 +506,16 @@ __global__ __launch_bounds__(kStreamThreads) void k_vjp_reduce(const float* __re
         for (long long i = (long long)blockIdx.x * kStreamThreads + tid; i < n; i += stride) one(r[i], g[i]);
     }
     constexpr int NP = KT ? 4 : 2;
-    const double t0 = block_sum<kStreamThreads>(sfg, s_red);
-    const double t1 = block_sum<kStreamThreads>(sf, s_red);
-    double t2 = 0.0, t3 = 0.0;
-    if (KT) {
-        t2 = block_sum<kStreamThreads>(sfgd, s_red);
-        t3 = block_sum<kStreamThreads>(sfd, s_red);
-    }
+    double d[NP];
+    d[0] = sfg;
+    d[1] = sf;
+    if constexpr (KT) { d[2] = sfgd; d[3] = sfd; }
+    unsigned long long u0[1] = {0ull};
+    uint32_t m0[1] = {0u};
+    block_reduce_multi<kStreamThreads>(d, u0, m0, s_rd, s_ru, s_rm);
     if (tid == 0) {
-        part[NP * blockIdx.x] = t0;
-        part[NP * blockIdx.x + 1] = t1;
-        if (KT) { part[NP * blockIdx.x + 2] = t2; part[NP * blockIdx.x + 3] = t3; }
+#pragma unroll
+        for (int q = 0; q < NP; ++q) part[NP * blockIdx.x + q] = d[q];
     }
 }
 
@@ -521,15 +525,34 @@ __global__ __launch_bounds__(kStreamThreads) void k_vjp_reduce(const float* __re
 template <bool KT>
 __global__ __launch_bounds__(1024) void k_vjp_c(const double* part, int nparts, Ctl* ctl, double t, double* dk_out,
                                                 double* dt_out) {
-    __shared__ double s_red[1024 / 64];
+    constexpr int NT = 1024, NW = NT / 64;
+    __shared__ double s_rd[4 * NW];
+    __shared__ unsigned long long s_ru[NW];
+    __shared__ uint32_t s_rm[NW];
     constexpr int NP = KT ? 4 : 2;
-    const double T0 = sum_parts<1024>(part, NP, 0, nparts, s_red);
-    const double T1 = sum_parts<1024>(part, NP, 1, nparts, s_red);
-    double T2 = 0.0, T3 = 0.0;
-    if (KT) {
-        T2 = sum_parts<1024>(part, NP, 2, nparts, s_red);
-        T3 = sum_parts<1024>(part, NP, 3, nparts, s_red);
+    // every partial of a thread loaded in one batch (nparts <= 8 NT), then
+    // summed in a fixed order
+    constexpr int B = kReduceGrid / NT;
+    static_assert(B * NT == kReduceGrid, "");
+    double v[B][NP];
+#pragma unroll
+    for (int q = 0; q < B; ++q) {
+        const int i = (int)threadIdx.x + q * NT;
+#pragma unroll
+        for (int x = 0; x < NP; ++x) v[q][x] = i < nparts ? part[(size_t)i * NP + x] : 0.0;
     }
+    double d[NP];
+#pragma unroll
+    for (int x = 0; x < NP; ++x) {
+        d[x] = 0.0;
+#pragma unroll
+        for (int q = 0; q < B; ++q) d[x] += v[q][x];
+    }
+    unsigned long long u0[1] = {0ull};
+    uint32_t m0[1] = {0u};
+    block_reduce_multi<NT>(d, u0, m0, s_rd, s_ru, s_rm);
+    const double T0 = d[0], T1 = d[1];
+    const double T2 = KT ? d[NP > 2 ? 2 : 0] : 0.0, T3 = KT ? d[NP > 3 ? 3 : 0] : 0.0;
     if (threadIdx.x == 0) {
         ctl->sumfg = T0; ctl->sumf = T1; ctl->c = T0 / T1;
         if (KT) {
