@@ -52,7 +52,7 @@ constexpr int kQueuePerWave = kQueueCap / (kStreamThreads / 64);  // each wave a
 // bounded number of workgroups walk the tiles; the light passes run one tile
 // per workgroup up to the partials' capacity.
 constexpr int kFilterV = 4, kFilterGrid = 1536;
-constexpr int kFinalizeThreads = 1024;  // one workgroup: two filter partials per thread
+constexpr int kFinalizeThreads = 256;  // one workgroup: eight filter partials per thread
 constexpr int kProbsV = 2, kProbsGrid = kMaxStreamParts;
 constexpr int kReduceV = 4, kReduceGrid = 8192;
 constexpr int kApplyV = 1, kApplyGrid = 1 << 24;
