@@ -36,7 +36,9 @@ constexpr int kFlagOverflow = 2;
 constexpr int kFlagInternal = 4;
 constexpr int kFlagBigRoot = 8;   // the root lies in a bucket too large for LDS (host sorts it)
 constexpr int kFlagCertified = 16;  // G(a_L) >= k > G(a_R) from the filter's sums
+constexpr int kFlagHeavy = 32;      // certified with overflowed buckets, and slots for them laid out
 constexpr uint32_t kNotHeavy = 0xFFFFFFFFu;  // bucket slot offset marker: not an overflowed bucket
+constexpr int kHeavyChunk = 2048;   // scores of an overflowed bucket per aggregation workgroup
 
 // ---------------------------------------------------------------------------
 // control block: one per workspace, in device memory
@@ -68,6 +70,26 @@ struct Ctl {
     // the band solve and p pass launched right behind it then do their work
     int32_t gate;
     int32_t pad2;
+    // overflowed buckets: aggregation chunks, and the slot offset of a root
+    // bucket too large for LDS (for the host's sort)
+    uint32_t hchunks;
+    uint32_t pad3;
+    unsigned long long root_off;
+};
+
+// Slots of the overflowed ("heavy") buckets, laid out by the filter's
+// finalize kernel: per bucket its slot offset (kNotHeavy for the others),
+// fill count, smallest and largest score key, and first aggregation chunk;
+// per chunk its four 64-bit fixed-point partial sums.
+struct HeavyArrays {
+    uint32_t* hoff;
+    uint32_t* hfill;
+    uint32_t* hmin;
+    uint32_t* hmax;
+    uint32_t* hch0;
+    unsigned long long* hpart;
+    unsigned long long base_off;   // slot offsets start here (elements past bucket_vals)
+    unsigned long long cap_total;  // scores the slot region holds
 };
 
 // host-pinned summary written by the filter's last workgroup; the host polls seq
@@ -79,8 +101,14 @@ struct HostSummary {
     int32_t flags;
     int32_t nb;
     unsigned long long max_bucket;
+    unsigned long long heavy_total;  // scores in overflowed buckets (kFlagHeavy)
+    uint32_t hchunks;                // their aggregation chunks
     volatile unsigned int seq;
-    unsigned int pad;
+    // written by the band solve of overflowed buckets when asked to
+    unsigned long long root_off;  // slot of a root bucket too large for LDS
+    unsigned long long root_m;    // its score count
+    int32_t root_flags;
+    volatile unsigned int root_seq;
 };
 
 enum DoneSlot { kDoneFilter = 0, kDoneHist = 1, kDoneCurve = 2, kDoneBucket = 3, kDoneProbs = 4, kDoneVjp = 5 };

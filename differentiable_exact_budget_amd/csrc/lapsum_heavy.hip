@@ -14,14 +14,13 @@ namespace lapsum {
 
 constexpr int kHeavyQueue = 2048;                            // per workgroup, in LDS
 constexpr int kHeavyQueuePerWave = kHeavyQueue / (kStreamThreads / 64);
-constexpr int kHeavyV = 4, kHeavyGrid = 1536;
+constexpr int kHeavyV = 4, kHeavyGrid = 1024;  // 36 KB of LDS per workgroup: four per CU
 
 // hoff[b]: element offset (from `base`) of heavy bucket b's slot, or
 // kNotHeavy; hfill[b]: scores placed so far (zeroed before the pass)
 __global__ __launch_bounds__(kStreamThreads) void k_heavy_collect(const float* __restrict__ r, long long n,
                                                                    const Ctl* ctl, const float* __restrict__ sp_g,
-                                                                   const float* __restrict__ iw_g,
-                                                                   const uint32_t* __restrict__ hoff_g, uint32_t* hfill,
+                                                                   const float* __restrict__ iw_g, HeavyArrays ha,
                                                                    uint32_t* base) {
     __shared__ float sp[kMaxBuckets + 1];
     __shared__ float iw[kMaxBuckets];
@@ -29,7 +28,12 @@ __global__ __launch_bounds__(kStreamThreads) void k_heavy_collect(const float* _
     __shared__ float q[kHeavyQueue];
     __shared__ uint32_t lcnt[kMaxBuckets];
     __shared__ uint32_t gbase[kMaxBuckets];
+    __shared__ uint32_t lmin[kMaxBuckets];
+    __shared__ uint32_t lmax[kMaxBuckets];
     __shared__ uint32_t s_wq[kStreamThreads / 64];
+    if (!(ctl->flags & kFlagHeavy)) return;  // no slots were laid out
+    const uint32_t* __restrict__ hoff_g = ha.hoff;
+    uint32_t* hfill = ha.hfill;
     const int tid = threadIdx.x, lane = lane_id();
     FilterState fs;
     fs.aL = ctl->aL; fs.aR = ctl->aR; fs.ls = 0.0f;
@@ -37,7 +41,12 @@ __global__ __launch_bounds__(kStreamThreads) void k_heavy_collect(const float* _
     const int nb = ctl->nb;
     for (int i = tid; i <= fs.ng; i += kStreamThreads) sp[i] = sp_g[i];
     for (int i = tid; i < fs.ng; i += kStreamThreads) iw[i] = iw_g[i];
-    for (int i = tid; i < nb; i += kStreamThreads) { hoff[i] = hoff_g[i]; lcnt[i] = 0u; }
+    for (int i = tid; i < nb; i += kStreamThreads) {
+        hoff[i] = hoff_g[i];
+        lcnt[i] = 0u;
+        lmin[i] = 0xFFFFFFFFu;
+        lmax[i] = 0u;
+    }
     fs.sp = sp; fs.iw = iw; fs.bucket_cnt = nullptr; fs.bucket_vals = nullptr;
     __syncthreads();
     const float aL = fs.aL, aR = fs.aR;
@@ -51,6 +60,9 @@ __global__ __launch_bounds__(kStreamThreads) void k_heavy_collect(const float* _
     auto direct = [&](float v, int bk) {
         const uint32_t pos = atomicAdd(&hfill[bk], 1u);
         base[(size_t)hoff[bk] + pos] = __float_as_uint(v);
+        const uint32_t key = f2key(v);
+        atomicMin(&ha.hmin[bk], key);
+        atomicMax(&ha.hmax[bk], key);
     };
     auto put = [&](float v, uint32_t pos) {
         if (pos < (uint32_t)kHeavyQueuePerWave) wq[pos] = v;
@@ -103,12 +115,30 @@ __global__ __launch_bounds__(kStreamThreads) void k_heavy_collect(const float* _
         if (i % (uint32_t)kHeavyQueuePerWave < s_wq[i / (uint32_t)kHeavyQueuePerWave]) {
             bk[k] = band_bucket(fs, q[i]);
             rk[k] = atomicAdd(&lcnt[bk[k]], 1u);
+            const uint32_t key = f2key(q[i]);
+            atomicMin(&lmin[bk[k]], key);
+            atomicMax(&lmax[bk[k]], key);
         }
     }
     __syncthreads();
-    for (int j = tid; j < nb; j += kStreamThreads) {
-        const uint32_t c = lcnt[j];
-        gbase[j] = c ? atomicAdd(&hfill[j], c) : 0u;
+    // per bucket one returning atomic for the slots and two for the range;
+    // a thread's returning atomics are all issued before any result is used
+    constexpr int BPT = kMaxBuckets / kStreamThreads;
+    uint32_t got[BPT];
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+        const int j = tid + u * kStreamThreads;
+        const uint32_t c = j < nb ? lcnt[j] : 0u;
+        got[u] = c ? atomicAdd(&hfill[j], c) : 0u;
+        if (c) {
+            atomicMin(&ha.hmin[j], lmin[j]);
+            atomicMax(&ha.hmax[j], lmax[j]);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+        const int j = tid + u * kStreamThreads;
+        if (j < nb) gbase[j] = got[u];
     }
     __syncthreads();
 #pragma unroll
@@ -120,18 +150,64 @@ __global__ __launch_bounds__(kStreamThreads) void k_heavy_collect(const float* _
     }
 }
 
-__global__ void k_zero_u32(uint32_t* a, int n) {
-    for (int i = threadIdx.x; i < n; i += blockDim.x) a[i] = 0u;
+// One workgroup per chunk of kHeavyChunk scores of an overflowed bucket:
+// the two fixed-point sums of the chunk, taken against the bucket's score
+// range (known once the collect pass is done), written as four 64-bit words.
+// The bucket aggregation adds a bucket's chunks (integer addition: the order
+// does not matter).  A persistent grid walks the chunks.
+__global__ __launch_bounds__(kStreamThreads) void k_heavy_agg(const uint32_t* __restrict__ base,
+                                                              const uint32_t* __restrict__ bucket_cnt,
+                                                              const Ctl* ctl, HeavyArrays ha, double inv_t) {
+    __shared__ uint32_t s_ch0[kMaxBuckets + 1];
+    __shared__ unsigned long long s_fx[4 * (kStreamThreads / 64)];
+    if (!(ctl->flags & kFlagHeavy)) return;
+    const int tid = threadIdx.x;
+    const int nb = ctl->nb;
+    const uint32_t nch = ctl->hchunks;
+    if ((uint32_t)blockIdx.x >= nch) return;
+    for (int i = tid; i < nb; i += kStreamThreads) s_ch0[i] = ha.hch0[i];
+    if (tid == 0) s_ch0[nb] = nch;
+    __syncthreads();
+    constexpr int E = kHeavyChunk / kStreamThreads;
+    for (uint32_t j = blockIdx.x; j < nch; j += gridDim.x) {
+        // the bucket whose chunk range holds j: the first b with s_ch0[b + 1] > j
+        int lo = 0, hi = nb - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (s_ch0[mid + 1] > j) hi = mid;
+            else lo = mid + 1;
+        }
+        const int b = lo;
+        const uint32_t c = bucket_cnt[b];
+        const uint32_t start = (j - s_ch0[b]) * (uint32_t)kHeavyChunk;
+        const uint32_t* vals = base + ha.hoff[b];
+        const double vmin = (double)key2f(ha.hmin[b]), vmax = (double)key2f(ha.hmax[b]);
+        Fx128 P = fx_zero(), Q = fx_zero();
+#pragma unroll
+        for (int q = 0; q < E; ++q) {
+            const uint32_t i = start + (uint32_t)tid + (uint32_t)q * kStreamThreads;
+            if (i < c) {
+                const double v = (double)key2f(f2key(__uint_as_float(vals[i])));
+                fx_add_term(P, exp((v - vmax) * inv_t));
+                fx_add_term(Q, exp((vmin - v) * inv_t));
+            }
+        }
+        block_sum_fx2<kStreamThreads>(P, Q, s_fx);
+        if (tid == 0) {
+            unsigned long long* o = ha.hpart + 4ull * j;
+            o[0] = P.lo; o[1] = P.hi; o[2] = Q.lo; o[3] = Q.hi;
+        }
+    }
 }
 
 void launch_heavy_collect(const float* r, long long n, const Ctl* ctl, const float* sp, const float* iw,
-                          const uint32_t* hoff, uint32_t* hfill, uint32_t* base, hipStream_t st) {
-    hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(1024), 0, st, hfill, kMaxBuckets);
+                          const HeavyArrays& ha, uint32_t* base, uint32_t hchunks, double t, hipStream_t st) {
     const bool vec = (reinterpret_cast<uintptr_t>(r) & 15u) == 0u;
     const long long tiles = stream_tiles<kHeavyV>(n >> 2);
     const int blocks = vec ? (int)std::max<long long>(1, std::min<long long>(tiles, kHeavyGrid)) : stream_blocks(n);
-    hipLaunchKernelGGL(k_heavy_collect, dim3(blocks), dim3(kStreamThreads), 0, st, r, n, ctl, sp, iw, hoff, hfill,
-                       base);
+    hipLaunchKernelGGL(k_heavy_collect, dim3(blocks), dim3(kStreamThreads), 0, st, r, n, ctl, sp, iw, ha, base);
+    const int ablocks = (int)std::max<uint32_t>(1u, std::min<uint32_t>(hchunks, (uint32_t)kHeavyGrid));
+    hipLaunchKernelGGL(k_heavy_agg, dim3(ablocks), dim3(kStreamThreads), 0, st, base, ha.hfill, ctl, ha, 1.0 / t);
 }
 
 }  // namespace lapsum

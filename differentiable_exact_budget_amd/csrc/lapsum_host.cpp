@@ -64,7 +64,7 @@ struct Workspace {
     uint32_t* bucket_vals = nullptr;
     uint32_t* hoff = nullptr;   // per bucket: slot offset of an overflowed bucket's scores, or kNotHeavy
     uint32_t* hfill = nullptr;  // per bucket: scores placed in that slot
-    std::vector<uint32_t> cnt_h, hoff_h;  // host copies (kept alive across async copies)
+    HeavyArrays heavy{};        // the slots of overflowed buckets (laid out on the device)
     SegArrays seg{};
     SolveScratch sc{};
     uint32_t* keysA = nullptr;
@@ -85,7 +85,8 @@ long long tiles_for(long long n) { return (n + kRadixTile - 1) / kRadixTile; }
 
 // layout of one workspace for forwards up to n_cap scores
 struct Layout {
-    size_t ctl, part, sample, sample_idx, sp, iw, bcnt, bvals, hoff, hfill, eU, eW, wide, seg_first, seg_last, seg_P, seg_Bx, seg_cnt, seg_off,
+    size_t ctl, part, sample, sample_idx, sp, iw, bcnt, bvals, hoff, hfill, hmin, hmax, hch0, hpart, eU, eW, wide,
+        seg_first, seg_last, seg_P, seg_Bx, seg_cnt, seg_off,
         sc_pk, sc_pv, sc_bk, sc_bv, sc_bfx, sc_rank, sc_eP, sc_eB, keysA, keysB, hist, goff, status, total;
     size_t status_bytes;
 };
@@ -106,6 +107,13 @@ Layout make_layout(long long n_cap) {
     L.bvals = take(sizeof(uint32_t) * (size_t)kMaxBuckets * kBucketCapMax);
     L.hoff = take(sizeof(uint32_t) * kMaxBuckets);
     L.hfill = take(sizeof(uint32_t) * kMaxBuckets);
+    L.hmin = take(sizeof(uint32_t) * kMaxBuckets);
+    L.hmax = take(sizeof(uint32_t) * kMaxBuckets);
+    L.hch0 = take(sizeof(uint32_t) * kMaxBuckets);
+    // overflowed buckets hold at most n_cap scores: at most n_cap / chunk + one
+    // partial chunk per bucket
+    L.hpart = take(sizeof(unsigned long long) * 4 *
+                   (size_t)(std::max<long long>(n_cap, 1) / kHeavyChunk + kMaxBuckets + 1));
     L.eU = 0; L.eW = 0; L.wide = 0;
     L.seg_first = take(sizeof(float) * nseg);
     L.seg_last = take(sizeof(float) * nseg);
@@ -172,6 +180,14 @@ lapsum_status_t alloc_ws(Workspace* w, long long n_cap) {
                          reinterpret_cast<double*>(base + L.sc_eP), reinterpret_cast<double*>(base + L.sc_eB)};
     w->keysA = reinterpret_cast<uint32_t*>(base + L.keysA);
     w->keysB = reinterpret_cast<uint32_t*>(base + L.keysB);
+    w->heavy.hoff = w->hoff;
+    w->heavy.hfill = w->hfill;
+    w->heavy.hmin = reinterpret_cast<uint32_t*>(base + L.hmin);
+    w->heavy.hmax = reinterpret_cast<uint32_t*>(base + L.hmax);
+    w->heavy.hch0 = reinterpret_cast<uint32_t*>(base + L.hch0);
+    w->heavy.hpart = reinterpret_cast<unsigned long long*>(base + L.hpart);
+    w->heavy.base_off = (unsigned long long)(w->keysB - w->bucket_vals);
+    w->heavy.cap_total = (unsigned long long)std::max<long long>(n_cap, 1);
     w->hist_part = reinterpret_cast<uint32_t*>(base + L.hist);
     w->goff = reinterpret_cast<uint32_t*>(base + L.goff);
     w->status = reinterpret_cast<unsigned long long*>(base + L.status);
@@ -417,34 +433,23 @@ lapsum_status_t fill_stats(Workspace* w, hipStream_t st, long long n, lapsum_sta
     return LAPSUM_OK;
 }
 
-// Buckets that overflowed (more band scores than their capacity; the counts
-// and sums stay exact): give each one a slot in keysB sized by its exact
-// count and collect its scores with one more pass over r.  Returns false when
-// the slots would not fit (the caller then takes the full-sort fallback).
-bool heavy_buckets(Workspace* w, const float* r, long long n, int nb, int cap, hipStream_t st,
-                   long long* max_heavy) {
-    w->cnt_h.assign((size_t)nb, 0u);
-    if (hipMemcpyAsync(w->cnt_h.data(), w->bucket_cnt, sizeof(uint32_t) * (size_t)nb, hipMemcpyDeviceToHost, st) !=
-            hipSuccess ||
-        hipStreamSynchronize(st) != hipSuccess)
-        return false;
-    const unsigned long long base_off = (unsigned long long)(w->keysB - w->bucket_vals);
-    w->hoff_h.assign((size_t)kMaxBuckets, kNotHeavy);
-    unsigned long long tot = 0;
-    *max_heavy = 0;
-    for (int b = 0; b < nb; ++b) {
-        if (w->cnt_h[(size_t)b] > (uint32_t)cap) {
-            w->hoff_h[(size_t)b] = (uint32_t)(base_off + tot);
-            tot += w->cnt_h[(size_t)b];
-            *max_heavy = std::max<long long>(*max_heavy, w->cnt_h[(size_t)b]);
-            if (base_off + tot >= 0xFFFFFFFFull || tot > (unsigned long long)w->n_cap) return false;
+// Waits for the band solve's root summary (written when the host asked for
+// it: the root may lie in a bucket too large for LDS).
+lapsum_status_t wait_root(Workspace* w, hipStream_t st, unsigned int seq) {
+    volatile unsigned int* flag = &w->hs->root_seq;
+    auto t0 = std::chrono::steady_clock::now();
+    for (unsigned long it = 0;; ++it) {
+        if (*flag == seq) { std::atomic_thread_fence(std::memory_order_acquire); return LAPSUM_OK; }
+        if ((it & 4095u) == 4095u && std::chrono::steady_clock::now() - t0 > std::chrono::milliseconds(2)) {
+            hipError_t e = hipStreamQuery(st);
+            if (e == hipSuccess) {
+                if (*flag == seq) { std::atomic_thread_fence(std::memory_order_acquire); return LAPSUM_OK; }
+                return LAPSUM_ERR_INTERNAL;
+            }
+            if (e != hipErrorNotReady) return LAPSUM_ERR_HIP;
+            if (std::chrono::steady_clock::now() - t0 > std::chrono::seconds(120)) return LAPSUM_ERR_INTERNAL;
         }
     }
-    if (hipMemcpyAsync(w->hoff, w->hoff_h.data(), sizeof(uint32_t) * kMaxBuckets, hipMemcpyHostToDevice, st) !=
-        hipSuccess)
-        return false;
-    launch_heavy_collect(r, n, w->ctl, w->sp, w->iw, w->hoff, w->hfill, w->bucket_vals, st);
-    return hipGetLastError() == hipSuccess;
 }
 
 lapsum_status_t forward_impl(const float* r, int64_t n, double k, float t_f, float* p, double* b_out,
@@ -512,7 +517,7 @@ lapsum_status_t forward_impl(const float* r, int64_t n, double k, float t_f, flo
         const unsigned int seq = ++w->seq;
         tm.begin("filter");
         launch_filter(r, n, t, w->ctl, w->sp, w->iw, w->bucket_cnt, w->bucket_vals, cap, w->part, nullptr,
-                      w->hs_dev, seq, st, k);
+                      w->hs_dev, seq, st, k, &w->heavy);
         tm.end();
         if (path != LAPSUM_PATH_FORCE_FALLBACK) {
             // launched before the host has the verdict: they run only when the
@@ -582,32 +587,42 @@ lapsum_status_t forward_impl(const float* r, int64_t n, double k, float t_f, flo
         }
         return LAPSUM_OK;
     }
+    // Overflowed buckets: the finalize kernel laid out a slot for each (flag
+    // kFlagHeavy) unless they would not fit; one more pass over r fills the
+    // slots and sums their aggregates in chunks, with no host round trip.
     long long max_heavy = 0;
     bool heavy = false;
     if (!fallback && br.overflow) {
-        tm.begin("heavy_collect");
-        heavy = heavy_buckets(w, r, n, br.h.nb, cap, st, &max_heavy);
-        tm.end();
-        if (!heavy) fallback = true;
+        if (br.h.flags & kFlagHeavy) {
+            heavy = true;
+            max_heavy = (long long)br.h.max_bucket;
+            tm.begin("heavy_collect");
+            launch_heavy_collect(r, n, w->ctl, w->sp, w->iw, w->heavy, w->bucket_vals, br.h.hchunks, t, st);
+            tm.end();
+        } else {
+            fallback = true;
+        }
     }
     if (fallback) {
         run_full(w, r, n, k, t, b_out, st, tm);
     } else {
+        // the root may lie in a bucket too large for the LDS sort: then the
+        // band root hands it over (flag, carries as tails, slot offset) and
+        // the host sorts that bucket and solves over it
+        const bool may_be_big = heavy && max_heavy > kBucketCapMax;
+        const unsigned int rseq = may_be_big ? ++w->seq : 0u;
         tm.begin("bucket_solve");
         launch_bucket_solve(w->bucket_vals, w->bucket_cnt, cap, br.h.nb, w->ctl, w->seg, w->sc, k, t, b_out, st,
-                            heavy ? w->hoff : nullptr);
+                            heavy ? &w->heavy : nullptr, nullptr, may_be_big ? w->hs_dev : nullptr, rseq);
         tm.end();
-        if (heavy && max_heavy > kBucketCapMax) {
-            // the root may lie in a bucket too large for the LDS sort: then the
-            // band root handed it over (flag, carries as tails); sort it and solve
-            Ctl c;
-            if (hipMemcpyAsync(&c, w->ctl, sizeof(Ctl), hipMemcpyDeviceToHost, st) != hipSuccess ||
-                hipStreamSynchronize(st) != hipSuccess)
-                return LAPSUM_ERR_HIP;
-            if (c.flags & kFlagBigRoot) {
-                const size_t bkt = (size_t)c.jstar;
-                const unsigned long long cnt = c.m;
-                const float* src = reinterpret_cast<const float*>(w->bucket_vals + w->hoff_h[bkt]);
+        if (may_be_big) {
+            if (hipGetLastError() != hipSuccess) return LAPSUM_ERR_HIP;
+            lapsum_status_t rs = wait_root(w, st, rseq);
+            if (rs != LAPSUM_OK) return rs;
+            const int rflags = w->hs->root_flags;
+            if (rflags & kFlagBigRoot) {
+                const unsigned long long cnt = w->hs->root_m;
+                const float* src = reinterpret_cast<const float*>(w->bucket_vals + w->hs->root_off);
                 tm.begin("root_bucket_sort");
                 sort_keys(w, src, (long long)cnt, st);
                 tm.end();

@@ -25,7 +25,8 @@ int stream_blocks(long long n);
 // k: the budget the finalize kernel certifies the bracket against
 void launch_filter(const float* r, long long n, double t, Ctl* ctl, const float* sp, const float* iw,
                    uint32_t* bucket_cnt, uint32_t* bucket_vals, int cap, double* part, unsigned long long* partc,
-                   HostSummary* hs_dev, unsigned int seq, hipStream_t st, double k);
+                   HostSummary* hs_dev, unsigned int seq, hipStream_t st, double k,
+                   const HeavyArrays* ha = nullptr);
 // returns the number of partials it left (for launch_sum_p)
 // gate (device, may be null): when it holds 0 the kernels return at once
 int launch_probs(const float* r, long long n, double t, float* p, Ctl* ctl, double* part, hipStream_t st,
@@ -50,8 +51,11 @@ void launch_bucket_pick(const uint32_t* bucket_vals, const uint32_t* bucket_cnt,
 void launch_mask(const float* r, long long n, const Ctl* ctl, float* mask, hipStream_t st);
 
 // lapsum_heavy.hip
+// collect every score of the overflowed buckets into their slots, then the
+// chunk sums of their aggregates (both run only when the finalize kernel set
+// kFlagHeavy; hchunks bounds the aggregation grid)
 void launch_heavy_collect(const float* r, long long n, const Ctl* ctl, const float* sp, const float* iw,
-                          const uint32_t* hoff, uint32_t* hfill, uint32_t* base, hipStream_t st);
+                          const HeavyArrays& ha, uint32_t* base, uint32_t hchunks, double t, hipStream_t st);
 
 // lapsum_batched.hip
 int rows_supported_max();
@@ -64,9 +68,12 @@ void launch_rows_vjp(const float* r, const float* g, long long rows, int n, doub
 void launch_small_solve(const float* r, int n, double k, double t, Ctl* ctl, SolveScratch sc, double* b_out,
                         uint32_t* keys_out, hipStream_t s);
 // hoff: null, or per bucket the slot offset of an overflowed bucket's scores (kNotHeavy otherwise)
+// ha: the overflowed buckets' slots (null: none); gate: run only when *gate
+// is nonzero; hs / seq: tell the host through the pinned summary when done
 void launch_bucket_solve(uint32_t* bucket_vals, const uint32_t* bucket_cnt, int cap, int nb, Ctl* ctl, SegArrays seg,
                          SolveScratch sc, double k, double t, double* b_out, hipStream_t s,
-                         const uint32_t* hoff = nullptr, const int* gate = nullptr);
+                         const HeavyArrays* ha = nullptr, const int* gate = nullptr, HostSummary* hs = nullptr,
+                         unsigned int seq = 0);
 int radix_hist_blocks(long long n);
 bool radix_uses_onesweep(long long n);  // else the split passes (counts, scan, scatter)
 void launch_radix_sort(const float* r, long long n, uint32_t* keysA, uint32_t* keysB, uint32_t* hist_part,

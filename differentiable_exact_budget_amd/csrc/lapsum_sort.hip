@@ -96,7 +96,8 @@ constexpr int kAggThreads = 256;
 // bucket_vals of the slot holding all of an overflowed bucket's scores
 __global__ __launch_bounds__(kAggThreads) void k_bucket_agg(const uint32_t* __restrict__ bucket_vals,
                                                              const uint32_t* bucket_cnt, int cap, SegArrays seg,
-                                                             double inv_t, const uint32_t* hoff, const int* gate) {
+                                                             double inv_t, HeavyArrays ha, int heavy,
+                                                             const int* gate) {
     constexpr int NW = kAggThreads / 64;
     constexpr int R = 4;  // scores a thread keeps in registers; a larger bucket is read twice
     __shared__ uint32_t s_mm[2 * NW];
@@ -104,11 +105,33 @@ __global__ __launch_bounds__(kAggThreads) void k_bucket_agg(const uint32_t* __re
     if (gate && *gate == 0) return;  // launched ahead of a certification that failed
     const int tid = threadIdx.x, w = tid >> 6;
     const int bkt = blockIdx.x;
-    const uint32_t ho = hoff ? hoff[bkt] : kNotHeavy;
+    const uint32_t ho = heavy ? ha.hoff[bkt] : kNotHeavy;
     const int c = ho != kNotHeavy ? (int)bucket_cnt[bkt] : (int)min(bucket_cnt[bkt], (uint32_t)cap);
     const size_t off = ho != kNotHeavy ? (size_t)ho : (size_t)bkt * (size_t)cap;
     if (tid == 0) { seg.cnt[bkt] = (uint32_t)c; seg.off[bkt] = (uint32_t)off; }
     if (c == 0) return;
+    if (ho != kNotHeavy) {
+        // an overflowed bucket: its range from the collect pass, its sums from
+        // the chunk partials (integer sums, any order)
+        const uint32_t j0 = ha.hch0[bkt];
+        const uint32_t nj = ((uint32_t)c + kHeavyChunk - 1) / kHeavyChunk;
+        Fx128 P = fx_zero(), Q = fx_zero();
+        for (uint32_t j = (uint32_t)tid; j < nj; j += kAggThreads) {
+            const unsigned long long* h = ha.hpart + 4ull * (j0 + j);
+            Fx128 y, z;
+            y.lo = h[0]; y.hi = h[1]; z.lo = h[2]; z.hi = h[3];
+            P = fx_add(P, y);
+            Q = fx_add(Q, z);
+        }
+        block_sum_fx2<kAggThreads>(P, Q, s_fx);
+        if (tid == 0) {
+            seg.first[bkt] = key2f(ha.hmin[bkt]);
+            seg.last[bkt] = key2f(ha.hmax[bkt]);
+            seg.P[bkt] = fx_to_double(P);
+            seg.Bx[bkt] = fx_to_double(fx_minus_one(Q));
+        }
+        return;
+    }
     const uint32_t* vals = bucket_vals + off;
     uint32_t kk[R];
     uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
@@ -151,7 +174,8 @@ __global__ __launch_bounds__(kAggThreads) void k_bucket_agg(const uint32_t* __re
 
 __global__ __launch_bounds__(kSortThreads) void k_band_root(const uint32_t* bucket_vals, int nb, Ctl* ctl,
                                                              SegArrays seg, SolveScratch sc, double k, double t,
-                                                             double inv_t, double* b_out, const int* gate) {
+                                                             double inv_t, double* b_out, const int* gate,
+                                                             HostSummary* hs, unsigned int seq) {
     if (gate && *gate == 0) return;  // launched ahead of a certification that failed
     __shared__ uint32_t sortbuf[kBucketCapMax];
     __shared__ float s_k[kSortThreads];
@@ -172,12 +196,21 @@ __global__ __launch_bounds__(kSortThreads) void k_band_root(const uint32_t* buck
             ctl->aL = sc.pk[s]; ctl->S_L = sc.pv[s];
             ctl->aR = sc.bk[s]; ctl->S_R = sc.bv[s];
             ctl->jstar = s;
+            ctl->root_off = seg.off[s];
             atomicOr(&ctl->flags, kFlagBigRoot);
         } else {
             if (!o.ok) atomicOr(&ctl->flags, kFlagInternal);
             ctl->b = o.b;
             ctl->jstar = o.jstar;
             if (b_out) *b_out = o.b;
+        }
+        if (hs) {  // the host waits for this one (a root bucket too large for LDS is its job)
+            hs->root_off = ctl->root_off;
+            hs->root_m = ctl->m;
+            hs->root_flags = ctl->flags;
+            __threadfence_system();
+            hs->root_seq = seq;
+            __threadfence_system();
         }
     }
 }
@@ -572,12 +605,14 @@ void launch_small_solve(const float* r, int n, double k, double t, Ctl* ctl, Sol
 }
 
 void launch_bucket_solve(uint32_t* bucket_vals, const uint32_t* bucket_cnt, int cap, int nb, Ctl* ctl, SegArrays seg,
-                         SolveScratch sc, double k, double t, double* b_out, hipStream_t s, const uint32_t* hoff,
-                         const int* gate) {
-    hipLaunchKernelGGL(k_bucket_agg, dim3(nb), dim3(kAggThreads), 0, s, bucket_vals, bucket_cnt, cap, seg, 1.0 / t,
-                       hoff, gate);
+                         SolveScratch sc, double k, double t, double* b_out, hipStream_t s, const HeavyArrays* ha,
+                         const int* gate, HostSummary* hs, unsigned int seq) {
+    HeavyArrays hv{};
+    if (ha) hv = *ha;
+    hipLaunchKernelGGL(k_bucket_agg, dim3(nb), dim3(kAggThreads), 0, s, bucket_vals, bucket_cnt, cap, seg, 1.0 / t, hv,
+                       ha ? 1 : 0, gate);
     hipLaunchKernelGGL(k_band_root, dim3(1), dim3(kSortThreads), 0, s, bucket_vals, nb, ctl, seg, sc, k, t, 1.0 / t,
-                       b_out, gate);
+                       b_out, gate, hs, seq);
 }
 
 int radix_hist_blocks(long long n) {

@@ -299,26 +299,29 @@ __global__ __launch_bounds__(kStreamThreads) void k_filter(const float* __restri
 __global__ __launch_bounds__(kFinalizeThreads) void k_filter_finalize(const FilterPart* part, int nparts, long long n,
                                                                      Ctl* ctl, const uint32_t* bucket_cnt, int cap,
                                                                      HostSummary* hs, unsigned int seq, double k,
-                                                                     double t) {
-    __shared__ double s_rd[4 * (kFinalizeThreads / 64)];
-    __shared__ unsigned long long s_ru[3 * (kFinalizeThreads / 64)];
-    __shared__ uint32_t s_rm[3 * (kFinalizeThreads / 64)];
+                                                                     double t, HeavyArrays ha) {
+    constexpr int NT = kFinalizeThreads;
+    __shared__ double s_rd[4 * (NT / 64)];
+    __shared__ unsigned long long s_ru[3 * (NT / 64)];
+    __shared__ uint32_t s_rm[3 * (NT / 64)];
+    __shared__ uint32_t s_scr[NT / 64 + 2];
     const int tid = threadIdx.x;
     // every load first (one memory round trip), then combine in a fixed order
-    constexpr int PP = kMaxStreamBlocks / kFinalizeThreads;
+    constexpr int PP = kMaxStreamBlocks / NT;
     FilterPart fp[PP];
 #pragma unroll
     for (int q = 0; q < PP; ++q) {
-        const int b = tid + q * kFinalizeThreads;
+        const int b = tid + q * NT;
         if (b < nparts) fp[q] = part[b];
     }
-    // bucket counts: a thread sums its buckets and keeps their maximum
+    // bucket counts: thread tid holds buckets tid*BQ .. tid*BQ + BQ - 1 (in
+    // order, for the slot layout below)
     const int nbk = ctl->nb;
-    constexpr int BQ = kMaxBuckets / kFinalizeThreads;
+    constexpr int BQ = kMaxBuckets / NT;
     uint32_t bcv[BQ];
 #pragma unroll
     for (int q = 0; q < BQ; ++q) {
-        const int b = tid + q * kFinalizeThreads;
+        const int b = tid * BQ + q;
         bcv[q] = b < nbk ? bucket_cnt[b] : 0u;
     }
     unsigned long long bc = 0ull;
@@ -331,7 +334,7 @@ __global__ __launch_bounds__(kFinalizeThreads) void k_filter_finalize(const Filt
     float amx = 0.0f;
 #pragma unroll
     for (int q = 0; q < PP; ++q) {
-        const int b = tid + q * kFinalizeThreads;
+        const int b = tid + q * NT;
         if (b < nparts) {
             a0 += fp[q].S[0]; a1 += fp[q].S[1]; a2 += fp[q].S[2]; a3 += fp[q].S[3];
             u0 += fp[q].c[0]; u1 += fp[q].c[1];
@@ -342,31 +345,64 @@ __global__ __launch_bounds__(kFinalizeThreads) void k_filter_finalize(const Filt
     double d[4] = {a0, a1, a2, a3};
     unsigned long long u[3] = {u0, u1, bc};
     uint32_t mx[3] = {__float_as_uint(amx), (uint32_t)anynan, bmx};  // |v| >= 0: uint order = float order
-    block_reduce_multi<kFinalizeThreads>(d, u, mx, s_rd, s_ru, s_rm);
+    block_reduce_multi<NT>(d, u, mx, s_rd, s_ru, s_rm);
     const double T0 = d[0], T1 = d[1], T2 = d[2], T3 = d[3];
     const unsigned long long NAN_ = u[0], CR = u[1], M = u[2];
     const int nb = ctl->nb;
+    // the verdict, in every thread (same totals, same arithmetic)
+    int flags = 0;
+    if (mx[1] || !finite_f(__uint_as_float(mx[0]))) flags |= kFlagNonFinite;
+    if (mx[2] > (uint32_t)cap) flags |= kFlagOverflow;
+    const unsigned long long CL = (unsigned long long)n - M - CR - NAN_;
+    const float aLf = ctl->aL, aRf = ctl->aR;
+    const bool finL = finite_f(aLf), finR = finite_f(aRf);
+    const double cross = (finL && finR) ? exp(((double)aLf - (double)aRf) / t) : 0.0;
+    const double gL = finL ? 0.5 * T0 + (double)M - 0.5 * T2 + (double)CR - 0.5 * cross * T1 : (double)(CL + M + CR);
+    const double gR = finR ? 0.5 * cross * T0 + 0.5 * T3 + (double)CR - 0.5 * T1 : 0.0;
+    if (gL >= k && gR < k) flags |= kFlagCertified;
+    // Certified, but some buckets overflowed: lay out a slot per overflowed
+    // bucket (sized by its exact count, in bucket order, from base_off) and
+    // its aggregation chunks, and reset its fill count and score range.
+    unsigned long long htot = 0ull;
+    uint32_t hch = 0u;
+    if (flags == (kFlagCertified | kFlagOverflow) && ha.hoff) {
+        uint32_t hc = 0u, ch = 0u;
+#pragma unroll
+        for (int q = 0; q < BQ; ++q)
+            if (bcv[q] > (uint32_t)cap) { hc += bcv[q]; ch += (bcv[q] + kHeavyChunk - 1) / kHeavyChunk; }
+        uint32_t tot_h = 0u, tot_c = 0u;
+        uint32_t ex_h = block_exclusive_scan<NT>(hc, &tot_h, s_scr);
+        uint32_t ex_c = block_exclusive_scan<NT>(ch, &tot_c, s_scr);
+        htot = tot_h;
+        hch = tot_c;
+        if (ha.base_off + htot < 0xFFFFFFFFull && htot <= ha.cap_total) {
+#pragma unroll
+            for (int q = 0; q < BQ; ++q) {
+                const int b = tid * BQ + q;
+                const bool heavy = bcv[q] > (uint32_t)cap;
+                ha.hoff[b] = heavy ? (uint32_t)(ha.base_off + ex_h) : kNotHeavy;
+                ha.hch0[b] = ex_c;
+                ha.hfill[b] = 0u;
+                ha.hmin[b] = 0xFFFFFFFFu;
+                ha.hmax[b] = 0u;
+                if (heavy) { ex_h += bcv[q]; ex_c += (bcv[q] + kHeavyChunk - 1) / kHeavyChunk; }
+            }
+            flags |= kFlagHeavy;
+        }
+    }
     if (tid == 0) {
-        int flags = 0;
-        if (mx[1] || !finite_f(__uint_as_float(mx[0]))) flags |= kFlagNonFinite;
-        if (mx[2] > (uint32_t)cap) flags |= kFlagOverflow;
-        const unsigned long long CL = (unsigned long long)n - M - CR - NAN_;
         ctl->S_L = T0; ctl->S_R = T1; ctl->B_L = T2; ctl->B_R = T3;
         ctl->c_L = CL; ctl->c_R = CR; ctl->m = M;
-        const float aLf = ctl->aL, aRf = ctl->aR;
-        const bool finL = finite_f(aLf), finR = finite_f(aRf);
-        const double cross = (finL && finR) ? exp(((double)aLf - (double)aRf) / t) : 0.0;
-        const double gL = finL ? 0.5 * T0 + (double)M - 0.5 * T2 + (double)CR - 0.5 * cross * T1 : (double)(CL + M + CR);
-        const double gR = finR ? 0.5 * cross * T0 + 0.5 * T3 + (double)CR - 0.5 * T1 : 0.0;
-        if (gL >= k && gR < k) flags |= kFlagCertified;
         ctl->gate = (flags == kFlagCertified) ? 1 : 0;
         ctl->flags = flags;
+        ctl->hchunks = hch;
         if (hs) {
             hs->c_L = CL; hs->m = M; hs->c_R = CR;
             hs->S_L = T0; hs->S_R = T1; hs->B_L = T2; hs->B_R = T3;
             hs->g_aL = gL; hs->g_aR = gR;
             hs->aL = ctl->aL; hs->aR = ctl->aR;
             hs->flags = flags; hs->nb = nb; hs->max_bucket = mx[2];
+            hs->heavy_total = htot; hs->hchunks = hch;
             __threadfence_system();
             hs->seq = seq;
             __threadfence_system();
@@ -376,7 +412,7 @@ __global__ __launch_bounds__(kFinalizeThreads) void k_filter_finalize(const Filt
 
 void launch_filter(const float* r, long long n, double t, Ctl* ctl, const float* sp, const float* iw,
                    uint32_t* bucket_cnt, uint32_t* bucket_vals, int cap, double* part, unsigned long long* /*partc*/,
-                   HostSummary* hs_dev, unsigned int seq, hipStream_t st, double k) {
+                   HostSummary* hs_dev, unsigned int seq, hipStream_t st, double k, const HeavyArrays* ha) {
     const float ls = (float)(1.4426950408889634 / t);
     FilterPart* fp = reinterpret_cast<FilterPart*>(part);
     const bool vec = (reinterpret_cast<uintptr_t>(r) & 15u) == 0u;
@@ -387,8 +423,10 @@ void launch_filter(const float* r, long long n, double t, Ctl* ctl, const float*
     else
         hipLaunchKernelGGL(k_filter<false>, dim3(blocks), dim3(kStreamThreads), 0, st, r, n, ls, ctl, sp, iw,
                            bucket_cnt, bucket_vals, cap, fp);
+    HeavyArrays hv{};
+    if (ha) hv = *ha;
     hipLaunchKernelGGL(k_filter_finalize, dim3(1), dim3(kFinalizeThreads), 0, st, fp, blocks, n, ctl, bucket_cnt, cap,
-                       hs_dev, seq, k, t);
+                       hs_dev, seq, k, t, hv);
 }
 
 // ---------------------------------------------------------------------------
