@@ -311,13 +311,23 @@ LS_DEV unsigned long long st_pack(uint32_t epoch, unsigned long long flag, uint3
     return ((unsigned long long)epoch << 34) | (flag << 32) | (unsigned long long)v;
 }
 
-__global__ __launch_bounds__(kRadixThreads) void k_radix_pass(const uint32_t* __restrict__ in, int in_is_float,
-                                                               uint32_t* __restrict__ out, long long n, int pass,
-                                                               unsigned long long* status, uint32_t epoch,
-                                                               const uint32_t* goff, Ctl* ctl) {
-    constexpr int NW = kRadixThreads / 64;
+// 1024 threads per 4096-key tile: each wave ranks four rows of 64 keys, so
+// the serial chain of counter updates is four long, not sixteen.  All tiles
+// of a pass run at once, so a tile adds up its predecessors' counts until it
+// meets an inclusive prefix, several predecessors per round trip (measured
+// on gfx950: 8 beats 1 and 32; 8192-key tiles gain nothing)
+constexpr int kPassThreads = 1024;
+constexpr int kPassItems = 4;
+constexpr int kPassTile = kPassThreads * kPassItems;
+constexpr int kLookWindow = 8;  // predecessors' status words read per round trip
+
+__global__ __launch_bounds__(kPassThreads) void k_radix_pass(const uint32_t* __restrict__ in, int in_is_float,
+                                                              uint32_t* __restrict__ out, long long n, int pass,
+                                                              unsigned long long* status, uint32_t epoch,
+                                                              const uint32_t* goff, Ctl* ctl) {
+    constexpr int NW = kPassThreads / 64;
     __shared__ uint32_t cnt[256 * NW];
-    __shared__ uint32_t stage[kRadixTile];
+    __shared__ uint32_t stage[kPassTile];
     __shared__ uint32_t loc[256];
     __shared__ uint32_t gbase[256];
     __shared__ uint32_t scr[NW + 2];
@@ -325,23 +335,23 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_pass(const uint32_t* __
     const int tid = threadIdx.x, w = tid >> 6, lane = lane_id();
     const int shift = 8 * pass;
     if (tid == 0) s_tile = atomicAdd(&ctl->tile_ctr[pass], 1u);
-    for (int e = tid; e < 256 * NW; e += kRadixThreads) cnt[e] = 0u;
+    for (int e = tid; e < 256 * NW; e += kPassThreads) cnt[e] = 0u;
     __syncthreads();
     const uint32_t tile = s_tile;
-    const long long base = (long long)tile * kRadixTile;
-    uint32_t kr[kRadixItems];
-    uint32_t rk[kRadixItems];
+    const long long base = (long long)tile * kPassTile;
+    uint32_t kr[kPassItems];
+    uint32_t rk[kPassItems];
 #pragma unroll
-    for (int i = 0; i < kRadixItems; ++i) {
-        const long long idx = base + (long long)((w * kRadixItems + i) * 64 + lane);
+    for (int i = 0; i < kPassItems; ++i) {
+        const long long idx = base + (long long)((w * kPassItems + i) * 64 + lane);
         uint32_t key = 0u;
         if (idx < n) key = in_is_float ? f2key(__uint_as_float(in[idx])) : in[idx];
         kr[i] = key;
     }
     volatile uint32_t* vc = cnt;
 #pragma unroll
-    for (int i = 0; i < kRadixItems; ++i) {
-        const long long idx = base + (long long)((w * kRadixItems + i) * 64 + lane);
+    for (int i = 0; i < kPassItems; ++i) {
+        const long long idx = base + (long long)((w * kPassItems + i) * 64 + lane);
         const bool valid = idx < n;
         const unsigned long long act = ballot(valid);
         rk[i] = 0u;
@@ -354,48 +364,65 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_pass(const uint32_t* __
         }
     }
     __syncthreads();
-    // thread d: per-wave exclusive offsets and the tile total of digit d
-    const int d = tid;  // kRadixThreads == 256
+    // thread d < 256: per-wave exclusive offsets and the tile total of digit d
+    const int d = tid;
     uint32_t tot = 0u;
+    if (d < 256) {
 #pragma unroll
-    for (int q = 0; q < NW; ++q) { const uint32_t x = cnt[d * NW + q]; cnt[d * NW + q] = tot; tot += x; }
-    uint32_t dex = block_exclusive_scan<kRadixThreads>(tot, nullptr, scr);
-    loc[d] = dex;
-    // decoupled look-back on digit d
-    unsigned long long* st = status + (size_t)tile * 256 + d;
-    if (tile == 0) {
-        __hip_atomic_store(st, st_pack(epoch, kStInc, tot), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        gbase[d] = goff[pass * 256 + d];
-    } else {
-        __hip_atomic_store(st, st_pack(epoch, kStAgg, tot), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        uint32_t excl = 0u;
-        long long j = (long long)tile - 1;
-        unsigned int spins = 0u;
-        while (j >= 0) {
-            const unsigned long long s = __hip_atomic_load(status + (size_t)j * 256 + d, __ATOMIC_RELAXED,
-                                                           __HIP_MEMORY_SCOPE_AGENT);
-            const uint32_t ep = (uint32_t)(s >> 34);
-            const unsigned long long fl = (s >> 32) & 3ull;
-            if (ep != epoch || fl == 0ull) {
-                // tiles are handed out in order, so the predecessor is resident and
-                // publishes within microseconds; a bounded wait turns a broken
-                // invariant into a reported error instead of a hang
-                if (++spins > (1u << 24)) { atomicOr(&ctl->flags, kFlagInternal); break; }
-                __builtin_amdgcn_s_sleep(1);
-                continue;
+        for (int q = 0; q < NW; ++q) { const uint32_t x = cnt[d * NW + q]; cnt[d * NW + q] = tot; tot += x; }
+    }
+    const uint32_t dex = block_exclusive_scan<kPassThreads>(tot, nullptr, scr);
+    if (d < 256) {
+        loc[d] = dex;
+        // decoupled look-back on digit d, up to kLookWindow predecessors per
+        // round trip: aggregates are added until an inclusive prefix ends it
+        unsigned long long* st = status + (size_t)tile * 256 + d;
+        if (tile == 0) {
+            __hip_atomic_store(st, st_pack(epoch, kStInc, tot), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            gbase[d] = goff[pass * 256 + d];
+        } else {
+            __hip_atomic_store(st, st_pack(epoch, kStAgg, tot), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            uint32_t excl = 0u;
+            long long j = (long long)tile - 1;
+            unsigned int spins = 0u;
+            bool done = false;
+            while (!done && j >= 0) {
+                unsigned long long sw[kLookWindow];
+#pragma unroll
+                for (int q = 0; q < kLookWindow; ++q)
+                    sw[q] = (j - q >= 0) ? __hip_atomic_load(status + (size_t)(j - q) * 256 + d, __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_AGENT)
+                                         : 0ull;
+                int used = 0;
+#pragma unroll
+                for (int q = 0; q < kLookWindow; ++q) {
+                    if (done || used < q || j - q < 0) continue;  // stop at the first word not yet usable
+                    const unsigned long long sq = sw[q];
+                    const uint32_t ep = (uint32_t)(sq >> 34);
+                    const unsigned long long fl = (sq >> 32) & 3ull;
+                    if (ep != epoch || fl == 0ull) continue;
+                    excl += (uint32_t)sq;
+                    used = q + 1;
+                    if (fl == kStInc) done = true;
+                }
+                j -= used;
+                if (!done && used == 0) {
+                    // tiles are handed out in order, so the predecessor is
+                    // resident and publishes within microseconds; a bounded
+                    // wait turns a broken invariant into a reported error
+                    if (++spins > (1u << 24)) { atomicOr(&ctl->flags, kFlagInternal); break; }
+                    __builtin_amdgcn_s_sleep(1);
+                }
             }
-            excl += (uint32_t)s;
-            if (fl == kStInc) break;
-            --j;
+            __hip_atomic_store(st, st_pack(epoch, kStInc, excl + tot), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            gbase[d] = goff[pass * 256 + d] + excl;
         }
-        __hip_atomic_store(st, st_pack(epoch, kStInc, excl + tot), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        gbase[d] = goff[pass * 256 + d] + excl;
     }
     __syncthreads();
     // local scatter into LDS in digit order, then coalesced runs to global
 #pragma unroll
-    for (int i = 0; i < kRadixItems; ++i) {
-        const long long idx = base + (long long)((w * kRadixItems + i) * 64 + lane);
+    for (int i = 0; i < kPassItems; ++i) {
+        const long long idx = base + (long long)((w * kPassItems + i) * 64 + lane);
         if (idx < n) {
             const uint32_t dd = (kr[i] >> shift) & 0xFFu;
             stage[loc[dd] + cnt[dd * NW + w] + rk[i]] = kr[i];
@@ -403,11 +430,11 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_pass(const uint32_t* __
     }
     __syncthreads();
     const long long rem = n - base;
-    const int tcount = rem < kRadixTile ? (int)rem : kRadixTile;
-    for (int j = tid; j < tcount; j += kRadixThreads) {
-        const uint32_t key = stage[j];
+    const int tcount = rem < kPassTile ? (int)rem : kPassTile;
+    for (int jj = tid; jj < tcount; jj += kPassThreads) {
+        const uint32_t key = stage[jj];
         const uint32_t dd = (key >> shift) & 0xFFu;
-        out[(size_t)gbase[dd] + (size_t)(j - (int)loc[dd])] = key;
+        out[(size_t)gbase[dd] + (size_t)(jj - (int)loc[dd])] = key;
     }
 }
 
@@ -641,8 +668,9 @@ void launch_radix_sort(const float* r, long long n, uint32_t* keysA, uint32_t* k
     for (int p = 0; p < 4; ++p) {
         const int is_float = p == 0 ? 1 : 0;
         if (T <= kOnesweepMaxTiles) {
-            hipLaunchKernelGGL(k_radix_pass, dim3((unsigned)T), dim3(kRadixThreads), 0, s, src, is_float, dst, n, p,
-                               status, epoch_base + (uint32_t)p, goff, ctl);
+            const unsigned Tp = (unsigned)((n + kPassTile - 1) / kPassTile);
+            hipLaunchKernelGGL(k_radix_pass, dim3(Tp), dim3(kPassThreads), 0, s, src, is_float, dst, n, p, status,
+                               epoch_base + (uint32_t)p, goff, ctl);
         } else {
             hipLaunchKernelGGL(k_radix_count, dim3((unsigned)T), dim3(kRadixThreads), 0, s, src, is_float, n, p,
                                counts, T);
