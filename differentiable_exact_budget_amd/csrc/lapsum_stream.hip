@@ -49,9 +49,15 @@ constexpr int kQueuePerWave = kQueueCap / (kStreamThreads / 64);  // each wave a
 
 // Launch shapes of the tiled passes (tile = kStreamThreads * V float4).  The
 // filter ends every workgroup with an LDS queue flush and a reduction, so a
-// bounded number of workgroups walk the tiles; the light passes run one tile
-// per workgroup up to the partials' capacity.
+// bounded number of workgroups walk the tiles (kFilterGrid with a fixed
+// stride when the input is misaligned or tiny); the light passes run one
+// tile per workgroup up to the partials' capacity.
 constexpr int kFilterV = 4, kFilterGrid = 1536;
+// One 1024-thread workgroup per CU whose waves take wave tiles at run time
+// (measured on gfx950: with several workgroups per CU and a fixed share each,
+// the CU serves its older workgroups first and the younger ones finish up to
+// 25% later; 512 or 1024 workgroups, V = 2 or 8 are no better).
+constexpr int kFilterCuThreads = 1024, kFilterCuGrid = 256, kFilterWaveV = 4;
 constexpr int kFinalizeThreads = 256;  // one workgroup: eight filter partials per thread
 constexpr int kProbsV = 2, kProbsGrid = kMaxStreamParts;
 constexpr int kReduceV = 4, kReduceGrid = 8192;
@@ -110,31 +116,40 @@ LS_DEV void band_direct(const FilterState& fs, float v, double& BL, double& BR, 
     if (pos < (uint32_t)fs.cap) fs.bucket_vals[(size_t)bkt * (size_t)fs.cap + pos] = __float_as_uint(v);
 }
 
-template <bool VEC>
-__global__ __launch_bounds__(kStreamThreads) void k_filter(const float* __restrict__ r, long long n, float ls,
+template <bool VEC, int NT, bool DYN>
+__global__ __launch_bounds__(NT) void k_filter(const float* __restrict__ r, long long n, float ls,
                                                             const Ctl* ctl, const float* __restrict__ sp_g,
                                                             const float* __restrict__ iw_g, uint32_t* bucket_cnt,
                                                             uint32_t* bucket_vals, int cap, FilterPart* part) {
     __shared__ float sp[kMaxBuckets + 1];
     __shared__ float iw[kMaxBuckets];
-    __shared__ float q[kQueueCap];
+    constexpr int NWV = NT / 64;
+    constexpr int QCAP = NWV * kQueuePerWave;
+    __shared__ float q[QCAP];
     __shared__ uint32_t lcnt[kMaxBuckets];
     __shared__ uint32_t gbase[kMaxBuckets];
-    __shared__ uint32_t s_wq[kStreamThreads / 64];
-    __shared__ double s_rd[4 * (kStreamThreads / 64)];
-    __shared__ unsigned long long s_ru[2 * (kStreamThreads / 64)];
-    __shared__ uint32_t s_rm[2 * (kStreamThreads / 64)];
+    __shared__ uint32_t s_wq[NWV];
+    __shared__ double s_rd[4 * NWV];
+    __shared__ unsigned long long s_ru[2 * NWV];
+    __shared__ uint32_t s_rm[2 * NWV];
+    __shared__ unsigned int s_ctr;
     const int tid = threadIdx.x;
     const int lane = lane_id();
     FilterState fs;
     fs.aL = ctl->aL; fs.aR = ctl->aR; fs.ls = ls;
     fs.ng = ctl->ng; fs.J = ctl->J; fs.cap = cap;
     const int nb = ctl->nb;
-    for (int i = tid; i <= fs.ng; i += kStreamThreads) sp[i] = sp_g[i];
-    for (int i = tid; i < fs.ng; i += kStreamThreads) iw[i] = iw_g[i];
-    for (int i = tid; i < nb; i += kStreamThreads) lcnt[i] = 0u;
     fs.sp = sp; fs.iw = iw; fs.bucket_cnt = bucket_cnt; fs.bucket_vals = bucket_vals;
-    __syncthreads();
+    // splitters and inverse widths into LDS, counters cleared (the dynamic
+    // walk runs this after issuing each wave's first loads)
+    auto prologue = [&]() {
+        for (int i = tid; i <= fs.ng; i += NT) sp[i] = sp_g[i];
+        for (int i = tid; i < fs.ng; i += NT) iw[i] = iw_g[i];
+        for (int i = tid; i < nb; i += NT) lcnt[i] = 0u;
+        if (tid == 0) s_ctr = 0u;
+        __syncthreads();
+    };
+    if (!(VEC && DYN)) prologue();
 
     // Per score: one exponential, e = e^{-|r - edge|/t} with edge a_L below the
     // band and a_R otherwise; it feeds S_L (below) or S_R (at/above a_R).
@@ -201,23 +216,32 @@ __global__ __launch_bounds__(kStreamThreads) void k_filter(const float* __restri
 
     if (VEC) {
         const long long n4 = n >> 2;
-        tile_f4_pipelined<kFilterV, kFilterNT>(reinterpret_cast<const float4*>(r), n4,
-                     [&](float4 qv, long long) { quad(qv); },
-                     [&](float4 qv, long long) { one_lane(qv.x); one_lane(qv.y); one_lane(qv.z); one_lane(qv.w); });
+        auto main_f = [&](float4 qv, long long) { quad(qv); };
+        auto tail_f = [&](float4 qv, long long) { one_lane(qv.x); one_lane(qv.y); one_lane(qv.z); one_lane(qv.w); };
+        if constexpr (DYN) {
+            // this workgroup's share of the wave tiles, handed to its waves at run time
+            constexpr long long WT = 64LL * kFilterWaveV;
+            const long long tiles = (n4 + WT - 1) / WT;
+            const long long per = (tiles + gridDim.x - 1) / gridDim.x;
+            const long long t0 = min(tiles, (long long)blockIdx.x * per), t1 = min(tiles, t0 + per);
+            wave_tiles_dynamic<kFilterWaveV, kFilterNT>(reinterpret_cast<const float4*>(r), n4, t0, t1, &s_ctr,
+                                                        main_f, tail_f, prologue);
+        } else {
+            tile_f4_pipelined<kFilterV, kFilterNT>(reinterpret_cast<const float4*>(r), n4, main_f, tail_f);
+        }
         if (blockIdx.x == 0 && tid < 4) {
             const long long j = (n4 << 2) + tid;
             if (j < n) one_lane(r[j]);
         }
     } else {
-        const long long stride = (long long)gridDim.x * kStreamThreads;
-        for (long long i = (long long)blockIdx.x * kStreamThreads + tid; i < n; i += stride) one_lane(r[i]);
+        const long long stride = (long long)gridDim.x * NT;
+        for (long long i = (long long)blockIdx.x * NT + tid; i < n; i += stride) one_lane(r[i]);
     }
 
     // ---- flush the LDS queue: bucket by value, one global atomic per bucket ----
     // The wave slices, concatenated, are the workgroup's queue; its item i
     // goes to thread i mod NT, so the usual handful of band scores takes a
     // single pass (one bucket search) instead of one per slice position.
-    constexpr int NWV = kStreamThreads / 64;
     if (lane == 0) s_wq[tid >> 6] = min(wfill, (uint32_t)kQueuePerWave);
     __syncthreads();
     uint32_t qoff[NWV + 1];
@@ -225,14 +249,14 @@ __global__ __launch_bounds__(kStreamThreads) void k_filter(const float* __restri
 #pragma unroll
     for (int w = 0; w < NWV; ++w) qoff[w + 1] = qoff[w] + s_wq[w];
     const uint32_t qn = qoff[NWV];
-    constexpr int QPT = kQueueCap / kStreamThreads;
+    constexpr int QPT = QCAP / NT;
     int bk[QPT];
     uint32_t rk[QPT];
     float qv[QPT];
 #pragma unroll
     for (int k = 0; k < QPT; ++k) {
         bk[k] = -1;
-        const uint32_t i = (uint32_t)tid + (uint32_t)k * kStreamThreads;
+        const uint32_t i = (uint32_t)tid + (uint32_t)k * NT;
         if (i < qn) {
             int w = 0;
 #pragma unroll
@@ -251,18 +275,36 @@ __global__ __launch_bounds__(kStreamThreads) void k_filter(const float* __restri
     }
     __syncthreads();
     // a thread's (up to kMaxBuckets / NT) returning atomics are all in flight
-    // before any result is used: one round trip, not one per bucket
-    constexpr int BPT = kMaxBuckets / kStreamThreads;
+    // before any result is used: one round trip, not one per bucket; the
+    // workgroup's reduction runs while they are in flight
+    constexpr int BPT = (kMaxBuckets + NT - 1) / NT;
     uint32_t got[BPT];
 #pragma unroll
     for (int u = 0; u < BPT; ++u) {
-        const int j = tid + u * kStreamThreads;
+        const int j = tid + u * NT;
         const uint32_t c = j < nb ? lcnt[j] : 0u;
         got[u] = c ? atomicAdd(&bucket_cnt[j], c) : 0u;
     }
+
+    // ---- workgroup partials (fixed-order reduction; reduced by k_filter_finalize) ----
+    {
+        double d[4] = {SL, SR, BL, BR};
+        unsigned long long u[2] = {(unsigned long long)nnan, (unsigned long long)cR};
+        uint32_t m[2] = {__float_as_uint(amax), (uint32_t)nan};  // |v| >= 0: uint order = float order
+        block_reduce_multi<NT>(d, u, m, s_rd, s_ru, s_rm);
+        if (tid == 0) {
+            FilterPart& fp = part[blockIdx.x];
+            fp.S[0] = d[0]; fp.S[1] = d[1]; fp.S[2] = d[2]; fp.S[3] = d[3];
+            fp.c[0] = u[0]; fp.c[1] = u[1];
+            fp.mn = 0.0f;
+            fp.mx = __uint_as_float(m[0]);
+            fp.nan = (int)m[1];
+        }
+    }
+
 #pragma unroll
     for (int u = 0; u < BPT; ++u) {
-        const int j = tid + u * kStreamThreads;
+        const int j = tid + u * NT;
         if (j < nb) gbase[j] = got[u];
     }
     __syncthreads();
@@ -272,20 +314,6 @@ __global__ __launch_bounds__(kStreamThreads) void k_filter(const float* __restri
             const uint32_t pos = gbase[bk[k]] + rk[k];
             if (pos < (uint32_t)cap) bucket_vals[(size_t)bk[k] * (size_t)cap + pos] = __float_as_uint(qv[k]);
         }
-    }
-
-    // ---- workgroup partials (fixed-order reduction; reduced by k_filter_finalize) ----
-    double d[4] = {SL, SR, BL, BR};
-    unsigned long long u[2] = {(unsigned long long)nnan, (unsigned long long)cR};
-    uint32_t m[2] = {__float_as_uint(amax), (uint32_t)nan};  // |v| >= 0: uint order = float order
-    block_reduce_multi<kStreamThreads>(d, u, m, s_rd, s_ru, s_rm);
-    if (tid == 0) {
-        FilterPart& fp = part[blockIdx.x];
-        fp.S[0] = d[0]; fp.S[1] = d[1]; fp.S[2] = d[2]; fp.S[3] = d[3];
-        fp.c[0] = u[0]; fp.c[1] = u[1];
-        fp.mn = 0.0f;
-        fp.mx = __uint_as_float(m[0]);
-        fp.nan = (int)m[1];
     }
 }
 
@@ -416,13 +444,23 @@ void launch_filter(const float* r, long long n, double t, Ctl* ctl, const float*
     const float ls = (float)(1.4426950408889634 / t);
     FilterPart* fp = reinterpret_cast<FilterPart*>(part);
     const bool vec = (reinterpret_cast<uintptr_t>(r) & 15u) == 0u;
-    const int blocks = vec ? tiled_grid<kFilterV>(n >> 2, kFilterGrid) : stream_blocks(n);
-    if (vec)
-        hipLaunchKernelGGL(k_filter<true>, dim3(blocks), dim3(kStreamThreads), 0, st, r, n, ls, ctl, sp, iw,
-                           bucket_cnt, bucket_vals, cap, fp);
-    else
-        hipLaunchKernelGGL(k_filter<false>, dim3(blocks), dim3(kStreamThreads), 0, st, r, n, ls, ctl, sp, iw,
-                           bucket_cnt, bucket_vals, cap, fp);
+    const long long n4 = n >> 2;
+    const bool dyn = vec && n4 >= 64LL * kFilterWaveV;
+    int blocks;
+    if (dyn) {
+        const long long wt = (n4 + 64LL * kFilterWaveV - 1) / (64LL * kFilterWaveV);
+        blocks = (int)std::max<long long>(1, std::min<long long>(kFilterCuGrid, (wt + 15) / 16));
+        hipLaunchKernelGGL((k_filter<true, kFilterCuThreads, true>), dim3(blocks), dim3(kFilterCuThreads), 0, st, r, n,
+                           ls, ctl, sp, iw, bucket_cnt, bucket_vals, cap, fp);
+    } else if (vec) {
+        blocks = tiled_grid<kFilterV>(n4, kFilterGrid);
+        hipLaunchKernelGGL((k_filter<true, kStreamThreads, false>), dim3(blocks), dim3(kStreamThreads), 0, st, r, n,
+                           ls, ctl, sp, iw, bucket_cnt, bucket_vals, cap, fp);
+    } else {
+        blocks = stream_blocks(n);
+        hipLaunchKernelGGL((k_filter<false, kStreamThreads, false>), dim3(blocks), dim3(kStreamThreads), 0, st, r, n,
+                           ls, ctl, sp, iw, bucket_cnt, bucket_vals, cap, fp);
+    }
     HeavyArrays hv{};
     if (ha) hv = *ha;
     hipLaunchKernelGGL(k_filter_finalize, dim3(1), dim3(kFinalizeThreads), 0, st, fp, blocks, n, ctl, bucket_cnt, cap,

@@ -182,6 +182,62 @@ LS_DEV void tile_f4_pipelined(const float4* __restrict__ a, long long n4, Main&&
     }
 }
 
+// Wave tiles of 64 * V float4 handed out at run time inside a workgroup
+// that owns tiles [t0, t1).  Wave w starts on tile t0 + w, issuing its loads
+// before prologue() runs (the workgroup's set-up, which must end with a
+// barrier and is called by every thread); every further tile comes from an
+// LDS counter, claimed one tile ahead (the claim's latency hides behind the
+// current tile) and prefetched before the current one is used.  The waves
+// the CU serves faster take more tiles, so the workgroup's waves finish
+// together.  prologue() must set *s_ctr to 0.  main(v, idx) runs on full
+// tiles (every lane of the wave active); tail(v, idx) on the elements of a
+// partial last tile.  Needs n4 >= 64 * V (a full tile 0 to fall back on).
+template <int V, bool NT, class Main, class Tail, class Prologue>
+LS_DEV void wave_tiles_dynamic(const float4* __restrict__ a, long long n4, long long t0, long long t1,
+                               unsigned int* s_ctr, Main&& main, Tail&& tail, Prologue&& prologue) {
+    constexpr long long T = 64LL * V;
+    const long long lane = lane_id();
+    const long long nw = blockDim.x >> 6;
+    auto claim = [&]() -> unsigned int {
+        unsigned int c = 0u;
+        if (lane == 0) c = atomicAdd(s_ctr, 1u);
+        return c;
+    };
+    auto full = [&](long long t) { return (t + 1) * T <= n4; };
+    long long j = t0 + (long long)(threadIdx.x >> 6);
+    float4 x[V];
+    {
+        const long long src = (j < t1 && full(j)) ? j : 0;  // a partial tile is read in the tail path
+#pragma unroll
+        for (int v = 0; v < V; ++v) x[v] = ld4<NT>(a + src * T + lane + v * 64);
+    }
+    prologue();
+    if (j >= t1) return;
+    unsigned int cn = claim();  // the tile after j
+    while (true) {
+        const long long jn = t0 + nw + (long long)__builtin_amdgcn_readfirstlane(cn);
+        const bool more = jn < t1;  // wave-uniform
+        if (more) cn = claim();
+        const long long pf = (more && full(jn)) ? jn : (full(j) ? j : 0);
+        float4 y[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) y[v] = ld4<NT>(a + pf * T + lane + v * 64);
+        if (full(j)) {
+#pragma unroll
+            for (int v = 0; v < V; ++v) main(x[v], j * T + lane + v * 64);
+        } else {
+            for (int v = 0; v < V; ++v) {
+                const long long i = j * T + lane + v * 64;
+                if (i < n4) tail(a[i], i);
+            }
+        }
+        if (!more) break;
+        j = jn;
+#pragma unroll
+        for (int v = 0; v < V; ++v) x[v] = y[v];
+    }
+}
+
 // the same over two arrays read in lockstep
 template <int V, bool NT, class Main, class Tail>
 LS_DEV void tile_f4x2(const float4* __restrict__ a, const float4* __restrict__ b, long long n4, bool reverse,
