@@ -12,13 +12,18 @@
 
 namespace lapsum {
 
-constexpr int kHeavyQueue = 2048;                            // per workgroup, in LDS
-constexpr int kHeavyQueuePerWave = kHeavyQueue / (kStreamThreads / 64);
-constexpr int kHeavyV = 4, kHeavyGrid = 1024;  // 36 KB of LDS per workgroup: four per CU
+// The collect pass walks r like the filter: one 1024-thread workgroup per CU
+// over a fixed share, its waves taking 1024-score tiles at run time (the
+// misaligned fallback strides over r with the same workgroups)
+constexpr int kHeavyThreads = 1024;
+constexpr int kHeavyQueuePerWave = 512;
+constexpr int kHeavyQueue = kHeavyQueuePerWave * (kHeavyThreads / 64);  // per workgroup, in LDS
+constexpr int kHeavyWaveV = 4, kHeavyGrid = 256;
+constexpr int kHeavyAggGrid = 1024;
 
 // hoff[b]: element offset (from `base`) of heavy bucket b's slot, or
 // kNotHeavy; hfill[b]: scores placed so far (zeroed before the pass)
-__global__ __launch_bounds__(kStreamThreads) void k_heavy_collect(const float* __restrict__ r, long long n,
+__global__ __launch_bounds__(kHeavyThreads) void k_heavy_collect(const float* __restrict__ r, long long n,
                                                                    const Ctl* ctl, const float* __restrict__ sp_g,
                                                                    const float* __restrict__ iw_g, HeavyArrays ha,
                                                                    uint32_t* base) {
@@ -30,7 +35,8 @@ __global__ __launch_bounds__(kStreamThreads) void k_heavy_collect(const float* _
     __shared__ uint32_t gbase[kMaxBuckets];
     __shared__ uint32_t lmin[kMaxBuckets];
     __shared__ uint32_t lmax[kMaxBuckets];
-    __shared__ uint32_t s_wq[kStreamThreads / 64];
+    __shared__ uint32_t s_wq[kHeavyThreads / 64];
+    __shared__ unsigned int s_ctr;
     if (!(ctl->flags & kFlagHeavy)) return;  // no slots were laid out
     const uint32_t* __restrict__ hoff_g = ha.hoff;
     uint32_t* hfill = ha.hfill;
@@ -39,16 +45,19 @@ __global__ __launch_bounds__(kStreamThreads) void k_heavy_collect(const float* _
     fs.aL = ctl->aL; fs.aR = ctl->aR; fs.ls = 0.0f;
     fs.ng = ctl->ng; fs.J = ctl->J; fs.cap = 0;
     const int nb = ctl->nb;
-    for (int i = tid; i <= fs.ng; i += kStreamThreads) sp[i] = sp_g[i];
-    for (int i = tid; i < fs.ng; i += kStreamThreads) iw[i] = iw_g[i];
-    for (int i = tid; i < nb; i += kStreamThreads) {
-        hoff[i] = hoff_g[i];
-        lcnt[i] = 0u;
-        lmin[i] = 0xFFFFFFFFu;
-        lmax[i] = 0u;
-    }
     fs.sp = sp; fs.iw = iw; fs.bucket_cnt = nullptr; fs.bucket_vals = nullptr;
-    __syncthreads();
+    auto prologue = [&]() {
+        for (int i = tid; i <= fs.ng; i += kHeavyThreads) sp[i] = sp_g[i];
+        for (int i = tid; i < fs.ng; i += kHeavyThreads) iw[i] = iw_g[i];
+        for (int i = tid; i < nb; i += kHeavyThreads) {
+            hoff[i] = hoff_g[i];
+            lcnt[i] = 0u;
+            lmin[i] = 0xFFFFFFFFu;
+            lmax[i] = 0u;
+        }
+        if (tid == 0) s_ctr = 0u;
+        __syncthreads();
+    };
     const float aL = fs.aL, aR = fs.aR;
     float* const wq = q + (tid >> 6) * kHeavyQueuePerWave;
     uint32_t wfill = 0u;  // wave-uniform
@@ -87,30 +96,36 @@ __global__ __launch_bounds__(kStreamThreads) void k_heavy_collect(const float* _
         const int bk = heavy_of(v);
         if (bk >= 0) direct(v, bk);
     };
-    if ((reinterpret_cast<uintptr_t>(r) & 15u) == 0u) {
-        const long long n4 = n >> 2;
-        tile_f4_pipelined<kHeavyV, true>(reinterpret_cast<const float4*>(r), n4,
-                                         [&](float4 qv, long long) { quad(qv); },
-                                         [&](float4 qv, long long) {
-                                             one_lane(qv.x); one_lane(qv.y); one_lane(qv.z); one_lane(qv.w);
-                                         });
+    const long long n4 = n >> 2;
+    if ((reinterpret_cast<uintptr_t>(r) & 15u) == 0u && n4 >= 64LL * kHeavyWaveV) {
+        constexpr long long WT = 64LL * kHeavyWaveV;
+        const long long tiles = (n4 + WT - 1) / WT;
+        const long long per = (tiles + gridDim.x - 1) / gridDim.x;
+        const long long t0 = min(tiles, (long long)blockIdx.x * per), t1 = min(tiles, t0 + per);
+        wave_tiles_dynamic<kHeavyWaveV, true>(reinterpret_cast<const float4*>(r), n4, t0, t1, &s_ctr,
+                                              [&](float4 qv, long long) { quad(qv); },
+                                              [&](float4 qv, long long) {
+                                                  one_lane(qv.x); one_lane(qv.y); one_lane(qv.z); one_lane(qv.w);
+                                              },
+                                              prologue);
         if (blockIdx.x == 0 && tid < 4) {
             const long long j = (n4 << 2) + tid;
             if (j < n) one_lane(r[j]);
         }
     } else {
-        const long long stride = (long long)gridDim.x * kStreamThreads;
-        for (long long i = (long long)blockIdx.x * kStreamThreads + tid; i < n; i += stride) one_lane(r[i]);
+        prologue();
+        const long long stride = (long long)gridDim.x * kHeavyThreads;
+        for (long long i = (long long)blockIdx.x * kHeavyThreads + tid; i < n; i += stride) one_lane(r[i]);
     }
     // flush: rank within the workgroup per bucket, one global atomic per bucket
     if (lane == 0) s_wq[tid >> 6] = min(wfill, (uint32_t)kHeavyQueuePerWave);
     __syncthreads();
-    constexpr int QPT = kHeavyQueue / kStreamThreads;
+    constexpr int QPT = kHeavyQueue / kHeavyThreads;
     int bk[QPT];
     uint32_t rk[QPT];
 #pragma unroll
     for (int k = 0; k < QPT; ++k) {
-        const uint32_t i = (uint32_t)tid + (uint32_t)k * kStreamThreads;
+        const uint32_t i = (uint32_t)tid + (uint32_t)k * kHeavyThreads;
         bk[k] = -1;
         if (i % (uint32_t)kHeavyQueuePerWave < s_wq[i / (uint32_t)kHeavyQueuePerWave]) {
             bk[k] = band_bucket(fs, q[i]);
@@ -123,11 +138,11 @@ __global__ __launch_bounds__(kStreamThreads) void k_heavy_collect(const float* _
     __syncthreads();
     // per bucket one returning atomic for the slots and two for the range;
     // a thread's returning atomics are all issued before any result is used
-    constexpr int BPT = kMaxBuckets / kStreamThreads;
+    constexpr int BPT = (kMaxBuckets + kHeavyThreads - 1) / kHeavyThreads;
     uint32_t got[BPT];
 #pragma unroll
     for (int u = 0; u < BPT; ++u) {
-        const int j = tid + u * kStreamThreads;
+        const int j = tid + u * kHeavyThreads;
         const uint32_t c = j < nb ? lcnt[j] : 0u;
         got[u] = c ? atomicAdd(&hfill[j], c) : 0u;
         if (c) {
@@ -137,14 +152,14 @@ __global__ __launch_bounds__(kStreamThreads) void k_heavy_collect(const float* _
     }
 #pragma unroll
     for (int u = 0; u < BPT; ++u) {
-        const int j = tid + u * kStreamThreads;
+        const int j = tid + u * kHeavyThreads;
         if (j < nb) gbase[j] = got[u];
     }
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < QPT; ++k) {
         if (bk[k] >= 0) {
-            const uint32_t i = (uint32_t)tid + (uint32_t)k * kStreamThreads;
+            const uint32_t i = (uint32_t)tid + (uint32_t)k * kHeavyThreads;
             base[(size_t)hoff[bk[k]] + gbase[bk[k]] + rk[k]] = __float_as_uint(q[i]);
         }
     }
@@ -202,11 +217,10 @@ __global__ __launch_bounds__(kStreamThreads) void k_heavy_agg(const uint32_t* __
 
 void launch_heavy_collect(const float* r, long long n, const Ctl* ctl, const float* sp, const float* iw,
                           const HeavyArrays& ha, uint32_t* base, uint32_t hchunks, double t, hipStream_t st) {
-    const bool vec = (reinterpret_cast<uintptr_t>(r) & 15u) == 0u;
-    const long long tiles = stream_tiles<kHeavyV>(n >> 2);
-    const int blocks = vec ? (int)std::max<long long>(1, std::min<long long>(tiles, kHeavyGrid)) : stream_blocks(n);
-    hipLaunchKernelGGL(k_heavy_collect, dim3(blocks), dim3(kStreamThreads), 0, st, r, n, ctl, sp, iw, ha, base);
-    const int ablocks = (int)std::max<uint32_t>(1u, std::min<uint32_t>(hchunks, (uint32_t)kHeavyGrid));
+    const long long wt = ((n >> 2) + 64LL * kHeavyWaveV - 1) / (64LL * kHeavyWaveV);
+    const int blocks = (int)std::max<long long>(1, std::min<long long>(kHeavyGrid, (wt + 15) / 16));
+    hipLaunchKernelGGL(k_heavy_collect, dim3(blocks), dim3(kHeavyThreads), 0, st, r, n, ctl, sp, iw, ha, base);
+    const int ablocks = (int)std::max<uint32_t>(1u, std::min<uint32_t>(hchunks, (uint32_t)kHeavyAggGrid));
     hipLaunchKernelGGL(k_heavy_agg, dim3(ablocks), dim3(kStreamThreads), 0, st, base, ha.hfill, ctl, ha, 1.0 / t);
 }
 
