@@ -516,8 +516,11 @@ lapsum_status_t forward_impl(const float* r, int64_t n, double k, float t_f, flo
         tm.end();
         const unsigned int seq = ++w->seq;
         tm.begin("filter");
-        launch_filter(r, n, t, w->ctl, w->sp, w->iw, w->bucket_cnt, w->bucket_vals, cap, w->part, nullptr,
-                      w->hs_dev, seq, st, k, &w->heavy);
+        const int fparts = launch_filter_pass(r, n, t, w->ctl, w->sp, w->iw, w->bucket_cnt, w->bucket_vals, cap,
+                                              w->part, st);
+        tm.end();
+        tm.begin("finalize");
+        launch_filter_finalize(n, t, w->ctl, w->bucket_cnt, cap, w->part, fparts, w->hs_dev, seq, st, k, &w->heavy);
         tm.end();
         if (path != LAPSUM_PATH_FORCE_FALLBACK) {
             // launched before the host has the verdict: they run only when the

@@ -23,6 +23,13 @@ void launch_select(const float* x, int s, long long l, long long h, int cap, Ctl
 // lapsum_stream.hip
 int stream_blocks(long long n);
 // k: the budget the finalize kernel certifies the bracket against
+// the filter pass alone (returns its workgroup count, the number of
+// partials) and its finalize kernel; launch_filter runs both
+int launch_filter_pass(const float* r, long long n, double t, Ctl* ctl, const float* sp, const float* iw,
+                       uint32_t* bucket_cnt, uint32_t* bucket_vals, int cap, double* part, hipStream_t st);
+void launch_filter_finalize(long long n, double t, Ctl* ctl, const uint32_t* bucket_cnt, int cap, double* part,
+                            int nparts, HostSummary* hs_dev, unsigned int seq, hipStream_t st, double k,
+                            const HeavyArrays* ha);
 void launch_filter(const float* r, long long n, double t, Ctl* ctl, const float* sp, const float* iw,
                    uint32_t* bucket_cnt, uint32_t* bucket_vals, int cap, double* part, unsigned long long* partc,
                    HostSummary* hs_dev, unsigned int seq, hipStream_t st, double k,

@@ -438,9 +438,8 @@ __global__ __launch_bounds__(kFinalizeThreads) void k_filter_finalize(const Filt
     }
 }
 
-void launch_filter(const float* r, long long n, double t, Ctl* ctl, const float* sp, const float* iw,
-                   uint32_t* bucket_cnt, uint32_t* bucket_vals, int cap, double* part, unsigned long long* /*partc*/,
-                   HostSummary* hs_dev, unsigned int seq, hipStream_t st, double k, const HeavyArrays* ha) {
+int launch_filter_pass(const float* r, long long n, double t, Ctl* ctl, const float* sp, const float* iw,
+                       uint32_t* bucket_cnt, uint32_t* bucket_vals, int cap, double* part, hipStream_t st) {
     const float ls = (float)(1.4426950408889634 / t);
     FilterPart* fp = reinterpret_cast<FilterPart*>(part);
     const bool vec = (reinterpret_cast<uintptr_t>(r) & 15u) == 0u;
@@ -461,10 +460,24 @@ void launch_filter(const float* r, long long n, double t, Ctl* ctl, const float*
         hipLaunchKernelGGL((k_filter<false, kStreamThreads, false>), dim3(blocks), dim3(kStreamThreads), 0, st, r, n,
                            ls, ctl, sp, iw, bucket_cnt, bucket_vals, cap, fp);
     }
+    return blocks;
+}
+
+void launch_filter_finalize(long long n, double t, Ctl* ctl, const uint32_t* bucket_cnt, int cap, double* part,
+                            int nparts, HostSummary* hs_dev, unsigned int seq, hipStream_t st, double k,
+                            const HeavyArrays* ha) {
     HeavyArrays hv{};
     if (ha) hv = *ha;
-    hipLaunchKernelGGL(k_filter_finalize, dim3(1), dim3(kFinalizeThreads), 0, st, fp, blocks, n, ctl, bucket_cnt, cap,
-                       hs_dev, seq, k, t, hv);
+    hipLaunchKernelGGL(k_filter_finalize, dim3(1), dim3(kFinalizeThreads), 0, st,
+                       reinterpret_cast<const FilterPart*>(part), nparts, n, ctl, bucket_cnt, cap, hs_dev, seq, k, t,
+                       hv);
+}
+
+void launch_filter(const float* r, long long n, double t, Ctl* ctl, const float* sp, const float* iw,
+                   uint32_t* bucket_cnt, uint32_t* bucket_vals, int cap, double* part, unsigned long long* /*partc*/,
+                   HostSummary* hs_dev, unsigned int seq, hipStream_t st, double k, const HeavyArrays* ha) {
+    const int blocks = launch_filter_pass(r, n, t, ctl, sp, iw, bucket_cnt, bucket_vals, cap, part, st);
+    launch_filter_finalize(n, t, ctl, bucket_cnt, cap, part, blocks, hs_dev, seq, st, k, ha);
 }
 
 // ---------------------------------------------------------------------------
