@@ -56,8 +56,9 @@ constexpr int kFilterV = 4, kFilterGrid = 1536;
 // One 1024-thread workgroup per CU whose waves take wave tiles at run time
 // (measured on gfx950: with several workgroups per CU and a fixed share each,
 // the CU serves its older workgroups first and the younger ones finish up to
-// 25% later; 512 or 1024 workgroups, V = 2 or 8 are no better).
-constexpr int kFilterCuThreads = 1024, kFilterCuGrid = 256, kFilterWaveV = 4;
+// 25% later; 512 or 1024 workgroups are no better, and V = 2 ends the
+// walk with its waves closer together than V = 4 or 8).
+constexpr int kFilterCuThreads = 1024, kFilterCuGrid = 256, kFilterWaveV = 2;
 constexpr int kFinalizeThreads = 256;  // one workgroup: eight filter partials per thread
 constexpr int kProbsV = 2, kProbsGrid = kMaxStreamParts;
 constexpr int kReduceV = 4, kReduceGrid = 8192;
@@ -126,9 +127,9 @@ __global__ __launch_bounds__(NT) void k_filter(const float* __restrict__ r, long
     constexpr int NWV = NT / 64;
     constexpr int QCAP = NWV * kQueuePerWave;
     __shared__ float q[QCAP];
+    __shared__ uint32_t qbr[QCAP];  // per queued score: bucket << 16 | rank in the workgroup's bucket
     __shared__ uint32_t lcnt[kMaxBuckets];
     __shared__ uint32_t gbase[kMaxBuckets];
-    __shared__ uint32_t s_wq[NWV];
     __shared__ double s_rd[4 * NWV];
     __shared__ unsigned long long s_ru[2 * NWV];
     __shared__ uint32_t s_rm[2 * NWV];
@@ -238,45 +239,43 @@ __global__ __launch_bounds__(NT) void k_filter(const float* __restrict__ r, long
         for (long long i = (long long)blockIdx.x * NT + tid; i < n; i += stride) one_lane(r[i]);
     }
 
-    // ---- flush the LDS queue: bucket by value, one global atomic per bucket ----
-    // The wave slices, concatenated, are the workgroup's queue; its item i
-    // goes to thread i mod NT, so the usual handful of band scores takes a
-    // single pass (one bucket search) instead of one per slice position.
-    if (lane == 0) s_wq[tid >> 6] = min(wfill, (uint32_t)kQueuePerWave);
-    __syncthreads();
-    uint32_t qoff[NWV + 1];
-    qoff[0] = 0u;
-#pragma unroll
-    for (int w = 0; w < NWV; ++w) qoff[w + 1] = qoff[w] + s_wq[w];
-    const uint32_t qn = qoff[NWV];
-    constexpr int QPT = QCAP / NT;
-    int bk[QPT];
-    uint32_t rk[QPT];
-    float qv[QPT];
-#pragma unroll
-    for (int k = 0; k < QPT; ++k) {
-        bk[k] = -1;
-        const uint32_t i = (uint32_t)tid + (uint32_t)k * NT;
-        if (i < qn) {
-            int w = 0;
-#pragma unroll
-            for (int x = 1; x < NWV; ++x) w += i >= qoff[x] ? 1 : 0;
-            const float v = q[w * kQueuePerWave + (i - qoff[w])];
-            qv[k] = v;
+    // ---- each wave, right after its own walk: bucket, band sums and a
+    // workgroup-wide rank (LDS atomic) for every score of its queue slice,
+    // then its partial sums into LDS, all before the workgroup barrier ----
+    const uint32_t nq = min(wfill, (uint32_t)kQueuePerWave);  // wave-uniform
+    uint32_t* const wbr = qbr + (tid >> 6) * kQueuePerWave;
+    for (uint32_t q0 = 0; q0 < nq; q0 += 64u) {
+        const uint32_t i = q0 + (uint32_t)lane;
+        if (i < nq) {
+            const float v = wq[i];
             if (v != v) {
                 nan = 1;
                 ++nnan;
+                wbr[i] = 0xFFFFFFFFu;
             } else {
                 band_sums(fs, v, BL, BR);
-                bk[k] = band_bucket(fs, v);
-                rk[k] = atomicAdd(&lcnt[bk[k]], 1u);
+                const int bk = band_bucket(fs, v);
+                const uint32_t rk = atomicAdd(&lcnt[bk], 1u);
+                wbr[i] = ((uint32_t)bk << 16) | rk;  // bk < 2^10, rk < 2^16
             }
         }
     }
+    {
+        const double d0 = wave_sum(SL), d1 = wave_sum(SR), d2 = wave_sum(BL), d3 = wave_sum(BR);
+        const unsigned long long u0 = wave_sum_u64(nnan), u1 = wave_sum_u64(cR);
+        const uint32_t m0 = wave_max_u32(__float_as_uint(amax));  // |v| >= 0: uint order = float order
+        const uint32_t m1 = wave_max_u32((uint32_t)nan);
+        if (lane == 0) {
+            const int w = tid >> 6;
+            s_rd[w] = d0; s_rd[NWV + w] = d1; s_rd[2 * NWV + w] = d2; s_rd[3 * NWV + w] = d3;
+            s_ru[w] = u0; s_ru[NWV + w] = u1;
+            s_rm[w] = m0; s_rm[NWV + w] = m1;
+        }
+    }
     __syncthreads();
-    // a thread's (up to kMaxBuckets / NT) returning atomics are all in flight
-    // before any result is used: one round trip, not one per bucket; the
-    // workgroup's reduction runs while they are in flight
+    // ---- the workgroup: one returning atomic per bucket for its slots (a
+    // thread's atomics all in flight before any result is used), and the
+    // workgroup partials combined by wave 0 in wave order while they fly ----
     constexpr int BPT = (kMaxBuckets + NT - 1) / NT;
     uint32_t got[BPT];
 #pragma unroll
@@ -285,34 +284,38 @@ __global__ __launch_bounds__(NT) void k_filter(const float* __restrict__ r, long
         const uint32_t c = j < nb ? lcnt[j] : 0u;
         got[u] = c ? atomicAdd(&bucket_cnt[j], c) : 0u;
     }
-
-    // ---- workgroup partials (fixed-order reduction; reduced by k_filter_finalize) ----
-    {
-        double d[4] = {SL, SR, BL, BR};
-        unsigned long long u[2] = {(unsigned long long)nnan, (unsigned long long)cR};
-        uint32_t m[2] = {__float_as_uint(amax), (uint32_t)nan};  // |v| >= 0: uint order = float order
-        block_reduce_multi<NT>(d, u, m, s_rd, s_ru, s_rm);
+    if (tid < 64) {
+        const bool in = lane < NWV;
+        const double d0 = wave_sum(in ? s_rd[lane] : 0.0), d1 = wave_sum(in ? s_rd[NWV + lane] : 0.0);
+        const double d2 = wave_sum(in ? s_rd[2 * NWV + lane] : 0.0), d3 = wave_sum(in ? s_rd[3 * NWV + lane] : 0.0);
+        const unsigned long long u0 = wave_sum_u64(in ? s_ru[lane] : 0ull);
+        const unsigned long long u1 = wave_sum_u64(in ? s_ru[NWV + lane] : 0ull);
+        const uint32_t m0 = wave_max_u32(in ? s_rm[lane] : 0u), m1 = wave_max_u32(in ? s_rm[NWV + lane] : 0u);
         if (tid == 0) {
             FilterPart& fp = part[blockIdx.x];
-            fp.S[0] = d[0]; fp.S[1] = d[1]; fp.S[2] = d[2]; fp.S[3] = d[3];
-            fp.c[0] = u[0]; fp.c[1] = u[1];
+            fp.S[0] = d0; fp.S[1] = d1; fp.S[2] = d2; fp.S[3] = d3;
+            fp.c[0] = u0; fp.c[1] = u1;
             fp.mn = 0.0f;
-            fp.mx = __uint_as_float(m[0]);
-            fp.nan = (int)m[1];
+            fp.mx = __uint_as_float(m0);
+            fp.nan = (int)m1;
         }
     }
-
 #pragma unroll
     for (int u = 0; u < BPT; ++u) {
         const int j = tid + u * NT;
         if (j < nb) gbase[j] = got[u];
     }
     __syncthreads();
-#pragma unroll
-    for (int k = 0; k < QPT; ++k) {
-        if (bk[k] >= 0) {
-            const uint32_t pos = gbase[bk[k]] + rk[k];
-            if (pos < (uint32_t)cap) bucket_vals[(size_t)bk[k] * (size_t)cap + pos] = __float_as_uint(qv[k]);
+    // ---- each wave stores its own slice's scores into their slots ----
+    for (uint32_t q0 = 0; q0 < nq; q0 += 64u) {
+        const uint32_t i = q0 + (uint32_t)lane;
+        if (i < nq) {
+            const uint32_t br = wbr[i];
+            if (br != 0xFFFFFFFFu) {
+                const uint32_t bk = br >> 16;
+                const uint32_t pos = gbase[bk] + (br & 0xFFFFu);
+                if (pos < (uint32_t)cap) bucket_vals[(size_t)bk * (size_t)cap + pos] = __float_as_uint(wq[i]);
+            }
         }
     }
 }
