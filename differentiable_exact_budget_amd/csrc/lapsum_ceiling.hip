@@ -16,7 +16,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_copy(const float* __restrict
                                                           long long n) {
     const long long n4 = n / 4;
     float4* b4 = reinterpret_cast<float4*>(b);
-    auto f = [&](const float4& v, long long i) { b4[i] = v; };
+    auto f = [&](const float4& v, long long i) { st4<true>(b4 + i, v); };
     tile_f4<kCopyV, true>(reinterpret_cast<const float4*>(a), n4, false, f, f);
     if (blockIdx.x == 0)
         for (long long j = n4 * 4 + threadIdx.x; j < n; j += kStreamThreads) b[j] = a[j];

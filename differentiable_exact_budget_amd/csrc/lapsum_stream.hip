@@ -68,7 +68,10 @@ constexpr int kApplyV = 1, kApplyGrid = 1 << 24;
 // memory-side cache may still hold.
 constexpr int kProbsReverse = 1;
 constexpr int kApplyReverse = 1;
-// non-temporal loads for the read-only inputs
+// non-temporal loads for the read-only inputs, and non-temporal stores for
+// p and grad (measured on gfx950 at 10^8 scores: the p and grad passes 6% and
+// 4% faster, and the sample, select and band solve of the next step too)
+constexpr bool kStoreNT = true;
 constexpr bool kFilterNT = true;
 constexpr bool kProbsNT = true;
 constexpr bool kReduceNT = true;
@@ -509,7 +512,9 @@ __global__ __launch_bounds__(kStreamThreads) void k_probs(const float* __restric
     if (VEC) {
         const long long n4 = n >> 2;
         float4* p4 = reinterpret_cast<float4*>(p);
-        auto body = [&](float4 q, long long idx) { p4[idx] = make_float4(one(q.x), one(q.y), one(q.z), one(q.w)); };
+        auto body = [&](float4 q, long long idx) {
+            st4<kStoreNT>(p4 + idx, make_float4(one(q.x), one(q.y), one(q.z), one(q.w)));
+        };
         tile_f4<kProbsV, kProbsNT>(reinterpret_cast<const float4*>(r), n4, rev != 0, body, body);
         if (blockIdx.x == 0) {
             const long long j = (n4 << 2) + tid;
@@ -676,7 +681,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_vjp_apply(const float* __res
         const long long n4 = n >> 2;
         float4* o4 = reinterpret_cast<float4*>(grad);
         auto body = [&](float4 q, float4 h, long long idx) {
-            o4[idx] = make_float4(one(q.x, h.x), one(q.y, h.y), one(q.z, h.z), one(q.w, h.w));
+            st4<kStoreNT>(o4 + idx, make_float4(one(q.x, h.x), one(q.y, h.y), one(q.z, h.z), one(q.w, h.w)));
         };
         tile_f4x2<kApplyV, kApplyNT>(reinterpret_cast<const float4*>(r), reinterpret_cast<const float4*>(g), n4,
                                      rev != 0, body, body);

@@ -28,6 +28,19 @@ LS_DEV float4 ld4(const float4* p) {
     return *p;
 }
 
+// 16-byte store, optionally non-temporal: the streamed outputs (p, grad) are
+// not read back by this step, and keeping them out of the caches leaves the
+// latency-bound kernels of the next step less dirty data to write back
+template <bool NT>
+LS_DEV void st4(float4* p, float4 v) {
+    if (NT) {
+        const f4v t = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(t, reinterpret_cast<f4v*>(p));
+    } else {
+        *p = v;
+    }
+}
+
 template <int U, bool NT = false, class Main, class Tail>
 LS_DEV void stream_f4(const float4* __restrict__ a, long long n4, bool reverse, Main&& main, Tail&& tail) {
     const long long stride = (long long)gridDim.x * blockDim.x;
