@@ -221,10 +221,10 @@ __global__ __launch_bounds__(kSortThreads) void k_band_root(const uint32_t* buck
 // "Single-pass parallel prefix scan with decoupled look-back", and Adinets
 // & Merrill, "Onesweep", 2022)
 // ---------------------------------------------------------------------------
-// Digit histograms of all four LSD passes in one read.  Per workgroup in LDS:
-// the lanes of a wave that share a digit are found with ballots and one of
-// them adds their count (many keys share the high digits; plain per-lane
-// atomics on one LDS word would serialise).  The workgroup totals then go
+// Digit histograms of all four LSD passes in one read.  Per workgroup in LDS,
+// one atomic add per key and digit (measured on gfx950: 2.3x faster than
+// grouping a wave's equal digits with ballots first), except that a wave
+// whose keys all share a digit adds once.  The workgroup totals then go
 // into the global totals with integer atomics (order-free: deterministic).
 // hist: global uint32[1025] (four 256-bin histograms, then a non-finite
 // flag), all zero on entry; k_radix_offsets reads and re-zeroes it.
@@ -245,8 +245,12 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_hist(const float* __res
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const uint32_t d = (key >> (8 * p)) & 0xFFu;
-            const unsigned long long peers = match_digit8(d, act);
-            if (valid && lane == __ffsll((long long)peers) - 1) atomicAdd(&h[p * 256 + d], (uint32_t)popc64(peers));
+            const uint32_t d0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)d);
+            if (ballot(valid && d == d0) == act) {  // one digit for the whole wave: one add
+                if (lane == __ffsll((long long)act) - 1) atomicAdd(&h[p * 256 + d0], (uint32_t)popc64(act));
+            } else if (valid) {
+                atomicAdd(&h[p * 256 + d], 1u);
+            }
         }
     };
     const long long stride = (long long)gridDim.x * kRadixThreads;
@@ -453,13 +457,12 @@ LS_DEV uint32_t radix_key(const uint32_t* in, int in_is_float, long long idx) {
 __global__ __launch_bounds__(kRadixThreads) void k_radix_count(const uint32_t* __restrict__ in, int in_is_float,
                                                                 long long n, int pass, uint32_t* __restrict__ counts,
                                                                 long long T) {
-    constexpr int NW = kRadixThreads / 64;
-    __shared__ uint32_t cnt[256 * NW];
+    __shared__ uint32_t cnt[256];
     const int tid = threadIdx.x, w = tid >> 6, lane = lane_id();
     const int shift = 8 * pass;
     const long long tile = blockIdx.x;
     const long long base = tile * kRadixTile;
-    for (int e = tid; e < 256 * NW; e += kRadixThreads) cnt[e] = 0u;
+    cnt[tid] = 0u;  // kRadixThreads == 256
     __syncthreads();
     uint32_t kr[kRadixItems];
 #pragma unroll
@@ -467,23 +470,23 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_count(const uint32_t* _
         const long long idx = base + (long long)((w * kRadixItems + i) * 64 + lane);
         kr[i] = idx < n ? radix_key(in, in_is_float, idx) : 0u;
     }
-    volatile uint32_t* vc = cnt;  // successive leader lanes update one word: keep the wave's order
+    // counts only: one LDS atomic add per key (one per wave when the wave's
+    // keys all share the digit)
 #pragma unroll
     for (int i = 0; i < kRadixItems; ++i) {
         const long long idx = base + (long long)((w * kRadixItems + i) * 64 + lane);
         const bool valid = idx < n;
         const unsigned long long act = ballot(valid);
-        if (act != 0ull) {
-            const uint32_t d = (kr[i] >> shift) & 0xFFu;
-            const unsigned long long peers = match_digit8(d, act);
-            if (valid && lane == 63 - __clzll(peers)) vc[d * NW + w] = vc[d * NW + w] + (uint32_t)popc64(peers);
+        const uint32_t d = (kr[i] >> shift) & 0xFFu;
+        const uint32_t d0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)d);
+        if (act != 0ull && ballot(valid && d == d0) == act) {
+            if (lane == __ffsll((long long)act) - 1) atomicAdd(&cnt[d0], (uint32_t)popc64(act));
+        } else if (valid) {
+            atomicAdd(&cnt[d], 1u);
         }
     }
     __syncthreads();
-    uint32_t tot = 0u;
-#pragma unroll
-    for (int q = 0; q < NW; ++q) tot += cnt[tid * NW + q];
-    counts[(size_t)tid * (size_t)T + (size_t)tile] = tot;  // kRadixThreads == 256: thread = digit
+    counts[(size_t)tid * (size_t)T + (size_t)tile] = cnt[tid];  // thread = digit
 }
 
 // one workgroup per digit: exclusive scan of its counts over the tiles
