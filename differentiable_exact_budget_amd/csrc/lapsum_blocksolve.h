@@ -569,7 +569,8 @@ __device__ __attribute__((always_inline)) SolveOut segment_solve(const SegView s
     SegCarries cr{};  // per == 1
     if (per == 1) {
         const bool global = tl.aL > -INFINITY && tl.aR < INFINITY && ((double)tl.aR - (double)tl.aL) * inv_t <= 600.0;
-        cr = block_seg_carries<NT>(c1, f1, ak, av, Bx1, tl, global, s_k, s_v, reinterpret_cast<uint32_t*>(s_int));
+        __shared__ uint32_t s_su[3 * (NT / 64)];  // per-wave counts, prefixes and frame flags
+        cr = block_seg_carries<NT>(c1, f1, ak, av, Bx1, tl, global, s_k, s_v, s_su);
         rbase = cr.rank;
     } else {
         rbase = block_exclusive_scan<NT>(rc, nullptr, reinterpret_cast<uint32_t*>(s_int));

@@ -62,10 +62,9 @@ struct Ctl {
     double sum_p;
     // VJP
     double sumfg, sumf, c;
-    // last-workgroup tickets (each returns to 0 after use) and tile counters
+    // last-workgroup tickets (each returns to 0 after use)
     unsigned int done[8];
-    unsigned int tile_ctr[4];
-    unsigned int pad1[4];
+    unsigned int pad1[8];
     // 1 when the filter certified the bracket with every band score stored:
     // the band solve and p pass launched right behind it then do their work
     int32_t gate;

@@ -134,7 +134,7 @@ Layout make_layout(long long n_cap) {
     L.keysB = take(sizeof(uint32_t) * nk);
     L.hist = take(sizeof(uint32_t) * kHistStride * kRadixHistBlocks);
     L.goff = take(sizeof(uint32_t) * 1024);
-    L.status_bytes = sizeof(unsigned long long) * 256 * (size_t)std::max<long long>(tiles_for(n_cap), 1);
+    L.status_bytes = sizeof(unsigned long long) * radix_status_words(n_cap);
     L.status = take(L.status_bytes);
     L.total = o;
     return L;

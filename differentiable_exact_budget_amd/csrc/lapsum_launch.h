@@ -82,7 +82,8 @@ void launch_bucket_solve(uint32_t* bucket_vals, const uint32_t* bucket_cnt, int 
                          const HeavyArrays* ha = nullptr, const int* gate = nullptr, HostSummary* hs = nullptr,
                          unsigned int seq = 0);
 int radix_hist_blocks(long long n);
-bool radix_uses_onesweep(long long n);  // else the split passes (counts, scan, scatter)
+bool radix_uses_onesweep(long long n);
+size_t radix_status_words(long long n_cap);  // else the split passes (counts, scan, scatter)
 void launch_radix_sort(const float* r, long long n, uint32_t* keysA, uint32_t* keysB, uint32_t* hist_part,
                        uint32_t* goff, unsigned long long* status, uint32_t epoch_base, Ctl* ctl, hipStream_t s);
 void launch_curve_tiles(const uint32_t* keys, long long n, Ctl* ctl, SegArrays seg, SolveScratch sc, double k, double t,

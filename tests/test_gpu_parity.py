@@ -59,7 +59,9 @@ def test_small_solve_ties_and_zero_temperature(oracle_mod):
     assert np.max(np.abs(p - (r >= 15))) <= 1e-6
 
 
-@pytest.mark.parametrize("n", [1, 2, 17, 4096, 16384, 16385, 65537, 300_001])
+# 16385 keys: 5 tiles, so a wave scans several digits; 2^20 keys: 256 tiles, a
+# workgroup per CU; 2^20 + 1: one tile more than the CUs, the split passes
+@pytest.mark.parametrize("n", [1, 2, 17, 4096, 16384, 16385, 65537, 300_001, 1 << 20, (1 << 20) + 1])
 def test_sort_bit_exact(oracle_mod, n):
     rng = np.random.default_rng(100 + n)
     r = rng.standard_normal(n).astype(np.float32)
@@ -78,9 +80,10 @@ def test_sort_bit_exact(oracle_mod, n):
 
 def test_sort_forms_alternate(oracle_mod):
     """Large inputs take the split radix passes (counts, scan, scatter), small
-    ones the one-kernel passes with look-back; the split passes leave data in
-    the region the look-back reads, which must be cleared in between.  Sorts of
-    both kinds, alternating on one workspace, all bit-exact."""
+    ones the one-kernel passes (epoch-tagged count and offset words); the split
+    passes leave data in the region the one-kernel passes read, which must be
+    cleared in between.  Sorts of both kinds, alternating on one workspace, all
+    bit-exact."""
     for n in (2_500_001, 300_001, 4_000_000, 65_537):
         r = np.random.default_rng(n).standard_normal(n).astype(np.float32)
         r[::5] = r[2]
