@@ -57,7 +57,7 @@ __global__ __launch_bounds__(NT) void k_rows_forward(const float* __restrict__ r
     __syncthreads();
     SegView sv{1, &sg_first, &sg_last, &sg_P, &sg_Bx, &sg_cnt, &sg_off, keys, nullptr, nullptr, nullptr, nullptr};
     SolveScratch sc{&sc_pk, &sc_pv, &sc_bk, &sc_bv, &sc_bfx, &sc_rank, nullptr, nullptr};
-    Tails tl{-INFINITY, INFINITY, 0.0, 0.0, (double)n, 0.0, k, t, inv_t};
+    Tails tl{-INFINITY, INFINITY, 0.0, 0.0, (double)n, 0.0, k, t, inv_t, -INFINITY, INFINITY};
     const SolveOut o = segment_solve<NT, ITEMS>(sv, tl, sc, s_k, s_v, s_int);
     if (tid == 0) {
         const double nanv = __longlong_as_double(0x7ff8000000000000ll);

@@ -203,13 +203,19 @@ LS_DEV void block_scan_bwd_excl(float& k, double& v, float* sk, double* sv, doub
     k = ek; v = ev;
 }
 
+// largest x >= -1 over the workgroup (all threads call it; s: >= NT/64
+// words).  A wave maximum by lane exchanges, then one word per wave: no
+// same-address LDS atomics, which serialize when many threads hold a value.
 template <int NT>
 LS_DEV int block_max_int(int x, int* s) {
-    if (threadIdx.x == 0) *s = -1;
+    constexpr int NW = NT / 64;
+    const int w = threadIdx.x >> 6;
+    const int m = (int)wave_max_u32((uint32_t)(x + 1)) - 1;
+    if (lane_id() == 0) s[w] = m;
     __syncthreads();
-    if (x >= 0) atomicMax(s, x);
-    __syncthreads();
-    int r = *s;
+    int r = s[0];
+#pragma unroll
+    for (int q = 1; q < NW; ++q) r = max(r, s[q]);
     __syncthreads();
     return r;
 }
@@ -263,6 +269,10 @@ struct Tails {
     double m;              // scores in the segments
     double c_R;            // scores >= a_R
     double k, t, inv_t;
+    // a range [fL, fH] holding every score and tail key (+-inf: unknown);
+    // when it spans at most 600 t, all carries share one additive frame
+    // with key fL (fL = aL whenever the lower tail is not empty)
+    float fL, fH;
 };
 
 struct SolveScratch {      // global scratch
@@ -355,7 +365,7 @@ LS_DEV SegCarries block_seg_carries(uint32_t c, float f, float l, double P, doub
     const float wmin = __uint_as_float(wave_min_f32_bits(fk)), wmax = __uint_as_float(wave_max_f32_bits(lk));
     const bool empty = !(wmax > -INFINITY);
     const bool wadd = global || empty || ((double)wmax - (double)wmin) * inv_t <= 600.0;
-    const float ref = global ? tl.aL : (empty ? -INFINITY : wmin);
+    const float ref = global ? tl.fL : (empty ? -INFINITY : wmin);
     SegCarries r;
     r.frame = wadd ? 1 : 0;
     r.E = 1.0;
@@ -438,13 +448,13 @@ LS_DEV SegCarries block_seg_carries(uint32_t c, float f, float l, double P, doub
         // one frame for the whole band: each thread adds the other waves'
         // totals itself, in wave order (no exponential, no second stage)
         uint32_t pcn = 0u;
-        double pv = tl.S_L > 0.0 ? tl.S_L : 0.0, qv = 0.0;
+        double pv = tl.S_L > 0.0 ? tl.S_L * exp(((double)tl.aL - (double)tl.fL) * inv_t) : 0.0, qv = 0.0;
         float pmx = -INFINITY, qmn = INFINITY;
         for (int x = 0; x < w; ++x) { pcn += su[x]; pv += sv[x]; pmx = fmaxf(pmx, sk[2 * NW + x]); }
         for (int x = NW - 1; x > w; --x) { qv += sv[NW + x]; qmn = fminf(qmn, sk[3 * NW + x]); }
-        if (tl.S_R > 0.0) qv += tl.S_R * exp(((double)tl.aL - (double)tl.aR) * inv_t);
+        if (tl.S_R > 0.0) qv += tl.S_R * exp(((double)tl.fL - (double)tl.aR) * inv_t);
         r.rank += pcn;
-        r.kf_w = r.kb_w = r.kf_o = r.kb_o = tl.aL;
+        r.kf_w = r.kb_w = r.kf_o = r.kb_o = tl.fL;
         r.vf_w = r.vf_o = pv;
         r.vb_w = r.vb_o = qv;
         r.last_before = fmaxf(el, pmx);
@@ -568,7 +578,7 @@ __device__ __attribute__((always_inline)) SolveOut segment_solve(const SegView s
     uint32_t rbase;
     SegCarries cr{};  // per == 1
     if (per == 1) {
-        const bool global = tl.aL > -INFINITY && tl.aR < INFINITY && ((double)tl.aR - (double)tl.aL) * inv_t <= 600.0;
+        const bool global = tl.fL > -INFINITY && tl.fH < INFINITY && ((double)tl.fH - (double)tl.fL) * inv_t <= 600.0;
         __shared__ uint32_t s_su[3 * (NT / 64)];  // per-wave counts, prefixes and frame flags
         cr = block_seg_carries<NT>(c1, f1, ak, av, Bx1, tl, global, s_k, s_v, s_su);
         rbase = cr.rank;

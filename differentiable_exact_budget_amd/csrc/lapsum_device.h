@@ -232,14 +232,26 @@ LS_DEV uint32_t wave_max_u32(uint32_t v) {
     return v;
 }
 
-// inclusive scan of uint32 over the wave (Hillis-Steele with shuffles)
+// Inclusive scans over the wave as a butterfly of lane exchanges: at
+// distance D each lane takes the total of its partner's aligned D-block and
+// adds it when that block lies before it (after it, for a reverse scan).
+// The exchanges are DPP / lane swaps, not LDS permutes; the order of the
+// additions is fixed.  All 64 lanes must be active.
+template <int D>
+LS_DEV void scan_step_u32(uint32_t& v, uint32_t& tot, int l) {
+    const uint32_t o = xor_lane<D>(tot);
+    if (l & D) v += o;
+    tot += o;
+}
 LS_DEV uint32_t wave_inclusive_scan(uint32_t v) {
     const int l = lane_id();
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        uint32_t y = __shfl_up(v, o, 64);
-        if (l >= o) v += y;
-    }
+    uint32_t tot = v;
+    scan_step_u32<1>(v, tot, l);
+    scan_step_u32<2>(v, tot, l);
+    scan_step_u32<4>(v, tot, l);
+    scan_step_u32<8>(v, tot, l);
+    scan_step_u32<16>(v, tot, l);
+    scan_step_u32<32>(v, tot, l);
     return v;
 }
 
@@ -485,13 +497,23 @@ LS_DEV int next_pow2(int x) {
 // each wave, then the wave totals scanned by wave 0 (s: >= NT/64 entries).
 // The exclusive value is read from the neighbour's inclusive sum, never
 // formed as (inclusive - own).
+// fp64 sums over the wave, forward or reverse: the butterfly scan of
+// wave_inclusive_scan (all 64 lanes active)
+template <int D>
+LS_DEV void scan_step_f64(double& v, double& tot, int l, bool reverse) {
+    const double o = xor_lane_f64<D>(tot);
+    if (((l & D) != 0) != reverse) v += o;
+    tot += o;  // the partner forms o + tot: the same value
+}
 LS_DEV double wave_scan_add_incl(double v, bool reverse) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const double y = reverse ? __shfl_down(v, o, 64) : __shfl_up(v, o, 64);
-        if (reverse ? (lane + o < 64) : (lane >= o)) v += y;
-    }
+    const int l = lane_id();
+    double tot = v;
+    scan_step_f64<1>(v, tot, l, reverse);
+    scan_step_f64<2>(v, tot, l, reverse);
+    scan_step_f64<4>(v, tot, l, reverse);
+    scan_step_f64<8>(v, tot, l, reverse);
+    scan_step_f64<16>(v, tot, l, reverse);
+    scan_step_f64<32>(v, tot, l, reverse);
     return v;
 }
 LS_DEV double wave_excl_from_incl(double inc, bool reverse) {

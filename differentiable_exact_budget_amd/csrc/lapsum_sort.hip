@@ -71,7 +71,7 @@ __global__ __launch_bounds__(kSortThreads) void k_small_solve(const float* __res
     if (tid == 0) { sg_cnt = (uint32_t)n; sg_off = 0u; }
     __syncthreads();
     SegView sv{1, &sg_first, &sg_last, &sg_P, &sg_Bx, &sg_cnt, &sg_off, keys, nullptr, nullptr, nullptr, nullptr};
-    Tails tl{-INFINITY, INFINITY, 0.0, 0.0, (double)n, 0.0, k, t, inv_t};
+    Tails tl{-INFINITY, INFINITY, 0.0, 0.0, (double)n, 0.0, k, t, inv_t, -INFINITY, INFINITY};
     SolveOut o = segment_solve<kSortThreads, kSortItems>(sv, tl, sc, s_k, s_v, s_int);
     if (tid == 0) {
         double b = o.b;
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(kSortThreads) void k_band_root(const uint32_t* buck
     __shared__ double s_v[kSortThreads];
     __shared__ int s_int[32];
     SegView sv{nb, seg.first, seg.last, seg.P, seg.Bx, seg.cnt, seg.off, bucket_vals, nullptr, nullptr, nullptr, sortbuf};
-    Tails tl{ctl->aL, ctl->aR, ctl->S_L, ctl->S_R, (double)ctl->m, (double)ctl->c_R, k, t, inv_t};
+    Tails tl{ctl->aL, ctl->aR, ctl->S_L, ctl->S_R, (double)ctl->m, (double)ctl->c_R, k, t, inv_t, ctl->aL, ctl->aR};
     SolveOut o = segment_solve<kSortThreads, kSortItems>(sv, tl, sc, s_k, s_v, s_int);
     if (threadIdx.x == 0) {
         if (o.big) {
@@ -679,11 +679,13 @@ __global__ __launch_bounds__(kCurveRootThreads) void k_curve_root(const uint32_t
     __shared__ double s_v[kCurveRootThreads];
     __shared__ int s_int[32];
     SegView sv{ntiles, seg.first, seg.last, seg.P, seg.Bx, seg.cnt, seg.off, keys, nullptr, nullptr, nullptr, nullptr};
-    Tails tl{-INFINITY, INFINITY, 0.0, 0.0, (double)n, 0.0, k, t, inv_t};
+    // the sorted scores run from keys[0] to keys[n - 1]
+    Tails tl{-INFINITY, INFINITY, 0.0, 0.0, (double)n, 0.0, k, t, inv_t, key2f(keys[0]), key2f(keys[n - 1])};
     if (ctl_tails) {
         tl.aL = ctl->aL; tl.S_L = ctl->S_L;
         tl.aR = ctl->aR; tl.S_R = ctl->S_R;
         tl.c_R = (double)ctl->c_R;
+        tl.fL = tl.aL; tl.fH = tl.aR;
     }
     SolveOut o = segment_solve<kCurveRootThreads, kCurveTile / kCurveRootThreads>(sv, tl, sc, s_k, s_v, s_int);
     if (threadIdx.x == 0) {
