@@ -12,8 +12,8 @@
 //                   two order-free exp-sums of its (unsorted) scores.
 //   k_band_root     one workgroup: the curve across buckets, the root bucket
 //                   sorted in LDS, the root.
-//   k_radix_hist    all four 8-bit digit histograms in one read.
-//   k_radix_offsets the global digit offsets of the four passes.
+//   k_radix_hist    all four 8-bit digit histograms in one read; the last
+//                   workgroup turns them into the passes' digit offsets.
 //   k_radix_pass    one LSD digit pass in one kernel (up to 512 tiles).
 //   k_radix_count / k_radix_scan / k_radix_scatter  the same pass in three
 //                   kernels (more tiles).
@@ -234,14 +234,19 @@ __global__ __launch_bounds__(kSortThreads) void k_band_root(const uint32_t* buck
 // with ballots first, or a one-digit-wave test, costs more).  The workgroup
 // totals then go into the global totals with integer atomics (order-free:
 // deterministic).
+// The last workgroup to finish turns the totals into the four passes'
+// exclusive digit offsets (goff), sets the control flags for the sort and
+// re-zeroes the totals and its ticket.
 // hist: global uint32[1025] (four 256-bin histograms, then a non-finite
-// flag), all zero on entry; k_radix_offsets reads and re-zeroes it.
+// flag), all zero on entry and on exit.
 constexpr int kHistCopies = 4;  // LDS histogram copies, by lane & 3
 
 __global__ __launch_bounds__(kRadixThreads) void k_radix_hist(const float* __restrict__ r, long long n,
-                                                               uint32_t* __restrict__ hist) {
+                                                               uint32_t* __restrict__ hist, uint32_t* goff,
+                                                               Ctl* ctl) {
     __shared__ uint32_t h[kHistCopies * 1024];
-    __shared__ int s_bad;
+    __shared__ uint32_t scr[kRadixThreads / 64 + 2];
+    __shared__ int s_bad, s_last;
     const int tid = threadIdx.x, lane = lane_id();
     for (int i = tid; i < kHistCopies * 1024; i += kRadixThreads) h[i] = 0u;
     uint32_t* hl = h + (lane & (kHistCopies - 1)) * 1024;
@@ -280,33 +285,43 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_hist(const float* __res
     }
     if (bad) atomicOr(&s_bad, 1);
     __syncthreads();
-    for (int i = tid; i < 1024; i += kRadixThreads) {
+    // the adds return their old values and the wave waits for them, so that
+    // every add is done (device scope) before the ticket is taken; a fence
+    // here would also write back and invalidate the L2 in every workgroup
+    constexpr int NB = 1024 / kRadixThreads;
+    uint32_t old[NB + 1];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {  // all adds in flight, then one wait
+        const int i = tid + b * kRadixThreads;
         uint32_t c = 0u;
 #pragma unroll
         for (int q = 0; q < kHistCopies; ++q) c += h[q * 1024 + i];
-        if (c) atomicAdd(&hist[i], c);
+        old[b] = c ? atomicAdd(&hist[i], c) : 0u;
     }
-    if (tid == 0 && s_bad) atomicOr(&hist[1024], 1u);
-}
-
-// exclusive digit offsets of the four passes from the global totals; the
-// totals are re-zeroed for the next sort
-__global__ __launch_bounds__(256) void k_radix_offsets(uint32_t* hist, uint32_t* goff, Ctl* ctl) {
-    __shared__ uint32_t scr[256 / 64 + 2];
-    const int tid = threadIdx.x;
+    old[NB] = (tid == 0 && s_bad) ? atomicOr(&hist[1024], 1u) : 0u;
+    uint32_t acc = 0u;
+#pragma unroll
+    for (int b = 0; b <= NB; ++b) acc |= old[b];
+    asm volatile("" ::"v"(acc));
+    __syncthreads();
+    if (tid == 0) s_last = atomicAdd(&ctl->done[0], 1u) == gridDim.x - 1u;
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
     uint32_t x[4];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) x[p] = hist[p * 256 + tid];
-    const uint32_t bad = hist[1024];
-    __syncthreads();
+    for (int p = 0; p < 4; ++p)
+        x[p] = __hip_atomic_load(&hist[p * 256 + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t any_bad = __hip_atomic_load(&hist[1024], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        goff[p * 256 + tid] = block_exclusive_scan<256>(x[p], nullptr, scr);
+        goff[p * 256 + tid] = block_exclusive_scan<kRadixThreads>(x[p], nullptr, scr);  // thread = digit
         hist[p * 256 + tid] = 0u;
     }
     if (tid == 0) {
         hist[1024] = 0u;
-        ctl->flags = bad ? kFlagNonFinite : 0;
+        ctl->done[0] = 0u;
+        ctl->flags = any_bad ? kFlagNonFinite : 0;
     }
 }
 
@@ -762,8 +777,7 @@ bool radix_uses_onesweep(long long n) {
 void launch_radix_sort(const float* r, long long n, uint32_t* keysA, uint32_t* keysB, uint32_t* hist_part,
                        uint32_t* goff, unsigned long long* status, uint32_t epoch_base, Ctl* ctl, hipStream_t s) {
     const int hb = radix_hist_blocks(n);
-    hipLaunchKernelGGL(k_radix_hist, dim3(hb), dim3(kRadixThreads), 0, s, r, n, hist_part);
-    hipLaunchKernelGGL(k_radix_offsets, dim3(1), dim3(256), 0, s, hist_part, goff, ctl);
+    hipLaunchKernelGGL(k_radix_hist, dim3(hb), dim3(kRadixThreads), 0, s, r, n, hist_part, goff, ctl);
     const bool onesweep = radix_uses_onesweep(n);
     const long long T = onesweep ? (n + kPassTile - 1) / kPassTile : (n + kSplitTile - 1) / kSplitTile;
     // the status region: the one-kernel passes' count and offset words (8
