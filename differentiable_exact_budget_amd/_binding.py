@@ -89,7 +89,7 @@ EXPORTED = [
     "lapsum_vjp_ex", "lapsum_vjp_kt", "lapsum_topk_threshold", "lapsum_hard_topk", "lapsum_dftopk",
     "lapsum_forward_batched", "lapsum_vjp_batched",
     "lapsum_release_workspaces", "lapsum_workspace_bytes",
-    "lapsum_test_sort", "lapsum_test_sample", "lapsum_test_select", "lapsum_test_filter",
+    "lapsum_test_sort", "lapsum_test_sort_form", "lapsum_test_sample", "lapsum_test_select", "lapsum_test_filter",
     "lapsum_test_copy", "lapsum_test_read", "lapsum_test_binomial_ranks",
 ]
 
@@ -134,6 +134,8 @@ def lib():
     L.lapsum_workspace_bytes.restype = ctypes.c_size_t
     L.lapsum_test_sort.argtypes = [vp, i64, vp, vp]
     L.lapsum_test_sort.restype = ctypes.c_int
+    L.lapsum_test_sort_form.argtypes = [vp, i64, vp, ctypes.c_int32, vp]
+    L.lapsum_test_sort_form.restype = ctypes.c_int
     L.lapsum_test_sample.argtypes = [vp, i64, f32, u64, i64, vp, vp, vp]
     L.lapsum_test_sample.restype = ctypes.c_int
     L.lapsum_test_select.argtypes = [vp, i64, i64, i64, ctypes.POINTER(f32), ctypes.POINTER(f32),

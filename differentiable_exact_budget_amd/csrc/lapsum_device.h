@@ -64,7 +64,11 @@ struct Ctl {
     double sumfg, sumf, c;
     // last-workgroup tickets (each returns to 0 after use)
     unsigned int done[8];
-    unsigned int pad1[8];
+    // radix sort: tile counters of the look-back passes, and 1 when this sort
+    // holds the device's resident-pass lock (set by the histogram kernel)
+    unsigned int tile_ctr[4];
+    int resident;
+    unsigned int pad1[3];
     // 1 when the filter certified the bracket with every band score stored:
     // the band solve and p pass launched right behind it then do their work
     int32_t gate;

@@ -374,10 +374,11 @@ uint32_t next_epoch(Workspace* w, hipStream_t st) {
 // read epoch-tagged status words; the split passes leave counts and offsets
 // in the same region, which must not pass for status words: the region is
 // cleared before the next sort that reads it.
-void sort_keys(Workspace* w, const float* r, long long n, hipStream_t st) {
+// form: as launch_radix_sort (0 picks by size).
+void sort_keys(Workspace* w, const float* r, long long n, hipStream_t st, int form = 0) {
     const uint32_t epoch = next_epoch(w, st);
-    launch_radix_sort(r, n, w->keysA, w->keysB, w->hist_part, w->goff, w->status, epoch, w->ctl, st);
-    if (!radix_uses_onesweep(n)) w->status_dirty = true;
+    launch_radix_sort(r, n, w->keysA, w->keysB, w->hist_part, w->goff, w->status, epoch, w->ctl, st, form);
+    if (form == 2 || !radix_uses_onesweep(n)) w->status_dirty = true;
 }
 
 void run_full(Workspace* w, const float* r, long long n, double k, double t, double* b_out, hipStream_t st, Timer& tm) {
@@ -932,8 +933,9 @@ lapsum_status_t lapsum_test_read(const float* src, int64_t n, float* sink, lapsu
     return hip_ok(hipGetLastError());
 }
 
-lapsum_status_t lapsum_test_sort(const float* scores, int64_t n, float* out, lapsum_stream_t stream) {
-    if (!scores || !out || n < 1 || n > 0xFFFFFFFFll) return LAPSUM_ERR_INVALID_ARGUMENT;
+lapsum_status_t lapsum_test_sort_form(const float* scores, int64_t n, float* out, int32_t form,
+                                      lapsum_stream_t stream) {
+    if (!scores || !out || n < 1 || n > 0xFFFFFFFFll || form < 0 || form > 2) return LAPSUM_ERR_INVALID_ARGUMENT;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     Workspace* w = nullptr;
     lapsum_status_t gs = get_ws(st, n, &w);
@@ -942,7 +944,7 @@ lapsum_status_t lapsum_test_sort(const float* scores, int64_t n, float* out, lap
     if (n <= kSmallMax) {
         launch_small_solve(scores, (int)n, k, 1.0, w->ctl, w->sc, nullptr, w->keysB, st);
     } else {
-        sort_keys(w, scores, n, st);
+        sort_keys(w, scores, n, st, form);
     }
     if (hipStreamSynchronize(st) != hipSuccess) return LAPSUM_ERR_HIP;
     std::vector<uint32_t> keys((size_t)n);
@@ -955,6 +957,10 @@ lapsum_status_t lapsum_test_sort(const float* scores, int64_t n, float* out, lap
         std::memcpy(&vals[i], &u, 4);
     }
     return hip_ok(hipMemcpy(out, vals.data(), sizeof(float) * (size_t)n, hipMemcpyHostToDevice));
+}
+
+lapsum_status_t lapsum_test_sort(const float* scores, int64_t n, float* out, lapsum_stream_t stream) {
+    return lapsum_test_sort_form(scores, n, out, 0, stream);
 }
 
 lapsum_status_t lapsum_test_sample(const float* scores, int64_t n, float t, uint64_t seed, int64_t s, float* x_out,

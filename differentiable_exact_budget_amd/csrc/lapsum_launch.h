@@ -85,7 +85,8 @@ int radix_hist_blocks(long long n);
 bool radix_uses_onesweep(long long n);
 size_t radix_status_words(long long n_cap);  // else the split passes (counts, scan, scatter)
 void launch_radix_sort(const float* r, long long n, uint32_t* keysA, uint32_t* keysB, uint32_t* hist_part,
-                       uint32_t* goff, unsigned long long* status, uint32_t epoch_base, Ctl* ctl, hipStream_t s);
+                       uint32_t* goff, unsigned long long* status, uint32_t epoch_base, Ctl* ctl, hipStream_t s,
+                       int form = 0);  // 0: by size; 1: one-kernel passes in the look-back design; 2: split passes
 void launch_curve_tiles(const uint32_t* keys, long long n, Ctl* ctl, SegArrays seg, SolveScratch sc, double k, double t,
                         double* b_out, hipStream_t s, bool ctl_tails = false);
 

@@ -241,9 +241,12 @@ __global__ __launch_bounds__(kSortThreads) void k_band_root(const uint32_t* buck
 // flag), all zero on entry and on exit.
 constexpr int kHistCopies = 4;  // LDS histogram copies, by lane & 3
 
+// the device's resident-pass lock: 0 when free, else the holder's token
+static __device__ unsigned int g_resident_owner;
+
 __global__ __launch_bounds__(kRadixThreads) void k_radix_hist(const float* __restrict__ r, long long n,
                                                                uint32_t* __restrict__ hist, uint32_t* goff,
-                                                               Ctl* ctl) {
+                                                               Ctl* ctl, int want_resident, unsigned int token) {
     __shared__ uint32_t h[kHistCopies * 1024];
     __shared__ uint32_t scr[kRadixThreads / 64 + 2];
     __shared__ int s_bad, s_last;
@@ -322,6 +325,10 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_hist(const float* __res
         hist[1024] = 0u;
         ctl->done[0] = 0u;
         ctl->flags = any_bad ? kFlagNonFinite : 0;
+        // the one-kernel passes: resident when the lock is free (the sort's
+        // last pass frees it), else look-back
+        for (int p = 0; p < 4; ++p) ctl->tile_ctr[p] = 0u;
+        ctl->resident = want_resident && atomicCAS(&g_resident_owner, 0u, token) == 0u ? 1 : 0;
     }
 }
 
@@ -330,8 +337,12 @@ LS_DEV unsigned long long st_pack(uint32_t epoch, unsigned long long flag, uint3
     return ((unsigned long long)epoch << 34) | (flag << 32) | (unsigned long long)v;
 }
 
-// One LSD pass in one kernel, launched cooperatively so that every tile is
-// resident; 1024 threads per 4096-key tile (four rows of 64 keys per wave).
+// One LSD pass in one kernel, 1024 threads per 4096-key tile (four rows of
+// 64 keys per wave, so that a wave's chain of rank-counter updates is four
+// long).  Two designs; the histogram kernel picks one per sort.
+//
+// Resident (when the sort holds the device's resident-pass lock; every tile
+// of the pass is then on the device at once, T <= one workgroup per CU):
 //   1. each tile counts its digits (LDS atomics) and publishes the 256 counts
 //      as soon as its keys are in;
 //   2. digit d's scan over the tiles runs in one wave of tile d mod T (wave
@@ -341,19 +352,39 @@ LS_DEV unsigned long long st_pack(uint32_t epoch, unsigned long long flag, uint3
 //      order) and scatters them into LDS in digit order; it then takes its
 //      256 offsets and writes runs out.
 // Every published word carries the pass's epoch, so a reader waits on the
-// word itself: no grid barrier, and each word is read about once.  Measured
-// on gfx950 at 10^6 keys: 12.6 us a pass, against 20 us for a decoupled
-// look-back (all tiles run at once, so the look-back chain and its polling of
-// status words that cross the XCDs' L2 caches set the time).  Each array is
-// laid out so that its writer writes whole lines (partial-line writes of
-// coherent words stall): counts tile-major, written by the tile; offsets
-// digit-major, written by the digit's wave.
+// word itself: no grid barrier, and each word is read about once.  Each
+// array is laid out so that its writer writes whole lines (partial-line
+// writes of coherent words stall): counts tile-major, written by the tile;
+// offsets digit-major, written by the digit's wave.  A tile waits on every
+// other tile, so all of them must be resident: two such sorts at once could
+// each hold part of the CUs, hence the lock (a sort that finds it taken uses
+// the look-back), and a bounded wait as the last guard.
+//
+// Look-back (decoupled look-back): tiles take numbers in arrival order and
+// a tile adds up its predecessors' published counts until it meets an
+// inclusive prefix; a tile waits only on tiles that started before it.
+//
+// Measured on gfx950 at 10^6 keys: 11.5 us a pass resident, 20 us look-back
+// (all tiles run at once there, so the look-back chain and its polling of
+// status words that cross the XCDs' L2 caches set the time).
 constexpr int kPassThreads = 1024;
 constexpr int kPassItems = 4;
 constexpr int kPassTile = kPassThreads * kPassItems;
 static_assert(kHistCopies * 256 == kPassThreads, "one histogram word per thread");
-constexpr unsigned long long kStCount = 1ull, kStBase = 2ull;
+constexpr unsigned long long kStCount = 1ull, kStBase = 2ull;  // resident: count / offset words
+constexpr unsigned long long kStAgg = 1ull, kStInc = 2ull;     // look-back: aggregate / inclusive prefix
 constexpr long long kOnesweepMaxTiles = 512;  // up to ~2M keys: one kernel per pass
+constexpr int kLookWindow = 8;  // look-back: predecessors' status words read per round trip
+
+
+struct PassLds {
+    uint32_t* cnt;    // 256 * 16: per-wave digit counters
+    uint32_t* stage;  // kPassTile: the tile in digit order
+    uint32_t* hist;   // kHistCopies * 256
+    uint32_t* loc;    // 256
+    uint32_t* gbase;  // 256
+    uint32_t* scr;    // 18
+};
 
 // waits for the word at p to carry this pass's epoch (bounded: a broken
 // invariant becomes a reported error, not a hang)
@@ -368,17 +399,16 @@ LS_DEV uint32_t wait_word(const unsigned long long* p, uint32_t epoch, Ctl* ctl)
     }
 }
 
-__global__ __launch_bounds__(kPassThreads) void k_radix_pass(const uint32_t* __restrict__ in, int in_is_float,
-                                                              uint32_t* __restrict__ out, long long n, int pass,
-                                                              unsigned long long* status, uint32_t epoch,
-                                                              const uint32_t* goff, Ctl* ctl) {
+LS_DEV void pass_resident(const uint32_t* __restrict__ in, int in_is_float, uint32_t* __restrict__ out, long long n,
+                          int pass, unsigned long long* status, uint32_t epoch, const uint32_t* goff, Ctl* ctl,
+                          const PassLds& sm) {
     constexpr int NW = kPassThreads / 64;
-    __shared__ uint32_t cnt[256 * NW];
-    __shared__ uint32_t stage[kPassTile];
-    __shared__ uint32_t hist[kHistCopies * 256];
-    __shared__ uint32_t loc[256];
-    __shared__ uint32_t gbase[256];
-    __shared__ uint32_t scr[4];
+    uint32_t* cnt = sm.cnt;
+    uint32_t* stage = sm.stage;
+    uint32_t* hist = sm.hist;
+    uint32_t* loc = sm.loc;
+    uint32_t* gbase = sm.gbase;
+    uint32_t* scr = sm.scr;
     const int tid = threadIdx.x, w = tid >> 6, lane = lane_id();
     const int shift = 8 * pass;
     const uint32_t T = gridDim.x;
@@ -500,6 +530,14 @@ __global__ __launch_bounds__(kPassThreads) void k_radix_pass(const uint32_t* __r
     // 3. this tile's global offsets
     if (tid < 256) gbase[tid] = wait_word(base_words + (size_t)tid * T + tile, epoch, ctl);
     __syncthreads();
+    if (pass == 3 && tid == 0) {
+        // the sort's last pass: once every tile has its offsets nothing waits
+        // any more, and the last tile here frees the lock
+        if (atomicAdd(&ctl->done[1], 1u) == T - 1u) {
+            ctl->done[1] = 0u;
+            atomicExch(&g_resident_owner, 0u);
+        }
+    }
     const long long rem = n - base;
     const int tcount = rem < kPassTile ? (int)rem : kPassTile;
     for (int jj = tid; jj < tcount; jj += kPassThreads) {
@@ -507,6 +545,137 @@ __global__ __launch_bounds__(kPassThreads) void k_radix_pass(const uint32_t* __r
         const uint32_t dd = (key >> shift) & 0xFFu;
         out[(size_t)gbase[dd] + (size_t)(jj - (int)loc[dd])] = key;
     }
+}
+
+LS_DEV void pass_lookback(const uint32_t* __restrict__ in, int in_is_float, uint32_t* __restrict__ out, long long n,
+                          int pass, unsigned long long* status, uint32_t epoch, const uint32_t* goff, Ctl* ctl,
+                          const PassLds& sm) {
+    constexpr int NW = kPassThreads / 64;
+    uint32_t* cnt = sm.cnt;
+    uint32_t* stage = sm.stage;
+    uint32_t* loc = sm.loc;
+    uint32_t* gbase = sm.gbase;
+    uint32_t* scr = sm.scr;
+    uint32_t& s_tile = sm.hist[0];
+    const int tid = threadIdx.x, w = tid >> 6, lane = lane_id();
+    const int shift = 8 * pass;
+    if (tid == 0) s_tile = atomicAdd(&ctl->tile_ctr[pass], 1u);
+    for (int e = tid; e < 256 * NW; e += kPassThreads) cnt[e] = 0u;
+    __syncthreads();
+    const uint32_t tile = s_tile;
+    const long long base = (long long)tile * kPassTile;
+    uint32_t kr[kPassItems];
+    uint32_t rk[kPassItems];
+#pragma unroll
+    for (int i = 0; i < kPassItems; ++i) {
+        const long long idx = base + (long long)((w * kPassItems + i) * 64 + lane);
+        uint32_t key = 0u;
+        if (idx < n) key = in_is_float ? f2key(__uint_as_float(in[idx])) : in[idx];
+        kr[i] = key;
+    }
+    volatile uint32_t* vc = cnt;
+#pragma unroll
+    for (int i = 0; i < kPassItems; ++i) {
+        const long long idx = base + (long long)((w * kPassItems + i) * 64 + lane);
+        const bool valid = idx < n;
+        const unsigned long long act = ballot(valid);
+        rk[i] = 0u;
+        if (act != 0ull) {
+            const uint32_t d = (kr[i] >> shift) & 0xFFu;
+            const unsigned long long peers = match_digit8(d, act);
+            const uint32_t b0 = vc[d * NW + w];
+            rk[i] = b0 + (uint32_t)mbcnt(peers);
+            if (valid && lane == 63 - __clzll(peers)) vc[d * NW + w] = b0 + (uint32_t)popc64(peers);
+        }
+    }
+    __syncthreads();
+    // thread d < 256: per-wave exclusive offsets and the tile total of digit d
+    const int d = tid;
+    uint32_t tot = 0u;
+    if (d < 256) {
+#pragma unroll
+        for (int q = 0; q < NW; ++q) { const uint32_t x = cnt[d * NW + q]; cnt[d * NW + q] = tot; tot += x; }
+    }
+    const uint32_t dex = block_exclusive_scan<kPassThreads>(tot, nullptr, scr);
+    if (d < 256) {
+        loc[d] = dex;
+        // decoupled look-back on digit d, up to kLookWindow predecessors per
+        // round trip: aggregates are added until an inclusive prefix ends it
+        unsigned long long* st = status + (size_t)tile * 256 + d;
+        if (tile == 0) {
+            __hip_atomic_store(st, st_pack(epoch, kStInc, tot), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            gbase[d] = goff[pass * 256 + d];
+        } else {
+            __hip_atomic_store(st, st_pack(epoch, kStAgg, tot), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            uint32_t excl = 0u;
+            long long j = (long long)tile - 1;
+            unsigned int spins = 0u;
+            bool done = false;
+            while (!done && j >= 0) {
+                unsigned long long sw[kLookWindow];
+#pragma unroll
+                for (int q = 0; q < kLookWindow; ++q)
+                    sw[q] = (j - q >= 0) ? __hip_atomic_load(status + (size_t)(j - q) * 256 + d, __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_AGENT)
+                                         : 0ull;
+                int used = 0;
+#pragma unroll
+                for (int q = 0; q < kLookWindow; ++q) {
+                    if (done || used < q || j - q < 0) continue;  // stop at the first word not yet usable
+                    const unsigned long long sq = sw[q];
+                    const uint32_t ep = (uint32_t)(sq >> 34);
+                    const unsigned long long fl = (sq >> 32) & 3ull;
+                    if (ep != epoch || fl == 0ull) continue;
+                    excl += (uint32_t)sq;
+                    used = q + 1;
+                    if (fl == kStInc) done = true;
+                }
+                j -= used;
+                if (!done && used == 0) {
+                    // tiles are handed out in order, so the predecessor is
+                    // resident and publishes within microseconds; a bounded
+                    // wait turns a broken invariant into a reported error
+                    if (++spins > (1u << 24)) { atomicOr(&ctl->flags, kFlagInternal); break; }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+            }
+            __hip_atomic_store(st, st_pack(epoch, kStInc, excl + tot), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            gbase[d] = goff[pass * 256 + d] + excl;
+        }
+    }
+    __syncthreads();
+    // local scatter into LDS in digit order, then coalesced runs to global
+#pragma unroll
+    for (int i = 0; i < kPassItems; ++i) {
+        const long long idx = base + (long long)((w * kPassItems + i) * 64 + lane);
+        if (idx < n) {
+            const uint32_t dd = (kr[i] >> shift) & 0xFFu;
+            stage[loc[dd] + cnt[dd * NW + w] + rk[i]] = kr[i];
+        }
+    }
+    __syncthreads();
+    const long long rem = n - base;
+    const int tcount = rem < kPassTile ? (int)rem : kPassTile;
+    for (int jj = tid; jj < tcount; jj += kPassThreads) {
+        const uint32_t key = stage[jj];
+        const uint32_t dd = (key >> shift) & 0xFFu;
+        out[(size_t)gbase[dd] + (size_t)(jj - (int)loc[dd])] = key;
+    }
+}
+
+__global__ __launch_bounds__(kPassThreads) void k_radix_pass(const uint32_t* __restrict__ in, int in_is_float,
+                                                              uint32_t* __restrict__ out, long long n, int pass,
+                                                              unsigned long long* status, uint32_t epoch,
+                                                              const uint32_t* goff, Ctl* ctl) {
+    __shared__ uint32_t cnt[256 * (kPassThreads / 64)];
+    __shared__ uint32_t stage[kPassTile];
+    __shared__ uint32_t hist[kHistCopies * 256];
+    __shared__ uint32_t loc[256];
+    __shared__ uint32_t gbase[256];
+    __shared__ uint32_t scr[kPassThreads / 64 + 2];
+    const PassLds sm{cnt, stage, hist, loc, gbase, scr};
+    if (ctl->resident) pass_resident(in, in_is_float, out, n, pass, status, epoch, goff, ctl, sm);
+    else pass_lookback(in, in_is_float, out, n, pass, status, epoch, goff, ctl, sm);
 }
 
 // One LSD pass as count, scan, scatter, for more tiles than fit on the
@@ -740,19 +909,17 @@ int radix_hist_blocks(long long n) {
     return (int)b;
 }
 
-// The one-kernel pass needs every tile resident at once (it is launched
-// cooperatively): at most the device's co-resident workgroups of the pass
-// kernel, queried once per device.
+// The resident pass needs every tile on the device at once: at most the
+// device's co-resident workgroups of the pass kernel, queried once per device.
 static long long onesweep_capacity() {
     static std::atomic<long long> cap[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
     long long c = cap[dev].load(std::memory_order_relaxed);
     if (c == 0) {
-        int coop = 0, cus = 0, per = 0;
+        int cus = 0, per = 0;
         c = -1;
-        if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess && coop &&
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
             hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k_radix_pass, kPassThreads, 0) == hipSuccess)
             c = (long long)cus * (long long)per;
         cap[dev].store(c, std::memory_order_relaxed);
@@ -775,10 +942,14 @@ bool radix_uses_onesweep(long long n) {
 }
 
 void launch_radix_sort(const float* r, long long n, uint32_t* keysA, uint32_t* keysB, uint32_t* hist_part,
-                       uint32_t* goff, unsigned long long* status, uint32_t epoch_base, Ctl* ctl, hipStream_t s) {
+                       uint32_t* goff, unsigned long long* status, uint32_t epoch_base, Ctl* ctl, hipStream_t s,
+                       int form) {
     const int hb = radix_hist_blocks(n);
-    hipLaunchKernelGGL(k_radix_hist, dim3(hb), dim3(kRadixThreads), 0, s, r, n, hist_part, goff, ctl);
-    const bool onesweep = radix_uses_onesweep(n);
+    const bool onesweep = form != 2 && radix_uses_onesweep(n);
+    // the lock holder's token: the control block's address (distinct per workspace)
+    const unsigned int token = (unsigned int)(reinterpret_cast<uintptr_t>(ctl) >> 8) | 1u;
+    hipLaunchKernelGGL(k_radix_hist, dim3(hb), dim3(kRadixThreads), 0, s, r, n, hist_part, goff, ctl,
+                       onesweep && form == 0 ? 1 : 0, token);
     const long long T = onesweep ? (n + kPassTile - 1) / kPassTile : (n + kSplitTile - 1) / kSplitTile;
     // the status region: the one-kernel passes' count and offset words (8
     // bytes, 256 T each), or the split passes' tile counts and tile offsets
@@ -790,15 +961,8 @@ void launch_radix_sort(const float* r, long long n, uint32_t* keysA, uint32_t* k
     for (int p = 0; p < 4; ++p) {
         int is_float = p == 0 ? 1 : 0;
         if (onesweep) {
-            uint32_t ep = epoch_base + (uint32_t)p;
-            int pass = p;
-            const uint32_t* cgoff = goff;
-            void* args[] = {(void*)&src, (void*)&is_float, (void*)&dst, (void*)&n, (void*)&pass,
-                            (void*)&status, (void*)&ep, (void*)&cgoff, (void*)&ctl};
-            // a failed launch is left in the HIP error state for the caller
-            if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_radix_pass), dim3((unsigned)T),
-                                           dim3(kPassThreads), args, 0, s) != hipSuccess)
-                return;
+            hipLaunchKernelGGL(k_radix_pass, dim3((unsigned)T), dim3(kPassThreads), 0, s, src, is_float, dst, n, p,
+                               status, epoch_base + (uint32_t)p, goff, ctl);
         } else {
             hipLaunchKernelGGL(k_radix_count, dim3(xcd_grid(T)), dim3(kRadixThreads), 0, s, src, is_float, n, p,
                                counts, T);

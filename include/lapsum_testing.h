@@ -23,6 +23,17 @@ extern "C" {
 lapsum_status_t lapsum_test_sort(const float* scores, int64_t n, float* out, lapsum_stream_t stream);
 
 /*
+ * The same sort in a given form of its multi-workgroup passes: form 0 picks
+ * by size (as lapsum_test_sort); 1 takes the one-kernel passes in their
+ * look-back design (the design a sort uses while another holds the device's
+ * resident-pass lock) where the size allows one-kernel passes; 2 takes the
+ * split passes (count, scan, scatter).  The result is the same in every
+ * form.  LAPSUM_ERR_INVALID_ARGUMENT for another form.
+ */
+lapsum_status_t lapsum_test_sort_form(const float* scores, int64_t n, float* out, int32_t form,
+                                      lapsum_stream_t stream);
+
+/*
  * The kernel-noised sample (section 2.2, localisation step): x_j = fp32 of
  * r[I_j] + eps_j for j < s, with Philox4x32-10 counter (j, 0, 0) and key
  * `seed`; I_j uniform in [0, n), eps_j ~ Laplace(0, t).  idx_out may be NULL.

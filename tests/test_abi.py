@@ -129,6 +129,8 @@ def test_vjp_and_stage_entry_points_reject_bad_arguments():
     assert lib.lapsum_vjp(FAKE, None, FAKE, 0, 0.1, FAKE, FAKE, None) == INVALID
     assert lib.lapsum_vjp(FAKE, None, FAKE, 100, 0.0, FAKE, FAKE, None) == INVALID
     assert lib.lapsum_test_sort(None, 10, FAKE, None) == INVALID
+    assert lib.lapsum_test_sort_form(None, 10, FAKE, 0, None) == INVALID
+    assert lib.lapsum_test_sort_form(FAKE, 10, FAKE, 3, None) == INVALID
     assert lib.lapsum_test_copy(FAKE + 4, FAKE, 10, None) == INVALID  # misaligned
     assert lib.lapsum_test_read(FAKE, 0, FAKE, None) == INVALID
     lo, hi = ctypes.c_int64(), ctypes.c_int64()

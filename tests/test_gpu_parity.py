@@ -93,6 +93,43 @@ def test_sort_forms_alternate(oracle_mod):
         assert np.array_equal(got.view(np.uint32), oracle_mod.sort_keys(r).view(np.uint32)), n
 
 
+@pytest.mark.parametrize("form", [1, 2])
+@pytest.mark.parametrize("n", [16385, 300_001, 1 << 20])
+def test_sort_form_bit_exact(oracle_mod, n, form):
+    """Every form of the multi-workgroup passes gives the same keys: 1 the
+    one-kernel passes in their look-back design (what a sort runs while
+    another sort holds the device's resident-pass lock), 2 the split passes."""
+    rng = np.random.default_rng(300 + n)
+    r = rng.standard_normal(n).astype(np.float32)
+    r[::9] = r[4]
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    assert L.lib().lapsum_test_sort_form(to_dev(r).data_ptr(), n, out.data_ptr(), form, None) == 0
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), oracle_mod.sort_keys(r).view(np.uint32))
+    assert L.lib().lapsum_test_sort_form(to_dev(r).data_ptr(), n, out.data_ptr(), 3, None) != 0
+
+
+def test_full_path_concurrent_streams():
+    """Full-sort solves on two streams at once: at most one of them holds the
+    resident-pass lock and the other runs the look-back passes; both must
+    give the single-stream result bit for bit, on every repetition."""
+    r, g, cfg = workloads.config_inputs("C2")
+    rd = to_dev(r)
+    opt = L.default_options(path=L.PATH_FULL)
+    p_ref, b_ref = L.forward(rd, cfg.k, cfg.t, options=opt)
+    torch.cuda.synchronize()
+    p_ref, b_ref = p_ref.cpu().numpy(), b_ref.cpu().numpy()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(5):
+        outs = []
+        for s in streams:
+            with torch.cuda.stream(s):
+                outs.append(L.forward(rd, cfg.k, cfg.t, options=opt))
+        torch.cuda.synchronize()
+        for p, b in outs:
+            assert np.array_equal(b.cpu().numpy().view(np.uint64), b_ref.view(np.uint64)), rep
+            assert np.array_equal(p.cpu().numpy().view(np.uint32), p_ref.view(np.uint32)), rep
+
+
 @pytest.mark.parametrize("n,dist", [(16385, "normal"), (200_000, "student_t3"), (1_000_000, "normal")])
 def test_full_sort_path(oracle_mod, n, dist):
     r = workloads.scores(dist, n, 7 + n)
