@@ -386,28 +386,33 @@ LS_DEV SegCarries block_seg_carries(uint32_t c, float f, float l, double P, doub
         av = P;
         bv = 1.0 + Bx;
     }
+    if (wadd) {
+        // plain sums, maxima and minima: butterfly scans over lane exchanges
+        // (wadd is wave-uniform, so every lane is here)
+        ir = wave_inclusive_scan(ir);
+        il = wave_scan_max_f32(il);
+        iF = wave_rscan_min_f32(iF);
+        av = wave_scan_add_incl(av, false);
+        bv = wave_scan_add_incl(bv, true);
+    } else {
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t a2 = __shfl_up(ir, o, 64);
-        const float il2 = __shfl_up(il, o, 64);
-        const float iF2 = __shfl_down(iF, o, 64);
-        const double lv2 = __shfl_up(av, o, 64);
-        const double rv2 = __shfl_down(bv, o, 64);
-        float lk2 = 0.0f, rk2 = 0.0f;
-        if (!wadd) {
-            lk2 = __shfl_up(ak, o, 64);
-            rk2 = __shfl_down(bk, o, 64);
-        }
-        if (lane >= o) {
-            ir += a2;
-            il = fmaxf(il, il2);
-            if (wadd) av += lv2;
-            else fwd_combine(lk2, lv2, ak, av, inv_t);
-        }
-        if (lane + o < 64) {
-            iF = fminf(iF, iF2);
-            if (wadd) bv += rv2;
-            else bwd_combine(bk, bv, rk2, rv2, inv_t);
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t a2 = __shfl_up(ir, o, 64);
+            const float il2 = __shfl_up(il, o, 64);
+            const float iF2 = __shfl_down(iF, o, 64);
+            const double lv2 = __shfl_up(av, o, 64);
+            const double rv2 = __shfl_down(bv, o, 64);
+            const float lk2 = __shfl_up(ak, o, 64);
+            const float rk2 = __shfl_down(bk, o, 64);
+            if (lane >= o) {
+                ir += a2;
+                il = fmaxf(il, il2);
+                fwd_combine(lk2, lv2, ak, av, inv_t);
+            }
+            if (lane + o < 64) {
+                iF = fminf(iF, iF2);
+                bwd_combine(bk, bv, rk2, rv2, inv_t);
+            }
         }
     }
     r.rank = __shfl_up(ir, 1, 64);

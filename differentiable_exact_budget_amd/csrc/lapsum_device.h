@@ -247,6 +247,41 @@ LS_DEV void scan_step_u32(uint32_t& v, uint32_t& tot, int l) {
     if (l & D) v += o;
     tot += o;
 }
+template <int D>
+LS_DEV void scan_step_max_f32(float& v, float& tot, int l) {
+    const float o = __uint_as_float(xor_lane<D>(__float_as_uint(tot)));
+    if (l & D) v = fmaxf(v, o);
+    tot = fmaxf(tot, o);
+}
+template <int D>
+LS_DEV void rscan_step_min_f32(float& v, float& tot, int l) {
+    const float o = __uint_as_float(xor_lane<D>(__float_as_uint(tot)));
+    if (!(l & D)) v = fminf(v, o);
+    tot = fminf(tot, o);
+}
+// running maximum over lanes <= l; running minimum over lanes >= l
+LS_DEV float wave_scan_max_f32(float v) {
+    const int l = lane_id();
+    float tot = v;
+    scan_step_max_f32<1>(v, tot, l);
+    scan_step_max_f32<2>(v, tot, l);
+    scan_step_max_f32<4>(v, tot, l);
+    scan_step_max_f32<8>(v, tot, l);
+    scan_step_max_f32<16>(v, tot, l);
+    scan_step_max_f32<32>(v, tot, l);
+    return v;
+}
+LS_DEV float wave_rscan_min_f32(float v) {
+    const int l = lane_id();
+    float tot = v;
+    rscan_step_min_f32<1>(v, tot, l);
+    rscan_step_min_f32<2>(v, tot, l);
+    rscan_step_min_f32<4>(v, tot, l);
+    rscan_step_min_f32<8>(v, tot, l);
+    rscan_step_min_f32<16>(v, tot, l);
+    rscan_step_min_f32<32>(v, tot, l);
+    return v;
+}
 LS_DEV uint32_t wave_inclusive_scan(uint32_t v) {
     const int l = lane_id();
     uint32_t tot = v;

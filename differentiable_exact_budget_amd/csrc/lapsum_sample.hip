@@ -51,7 +51,7 @@ void launch_sample(const float* r, long long n, double t, unsigned long long see
 
 // ---------------------------------------------------------------------------
 // select
-// Fast path: sort a subsample of 2048 sample keys, read off a rank window
+// Fast path: sort a subsample of 1024 sample keys, read off a rank window
 // that contains ranks l..h with a wide safety margin, count the sample keys
 // below the window and collect the ones inside it, and sort only those
 // (<= 4096).  The exact order statistics x_(l) .. x_(h) are then read from
@@ -59,13 +59,13 @@ void launch_sample(const float* r, long long n, double t, unsigned long long see
 // an 8-bit MSD radix select finds x_(l) and x_(h) instead.
 // ---------------------------------------------------------------------------
 constexpr int kWinMax = 4096;
-constexpr int kSubMax = 2048;
+constexpr int kSubMax = 1024;  // measured on gfx950: 1024 beats 2048 (C3, C4) and 512 (C4)
 
 __global__ __launch_bounds__(kSelectThreads) void k_select(const float* __restrict__ x, int s, long long l, long long h,
                                                             int cap, Ctl* ctl, float* sp, float* iw,
                                                             uint32_t* bucket_cnt) {
     __shared__ uint32_t hist[2][256];
-    __shared__ uint32_t sub[kSubMax];
+    __shared__ uint32_t sub[kSubMax > kCandMax ? kSubMax : kCandMax];  // the fallback's candidates too
     __shared__ uint32_t win[kWinMax];
     __shared__ uint32_t scr[kSelectThreads / 64 + 2];
     __shared__ unsigned long long s_redu[kSelectThreads / 64];
