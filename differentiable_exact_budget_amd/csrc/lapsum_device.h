@@ -531,11 +531,6 @@ LS_DEV int next_pow2(int x) {
     return p;
 }
 
-// additive exclusive scan of double over the workgroup.  reverse = false:
-// sum over lower thread indices; true: over higher ones.  Shuffles inside
-// each wave, then the wave totals scanned by wave 0 (s: >= NT/64 entries).
-// The exclusive value is read from the neighbour's inclusive sum, never
-// formed as (inclusive - own).
 // fp64 sums over the wave, forward or reverse: the butterfly scan of
 // wave_inclusive_scan (all 64 lanes active)
 template <int D>
@@ -560,6 +555,11 @@ LS_DEV double wave_excl_from_incl(double inc, bool reverse) {
     const double e = reverse ? __shfl_down(inc, 1, 64) : __shfl_up(inc, 1, 64);
     return (reverse ? lane == 63 : lane == 0) ? 0.0 : e;
 }
+// additive exclusive scan of double over the workgroup.  reverse = false:
+// sum over lower thread indices; true: over higher ones.  Butterfly scans inside
+// each wave, then the wave totals scanned by wave 0 (s: >= NT/64 entries).
+// The exclusive value is read from the neighbour's inclusive sum, never
+// formed as (inclusive - own).
 template <int NT>
 LS_DEV double block_scan_add_excl(double v, double* s, bool reverse) {
     constexpr int NW = NT / 64;

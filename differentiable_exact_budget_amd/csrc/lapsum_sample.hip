@@ -68,11 +68,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(const float* __restri
     __shared__ uint32_t sub[kSubMax > kCandMax ? kSubMax : kCandMax];  // the fallback's candidates too
     __shared__ uint32_t win[kWinMax];
     __shared__ uint32_t scr[kSelectThreads / 64 + 2];
-    __shared__ unsigned long long s_redu[kSelectThreads / 64];
     __shared__ uint32_t s_pre[2], s_rem[2];
-    __shared__ uint32_t s_lo, s_hi;
-    __shared__ int s_fast;
-    __shared__ long long s_nlo;
     const int tid = threadIdx.x;
     // the sample, 16 bytes per load where it can (thread tid holds elements
     // i * kSelectThreads + tid)
@@ -114,44 +110,43 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(const float* __restri
     const bool want_h = h >= 1 && h <= s;
 
     // ---- subsample and window ----
-    const int msub = s < kSubMax ? s : kSubMax;
-    for (int i = tid; i < kSubMax; i += kSelectThreads)
-        sub[i] = i < msub ? f2key(x[(int)((float)i * ((float)s / (float)msub))]) : 0xFFFFFFFFu;
+    // The sample values are independent draws, so any fixed subset of them is
+    // a random subsample: thread i contributes its first key (sample value
+    // 4i, already in its registers), for the first kSubMax threads.
+    static_assert(kSubMax <= kSelectThreads, "one subsample key per thread");
+    const int msub = (s + 3) / 4 < kSubMax ? (s + 3) / 4 : kSubMax;
+    if (tid < kSubMax) sub[tid] = tid < msub ? kr[0] : 0xFFFFFFFFu;
     __syncthreads();
     sort_pow2_lds<kSelectThreads>(sub, kSubMax);
-    if (tid == 0) {
-        uint32_t lo = 0u, hi = 0xFFFFFFFFu;
-        if (want_l) {
-            const double pl = (double)l / (double)s;
-            const long long r0 = (long long)floor((double)msub * pl - 5.0 * sqrt((double)msub * pl * (1.0 - pl)) - 3.0);
-            lo = r0 < 0 ? 0u : sub[r0];
-        }
-        if (want_h) {
-            const double ph = (double)h / (double)s;
-            const long long r1 = (long long)ceil((double)msub * ph + 5.0 * sqrt((double)msub * ph * (1.0 - ph)) + 3.0);
-            hi = r1 >= msub ? 0xFFFFFFFFu : sub[r1];
-        }
-        s_lo = lo; s_hi = hi;
+    // every thread reads the window ends off the sorted subsample (the sort
+    // ends with a barrier)
+    uint32_t wlo = 0u, whi = 0xFFFFFFFFu;
+    if (want_l) {
+        const double pl = (double)l / (double)s;
+        const long long r0 = (long long)floor((double)msub * pl - 5.0 * sqrt((double)msub * pl * (1.0 - pl)) - 3.0);
+        wlo = r0 < 0 ? 0u : sub[r0];
     }
-    __syncthreads();
-    const uint32_t wlo = s_lo, whi = s_hi;
+    if (want_h) {
+        const double ph = (double)h / (double)s;
+        const long long r1 = (long long)ceil((double)msub * ph + 5.0 * sqrt((double)msub * ph * (1.0 - ph)) + 3.0);
+        whi = r1 >= msub ? 0xFFFFFFFFu : sub[r1];
+    }
     uint32_t nbelow = 0u, nin = 0u;
 #pragma unroll
     for (int i = 0; i < kSelectItems; ++i) {
         if ((vmask >> i) & 1ull) { nbelow += kr[i] < wlo; nin += (kr[i] >= wlo && kr[i] <= whi); }
     }
-    const unsigned long long NLO = block_sum_u64<kSelectThreads>((unsigned long long)nbelow, s_redu);
-    uint32_t W = 0u;
-    uint32_t pos = block_exclusive_scan<kSelectThreads>(nin, &W, scr);
-    if (tid == 0) {
-        const long long nlo = (long long)NLO;
-        const bool okl = !want_l || nlo <= l - 1;
-        const bool okh = !want_h || nlo + (long long)W >= h;
-        s_fast = (okl && okh && W >= 1 && W <= (uint32_t)kWinMax) ? 1 : 0;
-        s_nlo = nlo;
-    }
-    __syncthreads();
-    const bool fast = s_fast != 0;
+    // one scan of both counts packed in a word (each total <= kSampleMax <
+    // 2^16): the low half gives each thread its slot in the window, and every
+    // thread gets both totals and takes the same decision
+    static_assert(kSampleMax < 65536, "two 16-bit counts per word");
+    uint32_t tot2 = 0u;
+    uint32_t pos = block_exclusive_scan<kSelectThreads>(nin | (nbelow << 16), &tot2, scr) & 0xFFFFu;
+    const uint32_t W = tot2 & 0xFFFFu;
+    const long long nlo_all = (long long)(tot2 >> 16);
+    const bool okl = !want_l || nlo_all <= l - 1;
+    const bool okh = !want_h || nlo_all + (long long)W >= h;
+    const bool fast = okl && okh && W >= 1 && W <= (uint32_t)kWinMax;
 
     uint32_t key_l = 0u, key_h = 0xFFFFFFFFu;
     const uint32_t* csorted;  // sorted sample keys from x_(l) (or the minimum) to x_(h) (or the maximum)
@@ -165,9 +160,8 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(const float* __restri
         for (int e = (int)W + tid; e < wp; e += kSelectThreads) win[e] = 0xFFFFFFFFu;
         __syncthreads();
         sort_pow2_lds<kSelectThreads>(win, wp);
-        const long long nlo = s_nlo;
-        const int i0 = want_l ? (int)(l - 1 - nlo) : 0;
-        const int i1 = want_h ? (int)(h - 1 - nlo) : (int)W - 1;
+        const int i0 = want_l ? (int)(l - 1 - nlo_all) : 0;
+        const int i1 = want_h ? (int)(h - 1 - nlo_all) : (int)W - 1;
         key_l = win[i0];
         key_h = win[i1];
         csorted = win + i0;
