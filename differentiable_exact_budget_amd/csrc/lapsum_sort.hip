@@ -221,10 +221,10 @@ __global__ __launch_bounds__(kSortThreads) void k_band_root(const uint32_t* buck
 }
 
 // ---------------------------------------------------------------------------
-// multi-workgroup LSD radix sort (Onesweep-style: one histogram pass, then
-// one pass per 8-bit digit with decoupled look-back; Merrill & Garland,
-// "Single-pass parallel prefix scan with decoupled look-back", and Adinets
-// & Merrill, "Onesweep", 2022)
+// multi-workgroup LSD radix sort: one histogram pass, then one pass per
+// 8-bit digit (after Adinets & Merrill, "Onesweep", 2022; the look-back form
+// follows Merrill & Garland, "Single-pass parallel prefix scan with
+// decoupled look-back", 2016)
 // ---------------------------------------------------------------------------
 // Digit histograms of all four LSD passes in one read.  Per workgroup in LDS,
 // one atomic add per key and digit into one of four copies picked by the
