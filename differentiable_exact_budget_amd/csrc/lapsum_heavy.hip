@@ -18,7 +18,7 @@ namespace lapsum {
 constexpr int kHeavyThreads = 1024;
 constexpr int kHeavyQueuePerWave = 512;
 constexpr int kHeavyQueue = kHeavyQueuePerWave * (kHeavyThreads / 64);  // per workgroup, in LDS
-constexpr int kHeavyWaveV = 4, kHeavyGrid = 256;
+constexpr int kHeavyWaveV = 2, kHeavyGrid = 256;  // measured on gfx950: 2 beats 4
 constexpr int kHeavyAggGrid = 1024;
 
 // hoff[b]: element offset (from `base`) of heavy bucket b's slot, or
@@ -73,13 +73,22 @@ __global__ __launch_bounds__(kHeavyThreads) void k_heavy_collect(const float* __
         atomicMin(&ha.hmin[bk], key);
         atomicMax(&ha.hmax[bk], key);
     };
+    // a full wave queue: look the bucket up here and append if it overflowed
     auto put = [&](float v, uint32_t pos) {
-        if (pos < (uint32_t)kHeavyQueuePerWave) wq[pos] = v;
-        else direct(v, band_bucket(fs, v));
+        if (pos < (uint32_t)kHeavyQueuePerWave) {
+            wq[pos] = v;
+        } else {
+            const int bk = band_bucket(fs, v);
+            if (hoff[bk] != kNotHeavy) direct(v, bk);
+        }
     };
+    // the walk only queues band scores (four compares per float4); the
+    // bucket look-up, a chain of dependent LDS reads, runs after the walk for
+    // the whole queue at once (inline it stalled the wave's walk once per
+    // band score)
     auto quad = [&](float4 qv) {
-        const bool b0 = heavy_of(qv.x) >= 0, b1 = heavy_of(qv.y) >= 0;
-        const bool b2 = heavy_of(qv.z) >= 0, b3 = heavy_of(qv.w) >= 0;
+        const bool b0 = qv.x >= aL && qv.x < aR, b1 = qv.y >= aL && qv.y < aR;
+        const bool b2 = qv.z >= aL && qv.z < aR, b3 = qv.w >= aL && qv.w < aR;
         const unsigned long long m0 = ballot(b0), m1 = ballot(b1), m2 = ballot(b2), m3 = ballot(b3);
         if (m0 | m1 | m2 | m3) {
             const uint32_t c0 = (uint32_t)popc64(m0), c1 = (uint32_t)popc64(m1), c2 = (uint32_t)popc64(m2);
@@ -128,7 +137,9 @@ __global__ __launch_bounds__(kHeavyThreads) void k_heavy_collect(const float* __
         const uint32_t i = (uint32_t)tid + (uint32_t)k * kHeavyThreads;
         bk[k] = -1;
         if (i % (uint32_t)kHeavyQueuePerWave < s_wq[i / (uint32_t)kHeavyQueuePerWave]) {
-            bk[k] = band_bucket(fs, q[i]);
+            const int b = band_bucket(fs, q[i]);
+            if (hoff[b] == kNotHeavy) continue;  // a band score of a bucket that did not overflow
+            bk[k] = b;
             rk[k] = atomicAdd(&lcnt[bk[k]], 1u);
             const uint32_t key = f2key(q[i]);
             atomicMin(&lmin[bk[k]], key);
