@@ -264,6 +264,25 @@ def test_forced_fallback_and_widening(oracle_mod):
     check_forward(oracle_mod, r, k, cfg.t, p, b, b_ref=b_ref, label="overflow")
 
 
+def test_overflow_collection_wide_band(oracle_mod):
+    """A band holding most of the scores, with buckets far too small: every
+    bucket overflows, and the collection pass's walk queues more band scores
+    per wave than its LDS queue holds, so the rest go straight to their slots
+    (the queue-overflow path).  Parity with the oracle; no full-sort
+    fallback.  At 4M scores each of the pass's 4096 waves walks ~980 band
+    scores against a 512-entry queue."""
+    n = 4_000_000
+    r = np.random.default_rng(91).standard_normal(n).astype(np.float32)
+    k, t = float(n // 2), 0.05
+    g = workloads.upstream(n, 92)
+    p, b, st, grad = run(r, k, t, g, path=L.PATH_BRACKET, margin_scale=400.0, bucket_capacity=16, profile=1)
+    assert st["status"] == 0 and st["path_taken"] == 2, st
+    assert st["band_size"] > n // 2, st["band_size"]
+    assert "heavy_collect" in [nm for nm, _ in st["kernels"]]
+    b_ref = check_forward(oracle_mod, r, k, t, p, b, label="wide band, overflowed buckets")
+    check_vjp(oracle_mod, r, g, t, b_ref, grad, label="wide band, overflowed buckets")
+
+
 def test_deterministic(oracle_mod):
     r, _, cfg = workloads.config_inputs("C3", 2_000_000)
     p1, b1, _, _ = run(r, 2000.0, cfg.t)
