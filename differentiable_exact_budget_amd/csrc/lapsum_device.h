@@ -381,21 +381,6 @@ LS_DEV double block_sum(double v, double* scratch /* >= NT/64 */) {
     return r;  // valid in wave 0
 }
 
-template <int NT>
-LS_DEV unsigned long long block_sum_u64(unsigned long long v, unsigned long long* scratch) {
-    constexpr int NW = NT / 64;
-    const int w = threadIdx.x >> 6, l = lane_id();
-    v = wave_sum_u64(v);
-    if (l == 0) scratch[w] = v;
-    __syncthreads();
-    unsigned long long r = 0;
-    if (w == 0) {
-        unsigned long long x = (l < NW) ? scratch[l] : 0ull;
-        r = wave_sum_u64(x);
-    }
-    __syncthreads();
-    return r;  // valid in wave 0
-}
 
 // ascending bitonic sort of N (a power of two) keys in LDS by NT threads
 template <int NT>
@@ -734,20 +719,5 @@ LS_DEV uint32_t wave_min_u32(uint32_t v) {
     return v;
 }
 
-// device-scope ticket for the last-workgroup pattern: release this
-// workgroup's global writes, take a ticket, and tell every thread whether it
-// is in the last workgroup to finish (which then sees all earlier writes).
-LS_DEV bool last_block_ticket(unsigned int* counter, int* s_flag) {
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        __threadfence();
-        unsigned int prev = atomicAdd(counter, 1u);
-        *s_flag = (prev == gridDim.x - 1) ? 1 : 0;
-    }
-    __syncthreads();
-    bool last = *s_flag != 0;
-    if (last) __threadfence();
-    return last;
-}
 
 }  // namespace lapsum
