@@ -9,8 +9,10 @@ the bracketing path with certification (the largest configuration, 400 MB).
 
 Prints ONE JSON line.  Per-kernel durations come from HIP events recorded on
 the library's stream in a second timed loop (options.profile); the roofline
-entry uses the dominant kernel's algorithmic bytes per launch.  The CPU
-baseline times the fp64 oracle on a bounded prefix of the same workload.
+entry uses the dominant kernel's algorithmic bytes per launch.  The smaller
+workloads are timed warm (inputs left in the caches across steps) and cold
+(1 GiB written before each step).  The CPU baseline times the fp64 oracle on
+the same workload with all threads, and on one thread over a prefix.
 
 The roofline's `traffic` is the dominant kernel's HBM bytes per launch from
 hardware counters (FETCH_SIZE and WRITE_SIZE, calibrated against a plain
@@ -148,6 +150,29 @@ def time_steps(L, torch, rd, gd, k, t, steps, warmup, options=None):
     return total, per
 
 
+def time_steps_cold(L, torch, rd, gd, k, t, steps, options=None, flush_bytes=1 << 30):
+    """Per-step ms with the caches cold: before each step (outside its events)
+    a scratch buffer of `flush_bytes` is written, which evicts the inputs from
+    the 256 MB memory-side cache and the L2s."""
+    p = torch.empty_like(rd)
+    b = torch.empty(1, dtype=torch.float64, device=rd.device)
+    grad = torch.empty_like(rd)
+    flush = torch.empty(flush_bytes // 4, dtype=torch.float32, device=rd.device)
+    L.forward(rd, k, t, options=options, p_out=p, b_out=b)
+    L.vjp(rd, gd, t, b, grad_out=grad)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        flush.fill_(float(i))
+        starts[i].record()
+        L.forward(rd, k, t, options=options, p_out=p, b_out=b)
+        L.vjp(rd, gd, t, b, grad_out=grad)
+        ends[i].record()
+    torch.cuda.synchronize()
+    del flush
+    return [s.elapsed_time(e) for s, e in zip(starts, ends)]
+
+
 def kernel_profile(L, torch, rd, gd, k, t, steps):
     """Per-kernel durations (ms) from HIP events recorded by the library."""
     opt = L.default_options(profile=1)
@@ -221,15 +246,31 @@ def cpu_baseline(cfg, r, g, n_sample):
     ks = max(cfg.k * ns / r.size, 1.0)
     t = float(np.float32(cfg.t))
     oracle._load()
-    t0 = time.perf_counter()
-    b, _ = oracle.solve(rs, ks, t)
-    oracle.probs(rs, t, b)
-    oracle.vjp(rs, gs, t, b)
-    dt = time.perf_counter() - t0
-    return {"value": ns / dt, "unit": "scores/s", "cores": oracle.get_threads(), "kind": "oracle",
-            "sample": (f"first {ns} scores of the {cfg.name} input (k scaled to {ks:g})" if ns < r.size else
-                       f"the whole {cfg.name} input ({ns} scores, k={ks:g})") +
-                      f": fp64 bisection solve + p + VJP, {dt:.2f} s wall"}
+
+    def run(m):
+        km = max(cfg.k * m / r.size, 1.0)
+        t0 = time.perf_counter()
+        b, _ = oracle.solve(rs[:m], km, t)
+        oracle.probs(rs[:m], t, b)
+        oracle.vjp(rs[:m], gs[:m], t, b)
+        return time.perf_counter() - t0
+
+    dt = run(ns)
+    out = {"value": ns / dt, "unit": "scores/s", "cores": oracle.get_threads(), "kind": "oracle",
+           "sample": (f"first {ns} scores of the {cfg.name} input (k scaled to {ks:g})" if ns < r.size else
+                      f"the whole {cfg.name} input ({ns} scores, k={ks:g})") +
+                     f": fp64 bisection solve + p + VJP, {dt:.2f} s wall"}
+    # the same oracle on one thread, over a prefix sized to about 10 s
+    threads = oracle.get_threads()
+    n1 = int(min(ns, max(1 << 16, 10.0 * ns / dt / max(threads, 1))))
+    oracle.set_threads(1)
+    try:
+        d1 = run(n1)
+    finally:
+        oracle.set_threads(threads)
+    out["one_thread"] = {"value": n1 / d1, "unit": "scores/s", "cores": 1,
+                         "sample": f"first {n1} scores (k scaled to {max(cfg.k * n1 / r.size, 1.0):g}), {d1:.2f} s wall"}
+    return out
 
 
 def main():
@@ -310,14 +351,20 @@ def main():
             a = torch.from_numpy(r2).to(dev)
             b2 = torch.from_numpy(g2).to(dev)
             tot2, per2 = time_steps(L, torch, a, b2, c2.k, c2.t, 20, 3)
+            cold2 = time_steps_cold(L, torch, a, b2, c2.k, c2.t, 10)
             others[name] = {"median_ms": round(statistics.median(per2), 5),
-                            "scores_per_s": c2.n / (statistics.median(per2) * 1e-3)}
+                            "scores_per_s": c2.n / (statistics.median(per2) * 1e-3),
+                            "cold_median_ms": round(statistics.median(cold2), 5)}
             if name == "C5":
                 o5 = L.default_options(path=L.PATH_FORCE_FALLBACK)
                 tot3, per3 = time_steps(L, torch, a, b2, c2.k, c2.t, 10, 2, o5)
+                cold3 = time_steps_cold(L, torch, a, b2, c2.k, c2.t, 10, o5)
                 others["C5_forced_fallback"] = {"median_ms": round(statistics.median(per3), 5),
-                                                "scores_per_s": c2.n / (statistics.median(per3) * 1e-3)}
+                                                "scores_per_s": c2.n / (statistics.median(per3) * 1e-3),
+                                                "cold_median_ms": round(statistics.median(cold3), 5)}
             del a, b2
+        others["note"] = ("median_ms: inputs warm in the caches across steps; cold_median_ms: 1 GiB written "
+                          "before each step, outside its timed events")
         out["other_configs"] = others
 
     if not args.no_other_configs and cfg.name == "C4":
