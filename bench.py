@@ -113,6 +113,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="C4")
+    ap.add_argument("--force-fallback", action="store_true",
+                    help="bracketing pass, then the full-sort fallback regardless (path 3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0,
@@ -173,9 +175,9 @@ def time_steps_cold(L, torch, rd, gd, k, t, steps, options=None, flush_bytes=1 <
     return [s.elapsed_time(e) for s, e in zip(starts, ends)]
 
 
-def kernel_profile(L, torch, rd, gd, k, t, steps):
+def kernel_profile(L, torch, rd, gd, k, t, steps, path=0):
     """Per-kernel durations (ms) from HIP events recorded by the library."""
-    opt = L.default_options(profile=1)
+    opt = L.default_options(profile=1, path=path)
     acc = {}
     info = None
     p = torch.empty_like(rd)
@@ -289,12 +291,14 @@ def main():
     dev = torch.device("cuda:0")
     rd = torch.from_numpy(r).to(dev)
     gd = torch.from_numpy(g).to(dev)
-    opts = L.default_options(path=L.PATH_FORCE_FALLBACK) if cfg.path == "fallback" else None
+    forced = args.force_fallback or cfg.path == "fallback"
+    opts = L.default_options(path=L.PATH_FORCE_FALLBACK) if forced else None
 
     total, per = time_steps(L, torch, rd, gd, cfg.k, cfg.t, args.steps, args.warmup, opts)
     ms_per_step = total * 1000.0 / args.steps
     med = statistics.median(per)
-    kern, info = kernel_profile(L, torch, rd, gd, cfg.k, cfg.t, max(5, min(args.steps, 20)))
+    kern, info = kernel_profile(L, torch, rd, gd, cfg.k, cfg.t, max(5, min(args.steps, 20)),
+                                L.PATH_FORCE_FALLBACK if forced else 0)
 
     # roofline of the dominant kernel (largest average duration)
     dom = max(kern, key=kern.get)
@@ -314,7 +318,7 @@ def main():
             e["frac_peak"] = round(gbps / PEAK_HBM_GBPS, 4)
         kernels[name] = e
     # whole-step byte roofline (bracketing path: 32 B per score)
-    step_bytes = 32 * cfg.n if cfg.path == "bracket" else None
+    step_bytes = 32 * cfg.n if cfg.path == "bracket" and not forced else None
 
     out = {
         "metric": METRIC,
@@ -332,7 +336,9 @@ def main():
         "vs_baseline": None,
         "dtype": "fp32",
         "data": "synthetic (seeded numpy PCG64)",
-        "config": {"workload": describe(cfg), "n": cfg.n, "k": cfg.k, "t": cfg.t, "parallelism": "single GPU"},
+        "config": {"workload": describe(cfg) + (" (forced full-sort fallback)" if forced and cfg.path != "fallback"
+                                                else ""),
+                   "n": cfg.n, "k": cfg.k, "t": cfg.t, "parallelism": "single GPU"},
         "roofline": roof,
         "ceilings": ceil,
         "kernels": kernels,

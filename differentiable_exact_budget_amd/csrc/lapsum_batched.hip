@@ -20,9 +20,6 @@ __global__ __launch_bounds__(NT) void k_rows_forward(const float* __restrict__ r
     __shared__ float s_k[NT];
     __shared__ double s_v[NT];
     __shared__ int s_int[32];
-    __shared__ double s_red[NT / 64 > 0 ? NT / 64 : 1];
-    __shared__ float sg_first, sg_last;
-    __shared__ double sg_P, sg_Bx;
     __shared__ uint32_t sg_cnt, sg_off;
     __shared__ float sc_pk, sc_bk;
     __shared__ double sc_pv, sc_bv, sc_bfx;
@@ -52,10 +49,11 @@ __global__ __launch_bounds__(NT) void k_rows_forward(const float* __restrict__ r
     __syncthreads();
     if (n <= 4 * NT) sort_pow2_lds<NT>(keys, np);
     else block_sort_lds<NT, ITEMS>(keys, n, cnt, scr);
-    segment_aggregates<NT>(keys, n, inv_t, &sg_first, &sg_last, &sg_P, &sg_Bx, s_red);
     if (tid == 0) { sg_cnt = (uint32_t)n; sg_off = 0u; }
     __syncthreads();
-    SegView sv{1, &sg_first, &sg_last, &sg_P, &sg_Bx, &sg_cnt, &sg_off, keys, nullptr, nullptr, nullptr, nullptr};
+    // the whole sorted array as one segment, no aggregates: the solve tests G
+    // at every score
+    SegView sv{1, nullptr, nullptr, nullptr, nullptr, &sg_cnt, &sg_off, keys, nullptr, nullptr, nullptr, nullptr};
     SolveScratch sc{&sc_pk, &sc_pv, &sc_bk, &sc_bv, &sc_bfx, &sc_rank, nullptr, nullptr};
     Tails tl{-INFINITY, INFINITY, 0.0, 0.0, (double)n, 0.0, k, t, inv_t, -INFINITY, INFINITY};
     const SolveOut o = segment_solve<NT, ITEMS>(sv, tl, sc, s_k, s_v, s_int);

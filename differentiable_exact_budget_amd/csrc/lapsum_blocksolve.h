@@ -549,6 +549,17 @@ __device__ __attribute__((always_inline)) SolveOut segment_solve(const SegView s
     const int nseg = sv.nseg;
     __shared__ double s_root[4];
     __shared__ int s_owner;
+    // the root segment's count, offset, rank and carries (phases 1-3 to 4)
+    __shared__ uint32_t s_seg[3];
+    __shared__ float s_ck[2];
+    __shared__ double s_cv[2];
+    // Whole-array mode (no segment aggregates given, sv.P null): one segment
+    // holding every score, no tails.  Phases 1-3 are skipped: phase 4 tests
+    // G at every score itself, and when none passes the root lies below the
+    // first score.
+    const bool whole = sv.P == nullptr;
+    int sstar = 0;
+    if (!whole) {
 
     // ---- phases 1-3: carries before/after every segment, segment ranks, and
     // G at every segment's first score; each thread owns a contiguous run of
@@ -642,12 +653,9 @@ __device__ __attribute__((always_inline)) SolveOut segment_solve(const SegView s
         }
     }
     __threadfence_block();
-    const int sstar = block_max_int<NT>(cand, s_int);
+    sstar = block_max_int<NT>(cand, s_int);
     // the root segment's count, offset, rank and carries, published through
     // LDS by the thread that holds them (per == 1) or read back by thread 0
-    __shared__ uint32_t s_seg[3];
-    __shared__ float s_ck[2];
-    __shared__ double s_cv[2];
     if (sstar >= 0) {
         if (per == 1) {
             if (tid == sstar) {
@@ -679,6 +687,10 @@ __device__ __attribute__((always_inline)) SolveOut segment_solve(const SegView s
             s_seg[0] = sv.cnt[sstar]; s_seg[1] = sv.off[sstar]; s_seg[2] = sc.rank[sstar];
             s_ck[0] = sc.pk[sstar]; s_cv[0] = sc.pv[sstar]; s_ck[1] = sc.bk[sstar]; s_cv[1] = sc.bv[sstar];
         }
+    }
+    } else if (tid == 0) {  // whole array: the one segment, rank 0, no carries
+        s_seg[0] = *sv.cnt; s_seg[1] = *sv.off; s_seg[2] = 0u;
+        s_ck[0] = -INFINITY; s_cv[0] = 0.0; s_ck[1] = INFINITY; s_cv[1] = 0.0;
     }
     __threadfence_block();
     __syncthreads();
@@ -817,7 +829,7 @@ __device__ __attribute__((always_inline)) SolveOut segment_solve(const SegView s
             s_k[tid] = vv[0];
             s_v[tid] = e0 < e1 ? Bj[0] : 0.0;
             int jl = block_max_int<NT>(myj, s_int);  // (has barriers; also orders the LDS writes above)
-            if (jl < 0) jl = 0;                       // the segment's first score passed in phase 3
+            if (jl < 0 && !whole) jl = 0;             // the segment's first score passed in phase 3
             if (jl >= e0 && jl < e1) {
                 // this thread owns j*: lower end, P there, and the next score with its B
                 const int q = jl - e0;
@@ -836,7 +848,20 @@ __device__ __attribute__((always_inline)) SolveOut segment_solve(const SegView s
                 s_owner = has_next;
             }
             __syncthreads();
-            if (tid == 0) {
+            if (tid == 0 && jl < 0) {
+                // whole array, G(v_first) < k: b lies below every score, where
+                // G(b) = n - w (1 + B_first)/2 with w = e^{(b - v_first)/t}, so
+                // w = 2 (n - k)/(1 + B_first): the quadratic with A = 0.
+                // Thread 0 holds B_first (its first element is score 0).
+                const double ref = (double)vfirst;
+                const double D = tl.m + tl.c_R - tl.k;
+                const double lnw = log_root(-INFINITY, log1p(Bj[0]), D);
+                double b = ref + tl.t * lnw;
+                if (b > ref) b = ref;
+                out.jstar = -1;
+                out.b = b;
+                out.ok = (b == b) && (b > -INFINITY) && (b < INFINITY);
+            } else if (tid == 0) {
                 const double lo = s_root[1];
                 double lnA = log(s_root[0]), lnB, chi;
                 const double J = (double)(rankS + (uint32_t)jl);

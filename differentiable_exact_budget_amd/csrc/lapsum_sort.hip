@@ -39,9 +39,6 @@ __global__ __launch_bounds__(kSortThreads) void k_small_solve(const float* __res
     __shared__ float s_k[kSortThreads];
     __shared__ double s_v[kSortThreads];
     __shared__ int s_int[32];
-    __shared__ double s_red[kSortThreads / 64];
-    __shared__ float sg_first, sg_last;
-    __shared__ double sg_P, sg_Bx;
     __shared__ uint32_t sg_cnt, sg_off;
     __shared__ int s_bad;
 
@@ -67,10 +64,11 @@ __global__ __launch_bounds__(kSortThreads) void k_small_solve(const float* __res
     else block_sort_lds<kSortThreads, kSortItems>(keys, n, cnt, scr);
     if (keys_out)
         for (int i = tid; i < n; i += kSortThreads) keys_out[i] = keys[i];
-    segment_aggregates<kSortThreads>(keys, n, inv_t, &sg_first, &sg_last, &sg_P, &sg_Bx, s_red);
     if (tid == 0) { sg_cnt = (uint32_t)n; sg_off = 0u; }
     __syncthreads();
-    SegView sv{1, &sg_first, &sg_last, &sg_P, &sg_Bx, &sg_cnt, &sg_off, keys, nullptr, nullptr, nullptr, nullptr};
+    // the whole sorted array as one segment, no aggregates: the solve tests G
+    // at every score
+    SegView sv{1, nullptr, nullptr, nullptr, nullptr, &sg_cnt, &sg_off, keys, nullptr, nullptr, nullptr, nullptr};
     Tails tl{-INFINITY, INFINITY, 0.0, 0.0, (double)n, 0.0, k, t, inv_t, -INFINITY, INFINITY};
     SolveOut o = segment_solve<kSortThreads, kSortItems>(sv, tl, sc, s_k, s_v, s_int);
     if (tid == 0) {

@@ -37,7 +37,9 @@ def test_c1_small_solve(oracle_mod):
 
 
 @pytest.mark.parametrize("n,k,t", [(1, 0.3, 0.5), (2, 1.0, 0.1), (3, 2.5, 1.0), (17, 4.0, 0.05),
-                                   (1000, 999.5, 0.01), (16384, 100.0, 0.01), (5, 0.001, 0.2)])
+                                   (1000, 999.5, 0.01), (16384, 100.0, 0.01), (5, 0.001, 0.2),
+                                   # k close to n: b below every score (the solve's below-range edge)
+                                   (4096, 4095.9, 0.05), (10000, 9999.7, 0.02), (16384, 16383.5, 0.1)])
 def test_small_solve_edges(oracle_mod, n, k, t):
     rng = np.random.default_rng(n)
     r = rng.standard_normal(n).astype(np.float32)
@@ -45,6 +47,8 @@ def test_small_solve_edges(oracle_mod, n, k, t):
     p, b, st, grad = run(r, k, t, g)
     b_ref = check_forward(oracle_mod, r, k, t, p, b, label=f"n={n}")
     check_vjp(oracle_mod, r, g, t, b_ref, grad, label=f"n={n}")
+    if k > n - 0.5:
+        assert b_ref < float(r.min())  # the case is the below-range edge
 
 
 def test_small_solve_ties_and_zero_temperature(oracle_mod):
