@@ -560,134 +560,133 @@ __device__ __attribute__((always_inline)) SolveOut segment_solve(const SegView s
     const bool whole = sv.P == nullptr;
     int sstar = 0;
     if (!whole) {
-
-    // ---- phases 1-3: carries before/after every segment, segment ranks, and
-    // G at every segment's first score; each thread owns a contiguous run of
-    // segments (one segment when nseg <= NT, kept in registers) ----
-    const int per = (nseg + NT - 1) / NT;
-    const int s0 = min(nseg, tid * per), s1 = min(nseg, s0 + per);
-    float ak = -INFINITY, bk = INFINITY;
-    double av = 0.0, bvv = 0.0;
-    uint32_t rc = 0u;
-    uint32_t c1 = 0u, o1 = 0u; float f1 = 0.0f; double Bx1 = 0.0;  // the one segment (per == 1)
-    if (per == 1) {
-        if (s0 < s1) {
-            c1 = sv.cnt[s0];
-            o1 = sv.off[s0];
-            if (c1) {
-                f1 = sv.first[s0]; Bx1 = sv.Bx[s0];
-                ak = sv.last[s0]; av = sv.P[s0];
-                bk = f1; bvv = 1.0 + Bx1;
-            }
-            rc = c1;
-        }
-    } else {
-        for (int s = s0; s < s1; ++s) {
-            const uint32_t c = sv.cnt[s];
-            if (c) { float lk = ak; double lv = av; ak = sv.last[s]; av = sv.P[s]; fwd_combine(lk, lv, ak, av, inv_t); }
-            rc += c;
-        }
-        for (int s = s1 - 1; s >= s0; --s) {
-            if (sv.cnt[s]) { float k2 = sv.first[s]; double v2 = 1.0 + sv.Bx[s]; bwd_combine(k2, v2, bk, bvv, inv_t); bk = k2; bvv = v2; }
-        }
-    }
-    uint32_t rbase;
-    SegCarries cr{};  // per == 1
-    if (per == 1) {
-        const bool global = tl.fL > -INFINITY && tl.fH < INFINITY && ((double)tl.fH - (double)tl.fL) * inv_t <= 600.0;
-        __shared__ uint32_t s_su[3 * (NT / 64)];  // per-wave counts, prefixes and frame flags
-        cr = block_seg_carries<NT>(c1, f1, ak, av, Bx1, tl, global, s_k, s_v, s_su);
-        rbase = cr.rank;
-    } else {
-        rbase = block_exclusive_scan<NT>(rc, nullptr, reinterpret_cast<uint32_t*>(s_int));
-        block_scan_fwd_excl<NT>(ak, av, s_k, s_v, inv_t);
-        {   // the lower tail precedes everything
-            float tk = -INFINITY; double tv = 0.0;
-            if (tl.S_L > 0.0 && tl.aL > -INFINITY) { tk = tl.aL; tv = tl.S_L; }
-            fwd_combine(tk, tv, ak, av, inv_t);
-        }
-        block_scan_bwd_excl<NT>(bk, bvv, s_k, s_v, inv_t);
-        if (tl.S_R > 0.0 && tl.aR < INFINITY) bwd_combine(bk, bvv, tl.aR, tl.S_R, inv_t);
-    }
-    int cand = -1;
-    auto g_test = [&](int s, double Pf, double Bf, uint32_t rank) {
-        sc.bfx[s] = Bf;
-        const double G = 0.5 * Pf + (tl.m - 1.0 - (double)rank) + tl.c_R - 0.5 * Bf;
-        if (G >= tl.k) cand = max(cand, s);
-    };
-    auto g_at_first = [&](int s, float f, double Bx, float pk, double pv, float nk, double nv, uint32_t rank) {
-        const double Pf = 1.0 + (pv != 0.0 ? ecoef(((double)pk - (double)f) * inv_t) * pv : 0.0);
-        const double Bf = Bx + (nv != 0.0 ? ecoef(((double)f - (double)nk) * inv_t) * nv : 0.0);
-        g_test(s, Pf, Bf, rank);
-    };
-    if (per == 1) {
-        if (s0 < s1 && c1) {
-            // the curve at the segment's first score from the four carries
-            const double x = (double)f1;
-            double Pf = 1.0, Bf = Bx1;
-            if (cr.frame) {  // all four carries have key ref; E = e^{(x - ref)/t}
-                Pf += (cr.vf_in + cr.vf_w) / cr.E;
-                Bf += (cr.vb_in + cr.vb_w) * cr.E;
-            } else {
-                if (cr.vf_in != 0.0) Pf += cr.vf_in * exp(((double)cr.kf_in - x) * inv_t);
-                if (cr.vf_w != 0.0) Pf += cr.vf_w * exp(((double)cr.kf_w - x) * inv_t);
-                if (cr.vb_in != 0.0) Bf += cr.vb_in * exp((x - (double)cr.kb_in) * inv_t);
-                if (cr.vb_w != 0.0) Bf += cr.vb_w * exp((x - (double)cr.kb_w) * inv_t);
-            }
-            g_test(s0, Pf, Bf, rbase);
-        }
-    } else {
-        for (int s = s0; s < s1; ++s) {
-            const uint32_t c = sv.cnt[s];
-            sc.pk[s] = ak; sc.pv[s] = av; sc.rank[s] = rbase;
-            rbase += c;
-            if (c) { float lk = ak; double lv = av; ak = sv.last[s]; av = sv.P[s]; fwd_combine(lk, lv, ak, av, inv_t); }
-        }
-        for (int s = s1 - 1; s >= s0; --s) {
-            sc.bk[s] = bk; sc.bv[s] = bvv;
-            if (sv.cnt[s]) {
-                const float f = sv.first[s]; const double Bx = sv.Bx[s];
-                g_at_first(s, f, Bx, sc.pk[s], sc.pv[s], bk, bvv, sc.rank[s]);
-                float k2 = f; double v2 = 1.0 + Bx; bwd_combine(k2, v2, bk, bvv, inv_t); bk = k2; bvv = v2;
-            }
-        }
-    }
-    __threadfence_block();
-    sstar = block_max_int<NT>(cand, s_int);
-    // the root segment's count, offset, rank and carries, published through
-    // LDS by the thread that holds them (per == 1) or read back by thread 0
-    if (sstar >= 0) {
+        // ---- phases 1-3: carries before/after every segment, segment ranks, and
+        // G at every segment's first score; each thread owns a contiguous run of
+        // segments (one segment when nseg <= NT, kept in registers) ----
+        const int per = (nseg + NT - 1) / NT;
+        const int s0 = min(nseg, tid * per), s1 = min(nseg, s0 + per);
+        float ak = -INFINITY, bk = INFINITY;
+        double av = 0.0, bvv = 0.0;
+        uint32_t rc = 0u;
+        uint32_t c1 = 0u, o1 = 0u; float f1 = 0.0f; double Bx1 = 0.0;  // the one segment (per == 1)
         if (per == 1) {
-            if (tid == sstar) {
-                // the carries in (nearest score, sum) form: key = the nearest
-                // score of another segment (else the tail's end), every
-                // exponent <= 0 (the in-wave backward carry of an additive
-                // wave: at most 600 t)
-                // (the carries from other waves in their form before the move
-                // into this wave's frame: their keys are scores of those waves)
-                if (cr.last_before > -INFINITY) {
-                    ak = cr.last_before;
-                    av = 0.0;
-                    if (cr.vf_in != 0.0) av += cr.vf_in * exp(((double)cr.kf_in - (double)ak) * inv_t);
-                    if (cr.vf_o != 0.0) av += cr.vf_o * exp(((double)cr.kf_o - (double)ak) * inv_t);
-                } else if (tl.S_L > 0.0 && tl.aL > -INFINITY) { ak = tl.aL; av = tl.S_L; }
-                else { ak = -INFINITY; av = 0.0; }
-                if (cr.first_after < INFINITY) {
-                    bk = cr.first_after;
-                    bvv = 0.0;
-                    if (cr.vb_in != 0.0) bvv += cr.vb_in * exp(((double)bk - (double)cr.kb_in) * inv_t);
-                    if (cr.vb_o != 0.0) bvv += cr.vb_o * exp(((double)bk - (double)cr.kb_o) * inv_t);
-                } else if (tl.S_R > 0.0 && tl.aR < INFINITY) { bk = tl.aR; bvv = tl.S_R; }
-                else { bk = INFINITY; bvv = 0.0; }
-                sc.pk[s0] = ak; sc.pv[s0] = av; sc.bk[s0] = bk; sc.bv[s0] = bvv; sc.rank[s0] = rbase;
-                s_seg[0] = c1; s_seg[1] = o1; s_seg[2] = rbase;
-                s_ck[0] = ak; s_cv[0] = av; s_ck[1] = bk; s_cv[1] = bvv;
+            if (s0 < s1) {
+                c1 = sv.cnt[s0];
+                o1 = sv.off[s0];
+                if (c1) {
+                    f1 = sv.first[s0]; Bx1 = sv.Bx[s0];
+                    ak = sv.last[s0]; av = sv.P[s0];
+                    bk = f1; bvv = 1.0 + Bx1;
+                }
+                rc = c1;
             }
-        } else if (tid == 0) {
-            s_seg[0] = sv.cnt[sstar]; s_seg[1] = sv.off[sstar]; s_seg[2] = sc.rank[sstar];
-            s_ck[0] = sc.pk[sstar]; s_cv[0] = sc.pv[sstar]; s_ck[1] = sc.bk[sstar]; s_cv[1] = sc.bv[sstar];
+        } else {
+            for (int s = s0; s < s1; ++s) {
+                const uint32_t c = sv.cnt[s];
+                if (c) { float lk = ak; double lv = av; ak = sv.last[s]; av = sv.P[s]; fwd_combine(lk, lv, ak, av, inv_t); }
+                rc += c;
+            }
+            for (int s = s1 - 1; s >= s0; --s) {
+                if (sv.cnt[s]) { float k2 = sv.first[s]; double v2 = 1.0 + sv.Bx[s]; bwd_combine(k2, v2, bk, bvv, inv_t); bk = k2; bvv = v2; }
+            }
         }
-    }
+        uint32_t rbase;
+        SegCarries cr{};  // per == 1
+        if (per == 1) {
+            const bool global = tl.fL > -INFINITY && tl.fH < INFINITY && ((double)tl.fH - (double)tl.fL) * inv_t <= 600.0;
+            __shared__ uint32_t s_su[3 * (NT / 64)];  // per-wave counts, prefixes and frame flags
+            cr = block_seg_carries<NT>(c1, f1, ak, av, Bx1, tl, global, s_k, s_v, s_su);
+            rbase = cr.rank;
+        } else {
+            rbase = block_exclusive_scan<NT>(rc, nullptr, reinterpret_cast<uint32_t*>(s_int));
+            block_scan_fwd_excl<NT>(ak, av, s_k, s_v, inv_t);
+            {   // the lower tail precedes everything
+                float tk = -INFINITY; double tv = 0.0;
+                if (tl.S_L > 0.0 && tl.aL > -INFINITY) { tk = tl.aL; tv = tl.S_L; }
+                fwd_combine(tk, tv, ak, av, inv_t);
+            }
+            block_scan_bwd_excl<NT>(bk, bvv, s_k, s_v, inv_t);
+            if (tl.S_R > 0.0 && tl.aR < INFINITY) bwd_combine(bk, bvv, tl.aR, tl.S_R, inv_t);
+        }
+        int cand = -1;
+        auto g_test = [&](int s, double Pf, double Bf, uint32_t rank) {
+            sc.bfx[s] = Bf;
+            const double G = 0.5 * Pf + (tl.m - 1.0 - (double)rank) + tl.c_R - 0.5 * Bf;
+            if (G >= tl.k) cand = max(cand, s);
+        };
+        auto g_at_first = [&](int s, float f, double Bx, float pk, double pv, float nk, double nv, uint32_t rank) {
+            const double Pf = 1.0 + (pv != 0.0 ? ecoef(((double)pk - (double)f) * inv_t) * pv : 0.0);
+            const double Bf = Bx + (nv != 0.0 ? ecoef(((double)f - (double)nk) * inv_t) * nv : 0.0);
+            g_test(s, Pf, Bf, rank);
+        };
+        if (per == 1) {
+            if (s0 < s1 && c1) {
+                // the curve at the segment's first score from the four carries
+                const double x = (double)f1;
+                double Pf = 1.0, Bf = Bx1;
+                if (cr.frame) {  // all four carries have key ref; E = e^{(x - ref)/t}
+                    Pf += (cr.vf_in + cr.vf_w) / cr.E;
+                    Bf += (cr.vb_in + cr.vb_w) * cr.E;
+                } else {
+                    if (cr.vf_in != 0.0) Pf += cr.vf_in * exp(((double)cr.kf_in - x) * inv_t);
+                    if (cr.vf_w != 0.0) Pf += cr.vf_w * exp(((double)cr.kf_w - x) * inv_t);
+                    if (cr.vb_in != 0.0) Bf += cr.vb_in * exp((x - (double)cr.kb_in) * inv_t);
+                    if (cr.vb_w != 0.0) Bf += cr.vb_w * exp((x - (double)cr.kb_w) * inv_t);
+                }
+                g_test(s0, Pf, Bf, rbase);
+            }
+        } else {
+            for (int s = s0; s < s1; ++s) {
+                const uint32_t c = sv.cnt[s];
+                sc.pk[s] = ak; sc.pv[s] = av; sc.rank[s] = rbase;
+                rbase += c;
+                if (c) { float lk = ak; double lv = av; ak = sv.last[s]; av = sv.P[s]; fwd_combine(lk, lv, ak, av, inv_t); }
+            }
+            for (int s = s1 - 1; s >= s0; --s) {
+                sc.bk[s] = bk; sc.bv[s] = bvv;
+                if (sv.cnt[s]) {
+                    const float f = sv.first[s]; const double Bx = sv.Bx[s];
+                    g_at_first(s, f, Bx, sc.pk[s], sc.pv[s], bk, bvv, sc.rank[s]);
+                    float k2 = f; double v2 = 1.0 + Bx; bwd_combine(k2, v2, bk, bvv, inv_t); bk = k2; bvv = v2;
+                }
+            }
+        }
+        __threadfence_block();
+        sstar = block_max_int<NT>(cand, s_int);
+        // the root segment's count, offset, rank and carries, published through
+        // LDS by the thread that holds them (per == 1) or read back by thread 0
+        if (sstar >= 0) {
+            if (per == 1) {
+                if (tid == sstar) {
+                    // the carries in (nearest score, sum) form: key = the nearest
+                    // score of another segment (else the tail's end), every
+                    // exponent <= 0 (the in-wave backward carry of an additive
+                    // wave: at most 600 t)
+                    // (the carries from other waves in their form before the move
+                    // into this wave's frame: their keys are scores of those waves)
+                    if (cr.last_before > -INFINITY) {
+                        ak = cr.last_before;
+                        av = 0.0;
+                        if (cr.vf_in != 0.0) av += cr.vf_in * exp(((double)cr.kf_in - (double)ak) * inv_t);
+                        if (cr.vf_o != 0.0) av += cr.vf_o * exp(((double)cr.kf_o - (double)ak) * inv_t);
+                    } else if (tl.S_L > 0.0 && tl.aL > -INFINITY) { ak = tl.aL; av = tl.S_L; }
+                    else { ak = -INFINITY; av = 0.0; }
+                    if (cr.first_after < INFINITY) {
+                        bk = cr.first_after;
+                        bvv = 0.0;
+                        if (cr.vb_in != 0.0) bvv += cr.vb_in * exp(((double)bk - (double)cr.kb_in) * inv_t);
+                        if (cr.vb_o != 0.0) bvv += cr.vb_o * exp(((double)bk - (double)cr.kb_o) * inv_t);
+                    } else if (tl.S_R > 0.0 && tl.aR < INFINITY) { bk = tl.aR; bvv = tl.S_R; }
+                    else { bk = INFINITY; bvv = 0.0; }
+                    sc.pk[s0] = ak; sc.pv[s0] = av; sc.bk[s0] = bk; sc.bv[s0] = bvv; sc.rank[s0] = rbase;
+                    s_seg[0] = c1; s_seg[1] = o1; s_seg[2] = rbase;
+                    s_ck[0] = ak; s_cv[0] = av; s_ck[1] = bk; s_cv[1] = bvv;
+                }
+            } else if (tid == 0) {
+                s_seg[0] = sv.cnt[sstar]; s_seg[1] = sv.off[sstar]; s_seg[2] = sc.rank[sstar];
+                s_ck[0] = sc.pk[sstar]; s_cv[0] = sc.pv[sstar]; s_ck[1] = sc.bk[sstar]; s_cv[1] = sc.bv[sstar];
+            }
+        }
     } else if (tid == 0) {  // whole array: the one segment, rank 0, no carries
         s_seg[0] = *sv.cnt; s_seg[1] = *sv.off; s_seg[2] = 0u;
         s_ck[0] = -INFINITY; s_cv[0] = 0.0; s_ck[1] = INFINITY; s_cv[1] = 0.0;
