@@ -43,6 +43,7 @@ class Options(ctypes.Structure):
         ("auto_threshold", ctypes.c_int64),
         ("bucket_capacity", ctypes.c_int32),
         ("profile", ctypes.c_int32),
+        ("cert_mode", ctypes.c_int32),
     ]
 
 
@@ -64,6 +65,8 @@ class Stats(ctypes.Structure):
         ("a_R", ctypes.c_float),
         ("g_aL", ctypes.c_double),
         ("g_aR", ctypes.c_double),
+        ("g_aL_direct", ctypes.c_double),
+        ("g_aR_direct", ctypes.c_double),
         ("sum_p", ctypes.c_double),
         ("b", ctypes.c_double),
         ("tail_S_L", ctypes.c_double),
@@ -90,7 +93,7 @@ EXPORTED = [
     "lapsum_forward_batched", "lapsum_vjp_batched",
     "lapsum_release_workspaces", "lapsum_workspace_bytes",
     "lapsum_test_sort", "lapsum_test_sort_form", "lapsum_test_sample", "lapsum_test_select", "lapsum_test_filter",
-    "lapsum_test_copy", "lapsum_test_read", "lapsum_test_binomial_ranks",
+    "lapsum_test_copy", "lapsum_test_read", "lapsum_test_binomial_ranks", "lapsum_test_inject_internal",
 ]
 
 
@@ -130,7 +133,7 @@ def lib():
     L.lapsum_vjp_batched.restype = ctypes.c_int
     L.lapsum_release_workspaces.argtypes = []
     L.lapsum_release_workspaces.restype = None
-    L.lapsum_workspace_bytes.argtypes = [i64]
+    L.lapsum_workspace_bytes.argtypes = [i64, ctypes.POINTER(Options)]
     L.lapsum_workspace_bytes.restype = ctypes.c_size_t
     L.lapsum_test_sort.argtypes = [vp, i64, vp, vp]
     L.lapsum_test_sort.restype = ctypes.c_int
@@ -150,6 +153,8 @@ def lib():
     L.lapsum_test_read.restype = ctypes.c_int
     L.lapsum_test_binomial_ranks.argtypes = [i64, f64, f64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     L.lapsum_test_binomial_ranks.restype = ctypes.c_int
+    L.lapsum_test_inject_internal.argtypes = [vp]
+    L.lapsum_test_inject_internal.restype = ctypes.c_int
     _lib = L
     return L
 

@@ -78,6 +78,10 @@ struct Ctl {
     uint32_t hchunks;
     uint32_t pad3;
     unsigned long long root_off;
+    // G at the bracket ends from the filter's sums (kept for the summary the
+    // certification pass writes when it decides instead)
+    double gL_alg, gR_alg;
+    unsigned long long max_bucket, heavy_total;  // largest bucket count; scores in overflowed buckets
 };
 
 // Slots of the overflowed ("heavy") buckets, laid out by the filter's
@@ -99,7 +103,8 @@ struct HeavyArrays {
 struct HostSummary {
     unsigned long long c_L, m, c_R;
     double S_L, S_R, B_L, B_R;
-    double g_aL, g_aR;  // G at the bracket ends (the certification quantities)
+    double g_aL, g_aR;  // G at the bracket ends from the filter's sums
+    double g_aL_direct, g_aR_direct;  // the same summed directly by the certification pass (when it ran)
     float aL, aR;
     int32_t flags;
     int32_t nb;
@@ -717,6 +722,35 @@ LS_DEV uint32_t wave_min_u32(uint32_t v) {
     v = min(v, xor_lane<2>(v));
     v = min(v, xor_lane<1>(v));
     return v;
+}
+
+// wave minimum of a non-negative double (+inf allowed): the bit patterns of
+// non-negative doubles order like the values (all 64 lanes active)
+LS_DEV double wave_min_nonneg_f64(double x) {
+    unsigned long long v = (unsigned long long)__double_as_longlong(x);
+    auto step = [&](unsigned long long o) { v = o < v ? o : v; };
+    step(xor_lane64<32>(v));
+    step(xor_lane64<16>(v));
+    step(xor_lane64<8>(v));
+    step(xor_lane64<4>(v));
+    step(xor_lane64<2>(v));
+    step(xor_lane64<1>(v));
+    return __longlong_as_double((long long)v);
+}
+
+// minimum of a non-negative double over the workgroup, in every thread
+// (s: >= NT/64 doubles; every thread calls it)
+template <int NT>
+LS_DEV double block_min_nonneg_f64(double x, double* s) {
+    constexpr int NW = NT / 64;
+    const double wm = wave_min_nonneg_f64(x);
+    if (lane_id() == 0) s[threadIdx.x >> 6] = wm;
+    __syncthreads();
+    double r = s[0];
+#pragma unroll
+    for (int q = 1; q < NW; ++q) r = fmin(r, s[q]);
+    __syncthreads();
+    return r;
 }
 
 

@@ -44,7 +44,15 @@ namespace {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
+// Scratch memory of one (device, stream).  A call holds `mu` from the moment
+// it finds its workspace until it returns, so calls on one stream from
+// several host threads take turns (their device work is ordered on the
+// stream in the order they took the workspace), and a release waits for the
+// call in flight.  Workspace objects are never deleted: a release frees
+// their memory and the next call allocates it again.
 struct Workspace {
+    std::mutex mu;
+    bool inject_internal = false;  // lapsum_test_inject_internal: mark the next solve failed
     int device = 0;
     hipStream_t stream = nullptr;
     long long n_cap = 0;
@@ -140,17 +148,22 @@ Layout make_layout(long long n_cap) {
     return L;
 }
 
-void free_ws(Workspace* w) {
-    if (!w) return;
+// frees a workspace's memory (the caller holds w->mu)
+void free_ws_memory(Workspace* w) {
     int cur = 0;
     (void)hipGetDevice(&cur);
     (void)hipSetDevice(w->device);
     (void)hipStreamSynchronize(w->stream);
     for (hipEvent_t e : w->events) (void)hipEventDestroy(e);
+    w->events.clear();
     if (w->base) (void)hipFree(w->base);
     if (w->hs) (void)hipHostFree(w->hs);
+    w->base = nullptr;
+    w->bytes = 0;
+    w->n_cap = 0;
+    w->hs = nullptr;
+    w->hs_dev = nullptr;
     (void)hipSetDevice(cur);
-    delete w;
 }
 
 lapsum_status_t alloc_ws(Workspace* w, long long n_cap) {
@@ -201,44 +214,60 @@ lapsum_status_t alloc_ws(Workspace* w, long long n_cap) {
     return LAPSUM_OK;
 }
 
-lapsum_status_t get_ws(hipStream_t stream, long long n, Workspace** out) {
+// The workspace of (current device, stream), locked for the rest of the
+// caller's call and grown to forwards of n scores if it is smaller.
+struct WsGuard {
+    Workspace* w = nullptr;
+    std::unique_lock<std::mutex> lk;
+};
+
+lapsum_status_t get_ws(hipStream_t stream, long long n, WsGuard* g) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return LAPSUM_ERR_HIP;
-    std::lock_guard<std::mutex> lk(g_mu);
-    auto key = std::make_pair(dev, stream);
-    auto it = g_ws.find(key);
-    Workspace* w = (it == g_ws.end()) ? nullptr : it->second;
-    if (w && w->n_cap >= n) { *out = w; return LAPSUM_OK; }
-    if (w) {
-        // grow: wait for this stream's work, then replace the device buffer
-        (void)hipStreamSynchronize(stream);
-        (void)hipFree(w->base);
-        w->base = nullptr;
-    } else {
-        w = new Workspace();
-        w->device = dev;
-        w->stream = stream;
-        void* hp = nullptr;
-        if (hipHostMalloc(&hp, sizeof(HostSummary), hipHostMallocCoherent | hipHostMallocMapped) != hipSuccess) {
-            delete w;
-            return LAPSUM_ERR_OUT_OF_MEMORY;
+    Workspace* w = nullptr;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        auto key = std::make_pair(dev, stream);
+        auto it = g_ws.find(key);
+        if (it == g_ws.end()) {
+            w = new Workspace();
+            w->device = dev;
+            w->stream = stream;
+            g_ws[key] = w;
+        } else {
+            w = it->second;
         }
+    }
+    std::unique_lock<std::mutex> lk(w->mu);
+    if (!w->hs) {
+        void* hp = nullptr;
+        if (hipHostMalloc(&hp, sizeof(HostSummary), hipHostMallocCoherent | hipHostMallocMapped) != hipSuccess)
+            return LAPSUM_ERR_OUT_OF_MEMORY;
         std::memset(hp, 0, sizeof(HostSummary));
         w->hs = reinterpret_cast<HostSummary*>(hp);
         void* dp = nullptr;
         if (hipHostGetDevicePointer(&dp, hp, 0) != hipSuccess) dp = hp;
         w->hs_dev = reinterpret_cast<HostSummary*>(dp);
-        g_ws[key] = w;
+        w->seq = 0;
     }
-    lapsum_status_t st = alloc_ws(w, std::max<long long>(n, 1 << 16));
-    if (st != LAPSUM_OK) {
-        g_ws.erase(key);
-        if (w->hs) (void)hipHostFree(w->hs);
-        if (w->base) (void)hipFree(w->base);
-        delete w;
-        return st;
+    if (!w->base || w->n_cap < n) {
+        if (w->base) {
+            // grow: wait for this stream's work, then replace the device buffer
+            (void)hipStreamSynchronize(stream);
+            (void)hipFree(w->base);
+            w->base = nullptr;
+            w->n_cap = 0;
+        }
+        lapsum_status_t st = alloc_ws(w, std::max<long long>(n, 1 << 16));
+        if (st != LAPSUM_OK) {
+            if (w->base) (void)hipFree(w->base);
+            w->base = nullptr;
+            w->n_cap = 0;
+            return st;
+        }
     }
-    *out = w;
+    g->w = w;
+    g->lk = std::move(lk);
     return LAPSUM_OK;
 }
 
@@ -335,6 +364,9 @@ void binomial_ranks(long long s, double q, double delta, long long* l_out, long 
     *l_out = l;
     *h_out = h;
     std::lock_guard<std::mutex> lk(mu);
+    // a bounded memo: a caller whose budget changes every call (a learned k)
+    // would otherwise grow it without end
+    if (cache.size() >= 64) cache.clear();
     cache[std::make_tuple(s, q, delta)] = std::make_pair(l, h);
 }
 
@@ -420,6 +452,23 @@ lapsum_status_t check_args(const float* r, int64_t n, double k, float t, const v
     return LAPSUM_OK;
 }
 
+// status of the device-side checks recorded in the control block's flags
+lapsum_status_t device_status(int flags) {
+    if (flags & kFlagNonFinite) return LAPSUM_ERR_NONFINITE_INPUT;
+    if (flags & kFlagInternal) return LAPSUM_ERR_INTERNAL;
+    return LAPSUM_OK;
+}
+
+// A test hook (lapsum_test_inject_internal): the next solve on the workspace
+// ends with its control block marked as a failed consistency check.
+void apply_injected(Workspace* w, hipStream_t st) {
+    if (!w->inject_internal) return;
+    w->inject_internal = false;
+    launch_or_flags(w->ctl, kFlagInternal, st);
+}
+
+// Waits for the call's work, fills the stats and returns the device-side
+// status (a call with stats reports what the device found)
 lapsum_status_t fill_stats(Workspace* w, hipStream_t st, long long n, lapsum_stats_t* stats) {
     if (!stats) return LAPSUM_OK;
     launch_sum_p(w->ctl, w->part, w->probs_parts, st);
@@ -428,10 +477,8 @@ lapsum_status_t fill_stats(Workspace* w, hipStream_t st, long long n, lapsum_sta
     if (hipMemcpy(&c, w->ctl, sizeof(Ctl), hipMemcpyDeviceToHost) != hipSuccess) return LAPSUM_ERR_HIP;
     stats->b = c.b;
     stats->sum_p = c.sum_p;
-    if (c.flags & kFlagNonFinite) stats->status = LAPSUM_ERR_NONFINITE_INPUT;
-    else if (c.flags & kFlagInternal) stats->status = LAPSUM_ERR_INTERNAL;
-    else stats->status = LAPSUM_OK;
-    return LAPSUM_OK;
+    stats->status = device_status(c.flags);
+    return (lapsum_status_t)stats->status;
 }
 
 // Waits for the band solve's root summary (written when the host asked for
@@ -453,17 +500,18 @@ lapsum_status_t wait_root(Workspace* w, hipStream_t st, unsigned int seq) {
     }
 }
 
-lapsum_status_t forward_impl(const float* r, int64_t n, double k, float t_f, float* p, double* b_out,
-                             const lapsum_options_t& opt, lapsum_stats_t* stats, hipStream_t st) {
-    lapsum_status_t a = check_args(r, n, k, t_f, p, b_out);
-    if (a != LAPSUM_OK) return a;
+lapsum_status_t check_options(const lapsum_options_t& opt) {
     if (opt.path < LAPSUM_PATH_AUTO || opt.path > LAPSUM_PATH_FORCE_FALLBACK) return LAPSUM_ERR_INVALID_ARGUMENT;
     if (opt.bucket_capacity < 1 || opt.bucket_capacity > kBucketCapMax || !(opt.sample_factor > 0.0) ||
-        !(opt.delta > 0.0 && opt.delta < 0.5) || !(opt.margin_scale >= 0.0) || opt.max_widen < 0)
+        !(opt.delta > 0.0 && opt.delta < 0.5) || !(opt.margin_scale >= 0.0) || opt.max_widen < 0 ||
+        opt.cert_mode < 0 || opt.cert_mode > 1)
         return LAPSUM_ERR_INVALID_ARGUMENT;
-    Workspace* w = nullptr;
-    lapsum_status_t gs = get_ws(st, n, &w);
-    if (gs != LAPSUM_OK) return gs;
+    return LAPSUM_OK;
+}
+
+// the forward solve on a workspace the caller holds (arguments checked)
+lapsum_status_t forward_locked(Workspace* w, const float* r, int64_t n, double k, float t_f, float* p, double* b_out,
+                               const lapsum_options_t& opt, lapsum_stats_t* stats, hipStream_t st) {
     const double t = (double)t_f;
     Timer tm{w, st, opt.profile != 0};
     if (stats) {
@@ -482,10 +530,12 @@ lapsum_status_t forward_impl(const float* r, int64_t n, double k, float t_f, flo
         if (stats) {
             stats->path_taken = 1;
             stats->band_size = n;
+            apply_injected(w, st);
             lapsum_status_t fs = fill_stats(w, st, n, stats);
             tm.collect(stats);
             return fs;
         }
+        apply_injected(w, st);
         return LAPSUM_OK;
     }
 
@@ -521,8 +571,16 @@ lapsum_status_t forward_impl(const float* r, int64_t n, double k, float t_f, flo
                                               w->part, st);
         tm.end();
         tm.begin("finalize");
-        launch_filter_finalize(n, t, w->ctl, w->bucket_cnt, cap, w->part, fparts, w->hs_dev, seq, st, k, &w->heavy);
+        launch_filter_finalize(n, t, w->ctl, w->bucket_cnt, cap, w->part, fparts, w->hs_dev, seq, st, k, &w->heavy,
+                               opt.cert_mode == 1);
         tm.end();
+        if (opt.cert_mode == 1) {
+            // the pages' certification: one more linear pass sums G(a_L) and
+            // G(a_R) directly, and its verdict decides
+            tm.begin("cert");
+            launch_cert(r, n, t, w->ctl, w->part, w->hs_dev, seq, k, st);
+            tm.end();
+        }
         if (path != LAPSUM_PATH_FORCE_FALLBACK) {
             // launched before the host has the verdict: they run only when the
             // finalize kernel opened the gate (certified, every band score
@@ -571,6 +629,8 @@ lapsum_status_t forward_impl(const float* r, int64_t n, double k, float t_f, flo
         stats->a_R = br.h.aR;
         stats->g_aL = br.gL;
         stats->g_aR = br.gR;
+        stats->g_aL_direct = br.h.g_aL_direct;
+        stats->g_aR_direct = br.h.g_aR_direct;
         stats->tail_S_L = br.h.S_L; stats->tail_S_R = br.h.S_R;
         stats->band_B_L = br.h.B_L; stats->band_B_R = br.h.B_R;
     }
@@ -585,10 +645,12 @@ lapsum_status_t forward_impl(const float* r, int64_t n, double k, float t_f, flo
         // the gate was open: the band solve and p pass launched behind the filter did the work
         if (stats) {
             stats->path_taken = 2;
+            apply_injected(w, st);
             lapsum_status_t fs = fill_stats(w, st, n, stats);
             tm.collect(stats);
             return fs;
         }
+        apply_injected(w, st);
         return LAPSUM_OK;
     }
     // Overflowed buckets: the finalize kernel laid out a slot for each (flag
@@ -642,10 +704,12 @@ lapsum_status_t forward_impl(const float* r, int64_t n, double k, float t_f, flo
     if (hipGetLastError() != hipSuccess) return LAPSUM_ERR_HIP;
     if (stats) {
         stats->path_taken = fallback ? 3 : 2;
+        apply_injected(w, st);
         lapsum_status_t fs = fill_stats(w, st, n, stats);
         tm.collect(stats);
         return fs;
     }
+    apply_injected(w, st);
     return LAPSUM_OK;
 }
 
@@ -760,9 +824,9 @@ lapsum_status_t order_stats_impl(Workspace* w, const float* r, long long n, long
         Ctl c;
         if (hipMemcpy(&c, w->ctl, sizeof(Ctl), hipMemcpyDeviceToHost) != hipSuccess) return LAPSUM_ERR_HIP;
         stats->b = c.b;
-        stats->status = (c.flags & kFlagNonFinite) ? LAPSUM_ERR_NONFINITE_INPUT
-                        : (c.flags & kFlagInternal) ? LAPSUM_ERR_INTERNAL : LAPSUM_OK;
+        stats->status = device_status(c.flags);
         tm.collect(stats);
+        return (lapsum_status_t)stats->status;
     }
     return LAPSUM_OK;
 }
@@ -796,6 +860,7 @@ void lapsum_default_options(lapsum_options_t* opt) {
     opt->auto_threshold = 1000000;
     opt->bucket_capacity = kBucketCapMax;
     opt->profile = 0;
+    opt->cert_mode = 0;
 }
 
 const char* lapsum_status_string(lapsum_status_t s) {
@@ -814,8 +879,15 @@ lapsum_status_t lapsum_forward_ex(const float* scores, int64_t n, double k, floa
                                   const lapsum_options_t* opt, lapsum_stats_t* stats, lapsum_stream_t stream) {
     lapsum_options_t o;
     if (opt) o = *opt; else lapsum_default_options(&o);
+    lapsum_status_t a = check_args(scores, n, k, t, p_out, b_out);
+    if (a != LAPSUM_OK) return a;
+    if (check_options(o) != LAPSUM_OK) return LAPSUM_ERR_INVALID_ARGUMENT;
     try {
-        return forward_impl(scores, n, k, t, p_out, b_out, o, stats, reinterpret_cast<hipStream_t>(stream));
+        hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+        WsGuard wsg;
+        lapsum_status_t gs = get_ws(st, n, &wsg);
+        if (gs != LAPSUM_OK) return gs;
+        return forward_locked(wsg.w, scores, n, k, t, p_out, b_out, o, stats, st);
     } catch (...) {
         return LAPSUM_ERR_INTERNAL;
     }
@@ -837,9 +909,10 @@ lapsum_status_t vjp_impl(const float* scores, const float* g, int64_t n, float t
     if (!(t > 0.0f) || !std::isfinite(t)) return LAPSUM_ERR_INVALID_ARGUMENT;
     try {
         hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-        Workspace* w = nullptr;
-        lapsum_status_t gs = get_ws(st, 0, &w);
+        WsGuard wsg;
+        lapsum_status_t gs = get_ws(st, 0, &wsg);
         if (gs != LAPSUM_OK) return gs;
+        Workspace* w = wsg.w;
         const bool prof = opt && opt->profile;
         if (stats) std::memset(stats, 0, sizeof(*stats));
         if (prof) {
@@ -895,11 +968,30 @@ lapsum_status_t lapsum_vjp(const float* scores, const float* p, const float* g, 
 
 void lapsum_release_workspaces(void) {
     std::lock_guard<std::mutex> lk(g_mu);
-    for (auto& kv : g_ws) free_ws(kv.second);
-    g_ws.clear();
+    for (auto& kv : g_ws) {
+        std::lock_guard<std::mutex> wl(kv.second->mu);  // waits for a call in flight on that stream
+        free_ws_memory(kv.second);
+    }
 }
 
-size_t lapsum_workspace_bytes(int64_t n) { return make_layout(std::max<long long>(n, 1 << 16)).total; }
+size_t lapsum_workspace_bytes(int64_t n, const lapsum_options_t* opt) {
+    lapsum_options_t o;
+    if (opt) o = *opt; else lapsum_default_options(&o);
+    if (n < 1 || n > 0xFFFFFFFFll || check_options(o) != LAPSUM_OK) return 0;
+    return make_layout(std::max<long long>(n, 1 << 16)).total;
+}
+
+lapsum_status_t lapsum_test_inject_internal(lapsum_stream_t stream) {
+    try {
+        WsGuard wsg;
+        lapsum_status_t gs = get_ws(reinterpret_cast<hipStream_t>(stream), 0, &wsg);
+        if (gs != LAPSUM_OK) return gs;
+        wsg.w->inject_internal = true;
+        return LAPSUM_OK;
+    } catch (...) {
+        return LAPSUM_ERR_INTERNAL;
+    }
+}
 
 // ---------------------------------------------------------------------------
 // stage entry points for parity tests
@@ -937,9 +1029,10 @@ lapsum_status_t lapsum_test_sort_form(const float* scores, int64_t n, float* out
                                       lapsum_stream_t stream) {
     if (!scores || !out || n < 1 || n > 0xFFFFFFFFll || form < 0 || form > 2) return LAPSUM_ERR_INVALID_ARGUMENT;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    Workspace* w = nullptr;
-    lapsum_status_t gs = get_ws(st, n, &w);
+    WsGuard wsg;
+    lapsum_status_t gs = get_ws(st, n, &wsg);
     if (gs != LAPSUM_OK) return gs;
+    Workspace* w = wsg.w;
     const double k = n > 1 ? 0.5 * (double)n : 0.5;
     if (n <= kSmallMax) {
         launch_small_solve(scores, (int)n, k, 1.0, w->ctl, w->sc, nullptr, w->keysB, st);
@@ -975,9 +1068,10 @@ lapsum_status_t lapsum_test_select(const float* x, int64_t s, int64_t l, int64_t
                                    int32_t* nbuckets_host, lapsum_stream_t stream) {
     if (!x || s < 1 || s > kSampleMax || l < 0 || h > s + 1 || l > s || h < 1) return LAPSUM_ERR_INVALID_ARGUMENT;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    Workspace* w = nullptr;
-    lapsum_status_t gs = get_ws(st, 0, &w);
+    WsGuard wsg;
+    lapsum_status_t gs = get_ws(st, 0, &wsg);
     if (gs != LAPSUM_OK) return gs;
+    Workspace* w = wsg.w;
     launch_select(x, (int)s, l, h, kBucketCapMax, w->ctl, w->sp, w->iw, w->bucket_cnt, st);
     if (hipStreamSynchronize(st) != hipSuccess) return LAPSUM_ERR_HIP;
     Ctl c;
@@ -993,9 +1087,10 @@ lapsum_status_t lapsum_test_filter(const float* scores, int64_t n, float t, floa
                                    int32_t* nbuckets_host, int64_t* bucket_sizes_host, lapsum_stream_t stream) {
     if (!scores || n < 1 || n > 0xFFFFFFFFll || !(t > 0.0f) || !(a_L <= a_R)) return LAPSUM_ERR_INVALID_ARGUMENT;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    Workspace* w = nullptr;
-    lapsum_status_t gs = get_ws(st, n, &w);
+    WsGuard wsg;
+    lapsum_status_t gs = get_ws(st, n, &wsg);
     if (gs != LAPSUM_OK) return gs;
+    Workspace* w = wsg.w;
     // a two-point "sample" whose order statistics are exactly a_L and a_R
     float two[2] = {a_L, a_R};
     if (hipMemcpy(w->sample, two, sizeof(two), hipMemcpyHostToDevice) != hipSuccess) return LAPSUM_ERR_HIP;
@@ -1055,9 +1150,10 @@ lapsum_status_t lapsum_topk_threshold(const float* scores, int64_t n, int64_t k,
     if (a != LAPSUM_OK || !tau_out) return LAPSUM_ERR_INVALID_ARGUMENT;
     try {
         hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-        Workspace* w = nullptr;
-        lapsum_status_t gs = get_ws(st, n, &w);
+        WsGuard wsg;
+        lapsum_status_t gs = get_ws(st, n, &wsg);
         if (gs != LAPSUM_OK) return gs;
+        Workspace* w = wsg.w;
         return order_stats_impl(w, scores, n, k, o, stats, st, tau_out);
     } catch (...) {
         return LAPSUM_ERR_INTERNAL;
@@ -1072,9 +1168,10 @@ lapsum_status_t lapsum_hard_topk(const float* scores, int64_t n, int64_t k, floa
     if (a != LAPSUM_OK || !mask_out) return LAPSUM_ERR_INVALID_ARGUMENT;
     try {
         hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-        Workspace* w = nullptr;
-        lapsum_status_t gs = get_ws(st, n, &w);
+        WsGuard wsg;
+        lapsum_status_t gs = get_ws(st, n, &wsg);
         if (gs != LAPSUM_OK) return gs;
+        Workspace* w = wsg.w;
         lapsum_status_t rs = order_stats_impl(w, scores, n, k, o, stats, st, tau_out);
         if (rs == LAPSUM_ERR_NONFINITE_INPUT) {
             launch_fill(mask_out, n, std::numeric_limits<float>::quiet_NaN(), st);
@@ -1096,9 +1193,10 @@ lapsum_status_t lapsum_dftopk(const float* scores, int64_t n, int64_t k, float t
     if (a != LAPSUM_OK || !p_out || !(t > 0.0f) || !std::isfinite(t)) return LAPSUM_ERR_INVALID_ARGUMENT;
     try {
         hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-        Workspace* w = nullptr;
-        lapsum_status_t gs = get_ws(st, n, &w);
+        WsGuard wsg;
+        lapsum_status_t gs = get_ws(st, n, &wsg);
         if (gs != LAPSUM_OK) return gs;
+        Workspace* w = wsg.w;
         lapsum_status_t rs = order_stats_impl(w, scores, n, k, o, nullptr, st, nullptr);
         if (rs == LAPSUM_ERR_NONFINITE_INPUT) {
             launch_set_nan_b(w->ctl, b_out, st);
@@ -1117,8 +1215,8 @@ lapsum_status_t lapsum_dftopk(const float* scores, int64_t n, int64_t k, float t
             if (hipMemcpy(&c, w->ctl, sizeof(Ctl), hipMemcpyDeviceToHost) != hipSuccess) return LAPSUM_ERR_HIP;
             stats->b = c.b;
             stats->sum_p = c.sum_p;
-            stats->status = (c.flags & kFlagNonFinite) ? LAPSUM_ERR_NONFINITE_INPUT
-                            : (c.flags & kFlagInternal) ? LAPSUM_ERR_INTERNAL : LAPSUM_OK;
+            stats->status = device_status(c.flags);
+            return (lapsum_status_t)stats->status;
         }
         return LAPSUM_OK;
     } catch (...) {
@@ -1153,9 +1251,10 @@ lapsum_status_t lapsum_forward_batched(const float* scores, int64_t rows, int64_
         }
         lapsum_options_t o;
         lapsum_default_options(&o);
-        Workspace* w = nullptr;
-        lapsum_status_t gs = get_ws(st, n, &w);
+        WsGuard wsg;
+        lapsum_status_t gs = get_ws(st, n, &wsg);
         if (gs != LAPSUM_OK) return gs;
+        Workspace* w = wsg.w;
         for (int64_t i = 0; i < rows; ++i) {
             const double ki = k_rows ? kh[(size_t)i] : k;
             const float* ri = scores + i * n;
@@ -1164,7 +1263,7 @@ lapsum_status_t lapsum_forward_batched(const float* scores, int64_t rows, int64_
                 launch_fill(p_out + i * n, n, std::numeric_limits<float>::quiet_NaN(), st);
                 continue;
             }
-            lapsum_status_t rs = forward_impl(ri, n, ki, t, p_out + i * n, b_out + i, o, nullptr, st);
+            lapsum_status_t rs = forward_locked(w, ri, n, ki, t, p_out + i * n, b_out + i, o, nullptr, st);
             if (rs != LAPSUM_OK && rs != LAPSUM_ERR_NONFINITE_INPUT) return rs;
         }
         return hip_ok(hipGetLastError());
@@ -1184,9 +1283,10 @@ lapsum_status_t lapsum_vjp_batched(const float* scores, const float* g, int64_t 
             launch_rows_vjp(scores, g, rows, (int)n, (double)t, b, grad_out, st);
             return hip_ok(hipGetLastError());
         }
-        Workspace* w = nullptr;
-        lapsum_status_t gs = get_ws(st, 0, &w);
+        WsGuard wsg;
+        lapsum_status_t gs = get_ws(st, 0, &wsg);
         if (gs != LAPSUM_OK) return gs;
+        Workspace* w = wsg.w;
         for (int64_t i = 0; i < rows; ++i)
             launch_vjp(scores + i * n, g + i * n, n, (double)t, b + i, grad_out + i * n, w->ctl, w->part, st, nullptr,
                        false, nullptr, nullptr);

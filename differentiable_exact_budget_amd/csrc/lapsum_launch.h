@@ -27,9 +27,17 @@ int stream_blocks(long long n);
 // partials) and its finalize kernel; launch_filter runs both
 int launch_filter_pass(const float* r, long long n, double t, Ctl* ctl, const float* sp, const float* iw,
                        uint32_t* bucket_cnt, uint32_t* bucket_vals, int cap, double* part, hipStream_t st);
+// defer: the certification pass (launch_cert) decides instead; the gate
+// stays shut and the host summary is left to it
 void launch_filter_finalize(long long n, double t, Ctl* ctl, const uint32_t* bucket_cnt, int cap, double* part,
                             int nparts, HostSummary* hs_dev, unsigned int seq, hipStream_t st, double k,
-                            const HeavyArrays* ha);
+                            const HeavyArrays* ha, bool defer = false);
+// The certification pass as a pass of its own (cert_mode 1): G(a_L) and
+// G(a_R) summed directly over every score, then the verdict, the gate and the
+// host summary (after a deferred launch_filter_finalize)
+void launch_cert(const float* r, long long n, double t, Ctl* ctl, double* part, HostSummary* hs_dev,
+                 unsigned int seq, double k, hipStream_t st);
+void launch_or_flags(Ctl* ctl, int flags, hipStream_t st);
 void launch_filter(const float* r, long long n, double t, Ctl* ctl, const float* sp, const float* iw,
                    uint32_t* bucket_cnt, uint32_t* bucket_vals, int cap, double* part, unsigned long long* partc,
                    HostSummary* hs_dev, unsigned int seq, hipStream_t st, double k,

@@ -330,10 +330,12 @@ __global__ __launch_bounds__(NT) void k_filter(const float* __restrict__ r, long
 //   G(a_R) = e^{(a_L - a_R)/t} S_L/2 + B_R/2 + c_R - S_R/2,
 // and the bracket holds iff G(a_L) >= k > G(a_R) (an open end holds); the
 // gate opens when it holds and every band score was stored.
+// defer: the certification pass decides after this kernel (it opens the
+// gate and writes the host summary; here the gate stays shut).
 __global__ __launch_bounds__(kFinalizeThreads) void k_filter_finalize(const FilterPart* part, int nparts, long long n,
                                                                      Ctl* ctl, const uint32_t* bucket_cnt, int cap,
                                                                      HostSummary* hs, unsigned int seq, double k,
-                                                                     double t, HeavyArrays ha) {
+                                                                     double t, HeavyArrays ha, int defer) {
     constexpr int NT = kFinalizeThreads;
     __shared__ double s_rd[4 * (NT / 64)];
     __shared__ unsigned long long s_ru[3 * (NT / 64)];
@@ -427,13 +429,16 @@ __global__ __launch_bounds__(kFinalizeThreads) void k_filter_finalize(const Filt
     if (tid == 0) {
         ctl->S_L = T0; ctl->S_R = T1; ctl->B_L = T2; ctl->B_R = T3;
         ctl->c_L = CL; ctl->c_R = CR; ctl->m = M;
-        ctl->gate = (flags == kFlagCertified) ? 1 : 0;
+        ctl->gate = (!defer && flags == kFlagCertified) ? 1 : 0;
         ctl->flags = flags;
         ctl->hchunks = hch;
-        if (hs) {
+        ctl->gL_alg = gL; ctl->gR_alg = gR;
+        ctl->max_bucket = mx[2]; ctl->heavy_total = htot;
+        if (hs && !defer) {
             hs->c_L = CL; hs->m = M; hs->c_R = CR;
             hs->S_L = T0; hs->S_R = T1; hs->B_L = T2; hs->B_R = T3;
             hs->g_aL = gL; hs->g_aR = gR;
+            hs->g_aL_direct = 0.0; hs->g_aR_direct = 0.0;
             hs->aL = ctl->aL; hs->aR = ctl->aR;
             hs->flags = flags; hs->nb = nb; hs->max_bucket = mx[2];
             hs->heavy_total = htot; hs->hchunks = hch;
@@ -471,12 +476,12 @@ int launch_filter_pass(const float* r, long long n, double t, Ctl* ctl, const fl
 
 void launch_filter_finalize(long long n, double t, Ctl* ctl, const uint32_t* bucket_cnt, int cap, double* part,
                             int nparts, HostSummary* hs_dev, unsigned int seq, hipStream_t st, double k,
-                            const HeavyArrays* ha) {
+                            const HeavyArrays* ha, bool defer) {
     HeavyArrays hv{};
     if (ha) hv = *ha;
     hipLaunchKernelGGL(k_filter_finalize, dim3(1), dim3(kFinalizeThreads), 0, st,
                        reinterpret_cast<const FilterPart*>(part), nparts, n, ctl, bucket_cnt, cap, hs_dev, seq, k, t,
-                       hv);
+                       hv, defer ? 1 : 0);
 }
 
 void launch_filter(const float* r, long long n, double t, Ctl* ctl, const float* sp, const float* iw,
@@ -484,6 +489,139 @@ void launch_filter(const float* r, long long n, double t, Ctl* ctl, const float*
                    HostSummary* hs_dev, unsigned int seq, hipStream_t st, double k, const HeavyArrays* ha) {
     const int blocks = launch_filter_pass(r, n, t, ctl, sp, iw, bucket_cnt, bucket_vals, cap, part, st);
     launch_filter_finalize(n, t, ctl, bucket_cnt, cap, part, blocks, hs_dev, seq, st, k, ha);
+}
+
+// ---------------------------------------------------------------------------
+// certification as a pass of its own (the arxivdaily abstract: the bracket is
+// verified with one additional linear pass; gist.science summary section 2.2,
+// bracketing step 4).  G(a) = sum_i F((r_i - a)/t) at a = a_L and a = a_R,
+// summed directly over every score: for each end, the scores below it give
+// e^{(r - a)/t}/2, the others 1 - e^{(a - r)/t}/2, kept as a count and two
+// fp64 sums.  An open end needs no special case: a_L = -inf counts every
+// score as at or above it (G = n) and a_R = +inf none (G = 0).
+// ---------------------------------------------------------------------------
+struct CertPart {
+    double sb[2];              // per end: sum over scores below it of e^{(r - a)/t}
+    double sa[2];              // per end: sum over the others of e^{(a - r)/t}
+    unsigned long long ge[2];  // per end: scores at or above it
+};
+constexpr int kCertV = 4, kCertGrid = 8192, kCertFinalThreads = 1024;
+
+template <bool VEC>
+__global__ __launch_bounds__(kStreamThreads) void k_cert(const float* __restrict__ r, long long n, float ls,
+                                                          const Ctl* ctl, CertPart* part) {
+    constexpr int NWV = kStreamThreads / 64;
+    __shared__ double s_rd[4 * NWV];
+    __shared__ unsigned long long s_ru[2 * NWV];
+    __shared__ uint32_t s_rm[NWV];
+    const float aL = ctl->aL, aR = ctl->aR;
+    const int tid = threadIdx.x;
+    double sbL = 0.0, saL = 0.0, sbR = 0.0, saR = 0.0;
+    uint32_t geL = 0u, geR = 0u;
+    auto one = [&](float v, float& bL, float& xL, float& bR, float& xR) {
+        const float eL = __builtin_amdgcn_exp2f(-fabsf(v - aL) * ls);
+        const float eR = __builtin_amdgcn_exp2f(-fabsf(v - aR) * ls);
+        const bool belowL = v < aL, belowR = v < aR;
+        bL += belowL ? eL : 0.0f;
+        xL += belowL ? 0.0f : eL;
+        bR += belowR ? eR : 0.0f;
+        xR += belowR ? 0.0f : eR;
+        geL += belowL ? 0u : 1u;
+        geR += belowR ? 0u : 1u;
+    };
+    auto quad = [&](float4 q, long long) {
+        float bL = 0.0f, xL = 0.0f, bR = 0.0f, xR = 0.0f;
+        one(q.x, bL, xL, bR, xR); one(q.y, bL, xL, bR, xR); one(q.z, bL, xL, bR, xR); one(q.w, bL, xL, bR, xR);
+        sbL += (double)bL; saL += (double)xL; sbR += (double)bR; saR += (double)xR;
+    };
+    auto single = [&](float v) {
+        float bL = 0.0f, xL = 0.0f, bR = 0.0f, xR = 0.0f;
+        one(v, bL, xL, bR, xR);
+        sbL += (double)bL; saL += (double)xL; sbR += (double)bR; saR += (double)xR;
+    };
+    if (VEC) {
+        const long long n4 = n >> 2;
+        tile_f4<kCertV, kFilterNT>(reinterpret_cast<const float4*>(r), n4, false, quad, quad);
+        if (blockIdx.x == 0) {
+            const long long j = (n4 << 2) + tid;
+            if (tid < 4 && j < n) single(r[j]);
+        }
+    } else {
+        const long long stride = (long long)gridDim.x * kStreamThreads;
+        for (long long i = (long long)blockIdx.x * kStreamThreads + tid; i < n; i += stride) single(r[i]);
+    }
+    double d[4] = {sbL, saL, sbR, saR};
+    unsigned long long u[2] = {geL, geR};
+    uint32_t m0[1] = {0u};
+    block_reduce_multi<kStreamThreads>(d, u, m0, s_rd, s_ru, s_rm);
+    if (tid == 0) {
+        CertPart& cp = part[blockIdx.x];
+        cp.sb[0] = d[0]; cp.sa[0] = d[1]; cp.sb[1] = d[2]; cp.sa[1] = d[3];
+        cp.ge[0] = u[0]; cp.ge[1] = u[1];
+    }
+}
+
+// one workgroup: the pass's partials in a fixed order, G at both ends, the
+// verdict G(a_L) >= k > G(a_R) in place of the one from the filter's sums,
+// the gate for the kernels launched behind it, and the host summary
+__global__ __launch_bounds__(kCertFinalThreads) void k_cert_finalize(const CertPart* part, int nparts, Ctl* ctl,
+                                                                     HostSummary* hs, unsigned int seq, double k) {
+    constexpr int NT = kCertFinalThreads, NW = NT / 64;
+    __shared__ double s_rd[4 * NW];
+    __shared__ unsigned long long s_ru[2 * NW];
+    __shared__ uint32_t s_rm[NW];
+    constexpr int PP = kCertGrid / NT;
+    double d[4] = {0.0, 0.0, 0.0, 0.0};
+    unsigned long long u[2] = {0ull, 0ull};
+    CertPart cp[PP];
+#pragma unroll
+    for (int q = 0; q < PP; ++q) {
+        const int i = (int)threadIdx.x + q * NT;
+        if (i < nparts) cp[q] = part[i];
+    }
+#pragma unroll
+    for (int q = 0; q < PP; ++q) {
+        const int i = (int)threadIdx.x + q * NT;
+        if (i < nparts) {
+            d[0] += cp[q].sb[0]; d[1] += cp[q].sa[0]; d[2] += cp[q].sb[1]; d[3] += cp[q].sa[1];
+            u[0] += cp[q].ge[0]; u[1] += cp[q].ge[1];
+        }
+    }
+    uint32_t m0[1] = {0u};
+    block_reduce_multi<NT>(d, u, m0, s_rd, s_ru, s_rm);
+    if (threadIdx.x == 0) {
+        const double gL = (double)u[0] + 0.5 * d[0] - 0.5 * d[1];
+        const double gR = (double)u[1] + 0.5 * d[2] - 0.5 * d[3];
+        int flags = ctl->flags & ~kFlagCertified;
+        if (gL >= k && gR < k) flags |= kFlagCertified;
+        else flags &= ~kFlagHeavy;  // slots are laid out for a certified bracket only
+        ctl->flags = flags;
+        ctl->gate = (flags == kFlagCertified) ? 1 : 0;
+        if (hs) {
+            hs->c_L = ctl->c_L; hs->m = ctl->m; hs->c_R = ctl->c_R;
+            hs->S_L = ctl->S_L; hs->S_R = ctl->S_R; hs->B_L = ctl->B_L; hs->B_R = ctl->B_R;
+            hs->g_aL = ctl->gL_alg; hs->g_aR = ctl->gR_alg;
+            hs->g_aL_direct = gL; hs->g_aR_direct = gR;
+            hs->aL = ctl->aL; hs->aR = ctl->aR;
+            hs->flags = flags; hs->nb = ctl->nb; hs->max_bucket = ctl->max_bucket;
+            hs->heavy_total = ctl->heavy_total; hs->hchunks = ctl->hchunks;
+            __threadfence_system();
+            hs->seq = seq;
+            __threadfence_system();
+        }
+    }
+}
+
+void launch_cert(const float* r, long long n, double t, Ctl* ctl, double* part, HostSummary* hs_dev, unsigned int seq,
+                 double k, hipStream_t st) {
+    static_assert(sizeof(CertPart) * kCertGrid <= sizeof(double) * 2 * (size_t)kMaxStreamParts, "partials");
+    const float ls = (float)(1.4426950408889634 / t);
+    CertPart* cp = reinterpret_cast<CertPart*>(part);
+    const bool vec = (reinterpret_cast<uintptr_t>(r) & 15u) == 0u;
+    const int blocks = vec ? tiled_grid<kCertV>(n >> 2, kCertGrid) : std::min(stream_blocks(n), kCertGrid);
+    if (vec) hipLaunchKernelGGL(k_cert<true>, dim3(blocks), dim3(kStreamThreads), 0, st, r, n, ls, ctl, cp);
+    else hipLaunchKernelGGL(k_cert<false>, dim3(blocks), dim3(kStreamThreads), 0, st, r, n, ls, ctl, cp);
+    hipLaunchKernelGGL(k_cert_finalize, dim3(1), dim3(kCertFinalThreads), 0, st, cp, blocks, ctl, hs_dev, seq, k);
 }
 
 // ---------------------------------------------------------------------------
@@ -555,70 +693,166 @@ int launch_probs(const float* r, long long n, double t, float* p, Ctl* ctl, doub
 // ---------------------------------------------------------------------------
 // VJP
 // ---------------------------------------------------------------------------
-LS_DEV float lap_pdf_f(float x) { return 0.5f * __builtin_amdgcn_exp2f(-fabsf(x) * 1.4426950408889634f); }
+// The reduction's sums in a shifted frame.  With a_i = |r_i - b|/t, c needs
+// only the ratio of sum f g and sum f (f = e^{-a}/2), and both scale alike,
+// so each lane sums e^{m - a_i}/2 against a reference m of its own: the
+// smallest a its wave met in its first tile, lowered (and the sums rescaled
+// by e^{a_new - m}, a factor < 1) whenever a score comes more than
+// kVjpSlack below it.  Every term is then at most e^{kVjpSlack}/2, and the
+// score nearest b contributes a term of order 1 wherever it sits: in a fixed
+// frame (m = 0) the fp32 exponential flushes to 0 once every score is more
+// than ~87 t from b, and sum f = 0 would make c = 0/0.  Workgroups publish
+// their sums with their reference; k_vjp_c brings them to the smallest one.
+constexpr double kVjpSlack = 16.0;
 
-// Per workgroup: sum f g and sum f; with KT also sum f g d and sum f d
-// (d = r - b), which the budget and temperature gradients need.
-template <bool VEC, bool KT>
-__global__ __launch_bounds__(kStreamThreads) void k_vjp_reduce(const float* __restrict__ r, const float* __restrict__ g,
-                                                                long long n, const double* bptr, double inv_t,
-                                                                double* part) {
-    __shared__ double s_rd[4 * (kStreamThreads / 64)];
-    __shared__ unsigned long long s_ru[kStreamThreads / 64];
-    __shared__ uint32_t s_rm[kStreamThreads / 64];
-    const double b = *bptr;
-    const int tid = threadIdx.x;
+template <bool KT>
+struct VjpAcc {
+    double m = INFINITY;  // reference (a units); +inf until the lane's first score
     double sfg = 0.0, sf = 0.0, sfgd = 0.0, sfd = 0.0;
-    auto one = [&](float v, float gv) {
-        const double d = (double)v - b;
-        const float f = lap_pdf_f((float)(d * inv_t));
+    // new reference a_new < m - slack: every sum so far times e^{a_new - m},
+    // formed as 2^i * 2^f from y = (a_new - m) log2(e) = i + f (the fraction
+    // by the hardware exp2, the integer part exact)
+    LS_DEV void lower(double a_new) {
+        const double y = (a_new - m) * 1.4426950408889634;
+        double s = 0.0;  // while m = +inf (the sums are 0 then), or far below fp64
+        if (y > -1100.0) {
+            const double yi = floor(y);
+            s = ldexp((double)__builtin_amdgcn_exp2f((float)(y - yi)), (int)yi);
+        }
+        sfg *= s; sf *= s;
+        if (KT) { sfgd *= s; sfd *= s; }
+        m = a_new;
+    }
+    // one score: d = r - b; e^{m - |d|/t}/2 as exp2 of an fp32 exponent
+    // lowers m when a score of a tile (smallest distance dmin from b) comes
+    // more than kVjpSlack below it
+    LS_DEV void fit(double dmin, double inv_t) {
+        const double a = dmin * inv_t;
+        if (a < m - kVjpSlack) lower(a);
+    }
+    LS_DEV void one(double d, float gv, double inv_t) {
+        const double a = fabs(d) * inv_t;
+        if (a < m - kVjpSlack) lower(a);
+        const float f = __builtin_amdgcn_exp2f(fmaf((float)(m - a), 1.4426950408889634f, -1.0f));
         const float fg = f * gv;
         sfg += (double)fg;
         sf += (double)f;
         if (KT) { sfgd += (double)fg * d; sfd += (double)f * d; }
-    };
-    auto quad = [&](float4 q, float4 gg) {
+    }
+    // the scores of a quad whose smallest a the caller has already brought
+    // within kVjpSlack of m (fit)
+    LS_DEV void quad(float4 q, float4 gg, double b, double inv_t) {
+        const double d0 = (double)q.x - b, d1 = (double)q.y - b, d2 = (double)q.z - b, d3 = (double)q.w - b;
         if (KT) {
-            one(q.x, gg.x); one(q.y, gg.y); one(q.z, gg.z); one(q.w, gg.w);
-        } else {
-            const float f0 = lap_pdf_f((float)(((double)q.x - b) * inv_t));
-            const float f1 = lap_pdf_f((float)(((double)q.y - b) * inv_t));
-            const float f2 = lap_pdf_f((float)(((double)q.z - b) * inv_t));
-            const float f3 = lap_pdf_f((float)(((double)q.w - b) * inv_t));
-            sfg += (double)(f0 * gg.x + f1 * gg.y) + (double)(f2 * gg.z + f3 * gg.w);
-            sf += (double)((f0 + f1) + (f2 + f3));
+            one(d0, gg.x, inv_t); one(d1, gg.y, inv_t); one(d2, gg.z, inv_t); one(d3, gg.w, inv_t);
+            return;
         }
-    };
+        // m - |d|/t as one fma in fp64, then the exponent in fp32 (|.| <= 87
+        // for every term that does not flush)
+        const float f0 = __builtin_amdgcn_exp2f(fmaf((float)fma(-fabs(d0), inv_t, m), 1.4426950408889634f, -1.0f));
+        const float f1 = __builtin_amdgcn_exp2f(fmaf((float)fma(-fabs(d1), inv_t, m), 1.4426950408889634f, -1.0f));
+        const float f2 = __builtin_amdgcn_exp2f(fmaf((float)fma(-fabs(d2), inv_t, m), 1.4426950408889634f, -1.0f));
+        const float f3 = __builtin_amdgcn_exp2f(fmaf((float)fma(-fabs(d3), inv_t, m), 1.4426950408889634f, -1.0f));
+        sfg += (double)(f0 * gg.x + f1 * gg.y) + (double)(f2 * gg.z + f3 * gg.w);
+        sf += (double)((f0 + f1) + (f2 + f3));
+    }
+};
+
+// Per workgroup: sum f g and sum f relative to the workgroup's reference M
+// (f = e^{M - a}/2), then M; with KT also sum f g d and sum f d (d = r - b),
+// which the budget and temperature gradients need.  Partial layout per
+// workgroup: NP sums, then M.
+template <bool VEC, bool KT>
+__global__ __launch_bounds__(kStreamThreads) void k_vjp_reduce(const float* __restrict__ r, const float* __restrict__ g,
+                                                                long long n, const double* bptr, double inv_t,
+                                                                double* part) {
+    constexpr int NWV = kStreamThreads / 64;
+    __shared__ double s_rd[4 * NWV];
+    __shared__ unsigned long long s_ru[NWV];
+    __shared__ uint32_t s_rm[NWV];
+    __shared__ double s_mn[NWV];
+    const double b = *bptr;
+    const int tid = threadIdx.x;
+    VjpAcc<KT> acc;
     if (VEC) {
         const long long n4 = n >> 2;
-        auto body = [&](float4 q, float4 gg, long long) { quad(q, gg); };
-        tile_f4x2<kReduceV, kReduceNT>(reinterpret_cast<const float4*>(r), reinterpret_cast<const float4*>(g), n4,
-                                       false, body, body);
+        const float4* r4 = reinterpret_cast<const float4*>(r);
+        const float4* g4 = reinterpret_cast<const float4*>(g);
+        constexpr int V = kReduceV;
+        constexpr long long T = (long long)kStreamThreads * V;
+        const long long ntiles = stream_tiles<V>(n4);
+        bool primed = false;
+        for (long long j = blockIdx.x; j < ntiles; j += gridDim.x) {
+            const long long base = j * T + tid;
+            if ((j + 1) * T <= n4) {  // full tile: workgroup-uniform, every lane active
+                float4 x[V], y[V];
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    x[v] = ld4<kReduceNT>(r4 + base + v * kStreamThreads);
+                    y[v] = ld4<kReduceNT>(g4 + base + v * kStreamThreads);
+                }
+                // the tile's smallest distance from b: the wave's first tile
+                // sets the reference, later tiles only ever lower it
+                // (through an opaque copy of b, so that these differences are
+                // not kept live for the quads, which form their own)
+                double bo = b;
+                asm volatile("" : "+v"(bo));
+                double dm = INFINITY;
+#pragma unroll
+                for (int v = 0; v < V; ++v)
+                    dm = fmin(fmin(dm, fmin(fabs((double)x[v].x - bo), fabs((double)x[v].y - bo))),
+                              fmin(fabs((double)x[v].z - bo), fabs((double)x[v].w - bo)));
+                if (!primed) {
+                    acc.m = wave_min_nonneg_f64(dm) * inv_t;
+                    primed = true;
+                }
+                acc.fit(dm, inv_t);
+#pragma unroll
+                for (int v = 0; v < V; ++v) acc.quad(x[v], y[v], b, inv_t);
+            } else {
+                for (int v = 0; v < V; ++v) {
+                    const long long i = base + v * kStreamThreads;
+                    if (i < n4) {
+                        const float4 q = r4[i], gg = g4[i];
+                        acc.one((double)q.x - b, gg.x, inv_t); acc.one((double)q.y - b, gg.y, inv_t);
+                        acc.one((double)q.z - b, gg.z, inv_t); acc.one((double)q.w - b, gg.w, inv_t);
+                    }
+                }
+            }
+        }
         if (blockIdx.x == 0) {
-            const long long j = (n4 << 2) + tid;
-            if (tid < 4 && j < n) one(r[j], g[j]);
+            const long long jj = (n4 << 2) + tid;
+            if (tid < 4 && jj < n) acc.one((double)r[jj] - b, g[jj], inv_t);
         }
     } else {
         const long long stride = (long long)gridDim.x * kStreamThreads;
-        for (long long i = (long long)blockIdx.x * kStreamThreads + tid; i < n; i += stride) one(r[i], g[i]);
+        for (long long i = (long long)blockIdx.x * kStreamThreads + tid; i < n; i += stride)
+            acc.one((double)r[i] - b, g[i], inv_t);
     }
+    // the workgroup's reference M, then every lane's sums brought to it
+    const double M = block_min_nonneg_f64<kStreamThreads>(acc.m, s_mn);
+    const double sc = acc.m == M ? 1.0 : exp(M - acc.m);  // M <= m; 0 for a lane that met no score
     constexpr int NP = KT ? 4 : 2;
     double d[NP];
-    d[0] = sfg;
-    d[1] = sf;
-    if constexpr (KT) { d[2] = sfgd; d[3] = sfd; }
+    d[0] = acc.sfg * sc;
+    d[1] = acc.sf * sc;
+    if constexpr (KT) { d[2] = acc.sfgd * sc; d[3] = acc.sfd * sc; }
     unsigned long long u0[1] = {0ull};
     uint32_t m0[1] = {0u};
     block_reduce_multi<kStreamThreads>(d, u0, m0, s_rd, s_ru, s_rm);
     if (tid == 0) {
 #pragma unroll
-        for (int q = 0; q < NP; ++q) part[NP * blockIdx.x + q] = d[q];
+        for (int q = 0; q < NP; ++q) part[(NP + 1) * blockIdx.x + q] = d[q];
+        part[(NP + 1) * blockIdx.x + NP] = M;
     }
 }
 
-// c = sum f g / sum f from the reduce pass's partials, in a fixed order; with
-// KT also dL/dk = c and dL/dt = -(sum f g d - mu sum f g)/t^2,
-// mu = sum f d / sum f, written to dk_out / dt_out when they are not null
+// c = sum f g / sum f from the reduce pass's partials, each first brought to
+// the smallest reference M (a factor e^{M - M_wg} <= 1), summed in a fixed
+// order.  The absolute sums carry a factor e^{-M}: sum f and sum f g in the
+// control block, and dL/dt, are formed with it.  With KT also dL/dk = c and
+// dL/dt = -(sum f g d - mu sum f g)/t^2, mu = sum f d / sum f, written to
+// dk_out / dt_out when they are not null.
 template <bool KT>
 __global__ __launch_bounds__(1024) void k_vjp_c(const double* part, int nparts, Ctl* ctl, double t, double* dk_out,
                                                 double* dt_out) {
@@ -626,24 +860,31 @@ __global__ __launch_bounds__(1024) void k_vjp_c(const double* part, int nparts, 
     __shared__ double s_rd[4 * NW];
     __shared__ unsigned long long s_ru[NW];
     __shared__ uint32_t s_rm[NW];
+    __shared__ double s_mn[NW];
     constexpr int NP = KT ? 4 : 2;
     // every partial of a thread loaded in one batch (nparts <= 8 NT), then
     // summed in a fixed order
     constexpr int B = kReduceGrid / NT;
     static_assert(B * NT == kReduceGrid, "");
-    double v[B][NP];
+    double v[B][NP + 1];
 #pragma unroll
     for (int q = 0; q < B; ++q) {
         const int i = (int)threadIdx.x + q * NT;
 #pragma unroll
-        for (int x = 0; x < NP; ++x) v[q][x] = i < nparts ? part[(size_t)i * NP + x] : 0.0;
+        for (int x = 0; x <= NP; ++x) v[q][x] = i < nparts ? part[(size_t)i * (NP + 1) + x] : (x == NP ? INFINITY : 0.0);
     }
+    double mt = INFINITY;
+#pragma unroll
+    for (int q = 0; q < B; ++q) mt = fmin(mt, v[q][NP]);
+    const double M = block_min_nonneg_f64<NT>(mt, s_mn);
     double d[NP];
 #pragma unroll
-    for (int x = 0; x < NP; ++x) {
-        d[x] = 0.0;
+    for (int x = 0; x < NP; ++x) d[x] = 0.0;
 #pragma unroll
-        for (int q = 0; q < B; ++q) d[x] += v[q][x];
+    for (int q = 0; q < B; ++q) {
+        const double sc = v[q][NP] == M ? 1.0 : exp(M - v[q][NP]);
+#pragma unroll
+        for (int x = 0; x < NP; ++x) d[x] += v[q][x] * sc;
     }
     unsigned long long u0[1] = {0ull};
     uint32_t m0[1] = {0u};
@@ -651,11 +892,12 @@ __global__ __launch_bounds__(1024) void k_vjp_c(const double* part, int nparts, 
     const double T0 = d[0], T1 = d[1];
     const double T2 = KT ? d[NP > 2 ? 2 : 0] : 0.0, T3 = KT ? d[NP > 3 ? 3 : 0] : 0.0;
     if (threadIdx.x == 0) {
-        ctl->sumfg = T0; ctl->sumf = T1; ctl->c = T0 / T1;
+        const double scale = exp(-M);  // e^{-M}: the frame back to f = e^{-a}/2 (may underflow to 0)
+        ctl->sumfg = T0 * scale; ctl->sumf = T1 * scale; ctl->c = T0 / T1;
         if (KT) {
             const double mu = T3 / T1;
             if (dk_out) *dk_out = T0 / T1;
-            if (dt_out) *dt_out = -(T2 - mu * T0) / (t * t);
+            if (dt_out) *dt_out = -(T2 - mu * T0) * scale / (t * t);
         }
     }
 }
@@ -736,6 +978,11 @@ __global__ void k_set_nan_b(Ctl* ctl, double* b_out) {
     const double nanv = __longlong_as_double(0x7ff8000000000000ll);
     ctl->b = nanv;
     if (b_out) *b_out = nanv;
+}
+
+__global__ void k_or_flags(Ctl* ctl, int flags) { atomicOr(&ctl->flags, flags); }
+void launch_or_flags(Ctl* ctl, int flags, hipStream_t st) {
+    hipLaunchKernelGGL(k_or_flags, dim3(1), dim3(1), 0, st, ctl, flags);
 }
 
 void launch_fill(float* p, long long n, float v, hipStream_t st) {

@@ -31,12 +31,22 @@
  *    stream).  Scratch memory is a per-(device, stream) workspace that the
  *    library allocates on first use and keeps until lapsum_release_workspaces.
  *  - Argument errors are returned before anything is launched and nothing is
- *    written.  Errors found on the device (non-finite scores) are returned
- *    by the bracketing path, which waits for its certification verdict; the
- *    full-sort path never blocks the host and reports them through
- *    lapsum_stats_t (b and p are then NaN).
+ *    written.
+ *  - Errors found on the device: non-finite scores (b and p are then NaN) and
+ *    failed consistency checks (LAPSUM_ERR_INTERNAL).  A call given a
+ *    lapsum_stats_t waits for the device and returns what it found (also in
+ *    stats->status).  Without stats, only what the device reported before the
+ *    host's last wait is returned: the bracketing path waits for its
+ *    certification verdict and returns non-finite scores found by then; the
+ *    full-sort path and the VJP never block the host, and a check that fails
+ *    after the last wait is visible only through stats.
  *  - n is limited to [1, 2^32 - 1].
- *  - No exception crosses this ABI; every call is thread-safe.
+ *  - No exception crosses this ABI.  Calls may come from several host
+ *    threads: a call holds its (device, stream) workspace from its start to
+ *    its return, so calls on one stream take turns (their device work is
+ *    ordered on the stream in the order they took it), calls on different
+ *    streams run side by side, and lapsum_release_workspaces waits for the
+ *    calls in flight.
  */
 #ifndef LAPSUM_H_
 #define LAPSUM_H_
@@ -80,6 +90,9 @@ typedef struct {
     int32_t bucket_capacity;/* band scores per bucket, <= 16384 (default 16384; small values force
                                the overflow fallback in tests) */
     int32_t profile;        /* 1: time every kernel with HIP events (reported in stats) */
+    int32_t cert_mode;      /* certification of the bracket: 0 (default) from the streaming pass's own
+                               sums at no extra read; 1 one more linear pass over the scores that sums
+                               G(a_L) and G(a_R) directly, whose verdict decides (the pages' form) */
 } lapsum_options_t;
 
 #define LAPSUM_MAX_TIMED_KERNELS 24
@@ -100,6 +113,8 @@ typedef struct {
     int32_t n_timed;         /* entries in kernel_ms / kernel_name */
     float a_L, a_R;          /* final bracket */
     double g_aL, g_aR;       /* G at the bracket ends, rebuilt from the streaming pass's tail sums */
+    double g_aL_direct, g_aR_direct; /* cert_mode 1: G at the bracket ends summed by the certification
+                                        pass (0 otherwise) */
     double sum_p;            /* sum of the written p, accumulated in fp64 on the device */
     double b;                /* threshold */
     double tail_S_L, tail_S_R, band_B_L, band_B_R; /* the streaming pass's fp64 sums */
@@ -229,8 +244,12 @@ lapsum_status_t lapsum_vjp_batched(const float* scores, const float* g, int64_t 
 /* Free every cached workspace (waits for their streams). */
 void lapsum_release_workspaces(void);
 
-/* Bytes of workspace a forward of size n needs (informational). */
-size_t lapsum_workspace_bytes(int64_t n);
+/* Bytes of device workspace a forward of n scores with options `opt` (NULL =
+ * defaults) holds on its stream: the library allocates it on the first call
+ * on a stream that needs that much and keeps it until
+ * lapsum_release_workspaces.  It includes the full-sort fallback's buffers,
+ * which any forward may need.  0 for n outside [1, 2^32) or bad options. */
+size_t lapsum_workspace_bytes(int64_t n, const lapsum_options_t* opt);
 
 #ifdef __cplusplus
 }

@@ -87,6 +87,15 @@ lapsum_status_t lapsum_test_binomial_ranks(int64_t s, double q, double delta, in
 lapsum_status_t lapsum_test_copy(const float* src, float* dst, int64_t n, lapsum_stream_t stream);
 lapsum_status_t lapsum_test_read(const float* src, int64_t n, float* sink, lapsum_stream_t stream);
 
+/*
+ * Error-path check: the next forward solve on `stream` (on the current
+ * device) ends with a kernel that sets the consistency-failure flag in its
+ * control block, exactly as a failed device-side check does, so that the
+ * call reports LAPSUM_ERR_INTERNAL when it is given stats.  The solve itself
+ * runs as usual.  Returns an allocation or HIP error, else LAPSUM_OK.
+ */
+lapsum_status_t lapsum_test_inject_internal(lapsum_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

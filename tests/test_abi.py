@@ -78,6 +78,7 @@ def test_default_options_and_status_strings():
     assert o.path == 0 and o.max_widen == 2
     assert o.sample_factor == 4.0 and o.delta == 1e-5
     assert o.margin_scale == 1.0 and o.auto_threshold == 1_000_000
+    assert o.cert_mode == 0
     assert 1 <= o.bucket_capacity <= 16384
     lib = L.lib()
     seen = set()
@@ -90,9 +91,14 @@ def test_default_options_and_status_strings():
 
 def test_workspace_bytes_grows_with_n():
     lib = L.lib()
-    a, b, c = (lib.lapsum_workspace_bytes(n) for n in (1, 10**6, 10**8))
+    a, b, c = (lib.lapsum_workspace_bytes(n, None) for n in (1, 10**6, 10**8))
     assert 0 < a <= b < c
     assert c >= 4 * 10**8  # at least one fp32 array of n for the full-sort fallback
+    o = L.default_options(cert_mode=1)
+    assert lib.lapsum_workspace_bytes(10**8, ctypes.byref(o)) == c
+    assert lib.lapsum_workspace_bytes(0, None) == 0 and lib.lapsum_workspace_bytes(2**32, None) == 0
+    bad = L.default_options(cert_mode=2)
+    assert lib.lapsum_workspace_bytes(10**6, ctypes.byref(bad)) == 0
 
 
 @pytest.mark.parametrize("n,k,t", [
@@ -114,7 +120,7 @@ def test_forward_rejects_null_pointers_and_bad_options():
     assert lib.lapsum_forward(FAKE, 100, 5.0, 0.1, FAKE, None, None) == INVALID
     for field, value in (("path", 4), ("path", -1), ("bucket_capacity", 0), ("bucket_capacity", 1 << 20),
                          ("sample_factor", 0.0), ("delta", 0.0), ("delta", 0.5), ("margin_scale", -1.0),
-                         ("max_widen", -1)):
+                         ("max_widen", -1), ("cert_mode", -1), ("cert_mode", 2)):
         o = L.default_options(**{field: value})
         rc = lib.lapsum_forward_ex(FAKE, 100, 5.0, 0.1, FAKE, FAKE, ctypes.byref(o), None, None)
         assert rc == INVALID, (field, value)

@@ -1,0 +1,314 @@
+"""GPU parity on the property sweep: the corners of the operator's domain on
+both forward paths, against the CPU fp64 oracle.
+
+  - temperatures from 1e-4 to 10;
+  - the bracketing path at tiny and odd sizes (n = 1 ... 65537), forced;
+  - all-equal scores, and large-magnitude scores whose fp32 spacing is far
+    wider than t (10^4 + N(0,1) at t = 1e-4);
+  - budgets near 0 and near n on the bracketing path;
+  - a bracket that misses until the widenings run out, so the host falls back
+    to the full sort by itself (no forcing option);
+  - the plain lapsum_forward / lapsum_vjp entry points;
+  - the VJP when every score lies far from b in units of t (the Laplace
+    density underflows fp32 there);
+  - the certification pass as its own linear pass (cert_mode 1);
+  - a device-side failure reported through the return code;
+  - two host threads on one stream.
+
+The operator and its gradient are fixed by the budget equation
+sum_i F((r_i - b)/t) = k (gist.science summary section 2.1); the oracle is
+that definition solved by bisection in fp64.
+"""
+import ctypes
+import threading
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_helpers import check_forward, check_vjp, t32, to_dev
+
+pytestmark = pytest.mark.gpu
+
+L = pytest.importorskip("differentiable_exact_budget_amd")
+
+
+def run(r, k, t, g=None, **opts):
+    rd = to_dev(r)
+    o = L.default_options(**opts) if opts else None
+    p, b, st = L.forward(rd, k, t, options=o, stats=True)
+    grad = None
+    if g is not None:
+        grad = L.vjp(rd, to_dev(g), t, b).cpu().numpy()
+    torch.cuda.synchronize()
+    return p.cpu().numpy(), float(b.cpu().item()), st, grad
+
+
+def parity(oracle_mod, r, k, t, g=None, label="", **opts):
+    print(f"\n  case {label}: n={r.size} k={k} t={t} {opts}", flush=True)
+    p, b, st, grad = run(r, k, t, g, **opts)
+    assert st["status"] == 0, st
+    b_ref = check_forward(oracle_mod, r, k, t, p, b, label=label)
+    if g is not None:
+        check_vjp(oracle_mod, r, g, t, b_ref, grad, label=label)
+    return st, b_ref
+
+
+# ---------------------------------------------------------------------------
+# temperatures
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("t", [1e-4, 1e-3, 3.0, 10.0])
+@pytest.mark.parametrize("path,n", [(1, 5000), (1, 300_001), (2, 2_000_000)])
+def test_temperature_range(oracle_mod, t, path, n):
+    r = workloads.scores("normal", n, 11 + n)
+    g = workloads.upstream(n, 12 + n)
+    k = max(1.0, n / 200.0)
+    st, _ = parity(oracle_mod, r, k, t, g, label=f"t={t} path={path}", path=path)
+    assert st["path_taken"] in ((1,) if path == 1 else (2, 3))
+
+
+# ---------------------------------------------------------------------------
+# the bracketing path at small and odd sizes
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("n", [1, 2, 3, 17, 1023, 4096, 65537])
+@pytest.mark.parametrize("frac", [0.3, 0.9])
+def test_bracket_small_n(oracle_mod, n, frac):
+    r = workloads.scores("student_t3", n, 21 + n)
+    g = workloads.upstream(n, 22 + n)
+    k = frac * n if n > 1 else frac
+    st, _ = parity(oracle_mod, r, k, 0.05, g, label=f"bracket n={n}", path=L.PATH_BRACKET)
+    assert st["path_taken"] in (2, 3)
+    assert st["sample_size"] == int(np.ceil(4.0 * np.sqrt(n)))
+
+
+# ---------------------------------------------------------------------------
+# all-equal and large-magnitude scores, on both paths
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("path,n", [(1, 1000), (1, 200_000), (2, 2_000_000)])
+@pytest.mark.parametrize("value", [0.0, -3.25, 7.5e3])
+def test_all_equal_scores(oracle_mod, path, n, value):
+    r = np.full(n, value, dtype=np.float32)
+    g = workloads.upstream(n, 31 + n)
+    k, t = 0.37 * n, 0.02
+    st, b_ref = parity(oracle_mod, r, k, t, g, label=f"equal {value}", path=path)
+    # the closed form: every p equals k/n, so b = value - t F^-1(k/n)
+    y = k / n
+    finv = np.log(2 * y) if y < 0.5 else -np.log(2 * (1 - y))
+    assert abs(b_ref - (float(value) - t32(t) * finv)) <= 1e-9 * max(1.0, abs(value))
+
+
+@pytest.mark.parametrize("path,n", [(1, 50_000), (1, 1_000_000), (2, 2_000_000)])
+def test_large_magnitude_scores(oracle_mod, path, n):
+    """10^4 + N(0,1): fp32 scores sit on a grid about 1e-3 apart, ten times t,
+    so most scores share their value with many others and b falls in a gap
+    wider than 9 t."""
+    rng = np.random.default_rng(41 + n)
+    r = (1e4 + rng.standard_normal(n)).astype(np.float32)
+    g = workloads.upstream(n, 42 + n)
+    k = n / 100.0
+    st, _ = parity(oracle_mod, r, k, 1e-4, g, label="1e4 + N(0,1)", path=path)
+
+
+# ---------------------------------------------------------------------------
+# budgets near 0 and near n on the bracketing path
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("k", [1e-3, 0.5, 3.0, 1_999_990.0, 1_999_999.5])
+def test_bracket_budget_extremes(oracle_mod, k):
+    n = 2_000_000
+    r = workloads.scores("normal", n, 51)
+    g = workloads.upstream(n, 52)
+    st, _ = parity(oracle_mod, r, k, 0.01, g, label=f"k={k}", path=L.PATH_BRACKET)
+    assert st["path_taken"] in (2, 3)
+
+
+# ---------------------------------------------------------------------------
+# a bracket that misses until the widenings run out
+# ---------------------------------------------------------------------------
+def test_widening_exhausted_falls_back(oracle_mod):
+    """With zero order-statistic margins the first bracket has zero width
+    and cannot hold b; each widening doubles the failing side's distance
+    from s q.  A seed is chosen (on the host, from the oracle's copy of the
+    sample) for which b lies at least four sample ranks away from s q, so one
+    widening cannot reach it either: the host then falls back to the full
+    sort by itself, with no forcing option."""
+    n, k, t = 2_000_000, 20_000.0, 0.01
+    r = workloads.scores("normal", n, 61)
+    g = workloads.upstream(n, 62)
+    b_ref, _ = oracle_mod.solve(r.astype(np.float64), k, t32(t))
+    s = int(np.ceil(4.0 * np.sqrt(n)))
+    c0 = s * (1.0 - k / n)
+    seed = None
+    for cand in range(1, 200):
+        _, x = oracle_mod.sample(r, t32(t), cand, s)
+        if abs(int(np.count_nonzero(x.astype(np.float64) < b_ref)) - c0) >= 4.0:
+            seed = cand
+            break
+    assert seed is not None
+    for widen in (0, 1):
+        st, _ = parity(oracle_mod, r, k, t, g, label=f"max_widen={widen}", path=L.PATH_AUTO, margin_scale=0.0,
+                       max_widen=widen, seed=seed)
+        assert st["path_taken"] == 3 and st["widenings"] == widen and st["certified"] == 0, st
+
+
+# ---------------------------------------------------------------------------
+# plain entry points
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name,n", [("C1", None), ("C2", None), ("C3", 2_000_000)])
+def test_plain_forward_and_vjp(oracle_mod, name, n):
+    r, g, cfg = workloads.config_inputs(name, n)
+    k = cfg.k * r.size / cfg.n
+    rd, gd = to_dev(r), to_dev(g)
+    p = torch.empty_like(rd)
+    b = torch.empty(1, dtype=torch.float64, device=rd.device)
+    grad = torch.empty_like(rd)
+    stream = torch.cuda.current_stream().cuda_stream
+    lib = L.lib()
+    assert lib.lapsum_forward(rd.data_ptr(), r.size, k, cfg.t, p.data_ptr(), b.data_ptr(), stream) == 0
+    assert lib.lapsum_vjp(rd.data_ptr(), p.data_ptr(), gd.data_ptr(), r.size, cfg.t, b.data_ptr(), grad.data_ptr(),
+                          stream) == 0
+    torch.cuda.synchronize()
+    b_ref = check_forward(oracle_mod, r, k, cfg.t, p.cpu().numpy(), float(b.item()), label=name)
+    check_vjp(oracle_mod, r, g, cfg.t, b_ref, grad.cpu().numpy(), label=name)
+
+
+# ---------------------------------------------------------------------------
+# the VJP far from every score
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("t", [0.005, 0.001])
+def test_vjp_every_score_far_from_b(oracle_mod, t):
+    """Scores 0..19, k = 5: b = 14.5 and every score lies at least 0.5/t from
+    it (100 t and 500 t), where the density underflows fp32.  The VJP and
+    the budget/temperature gradients still match the fp64 oracle."""
+    r = np.random.default_rng(3).permutation(np.arange(20, dtype=np.float32))
+    g = np.random.default_rng(4).standard_normal(20).astype(np.float32)
+    for path in (L.PATH_FULL, L.PATH_BRACKET):
+        st, b_ref = parity(oracle_mod, r, 5.0, t, g, label=f"far t={t}", path=path)
+        rd, gd = to_dev(r), to_dev(g)
+        _, b = L.forward(rd, 5.0, t, options=L.default_options(path=path))
+        grad, dk, dt = L.vjp_kt(rd, gd, t, b)
+        dk_ref, dt_ref = oracle_mod.vjp_kt(r.astype(np.float64), g.astype(np.float64), t32(t), b_ref)
+        assert np.isfinite(dk.item()) and abs(dk.item() - dk_ref) <= 1e-6 * max(1.0, abs(dk_ref))
+        assert abs(dt.item() - dt_ref) <= 1e-4 * abs(dt_ref) + 1e-300
+        check_vjp(oracle_mod, r, g, t, b_ref, grad.cpu().numpy(), label="vjp_kt far")
+
+
+def test_vjp_beyond_fp64_density_range():
+    """t = 1e-4 puts every score at least 5000 t from b = 14.5: e^{-5000}
+    underflows even fp64, and the plain definition of c = sum g f / sum f is
+    0/0.  Its limit is the mean of g over the two nearest scores (14 and 15,
+    equally far from b), which the shifted-frame sums reach."""
+    r = np.random.default_rng(3).permutation(np.arange(20, dtype=np.float32))
+    g = np.random.default_rng(4).standard_normal(20).astype(np.float32)
+    rd, gd = to_dev(r), to_dev(g)
+    _, b = L.forward(rd, 5.0, 1e-4)
+    assert abs(b.item() - 14.5) <= 1e-9
+    grad, dk, _ = L.vjp_kt(rd, gd, 1e-4, b)
+    c_lim = 0.5 * (float(g[r == 14][0]) + float(g[r == 15][0]))
+    assert abs(dk.item() - c_lim) <= 1e-6 * max(1.0, abs(c_lim)), (dk.item(), c_lim)
+    gr = L.vjp(rd, gd, 1e-4, b).cpu().numpy()
+    assert np.all(np.isfinite(gr)) and np.all(gr == 0.0)  # (f/t)(g - c) is below fp32's range
+
+
+@pytest.mark.parametrize("t", [0.005, 0.001])
+def test_rows_vjp_every_score_far_from_b(oracle_mod, t):
+    rows, n = 64, 20
+    rng = np.random.default_rng(5)
+    r = np.stack([rng.permutation(np.arange(n, dtype=np.float32)) for _ in range(rows)])
+    g = rng.standard_normal((rows, n)).astype(np.float32)
+    rd, gd = to_dev(r), to_dev(g)
+    p, b = L.forward_rows(rd, 5.0, t)
+    grad = L.vjp_rows(rd, gd, t, b).cpu().numpy()
+    bh = b.cpu().numpy()
+    for i in range(rows):
+        b_ref = check_forward(oracle_mod, r[i], 5.0, t, p[i].cpu().numpy(), float(bh[i]), label=f"row {i}")
+        check_vjp(oracle_mod, r[i], g[i], t, b_ref, grad[i], label=f"row {i}")
+
+
+# ---------------------------------------------------------------------------
+# certification as its own linear pass
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name,n", [("C3", 2_000_000), ("C4", 3_000_000), ("C5", 2_000_000)])
+def test_certification_pass(oracle_mod, name, n):
+    """cert_mode 1 sums G(a_L) and G(a_R) directly over every score (the
+    pages' extra linear pass) and its verdict decides.  The direct sums match
+    the oracle's, agree with the ones rebuilt from the streaming pass's tail
+    sums, and b and p are bit for bit those of the default mode."""
+    cfg = workloads.CONFIGS[name]
+    k = cfg.k * n / cfg.n
+    r = workloads.scores(cfg.dist, n, 1000 + cfg.number, k=k)
+    g = workloads.upstream(n, 2000 + cfg.number)
+    p1, b1, st1, grad1 = run(r, k, cfg.t, g, cert_mode=1, profile=1)
+    p0, b0, st0, grad0 = run(r, k, cfg.t, g)
+    assert st1["status"] == 0 and st1["path_taken"] == st0["path_taken"], (st0, st1)
+    assert st1["path_taken"] in (2, 3) and (name != "C4" or st1["path_taken"] == 2)
+    assert "cert" in [nm for nm, _ in st1["kernels"]]
+    assert b1 == b0 and np.array_equal(p1.view(np.uint32), p0.view(np.uint32))
+    ref = oracle_mod.bracket(r, t32(cfg.t), st1["a_L"], st1["a_R"], want_band=False)
+    if np.isfinite(st1["a_L"]):
+        assert abs(st1["g_aL_direct"] - ref["G_aL"]) <= 1e-6 * ref["G_aL"]
+        assert abs(st1["g_aL_direct"] - st1["g_aL"]) <= 1e-6 * ref["G_aL"]
+    else:
+        assert st1["g_aL_direct"] == n
+    if np.isfinite(st1["a_R"]):
+        assert abs(st1["g_aR_direct"] - ref["G_aR"]) <= 1e-6 * max(ref["G_aR"], 1.0)
+    else:
+        assert st1["g_aR_direct"] == 0.0
+    assert st1["g_aL_direct"] >= k > st1["g_aR_direct"]
+    b_ref = check_forward(oracle_mod, r, k, cfg.t, p1, b1, label=f"{name} cert pass")
+    check_vjp(oracle_mod, r, g, cfg.t, b_ref, grad1, label=f"{name} cert pass")
+
+
+# ---------------------------------------------------------------------------
+# a device-side failure reaches the caller
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("path,n", [(1, 4096), (1, 300_000), (2, 2_000_000)])
+def test_device_failure_is_reported(path, n):
+    r = workloads.scores("normal", n, 71)
+    rd = to_dev(r)
+    opt = L.default_options(path=path)
+    stream = torch.cuda.current_stream().cuda_stream
+    assert L.lib().lapsum_test_inject_internal(stream) == 0
+    with pytest.raises(L.LapsumError) as e:
+        L.forward(rd, n / 10.0, 0.1, options=opt, stats=True)
+    assert e.value.code == 5
+    # the flag belongs to that solve only
+    _, _, st = L.forward(rd, n / 10.0, 0.1, options=opt, stats=True)
+    assert st["status"] == 0
+
+
+# ---------------------------------------------------------------------------
+# two host threads on one stream
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name,n", [("C2", None), ("C3", 2_000_000)])
+def test_two_host_threads_one_stream(name, n):
+    """Calls from two host threads on the same stream take turns on its
+    workspace: every result equals the single-thread one bit for bit."""
+    r, g, cfg = workloads.config_inputs(name, n)
+    k = cfg.k * r.size / cfg.n
+    rd, gd = to_dev(r), to_dev(g)
+    p_ref, b_ref = L.forward(rd, k, cfg.t)
+    gr_ref = L.vjp(rd, gd, cfg.t, b_ref)
+    torch.cuda.synchronize()
+    p_ref, b_ref, gr_ref = p_ref.cpu().numpy(), b_ref.cpu().numpy(), gr_ref.cpu().numpy()
+    stream = torch.cuda.current_stream()
+    bad = []
+
+    def worker(reps):
+        with torch.cuda.stream(stream):
+            for _ in range(reps):
+                p, b = L.forward(rd, k, cfg.t)
+                gr = L.vjp(rd, gd, cfg.t, b)
+                stream.synchronize()
+                if not (np.array_equal(b.cpu().numpy().view(np.uint64), b_ref.view(np.uint64))
+                        and np.array_equal(p.cpu().numpy().view(np.uint32), p_ref.view(np.uint32))
+                        and np.array_equal(gr.cpu().numpy().view(np.uint32), gr_ref.view(np.uint32))):
+                    bad.append(1)
+
+    th = [threading.Thread(target=worker, args=(8,)) for _ in range(2)]
+    for x in th:
+        x.start()
+    for x in th:
+        x.join(timeout=120)
+    assert not any(x.is_alive() for x in th)
+    assert not bad
