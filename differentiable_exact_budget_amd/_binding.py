@@ -90,7 +90,7 @@ _lib = None
 EXPORTED = [
     "lapsum_default_options", "lapsum_status_string", "lapsum_forward", "lapsum_forward_ex", "lapsum_vjp",
     "lapsum_vjp_ex", "lapsum_vjp_kt", "lapsum_topk_threshold", "lapsum_hard_topk", "lapsum_dftopk",
-    "lapsum_forward_batched", "lapsum_vjp_batched",
+    "lapsum_forward_batched", "lapsum_vjp_batched", "lapsum_forward_noalloc",
     "lapsum_release_workspaces", "lapsum_workspace_bytes",
     "lapsum_test_sort", "lapsum_test_sort_form", "lapsum_test_sample", "lapsum_test_select", "lapsum_test_filter",
     "lapsum_test_copy", "lapsum_test_read", "lapsum_test_binomial_ranks", "lapsum_test_inject_internal",
@@ -131,6 +131,8 @@ def lib():
     L.lapsum_forward_batched.restype = ctypes.c_int
     L.lapsum_vjp_batched.argtypes = [vp, vp, i64, i64, f32, vp, vp, vp]
     L.lapsum_vjp_batched.restype = ctypes.c_int
+    L.lapsum_forward_noalloc.argtypes = [vp, i64, f64, f32, vp, vp, vp]
+    L.lapsum_forward_noalloc.restype = ctypes.c_int
     L.lapsum_release_workspaces.argtypes = []
     L.lapsum_release_workspaces.restype = None
     L.lapsum_workspace_bytes.argtypes = [i64, ctypes.POINTER(Options)]

@@ -241,6 +241,22 @@ lapsum_status_t lapsum_forward_batched(const float* scores, int64_t rows, int64_
 lapsum_status_t lapsum_vjp_batched(const float* scores, const float* g, int64_t rows, int64_t n, float t,
                                    const double* b, float* grad_out, lapsum_stream_t stream);
 
+/*
+ * lapsum_forward without any device allocation, for callers that cannot
+ * allocate (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, results and conventions as
+ * lapsum_forward on its full-sort path, for 1 <= n <= 2^20 scores; a larger n
+ * is LAPSUM_ERR_INVALID_ARGUMENT before anything is launched.  Scratch memory
+ * is one fixed device array of about 9 MB per GPU, inside the library's code
+ * object, held until the process ends; the call allocates nothing and frees
+ * nothing (its first call on a device only looks up that array's address).
+ * Every call on a GPU uses the same array: calls that overlap on one GPU
+ * (two streams, two host threads) race and must be serialised by the caller.
+ * Never blocks the host; non-finite scores give b = NaN and p = NaN.
+ */
+lapsum_status_t lapsum_forward_noalloc(const float* scores, int64_t n, double k, float t, float* p_out,
+                                       double* b_out, lapsum_stream_t stream);
+
 /* Free every cached workspace (waits for their streams). */
 void lapsum_release_workspaces(void);
 

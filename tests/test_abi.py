@@ -172,6 +172,16 @@ def test_order_statistic_entry_points_reject_bad_arguments():
     assert lib.lapsum_vjp_kt(FAKE, FAKE, 100, 0.1, FAKE, None, None, None, None, None, None) == INVALID
 
 
+def test_noalloc_entry_point_rejects_bad_arguments_before_any_launch():
+    lib = L.lib()
+    assert lib.lapsum_forward_noalloc(FAKE, (1 << 20) + 1, 5.0, 0.1, FAKE, FAKE, None) == INVALID
+    assert lib.lapsum_forward_noalloc(FAKE, 0, 5.0, 0.1, FAKE, FAKE, None) == INVALID
+    assert lib.lapsum_forward_noalloc(None, 100, 5.0, 0.1, FAKE, FAKE, None) == INVALID
+    assert lib.lapsum_forward_noalloc(FAKE, 100, 100.0, 0.1, FAKE, FAKE, None) == INVALID
+    assert lib.lapsum_forward_noalloc(FAKE, 100, 5.0, 0.0, FAKE, FAKE, None) == INVALID
+    assert lib.lapsum_forward_noalloc(FAKE, 100, 5.0, 0.1, FAKE, None, None) == INVALID
+
+
 def test_batched_entry_points_reject_bad_arguments():
     lib = L.lib()
     assert lib.lapsum_forward_batched(None, 4, 10, 2.0, None, 0.1, FAKE, FAKE, None) == INVALID
