@@ -75,10 +75,12 @@ __global__ __launch_bounds__(NT) void k_rows_forward(const float* __restrict__ r
 
 // per row: c = sum g f / sum f, grad = (f/t)(g - c), with f/t carried at
 // 2^32 times its value (one exp2 with log2(1/(2t)) + 32 folded in) so that
-// it does not flush where f itself would.  The two sums are taken relative
-// to the row's smallest a = |r - b|/t (a first pass over the row finds it):
-// terms e^{a_min - a}/2, so the score nearest b contributes 1/2 and sum f
-// cannot flush to 0 however far b lies from every score in units of t.
+// it does not flush where f itself would.  The two sums are taken with
+// f = e^{-a}/2 (a = |r - b|/t) while the row's smallest a is tracked; when
+// that is above 60 (every term of the row below e^{-60}, where fp32 flushes
+// the far ones and, past ~87, all of them) the row is summed again relative
+// to it, terms e^{a_min - a}/2, so sum f cannot vanish however far b lies
+// from every score in units of t.
 template <int NT>
 __global__ __launch_bounds__(NT) void k_rows_vjp(const float* __restrict__ r, const float* __restrict__ g, int n,
                                                   double inv_t, float log2_inv_2t, const double* __restrict__ b,
@@ -90,15 +92,25 @@ __global__ __launch_bounds__(NT) void k_rows_vjp(const float* __restrict__ r, co
     const float* rr = r + row * (long long)n;
     const float* gg = g + row * (long long)n;
     const double bb = b[row];
-    double dmin = INFINITY;
-    for (int i = tid; i < n; i += NT) dmin = fmin(dmin, fabs((double)rr[i] - bb));
-    const double M = block_min_nonneg_f64<NT>(dmin, s_mn) * inv_t;
-    double sfg = 0.0, sf = 0.0;
+    double sfg = 0.0, sf = 0.0, dmin = INFINITY;
     for (int i = tid; i < n; i += NT) {
-        const float y = (float)fma(-fabs((double)rr[i] - bb), inv_t, M);  // M - a <= 0
-        const float f = __builtin_amdgcn_exp2f(fmaf(y, 1.4426950408889634f, -1.0f));
+        const double d = (double)rr[i] - bb;
+        const float x = (float)(d * inv_t);
+        const float f = 0.5f * __builtin_amdgcn_exp2f(-fabsf(x) * 1.4426950408889634f);
         sfg += (double)(f * gg[i]);
         sf += (double)f;
+        dmin = fmin(dmin, fabs(d));
+    }
+    const double M = block_min_nonneg_f64<NT>(dmin, s_mn) * inv_t;  // workgroup-uniform
+    if (M > 60.0) {
+        sfg = 0.0;
+        sf = 0.0;
+        for (int i = tid; i < n; i += NT) {
+            const float y = (float)fma(-fabs((double)rr[i] - bb), inv_t, M);  // M - a <= 0
+            const float f = __builtin_amdgcn_exp2f(fmaf(y, 1.4426950408889634f, -1.0f));
+            sfg += (double)(f * gg[i]);
+            sf += (double)f;
+        }
     }
     const double T0 = block_sum<NT>(sfg, s_red);  // valid in wave 0
     const double T1 = block_sum<NT>(sf, s_red);
