@@ -43,6 +43,7 @@ ALG_BYTES = {
     "vjp_apply": 12,    # read r, g, write grad
     "radix_sort": 36,   # histogram read 4 + four digit passes (read 4 + write 4)
     "curve_solve": 4,   # read the sorted keys
+    "cert": 4,          # read r (the certification as a pass of its own)
 }
 
 
@@ -175,9 +176,9 @@ def time_steps_cold(L, torch, rd, gd, k, t, steps, options=None, flush_bytes=1 <
     return [s.elapsed_time(e) for s, e in zip(starts, ends)]
 
 
-def kernel_profile(L, torch, rd, gd, k, t, steps, path=0):
+def kernel_profile(L, torch, rd, gd, k, t, steps, path=0, cert_mode=0):
     """Per-kernel durations (ms) from HIP events recorded by the library."""
-    opt = L.default_options(profile=1, path=path)
+    opt = L.default_options(profile=1, path=path, cert_mode=cert_mode)
     acc = {}
     info = None
     p = torch.empty_like(rd)
@@ -223,9 +224,16 @@ def extras(L, torch, rd, gd, cfg):
         ms = timed(torch, fn)
         res[name] = {"median_ms": round(ms, 5), "scores_per_s": n / (ms * 1e-3),
                      "alg_GBps": round(bpe * n / (ms * 1e-3) / 1e9, 1)}
-    # many independent rows (seeded N(0,1) rows, k = n/32 per row, t = 0.05)
+    # DFTopK's mass at finite t (its threshold is the midpoint of the k-th and
+    # (k+1)-th largest scores, so sum p is not held at k)
+    _, _, sd = L.dftopk(rd, k, t, stats=True)
+    res["dftopk"]["sum_p_over_k"] = sd["sum_p"] / k
+    _, _, sl = L.forward(rd, cfg.k, t, stats=True)
+    res["dftopk"]["lapsum_sum_p_over_k"] = sl["sum_p"] / cfg.k
+    # many independent rows (seeded N(0,1) rows, k = n/32 per row, t = 0.05);
+    # algorithmic bytes: forward reads r and writes p (8), VJP 12
     import numpy as np
-    for rows, m in ((4096, 4096), (65536, 256)):
+    for rows, m in ((4096, 4096), (65536, 256), (1000, 65536)):
         rng = np.random.default_rng(rows + m)
         rr = torch.from_numpy(rng.standard_normal((rows, m)).astype(np.float32)).to(rd.device)
         gg = torch.from_numpy(rng.standard_normal((rows, m)).astype(np.float32)).to(rd.device)
@@ -233,10 +241,50 @@ def extras(L, torch, rd, gd, cfg):
         _, bb = L.forward_rows(rr, kk, 0.05)
         fwd = timed(torch, lambda: L.forward_rows(rr, kk, 0.05))
         bwd = timed(torch, lambda: L.vjp_rows(rr, gg, 0.05, bb))
+        gbps = 20 * rows * m / ((fwd + bwd) * 1e-3) / 1e9
         res[f"rows_{rows}x{m}"] = {"forward_ms": round(fwd, 5), "vjp_ms": round(bwd, 5),
-                                   "scores_per_s": rows * m / ((fwd + bwd) * 1e-3)}
+                                   "scores_per_s": rows * m / ((fwd + bwd) * 1e-3),
+                                   "alg_GBps": round(gbps, 1), "frac_peak": round(gbps / PEAK_HBM_GBPS, 4)}
         del rr, gg
     return res
+
+
+def step_bytes_per_score(n, path_taken, cert_mode=0):
+    """Algorithmic bytes per score of one forward + VJP step on the path it
+    took: the n-sized arrays the method itself must read or write (O(s + m)
+    terms left out).  VJP: reduce reads r, g (8); apply reads r, g, writes
+    grad (12)."""
+    vjp = 20
+    if path_taken == 1:
+        if n <= 16384:
+            return 4 + 8 + vjp  # one workgroup reads r; p pass reads r, writes p
+        return 4 + 4 * 8 + 4 + 8 + vjp  # histogram, four digit passes, curve, p
+    if path_taken == 2:
+        return 4 + 8 + vjp + (4 if cert_mode else 0)  # filter, [certification pass,] p
+    return 4 + (4 + 4 * 8 + 4) + 8 + vjp  # filter, then the full sort and curve, p
+
+
+def budget_error(L, torch, rd, k, t, options=None):
+    """|sum p - k| / k of one forward (sum p: fp64 on the device over the
+    written fp32 p) and the path it took."""
+    _, _, st = L.forward(rd, k, t, options=options, stats=True)
+    return abs(st["sum_p"] - k) / k, st
+
+
+def config_entry(L, torch, a, b2, c2, options=None, cert_mode=0, steps=20, warmup=3, cold=10):
+    """Warm and cold step medians of one workload, with its algorithmic
+    bytes, rate and fraction of peak, and the budget error."""
+    _, per = time_steps(L, torch, a, b2, c2.k, c2.t, steps, warmup, options)
+    med = statistics.median(per)
+    e = {"median_ms": round(med, 5), "scores_per_s": c2.n / (med * 1e-3)}
+    if cold:
+        e["cold_median_ms"] = round(statistics.median(time_steps_cold(L, torch, a, b2, c2.k, c2.t, cold, options)), 5)
+    err, st = budget_error(L, torch, a, c2.k, c2.t, options)
+    bps = step_bytes_per_score(c2.n, st["path_taken"], cert_mode)
+    gbps = bps * c2.n / (med * 1e-3) / 1e9
+    e.update({"path_taken": st["path_taken"], "alg_bytes_per_score": bps, "alg_GBps": round(gbps, 1),
+              "frac_peak": round(gbps / PEAK_HBM_GBPS, 4), "budget_rel_err": err})
+    return e
 
 
 def cpu_baseline(cfg, r, g, n_sample):
@@ -349,6 +397,9 @@ def main():
         out["step_roofline"] = {"alg_bytes": step_bytes, "ideal_ms_at_peak": step_bytes / PEAK_HBM_GBPS / 1e6,
                                 "frac_of_median": round(step_bytes / PEAK_HBM_GBPS / 1e6 / med, 4)}
 
+    err, _ = budget_error(L, torch, rd, cfg.k, cfg.t, opts)
+    out["budget_rel_err"] = err
+    out["alg_bytes_per_score"] = step_bytes_per_score(cfg.n, info["path_taken"])
     if not args.no_other_configs:
         others = {}
         for name in ("C1", "C2", "C3", "C5"):
@@ -356,21 +407,28 @@ def main():
             r2, g2, _ = workloads.config_inputs(name)
             a = torch.from_numpy(r2).to(dev)
             b2 = torch.from_numpy(g2).to(dev)
-            tot2, per2 = time_steps(L, torch, a, b2, c2.k, c2.t, 20, 3)
-            cold2 = time_steps_cold(L, torch, a, b2, c2.k, c2.t, 10)
-            others[name] = {"median_ms": round(statistics.median(per2), 5),
-                            "scores_per_s": c2.n / (statistics.median(per2) * 1e-3),
-                            "cold_median_ms": round(statistics.median(cold2), 5)}
+            others[name] = config_entry(L, torch, a, b2, c2)
             if name == "C5":
                 o5 = L.default_options(path=L.PATH_FORCE_FALLBACK)
-                tot3, per3 = time_steps(L, torch, a, b2, c2.k, c2.t, 10, 2, o5)
-                cold3 = time_steps_cold(L, torch, a, b2, c2.k, c2.t, 10, o5)
-                others["C5_forced_fallback"] = {"median_ms": round(statistics.median(per3), 5),
-                                                "scores_per_s": c2.n / (statistics.median(per3) * 1e-3),
-                                                "cold_median_ms": round(statistics.median(cold3), 5)}
+                others["C5_forced_fallback"] = config_entry(L, torch, a, b2, c2, o5, steps=10, warmup=2)
             del a, b2
+        if cfg.name == "C4" and not forced:
+            # the same workload forced onto the full-sort fallback, and with the
+            # certification as its own pass (cert_mode 1)
+            o4 = L.default_options(path=L.PATH_FORCE_FALLBACK)
+            e4 = config_entry(L, torch, rd, gd, cfg, o4, steps=5, warmup=2, cold=0)
+            e4["forced_over_auto"] = round(e4["median_ms"] / med, 3)
+            others["C4_forced_fallback"] = e4
+            oc = L.default_options(cert_mode=1)
+            ec = config_entry(L, torch, rd, gd, cfg, oc, cert_mode=1, steps=args.steps, warmup=3, cold=0)
+            kc, _ = kernel_profile(L, torch, rd, gd, cfg.k, cfg.t, 5, 0, cert_mode=1)
+            ec["cert_pass_ms"] = round(kc.get("cert", 0.0), 5)
+            ec["cert_pass_GBps"] = round(4 * cfg.n / (kc["cert"] * 1e-3) / 1e9, 1) if kc.get("cert") else None
+            ec["over_default"] = round(ec["median_ms"] / med, 4)
+            others["C4_cert_pass"] = ec
         others["note"] = ("median_ms: inputs warm in the caches across steps; cold_median_ms: 1 GiB written "
-                          "before each step, outside its timed events")
+                          "before each step, outside its timed events; alg_GBps: algorithmic bytes of the path "
+                          "taken / warm median; budget_rel_err: |sum p - k| / k of one forward")
         out["other_configs"] = others
 
     if not args.no_other_configs and cfg.name == "C4":

@@ -4,11 +4,17 @@
 // workgroup per row holds the row in LDS: radix sort, the full-sort curve
 // solve of one segment (gist.science section 2.2, full-sort solver), then p
 // for the row; the VJP reduces and applies per row.  Rows must be contiguous
-// (row i starts at i * n) and n <= 16384; the workgroup size follows n.
+// (row i starts at i * n).  Rows of n <= 16384 are sorted in LDS, the
+// workgroup size following n; longer rows, up to 65536, through global
+// scratch (below).
+#include <algorithm>
+
 #include "lapsum_blocksolve.h"
 #include "lapsum_launch.h"
 
 namespace lapsum {
+
+constexpr int kHistCopies_rows = 4;  // lane-group copies of the long-row histograms (as in the radix sort)
 
 template <int NT, int ITEMS>
 __global__ __launch_bounds__(NT) void k_rows_forward(const float* __restrict__ r, int n, const double* k_rows,
@@ -126,7 +132,202 @@ __global__ __launch_bounds__(NT) void k_rows_vjp(const float* __restrict__ r, co
     }
 }
 
-int rows_supported_max() { return kSmallMax; }
+// ---------------------------------------------------------------------------
+// Long rows (16384 < n <= 65536): a row does not fit one workgroup's LDS, so
+// one workgroup per row sorts it through two global scratch buffers of its
+// own -- an LSD radix sort whose passes it runs alone, 4096 keys at a time:
+// all four digit histograms in one read, then per pass each chunk ranked
+// stably in LDS and written out at its digits' running offsets -- and solves
+// over the sorted row in 4096-key segments (aggregates per segment, the curve
+// across them, the root segment's per-score curve, the root), then writes p.
+// A fixed grid of such workgroups takes rows blockIdx.x, + gridDim.x, ...
+// ---------------------------------------------------------------------------
+constexpr int kLongNT = 1024, kLongItems = 4, kLongChunk = kLongNT * kLongItems;  // 4096 keys
+constexpr int kLongMax = 65536;
+constexpr int kLongSegs = kLongMax / kLongChunk;  // 16
+
+__global__ __launch_bounds__(kLongNT) void k_rows_forward_long(const float* __restrict__ r, int n, long long rows,
+                                                                const double* k_rows, double k_all, double t,
+                                                                double inv_t, float* __restrict__ p,
+                                                                double* b_out, uint32_t* scratch) {
+    constexpr int NT = kLongNT, NW = NT / 64;
+    __shared__ uint32_t hist[kHistCopies_rows * 4 * 256];  // lane-group copies x digit positions x bins
+    __shared__ uint32_t offs[4 * 256];                      // per digit position: running digit offsets
+    __shared__ uint32_t cnt[256 * NW];                      // a chunk's per-wave digit counters
+    __shared__ uint32_t stage[kLongChunk];
+    __shared__ uint32_t loc[256];
+    __shared__ uint32_t scr[NW + 2];
+    __shared__ int s_bad, s_skip;
+    __shared__ float sg_first[kLongSegs], sg_last[kLongSegs];
+    __shared__ double sg_P[kLongSegs], sg_Bx[kLongSegs];
+    __shared__ uint32_t sg_cnt[kLongSegs], sg_off[kLongSegs];
+    __shared__ float sc_pk[kLongSegs], sc_bk[kLongSegs];
+    __shared__ double sc_pv[kLongSegs], sc_bv[kLongSegs], sc_bfx[kLongSegs];
+    __shared__ uint32_t sc_rank[kLongSegs];
+    __shared__ float s_k[NT];
+    __shared__ double s_v[NT];
+    __shared__ int s_int[32];
+    __shared__ double s_red[NW];
+    __shared__ double s_b;
+    const int tid = threadIdx.x, w = tid >> 6, lane = lane_id();
+    uint32_t* const bufA = scratch + (size_t)blockIdx.x * 2 * (size_t)n;
+    uint32_t* const bufB = bufA + n;
+    for (long long row = blockIdx.x; row < rows; row += gridDim.x) {  // workgroup-uniform
+        const float* rr = r + row * (long long)n;
+        const double k = k_rows ? k_rows[row] : k_all;
+        // 1. the four digit histograms in one read, and the finiteness check
+        for (int e = tid; e < kHistCopies_rows * 4 * 256; e += NT) hist[e] = 0u;
+        if (tid == 0) { s_bad = !(k > 0.0 && k < (double)n); s_skip = 0; }
+        __syncthreads();
+        {
+            int bad = 0;
+            uint32_t* hl = hist + (lane & (kHistCopies_rows - 1)) * 1024;
+            for (int i = tid; i < n; i += NT) {
+                const float v = rr[i];
+                bad |= !finite_f(v);
+                const uint32_t key = f2key(v);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) atomicAdd(&hl[q * 256 + ((key >> (8 * q)) & 0xFFu)], 1u);
+            }
+            if (bad) atomicOr(&s_bad, 1);
+        }
+        __syncthreads();
+        // exclusive digit offsets per position; a position whose digit is the
+        // same for every key (one bin holds n) needs no pass
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint32_t tot = 0u;
+            if (tid < 256)
+#pragma unroll
+                for (int c = 0; c < kHistCopies_rows; ++c) tot += hist[c * 1024 + q * 256 + tid];
+            const uint32_t ex = block_exclusive_scan<NT>(tot, nullptr, scr);
+            if (tid < 256) {
+                offs[q * 256 + tid] = ex;
+                if (q > 0 && tot == (uint32_t)n) atomicOr(&s_skip, 1 << q);
+            }
+        }
+        __syncthreads();
+        const int skip = s_skip;
+        // 2. the passes (the first always runs: it turns the scores into keys)
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(rr);
+        bool src_float = true;
+        uint32_t* dst = bufA;
+        for (int q = 0; q < 4; ++q) {
+            if ((skip >> q) & 1) continue;  // workgroup-uniform
+            const int shift = 8 * q;
+            for (int c0 = 0; c0 < n; c0 += kLongChunk) {
+                const int cc = n - c0 < kLongChunk ? n - c0 : kLongChunk;
+                uint32_t kr[kLongItems], rk[kLongItems];
+#pragma unroll
+                for (int i = 0; i < kLongItems; ++i) {
+                    const int o = (w * kLongItems + i) * 64 + lane;
+                    kr[i] = o < cc ? (src_float ? f2key(__uint_as_float(src[c0 + o])) : src[c0 + o]) : 0u;
+                }
+                for (int e = tid; e < 256 * NW; e += NT) cnt[e] = 0u;
+                __syncthreads();
+                // stable ranks: per wave and digit, in row order
+                volatile uint32_t* vc = cnt;
+#pragma unroll
+                for (int i = 0; i < kLongItems; ++i) {
+                    const bool valid = (w * kLongItems + i) * 64 + lane < cc;
+                    const unsigned long long act = ballot(valid);
+                    rk[i] = 0u;
+                    if (act != 0ull) {
+                        const uint32_t d = (kr[i] >> shift) & 0xFFu;
+                        const unsigned long long peers = match_digit8(d, act);
+                        const uint32_t b0 = vc[d * NW + w];
+                        rk[i] = b0 + (uint32_t)mbcnt(peers);
+                        if (valid && lane == 63 - __clzll(peers)) vc[d * NW + w] = b0 + (uint32_t)popc64(peers);
+                    }
+                }
+                __syncthreads();
+                // per-wave exclusive offsets of each digit and the chunk's digit totals
+                uint32_t tot = 0u;
+                if (tid < 256) {
+                    uint32_t cw[NW];
+#pragma unroll
+                    for (int x = 0; x < NW; ++x) cw[x] = cnt[tid * NW + x];
+#pragma unroll
+                    for (int x = 0; x < NW; ++x) { cnt[tid * NW + x] = tot; tot += cw[x]; }
+                }
+                const uint32_t lx = block_exclusive_scan<NT>(tot, nullptr, scr);
+                if (tid < 256) loc[tid] = lx;
+                __syncthreads();
+#pragma unroll
+                for (int i = 0; i < kLongItems; ++i) {
+                    if ((w * kLongItems + i) * 64 + lane < cc) {
+                        const uint32_t d = (kr[i] >> shift) & 0xFFu;
+                        stage[loc[d] + cnt[d * NW + w] + rk[i]] = kr[i];
+                    }
+                }
+                __syncthreads();
+                // runs out at the digits' running offsets
+                for (int j = tid; j < cc; j += NT) {
+                    const uint32_t key = stage[j];
+                    const uint32_t d = (key >> shift) & 0xFFu;
+                    dst[offs[q * 256 + d] + (uint32_t)j - loc[d]] = key;
+                }
+                __syncthreads();
+                if (tid < 256) offs[q * 256 + tid] += tot;
+            }
+            __syncthreads();  // the pass's writes before the next pass reads them
+            src = dst;
+            src_float = false;
+            dst = dst == bufA ? bufB : bufA;
+        }
+        const uint32_t* sorted = src;
+        // 3. segment aggregates and the solve over the sorted row
+        const int nseg = (n + kLongChunk - 1) / kLongChunk;
+        for (int sgi = 0; sgi < nseg; ++sgi) {
+            const int c = n - sgi * kLongChunk < kLongChunk ? n - sgi * kLongChunk : kLongChunk;
+            segment_aggregates<NT>(sorted + sgi * kLongChunk, c, inv_t, &sg_first[sgi], &sg_last[sgi], &sg_P[sgi],
+                                   &sg_Bx[sgi], s_red);
+            if (tid == 0) { sg_cnt[sgi] = (uint32_t)c; sg_off[sgi] = (uint32_t)(sgi * kLongChunk); }
+        }
+        __syncthreads();
+        SegView sv{nseg, sg_first, sg_last, sg_P, sg_Bx, sg_cnt, sg_off, sorted, nullptr, nullptr, nullptr, nullptr};
+        SolveScratch sc{sc_pk, sc_pv, sc_bk, sc_bv, sc_bfx, sc_rank, nullptr, nullptr};
+        Tails tl{-INFINITY, INFINITY, 0.0, 0.0, (double)n, 0.0, k, t, inv_t, key2f(sorted[0]), key2f(sorted[n - 1])};
+        const SolveOut o = segment_solve<NT, kLongItems>(sv, tl, sc, s_k, s_v, s_int);
+        if (tid == 0) {
+            const double nanv = __longlong_as_double(0x7ff8000000000000ll);
+            const double b = (s_bad || !o.ok) ? nanv : o.b;
+            s_b = b;
+            b_out[row] = b;
+        }
+        __syncthreads();
+        // 4. p for the row
+        const double b = s_b;
+        float* pr = p + row * (long long)n;
+        for (int i = tid; i < n; i += NT) {
+            const float x = (float)(((double)rr[i] - b) * inv_t);
+            const float e = 0.5f * __builtin_amdgcn_exp2f(-fabsf(x) * 1.4426950408889634f);
+            pr[i] = (b == b) ? (x < 0.0f ? e : 1.0f - e) : b;
+        }
+        __syncthreads();  // LDS is reused by the next row
+    }
+}
+
+int rows_supported_max() { return kLongMax; }
+
+// workgroups of the long-row kernel: one round of co-resident ones at most
+int rows_long_grid(long long rows) {
+    int dev = 0, cus = 0, per = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k_rows_forward_long, kLongNT, 0) != hipSuccess)
+        per = 0;
+    const long long g = std::max<long long>(1, (long long)cus * std::max(per, 1));
+    return (int)std::min<long long>(rows, g);
+}
+
+size_t rows_long_scratch_words(long long rows, int n) { return (size_t)rows_long_grid(rows) * 2 * (size_t)n; }
+
+void launch_rows_forward_long(const float* r, long long rows, int n, const double* k_rows, double k_all, double t,
+                              float* p, double* b_out, uint32_t* scratch, hipStream_t st) {
+    hipLaunchKernelGGL(k_rows_forward_long, dim3((unsigned)rows_long_grid(rows)), dim3(kLongNT), 0, st, r, n, rows,
+                       k_rows, k_all, t, 1.0 / t, p, b_out, scratch);
+}
 
 void launch_rows_forward(const float* r, long long rows, int n, const double* k_rows, double k_all, double t, float* p,
                          double* b_out, hipStream_t st) {

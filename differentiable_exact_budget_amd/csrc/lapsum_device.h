@@ -23,6 +23,8 @@ constexpr int kRadixItems = 16;
 constexpr int kRadixTile = kRadixThreads * kRadixItems;  // 4096 keys
 constexpr int kRadixHistBlocks = 512;
 constexpr int kHistStride = 1028;        // 4 x 256 digit counts + a non-finite flag, per workgroup
+constexpr int kHistGlobalCopies = 8;     // copies of the radix sort's global digit totals
+constexpr int kHistGlobalWords = kHistGlobalCopies * 1024 + 1;  // the copies, then a non-finite flag
 constexpr int kCurveThreads = 256;
 constexpr int kCurveTile = kRadixTile;   // sorted keys per curve segment
 constexpr int kSampleMax = 40960;        // sample size cap (select holds it in registers)

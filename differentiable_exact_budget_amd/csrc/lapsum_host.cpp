@@ -210,7 +210,8 @@ lapsum_status_t alloc_ws(Workspace* w, long long n_cap) {
     if (hipMemsetAsync(w->ctl, 0, sizeof(Ctl), w->stream) != hipSuccess) return LAPSUM_ERR_HIP;
     if (hipMemsetAsync(w->status, 0, w->status_bytes, w->stream) != hipSuccess) return LAPSUM_ERR_HIP;
     // the radix sort's global digit totals start (and are left) at zero
-    if (hipMemsetAsync(w->hist_part, 0, sizeof(uint32_t) * 1025, w->stream) != hipSuccess) return LAPSUM_ERR_HIP;
+    if (hipMemsetAsync(w->hist_part, 0, sizeof(uint32_t) * kHistGlobalWords, w->stream) != hipSuccess)
+        return LAPSUM_ERR_HIP;
     return LAPSUM_OK;
 }
 
@@ -391,14 +392,17 @@ lapsum_status_t wait_summary(Workspace* w, hipStream_t st, unsigned int seq) {
     }
 }
 
-uint32_t next_epoch(Workspace* w, hipStream_t st) {
-    if (w->epoch + 8u >= (1u << 30) || w->status_dirty) {
+// `count` fresh epochs for the words a sort publishes (one per pass); the
+// region is cleared when the epochs would run out or when split passes left
+// raw counts in it
+uint32_t next_epoch(Workspace* w, hipStream_t st, uint32_t count) {
+    if (w->epoch + count + 8u >= (1u << 30) || w->status_dirty) {
         (void)hipMemsetAsync(w->status, 0, w->status_bytes, st);
         w->epoch = 1;
         w->status_dirty = false;
     }
     uint32_t e = w->epoch;
-    w->epoch += 4;
+    w->epoch += count;
     return e;
 }
 
@@ -408,7 +412,7 @@ uint32_t next_epoch(Workspace* w, hipStream_t st) {
 // cleared before the next sort that reads it.
 // form: as launch_radix_sort (0 picks by size).
 void sort_keys(Workspace* w, const float* r, long long n, hipStream_t st, int form = 0) {
-    const uint32_t epoch = next_epoch(w, st);
+    const uint32_t epoch = next_epoch(w, st, 4u);
     launch_radix_sort(r, n, w->keysA, w->keysB, w->hist_part, w->goff, w->status, epoch, w->ctl, st, form);
     if (form == 2 || !radix_uses_onesweep(n)) w->status_dirty = true;
 }
@@ -1236,8 +1240,17 @@ lapsum_status_t lapsum_forward_batched(const float* scores, int64_t rows, int64_
     if (!(t > 0.0f) || !std::isfinite(t)) return LAPSUM_ERR_INVALID_ARGUMENT;
     try {
         hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-        if (n <= rows_supported_max()) {
+        if (n <= kRowsLdsMax) {
             launch_rows_forward(scores, rows, (int)n, k_rows, k, (double)t, p_out, b_out, st);
+            return hip_ok(hipGetLastError());
+        }
+        if (n <= rows_supported_max()) {
+            // one workgroup per row, sorting through scratch of the stream's
+            // workspace (its radix key buffer)
+            WsGuard wsg;
+            lapsum_status_t gs = get_ws(st, (long long)rows_long_scratch_words(rows, (int)n), &wsg);
+            if (gs != LAPSUM_OK) return gs;
+            launch_rows_forward_long(scores, rows, (int)n, k_rows, k, (double)t, p_out, b_out, wsg.w->keysA, st);
             return hip_ok(hipGetLastError());
         }
         // long rows: the single-vector solver, row by row

@@ -73,7 +73,11 @@ void launch_heavy_collect(const float* r, long long n, const Ctl* ctl, const flo
                           const HeavyArrays& ha, uint32_t* base, uint32_t hchunks, double t, hipStream_t st);
 
 // lapsum_batched.hip
-int rows_supported_max();
+int rows_supported_max();  // longest row the row kernels take (longer rows: the single-vector solver)
+constexpr int kRowsLdsMax = kSmallMax;  // rows up to this length are sorted in LDS
+size_t rows_long_scratch_words(long long rows, int n);  // scratch of launch_rows_forward_long (uint32 words)
+void launch_rows_forward_long(const float* r, long long rows, int n, const double* k_rows, double k_all, double t,
+                              float* p, double* b_out, uint32_t* scratch, hipStream_t st);
 void launch_rows_forward(const float* r, long long rows, int n, const double* k_rows, double k_all, double t, float* p,
                          double* b_out, hipStream_t st);
 void launch_rows_vjp(const float* r, const float* g, long long rows, int n, double t, const double* b, float* grad,

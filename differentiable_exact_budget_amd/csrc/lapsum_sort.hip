@@ -231,12 +231,15 @@ __global__ __launch_bounds__(kSortThreads) void k_band_root(const uint32_t* buck
 // 8.8 us for N(0,1) scores, 11.5 us for equal ones; grouping equal digits
 // with ballots first, or a one-digit-wave test, costs more).  The workgroup
 // totals then go into the global totals with integer atomics (order-free:
-// deterministic).
-// The last workgroup to finish turns the totals into the four passes'
-// exclusive digit offsets (goff), sets the control flags for the sort and
-// re-zeroes the totals and its ticket.
-// hist: global uint32[1025] (four 256-bin histograms, then a non-finite
-// flag), all zero on entry and on exit.
+// deterministic), into one of kHistGlobalCopies copies picked by the
+// workgroup, so that each global word takes a few dozen adds rather than one
+// from every workgroup (the adds are done at device scope, one after another
+// per word).
+// The last workgroup to finish sums the copies, turns the totals into the
+// four passes' exclusive digit offsets (goff), sets the control flags for the
+// sort and re-zeroes the copies and its ticket.
+// hist: global uint32[kHistGlobalCopies * 1024 + 1] (per copy four 256-bin
+// histograms; then a non-finite flag), all zero on entry and on exit.
 constexpr int kHistCopies = 4;  // LDS histogram copies, by lane & 3
 
 // the device's resident-pass lock: 0 when free, else the holder's token
@@ -297,9 +300,9 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_hist(const float* __res
         uint32_t c = 0u;
 #pragma unroll
         for (int q = 0; q < kHistCopies; ++q) c += h[q * 1024 + i];
-        old[b] = c ? atomicAdd(&hist[i], c) : 0u;
+        old[b] = c ? atomicAdd(&hist[(blockIdx.x % kHistGlobalCopies) * 1024 + i], c) : 0u;
     }
-    old[NB] = (tid == 0 && s_bad) ? atomicOr(&hist[1024], 1u) : 0u;
+    old[NB] = (tid == 0 && s_bad) ? atomicOr(&hist[kHistGlobalCopies * 1024], 1u) : 0u;
     uint32_t acc = 0u;
 #pragma unroll
     for (int b = 0; b <= NB; ++b) acc |= old[b];
@@ -309,18 +312,27 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_hist(const float* __res
     __syncthreads();
     if (!s_last) return;
     __threadfence();
-    uint32_t x[4];
+    uint32_t y[kHistGlobalCopies][4];  // every load in flight, then the sums
+#pragma unroll
+    for (int q = 0; q < kHistGlobalCopies; ++q)
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            y[q][p] = __hip_atomic_load(&hist[q * 1024 + p * 256 + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t any_bad =
+        __hip_atomic_load(&hist[kHistGlobalCopies * 1024], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t x[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int q = 0; q < kHistGlobalCopies; ++q)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            x[p] += y[q][p];
+            hist[q * 1024 + p * 256 + tid] = 0u;
+        }
 #pragma unroll
     for (int p = 0; p < 4; ++p)
-        x[p] = __hip_atomic_load(&hist[p * 256 + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t any_bad = __hip_atomic_load(&hist[1024], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
         goff[p * 256 + tid] = block_exclusive_scan<kRadixThreads>(x[p], nullptr, scr);  // thread = digit
-        hist[p * 256 + tid] = 0u;
-    }
     if (tid == 0) {
-        hist[1024] = 0u;
+        hist[kHistGlobalCopies * 1024] = 0u;
         ctl->done[0] = 0u;
         ctl->flags = any_bad ? kFlagNonFinite : 0;
         // the one-kernel passes: resident when the lock is free (the sort's

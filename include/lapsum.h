@@ -227,13 +227,18 @@ lapsum_status_t lapsum_dftopk(const float* scores, int64_t n, int64_t k, float t
  * grad_out: device fp32[rows * n], row i at offset i * n.  b_out / b: device
  * fp64[rows].  Budget: k_rows (device fp64[rows], each in (0, n)) when not
  * NULL, else the scalar k for every row.  Rows with n <= 16384 are solved one
- * workgroup per row in LDS (sort, curve scan, closed-form root, p); longer
- * rows run through lapsum_forward_ex's solver one after another.  A row with
- * a non-finite score or a budget outside (0, n) gets b = NaN and p = NaN;
- * the call still returns LAPSUM_OK.  Argument errors (NULL pointers,
- * rows < 1, n outside [1, 2^32), a bad scalar k when k_rows is NULL, a bad t)
- * return LAPSUM_ERR_INVALID_ARGUMENT before any launch.  Asynchronous on
- * `stream` (except for long rows with k_rows, whose budgets are read first).
+ * workgroup per row in LDS (sort, curve scan, closed-form root, p); rows up
+ * to 65536 scores one workgroup per row that sorts its row through scratch
+ * memory of the stream's workspace (2 n words per workgroup of a grid of one
+ * round of co-resident workgroups), then solves and writes p; longer rows run
+ * through lapsum_forward_ex's solver one after another.  A row with a
+ * non-finite score or a budget outside (0, n) gets b = NaN and p = NaN; the
+ * call still returns LAPSUM_OK.  Argument errors (NULL pointers, rows < 1, n
+ * outside [1, 2^32), a bad scalar k when k_rows is NULL, a bad t) return
+ * LAPSUM_ERR_INVALID_ARGUMENT before any launch.  Asynchronous on `stream`
+ * (except for rows longer than 65536 with k_rows, whose budgets are read
+ * first).  The VJP (lapsum_vjp_batched) runs one workgroup per row up to
+ * 65536 scores, and longer rows through lapsum_vjp's kernels one by one.
  */
 lapsum_status_t lapsum_forward_batched(const float* scores, int64_t rows, int64_t n, double k,
                                        const double* k_rows, float t, float* p_out, double* b_out,

@@ -1,6 +1,7 @@
 """GPU parity of the row-wise (batched) operator against the oracle, row by
 row: b, p, the mass of every row and the VJP, for each workgroup size, per-row
-budgets, long rows that go through the single-vector solver, and rows that
+budgets, long rows (sorted through global scratch by one workgroup each, up
+to 65536 scores; longer ones through the single-vector solver), and rows that
 must come out as NaN (a non-finite score, a budget outside (0, n))."""
 import numpy as np
 import pytest
@@ -16,6 +17,8 @@ L = pytest.importorskip("differentiable_exact_budget_amd")
 @pytest.mark.parametrize("rows,n,per_row_k,t", [
     (1000, 8, False, 0.3), (3000, 64, True, 0.05), (513, 257, False, 0.1), (200, 4096, True, 0.01),
     (20, 16384, False, 0.02), (3, 20000, True, 0.05),
+    # long rows: more rows than workgroups of the long-row grid, so each takes several
+    (600, 16385, True, 0.05), (300, 30001, False, 0.01), (100, 65536, True, 0.02), (2, 70000, False, 0.05),
 ])
 def test_rows_match_oracle(oracle_mod, rows, n, per_row_k, t):
     rng = np.random.default_rng(rows * 7 + n)
@@ -38,12 +41,13 @@ def test_rows_match_oracle(oracle_mod, rows, n, per_row_k, t):
         check_vjp(oracle_mod, r[i], g[i], t, b_ref, gh[i], label=f"row {i}")
 
 
-def test_rows_bad_rows_are_nan():
+@pytest.mark.parametrize("n", [100, 20000])
+def test_rows_bad_rows_are_nan(n):
     rng = np.random.default_rng(3)
-    r = rng.standard_normal((6, 100)).astype(np.float32)
+    r = rng.standard_normal((6, n)).astype(np.float32)
     r[2, 17] = np.nan
     r[4, 3] = np.inf
-    k = torch.tensor([5.0, 0.0, 5.0, 100.0, 5.0, 99.5], dtype=torch.float64, device="cuda")
+    k = torch.tensor([5.0, 0.0, 5.0, float(n), 5.0, n - 0.5], dtype=torch.float64, device="cuda")
     p, b = L.forward_rows(to_dev(r), k, 0.1)
     bh = b.cpu().numpy()
     ph = p.cpu().numpy()
@@ -67,3 +71,21 @@ def test_rows_autograd_matches_vjp(oracle_mod):
     assert torch.equal(rd.grad, ref)
     b_ref, _ = oracle_mod.solve(r[5].astype(np.float64), 16.0, t32(0.05))
     assert abs(float(b[5].item()) - b_ref) <= 1e-5 * 0.05
+
+
+@pytest.mark.parametrize("n", [16385, 50000])
+def test_long_rows_ties_and_equal(oracle_mod, n):
+    """Long rows whose digits repeat (all-equal rows skip their constant
+    digit positions) and rows of heavy ties."""
+    rng = np.random.default_rng(n)
+    rows = 8
+    r = np.empty((rows, n), dtype=np.float32)
+    r[0] = 2.5
+    r[1] = -1.0
+    r[2:] = np.round(rng.standard_normal((rows - 2, n)) * 4.0) / 4.0
+    k = np.full(rows, n / 3.0)
+    rd = to_dev(r)
+    p, b = L.forward_rows(rd, float(k[0]), 0.05)
+    ph, bh = p.cpu().numpy(), b.cpu().numpy()
+    for i in range(rows):
+        check_forward(oracle_mod, r[i], float(k[i]), 0.05, ph[i], float(bh[i]), label=f"row {i}")
