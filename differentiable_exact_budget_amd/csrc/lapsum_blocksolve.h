@@ -467,71 +467,38 @@ LS_DEV SegCarries block_seg_carries(uint32_t c, float f, float l, double P, doub
         __syncthreads();
         return r;
     }
-    if (w == 0) {
-        // lane x < NW: the carries of the waves before / after wave x, tails included
-        const bool in = lane < NW;
-        float ak = in ? sk[lane] : -INFINITY, bk = in ? sk[NW + lane] : INFINITY;
-        double av = in ? sv[lane] : 0.0, bv = in ? sv[NW + lane] : 0.0;
-        float mx = in ? sk[2 * NW + lane] : -INFINITY, mn = in ? sk[3 * NW + lane] : INFINITY;
-        const float rx = in ? sk[4 * NW + lane] : 0.0f;
-        const bool fx = in && su[2 * NW + lane] != 0u;
-        uint32_t cn = in ? su[lane] : 0u;
-#pragma unroll
-        for (int o = 1; o < NW; o <<= 1) {
-            const float lk2 = __shfl_up(ak, o, 64);
-            const double lv2 = __shfl_up(av, o, 64);
-            const float rk2 = __shfl_down(bk, o, 64);
-            const double rv2 = __shfl_down(bv, o, 64);
-            const float mx2 = __shfl_up(mx, o, 64), mn2 = __shfl_down(mn, o, 64);
-            const uint32_t cn2 = __shfl_up(cn, o, 64);
-            if (lane >= o) { fwd_combine(lk2, lv2, ak, av, inv_t); mx = fmaxf(mx, mx2); cn += cn2; }
-            if (lane + o < NW) { bwd_combine(bk, bv, rk2, rv2, inv_t); mn = fminf(mn, mn2); }
-        }
-        float pk = __shfl_up(ak, 1, 64);
-        if (lane == 0) pk = -INFINITY;
-        double pv = __shfl_up(av, 1, 64);
-        if (lane == 0) pv = 0.0;
-        float qk = __shfl_down(bk, 1, 64);
-        if (lane + 1 >= NW) qk = INFINITY;
-        double qv = __shfl_down(bv, 1, 64);
-        if (lane + 1 >= NW) qv = 0.0;
-        float pmx = __shfl_up(mx, 1, 64);
-        if (lane == 0) pmx = -INFINITY;
-        float qmn = __shfl_down(mn, 1, 64);
-        if (lane + 1 >= NW) qmn = INFINITY;
-        uint32_t pcn = __shfl_up(cn, 1, 64);
-        if (lane == 0) pcn = 0u;
-        {   // the lower tail precedes everything, the upper tail follows everything
-            float tk = -INFINITY; double tv = 0.0;
-            if (tl.S_L > 0.0 && tl.aL > -INFINITY) { tk = tl.aL; tv = tl.S_L; }
-            fwd_combine(tk, tv, pk, pv, inv_t);
-            if (tl.S_R > 0.0 && tl.aR < INFINITY) bwd_combine(qk, qv, tl.aR, tl.S_R, inv_t);
-        }
-        if (in) {
-            sk[6 * NW + lane] = pk; sv[4 * NW + lane] = pv;
-            sk[7 * NW + lane] = qk; sv[5 * NW + lane] = qv;
-        }
-        if (fx) {  // into the wave's own frame (key ref: every exponent <= 0)
-            pv = pv != 0.0 ? pv * exp(((double)pk - (double)rx) * inv_t) : 0.0;
-            qv = qv != 0.0 ? qv * exp(((double)rx - (double)qk) * inv_t) : 0.0;
-            pk = rx;
-            qk = rx;
-        }
-        if (in) {
-            sk[5 * NW + lane] = pk; sv[2 * NW + lane] = pv;
-            sk[NW + lane] = qk; sv[3 * NW + lane] = qv;
-            sk[2 * NW + lane] = pmx; sk[3 * NW + lane] = qmn;
-            su[NW + lane] = pcn;
-        }
+    // Every wave forms its own carries from the other waves' totals at once:
+    // lane y < NW stands for wave y, lane NW for the lower tail and lane
+    // NW + 1 for the upper tail.  A chain of forward combines leaves the key
+    // of its last non-empty member, K, and the sum over members j of
+    // V_j e^{(K_j - K)/t}: keys rise with the wave index, so K is the largest
+    // key and every exponent is <= 0; backward, the smallest key and
+    // e^{(K - K_j)/t}.  One exponential per lane, no serial chain.
+    const bool tailL = tl.S_L > 0.0 && tl.aL > -INFINITY;
+    const bool tailR = tl.S_R > 0.0 && tl.aR < INFINITY;
+    float xk = -INFINITY, yk = INFINITY, pm = -INFINITY, qm = INFINITY;
+    double xv = 0.0, yv = 0.0;
+    uint32_t pc = 0u;
+    if (lane < NW && lane < w) { xk = sk[lane]; xv = sv[lane]; pm = sk[2 * NW + lane]; pc = su[lane]; }
+    if (lane < NW && lane > w) { yk = sk[NW + lane]; yv = sv[NW + lane]; qm = sk[3 * NW + lane]; }
+    if (lane == NW && tailL) { xk = tl.aL; xv = tl.S_L; }
+    if (lane == NW + 1 && tailR) { yk = tl.aR; yv = tl.S_R; }
+    const float Kf = __uint_as_float(wave_max_f32_bits(xk));
+    const float Kb = __uint_as_float(wave_min_f32_bits(yk));
+    const double Vf = wave_sum(xv != 0.0 ? xv * exp(((double)xk - (double)Kf) * inv_t) : 0.0);
+    const double Vb = wave_sum(yv != 0.0 ? yv * exp(((double)Kb - (double)yk) * inv_t) : 0.0);
+    r.kf_o = Kf; r.vf_o = Vf;
+    r.kb_o = Kb; r.vb_o = Vb;
+    if (wadd && !empty) {  // into the wave's own frame (key ref: every exponent <= 0)
+        r.kf_w = ref; r.vf_w = Vf != 0.0 ? Vf * exp(((double)Kf - (double)ref) * inv_t) : 0.0;
+        r.kb_w = ref; r.vb_w = Vb != 0.0 ? Vb * exp(((double)ref - (double)Kb) * inv_t) : 0.0;
+    } else {
+        r.kf_w = Kf; r.vf_w = Vf;
+        r.kb_w = Kb; r.vb_w = Vb;
     }
-    __syncthreads();
-    r.kf_w = sk[5 * NW + w]; r.vf_w = sv[2 * NW + w];
-    r.kb_w = sk[NW + w]; r.vb_w = sv[3 * NW + w];
-    r.kf_o = sk[6 * NW + w]; r.vf_o = sv[4 * NW + w];
-    r.kb_o = sk[7 * NW + w]; r.vb_o = sv[5 * NW + w];
-    r.rank += su[NW + w];
-    r.last_before = fmaxf(el, sk[2 * NW + w]);
-    r.first_after = fminf(eF, sk[3 * NW + w]);
+    r.rank += (uint32_t)wave_sum_u64(pc);
+    r.last_before = fmaxf(el, __uint_as_float(wave_max_f32_bits(pm)));
+    r.first_after = fminf(eF, __uint_as_float(wave_min_f32_bits(qm)));
     return r;
 }
 

@@ -134,6 +134,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(const float* __restri
     uint32_t nbelow = 0u, nin = 0u;
 #pragma unroll
     for (int i = 0; i < kSelectItems; ++i) {
+        if ((i & 3) == 0 && (i / 4) * 4 * kSelectThreads >= s) break;  // past the sample's end (uniform)
         if ((vmask >> i) & 1ull) { nbelow += kr[i] < wlo; nin += (kr[i] >= wlo && kr[i] <= whi); }
     }
     // one scan of both counts packed in a word (each total <= kSampleMax <
@@ -154,6 +155,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(const float* __restri
     if (fast) {
 #pragma unroll
         for (int i = 0; i < kSelectItems; ++i) {
+            if ((i & 3) == 0 && (i / 4) * 4 * kSelectThreads >= s) break;
             if (((vmask >> i) & 1ull) && kr[i] >= wlo && kr[i] <= whi) win[pos++] = kr[i];
         }
         const int wp = max(next_pow2((int)W), 64);
