@@ -44,6 +44,8 @@ ALG_BYTES = {
     "radix_sort": 36,   # histogram read 4 + four digit passes (read 4 + write 4)
     "curve_solve": 4,   # read the sorted keys
     "cert": 4,          # read r (the certification as a pass of its own)
+    "heavy_collect": 4,  # read r again (scores of overflowed buckets)
+    "small_solve": 4,   # read r (one-workgroup sort and solve)
 }
 
 

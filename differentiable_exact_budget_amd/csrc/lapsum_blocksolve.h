@@ -502,6 +502,15 @@ LS_DEV SegCarries block_seg_carries(uint32_t c, float f, float l, double P, doub
     return r;
 }
 
+// Storage slot of segment s when each of nt threads owns per consecutive
+// segments (thread t: segments t*per .. t*per + per - 1): the q-th segment of
+// thread t sits at q*nt + t, so that the threads' q-th loads form one
+// contiguous run (with per consecutive segments per thread at consecutive
+// addresses, every lane of a load touched a different cache line).  The
+// identity when per == 1.  Every writer of segment aggregates for a solve
+// with more segments than threads uses the same slots.
+LS_DEV int seg_slot(int s, int per, int nt) { return (s % per) * nt + s / per; }
+
 // Runs on all NT threads of one workgroup; result valid in thread 0.
 // Memory round trips are kept to a handful: each lane of wave 0 fetches its
 // segments' aggregates in one batch, the root segment's scores are read
@@ -510,7 +519,7 @@ LS_DEV SegCarries block_seg_carries(uint32_t c, float f, float l, double P, doub
 template <int NT, int EMAX>
 __device__ __attribute__((always_inline)) SolveOut segment_solve(const SegView sv, const Tails tl, const SolveScratch sc,
                                   float* s_k, double* s_v, int* s_int) {
-    constexpr int SEGB = 8;  // segments fetched per batch by each lane of wave 0
+    constexpr int PB = 4;  // segments per batch of loads when a thread holds several
     const int tid = threadIdx.x;
     const double inv_t = tl.inv_t;
     const int nseg = sv.nseg;
@@ -525,6 +534,9 @@ __device__ __attribute__((always_inline)) SolveOut segment_solve(const SegView s
     // G at every score itself, and when none passes the root lies below the
     // first score.
     const bool whole = sv.P == nullptr;
+    // storage slot of segment s (see seg_slot): identity when nseg <= NT
+    const int per_seg = (nseg + NT - 1) / NT;
+    const auto slot = [&](int s) { return seg_slot(s, per_seg, NT); };
     int sstar = 0;
     if (!whole) {
         // ---- phases 1-3: carries before/after every segment, segment ranks, and
@@ -538,23 +550,43 @@ __device__ __attribute__((always_inline)) SolveOut segment_solve(const SegView s
         uint32_t c1 = 0u, o1 = 0u; float f1 = 0.0f; double Bx1 = 0.0;  // the one segment (per == 1)
         if (per == 1) {
             if (s0 < s1) {
-                c1 = sv.cnt[s0];
-                o1 = sv.off[s0];
+                c1 = sv.cnt[slot(s0)];
+                o1 = sv.off[slot(s0)];
                 if (c1) {
-                    f1 = sv.first[s0]; Bx1 = sv.Bx[s0];
-                    ak = sv.last[s0]; av = sv.P[s0];
+                    f1 = sv.first[slot(s0)]; Bx1 = sv.Bx[slot(s0)];
+                    ak = sv.last[slot(s0)]; av = sv.P[slot(s0)];
                     bk = f1; bvv = 1.0 + Bx1;
                 }
                 rc = c1;
             }
         } else {
-            for (int s = s0; s < s1; ++s) {
-                const uint32_t c = sv.cnt[s];
-                if (c) { float lk = ak; double lv = av; ak = sv.last[s]; av = sv.P[s]; fwd_combine(lk, lv, ak, av, inv_t); }
-                rc += c;
+            // several segments per thread: their aggregates are read PB at a
+            // time, all loads of a batch in flight before the combines
+            for (int sb = s0; sb < s1; sb += PB) {
+                uint32_t cq[PB]; float lq[PB]; double Pq[PB];
+#pragma unroll
+                for (int q = 0; q < PB; ++q) {
+                    const int s = sb + q;
+                    const bool in = s < s1;
+                    cq[q] = in ? sv.cnt[slot(s)] : 0u; lq[q] = in ? sv.last[slot(s)] : 0.0f; Pq[q] = in ? sv.P[slot(s)] : 0.0;
+                }
+#pragma unroll
+                for (int q = 0; q < PB; ++q) {
+                    if (cq[q]) { float lk = ak; double lv = av; ak = lq[q]; av = Pq[q]; fwd_combine(lk, lv, ak, av, inv_t); }
+                    rc += cq[q];
+                }
             }
-            for (int s = s1 - 1; s >= s0; --s) {
-                if (sv.cnt[s]) { float k2 = sv.first[s]; double v2 = 1.0 + sv.Bx[s]; bwd_combine(k2, v2, bk, bvv, inv_t); bk = k2; bvv = v2; }
+            for (int sb = s1 - 1; sb >= s0; sb -= PB) {
+                uint32_t cq[PB]; float fq[PB]; double Bq[PB];
+#pragma unroll
+                for (int q = 0; q < PB; ++q) {
+                    const int s = sb - q;
+                    const bool in = s >= s0;
+                    cq[q] = in ? sv.cnt[slot(s)] : 0u; fq[q] = in ? sv.first[slot(s)] : 0.0f; Bq[q] = in ? sv.Bx[slot(s)] : 0.0;
+                }
+#pragma unroll
+                for (int q = 0; q < PB; ++q)
+                    if (cq[q]) { float k2 = fq[q]; double v2 = 1.0 + Bq[q]; bwd_combine(k2, v2, bk, bvv, inv_t); bk = k2; bvv = v2; }
             }
         }
         uint32_t rbase;
@@ -577,7 +609,7 @@ __device__ __attribute__((always_inline)) SolveOut segment_solve(const SegView s
         }
         int cand = -1;
         auto g_test = [&](int s, double Pf, double Bf, uint32_t rank) {
-            sc.bfx[s] = Bf;
+            sc.bfx[slot(s)] = Bf;
             const double G = 0.5 * Pf + (tl.m - 1.0 - (double)rank) + tl.c_R - 0.5 * Bf;
             if (G >= tl.k) cand = max(cand, s);
         };
@@ -603,18 +635,39 @@ __device__ __attribute__((always_inline)) SolveOut segment_solve(const SegView s
                 g_test(s0, Pf, Bf, rbase);
             }
         } else {
-            for (int s = s0; s < s1; ++s) {
-                const uint32_t c = sv.cnt[s];
-                sc.pk[s] = ak; sc.pv[s] = av; sc.rank[s] = rbase;
-                rbase += c;
-                if (c) { float lk = ak; double lv = av; ak = sv.last[s]; av = sv.P[s]; fwd_combine(lk, lv, ak, av, inv_t); }
+            for (int sb = s0; sb < s1; sb += PB) {
+                uint32_t cq[PB]; float lq[PB]; double Pq[PB];
+#pragma unroll
+                for (int q = 0; q < PB; ++q) {
+                    const int s = sb + q;
+                    const bool in = s < s1;
+                    cq[q] = in ? sv.cnt[slot(s)] : 0u; lq[q] = in ? sv.last[slot(s)] : 0.0f; Pq[q] = in ? sv.P[slot(s)] : 0.0;
+                }
+#pragma unroll
+                for (int q = 0; q < PB; ++q) {
+                    const int s = sb + q;
+                    if (s < s1) { sc.pk[slot(s)] = ak; sc.pv[slot(s)] = av; sc.rank[slot(s)] = rbase; }
+                    rbase += cq[q];
+                    if (cq[q]) { float lk = ak; double lv = av; ak = lq[q]; av = Pq[q]; fwd_combine(lk, lv, ak, av, inv_t); }
+                }
             }
-            for (int s = s1 - 1; s >= s0; --s) {
-                sc.bk[s] = bk; sc.bv[s] = bvv;
-                if (sv.cnt[s]) {
-                    const float f = sv.first[s]; const double Bx = sv.Bx[s];
-                    g_at_first(s, f, Bx, sc.pk[s], sc.pv[s], bk, bvv, sc.rank[s]);
-                    float k2 = f; double v2 = 1.0 + Bx; bwd_combine(k2, v2, bk, bvv, inv_t); bk = k2; bvv = v2;
+            for (int sb = s1 - 1; sb >= s0; sb -= PB) {
+                uint32_t cq[PB], rq[PB]; float fq[PB], pkq[PB]; double Bq[PB], pvq[PB];
+#pragma unroll
+                for (int q = 0; q < PB; ++q) {
+                    const int s = sb - q;
+                    const bool in = s >= s0;
+                    cq[q] = in ? sv.cnt[slot(s)] : 0u; fq[q] = in ? sv.first[slot(s)] : 0.0f; Bq[q] = in ? sv.Bx[slot(s)] : 0.0;
+                    pkq[q] = in ? sc.pk[slot(s)] : 0.0f; pvq[q] = in ? sc.pv[slot(s)] : 0.0; rq[q] = in ? sc.rank[slot(s)] : 0u;
+                }
+#pragma unroll
+                for (int q = 0; q < PB; ++q) {
+                    const int s = sb - q;
+                    if (s >= s0) { sc.bk[slot(s)] = bk; sc.bv[slot(s)] = bvv; }
+                    if (cq[q]) {
+                        g_at_first(s, fq[q], Bq[q], pkq[q], pvq[q], bk, bvv, rq[q]);
+                        float k2 = fq[q]; double v2 = 1.0 + Bq[q]; bwd_combine(k2, v2, bk, bvv, inv_t); bk = k2; bvv = v2;
+                    }
                 }
             }
         }
@@ -645,13 +698,13 @@ __device__ __attribute__((always_inline)) SolveOut segment_solve(const SegView s
                         if (cr.vb_o != 0.0) bvv += cr.vb_o * exp(((double)bk - (double)cr.kb_o) * inv_t);
                     } else if (tl.S_R > 0.0 && tl.aR < INFINITY) { bk = tl.aR; bvv = tl.S_R; }
                     else { bk = INFINITY; bvv = 0.0; }
-                    sc.pk[s0] = ak; sc.pv[s0] = av; sc.bk[s0] = bk; sc.bv[s0] = bvv; sc.rank[s0] = rbase;
+                    sc.pk[slot(s0)] = ak; sc.pv[slot(s0)] = av; sc.bk[slot(s0)] = bk; sc.bv[slot(s0)] = bvv; sc.rank[slot(s0)] = rbase;
                     s_seg[0] = c1; s_seg[1] = o1; s_seg[2] = rbase;
                     s_ck[0] = ak; s_cv[0] = av; s_ck[1] = bk; s_cv[1] = bvv;
                 }
             } else if (tid == 0) {
-                s_seg[0] = sv.cnt[sstar]; s_seg[1] = sv.off[sstar]; s_seg[2] = sc.rank[sstar];
-                s_ck[0] = sc.pk[sstar]; s_cv[0] = sc.pv[sstar]; s_ck[1] = sc.bk[sstar]; s_cv[1] = sc.bv[sstar];
+                s_seg[0] = sv.cnt[slot(sstar)]; s_seg[1] = sv.off[slot(sstar)]; s_seg[2] = sc.rank[slot(sstar)];
+                s_ck[0] = sc.pk[slot(sstar)]; s_cv[0] = sc.pv[slot(sstar)]; s_ck[1] = sc.bk[slot(sstar)]; s_cv[1] = sc.bv[slot(sstar)];
             }
         }
     } else if (tid == 0) {  // whole array: the one segment, rank 0, no carries
@@ -863,19 +916,19 @@ __device__ __attribute__((always_inline)) SolveOut segment_solve(const SegView s
         // the root lies below the first score of the segments
         double ref, lnA, lnB, clo, chi;
         int s0n = -1;
-        for (int s = 0; s < nseg; ++s) if (sv.cnt[s]) { s0n = s; break; }
+        for (int s = 0; s < nseg; ++s) if (sv.cnt[slot(s)]) { s0n = s; break; }
         const double D = tl.m + tl.c_R - tl.k;
         if (tl.aL > -INFINITY) {
             ref = tl.aL; clo = tl.aL;
             lnA = tl.S_L > 0.0 ? log(tl.S_L) : -INFINITY;
-            if (s0n >= 0) { chi = sv.first[s0n]; lnB = ((double)tl.aL - chi) * inv_t + log1p(sc.bfx[s0n]); }
+            if (s0n >= 0) { chi = sv.first[slot(s0n)]; lnB = ((double)tl.aL - chi) * inv_t + log1p(sc.bfx[slot(s0n)]); }
             else {
                 chi = tl.aR;
                 lnB = (tl.S_R > 0.0 && tl.aR < INFINITY) ? log(tl.S_R) + ((double)tl.aL - (double)tl.aR) * inv_t : -INFINITY;
             }
         } else {
             clo = -INFINITY; lnA = -INFINITY;
-            if (s0n >= 0) { ref = sv.first[s0n]; chi = ref; lnB = log1p(sc.bfx[s0n]); }
+            if (s0n >= 0) { ref = sv.first[slot(s0n)]; chi = ref; lnB = log1p(sc.bfx[slot(s0n)]); }
             else { ref = tl.aR; chi = tl.aR; lnB = tl.S_R > 0.0 ? log(tl.S_R) : -INFINITY; }
         }
         out.jstar = -1;

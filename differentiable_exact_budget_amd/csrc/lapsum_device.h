@@ -27,6 +27,7 @@ constexpr int kHistGlobalCopies = 8;     // copies of the radix sort's global di
 constexpr int kHistGlobalWords = kHistGlobalCopies * 1024 + 1;  // the copies, then a non-finite flag
 constexpr int kCurveThreads = 256;
 constexpr int kCurveTile = kRadixTile;   // sorted keys per curve segment
+constexpr int kCurveRootThreads = 1024;  // the full-sort root's workgroup
 constexpr int kSampleMax = 40960;        // sample size cap (select holds it in registers)
 constexpr int kSelectThreads = 1024;
 constexpr int kSelectItems = kSampleMax / kSelectThreads;  // 40

@@ -103,7 +103,10 @@ Layout make_layout(long long n_cap) {
     Layout L{};
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
-    const long long nseg = std::max<long long>(std::max<long long>(kMaxBuckets, tiles_for(n_cap)), 1);
+    // segment slots: a whole number of kCurveRootThreads (the root reads
+    // segment s of more than one per thread from seg_slot's slot)
+    const long long nseg0 = std::max<long long>(std::max<long long>(kMaxBuckets, tiles_for(n_cap)), 1);
+    const long long nseg = (nseg0 + kCurveRootThreads - 1) / kCurveRootThreads * kCurveRootThreads;
     const long long elem = std::max<long long>(kBucketCapMax, std::max(kRadixTile, kSmallMax));
     L.ctl = take(sizeof(Ctl));
     L.part = take(sizeof(double) * 2 * (size_t)kMaxStreamParts);

@@ -854,16 +854,18 @@ __global__ __launch_bounds__(kCurveThreads) void k_curve_tiles(const uint32_t* _
     const long long base = (long long)tile * kCurveTile;
     const long long rem = n - base;
     const int c = rem < kCurveTile ? (int)rem : kCurveTile;
-    segment_aggregates<kCurveThreads>(keys + base, c, inv_t, &seg.first[tile], &seg.last[tile], &seg.P[tile],
-                                      &seg.Bx[tile], s_red);
-    if (threadIdx.x == 0) { seg.cnt[tile] = (uint32_t)c; seg.off[tile] = (uint32_t)base; }
+    // stored in the slot the one-workgroup root reads it from
+    const int at = seg_slot(tile, (int)((gridDim.x + kCurveRootThreads - 1) / kCurveRootThreads), kCurveRootThreads);
+    segment_aggregates<kCurveThreads>(keys + base, c, inv_t, &seg.first[at], &seg.last[at], &seg.P[at], &seg.Bx[at],
+                                      s_red);
+    if (threadIdx.x == 0) { seg.cnt[at] = (uint32_t)c; seg.off[at] = (uint32_t)base; }
 }
 
 // ctl_tails: the scores are a part of a larger set whose rest is summarised
 // in ctl as tails (aL, S_L below; aR, S_R and the count c_R above)
-// one workgroup of 1024 threads: a thread per segment (two or three past
-// 4M scores) and four scores per thread in the root segment
-constexpr int kCurveRootThreads = 1024;
+// one workgroup of kCurveRootThreads: a thread per segment (several past 4M
+// scores, stored in seg_slot order) and four scores per thread in the root
+// segment
 
 __global__ __launch_bounds__(kCurveRootThreads) void k_curve_root(const uint32_t* __restrict__ keys, long long n,
                                                                    int ntiles, Ctl* ctl, SegArrays seg,
