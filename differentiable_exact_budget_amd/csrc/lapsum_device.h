@@ -28,6 +28,9 @@ constexpr int kHistGlobalWords = kHistGlobalCopies * 1024 + 1;  // the copies, t
 constexpr int kCurveThreads = 256;
 constexpr int kCurveTile = kRadixTile;   // sorted keys per curve segment
 constexpr int kCurveRootThreads = 1024;  // the full-sort root's workgroup
+constexpr int kSplitThreads = 512;       // split radix passes: threads per workgroup (>= 256)
+constexpr int kSplitItems = 8;           // split radix passes: keys per thread
+constexpr int kSplitTileKeys = kSplitThreads * kSplitItems;
 constexpr int kSampleMax = 40960;        // sample size cap (select holds it in registers)
 constexpr int kSelectThreads = 1024;
 constexpr int kSelectItems = kSampleMax / kSelectThreads;  // 40

@@ -21,7 +21,6 @@ namespace lapsum {
 namespace {
 
 constexpr long long kNoAllocMaxN = 1LL << 20;  // scores per call
-constexpr int kSplitTileKeys = 2048;            // keys per tile of the split radix passes
 
 constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 

@@ -711,11 +711,15 @@ LS_DEV long long xcd_tile(long long T) {
 }
 inline unsigned xcd_grid(long long T) { return (unsigned)(kXcds * ((T + kXcds - 1) / kXcds)); }
 
-constexpr int kSplitItems = 8;  // keys per thread of the split passes (measured on gfx950
-                                // at 10^7 keys: 2048-key tiles beat 1024 and 4096)
-constexpr int kSplitTile = kRadixThreads * kSplitItems;
+// kSplitThreads, kSplitItems: measured on gfx950 at 10^7 and 10^8 keys,
+// 512 threads x 8 keys (4096-key tiles) beat 256 x 8 (313 against 293 us at
+// 10^7, 2664 against 2524 us at 10^8), 256 x 16, 384 x 8, 512 x 4, 6 and 12,
+// 768 x 8 and 1024 x 4 and 8.
+constexpr int kSplitTile = kSplitTileKeys;
+static_assert(kSplitTile == kSplitThreads * kSplitItems, "tile = threads x keys per thread");
+static_assert(kSplitThreads >= 256 && kSplitThreads % 64 == 0, "a thread per digit, whole waves");
 
-__global__ __launch_bounds__(kRadixThreads) void k_radix_count(const uint32_t* __restrict__ in, int in_is_float,
+__global__ __launch_bounds__(kSplitThreads) void k_radix_count(const uint32_t* __restrict__ in, int in_is_float,
                                                                 long long n, int pass, uint32_t* __restrict__ counts,
                                                                 long long T) {
     __shared__ uint32_t cnt[kHistCopies * 256];
@@ -724,8 +728,7 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_count(const uint32_t* _
     const long long tile = xcd_tile(T);
     if (tile >= T) return;
     const long long base = tile * kSplitTile;
-#pragma unroll
-    for (int q = 0; q < kHistCopies; ++q) cnt[q * 256 + tid] = 0u;  // kRadixThreads == 256
+    for (int e = tid; e < kHistCopies * 256; e += kSplitThreads) cnt[e] = 0u;
     __syncthreads();
     uint32_t kr[kSplitItems];
 #pragma unroll
@@ -742,10 +745,12 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_count(const uint32_t* _
         if (idx < n) atomicAdd(&cl[(kr[i] >> shift) & 0xFFu], 1u);
     }
     __syncthreads();
-    uint32_t c = 0u;
+    if (tid < 256) {  // thread = digit
+        uint32_t c = 0u;
 #pragma unroll
-    for (int q = 0; q < kHistCopies; ++q) c += cnt[q * 256 + tid];
-    counts[(size_t)tid * (size_t)T + (size_t)tile] = c;  // thread = digit
+        for (int q = 0; q < kHistCopies; ++q) c += cnt[q * 256 + tid];
+        counts[(size_t)tid * (size_t)T + (size_t)tile] = c;
+    }
 }
 
 // one workgroup per digit: exclusive scan of its counts over the tiles
@@ -779,10 +784,10 @@ __global__ __launch_bounds__(1024) void k_radix_scan(const uint32_t* __restrict_
     }
 }
 
-__global__ __launch_bounds__(kRadixThreads) void k_radix_scatter(const uint32_t* __restrict__ in, int in_is_float,
+__global__ __launch_bounds__(kSplitThreads) void k_radix_scatter(const uint32_t* __restrict__ in, int in_is_float,
                                                                   uint32_t* __restrict__ out, long long n, int pass,
                                                                   const uint32_t* __restrict__ tile_base, long long T) {
-    constexpr int NW = kRadixThreads / 64;
+    constexpr int NW = kSplitThreads / 64;
     __shared__ uint32_t cnt[256 * NW];
     __shared__ uint32_t stage[kSplitTile];
     __shared__ uint32_t loc[256];
@@ -793,8 +798,8 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_scatter(const uint32_t*
     const long long tile = xcd_tile(T);
     if (tile >= T) return;
     const long long base = tile * kSplitTile;
-    for (int e = tid; e < 256 * NW; e += kRadixThreads) cnt[e] = 0u;
-    gbase[tid] = tile_base[(size_t)tid * (size_t)T + (size_t)tile];
+    for (int e = tid; e < 256 * NW; e += kSplitThreads) cnt[e] = 0u;
+    if (tid < 256) gbase[tid] = tile_base[(size_t)tid * (size_t)T + (size_t)tile];
     __syncthreads();
     uint32_t kr[kSplitItems];
     uint32_t rk[kSplitItems];
@@ -819,12 +824,15 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_scatter(const uint32_t*
         }
     }
     __syncthreads();
-    // thread d: per-wave exclusive offsets and the tile's exclusive digit offsets
-    const int d = tid;  // kRadixThreads == 256
+    // thread d < 256: per-wave exclusive offsets and the tile's exclusive
+    // digit offsets
     uint32_t tot = 0u;
+    if (tid < 256) {
 #pragma unroll
-    for (int q = 0; q < NW; ++q) { const uint32_t x = cnt[d * NW + q]; cnt[d * NW + q] = tot; tot += x; }
-    loc[d] = block_exclusive_scan<kRadixThreads>(tot, nullptr, scr);
+        for (int q = 0; q < NW; ++q) { const uint32_t x = cnt[tid * NW + q]; cnt[tid * NW + q] = tot; tot += x; }
+    }
+    const uint32_t ex = block_exclusive_scan<kSplitThreads>(tot, nullptr, scr);
+    if (tid < 256) loc[tid] = ex;
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < kSplitItems; ++i) {
@@ -837,7 +845,7 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_scatter(const uint32_t*
     __syncthreads();
     const long long rem = n - base;
     const int tcount = rem < kSplitTile ? (int)rem : kSplitTile;
-    for (int j = tid; j < tcount; j += kRadixThreads) {
+    for (int j = tid; j < tcount; j += kSplitThreads) {
         const uint32_t key = stage[j];
         const uint32_t dd = (key >> shift) & 0xFFu;
         out[(size_t)gbase[dd] + (size_t)(j - (int)loc[dd])] = key;
@@ -976,10 +984,10 @@ void launch_radix_sort(const float* r, long long n, uint32_t* keysA, uint32_t* k
             hipLaunchKernelGGL(k_radix_pass, dim3((unsigned)T), dim3(kPassThreads), 0, s, src, is_float, dst, n, p,
                                status, epoch_base + (uint32_t)p, goff, ctl);
         } else {
-            hipLaunchKernelGGL(k_radix_count, dim3(xcd_grid(T)), dim3(kRadixThreads), 0, s, src, is_float, n, p,
+            hipLaunchKernelGGL(k_radix_count, dim3(xcd_grid(T)), dim3(kSplitThreads), 0, s, src, is_float, n, p,
                                counts, T);
             hipLaunchKernelGGL(k_radix_scan, dim3(256), dim3(1024), 0, s, counts, T, p, goff, tile_base);
-            hipLaunchKernelGGL(k_radix_scatter, dim3(xcd_grid(T)), dim3(kRadixThreads), 0, s, src, is_float, dst, n,
+            hipLaunchKernelGGL(k_radix_scatter, dim3(xcd_grid(T)), dim3(kSplitThreads), 0, s, src, is_float, dst, n,
                                p, tile_base, T);
         }
         src = dst;

@@ -1,8 +1,8 @@
 """GPU parity at the full sizes of the bracketing workloads.
 
 Workloads: C3 (10^7 Student-t), C4 (10^8 mixture), and C5 (10^7 with a
-cluster of 10^5 tied scores at the quantile), C5 also forced onto the
-full-sort fallback.  Each runs in the launch configuration bench.py times:
+cluster of 10^5 tied scores at the quantile); C5 and C4 also forced onto the
+full-sort fallback, and C4 with the certification as a pass of its own.  Each runs in the launch configuration bench.py times:
 default options, inputs resident on the device, one stream.
 
 The oracle solves each whole input in fp64 in a few seconds on the host's
@@ -21,15 +21,21 @@ pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 L = pytest.importorskip("differentiable_exact_budget_amd")
 
-CASES = [("C3", None), ("C4", None), ("C5", None), ("C5", "fallback"), ("C4", "fallback")]
+CASES = [("C3", None), ("C4", None), ("C5", None), ("C5", "fallback"), ("C4", "fallback"), ("C4", "cert")]
 
 
-@pytest.mark.parametrize("name,mode", CASES, ids=["C3", "C4", "C5", "C5-forced-fallback", "C4-forced-fallback"])
+@pytest.mark.parametrize("name,mode", CASES,
+                         ids=["C3", "C4", "C5", "C5-forced-fallback", "C4-forced-fallback", "C4-certification-pass"])
 def test_full_size(oracle_mod, name, mode):
     print(f"\nfull-size {name} {mode or 'auto'}", flush=True)
     r, g, cfg = workloads.config_inputs(name)
     rd, gd = to_dev(r), to_dev(g)
-    opts = L.default_options(path=L.PATH_FORCE_FALLBACK) if mode == "fallback" else None
+    if mode == "fallback":
+        opts = L.default_options(path=L.PATH_FORCE_FALLBACK)
+    elif mode == "cert":
+        opts = L.default_options(cert_mode=1)
+    else:
+        opts = None
     p, b, st = L.forward(rd, cfg.k, cfg.t, options=opts, stats=True)
     grad = L.vjp(rd, gd, cfg.t, b)
     torch.cuda.synchronize()
@@ -42,7 +48,7 @@ def test_full_size(oracle_mod, name, mode):
         assert st["path_taken"] == 3
     else:
         assert st["path_taken"] in (2, 3)
-    if name == "C4" and mode is None:
+    if name == "C4" and mode in (None, "cert"):
         assert st["path_taken"] == 2 and st["certified"] == 1 and st["band_size"] > 0
 
     b_ref = check_forward(oracle_mod, r, cfg.k, cfg.t, p_h, b_h, label=name)
@@ -57,6 +63,9 @@ def test_full_size(oracle_mod, name, mode):
         if np.isfinite(st["a_R"]):
             assert abs(st["g_aR"] - ref["G_aR"]) <= 1e-6 * max(ref["G_aR"], 1.0)
             assert ref["G_aR"] < cfg.k
+        if mode == "cert":  # the direct pass's sums against the oracle's
+            assert abs(st["g_aL_direct"] - ref["G_aL"]) <= 1e-6 * ref["G_aL"]
+            assert abs(st["g_aR_direct"] - ref["G_aR"]) <= 1e-6 * max(ref["G_aR"], 1.0)
 
 
 def test_full_size_order_statistics(oracle_mod):
