@@ -512,10 +512,11 @@ LS_DEV SegCarries block_seg_carries(uint32_t c, float f, float l, double P, doub
 LS_DEV int seg_slot(int s, int per, int nt) { return (s % per) * nt + s / per; }
 
 // Runs on all NT threads of one workgroup; result valid in thread 0.
-// Memory round trips are kept to a handful: each lane of wave 0 fetches its
-// segments' aggregates in one batch, the root segment's scores are read
-// once, and the root is taken by the thread that owns j* with its
-// neighbour's values exchanged through LDS.
+// Memory round trips are kept to a handful: each thread fetches its
+// segments' aggregates with PB loads in flight (in seg_slot order, so the
+// workgroup's loads coalesce), the root segment's scores are read once, and
+// the root is taken by the thread that owns j* with its neighbour's values
+// exchanged through LDS.
 template <int NT, int EMAX>
 __device__ __attribute__((always_inline)) SolveOut segment_solve(const SegView sv, const Tails tl, const SolveScratch sc,
                                   float* s_k, double* s_v, int* s_int) {

@@ -58,6 +58,54 @@ void launch_sample(const float* r, long long n, double t, unsigned long long see
 // the sorted window.  If the window check fails (or the window is too wide)
 // an 8-bit MSD radix select finds x_(l) and x_(h) instead.
 // ---------------------------------------------------------------------------
+// The keys of two ranks (0-based, ascending) among the keys the NT threads
+// hold, at most one each (has), by MSD radix select over 8-bit digits: per
+// digit, a histogram of the keys that share each target's prefix so far (LDS
+// adds into four copies picked by lane), then one wave per target finds the
+// digit holding its rank.  want[q] = false skips target q.  The result is in
+// every thread.  h: 2 * 4 * 256 words; st: 4 words.
+template <int NT>
+LS_DEV void block_select2(uint32_t key, bool has, const uint32_t rank[2], const bool want[2], uint32_t out[2],
+                          uint32_t* h, uint32_t* st) {
+    const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
+    if (tid < 2) { st[tid] = 0u; st[2 + tid] = rank[tid]; }  // prefix, rank left inside it
+    for (int pass = 3; pass >= 0; --pass) {
+        const int shift = 8 * pass;
+        const uint32_t hmask = pass == 3 ? 0u : (0xFFFFFFFFu << (shift + 8));
+        for (int e = tid; e < 2 * 4 * 256; e += NT) h[e] = 0u;
+        __syncthreads();
+        const uint32_t d = (key >> shift) & 0xFFu;
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            if (want[q] && has && (key & hmask) == (st[q] & hmask)) atomicAdd(&h[(q * 4 + (lane & 3)) * 256 + d], 1u);
+        __syncthreads();
+        if (wv < 2 && want[wv]) {  // wave q: lane l sums digits 4l .. 4l + 3
+            const int q = wv;
+            uint32_t c[4], sum = 0u;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int dd = 4 * lane + j;
+                c[j] = h[(q * 4 + 0) * 256 + dd] + h[(q * 4 + 1) * 256 + dd] + h[(q * 4 + 2) * 256 + dd] +
+                       h[(q * 4 + 3) * 256 + dd];
+                sum += c[j];
+            }
+            const uint32_t inc = wave_inclusive_scan(sum);
+            const uint32_t rem = st[2 + q];
+            uint32_t below = inc - sum;
+            if (below <= rem && rem < inc) {  // the one lane holding the rank
+                int j = 0;
+                while (j < 3 && below + c[j] <= rem) below += c[j++];
+                st[q] |= (uint32_t)(4 * lane + j) << shift;
+                st[2 + q] = rem - below;
+            }
+        }
+        __syncthreads();
+    }
+    out[0] = st[0];
+    out[1] = st[1];
+    __syncthreads();
+}
+
 constexpr int kWinMax = 4096;
 constexpr int kSubMax = 1024;  // measured on gfx950: 1024 beats 2048 (C3, C4) and 512 (C4)
 
@@ -69,6 +117,8 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(const float* __restri
     __shared__ uint32_t win[kWinMax];
     __shared__ uint32_t scr[kSelectThreads / 64 + 2];
     __shared__ uint32_t s_pre[2], s_rem[2];
+    __shared__ uint32_t s_selh[2 * 4 * 256];  // the subsample's radix select
+    __shared__ uint32_t s_selst[4];
     const int tid = threadIdx.x;
     // the sample, 16 bytes per load where it can (thread tid holds elements
     // i * kSelectThreads + tid)
@@ -113,24 +163,25 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(const float* __restri
     // The sample values are independent draws, so any fixed subset of them is
     // a random subsample: thread i contributes its first key (sample value
     // 4i, already in its registers), for the first kSubMax threads.
+    // The window ends are two order statistics of the subsample, found by a
+    // radix select (two ranks need no full sort).
     static_assert(kSubMax <= kSelectThreads, "one subsample key per thread");
     const int msub = (s + 3) / 4 < kSubMax ? (s + 3) / 4 : kSubMax;
-    if (tid < kSubMax) sub[tid] = tid < msub ? kr[0] : 0xFFFFFFFFu;
-    __syncthreads();
-    sort_pow2_lds<kSelectThreads>(sub, kSubMax);
-    // every thread reads the window ends off the sorted subsample (the sort
-    // ends with a barrier)
-    uint32_t wlo = 0u, whi = 0xFFFFFFFFu;
+    long long r0 = -1, r1 = msub;
     if (want_l) {
         const double pl = (double)l / (double)s;
-        const long long r0 = (long long)floor((double)msub * pl - 5.0 * sqrt((double)msub * pl * (1.0 - pl)) - 3.0);
-        wlo = r0 < 0 ? 0u : sub[r0];
+        r0 = (long long)floor((double)msub * pl - 5.0 * sqrt((double)msub * pl * (1.0 - pl)) - 3.0);
     }
     if (want_h) {
         const double ph = (double)h / (double)s;
-        const long long r1 = (long long)ceil((double)msub * ph + 5.0 * sqrt((double)msub * ph * (1.0 - ph)) + 3.0);
-        whi = r1 >= msub ? 0xFFFFFFFFu : sub[r1];
+        r1 = (long long)ceil((double)msub * ph + 5.0 * sqrt((double)msub * ph * (1.0 - ph)) + 3.0);
     }
+    const bool sel[2] = {r0 >= 0 && r0 < msub, r1 >= 0 && r1 < msub};
+    const uint32_t rk2[2] = {sel[0] ? (uint32_t)r0 : 0u, sel[1] ? (uint32_t)r1 : 0u};
+    uint32_t wend[2];
+    block_select2<kSelectThreads>(kr[0], tid < msub, rk2, sel, wend, s_selh, s_selst);
+    const uint32_t wlo = r0 < 0 ? 0u : (sel[0] ? wend[0] : 0xFFFFFFFFu);
+    const uint32_t whi = r1 >= msub ? 0xFFFFFFFFu : wend[1];
     uint32_t nbelow = 0u, nin = 0u;
 #pragma unroll
     for (int i = 0; i < kSelectItems; ++i) {

@@ -705,6 +705,16 @@ int launch_probs(const float* r, long long n, double t, float* p, Ctl* ctl, doub
 // their sums with their reference; k_vjp_c brings them to the smallest one.
 constexpr double kVjpSlack = 16.0;
 
+// e^x for x <= 0 in the frame changes of the VJP sums: y = x log2(e) =
+// i + f with i an integer, formed as 2^f (the hardware exp2, of fp32
+// accuracy like the terms it scales) times 2^i (exact); 0 below fp64's range
+LS_DEV double frame_factor(double x) {
+    const double y = x * 1.4426950408889634;
+    if (!(y > -1100.0)) return 0.0;
+    const double yi = floor(y);
+    return ldexp((double)__builtin_amdgcn_exp2f((float)(y - yi)), (int)yi);
+}
+
 template <bool KT>
 struct VjpAcc {
     double m = INFINITY;  // reference (a units); +inf until the lane's first score
@@ -713,12 +723,7 @@ struct VjpAcc {
     // formed as 2^i * 2^f from y = (a_new - m) log2(e) = i + f (the fraction
     // by the hardware exp2, the integer part exact)
     LS_DEV void lower(double a_new) {
-        const double y = (a_new - m) * 1.4426950408889634;
-        double s = 0.0;  // while m = +inf (the sums are 0 then), or far below fp64
-        if (y > -1100.0) {
-            const double yi = floor(y);
-            s = ldexp((double)__builtin_amdgcn_exp2f((float)(y - yi)), (int)yi);
-        }
+        const double s = frame_factor(a_new - m);  // 0 while m = +inf (the sums are 0 then)
         sfg *= s; sf *= s;
         if (KT) { sfgd *= s; sfd *= s; }
         m = a_new;
@@ -831,7 +836,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_vjp_reduce(const float* __re
     }
     // the workgroup's reference M, then every lane's sums brought to it
     const double M = block_min_nonneg_f64<kStreamThreads>(acc.m, s_mn);
-    const double sc = acc.m == M ? 1.0 : exp(M - acc.m);  // M <= m; 0 for a lane that met no score
+    const double sc = acc.m == M ? 1.0 : frame_factor(M - acc.m);  // M <= m; 0 for a lane that met no score
     constexpr int NP = KT ? 4 : 2;
     double d[NP];
     d[0] = acc.sfg * sc;
@@ -882,7 +887,7 @@ __global__ __launch_bounds__(1024) void k_vjp_c(const double* part, int nparts, 
     for (int x = 0; x < NP; ++x) d[x] = 0.0;
 #pragma unroll
     for (int q = 0; q < B; ++q) {
-        const double sc = v[q][NP] == M ? 1.0 : exp(M - v[q][NP]);
+        const double sc = v[q][NP] == M ? 1.0 : frame_factor(M - v[q][NP]);
 #pragma unroll
         for (int x = 0; x < NP; ++x) d[x] += v[q][x] * sc;
     }
