@@ -59,7 +59,7 @@ __global__ __launch_bounds__(NT) void k_rows_forward(const float* __restrict__ r
     __syncthreads();
     // the whole sorted array as one segment, no aggregates: the solve tests G
     // at every score
-    SegView sv{1, nullptr, nullptr, nullptr, nullptr, &sg_cnt, &sg_off, keys, nullptr, nullptr, nullptr, nullptr};
+    SegView sv{1, nullptr, nullptr, nullptr, nullptr, &sg_cnt, &sg_off, keys, nullptr};
     SolveScratch sc{&sc_pk, &sc_pv, &sc_bk, &sc_bv, &sc_bfx, &sc_rank, nullptr, nullptr};
     Tails tl{-INFINITY, INFINITY, 0.0, 0.0, (double)n, 0.0, k, t, inv_t, -INFINITY, INFINITY};
     const SolveOut o = segment_solve<NT, ITEMS>(sv, tl, sc, s_k, s_v, s_int);
@@ -285,7 +285,7 @@ __global__ __launch_bounds__(kLongNT) void k_rows_forward_long(const float* __re
             if (tid == 0) { sg_cnt[sgi] = (uint32_t)c; sg_off[sgi] = (uint32_t)(sgi * kLongChunk); }
         }
         __syncthreads();
-        SegView sv{nseg, sg_first, sg_last, sg_P, sg_Bx, sg_cnt, sg_off, sorted, nullptr, nullptr, nullptr, nullptr};
+        SegView sv{nseg, sg_first, sg_last, sg_P, sg_Bx, sg_cnt, sg_off, sorted, nullptr};
         SolveScratch sc{sc_pk, sc_pv, sc_bk, sc_bv, sc_bfx, sc_rank, nullptr, nullptr};
         Tails tl{-INFINITY, INFINITY, 0.0, 0.0, (double)n, 0.0, k, t, inv_t, key2f(sorted[0]), key2f(sorted[n - 1])};
         const SolveOut o = segment_solve<NT, kLongItems>(sv, tl, sc, s_k, s_v, s_int);

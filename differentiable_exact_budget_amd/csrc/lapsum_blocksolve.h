@@ -251,13 +251,6 @@ struct SegView {
     const uint32_t* cnt;   // scores in the segment (0 = empty)
     const uint32_t* off;   // offset of the segment's keys in `keys`
     const uint32_t* keys;  // sorted order-preserving keys (global or LDS)
-    // optional local curves (indexed like keys): with ref = the segment's
-    // first score and u_j = e^{(v_j - ref)/t}, eU_j = sum_{i<=j} u_i and
-    // eW_j = sum_{i>j} 1/u_i inside the segment; `wide` marks segments whose
-    // span exceeds 600 t (no local curve: computed in the solve instead)
-    const double* eU;
-    const double* eW;
-    const uint8_t* wide;
     // when set, segments hold raw (unsorted) fp32 bit patterns and the root
     // segment is sorted into this LDS buffer (capacity kBucketCapMax)
     uint32_t* sortbuf;
@@ -752,22 +745,14 @@ __device__ __attribute__((always_inline)) SolveOut segment_solve(const SegView s
             const float pk0 = s_ck[0]; const double pv0 = s_cv[0];
             const float bk0 = s_ck[1]; const double bv0 = s_cv[1];
             double Pj[EMX], Bj[EMX];
-            const bool have_local = sv.eU != nullptr && !sv.wide[sstar];
-            if (have_local || ((double)vlast - (double)vfirst) * inv_t <= 600.0) {
+            if (((double)vlast - (double)vfirst) * inv_t <= 600.0) {
                 // additive form relative to ref = v_first: u_j = e^{(v_j - ref)/t} in [1, e^600]
                 //   P_j = (carry_P + sum_{i<=j} u_i) / u_j,  B_j = u_j (carry_B + sum_{i>j} 1/u_i)
                 const double ref = (double)vfirst;
                 double u[EMX], Ul[EMX], Wl[EMX];
     #pragma unroll
                 for (int q = 0; q < EMX; ++q) u[q] = (e0 + q < e1) ? ecoef(((double)vv[q] - ref) * inv_t) : 1.0;
-                if (have_local) {
-    #pragma unroll
-                    for (int q = 0; q < EMX; ++q) {
-                        const int j = e0 + q;
-                        Ul[q] = j < e1 ? sv.eU[offS + j] : 0.0;
-                        Wl[q] = j < e1 ? sv.eW[offS + j] : 0.0;
-                    }
-                } else {
+                {
                     double ut = 0.0, wt = 0.0;
     #pragma unroll
                     for (int q = 0; q < EMX; ++q)

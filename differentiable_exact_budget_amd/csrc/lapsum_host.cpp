@@ -93,7 +93,7 @@ long long tiles_for(long long n) { return (n + kRadixTile - 1) / kRadixTile; }
 
 // layout of one workspace for forwards up to n_cap scores
 struct Layout {
-    size_t ctl, part, sample, sample_idx, sp, iw, bcnt, bvals, hoff, hfill, hmin, hmax, hch0, hpart, eU, eW, wide,
+    size_t ctl, part, sample, sample_idx, sp, iw, bcnt, bvals, hoff, hfill, hmin, hmax, hch0, hpart,
         seg_first, seg_last, seg_P, seg_Bx, seg_cnt, seg_off,
         sc_pk, sc_pv, sc_bk, sc_bv, sc_bfx, sc_rank, sc_eP, sc_eB, keysA, keysB, hist, goff, status, total;
     size_t status_bytes;
@@ -125,7 +125,6 @@ Layout make_layout(long long n_cap) {
     // partial chunk per bucket
     L.hpart = take(sizeof(unsigned long long) * 4 *
                    (size_t)(std::max<long long>(n_cap, 1) / kHeavyChunk + kMaxBuckets + 1));
-    L.eU = 0; L.eW = 0; L.wide = 0;
     L.seg_first = take(sizeof(float) * nseg);
     L.seg_last = take(sizeof(float) * nseg);
     L.seg_P = take(sizeof(double) * nseg);

@@ -182,11 +182,17 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(const float* __restri
     block_select2<kSelectThreads>(kr[0], tid < msub, rk2, sel, wend, s_selh, s_selst);
     const uint32_t wlo = r0 < 0 ? 0u : (sel[0] ? wend[0] : 0xFFFFFFFFu);
     const uint32_t whi = r1 >= msub ? 0xFFFFFFFFu : wend[1];
+    // Per key: below the window, or inside it (wlo <= k <= whi as one
+    // unsigned compare).  Groups of four keys past the sample's end are
+    // skipped, and only the group that straddles it tests vmask (uniform).
+    const uint32_t wspan = whi - wlo;
     uint32_t nbelow = 0u, nin = 0u;
 #pragma unroll
     for (int i = 0; i < kSelectItems; ++i) {
-        if ((i & 3) == 0 && (i / 4) * 4 * kSelectThreads >= s) break;  // past the sample's end (uniform)
-        if ((vmask >> i) & 1ull) { nbelow += kr[i] < wlo; nin += (kr[i] >= wlo && kr[i] <= whi); }
+        if ((i & 3) == 0 && (i / 4) * 4 * kSelectThreads >= s) break;
+        const bool v = (i / 4 + 1) * 4 * kSelectThreads <= s || ((vmask >> i) & 1ull);
+        nbelow += (v && kr[i] < wlo) ? 1u : 0u;
+        nin += (v && kr[i] - wlo <= wspan) ? 1u : 0u;
     }
     // one scan of both counts packed in a word (each total <= kSampleMax <
     // 2^16): the low half gives each thread its slot in the window, and every
@@ -207,7 +213,8 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(const float* __restri
 #pragma unroll
         for (int i = 0; i < kSelectItems; ++i) {
             if ((i & 3) == 0 && (i / 4) * 4 * kSelectThreads >= s) break;
-            if (((vmask >> i) & 1ull) && kr[i] >= wlo && kr[i] <= whi) win[pos++] = kr[i];
+            const bool v = (i / 4 + 1) * 4 * kSelectThreads <= s || ((vmask >> i) & 1ull);
+            if (v && kr[i] - wlo <= wspan) win[pos++] = kr[i];
         }
         const int wp = max(next_pow2((int)W), 64);
         for (int e = (int)W + tid; e < wp; e += kSelectThreads) win[e] = 0xFFFFFFFFu;

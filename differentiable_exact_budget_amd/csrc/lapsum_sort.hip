@@ -68,7 +68,7 @@ __global__ __launch_bounds__(kSortThreads) void k_small_solve(const float* __res
     __syncthreads();
     // the whole sorted array as one segment, no aggregates: the solve tests G
     // at every score
-    SegView sv{1, nullptr, nullptr, nullptr, nullptr, &sg_cnt, &sg_off, keys, nullptr, nullptr, nullptr, nullptr};
+    SegView sv{1, nullptr, nullptr, nullptr, nullptr, &sg_cnt, &sg_off, keys, nullptr};
     Tails tl{-INFINITY, INFINITY, 0.0, 0.0, (double)n, 0.0, k, t, inv_t, -INFINITY, INFINITY};
     SolveOut o = segment_solve<kSortThreads, kSortItems>(sv, tl, sc, s_k, s_v, s_int);
     if (tid == 0) {
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(kSortThreads) void k_band_root(const uint32_t* buck
     __shared__ float s_k[kSortThreads];
     __shared__ double s_v[kSortThreads];
     __shared__ int s_int[32];
-    SegView sv{nb, seg.first, seg.last, seg.P, seg.Bx, seg.cnt, seg.off, bucket_vals, nullptr, nullptr, nullptr, sortbuf};
+    SegView sv{nb, seg.first, seg.last, seg.P, seg.Bx, seg.cnt, seg.off, bucket_vals, sortbuf};
     Tails tl{ctl->aL, ctl->aR, ctl->S_L, ctl->S_R, (double)ctl->m, (double)ctl->c_R, k, t, inv_t, ctl->aL, ctl->aR};
     SolveOut o = segment_solve<kSortThreads, kSortItems>(sv, tl, sc, s_k, s_v, s_int);
     if (threadIdx.x == 0) {
@@ -882,7 +882,7 @@ __global__ __launch_bounds__(kCurveRootThreads) void k_curve_root(const uint32_t
     __shared__ float s_k[kCurveRootThreads];
     __shared__ double s_v[kCurveRootThreads];
     __shared__ int s_int[32];
-    SegView sv{ntiles, seg.first, seg.last, seg.P, seg.Bx, seg.cnt, seg.off, keys, nullptr, nullptr, nullptr, nullptr};
+    SegView sv{ntiles, seg.first, seg.last, seg.P, seg.Bx, seg.cnt, seg.off, keys, nullptr};
     // the sorted scores run from keys[0] to keys[n - 1]
     Tails tl{-INFINITY, INFINITY, 0.0, 0.0, (double)n, 0.0, k, t, inv_t, key2f(keys[0]), key2f(keys[n - 1])};
     if (ctl_tails) {

@@ -845,10 +845,10 @@ __global__ __launch_bounds__(kStreamThreads) void k_vjp_reduce(const float* __re
     unsigned long long u0[1] = {0ull};
     uint32_t m0[1] = {0u};
     block_reduce_multi<kStreamThreads>(d, u0, m0, s_rd, s_ru, s_rm);
-    if (tid == 0) {
+    if (tid == 0) {  // quantity-major (part[q * kReduceGrid + workgroup]): k_vjp_c's loads coalesce
 #pragma unroll
-        for (int q = 0; q < NP; ++q) part[(NP + 1) * blockIdx.x + q] = d[q];
-        part[(NP + 1) * blockIdx.x + NP] = M;
+        for (int q = 0; q < NP; ++q) part[(size_t)q * kReduceGrid + blockIdx.x] = d[q];
+        part[(size_t)NP * kReduceGrid + blockIdx.x] = M;
     }
 }
 
@@ -876,7 +876,7 @@ __global__ __launch_bounds__(1024) void k_vjp_c(const double* part, int nparts, 
     for (int q = 0; q < B; ++q) {
         const int i = (int)threadIdx.x + q * NT;
 #pragma unroll
-        for (int x = 0; x <= NP; ++x) v[q][x] = i < nparts ? part[(size_t)i * (NP + 1) + x] : (x == NP ? INFINITY : 0.0);
+        for (int x = 0; x <= NP; ++x) v[q][x] = i < nparts ? part[(size_t)x * kReduceGrid + i] : (x == NP ? INFINITY : 0.0);
     }
     double mt = INFINITY;
 #pragma unroll
