@@ -502,7 +502,7 @@ LS_DEV SegCarries block_seg_carries(uint32_t c, float f, float l, double P, doub
 // addresses, every lane of a load touched a different cache line).  The
 // identity when per == 1.  Every writer of segment aggregates for a solve
 // with more segments than threads uses the same slots.
-LS_DEV int seg_slot(int s, int per, int nt) { return (s % per) * nt + s / per; }
+LS_DEV int seg_slot(int s, int per, int nt) { return per == 1 ? s : (s % per) * nt + s / per; }
 
 // Runs on all NT threads of one workgroup; result valid in thread 0.
 // Memory round trips are kept to a handful: each thread fetches its
