@@ -13,7 +13,7 @@
 namespace lapsum {
 
 // The collect pass walks r like the filter: one 1024-thread workgroup per CU
-// over a fixed share, its waves taking 1024-score tiles at run time (the
+// over a fixed share, its waves taking 512-score tiles at run time (the
 // misaligned fallback strides over r with the same workgroups)
 constexpr int kHeavyThreads = 1024;
 constexpr int kHeavyQueuePerWave = 512;
