@@ -8,10 +8,14 @@
 //            b is the (1 - k/n) quantile of x whatever the scores are.
 //            Random numbers: Philox4x32-10 (Salmon et al., SC'11), counter
 //            (j_lo, j_hi, 0, 0), key (seed_lo, seed_hi).
-//  k_select  one workgroup: a_L = x_(l), a_R = x_(h) by 8-bit MSD radix
-//            select, then up to 1024 value-ordered buckets for the band:
-//            sample values between a_L and a_R as gap splitters, each finite
-//            gap cut into J equal-width sub-buckets.
+//  k_select  one workgroup: a_L = x_(l), a_R = x_(h), exactly: a window
+//            of sample ranks around l..h from two order statistics of a
+//            1024-key subsample (radix select), the sample keys inside it
+//            sorted and the two read off (an 8-bit MSD radix select over
+//            the whole sample when the window misses); then up to 1024
+//            value-ordered buckets for the band: sample values between a_L
+//            and a_R as gap splitters, each finite gap cut into J
+//            equal-width sub-buckets.
 #include "lapsum_launch.h"
 
 namespace lapsum {
@@ -51,10 +55,10 @@ void launch_sample(const float* r, long long n, double t, unsigned long long see
 
 // ---------------------------------------------------------------------------
 // select
-// Fast path: sort a subsample of 1024 sample keys, read off a rank window
-// that contains ranks l..h with a wide safety margin, count the sample keys
-// below the window and collect the ones inside it, and sort only those
-// (<= 4096).  The exact order statistics x_(l) .. x_(h) are then read from
+// Fast path: two order statistics of a subsample of 1024 sample keys give a
+// rank window that contains ranks l..h with a wide safety margin; count the
+// sample keys below the window, collect the ones inside it, and sort only
+// those (<= 4096).  The exact order statistics x_(l) .. x_(h) are then read from
 // the sorted window.  If the window check fails (or the window is too wide)
 // an 8-bit MSD radix select finds x_(l) and x_(h) instead.
 // ---------------------------------------------------------------------------
