@@ -892,7 +892,90 @@ __device__ __attribute__((always_inline)) SolveOut segment_solve(const SegView s
                 out.ok = (b == b) && (b > -INFINITY) && (b < INFINITY);
             }
         };
-        if ((int)cS <= NT) phase4(std::integral_constant<int, 1>{});
+        // A root segment of at most 64 scores: wave 0 alone, one score per
+        // lane, with the same arithmetic as phase4 at one score per thread
+        // (the cross-wave parts of its scans only add identities there) but
+        // no barrier; the other waves go on to the caller.
+        auto phase4_wave = [&]() {
+            if (tid >= 64) return;
+            const int l = tid;
+            const bool in = l < (int)cS;
+            const float vv = in ? key2f(rk[l]) : 0.0f;
+            const float vfirst = key2f(rk[0]);
+            const float vlast = key2f(rk[cS - 1]);
+            const float pk0 = s_ck[0]; const double pv0 = s_cv[0];
+            const float bk0 = s_ck[1]; const double bv0 = s_cv[1];
+            double Pj = 0.0, Bj = 0.0;
+            if (((double)vlast - (double)vfirst) * inv_t <= 600.0) {
+                const double ref = (double)vfirst;
+                const double u = in ? ecoef(((double)vv - ref) * inv_t) : 1.0;
+                const double U = wave_excl_from_incl(wave_scan_add_incl(in ? u : 0.0, false), false);
+                const double W = wave_excl_from_incl(wave_scan_add_incl(in ? 1.0 / u : 0.0, true), true);
+                const double pc = (pv0 != 0.0) ? pv0 * ecoef(((double)pk0 - ref) * inv_t) : 0.0;
+                const double bc = (bv0 != 0.0) ? bv0 * ecoef((ref - (double)bk0) * inv_t) : 0.0;
+                Pj = (pc + (U + u)) / u;
+                Bj = u * (bc + W);
+            } else {
+                float fk = in ? vv : -INFINITY;
+                double fv = in ? 1.0 : 0.0;
+                wave_scan_fwd_excl(fk, fv, inv_t);
+                {
+                    float pk = pk0; double pv = pv0;
+                    fwd_combine(pk, pv, fk, fv, inv_t);
+                }
+                if (in) Pj = 1.0 + (fv != 0.0 ? ecoef(((double)fk - (double)vv) * inv_t) * fv : 0.0);
+                float rk2 = in ? vv : INFINITY;
+                double rv2 = in ? 1.0 : 0.0;
+                wave_scan_bwd_excl(rk2, rv2, inv_t);
+                {
+                    float bk = bk0; double bvv = bv0;
+                    bwd_combine(rk2, rv2, bk, bvv, inv_t);
+                }
+                if (in) Bj = (rv2 != 0.0) ? ecoef(((double)vv - (double)rk2) * inv_t) * rv2 : 0.0;
+            }
+            int myj = -1;
+            if (in) {
+                const double G = 0.5 * Pj + (tl.m - 1.0 - (double)(rankS + (uint32_t)l)) + tl.c_R - 0.5 * Bj;
+                if (G >= tl.k) myj = l;
+            }
+            int jl = (int)wave_max_u32((uint32_t)(myj + 1)) - 1;
+            if (jl < 0 && !whole) jl = 0;  // the segment's first score passed in phase 3
+            const int js = jl < 0 ? 0 : jl, jn = min(js + 1, 63);
+            const double Pjs = __shfl(Pj, js, 64), vlo = (double)__shfl(vv, js, 64);
+            const double vnx = (double)__shfl(vv, jn, 64), Bnx = __shfl(Bj, jn, 64);
+            if (tid == 0 && jl < 0) {
+                // whole array, G(v_first) < k: b lies below every score (as in phase4)
+                const double ref = (double)vfirst;
+                const double D = tl.m + tl.c_R - tl.k;
+                const double lnw = log_root(-INFINITY, log1p(Bj), D);
+                double b = ref + tl.t * lnw;
+                if (b > ref) b = ref;
+                out.jstar = -1;
+                out.b = b;
+                out.ok = (b == b) && (b > -INFINITY) && (b < INFINITY);
+            } else if (tid == 0) {
+                const double lo = vlo;
+                double lnA = log(Pjs), lnB, chi;
+                const double J = (double)(rankS + (uint32_t)jl);
+                const double D = (tl.m - 1.0 - J) + tl.c_R - tl.k;
+                out.jstar = (long long)(rankS + (uint32_t)jl);
+                if ((uint32_t)jl + 1u < cS) {
+                    chi = vnx; lnB = (lo - vnx) * inv_t + log1p(Bnx);
+                } else if (bv0 != 0.0) {
+                    chi = (double)bk0; lnB = (lo - (double)bk0) * inv_t + log(bv0);
+                } else {
+                    chi = tl.aR; lnB = -INFINITY;
+                }
+                const double lnw = log_root(lnA, lnB, D);
+                double b = lo + tl.t * lnw;
+                if (b < lo) b = lo;
+                if (b > chi) b = chi;
+                out.b = b;
+                out.ok = (b == b) && (b > -INFINITY) && (b < INFINITY);
+            }
+        };
+        if ((int)cS <= 64) phase4_wave();
+        else if ((int)cS <= NT) phase4(std::integral_constant<int, 1>{});
         else if constexpr (EMAX > 4) {
             if ((int)cS <= 4 * NT) phase4(std::integral_constant<int, 4>{});
             else phase4(std::integral_constant<int, EMAX>{});
