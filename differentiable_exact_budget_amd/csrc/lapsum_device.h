@@ -35,6 +35,10 @@ constexpr int kSampleMax = 40960;        // sample size cap (select holds it in 
 constexpr int kSelectThreads = 1024;
 constexpr int kSelectItems = kSampleMax / kSelectThreads;  // 40
 constexpr int kCandMax = 2048;           // sample values kept for the splitters
+constexpr int kSelHistShift = 20;        // sample histogram bin of a key: its leading 12 bits
+constexpr int kSelHistBins = 1 << (32 - kSelHistShift);  // 4096
+constexpr int kWinMax = 4096;            // sample keys the select sorts around ranks l..h
+constexpr int kWinHdr = 4;               // window buffer header: fill count, ok, size, keys below
 
 // control-block flags
 constexpr int kFlagNonFinite = 1;

@@ -66,6 +66,9 @@ struct Workspace {
     int probs_parts = 1;  // partials the last p pass left
     float* sample = nullptr;
     long long* sample_idx = nullptr;
+    uint32_t* shist = nullptr;  // two sample histograms (kSelHistBins words each), used in turn
+    uint32_t* swin = nullptr;   // the select's gathered window (kWinHdr + kWinMax words)
+    unsigned int shist_turn = 0;
     float* sp = nullptr;
     float* iw = nullptr;
     uint32_t* bucket_cnt = nullptr;
@@ -93,7 +96,7 @@ long long tiles_for(long long n) { return (n + kRadixTile - 1) / kRadixTile; }
 
 // layout of one workspace for forwards up to n_cap scores
 struct Layout {
-    size_t ctl, part, sample, sample_idx, sp, iw, bcnt, bvals, hoff, hfill, hmin, hmax, hch0, hpart,
+    size_t ctl, part, sample, sample_idx, shist, swin, sp, iw, bcnt, bvals, hoff, hfill, hmin, hmax, hch0, hpart,
         seg_first, seg_last, seg_P, seg_Bx, seg_cnt, seg_off,
         sc_pk, sc_pv, sc_bk, sc_bv, sc_bfx, sc_rank, sc_eP, sc_eB, keysA, keysB, hist, goff, status, total;
     size_t status_bytes;
@@ -112,6 +115,8 @@ Layout make_layout(long long n_cap) {
     L.part = take(sizeof(double) * 2 * (size_t)kMaxStreamParts);
     L.sample = take(sizeof(float) * kSampleMax);
     L.sample_idx = take(sizeof(long long) * kSampleMax);
+    L.shist = take(sizeof(uint32_t) * 2 * kSelHistBins);
+    L.swin = take(sizeof(uint32_t) * (kWinHdr + kWinMax));
     L.sp = take(sizeof(float) * (kMaxBuckets + 1));
     L.iw = take(sizeof(float) * kMaxBuckets);
     L.bcnt = take(sizeof(uint32_t) * kMaxBuckets);
@@ -179,6 +184,9 @@ lapsum_status_t alloc_ws(Workspace* w, long long n_cap) {
     w->part = reinterpret_cast<double*>(base + L.part);
     w->sample = reinterpret_cast<float*>(base + L.sample);
     w->sample_idx = reinterpret_cast<long long*>(base + L.sample_idx);
+    w->shist = reinterpret_cast<uint32_t*>(base + L.shist);
+    w->swin = reinterpret_cast<uint32_t*>(base + L.swin);
+    w->shist_turn = 0;
     w->sp = reinterpret_cast<float*>(base + L.sp);
     w->iw = reinterpret_cast<float*>(base + L.iw);
     w->bucket_cnt = reinterpret_cast<uint32_t*>(base + L.bcnt);
@@ -211,6 +219,10 @@ lapsum_status_t alloc_ws(Workspace* w, long long n_cap) {
     // the control block (tickets, counters) and the look-back words start at zero
     if (hipMemsetAsync(w->ctl, 0, sizeof(Ctl), w->stream) != hipSuccess) return LAPSUM_ERR_HIP;
     if (hipMemsetAsync(w->status, 0, w->status_bytes, w->stream) != hipSuccess) return LAPSUM_ERR_HIP;
+    // both sample histograms and the window header start at zero
+    if (hipMemsetAsync(w->shist, 0, sizeof(uint32_t) * 2 * kSelHistBins, w->stream) != hipSuccess)
+        return LAPSUM_ERR_HIP;
+    if (hipMemsetAsync(w->swin, 0, sizeof(uint32_t) * kWinHdr, w->stream) != hipSuccess) return LAPSUM_ERR_HIP;
     // the radix sort's global digit totals start (and are left) at zero
     if (hipMemsetAsync(w->hist_part, 0, sizeof(uint32_t) * kHistGlobalWords, w->stream) != hipSuccess)
         return LAPSUM_ERR_HIP;
@@ -374,6 +386,17 @@ void binomial_ranks(long long s, double q, double delta, long long* l_out, long 
 }
 
 lapsum_status_t hip_ok(hipError_t e) { return e == hipSuccess ? LAPSUM_OK : LAPSUM_ERR_HIP; }
+
+// The sample histogram a call builds: the two buffers are used in turn, and
+// the sampler clears the other one, so each call finds its own at zero
+// without a clearing launch of its own (the widenings of one call reuse it).
+uint32_t* next_sample_hist(Workspace* w) {
+    w->shist_turn ^= 1u;
+    return w->shist + (size_t)w->shist_turn * kSelHistBins;
+}
+uint32_t* other_sample_hist(Workspace* w, uint32_t* hist) {
+    return hist == w->shist ? w->shist + kSelHistBins : w->shist;
+}
 
 lapsum_status_t wait_summary(Workspace* w, hipStream_t st, unsigned int seq) {
     volatile unsigned int* flag = &w->hs->seq;
@@ -562,14 +585,15 @@ lapsum_status_t forward_locked(Workspace* w, const float* r, int64_t n, double k
     if (opt.margin_scale == 1.0) { l = l0; h = h0; }
     const int cap = opt.bucket_capacity;
 
+    uint32_t* shist = next_sample_hist(w);
     tm.begin("sample");
-    launch_sample(r, n, t, opt.seed, (int)s, w->sample, nullptr, st);
+    launch_sample(r, n, t, opt.seed, (int)s, w->sample, nullptr, st, shist, other_sample_hist(w, shist));
     tm.end();
     BracketResult br;
     int widen = 0;
     for (;;) {
         tm.begin("select");
-        launch_select(w->sample, (int)s, l, h, cap, w->ctl, w->sp, w->iw, w->bucket_cnt, st);
+        launch_select(w->sample, (int)s, l, h, cap, w->ctl, w->sp, w->iw, w->bucket_cnt, st, shist, w->swin);
         tm.end();
         const unsigned int seq = ++w->seq;
         tm.begin("filter");
@@ -765,12 +789,14 @@ lapsum_status_t order_stats_impl(Workspace* w, const float* r, long long n, long
         binomial_ranks(s, q, opt.delta, &l, &hh);
         const double c0 = (double)s * q;
         const int cap = opt.bucket_capacity;
+        uint32_t* shist = next_sample_hist(w);
         tm.begin("sample");
-        launch_sample(r, n, 0.0, opt.seed, (int)s, w->sample, nullptr, st);  // no noise: the scores themselves
+        // no noise: the scores themselves
+        launch_sample(r, n, 0.0, opt.seed, (int)s, w->sample, nullptr, st, shist, other_sample_hist(w, shist));
         tm.end();
         for (;;) {
             tm.begin("select");
-            launch_select(w->sample, (int)s, l, hh, cap, w->ctl, w->sp, w->iw, w->bucket_cnt, st);
+            launch_select(w->sample, (int)s, l, hh, cap, w->ctl, w->sp, w->iw, w->bucket_cnt, st, shist, w->swin);
             tm.end();
             const unsigned int seq = ++w->seq;
             tm.begin("filter");
@@ -1078,7 +1104,10 @@ lapsum_status_t lapsum_test_select(const float* x, int64_t s, int64_t l, int64_t
     lapsum_status_t gs = get_ws(st, 0, &wsg);
     if (gs != LAPSUM_OK) return gs;
     Workspace* w = wsg.w;
-    launch_select(x, (int)s, l, h, kBucketCapMax, w->ctl, w->sp, w->iw, w->bucket_cnt, st);
+    // as in a forward: the sample histogram, then the gathered window
+    uint32_t* shist = next_sample_hist(w);
+    launch_key_hist(x, (int)s, shist, other_sample_hist(w, shist), st);
+    launch_select(x, (int)s, l, h, kBucketCapMax, w->ctl, w->sp, w->iw, w->bucket_cnt, st, shist, w->swin);
     if (hipStreamSynchronize(st) != hipSuccess) return LAPSUM_ERR_HIP;
     Ctl c;
     if (hipMemcpy(&c, w->ctl, sizeof(Ctl), hipMemcpyDeviceToHost) != hipSuccess) return LAPSUM_ERR_HIP;

@@ -15,10 +15,19 @@ struct SegArrays {
 };
 
 // lapsum_sample.hip
+// hist (may be null): zero on entry, left holding the histogram of the
+// sample keys' leading 12 bits (kSelHistBins words); hclr (may be null): a
+// histogram buffer to clear for the next call
 void launch_sample(const float* r, long long n, double t, unsigned long long seed, int s, float* x, long long* idx_out,
-                   hipStream_t st);
+                   hipStream_t st, uint32_t* hist = nullptr, uint32_t* hclr = nullptr);
+// the sample histogram alone (clears hclr as launch_sample does)
+void launch_key_hist(const float* x, int s, uint32_t* hist, uint32_t* hclr, hipStream_t st);
+// hist, win (both or neither): the sample's histogram from launch_sample and
+// a window buffer (kWinHdr + kWinMax words, fill count zero on entry and on
+// exit): the window of sample keys around ranks l..h is gathered by many
+// workgroups first
 void launch_select(const float* x, int s, long long l, long long h, int cap, Ctl* ctl, float* sp, float* iw,
-                   uint32_t* bucket_cnt, hipStream_t st);
+                   uint32_t* bucket_cnt, hipStream_t st, const uint32_t* hist = nullptr, uint32_t* win = nullptr);
 
 // lapsum_stream.hip
 int stream_blocks(long long n);

@@ -188,6 +188,39 @@ def test_select_order_statistics():
             assert 1 <= nb.value <= 1024
 
 
+# Samples built so that the select's three ways to its order statistics all
+# run: the window the sample histogram names (keys spread over many 12-bit
+# bins), the select's own subsample window (every key in one 12-bit bin, so
+# the histogram's window is the whole sample) and the radix select (every key
+# in one 16-bit bin too), plus ties.  Each must give x_(l) and x_(h) exactly.
+SELECT_SAMPLES = {
+    "spread": lambda rng, s: rng.standard_normal(s) * 3.0,
+    "one_12bit_bin": lambda rng, s: 1.0 + rng.uniform(0.0, 0.1249, s),
+    "one_16bit_bin": lambda rng, s: 1.0 + rng.uniform(0.0, 0.0078, s),
+    "ties": lambda rng, s: rng.integers(0, 7, s).astype(np.float64),
+    "negative_cluster": lambda rng, s: -2.0 - rng.exponential(0.05, s),
+}
+
+
+@pytest.mark.parametrize("kind", sorted(SELECT_SAMPLES))
+@pytest.mark.parametrize("s", [3000, 12650, 40000])
+def test_select_window_forms(kind, s):
+    rng = np.random.default_rng(1000 * sorted(SELECT_SAMPLES).index(kind) + s)
+    x = SELECT_SAMPLES[kind](rng, s).astype(np.float32)
+    xs = np.sort(x)
+    for l, h in ((s - 40, s - 2), (s // 2, s // 2 + 30), (5, 60), (1, 1), (s, s), (0, 7), (s - 7, s + 1)):
+        aL = L._binding.ctypes.c_float()
+        aR = L._binding.ctypes.c_float()
+        nb = L._binding.ctypes.c_int32()
+        rc = L.lib().lapsum_test_select(to_dev(x).data_ptr(), s, l, h, L._binding.ctypes.byref(aL),
+                                        L._binding.ctypes.byref(aR), L._binding.ctypes.byref(nb), None)
+        assert rc == 0
+        eL = -np.inf if l < 1 else xs[l - 1]
+        eR = np.inf if h > s else xs[h - 1]
+        assert aL.value == eL and aR.value == eR, (kind, s, l, h, aL.value, eL, aR.value, eR)
+        assert 1 <= nb.value <= 1024
+
+
 @pytest.mark.parametrize("aL,aR", [(1.0, 2.5), (-np.inf, -1.0), (2.0, np.inf), (0.3, 0.3001), (0.5, 0.5)])
 def test_filter_band_bit_exact(oracle_mod, aL, aR):
     r, _, _ = workloads.config_inputs("C3", 400_003)
