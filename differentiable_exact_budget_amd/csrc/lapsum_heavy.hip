@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kHeavyThreads) void k_heavy_collect(const float* __
                                               [&](float4 qv, long long) {
                                                   one_lane(qv.x); one_lane(qv.y); one_lane(qv.z); one_lane(qv.w);
                                               },
-                                              prologue);
+                                              prologue, [](long long) {});
         if (blockIdx.x == 0 && tid < 4) {
             const long long j = (n4 << 2) + tid;
             if (j < n) one_lane(r[j]);

@@ -800,7 +800,7 @@ lapsum_status_t order_stats_impl(Workspace* w, const float* r, long long n, long
             tm.end();
             const unsigned int seq = ++w->seq;
             tm.begin("filter");
-            launch_filter(r, n, 1.0, w->ctl, w->sp, w->iw, w->bucket_cnt, w->bucket_vals, cap, w->part, nullptr,
+            launch_filter(r, n, 1.0, w->ctl, w->sp, w->iw, w->bucket_cnt, w->bucket_vals, cap, w->part,
                           w->hs_dev, seq, st, (double)k);
             tm.end();
             if (hipGetLastError() != hipSuccess) return LAPSUM_ERR_HIP;
@@ -1134,7 +1134,7 @@ lapsum_status_t lapsum_test_filter(const float* scores, int64_t n, float t, floa
     launch_select(w->sample, 2, l, h, kBucketCapMax, w->ctl, w->sp, w->iw, w->bucket_cnt, st);
     const unsigned int seq = ++w->seq;
     launch_filter(scores, n, (double)t, w->ctl, w->sp, w->iw, w->bucket_cnt, w->bucket_vals, kBucketCapMax, w->part,
-                  nullptr, w->hs_dev, seq, st, 0.5 * (double)n);
+                  w->hs_dev, seq, st, 0.5 * (double)n);
     lapsum_status_t ws = wait_summary(w, st, seq);
     if (ws != LAPSUM_OK) return ws;
     HostSummary hsum = *const_cast<HostSummary*>(w->hs);

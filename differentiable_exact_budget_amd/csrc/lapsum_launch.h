@@ -48,9 +48,8 @@ void launch_cert(const float* r, long long n, double t, Ctl* ctl, double* part, 
                  unsigned int seq, double k, hipStream_t st);
 void launch_or_flags(Ctl* ctl, int flags, hipStream_t st);
 void launch_filter(const float* r, long long n, double t, Ctl* ctl, const float* sp, const float* iw,
-                   uint32_t* bucket_cnt, uint32_t* bucket_vals, int cap, double* part, unsigned long long* partc,
-                   HostSummary* hs_dev, unsigned int seq, hipStream_t st, double k,
-                   const HeavyArrays* ha = nullptr);
+                   uint32_t* bucket_cnt, uint32_t* bucket_vals, int cap, double* part, HostSummary* hs_dev,
+                   unsigned int seq, hipStream_t st, double k, const HeavyArrays* ha = nullptr);
 // returns the number of partials it left (for launch_sum_p)
 // gate (device, may be null): when it holds 0 the kernels return at once
 int launch_probs(const float* r, long long n, double t, float* p, Ctl* ctl, double* part, hipStream_t st,

@@ -105,14 +105,23 @@ LS_DEV double sum_parts(const double* part, int stride, int off, int nparts, dou
 // ---------------------------------------------------------------------------
 // streaming filter
 // ---------------------------------------------------------------------------
-// e^{(a_L - v)/t} and e^{(v - a_R)/t} of a band score (0 for an open end)
-LS_DEV void band_sums(const FilterState& fs, float v, double& BL, double& BR) {
-    if (fs.aL > -INFINITY) BL += (double)__builtin_amdgcn_exp2f(-(v - fs.aL) * fs.ls);
-    if (fs.aR < INFINITY) BR += (double)__builtin_amdgcn_exp2f(-(fs.aR - v) * fs.ls);
+// x (0 <= x < 2^16) in units of 2^-36, rounded to nearest: x 2^36 + 2^52
+// puts that integer in the low mantissa bits of a double in [2^52, 2^53)
+LS_DEV unsigned long long fx36(double x) {
+    return (unsigned long long)__double_as_longlong(fma(x, 0x1p36, 0x1p52)) - 0x4330000000000000ull;
+}
+
+// e^{(a_L - v)/t} and e^{(v - a_R)/t} of a band score (0 for an open end),
+// added in fixed point (fx36): a wave meets the band scores of whichever
+// tiles it took, and integer sums do not depend on that
+LS_DEV void band_sums(const FilterState& fs, float v, unsigned long long& BL, unsigned long long& BR) {
+    if (fs.aL > -INFINITY) BL += fx36((double)__builtin_amdgcn_exp2f(-(v - fs.aL) * fs.ls));
+    if (fs.aR < INFINITY) BR += fx36((double)__builtin_amdgcn_exp2f(-(fs.aR - v) * fs.ls));
 }
 
 // spill path for a band score when the workgroup's LDS queue is full
-LS_DEV void band_direct(const FilterState& fs, float v, double& BL, double& BR, int& nan, uint32_t& nnan) {
+LS_DEV void band_direct(const FilterState& fs, float v, unsigned long long& BL, unsigned long long& BR, int& nan,
+                        uint32_t& nnan) {
     if (v != v) { nan = 1; ++nnan; return; }
     band_sums(fs, v, BL, BR);
     const int bkt = band_bucket(fs, v);
@@ -133,8 +142,8 @@ __global__ __launch_bounds__(NT) void k_filter(const float* __restrict__ r, long
     __shared__ uint32_t qbr[QCAP];  // per queued score: bucket << 16 | rank in the workgroup's bucket
     __shared__ uint32_t lcnt[kMaxBuckets];
     __shared__ uint32_t gbase[kMaxBuckets];
-    __shared__ double s_rd[4 * NWV];
-    __shared__ unsigned long long s_ru[2 * NWV];
+    __shared__ double s_rd[2 * NWV];
+    __shared__ unsigned long long s_ru[6 * NWV];  // NaNs, count above, then S_L, S_R, B_L, B_R in fixed point
     __shared__ uint32_t s_rm[2 * NWV];
     __shared__ unsigned int s_ctr;
     const int tid = threadIdx.x;
@@ -162,7 +171,9 @@ __global__ __launch_bounds__(NT) void k_filter(const float* __restrict__ r, long
     // of an LDS queue, its fill count kept in a wave-uniform register (no
     // atomic, no wait); NaNs land there too and are sorted out at the flush;
     // +-inf shows up in max |r|.
-    double SL = 0.0, SR = 0.0, BL = 0.0, BR = 0.0;
+    double SL = 0.0, SR = 0.0;
+    unsigned long long SLx = 0ull, SRx = 0ull;  // the dynamic walk's S_L and S_R, per tile into fixed point
+    unsigned long long BL = 0ull, BR = 0ull;    // band sums, fixed point
     uint32_t cR = 0u;
     uint32_t nnan = 0u;
     float amax = 0.0f;
@@ -223,13 +234,23 @@ __global__ __launch_bounds__(NT) void k_filter(const float* __restrict__ r, long
         auto main_f = [&](float4 qv, long long) { quad(qv); };
         auto tail_f = [&](float4 qv, long long) { one_lane(qv.x); one_lane(qv.y); one_lane(qv.z); one_lane(qv.w); };
         if constexpr (DYN) {
-            // this workgroup's share of the wave tiles, handed to its waves at run time
+            // this workgroup's share of the wave tiles, handed to its waves
+            // at run time.  A lane's part of a tile is fixed, so its fp64 sum
+            // over the tile is too; that sum goes into a 64-bit fixed-point
+            // total (units of 2^-36, rounded), and integer adds do not depend
+            // on which wave took which tile: the same S_L and S_R every run
             constexpr long long WT = 64LL * kFilterWaveV;
             const long long tiles = (n4 + WT - 1) / WT;
             const long long per = (tiles + gridDim.x - 1) / gridDim.x;
             const long long t0 = min(tiles, (long long)blockIdx.x * per), t1 = min(tiles, t0 + per);
+            auto tile_end = [&](long long) {
+                SLx += fx36(SL);
+                SRx += fx36(SR);
+                SL = 0.0;
+                SR = 0.0;
+            };
             wave_tiles_dynamic<kFilterWaveV, kFilterNT>(reinterpret_cast<const float4*>(r), n4, t0, t1, &s_ctr,
-                                                        main_f, tail_f, prologue);
+                                                        main_f, tail_f, prologue, tile_end);
         } else {
             tile_f4_pipelined<kFilterV, kFilterNT>(reinterpret_cast<const float4*>(r), n4, main_f, tail_f);
         }
@@ -264,14 +285,28 @@ __global__ __launch_bounds__(NT) void k_filter(const float* __restrict__ r, long
         }
     }
     {
-        const double d0 = wave_sum(SL), d1 = wave_sum(SR), d2 = wave_sum(BL), d3 = wave_sum(BR);
+        // the dynamic walk: what the lanes summed outside tiles (the last
+        // n mod 4 scores, fixed lanes) into fixed point too; the static walks
+        // keep fp64 lane sums (their lanes' shares are fixed)
+        double d0 = 0.0, d1 = 0.0;
+        if constexpr (VEC && DYN) {
+            SLx += fx36(SL);
+            SRx += fx36(SR);
+        } else {
+            d0 = wave_sum(SL);
+            d1 = wave_sum(SR);
+        }
         const unsigned long long u0 = wave_sum_u64(nnan), u1 = wave_sum_u64(cR);
+        const unsigned long long x0 = wave_sum_u64(SLx), x1 = wave_sum_u64(SRx);
+        const unsigned long long x2 = wave_sum_u64(BL), x3 = wave_sum_u64(BR);
         const uint32_t m0 = wave_max_u32(__float_as_uint(amax));  // |v| >= 0: uint order = float order
         const uint32_t m1 = wave_max_u32((uint32_t)nan);
         if (lane == 0) {
             const int w = tid >> 6;
-            s_rd[w] = d0; s_rd[NWV + w] = d1; s_rd[2 * NWV + w] = d2; s_rd[3 * NWV + w] = d3;
+            if constexpr (!(VEC && DYN)) { s_rd[w] = d0; s_rd[NWV + w] = d1; }
             s_ru[w] = u0; s_ru[NWV + w] = u1;
+            s_ru[2 * NWV + w] = x0; s_ru[3 * NWV + w] = x1;
+            s_ru[4 * NWV + w] = x2; s_ru[5 * NWV + w] = x3;
             s_rm[w] = m0; s_rm[NWV + w] = m1;
         }
     }
@@ -289,14 +324,22 @@ __global__ __launch_bounds__(NT) void k_filter(const float* __restrict__ r, long
     }
     if (tid < 64) {
         const bool in = lane < NWV;
-        const double d0 = wave_sum(in ? s_rd[lane] : 0.0), d1 = wave_sum(in ? s_rd[NWV + lane] : 0.0);
-        const double d2 = wave_sum(in ? s_rd[2 * NWV + lane] : 0.0), d3 = wave_sum(in ? s_rd[3 * NWV + lane] : 0.0);
-        const unsigned long long u0 = wave_sum_u64(in ? s_ru[lane] : 0ull);
-        const unsigned long long u1 = wave_sum_u64(in ? s_ru[NWV + lane] : 0ull);
+        double d0 = 0.0, d1 = 0.0;
+        if constexpr (!(VEC && DYN)) {
+            d0 = wave_sum(in ? s_rd[lane] : 0.0);
+            d1 = wave_sum(in ? s_rd[NWV + lane] : 0.0);
+        }
+        unsigned long long x[6];
+#pragma unroll
+        for (int q = 0; q < 6; ++q) x[q] = wave_sum_u64(in ? s_ru[q * NWV + lane] : 0ull);
         const uint32_t m0 = wave_max_u32(in ? s_rm[lane] : 0u), m1 = wave_max_u32(in ? s_rm[NWV + lane] : 0u);
         if (tid == 0) {
+            const unsigned long long u0 = x[0], u1 = x[1];
             FilterPart& fp = part[blockIdx.x];
-            fp.S[0] = d0; fp.S[1] = d1; fp.S[2] = d2; fp.S[3] = d3;
+            fp.S[0] = (double)x[2] * 0x1p-36 + d0;
+            fp.S[1] = (double)x[3] * 0x1p-36 + d1;
+            fp.S[2] = (double)x[4] * 0x1p-36;
+            fp.S[3] = (double)x[5] * 0x1p-36;
             fp.c[0] = u0; fp.c[1] = u1;
             fp.mn = 0.0f;
             fp.mx = __uint_as_float(m0);
@@ -485,8 +528,8 @@ void launch_filter_finalize(long long n, double t, Ctl* ctl, const uint32_t* buc
 }
 
 void launch_filter(const float* r, long long n, double t, Ctl* ctl, const float* sp, const float* iw,
-                   uint32_t* bucket_cnt, uint32_t* bucket_vals, int cap, double* part, unsigned long long* /*partc*/,
-                   HostSummary* hs_dev, unsigned int seq, hipStream_t st, double k, const HeavyArrays* ha) {
+                   uint32_t* bucket_cnt, uint32_t* bucket_vals, int cap, double* part, HostSummary* hs_dev,
+                   unsigned int seq, hipStream_t st, double k, const HeavyArrays* ha) {
     const int blocks = launch_filter_pass(r, n, t, ctl, sp, iw, bucket_cnt, bucket_vals, cap, part, st);
     launch_filter_finalize(n, t, ctl, bucket_cnt, cap, part, blocks, hs_dev, seq, st, k, ha);
 }

@@ -204,10 +204,13 @@ LS_DEV void tile_f4_pipelined(const float4* __restrict__ a, long long n4, Main&&
 // the CU serves faster take more tiles, so the workgroup's waves finish
 // together.  prologue() must set *s_ctr to 0.  main(v, idx) runs on full
 // tiles (every lane of the wave active); tail(v, idx) on the elements of a
-// partial last tile.  Needs n4 >= 64 * V (a full tile 0 to fall back on).
-template <int V, bool NT, class Main, class Tail, class Prologue>
+// partial last tile; tile_end(j) after each tile j, by the whole wave (so
+// that what depends on which wave met which tile can be settled per tile).
+// Needs n4 >= 64 * V (a full tile 0 to fall back on).
+template <int V, bool NT, class Main, class Tail, class Prologue, class TileEnd>
 LS_DEV void wave_tiles_dynamic(const float4* __restrict__ a, long long n4, long long t0, long long t1,
-                               unsigned int* s_ctr, Main&& main, Tail&& tail, Prologue&& prologue) {
+                               unsigned int* s_ctr, Main&& main, Tail&& tail, Prologue&& prologue,
+                               TileEnd&& tile_end) {
     constexpr long long T = 64LL * V;
     const long long lane = lane_id();
     const long long nw = blockDim.x >> 6;
@@ -244,6 +247,7 @@ LS_DEV void wave_tiles_dynamic(const float4* __restrict__ a, long long n4, long 
                 if (i < n4) tail(a[i], i);
             }
         }
+        tile_end(j);
         if (!more) break;
         j = jn;
 #pragma unroll

@@ -312,3 +312,30 @@ def test_two_host_threads_one_stream(name, n):
         x.join(timeout=120)
     assert not any(x.is_alive() for x in th)
     assert not bad
+
+
+# ---------------------------------------------------------------------------
+# run-to-run reproducibility
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name,t", [("C3", None), ("C3", 1.0), ("C5", None)])
+def test_bracketing_bit_reproducible(name, t):
+    """The filter hands its tiles to waves at run time, so which lanes sum
+    which scores changes from run to run; its tail and band sums are kept
+    in fixed point so that they, the certification and b do not.  Repeated
+    forwards and VJPs at 10^7 scores (many tiles per wave) must agree bit
+    for bit: b, p, the four filter sums, G at both bracket ends and grad."""
+    r, g, cfg = workloads.config_inputs(name)
+    tt = cfg.t if t is None else t
+    rd, gd = to_dev(r), to_dev(g)
+    ref = None
+    for rep in range(4):
+        p, b, st = L.forward(rd, cfg.k, tt, stats=True)
+        grad = L.vjp(rd, gd, tt, b)
+        assert st["path_taken"] == 2
+        cur = (float(b.item()), st["tail_S_L"], st["tail_S_R"], st["band_B_L"], st["band_B_R"], st["g_aL"], st["g_aR"],
+               p.cpu().numpy().tobytes(), grad.cpu().numpy().tobytes())
+        if ref is None:
+            ref = cur
+        else:
+            assert [x.hex() if isinstance(x, float) else x for x in cur] == \
+                   [x.hex() if isinstance(x, float) else x for x in ref], (name, rep)
