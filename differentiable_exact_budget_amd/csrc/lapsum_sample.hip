@@ -113,9 +113,9 @@ constexpr int kWinKeys = 4;  // sample keys per thread of k_select_window
 
 // One workgroup per kWinThreads * kWinKeys sample keys: every workgroup
 // scans the histogram (the same result in each), and appends its keys inside
-// the window to the window buffer at a place taken with one atomic add.
-// Workgroup 0 writes the header (ok, window size, keys below it); the fill
-// count starts at zero and k_select sets it back to zero.
+// the window to the window buffer, each wave at a place taken with one
+// atomic add.  Workgroup 0 writes the header (ok, window size, keys below
+// it); the fill count starts at zero and k_select sets it back to zero.
 __global__ __launch_bounds__(kWinThreads) void k_select_window(const float* __restrict__ x, int s, long long l,
                                                                long long h, const uint32_t* __restrict__ hist,
                                                                uint32_t* win) {
@@ -123,7 +123,6 @@ __global__ __launch_bounds__(kWinThreads) void k_select_window(const float* __re
     static_assert(BPT % 4 == 0, "");
     __shared__ uint32_t scr[NT / 64 + 2];
     __shared__ uint32_t s_res[4];  // bin of rank l, keys below it; bin of rank h, keys up to its end
-    __shared__ uint32_t s_base;
     const int tid = threadIdx.x;
     uint32_t kk[kWinKeys];
     bool kv[kWinKeys];
@@ -169,11 +168,12 @@ __global__ __launch_bounds__(kWinThreads) void k_select_window(const float* __re
     uint32_t m = 0u;
 #pragma unroll
     for (int q = 0; q < kWinKeys; ++q) m += (kv[q] && kk[q] - wlo <= wspan) ? 1u : 0u;
-    uint32_t wt = 0u;
-    uint32_t pos = block_exclusive_scan<NT>(m, &wt, scr);
-    if (tid == 0) s_base = wt ? atomicAdd(&win[0], wt) : 0u;
-    __syncthreads();
-    pos += s_base;
+    // a place per wave (no barrier): the wave's scan, one atomic add by its
+    // last lane, the base to every lane
+    const uint32_t inc = wave_inclusive_scan(m);
+    uint32_t base = 0u;
+    if (lane_id() == 63 && inc) base = atomicAdd(&win[0], inc);
+    uint32_t pos = __shfl(base, 63, 64) + inc - m;
 #pragma unroll
     for (int q = 0; q < kWinKeys; ++q) {
         if (kv[q] && kk[q] - wlo <= wspan) {
