@@ -117,7 +117,8 @@ typedef struct {
                                         pass (0 otherwise) */
     double sum_p;            /* sum of the written p, accumulated in fp64 on the device */
     double b;                /* threshold */
-    double tail_S_L, tail_S_R, band_B_L, band_B_R; /* the streaming pass's fp64 sums */
+    double tail_S_L, tail_S_R, band_B_L, band_B_R; /* the streaming pass's sums (fp64 per tile and lane, then
+                                                      fixed point in units of 2^-36: the same every run) */
     double vjp_c, vjp_sum_f;  /* lapsum_vjp_ex: c = sum g f / sum f and sum f */
     float kernel_ms[LAPSUM_MAX_TIMED_KERNELS];     /* with options.profile: per-launch times */
     const char* kernel_name[LAPSUM_MAX_TIMED_KERNELS];
