@@ -199,7 +199,7 @@ __global__ __launch_bounds__(NT) void k_filter(const float* __restrict__ r, long
     // four scores, all lanes of the wave active; the band scores among them
     // (rare) are appended to the wave's queue slice
     auto quad = [&](float4 qv) {
-        float eL = 0.0f, eR = 0.0f;
+        float eL = -0.0f, eR = -0.0f;  // -0 + x = x: the first add folds away
         bool b0, b1, b2, b3;
         one(qv.x, eL, eR, b0);
         one(qv.y, eL, eR, b1);
@@ -207,7 +207,12 @@ __global__ __launch_bounds__(NT) void k_filter(const float* __restrict__ r, long
         one(qv.w, eL, eR, b3);
         SL += (double)eL;
         SR += (double)eR;
-        const unsigned long long m0 = ballot(b0), m1 = ballot(b1), m2 = ballot(b2), m3 = ballot(b3);
+        // the band masks straight from the compares' lane masks (every lane
+        // is active here), not from the per-lane flags
+        const unsigned long long m0 = ~(ballot(qv.x < aL) | ballot(qv.x >= aR));
+        const unsigned long long m1 = ~(ballot(qv.y < aL) | ballot(qv.y >= aR));
+        const unsigned long long m2 = ~(ballot(qv.z < aL) | ballot(qv.z >= aR));
+        const unsigned long long m3 = ~(ballot(qv.w < aL) | ballot(qv.w >= aR));
         if (m0 | m1 | m2 | m3) {
             const uint32_t c0 = (uint32_t)popc64(m0), c1 = (uint32_t)popc64(m1), c2 = (uint32_t)popc64(m2);
             const uint32_t tot = c0 + c1 + c2 + (uint32_t)popc64(m3);
