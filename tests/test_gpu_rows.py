@@ -1,8 +1,9 @@
 """GPU parity of the row-wise (batched) operator against the oracle, row by
 row: b, p, the mass of every row and the VJP, for each workgroup size, per-row
-budgets, long rows (sorted through global scratch by one workgroup each, up
-to 65536 scores; longer ones through the single-vector solver), and rows that
-must come out as NaN (a non-finite score, a budget outside (0, n))."""
+budgets, long rows (one workgroup each, up to 65536 scores; longer ones
+through the single-vector solver), rows that the sort-free solve settles and
+rows it hands to the sort, and rows that must come out as NaN (a non-finite
+score, a budget outside (0, n))."""
 import numpy as np
 import pytest
 import torch
@@ -89,3 +90,34 @@ def test_long_rows_ties_and_equal(oracle_mod, n):
     ph, bh = p.cpu().numpy(), b.cpu().numpy()
     for i in range(rows):
         check_forward(oracle_mod, r[i], float(k[i]), 0.05, ph[i], float(bh[i]), label=f"row {i}")
+
+
+@pytest.mark.parametrize("n", [200, 3000, 9000, 30000])
+def test_rows_sort_free_and_sorted(oracle_mod, n):
+    """Rows the sort-free solve settles and rows it hands to the sort.
+
+    The solve moves along the closed-form pieces of the curve and hands a row
+    to the sort when a side of its sums underflows: integer scores one unit
+    apart at t = 1e-3 leave the neighbour on one side of the root about a
+    thousand t away, so those rows are sorted; the same scores at t = 0.5,
+    all-equal rows (root in closed form beside the common value), scores of
+    large magnitude and budgets near 0 and near n are solved without the
+    sort.  Every row is checked against the oracle."""
+    rng = np.random.default_rng(n + 11)
+    rows = 8
+    r = np.empty((rows, n), dtype=np.float32)
+    r[0] = rng.permutation(n).astype(np.float32)
+    r[1] = r[0]
+    r[2] = 0.75
+    r[3] = 0.75
+    r[4] = (1e4 + rng.standard_normal(n)).astype(np.float32)
+    r[5] = rng.standard_normal(n).astype(np.float32)
+    r[6] = rng.standard_normal(n).astype(np.float32)
+    r[7] = rng.permutation(n).astype(np.float32) * 0.5
+    k = np.array([n / 3 + 0.25, n / 3 + 0.25, n / 5, 0.9 * n, n / 7, 1e-3, n - 1e-3, n / 2 + 0.5])
+    ts = [1e-3, 0.5, 0.05, 0.05, 1e-3, 0.05, 0.05, 1e-3]
+    for i in range(rows):
+        rd = to_dev(r[i:i + 1])
+        p, b = L.forward_rows(rd, float(k[i]), ts[i])
+        check_forward(oracle_mod, r[i], float(k[i]), ts[i], p.cpu().numpy()[0], float(b.cpu().numpy()[0]),
+                      label=f"row {i} (t={ts[i]})")
