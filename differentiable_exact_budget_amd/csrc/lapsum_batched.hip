@@ -15,186 +15,27 @@
 
 #include "lapsum_blocksolve.h"
 #include "lapsum_launch.h"
+#include "lapsum_steps.h"
 
 namespace lapsum {
 
 constexpr int kHistCopies_rows = 4;  // lane-group copies of the long-row histograms (as in the radix sort)
 
-// ---------------------------------------------------------------------------
-// Rows solved without a sort, held in registers (score j * NT + tid of the
-// row in v[j] of thread tid).
-//
-// Between two consecutive scores G(x) = sum_i F((r_i - x)/t) has the closed
-// form P/(2w) + N - Q w/2 with w = e^{(x - b)/t}, for any b in that interval:
-// P sums e^{(r_i - b)/t} over the scores below b, Q sums e^{(b - r_i)/t} over
-// those at or above it, N counts the latter (the full-sort solver's curve and
-// its quadratic root in w, gist.science summary section 2.2).  A step takes
-// P, Q, N and the scores next to b in one pass and solves this piece for
-// G = k.  When the root x lies in b's interval it is the root of G;
-// otherwise the next step starts at x.  Carried past a score, the piece
-// underestimates G to the right of b and overestimates it to the left (each
-// branch of the Laplace CDF, extended, stays on one side of it), so the
-// steps approach the root from one side and never step over it: each step
-// but the last crosses at least one score.  Started next to the k-th
-// largest score, a row settles in one to three steps at the temperatures
-// tried; a row still moving after kRowSteps steps, or whose sums underflow on
-// one side (every score there more than ~87 t from b), is sorted instead.
-// ---------------------------------------------------------------------------
-constexpr int kRowSteps = 16;
-
-// a thread's scores of the row: held in registers, or read from the row in
-// global memory at every pass (rows too long for registers)
-template <int NT, int ITEMS>
-struct RegRow {
-    const float (&v)[ITEMS];
-    int n;
-    template <class F>
-    LS_DEV void each(F&& f) const {
-#pragma unroll
-        for (int j = 0; j < ITEMS; ++j)
-            if (j * NT + (int)threadIdx.x < n) f(v[j]);
-    }
-};
-template <int NT>
-struct GlobalRow {
-    const float* rr;
-    int n;
-    template <class F>
-    LS_DEV void each(F&& f) const {
-        constexpr int B = 16;  // loads in flight per thread
-        for (int i0 = (int)threadIdx.x; i0 < n; i0 += B * NT) {
-            float x[B];
-#pragma unroll
-            for (int q = 0; q < B; ++q) x[q] = i0 + q * NT < n ? rr[i0 + q * NT] : 0.0f;
-#pragma unroll
-            for (int q = 0; q < B; ++q)
-                if (i0 + q * NT < n) f(x[q]);
-        }
-    }
-};
-
-struct RowRoot {
-    double b;
-    int ok;
-};
-
-// The start: the middle of the range of keys that share their top 16 bits
-// (sign, exponent and 7 mantissa bits: a range 2^-7 wide relative to the
-// score) with the kk-th largest key of the row (1 <= kk <= n).  Two MSD radix
-// select digits: per 8-bit digit from the top, the keys that agree with the
-// digits found so far are counted by digit (four LDS copies picked by lane),
-// and the digit where the count from the top reaches the rank still to go is
-// kept (measured on gfx950: two digits beat all four, 4096 x 4096 rows 0.094
-// against 0.109 ms, as the steps that follow cost less than the two more
-// digits would).  hist: 4 * 256 words.
+// The sort-free start and steps (lapsum_steps.h) for a row: the
+// start is the middle of the key range that shares its top 16 bits (sign,
+// exponent and 7 mantissa bits: 2^-7 wide relative to the score) with the
+// k-th largest score, from two radix-select digits (measured on gfx950: two
+// digits beat all four, 4096 x 4096 rows 0.094 against 0.109 ms, as the steps
+// that follow cost less than the two more digits would).
 template <int NT, class Row>
-LS_DEV uint32_t row_start_key(const Row& row, uint32_t kk, uint32_t* hist, uint32_t* s_sel) {
-    const int tid = threadIdx.x, lane = lane_id();
-    uint32_t prefix = 0u, mask = 0u, rank = kk;
-    for (int shift = 24; shift >= 16; shift -= 8) {
-        for (int e = tid; e < 4 * 256; e += NT) hist[e] = 0u;
-        __syncthreads();
-        uint32_t* const hl = hist + (lane & 3) * 256;
-        row.each([&](float x) {
-            const uint32_t key = f2key(x);
-            if ((key & mask) == prefix) atomicAdd(&hl[(key >> shift) & 0xFFu], 1u);
-        });
-        __syncthreads();
-        if (tid < 64) {
-            // lane l holds digits 255 - 4l down to 252 - 4l
-            uint32_t c[4], sl = 0u;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int d = 255 - 4 * lane - q;
-                c[q] = hist[d] + hist[256 + d] + hist[512 + d] + hist[768 + d];
-                sl += c[q];
-            }
-            const uint32_t incl = wave_inclusive_scan(sl);
-            const unsigned long long hit = ballot(incl >= rank);
-            const int first = hit ? __ffsll((long long)hit) - 1 : 63;
-            if (lane == first) {
-                uint32_t before = incl - sl;
-                int q = 0;
-                while (q < 3 && before + c[q] < rank) { before += c[q]; ++q; }
-                s_sel[0] = (uint32_t)(255 - 4 * lane - q);
-                s_sel[1] = before;
-            }
-        }
-        __syncthreads();
-        prefix |= s_sel[0] << shift;
-        mask |= 0xFFu << shift;
-        rank -= s_sel[1];
-        __syncthreads();  // s_sel and hist are rewritten by the next digit
-    }
-    return prefix | 0x8000u;
-}
-
-// the steps from b (fixed-order block sums: every thread takes the same x)
-template <int NT, class Row>
-LS_DEV RowRoot row_solve_steps(const Row& row, double k, double t, double inv_t, double b, double* sd,
-                               unsigned long long* su, uint32_t* sm) {
-    const int n = row.n;
-    for (int step = 0; step < kRowSteps; ++step) {
-        double P = 0.0, Q = 0.0;
-        unsigned long long N = 0ull;
-        uint32_t kb = 0u, ka = 0u;  // largest key below b; complement of the smallest key at or above b
-        row.each([&](float x) {
-            const double d = (double)x - b;
-            const float e = __builtin_amdgcn_exp2f((float)(-fabs(d) * inv_t) * 1.4426950408889634f);
-            const uint32_t key = f2key(x);
-            if (d < 0.0) {
-                P += (double)e;
-                kb = max(kb, key);
-            } else {
-                Q += (double)e;
-                ++N;
-                ka = max(ka, ~key);
-            }
-        });
-        double dd[2] = {P, Q};
-        unsigned long long uu[1] = {N};
-        uint32_t mm[2] = {kb, ka};
-        block_reduce_multi<NT>(dd, uu, mm, sd, su, sm);
-        __syncthreads();  // the scratch is rewritten by the next step
-        P = dd[0];
-        Q = dd[1];
-        N = uu[0];
-        const bool below = N < (unsigned long long)n, above = N > 0ull;
-        if ((below && !(P > 0.0)) || (above && !(Q > 0.0))) return {b, 0};
-        const double lo = below ? (double)key2f(mm[0]) : -INFINITY;  // the largest score below b
-        const double hi = above ? (double)key2f(~mm[1]) : INFINITY;  // the smallest score at or above b
-        // P/(2w) + D - Q w/2 = 0 with D = N - k, in the form without cancellation
-        const double D = (double)N - k;
-        double w;
-        if (!above) w = D < 0.0 ? P / (-2.0 * D) : -1.0;
-        else if (!below) w = D > 0.0 ? 2.0 * D / Q : -1.0;
-        else {
-            const double sq = sqrt(D * D + P * Q);
-            w = D >= 0.0 ? (D + sq) / Q : P / (sq - D);
-        }
-        if (!(w > 0.0) || !(w < INFINITY)) return {b, 0};
-        const double x = b + t * log(w);
-        if (!(x == x)) return {b, 0};
-        if (lo < x && x <= hi) return {x, 1};
-        b = x;
-    }
-    return {b, 0};
-}
-
-// k-th largest start and the steps, for a row whose scores are finite and
-// whose budget lies in (0, n)
-template <int NT, class Row>
-LS_DEV RowRoot row_solve(const Row& row, double k, double t, double inv_t, uint32_t* hist, uint32_t* s_sel,
-                         double* sd, unsigned long long* su, uint32_t* sm) {
+LS_DEV StepRoot row_solve(const Row& row, double k, double t, double inv_t, uint32_t* hist, uint32_t* s_sel,
+                          double* sd, unsigned long long* su, uint32_t* sm) {
     const double kf = floor(k);
     const uint32_t kk = (uint32_t)(kf < 1.0 ? 1.0 : (kf > (double)row.n ? (double)row.n : kf));
-    const float b0 = key2f(row_start_key<NT>(row, kk, hist, s_sel));
-    return row_solve_steps<NT>(row, k, t, inv_t, (double)b0, sd, su, sm);
+    const float b0 = key2f(start_key<NT, 2>(row, kk, hist, s_sel));
+    return solve_steps<NT>(row, k, t, inv_t, (double)b0, sd, su, sm);
 }
 
-// 256-thread rows (257..4096 scores) are held to 128 VGPRs, four rows per CU
-// (measured on gfx950: 4096 x 4096 rows 0.354 -> 0.328 ms, 16384 x 1024
-// 0.308 -> 0.273 ms, against three rows per CU at 161 VGPRs)
 template <int NT, int ITEMS>
 __global__ __launch_bounds__(NT, (NT == 256 ? 4 : 1)) void k_rows_forward(const float* __restrict__ r, int n, const double* k_rows,
                                                       double k_all, double t, double inv_t, float* __restrict__ p,
@@ -233,7 +74,7 @@ __global__ __launch_bounds__(NT, (NT == 256 ? 4 : 1)) void k_rows_forward(const 
     __syncthreads();
     if (bad) atomicOr(&s_bad, 1);
     __syncthreads();
-    RowRoot rt{0.0, 0};
+    StepRoot rt{0.0, 0};
     if (!s_bad) rt = row_solve<NT>(RegRow<NT, ITEMS>{v, n}, k, t, inv_t, s_hist, s_sel, s_rd, s_ru, s_rm);
     if (rt.ok) {
         if (tid == 0) { s_b = rt.b; b_out[row] = rt.b; }
@@ -378,7 +219,7 @@ __global__ __launch_bounds__(kLongNT) void k_rows_forward_long(const float* __re
             __syncthreads();
             if (bad) atomicOr(&s_bad, 1);
             __syncthreads();
-            RowRoot rt{0.0, 0};
+            StepRoot rt{0.0, 0};
             if (!s_bad) rt = row_solve<NT>(GlobalRow<NT>{rr, n}, k, t, inv_t, hist, s_sel, s_rd2, s_ru2, s_rm2);
             if (tid == 0) s_skip = rt.ok;
             if (rt.ok && tid == 0) { s_b = rt.b; b_out[row] = rt.b; }
