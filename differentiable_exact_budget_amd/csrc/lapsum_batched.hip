@@ -165,9 +165,55 @@ __global__ __launch_bounds__(NT) void k_rows_vjp(const float* __restrict__ r, co
 }
 
 // ---------------------------------------------------------------------------
-// Long rows (16384 < n <= 65536): a row does not fit one workgroup's LDS, so
-// one workgroup per row sorts it through two global scratch buffers of its
-// own -- an LSD radix sort whose passes it runs alone, 4096 keys at a time:
+// Long rows (16384 < n <= 65536), first without a sort: one 1024-thread
+// workgroup per row reads the row from global memory at every pass (two
+// select digits and the steps) and writes b and p; a row it does not settle
+// gets kRowUnsolved (a NaN payload no other result carries) as its b, and
+// the sorting kernel below, launched behind it, takes exactly those rows.
+// The steps have a kernel of their own so that the sort's register pressure
+// (its spills) stays out of their loops.
+// ---------------------------------------------------------------------------
+constexpr unsigned long long kRowUnsolved = 0x7FF8D0D0D0D0D0D0ull;
+constexpr int kLongStepsNT = 1024;
+
+__global__ __launch_bounds__(kLongStepsNT) void k_rows_steps_long(const float* __restrict__ r, int n,
+                                                                  const double* k_rows, double k_all, double t,
+                                                                  double inv_t, float* __restrict__ p,
+                                                                  double* b_out) {
+    constexpr int NT = kLongStepsNT, NW = NT / 64;
+    __shared__ uint32_t hist[4 * 256];
+    __shared__ uint32_t s_sel[2];
+    __shared__ double s_rd[2 * NW];
+    __shared__ unsigned long long s_ru[NW];
+    __shared__ uint32_t s_rm[2 * NW];
+    __shared__ int s_bad;
+    const int tid = threadIdx.x;
+    const long long row = blockIdx.x;
+    const float* rr = r + row * (long long)n;
+    const double k = k_rows ? k_rows[row] : k_all;
+    if (tid == 0) s_bad = !(k > 0.0 && k < (double)n);
+    int bad = 0;
+    for (int i = tid; i < n; i += NT) bad |= !finite_f(rr[i]);
+    __syncthreads();
+    if (bad) atomicOr(&s_bad, 1);
+    __syncthreads();
+    StepRoot rt{0.0, 0};
+    if (!s_bad) rt = row_solve<NT>(GlobalRow<NT>{rr, n}, k, t, inv_t, hist, s_sel, s_rd, s_ru, s_rm);
+    if (tid == 0) b_out[row] = rt.ok ? rt.b : __longlong_as_double((long long)kRowUnsolved);
+    if (!rt.ok) return;  // workgroup-uniform
+    const double b = rt.b;
+    float* pr = p + row * (long long)n;
+    for (int i = tid; i < n; i += NT) {
+        const float x = (float)(((double)rr[i] - b) * inv_t);
+        const float e = 0.5f * __builtin_amdgcn_exp2f(-fabsf(x) * 1.4426950408889634f);
+        pr[i] = x < 0.0f ? e : 1.0f - e;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Long rows (16384 < n <= 65536) that the steps left: a row does not fit one
+// workgroup's LDS, so one workgroup per row sorts it through two global
+// scratch buffers of its own -- an LSD radix sort whose passes it runs alone, 4096 keys at a time:
 // all four digit histograms in one read, then per pass each chunk ranked
 // stably in LDS and written out at its digits' running offsets -- and solves
 // over the sorted row in 4096-key segments (aggregates per segment, the curve
@@ -204,28 +250,11 @@ __global__ __launch_bounds__(kLongNT) void k_rows_forward_long(const float* __re
     const int tid = threadIdx.x, w = tid >> 6, lane = lane_id();
     uint32_t* const bufA = scratch + (size_t)blockIdx.x * 2 * (size_t)n;
     uint32_t* const bufB = bufA + n;
-    __shared__ uint32_t s_sel[2];
-    __shared__ double s_rd2[2 * NW];
-    __shared__ unsigned long long s_ru2[NW];
-    __shared__ uint32_t s_rm2[2 * NW];
     for (long long row = blockIdx.x; row < rows; row += gridDim.x) {  // workgroup-uniform
         const float* rr = r + row * (long long)n;
         const double k = k_rows ? k_rows[row] : k_all;
-        // 0. the sort-free solve, reading the row at every pass
-        {
-            if (tid == 0) s_bad = !(k > 0.0 && k < (double)n);
-            int bad = 0;
-            for (int i = tid; i < n; i += NT) bad |= !finite_f(rr[i]);
-            __syncthreads();
-            if (bad) atomicOr(&s_bad, 1);
-            __syncthreads();
-            StepRoot rt{0.0, 0};
-            if (!s_bad) rt = row_solve<NT>(GlobalRow<NT>{rr, n}, k, t, inv_t, hist, s_sel, s_rd2, s_ru2, s_rm2);
-            if (tid == 0) s_skip = rt.ok;
-            if (rt.ok && tid == 0) { s_b = rt.b; b_out[row] = rt.b; }
-            __syncthreads();
-        }
-        if (!s_skip) {  // workgroup-uniform: the sort
+        // rows the sort-free kernel settled are done
+        if ((unsigned long long)__double_as_longlong(b_out[row]) != kRowUnsolved) continue;
         // 1. the four digit histograms in one read, and the finiteness check
         for (int e = tid; e < kHistCopies_rows * 4 * 256; e += NT) hist[e] = 0u;
         if (tid == 0) { s_bad = !(k > 0.0 && k < (double)n); s_skip = 0; }
@@ -346,7 +375,6 @@ __global__ __launch_bounds__(kLongNT) void k_rows_forward_long(const float* __re
             s_b = b;
             b_out[row] = b;
         }
-        }
         __syncthreads();
         // 4. p for the row
         const double b = s_b;
@@ -377,6 +405,8 @@ size_t rows_long_scratch_words(long long rows, int n) { return (size_t)rows_long
 
 void launch_rows_forward_long(const float* r, long long rows, int n, const double* k_rows, double k_all, double t,
                               float* p, double* b_out, uint32_t* scratch, hipStream_t st) {
+    hipLaunchKernelGGL(k_rows_steps_long, dim3((unsigned)rows), dim3(kLongStepsNT), 0, st, r, n, k_rows, k_all, t,
+                       1.0 / t, p, b_out);
     hipLaunchKernelGGL(k_rows_forward_long, dim3((unsigned)rows_long_grid(rows)), dim3(kLongNT), 0, st, r, n, rows,
                        k_rows, k_all, t, 1.0 / t, p, b_out, scratch);
 }
