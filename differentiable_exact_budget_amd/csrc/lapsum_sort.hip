@@ -241,6 +241,7 @@ __global__ __launch_bounds__(kSortThreads) void k_band_root(const uint32_t* buck
 // hist: global uint32[kHistGlobalCopies * 1024 + 1] (per copy four 256-bin
 // histograms; then a non-finite flag), all zero on entry and on exit.
 constexpr int kHistCopies = 4;  // LDS histogram copies, by lane & 3
+constexpr int kHistLoads = 4;   // quads a histogram thread has in flight
 
 // the device's resident-pass lock: 0 when free, else the holder's token
 static __device__ unsigned int g_resident_owner;
@@ -269,11 +270,20 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_hist(const float* __res
     if ((reinterpret_cast<uintptr_t>(r) & 15u) == 0u) {
         const long long n4 = n >> 2;
         const float4* r4 = reinterpret_cast<const float4*>(r);
-        for (long long base = (long long)blockIdx.x * kRadixThreads; base < n4; base += stride) {
-            const long long i = base + tid;
-            const bool valid = i < n4;
-            const float4 v = valid ? r4[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            add(v.x, valid); add(v.y, valid); add(v.z, valid); add(v.w, valid);
+        // kHistLoads quads per thread requested at once, then counted
+        for (long long base = (long long)blockIdx.x * (kRadixThreads * kHistLoads); base < n4;
+             base += stride * kHistLoads) {
+            float4 v[kHistLoads];
+#pragma unroll
+            for (int u = 0; u < kHistLoads; ++u) {
+                const long long i = base + u * kRadixThreads + tid;
+                v[u] = i < n4 ? r4[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            }
+#pragma unroll
+            for (int u = 0; u < kHistLoads; ++u) {
+                const bool valid = base + u * kRadixThreads + tid < n4;
+                add(v[u].x, valid); add(v[u].y, valid); add(v[u].z, valid); add(v[u].w, valid);
+            }
         }
         if (blockIdx.x == 0 && tid < 64) {  // the last n % 4 keys, one wave
             const long long j = (n4 << 2) + tid;
@@ -731,18 +741,38 @@ __global__ __launch_bounds__(kSplitThreads) void k_radix_count(const uint32_t* _
     for (int e = tid; e < kHistCopies * 256; e += kSplitThreads) cnt[e] = 0u;
     __syncthreads();
     uint32_t kr[kSplitItems];
-#pragma unroll
-    for (int i = 0; i < kSplitItems; ++i) {
-        const long long idx = base + (long long)((w * kSplitItems + i) * 64 + lane);
-        kr[i] = idx < n ? radix_key(in, in_is_float, idx) : 0u;
-    }
     // counts only: one LDS atomic add per key into the copy of its lane
     // group (as in k_radix_hist)
     uint32_t* cl = cnt + (lane & (kHistCopies - 1)) * 256;
+    if (base + kSplitTile <= n && (reinterpret_cast<uintptr_t>(in) & 15u) == 0u) {
+        // a whole tile (the order of counting is free): four consecutive
+        // keys per 16-byte load, every load of the thread in flight at once
+        constexpr int Q = kSplitItems / 4;
+        static_assert(Q * 4 == kSplitItems, "");
+        const uint4* in4 = reinterpret_cast<const uint4*>(in + base);
+        uint4 q[Q];
 #pragma unroll
-    for (int i = 0; i < kSplitItems; ++i) {
-        const long long idx = base + (long long)((w * kSplitItems + i) * 64 + lane);
-        if (idx < n) atomicAdd(&cl[(kr[i] >> shift) & 0xFFu], 1u);
+        for (int j = 0; j < Q; ++j) q[j] = in4[j * kSplitThreads + tid];
+#pragma unroll
+        for (int j = 0; j < Q; ++j) {
+            kr[4 * j] = q[j].x; kr[4 * j + 1] = q[j].y; kr[4 * j + 2] = q[j].z; kr[4 * j + 3] = q[j].w;
+        }
+#pragma unroll
+        for (int i = 0; i < kSplitItems; ++i) {
+            const uint32_t key = in_is_float ? f2key(__uint_as_float(kr[i])) : kr[i];
+            atomicAdd(&cl[(key >> shift) & 0xFFu], 1u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kSplitItems; ++i) {
+            const long long idx = base + (long long)((w * kSplitItems + i) * 64 + lane);
+            kr[i] = idx < n ? radix_key(in, in_is_float, idx) : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < kSplitItems; ++i) {
+            const long long idx = base + (long long)((w * kSplitItems + i) * 64 + lane);
+            if (idx < n) atomicAdd(&cl[(kr[i] >> shift) & 0xFFu], 1u);
+        }
     }
     __syncthreads();
     if (tid < 256) {  // thread = digit
@@ -864,8 +894,37 @@ __global__ __launch_bounds__(kCurveThreads) void k_curve_tiles(const uint32_t* _
     const int c = rem < kCurveTile ? (int)rem : kCurveTile;
     // stored in the slot the one-workgroup root reads it from
     const int at = seg_slot(tile, (int)((gridDim.x + kCurveRootThreads - 1) / kCurveRootThreads), kCurveRootThreads);
-    segment_aggregates<kCurveThreads>(keys + base, c, inv_t, &seg.first[at], &seg.last[at], &seg.P[at], &seg.Bx[at],
-                                      s_red);
+    if (c == kCurveTile && (reinterpret_cast<uintptr_t>(keys) & 15u) == 0u) {
+        // a whole tile: every key of a thread requested at once (four
+        // 16-byte loads), with the tile's first and last key
+        constexpr int Q = kCurveTile / (4 * kCurveThreads);
+        const uint4* k4 = reinterpret_cast<const uint4*>(keys + base);
+        const int tid = threadIdx.x;
+        uint4 q[Q];
+#pragma unroll
+        for (int j = 0; j < Q; ++j) q[j] = k4[j * kCurveThreads + tid];
+        const float f = key2f(keys[base]);
+        const float l = key2f(keys[base + c - 1]);
+        double p = 0.0, bx = 0.0;
+        auto one = [&](uint32_t key, bool first) {
+            const double v = (double)key2f(key);
+            p += (double)exp_neg((float)((v - (double)l) * inv_t));
+            if (!first) bx += (double)exp_neg((float)(((double)f - v) * inv_t));
+        };
+#pragma unroll
+        for (int j = 0; j < Q; ++j) {
+            one(q[j].x, j == 0 && tid == 0);  // key 0 is v_0 itself: no term in Bx
+            one(q[j].y, false);
+            one(q[j].z, false);
+            one(q[j].w, false);
+        }
+        const double ps = block_sum<kCurveThreads>(p, s_red);
+        const double bs = block_sum<kCurveThreads>(bx, s_red);
+        if (tid == 0) { seg.first[at] = f; seg.last[at] = l; seg.P[at] = ps; seg.Bx[at] = bs; }
+    } else {
+        segment_aggregates<kCurveThreads>(keys + base, c, inv_t, &seg.first[at], &seg.last[at], &seg.P[at],
+                                          &seg.Bx[at], s_red);
+    }
     if (threadIdx.x == 0) { seg.cnt[at] = (uint32_t)c; seg.off[at] = (uint32_t)base; }
 }
 
