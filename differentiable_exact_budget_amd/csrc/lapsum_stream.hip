@@ -991,6 +991,64 @@ __global__ __launch_bounds__(kStreamThreads) void k_vjp_apply(const float* __res
     }
 }
 
+// The apply pass with c formed in every workgroup from the reduce pass's
+// partials (at most kStreamThreads of them, one per thread), as k_vjp_c forms
+// it: each partial brought to the smallest reference M, then summed in a
+// fixed order.  This saves the launch of k_vjp_c where the reduce leaves few
+// partials (n up to about 10^6); workgroup 0 also stores sum f, sum f g and
+// c in the control block.
+constexpr int kFuseCParts = kStreamThreads;
+
+__global__ __launch_bounds__(kStreamThreads) void k_vjp_apply_fc(const float* __restrict__ r,
+                                                                  const float* __restrict__ g, long long n,
+                                                                  const double* bptr, double inv_t, float log2_inv_2t,
+                                                                  const double* part, int nparts, Ctl* ctl,
+                                                                  float* __restrict__ grad) {
+    constexpr int NW = kStreamThreads / 64;
+    __shared__ double s_rd[2 * NW];
+    __shared__ unsigned long long s_ru[NW];
+    __shared__ uint32_t s_rm[NW];
+    __shared__ double s_mn[NW];
+    const int tid = threadIdx.x;
+    const double b = *bptr;
+    // the tile's scores and upstream gradients requested before c is formed
+    const long long n4 = n >> 2;
+    const long long i4 = (long long)blockIdx.x * kStreamThreads + tid;
+    float4 x = make_float4(0.0f, 0.0f, 0.0f, 0.0f), y = x;
+    if (i4 < n4) {
+        x = ld4<kApplyNT>(reinterpret_cast<const float4*>(r) + i4);
+        y = ld4<kApplyNT>(reinterpret_cast<const float4*>(g) + i4);
+    }
+    const bool has = tid < nparts;
+    const double p0 = has ? part[tid] : 0.0;
+    const double p1 = has ? part[(size_t)kReduceGrid + tid] : 0.0;
+    const double ref = has ? part[(size_t)2 * kReduceGrid + tid] : INFINITY;
+    const double M = block_min_nonneg_f64<kStreamThreads>(ref, s_mn);
+    const double sc = !has ? 0.0 : (ref == M ? 1.0 : frame_factor(M - ref));
+    double d[2] = {p0 * sc, p1 * sc};
+    unsigned long long u0[1] = {0ull};
+    uint32_t m0[1] = {0u};
+    block_reduce_multi<kStreamThreads>(d, u0, m0, s_rd, s_ru, s_rm);
+    const double cd = d[0] / d[1];
+    if (blockIdx.x == 0 && tid == 0) {
+        const double scale = exp(-M);
+        ctl->sumfg = d[0] * scale; ctl->sumf = d[1] * scale; ctl->c = cd;
+    }
+    const float c = (float)cd;
+    auto one = [&](float v, float gv) -> float {
+        const float xx = (float)(((double)v - b) * inv_t);
+        const float f_over_t_2p32 = __builtin_amdgcn_exp2f(fmaf(-fabsf(xx), 1.4426950408889634f, log2_inv_2t));
+        return (f_over_t_2p32 * (gv - c)) * 0x1p-32f;
+    };
+    if (i4 < n4)
+        st4<kStoreNT>(reinterpret_cast<float4*>(grad) + i4,
+                      make_float4(one(x.x, y.x), one(x.y, y.y), one(x.z, y.z), one(x.w, y.w)));
+    if (blockIdx.x == 0) {
+        const long long j = (n4 << 2) + tid;
+        if (tid < 4 && j < n) grad[j] = one(r[j], g[j]);
+    }
+}
+
 void launch_vjp(const float* r, const float* g, long long n, double t, const double* b, float* grad, Ctl* ctl,
                 double* part, hipStream_t st, hipEvent_t* ev_mid, bool kt, double* dk_out, double* dt_out) {
     const bool vec = ((reinterpret_cast<uintptr_t>(r) | reinterpret_cast<uintptr_t>(g) |
@@ -1008,11 +1066,20 @@ void launch_vjp(const float* r, const float* g, long long n, double t, const dou
                                     inv_t, part);
         else hipLaunchKernelGGL((k_vjp_reduce<false, false>), dim3(rblocks), dim3(kStreamThreads), 0, st, r, g, n, b,
                                 inv_t, part);
-        hipLaunchKernelGGL(k_vjp_c<false>, dim3(1), dim3(1024), 0, st, part, rblocks, ctl, t, nullptr, nullptr);
+        // with few partials and a gradient to write, c is formed inside the
+        // apply pass (k_vjp_apply_fc)
+        if (!(vec && grad && rblocks <= kFuseCParts))
+            hipLaunchKernelGGL(k_vjp_c<false>, dim3(1), dim3(1024), 0, st, part, rblocks, ctl, t, nullptr, nullptr);
     }
     if (ev_mid) (void)hipEventRecord(*ev_mid, st);
     if (!grad) return;
     const float l2 = (float)(std::log2(0.5 * inv_t) + 32.0);
+    if (!kt && vec && rblocks <= kFuseCParts) {
+        const long long ab = std::max<long long>(1, ((n >> 2) + kStreamThreads - 1) / kStreamThreads);
+        hipLaunchKernelGGL(k_vjp_apply_fc, dim3((unsigned)ab), dim3(kStreamThreads), 0, st, r, g, n, b, inv_t, l2,
+                           part, rblocks, ctl, grad);
+        return;
+    }
     const int ablocks = vec ? tiled_grid<kApplyV>(n >> 2, kApplyGrid) : stream_blocks(n);
     if (vec) hipLaunchKernelGGL(k_vjp_apply<true>, dim3(ablocks), dim3(kStreamThreads), 0, st, r, g, n, b, inv_t, l2,
                                 ctl, grad, kApplyReverse);
