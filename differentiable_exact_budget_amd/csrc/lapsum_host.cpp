@@ -224,7 +224,7 @@ lapsum_status_t alloc_ws(Workspace* w, long long n_cap) {
         return LAPSUM_ERR_HIP;
     if (hipMemsetAsync(w->swin, 0, sizeof(uint32_t) * kWinHdr, w->stream) != hipSuccess) return LAPSUM_ERR_HIP;
     // the radix sort's global digit totals start (and are left) at zero
-    if (hipMemsetAsync(w->hist_part, 0, sizeof(uint32_t) * kHistGlobalWords, w->stream) != hipSuccess)
+    if (hipMemsetAsync(w->hist_part, 0, sizeof(uint32_t) * kHistRegionWords, w->stream) != hipSuccess)
         return LAPSUM_ERR_HIP;
     return LAPSUM_OK;
 }

@@ -31,7 +31,7 @@ struct NoAllocLayout {
     static constexpr long long kProbParts = (kNoAllocMaxN + 2047) / 2048 + 1;                 // p pass partials
     static constexpr size_t ctl = 0;
     static constexpr size_t hist = align256(ctl + sizeof(Ctl));
-    static constexpr size_t goff = align256(hist + sizeof(uint32_t) * kHistGlobalWords);
+    static constexpr size_t goff = align256(hist + sizeof(uint32_t) * kHistRegionWords);
     static constexpr size_t part = align256(goff + sizeof(uint32_t) * 1024);
     static constexpr size_t keysA = align256(part + sizeof(double) * kProbParts);
     static constexpr size_t keysB = align256(keysA + sizeof(uint32_t) * kNoAllocMaxN);

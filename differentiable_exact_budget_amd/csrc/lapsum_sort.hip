@@ -731,7 +731,7 @@ static_assert(kSplitThreads >= 256 && kSplitThreads % 64 == 0, "a thread per dig
 
 __global__ __launch_bounds__(kSplitThreads) void k_radix_count(const uint32_t* __restrict__ in, int in_is_float,
                                                                 long long n, int pass, uint32_t* __restrict__ counts,
-                                                                long long T) {
+                                                                long long T, unsigned long long* totw) {
     __shared__ uint32_t cnt[kHistCopies * 256];
     const int tid = threadIdx.x, w = tid >> 6, lane = lane_id();
     const int shift = 8 * pass;
@@ -757,22 +757,32 @@ __global__ __launch_bounds__(kSplitThreads) void k_radix_count(const uint32_t* _
         for (int j = 0; j < Q; ++j) {
             kr[4 * j] = q[j].x; kr[4 * j + 1] = q[j].y; kr[4 * j + 2] = q[j].z; kr[4 * j + 3] = q[j].w;
         }
+        bool bad = false;
 #pragma unroll
         for (int i = 0; i < kSplitItems; ++i) {
+            if (in_is_float) bad |= !finite_f(__uint_as_float(kr[i]));
             const uint32_t key = in_is_float ? f2key(__uint_as_float(kr[i])) : kr[i];
             atomicAdd(&cl[(key >> shift) & 0xFFu], 1u);
         }
+        if (ballot(bad) != 0ull && lane == 0) atomicOr(&totw[4 * 256], 1ull);
     } else {
+        bool bad = false;
 #pragma unroll
         for (int i = 0; i < kSplitItems; ++i) {
             const long long idx = base + (long long)((w * kSplitItems + i) * 64 + lane);
-            kr[i] = idx < n ? radix_key(in, in_is_float, idx) : 0u;
+            kr[i] = 0u;
+            if (idx < n) {
+                const uint32_t raw = in[idx];
+                if (in_is_float) bad |= !finite_f(__uint_as_float(raw));
+                kr[i] = in_is_float ? f2key(__uint_as_float(raw)) : raw;
+            }
         }
 #pragma unroll
         for (int i = 0; i < kSplitItems; ++i) {
             const long long idx = base + (long long)((w * kSplitItems + i) * 64 + lane);
             if (idx < n) atomicAdd(&cl[(kr[i] >> shift) & 0xFFu], 1u);
         }
+        if (ballot(bad) != 0ull && lane == 0) atomicOr(&totw[4 * 256], 1ull);
     }
     __syncthreads();
     if (tid < 256) {  // thread = digit
@@ -783,40 +793,88 @@ __global__ __launch_bounds__(kSplitThreads) void k_radix_count(const uint32_t* _
     }
 }
 
-// one workgroup per digit: exclusive scan of its counts over the tiles
+// One workgroup per digit: exclusive scan of its counts over the tiles,
+// starting at the digit's global offset, which the scan forms itself (no
+// histogram pass before the split sort): each workgroup takes a digit d in
+// arrival order (a ticket), publishes its column total, then adds up the
+// totals of the digits below d.  A workgroup waits only on workgroups that
+// took a ticket before it and publish without waiting, so the waits end
+// whatever the residency; they are bounded all the same (a broken invariant
+// becomes a reported error).  The workgroup with digit 0 of pass 0 also sets
+// the non-finite flag from what the count pass saw.
+// totw: this sort's uint64 words, [pass * 256 + d] = 2^32 | total, zero
+// until published (the scatter pass clears them); [4 * 256] non-finite.
 __global__ __launch_bounds__(1024) void k_radix_scan(const uint32_t* __restrict__ counts, long long T, int pass,
-                                                      const uint32_t* __restrict__ goff,
-                                                      uint32_t* __restrict__ tile_base) {
-    constexpr int IT = 8;
-    __shared__ uint32_t scr[1024 / 64 + 2];
-    const int d = blockIdx.x, tid = threadIdx.x;
+                                                      uint32_t* __restrict__ tile_base, unsigned long long* totw,
+                                                      Ctl* ctl) {
+    constexpr int IT = 8, NT = 1024;
+    __shared__ uint32_t scr[NT / 64 + 2];
+    __shared__ int s_d;
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        const unsigned int tk = atomicAdd(&ctl->scan_ticket, 1u);
+        if (tk == gridDim.x - 1u) atomicExch(&ctl->scan_ticket, 0u);  // every ticket of the pass is out
+        s_d = (int)tk;
+    }
+    __syncthreads();
+    const int d = s_d;
     const uint32_t* col = counts + (size_t)d * (size_t)T;
     uint32_t* out = tile_base + (size_t)d * (size_t)T;
-    uint32_t carry = goff[pass * 256 + d];
-    for (long long c0 = 0; c0 < T; c0 += 1024LL * IT) {
-        uint32_t v[IT];
+    // the column total (the first chunk stays in registers)
+    uint32_t v[IT];
+    uint32_t part = 0u;
+    for (long long c0 = 0; c0 < T; c0 += (long long)NT * IT) {
+#pragma unroll
+        for (int q = 0; q < IT; ++q) {
+            const long long t = c0 + (long long)tid * IT + q;
+            const uint32_t x = t < T ? col[t] : 0u;
+            if (c0 == 0) v[q] = x;
+            part += x;
+        }
+    }
+    uint32_t total = 0u;
+    (void)block_exclusive_scan<NT>(part, &total, scr);
+    unsigned long long* tw = totw + (size_t)pass * 256;
+    if (tid == 0) __hip_atomic_store(tw + d, (1ull << 32) | total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // the digits below d: thread i < d waits for total i
+    uint32_t below = 0u;
+    if (tid < d) {
+        unsigned int spins = 0u;
+        while (true) {
+            const unsigned long long x = __hip_atomic_load(tw + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (x >> 32) { below = (uint32_t)x; break; }
+            if (++spins > (1u << 24)) { atomicOr(&ctl->flags, kFlagInternal); break; }
+            __builtin_amdgcn_s_sleep(1);
+        }
+    }
+    uint32_t carry = 0u;
+    (void)block_exclusive_scan<NT>(below, &carry, scr);
+    if (pass == 0 && d == 0 && tid == 0)  // the sort starts the flags afresh, as the histogram kernel does
+        ctl->flags = __hip_atomic_load(totw + 4 * 256, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ? kFlagNonFinite : 0;
+    for (long long c0 = 0; c0 < T; c0 += (long long)NT * IT) {
         uint32_t sum = 0u;
 #pragma unroll
         for (int q = 0; q < IT; ++q) {
             const long long t = c0 + (long long)tid * IT + q;
-            v[q] = t < T ? col[t] : 0u;
+            if (c0 != 0) v[q] = t < T ? col[t] : 0u;
             sum += v[q];
         }
-        uint32_t total = 0u;
-        uint32_t ex = block_exclusive_scan<1024>(sum, &total, scr) + carry;
+        uint32_t ctotal = 0u;
+        uint32_t ex = block_exclusive_scan<NT>(sum, &ctotal, scr) + carry;
 #pragma unroll
         for (int q = 0; q < IT; ++q) {
             const long long t = c0 + (long long)tid * IT + q;
             if (t < T) out[t] = ex;
             ex += v[q];
         }
-        carry += total;
+        carry += ctotal;
     }
 }
 
 __global__ __launch_bounds__(kSplitThreads) void k_radix_scatter(const uint32_t* __restrict__ in, int in_is_float,
                                                                   uint32_t* __restrict__ out, long long n, int pass,
-                                                                  const uint32_t* __restrict__ tile_base, long long T) {
+                                                                  const uint32_t* __restrict__ tile_base, long long T,
+                                                                  unsigned long long* totw) {
     constexpr int NW = kSplitThreads / 64;
     __shared__ uint32_t cnt[256 * NW];
     __shared__ uint32_t stage[kSplitTile];
@@ -825,6 +883,10 @@ __global__ __launch_bounds__(kSplitThreads) void k_radix_scatter(const uint32_t*
     __shared__ uint32_t scr[NW + 2];
     const int tid = threadIdx.x, w = tid >> 6, lane = lane_id();
     const int shift = 8 * pass;
+    if (blockIdx.x == 0) {  // the scan has read this pass's digit totals (and the non-finite flag)
+        if (tid < 256) totw[pass * 256 + tid] = 0ull;
+        if (pass == 0 && tid == 0) totw[4 * 256] = 0ull;
+    }
     const long long tile = xcd_tile(T);
     if (tile >= T) return;
     const long long base = tile * kSplitTile;
@@ -1027,8 +1089,12 @@ void launch_radix_sort(const float* r, long long n, uint32_t* keysA, uint32_t* k
     const bool onesweep = form != 2 && radix_uses_onesweep(n);
     // the lock holder's token: the control block's address (distinct per workspace)
     const unsigned int token = (unsigned int)(reinterpret_cast<uintptr_t>(ctl) >> 8) | 1u;
-    hipLaunchKernelGGL(k_radix_hist, dim3(hb), dim3(kRadixThreads), 0, s, r, n, hist_part, goff, ctl,
-                       onesweep && form == 0 ? 1 : 0, token);
+    // the one-kernel passes take their digit offsets from the histogram
+    // kernel; the split passes form them in their scan kernels
+    if (onesweep)
+        hipLaunchKernelGGL(k_radix_hist, dim3(hb), dim3(kRadixThreads), 0, s, r, n, hist_part, goff, ctl,
+                           form == 0 ? 1 : 0, token);
+    unsigned long long* totw = reinterpret_cast<unsigned long long*>(hist_part + kSplitTotOffset);
     const long long T = onesweep ? (n + kPassTile - 1) / kPassTile : (n + kSplitTile - 1) / kSplitTile;
     // the status region: the one-kernel passes' count and offset words (8
     // bytes, 256 T each), or the split passes' tile counts and tile offsets
@@ -1044,10 +1110,10 @@ void launch_radix_sort(const float* r, long long n, uint32_t* keysA, uint32_t* k
                                status, epoch_base + (uint32_t)p, goff, ctl);
         } else {
             hipLaunchKernelGGL(k_radix_count, dim3(xcd_grid(T)), dim3(kSplitThreads), 0, s, src, is_float, n, p,
-                               counts, T);
-            hipLaunchKernelGGL(k_radix_scan, dim3(256), dim3(1024), 0, s, counts, T, p, goff, tile_base);
+                               counts, T, totw);
+            hipLaunchKernelGGL(k_radix_scan, dim3(256), dim3(1024), 0, s, counts, T, p, tile_base, totw, ctl);
             hipLaunchKernelGGL(k_radix_scatter, dim3(xcd_grid(T)), dim3(kSplitThreads), 0, s, src, is_float, dst, n,
-                               p, tile_base, T);
+                               p, tile_base, T, totw);
         }
         src = dst;
         dst = (dst == keysA) ? keysB : keysA;
