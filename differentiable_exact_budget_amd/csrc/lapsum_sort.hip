@@ -892,13 +892,32 @@ __global__ __launch_bounds__(kSplitThreads) void k_radix_scatter(const uint32_t*
     const long long base = tile * kSplitTile;
     for (int e = tid; e < 256 * NW; e += kSplitThreads) cnt[e] = 0u;
     if (tid < 256) gbase[tid] = tile_base[(size_t)tid * (size_t)T + (size_t)tile];
-    __syncthreads();
     uint32_t kr[kSplitItems];
     uint32_t rk[kSplitItems];
+    if (base + kSplitTile <= n && (reinterpret_cast<uintptr_t>(in) & 15u) == 0u) {
+        // a whole tile read with 16-byte loads, then turned into the rows the
+        // ranking walks (wave w, row i: keys (w * kSplitItems + i) * 64 + lane)
+        // through the stage buffer, which the ranking's barrier frees again
+        constexpr int Q = kSplitItems / 4;
+        const uint4* in4 = reinterpret_cast<const uint4*>(in + base);
+        uint4 q[Q];
 #pragma unroll
-    for (int i = 0; i < kSplitItems; ++i) {
-        const long long idx = base + (long long)((w * kSplitItems + i) * 64 + lane);
-        kr[i] = idx < n ? radix_key(in, in_is_float, idx) : 0u;
+        for (int j = 0; j < Q; ++j) q[j] = in4[j * kSplitThreads + tid];
+#pragma unroll
+        for (int j = 0; j < Q; ++j) reinterpret_cast<uint4*>(stage)[j * kSplitThreads + tid] = q[j];
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kSplitItems; ++i) {
+            const uint32_t raw = stage[(w * kSplitItems + i) * 64 + lane];
+            kr[i] = in_is_float ? f2key(__uint_as_float(raw)) : raw;
+        }
+    } else {
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kSplitItems; ++i) {
+            const long long idx = base + (long long)((w * kSplitItems + i) * 64 + lane);
+            kr[i] = idx < n ? radix_key(in, in_is_float, idx) : 0u;
+        }
     }
     volatile uint32_t* vc = cnt;
 #pragma unroll

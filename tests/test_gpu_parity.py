@@ -358,6 +358,27 @@ def test_nonfinite_scores(n, bad):
     assert e.value.code == 2
 
 
+@pytest.mark.parametrize("bad", [np.nan, -np.inf])
+def test_nonfinite_scores_split_sort(bad):
+    """Above 2^20 scores the full sort runs its split passes, whose first
+    count pass looks for non-finite scores: b is NaN, a call with stats
+    reports the error, and a finite call right after on the same workspace
+    is not affected (the flag is not left behind)."""
+    n = 2_000_000
+    r = workloads.scores("normal", n, 5)
+    good = r.copy()
+    r[n // 3] = bad
+    opt = L.default_options(path=L.PATH_FULL)
+    p, b = L.forward(to_dev(r), 10.0, 0.1, options=opt)
+    assert np.isnan(b.item())
+    with pytest.raises(L.LapsumError) as e:
+        L.forward(to_dev(r), 10.0, 0.1, options=opt, stats=True)
+    assert e.value.code == 2
+    p, b, st = L.forward(to_dev(good), 10.0, 0.1, options=opt, stats=True)
+    assert st["status"] == 0 and np.isfinite(b.item())
+    assert abs(p.double().sum().item() - 10.0) <= 1e-5 * 10.0
+
+
 @pytest.mark.parametrize("frac", [0.25, 0.5])
 def test_bracket_many_splitter_gaps(oracle_mod, frac):
     """Large budgets put hundreds of sample points inside the bracket, hence
