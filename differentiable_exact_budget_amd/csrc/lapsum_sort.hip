@@ -437,16 +437,32 @@ LS_DEV void pass_resident(const uint32_t* __restrict__ in, int in_is_float, uint
     unsigned long long* base_words = status + (size_t)256 * T;   // [digit][tile]
     const long long base = (long long)tile * kPassTile;
     uint32_t kr[kPassItems];
+    // a whole tile: one 16-byte load per thread, turned into the ranking's
+    // rows (wave w, row i: keys (w * kPassItems + i) * 64 + lane) through the
+    // stage buffer, which is written again only after the ranking's barrier
+    static_assert(kPassItems == 4, "one 16-byte load per thread");
+    const bool whole = base + kPassTile <= n && (reinterpret_cast<uintptr_t>(in) & 15u) == 0u;
+    if (whole) {
+        reinterpret_cast<uint4*>(stage)[tid] = reinterpret_cast<const uint4*>(in + base)[tid];
+    } else {
 #pragma unroll
-    for (int i = 0; i < kPassItems; ++i) {
-        const long long idx = base + (long long)((w * kPassItems + i) * 64 + lane);
-        uint32_t key = 0u;
-        if (idx < n) key = in_is_float ? f2key(__uint_as_float(in[idx])) : in[idx];
-        kr[i] = key;
+        for (int i = 0; i < kPassItems; ++i) {
+            const long long idx = base + (long long)((w * kPassItems + i) * 64 + lane);
+            uint32_t key = 0u;
+            if (idx < n) key = in_is_float ? f2key(__uint_as_float(in[idx])) : in[idx];
+            kr[i] = key;
+        }
     }
     for (int e = tid; e < 256 * NW; e += kPassThreads) cnt[e] = 0u;
     hist[tid] = 0u;  // kHistCopies * 256 == kPassThreads
     __syncthreads();
+    if (whole) {
+#pragma unroll
+        for (int i = 0; i < kPassItems; ++i) {
+            const uint32_t raw = stage[(w * kPassItems + i) * 64 + lane];
+            kr[i] = in_is_float ? f2key(__uint_as_float(raw)) : raw;
+        }
+    }
     // 1. the tile's digit counts, published as soon as the keys are in: one
     // LDS atomic add per key into the copy of its lane group (as in
     // k_radix_hist); the stable ranking below runs while the counts travel
