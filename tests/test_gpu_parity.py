@@ -428,3 +428,22 @@ def test_bracket_tie_cluster(oracle_mod, copies, k):
             assert "root_bucket_sort" in names, (names, info, float(q), k)
     b_ref = check_forward(oracle_mod, r, k, 0.01, p, b, label=f"cluster {copies}")
     check_vjp(oracle_mod, r, g, 0.01, b_ref, grad, label=f"cluster {copies}")
+
+
+@pytest.mark.parametrize("n", [4093, 1_048_576, 1_048_576 + 4097])
+def test_vjp_c_formed_in_apply_and_apart(oracle_mod, n):
+    """The VJP's reduce leaves one partial per 4096 scores: up to 256 of them
+    (n <= 2^20) the apply pass forms c itself, above that a kernel of its own
+    does.  Both sides of that switch, and a size with a ragged tail, against
+    the oracle; c and sum f from the stats against the oracle's sums."""
+    r = workloads.scores("normal", n, 900 + n % 97)
+    g = workloads.upstream(n, 901)
+    t = 0.05
+    b_ref, _ = oracle_mod.solve(r.astype(np.float64), 0.01 * n, t32(t))
+    b = torch.tensor([b_ref], dtype=torch.float64, device="cuda")
+    grad, st = L.vjp(to_dev(r), to_dev(g), t, b, stats=True)
+    check_vjp(oracle_mod, r, g, t, b_ref, grad.cpu().numpy(), label=f"n={n}")
+    r64, g64 = r.astype(np.float64), g.astype(np.float64)
+    f = 0.5 * np.exp(-np.abs(r64 - b_ref) / t32(t))
+    assert abs(st["vjp_c"] - (f * g64).sum() / f.sum()) <= 1e-6 * (np.abs(g64).max() + 1.0)
+    assert abs(st["vjp_sum_f"] / f.sum() - 1.0) <= 1e-6
