@@ -25,8 +25,9 @@ constexpr int kRadixHistBlocks = 512;
 constexpr int kHistStride = 1028;        // 4 x 256 digit counts + a non-finite flag, per workgroup
 constexpr int kHistGlobalCopies = 8;     // copies of the radix sort's global digit totals
 constexpr int kHistGlobalWords = kHistGlobalCopies * 1024 + 1;  // the copies, then a non-finite flag
-// the split radix passes' digit totals (uint64: a published flag and the
-// count, 256 per pass) and their non-finite flag, inside the same region
+// the split radix passes' digit totals (eight per-XCD copies of 256 uint32
+// words, for the pass under way) and their non-finite flag (uint64 word
+// 4 * 256), inside the same region
 constexpr int kSplitTotOffset = ((kHistGlobalWords + 63) / 64) * 64;  // uint32 words
 constexpr int kSplitTotWords = 4 * 256 + 1;                            // uint64 words
 constexpr int kHistRegionWords = kSplitTotOffset + 2 * kSplitTotWords;  // uint32 words, zero on entry and exit
@@ -83,8 +84,7 @@ struct Ctl {
     // holds the device's resident-pass lock (set by the histogram kernel)
     unsigned int tile_ctr[4];
     int resident;
-    unsigned int scan_ticket;  // split radix passes: digits taken by the scan's workgroups
-    unsigned int pad1[2];
+    unsigned int pad1[3];
     // 1 when the filter certified the bracket with every band score stored:
     // the band solve and p pass launched right behind it then do their work
     int32_t gate;

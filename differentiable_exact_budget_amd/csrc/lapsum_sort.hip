@@ -806,73 +806,45 @@ __global__ __launch_bounds__(kSplitThreads) void k_radix_count(const uint32_t* _
 #pragma unroll
         for (int q = 0; q < kHistCopies; ++q) c += cnt[q * 256 + tid];
         counts[(size_t)tid * (size_t)T + (size_t)tile] = c;
+        // the pass's digit totals: eight copies, one per XCD (workgroups are
+        // dealt to the XCDs in turn), so that each word takes the adds of
+        // one XCD's tiles only
+        if (c) atomicAdd(reinterpret_cast<uint32_t*>(totw) + (blockIdx.x % kXcds) * 256 + tid, c);
     }
 }
 
 // One workgroup per digit: exclusive scan of its counts over the tiles,
 // starting at the digit's global offset, which the scan forms itself (no
-// histogram pass before the split sort): each workgroup takes a digit d in
-// arrival order (a ticket), publishes its column total, then adds up the
-// totals of the digits below d.  A workgroup waits only on workgroups that
-// took a ticket before it and publish without waiting, so the waits end
-// whatever the residency; they are bounded all the same (a broken invariant
-// becomes a reported error).  The workgroup with digit 0 of pass 0 also sets
-// the non-finite flag from what the count pass saw.
-// totw: this sort's uint64 words, [pass * 256 + d] = 2^32 | total, zero
-// until published (the scatter pass clears them); [4 * 256] non-finite.
+// histogram pass before the split sort) from the digit totals the count
+// pass added up: eight copies of 256 words (one per XCD), uint32 words at
+// totw; totw[4 * 256] (uint64) is the non-finite flag.  The workgroup of
+// digit 0 of pass 0 also sets the status flags from that flag.
 __global__ __launch_bounds__(1024) void k_radix_scan(const uint32_t* __restrict__ counts, long long T, int pass,
                                                       uint32_t* __restrict__ tile_base, unsigned long long* totw,
                                                       Ctl* ctl) {
     constexpr int IT = 8, NT = 1024;
     __shared__ uint32_t scr[NT / 64 + 2];
-    __shared__ int s_d;
     const int tid = threadIdx.x;
-    if (tid == 0) {
-        const unsigned int tk = atomicAdd(&ctl->scan_ticket, 1u);
-        if (tk == gridDim.x - 1u) atomicExch(&ctl->scan_ticket, 0u);  // every ticket of the pass is out
-        s_d = (int)tk;
-    }
-    __syncthreads();
-    const int d = s_d;
+    const int d = blockIdx.x;
     const uint32_t* col = counts + (size_t)d * (size_t)T;
     uint32_t* out = tile_base + (size_t)d * (size_t)T;
-    // the column total (the first chunk stays in registers)
-    uint32_t v[IT];
-    uint32_t part = 0u;
-    for (long long c0 = 0; c0 < T; c0 += (long long)NT * IT) {
-#pragma unroll
-        for (int q = 0; q < IT; ++q) {
-            const long long t = c0 + (long long)tid * IT + q;
-            const uint32_t x = t < T ? col[t] : 0u;
-            if (c0 == 0) v[q] = x;
-            part += x;
-        }
-    }
-    uint32_t total = 0u;
-    (void)block_exclusive_scan<NT>(part, &total, scr);
-    unsigned long long* tw = totw + (size_t)pass * 256;
-    if (tid == 0) __hip_atomic_store(tw + d, (1ull << 32) | total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // the digits below d: thread i < d waits for total i
     uint32_t below = 0u;
     if (tid < d) {
-        unsigned int spins = 0u;
-        while (true) {
-            const unsigned long long x = __hip_atomic_load(tw + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (x >> 32) { below = (uint32_t)x; break; }
-            if (++spins > (1u << 24)) { atomicOr(&ctl->flags, kFlagInternal); break; }
-            __builtin_amdgcn_s_sleep(1);
-        }
+        const uint32_t* t32 = reinterpret_cast<const uint32_t*>(totw);
+#pragma unroll
+        for (int q = 0; q < kXcds; ++q) below += t32[q * 256 + tid];
     }
     uint32_t carry = 0u;
     (void)block_exclusive_scan<NT>(below, &carry, scr);
     if (pass == 0 && d == 0 && tid == 0)  // the sort starts the flags afresh, as the histogram kernel does
-        ctl->flags = __hip_atomic_load(totw + 4 * 256, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ? kFlagNonFinite : 0;
+        ctl->flags = totw[4 * 256] ? kFlagNonFinite : 0;
     for (long long c0 = 0; c0 < T; c0 += (long long)NT * IT) {
+        uint32_t v[IT];
         uint32_t sum = 0u;
 #pragma unroll
         for (int q = 0; q < IT; ++q) {
             const long long t = c0 + (long long)tid * IT + q;
-            if (c0 != 0) v[q] = t < T ? col[t] : 0u;
+            v[q] = t < T ? col[t] : 0u;
             sum += v[q];
         }
         uint32_t ctotal = 0u;
@@ -900,7 +872,8 @@ __global__ __launch_bounds__(kSplitThreads) void k_radix_scatter(const uint32_t*
     const int tid = threadIdx.x, w = tid >> 6, lane = lane_id();
     const int shift = 8 * pass;
     if (blockIdx.x == 0) {  // the scan has read this pass's digit totals (and the non-finite flag)
-        if (tid < 256) totw[pass * 256 + tid] = 0ull;
+        uint32_t* t32 = reinterpret_cast<uint32_t*>(totw);
+        for (int i = tid; i < kXcds * 256; i += kSplitThreads) t32[i] = 0u;
         if (pass == 0 && tid == 0) totw[4 * 256] = 0ull;
     }
     const long long tile = xcd_tile(T);
